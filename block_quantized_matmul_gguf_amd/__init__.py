@@ -1,0 +1,232 @@
+"""GGUF quantized matmul for MI355X (gfx950): thin binding over libqmatmul.so.
+
+y = x . W^T with W stored as GGUF Q8_0 or Q4_K blocks, in the two numerical
+forms of the page "同一个 GGUF，CPU 和 Metal 生成的文字不一样" (section 出处):
+
+* ``MODE_F32ACT`` (a): f32 activations, weight blocks dequantized in-kernel;
+* ``MODE_QACT`` (b): activation rows quantized to Q8_0 / Q8K first, integer
+  block dot products scaled by the block scales.
+
+This module only marshals arguments: it checks dtypes, devices, contiguity and
+sizes of torch tensors, then calls the C ABI (``include/qmatmul.h``) with their
+device pointers and the current HIP stream.  Every step of the computation runs
+in the library's HIP kernels; there is no other code path, and importing the
+module fails loudly if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+Q8_0, Q4_K, Q8_K = 8, 12, 15
+MODE_F32ACT, MODE_QACT = 0, 1
+OK, EINVAL, EBLOCK, EUNSUPPORTED, ENOMEM, EHIP = 0, 1, 2, 3, 4, 5
+BLOCK_VALUES = {Q8_0: 32, Q4_K: 256, Q8_K: 256}
+BLOCK_BYTES = {Q8_0: 34, Q4_K: 144, Q8_K: 292}
+ACT_FORMAT = {Q8_0: Q8_0, Q4_K: Q8_K}
+GEMV_MAX_M = 8
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqmatmul.so")
+
+_p, _i64, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+
+# name: (restype, argtypes) for every symbol the header declares
+SIGNATURES = {
+    "qmatmul_create": (_int, [ctypes.POINTER(_p), _int, _i64, _i64, _i64, _int]),
+    "qmatmul_run": (_int, [_p, _p, _p, _p, _i64, _p]),
+    "qmatmul_destroy": (_int, [_p]),
+    "qmatmul_quantize_act": (_int, [_int, _p, _i64, _i64, _p, _p]),
+    "qmatmul_quantize_weights": (_int, [_int, _p, _i64, _i64, _p, _p]),
+    "qmatmul_run_block_sums": (_int, [_p, _p, _p, _p, _i64, _p]),
+    "qmatmul_check": (_int, [_int, _i64, _i64, _i64, _int]),
+    "qmatmul_row_bytes": (_i64, [_int, _i64]),
+    "qmatmul_block_sums_per_row": (_i64, [_int, _i64]),
+    "qmatmul_workspace_bytes": (_i64, [_int, _i64, _i64, _i64, _int]),
+    "qmatmul_status_string": (ctypes.c_char_p, [_int]),
+    "qmatmul_last_error": (ctypes.c_char_p, []),
+    "qmatmul_version": (_int, []),
+}
+
+_lib = None
+
+
+class QmmError(RuntimeError):
+    def __init__(self, status: int, where: str, message: str):
+        super().__init__(f"{where}: status {status} ({status_string(status)}): {message}")
+        self.status = status
+
+
+def lib():
+    """The loaded C library (loaded once)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is not built; build it with "
+                "`python -c 'import __graft_entry__ as g; g.build()'` from the repository root")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().qmatmul_status_string(status).decode()
+
+
+def last_error() -> str:
+    return lib().qmatmul_last_error().decode()
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        raise QmmError(status, where, last_error())
+
+
+# ------------------------------------------------------------ host-only ----
+
+def check(fmt: int, n: int, k: int, m_max: int, mode: int) -> int:
+    """Validate a plan shape without touching the GPU; returns the status code."""
+    return int(lib().qmatmul_check(fmt, n, k, m_max, mode))
+
+
+def row_bytes(fmt: int, k: int) -> int:
+    return int(lib().qmatmul_row_bytes(fmt, k))
+
+
+def block_sums_per_row(fmt: int, k: int) -> int:
+    return int(lib().qmatmul_block_sums_per_row(fmt, k))
+
+
+def workspace_bytes(fmt: int, n: int, k: int, m_max: int, mode: int) -> int:
+    return int(lib().qmatmul_workspace_bytes(fmt, n, k, m_max, mode))
+
+
+# ---------------------------------------------------------- device calls ---
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, dtype, shape, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+class Plan:
+    """One weight shape and mode: ``Plan(fmt, N, K, M_max, mode)``.
+
+    ``run(w, x)`` computes y = x . W^T.  w: uint8 tensor of N*row_bytes(fmt, K)
+    bytes (any shape, contiguous), x: float32 [M, K] with M <= M_max; returns
+    (or fills) float32 [M, N].  The plan's workspace is shared by its runs:
+    use one plan per stream.
+    """
+
+    def __init__(self, fmt: int, n: int, k: int, m_max: int, mode: int):
+        self.fmt, self.n, self.k, self.m_max, self.mode = fmt, n, k, m_max, mode
+        self._h = ctypes.c_void_p()
+        _check(lib().qmatmul_create(ctypes.byref(self._h), fmt, n, k, m_max, mode), "qmatmul_create")
+
+    def _args(self, w, x):
+        torch = _torch()
+        _need(w, torch.uint8, None, "w")
+        if w.numel() != self.n * row_bytes(self.fmt, self.k):
+            raise ValueError(f"w has {w.numel()} bytes, expected {self.n * row_bytes(self.fmt, self.k)}")
+        _need(x, torch.float32, None, "x")
+        if x.dim() != 2 or x.shape[1] != self.k:
+            raise ValueError(f"x must be [M, {self.k}], got {tuple(x.shape)}")
+        return x.shape[0]
+
+    def run(self, w, x, y=None, stream=None):
+        torch = _torch()
+        m = self._args(w, x)
+        if y is None:
+            y = torch.empty((m, self.n), dtype=torch.float32, device=x.device)
+        _need(y, torch.float32, (m, self.n), "y")
+        _check(lib().qmatmul_run(self._h, _ptr(w), _ptr(x), _ptr(y), m, _stream(stream)), "qmatmul_run")
+        return y
+
+    def block_sums(self, w, x, out=None, stream=None):
+        torch = _torch()
+        m = self._args(w, x)
+        spr = block_sums_per_row(self.fmt, self.k)
+        if out is None:
+            out = torch.empty((m, self.n, spr), dtype=torch.int32, device=x.device)
+        _need(out, torch.int32, (m, self.n, spr), "sums")
+        _check(lib().qmatmul_run_block_sums(self._h, _ptr(w), _ptr(x), _ptr(out), m, _stream(stream)),
+               "qmatmul_run_block_sums")
+        return out
+
+    def close(self):
+        if self._h:
+            _check(lib().qmatmul_destroy(self._h), "qmatmul_destroy")
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            if self._h and _lib is not None:
+                _lib.qmatmul_destroy(self._h)
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+
+def quantize_act(act_fmt: int, x, out=None, stream=None):
+    """Canonical Q8_0 (34 B / 32) or Q8K (292 B / 256) blocks of the rows of x
+    (float32 [M, K] on the GPU); returns uint8 [M, row_bytes]."""
+    torch = _torch()
+    _need(x, torch.float32, None, "x")
+    m, k = x.shape
+    rb = row_bytes(act_fmt, k)
+    if rb < 0:
+        raise ValueError(f"K={k} is not a multiple of the block size of format {act_fmt}")
+    if out is None:
+        out = torch.empty((m, rb), dtype=torch.uint8, device=x.device)
+    _need(out, torch.uint8, (m, rb), "out")
+    _check(lib().qmatmul_quantize_act(act_fmt, _ptr(x), m, k, _ptr(out), _stream(stream)), "qmatmul_quantize_act")
+    return out
+
+
+def quantize_weights(fmt: int, w, out=None, stream=None):
+    """GGUF blocks of the rows of w (float32 [N, K] on the GPU); returns uint8 [N, row_bytes]."""
+    torch = _torch()
+    _need(w, torch.float32, None, "w")
+    n, k = w.shape
+    rb = row_bytes(fmt, k)
+    if rb < 0:
+        raise ValueError(f"K={k} is not a multiple of the block size of format {fmt}")
+    if out is None:
+        out = torch.empty((n, rb), dtype=torch.uint8, device=w.device)
+    _need(out, torch.uint8, (n, rb), "out")
+    _check(lib().qmatmul_quantize_weights(fmt, _ptr(w), n, k, _ptr(out), _stream(stream)), "qmatmul_quantize_weights")
+    return out

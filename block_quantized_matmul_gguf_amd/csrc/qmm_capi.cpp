@@ -1,0 +1,305 @@
+// qmm_capi.cpp -- the C ABI declared in include/qmatmul.h: argument checks,
+// plans and their workspace, and dispatch to the decode (M <= 8) or prefill
+// kernels.  Every check runs on the host before any HIP call, so the error
+// paths work without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "../../include/qmatmul.h"
+#include "qmm_internal.h"
+
+using namespace qmm;
+
+struct qmm_plan {
+    int fmt, mode;
+    int64_t N, K, M_max;
+    int device;
+    GemvGeom geom;
+    bool gemv_fast, gemm_fast;
+    void* ws;
+    size_t ws_bytes;
+    GemvBufs gv;
+    GemmBufs gm;
+};
+
+static thread_local char g_err[512];
+
+static int fail(int code, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+static int64_t block_values(int fmt)
+{
+    switch (fmt) {
+    case QMM_Q8_0: return 32;
+    case QMM_Q4_K: return 256;
+    case QMM_Q8_K: return 256;
+    default: return -1;
+    }
+}
+
+static int64_t block_bytes(int fmt)
+{
+    switch (fmt) {
+    case QMM_Q8_0: return 34;
+    case QMM_Q4_K: return 144;
+    case QMM_Q8_K: return 292;
+    default: return -1;
+    }
+}
+
+extern "C" int64_t qmatmul_row_bytes(int format, int64_t K)
+{
+    const int64_t qk = block_values(format);
+    if (qk < 0 || K <= 0 || K % qk) return -1;
+    return K / qk * block_bytes(format);
+}
+
+extern "C" int64_t qmatmul_block_sums_per_row(int format, int64_t K)
+{
+    if (format == QMM_Q8_0 && K > 0 && K % 32 == 0) return K / 32;
+    if (format == QMM_Q4_K && K > 0 && K % 256 == 0) return K / 256 * 10;
+    return -1;
+}
+
+static int check_shape(int format, int64_t N, int64_t K, int64_t M_max, int mode)
+{
+    if (format != QMM_Q8_0 && format != QMM_Q4_K)
+        return fail(QMM_EUNSUPPORTED, "unsupported weight format %d (expected %d Q8_0 or %d Q4_K)", format, QMM_Q8_0,
+                    QMM_Q4_K);
+    if (mode != QMM_MODE_F32ACT && mode != QMM_MODE_QACT)
+        return fail(QMM_EUNSUPPORTED, "unsupported mode %d (expected 0 f32 activations or 1 quantized activations)", mode);
+    if (N <= 0 || K <= 0 || M_max <= 0)
+        return fail(QMM_EINVAL, "sizes must be positive: N=%lld K=%lld M_max=%lld", (long long)N, (long long)K,
+                    (long long)M_max);
+    const int64_t qk = block_values(format);
+    if (K % qk)
+        return fail(QMM_EBLOCK, "quantized tensor must have their last dim divisible by block size [%lld, %lld] %lld",
+                    (long long)N, (long long)K, (long long)qk);
+    if (N > (1ll << 30) || K > (1ll << 20) || M_max > (1ll << 24) || N * (K / qk) * block_bytes(format) > (1ll << 40))
+        return fail(QMM_EINVAL, "shape too large: N=%lld K=%lld M_max=%lld", (long long)N, (long long)K,
+                    (long long)M_max);
+    const bool gemv_ok = gemv_supported(format, K);
+    const bool gemm_ok = format == QMM_Q4_K || (K / 32) % 2 == 0;
+    if (!gemv_ok || !gemm_ok)
+        return fail(QMM_EUNSUPPORTED, "K=%lld has no kernel for this format yet (Q8_0 needs K/32 even and K<=576 or K/32 a multiple of 8)",
+                    (long long)K);
+    return QMM_OK;
+}
+
+extern "C" int qmatmul_check(int format, int64_t N, int64_t K, int64_t M_max, int mode)
+{
+    g_err[0] = 0;
+    return check_shape(format, N, K, M_max, mode);
+}
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Byte layout of the workspace; fills the buffer pointers when base != null.
+static size_t layout(qmm_plan* p, char* base)
+{
+    const int64_t K = p->K, N = p->N;
+    const int64_t mg = p->M_max < GEMV_MAX_M ? p->M_max : GEMV_MAX_M;
+    const int64_t units = p->fmt == QMM_Q8_0 ? K / 32 : K / 256;
+    const bool a = p->mode == QMM_MODE_F32ACT, q4 = p->fmt == QMM_Q4_K;
+    size_t off = 0;
+    auto take = [&](size_t bytes) -> char* {
+        char* r = base ? base + off : nullptr;
+        off += align256(bytes ? bytes : 16);
+        return r;
+    };
+    // decode path
+    p->gv.img = take(a ? 4 * mg * K : mg * K);
+    p->gv.sc0 = (float*)take(a ? 4 * GEMV_MAX_M : 4 * units * GEMV_MAX_M);
+    p->gv.sc1 = take(q4 ? (a ? 4 * (K / 32) * GEMV_MAX_M : 4 * units * 64) : 0);
+    p->gv.part = (float*)take(p->geom.ks > 1 ? 4 * (size_t)p->geom.ks * GEMV_MAX_M * N : 0);
+    p->gv.cnt = (int*)take(4 * ((N + GEMV_ROWS - 1) / GEMV_ROWS));
+    // prefill path
+    if (p->M_max > GEMV_MAX_M) {
+        const int64_t M = p->M_max;
+        p->gm.a0 = (_Float16*)take(2 * M * K);
+        p->gm.a1 = (_Float16*)take(a ? 2 * M * K : 0);
+        p->gm.sc0 = (float*)take(a ? 4 * M : 4 * M * units);
+        p->gm.sc1 = take(q4 ? 4 * M * (K / 32) : 0);
+    } else {
+        p->gm = GemmBufs{};
+    }
+    return off;
+}
+
+extern "C" int64_t qmatmul_workspace_bytes(int format, int64_t N, int64_t K, int64_t M_max, int mode)
+{
+    if (check_shape(format, N, K, M_max, mode) != QMM_OK) return -1;
+    qmm_plan p{};
+    p.fmt = format;
+    p.mode = mode;
+    p.N = N;
+    p.K = K;
+    p.M_max = M_max;
+    p.geom = gemv_geom(format, K);
+    return (int64_t)layout(&p, nullptr);
+}
+
+extern "C" int qmatmul_create(qmm_plan** out, int format, int64_t N, int64_t K, int64_t M_max, int mode)
+{
+    g_err[0] = 0;
+    if (!out) return fail(QMM_EINVAL, "out is NULL");
+    *out = nullptr;
+    int st = check_shape(format, N, K, M_max, mode);
+    if (st != QMM_OK) return st;
+    qmm_plan* p = new (std::nothrow) qmm_plan{};
+    if (!p) return fail(QMM_ENOMEM, "host allocation failed");
+    p->fmt = format;
+    p->mode = mode;
+    p->N = N;
+    p->K = K;
+    p->M_max = M_max;
+    p->geom = gemv_geom(format, K);
+    p->ws_bytes = layout(p, nullptr);
+    hipError_t e = hipGetDevice(&p->device);
+    if (e != hipSuccess) {
+        delete p;
+        return fail(QMM_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    }
+    e = hipMalloc(&p->ws, p->ws_bytes);
+    if (e != hipSuccess) {
+        delete p;
+        return fail(e == hipErrorOutOfMemory ? QMM_ENOMEM : QMM_EHIP, "hipMalloc(%zu): %s", p->ws_bytes,
+                    hipGetErrorString(e));
+    }
+    layout(p, (char*)p->ws);
+    // split-K arrival counters start at zero; the kernel leaves them at zero
+    e = hipMemset(p->gv.cnt, 0, 4 * ((N + GEMV_ROWS - 1) / GEMV_ROWS));
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        (void)hipFree(p->ws);
+        delete p;
+        return fail(QMM_EHIP, "workspace init: %s", hipGetErrorString(e));
+    }
+    *out = p;
+    return QMM_OK;
+}
+
+extern "C" int qmatmul_destroy(qmm_plan* p)
+{
+    g_err[0] = 0;
+    if (!p) return QMM_OK;
+    hipError_t e = hipDeviceSynchronize();
+    hipError_t f = hipFree(p->ws);
+    delete p;
+    if (e != hipSuccess) return fail(QMM_EHIP, "hipDeviceSynchronize: %s", hipGetErrorString(e));
+    if (f != hipSuccess) return fail(QMM_EHIP, "hipFree: %s", hipGetErrorString(f));
+    return QMM_OK;
+}
+
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+static int check_run(const qmm_plan* p, const void* w, const float* x, const void* y, int64_t M)
+{
+    if (!p) return fail(QMM_EINVAL, "plan is NULL");
+    if (M < 0 || M > p->M_max)
+        return fail(QMM_EINVAL, "M=%lld outside [0, M_max=%lld]", (long long)M, (long long)p->M_max);
+    if (M == 0) return QMM_OK;
+    if (!w || !x || !y) return fail(QMM_EINVAL, "null pointer: w=%p x=%p out=%p", w, (const void*)x, y);
+    if (!aligned(w, 16)) return fail(QMM_EINVAL, "w_blocks must be 16-byte aligned");
+    if (!aligned(x, 16)) return fail(QMM_EINVAL, "x must be 16-byte aligned");
+    if (!aligned(y, 4)) return fail(QMM_EINVAL, "output must be 4-byte aligned");
+    return QMM_OK;
+}
+
+static int run_impl(const qmm_plan* p, const void* w, const float* x, float* y, int32_t* sums, int64_t M,
+                    void* stream)
+{
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (M <= GEMV_MAX_M) {
+        e = launch_gemv_prep(p->fmt, p->mode, x, (int)M, p->K, p->gv, s);
+        if (e == hipSuccess) e = launch_gemv(p->fmt, p->mode, w, p->N, p->K, (int)M, p->geom, p->gv, y, sums, s);
+    } else {
+        e = launch_gemm_prep(p->fmt, p->mode, x, M, p->K, p->gm, s);
+        if (e == hipSuccess) e = launch_gemm(p->fmt, p->mode, w, p->N, p->K, M, p->gm, y, sums, s);
+    }
+    if (e != hipSuccess) return fail(QMM_EHIP, "kernel launch: %s", hipGetErrorString(e));
+    return QMM_OK;
+}
+
+extern "C" int qmatmul_run(const qmm_plan* p, const void* w, const float* x, float* y, int64_t M, void* stream)
+{
+    g_err[0] = 0;
+    int st = check_run(p, w, x, y, M);
+    if (st != QMM_OK || M == 0) return st;
+    return run_impl(p, w, x, y, nullptr, M, stream);
+}
+
+extern "C" int qmatmul_run_block_sums(const qmm_plan* p, const void* w, const float* x, int32_t* sums, int64_t M,
+                                      void* stream)
+{
+    g_err[0] = 0;
+    int st = check_run(p, w, x, sums, M);
+    if (st != QMM_OK || M == 0) return st;
+    if (p->mode != QMM_MODE_QACT) return fail(QMM_EUNSUPPORTED, "block sums exist only for quantized activations (mode 1)");
+    return run_impl(p, w, x, nullptr, sums, M, stream);
+}
+
+extern "C" int qmatmul_quantize_act(int act_format, const float* x, int64_t M, int64_t K, void* out, void* stream)
+{
+    g_err[0] = 0;
+    if (act_format != QMM_Q8_0 && act_format != QMM_Q8_K)
+        return fail(QMM_EUNSUPPORTED, "unsupported activation format %d (expected %d Q8_0 or %d Q8_K)", act_format,
+                    QMM_Q8_0, QMM_Q8_K);
+    if (M < 0 || K <= 0) return fail(QMM_EINVAL, "bad sizes M=%lld K=%lld", (long long)M, (long long)K);
+    if (K % block_values(act_format))
+        return fail(QMM_EBLOCK, "last dim %lld not divisible by block size %lld", (long long)K,
+                    (long long)block_values(act_format));
+    if (M == 0) return QMM_OK;
+    if (!x || !out) return fail(QMM_EINVAL, "null pointer");
+    if (!aligned(x, 16)) return fail(QMM_EINVAL, "x must be 16-byte aligned");
+    if (!aligned(out, 4)) return fail(QMM_EINVAL, "out_blocks must be 4-byte aligned");
+    hipError_t e = launch_quantize_act(act_format, x, M, K, out, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(QMM_EHIP, "kernel launch: %s", hipGetErrorString(e));
+    return QMM_OK;
+}
+
+extern "C" int qmatmul_quantize_weights(int format, const float* w, int64_t N, int64_t K, void* out, void* stream)
+{
+    g_err[0] = 0;
+    if (format != QMM_Q8_0 && format != QMM_Q4_K)
+        return fail(QMM_EUNSUPPORTED, "unsupported weight format %d", format);
+    if (N < 0 || K <= 0) return fail(QMM_EINVAL, "bad sizes N=%lld K=%lld", (long long)N, (long long)K);
+    if (K % block_values(format))
+        return fail(QMM_EBLOCK, "quantized tensor must have their last dim divisible by block size [%lld, %lld] %lld",
+                    (long long)N, (long long)K, (long long)block_values(format));
+    if (N == 0) return QMM_OK;
+    if (!w || !out) return fail(QMM_EINVAL, "null pointer");
+    if (!aligned(w, 16)) return fail(QMM_EINVAL, "w must be 16-byte aligned");
+    if (!aligned(out, 16)) return fail(QMM_EINVAL, "out_blocks must be 16-byte aligned");
+    hipError_t e = launch_quantize_weights(format, w, N, K, out, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(QMM_EHIP, "kernel launch: %s", hipGetErrorString(e));
+    return QMM_OK;
+}
+
+extern "C" const char* qmatmul_status_string(int status)
+{
+    switch (status) {
+    case QMM_OK: return "ok";
+    case QMM_EINVAL: return "invalid argument";
+    case QMM_EBLOCK: return "K is not a multiple of the block size";
+    case QMM_EUNSUPPORTED: return "unsupported format, mode or shape";
+    case QMM_ENOMEM: return "out of device memory";
+    case QMM_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+extern "C" const char* qmatmul_last_error(void) { return g_err; }
+
+extern "C" int qmatmul_version(void) { return 1; }

@@ -1,0 +1,87 @@
+// qmm_device.h -- device-side helpers shared by the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qmm_internal.h"
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+#define QMM_DEV __device__ __forceinline__
+
+QMM_DEV float f16lo(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xffffu)); }
+QMM_DEV float f16hi(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16)); }
+QMM_DEV uint16_t f16bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+QMM_DEV float f16round(float f) { return (float)(_Float16)f; }
+
+// Four signed int8 in a dword -> four exact f16 (two half2 dwords, in order).
+// f16 bit pattern 0x64XX is 1024 + XX; bias the byte by 128 first so that
+// 1024 + (q + 128) - 1152 = q exactly.
+QMM_DEV void i8x4_to_f16(uint32_t d, uint32_t& p01, uint32_t& p23)
+{
+    const uint32_t u = d ^ 0x80808080u;
+    uint32_t a = __builtin_amdgcn_perm(0x64646464u, u, 0x05010400u);
+    uint32_t b = __builtin_amdgcn_perm(0x64646464u, u, 0x07030602u);
+    const half2_t bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+    p01 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, a) + bias);
+    p23 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, b) + bias);
+}
+
+// Eight 4-bit values selected by `shift` (0: low nibbles, 4: high nibbles) of
+// the bytes of (d0, d1) -> eight exact f16, element order [0,2,1,3,4,6,5,7].
+QMM_DEV half8_t nib8_to_f16(uint32_t d0, uint32_t d1, int shift)
+{
+    const half2_t bias = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+    uint32_t s0 = d0 >> shift, s1 = d1 >> shift;
+    uint32_t w0 = (s0 & 0x000f000fu) | 0x64006400u;
+    uint32_t w1 = ((s0 >> 8) & 0x000f000fu) | 0x64006400u;
+    uint32_t w2 = (s1 & 0x000f000fu) | 0x64006400u;
+    uint32_t w3 = ((s1 >> 8) & 0x000f000fu) | 0x64006400u;
+    half2_t h0 = __builtin_bit_cast(half2_t, w0) + bias;
+    half2_t h1 = __builtin_bit_cast(half2_t, w1) + bias;
+    half2_t h2 = __builtin_bit_cast(half2_t, w2) + bias;
+    half2_t h3 = __builtin_bit_cast(half2_t, w3) + bias;
+    half8_t r;
+    r[0] = h0[0]; r[1] = h0[1]; r[2] = h1[0]; r[3] = h1[1];
+    r[4] = h2[0]; r[5] = h2[1]; r[6] = h3[0]; r[7] = h3[1];
+    return r;
+}
+
+// Within-8 element permutation produced by nib8_to_f16: register slot e holds
+// element nib_perm(e) of {0,2,1,3,4,6,5,7} (the permutation is its own inverse).
+QMM_DEV int nib_perm(int e) { return (e & 4) | ((e & 1) << 1) | ((e & 2) >> 1); }
+
+// Q4_K: 6-bit scale and min of sub-block j from the 12 packed bytes held in
+// three dwords s0 (bytes 0-3), s1 (4-7), s2 (8-11).
+QMM_DEV void q4k_scale_min(uint32_t s0, uint32_t s1, uint32_t s2, int j, int& sc, int& mn)
+{
+    if (j < 4) {
+        sc = (s0 >> (8 * j)) & 63;
+        mn = (s1 >> (8 * j)) & 63;
+    } else {
+        const int jj = j - 4;
+        const uint32_t b8 = (s2 >> (8 * jj)) & 0xffu;
+        sc = (int)(b8 & 0x0fu) | (int)(((s0 >> (8 * jj + 6)) & 3u) << 4);
+        mn = (int)(b8 >> 4) | (int)(((s1 >> (8 * jj + 6)) & 3u) << 4);
+    }
+}
+
+// Q8_0 GEMV block-pair k permutation.  Inside a 4-byte-aligned pair of
+// blocks (68 bytes), lane group g (0..3) of the MFMA operand takes the 8
+// weight bytes at dwords (1+2g, 2+2g) of the even block; group 3 takes dword
+// 7 and the four bytes q0, q1, q30, q31.  The odd block's weights are
+// dword-aligned and go in natural order.  Returns the weight index (0..31)
+// held in slot t (0..7) of group g.
+QMM_DEV int q8_even_k(int g, int t)
+{
+    if (g < 3) return 2 + 8 * g + t;
+    if (t < 4) return 26 + t;
+    const int tail[4] = {0, 1, 30, 31};
+    return tail[t - 4];
+}

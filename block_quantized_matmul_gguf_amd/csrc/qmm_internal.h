@@ -1,0 +1,65 @@
+// qmm_internal.h -- interface between the host plan/dispatch code and the
+// kernel launchers.  Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmm {
+
+enum { FMT_Q8_0 = 8, FMT_Q4_K = 12, FMT_Q8_K = 15 };
+enum { MODE_A = 0, MODE_B = 1 };
+
+// Decode (GEMV) path: M <= 8 rows, 64 output rows per 256-thread workgroup
+// (four waves of 16), K split into ranges of at most 1024 values.
+constexpr int GEMV_MAX_M = 8;
+constexpr int GEMV_ROWS = 64;
+constexpr int GEMV_KRANGE = 1024;
+constexpr int GEMV_STAGE_BYTES = 9792;  // per-wave weight staging buffer (16 rows)
+
+// Prefill (GEMM) path tile.
+constexpr int GEMM_BM = 128;
+constexpr int GEMM_BN = 128;
+constexpr int GEMM_KS = 64;
+
+struct GemvGeom {
+    int units;        // weight blocks per row (Q8_0: 32 values, Q4_K: 256)
+    int unit_bytes;   // 34 or 144
+    int64_t row_bytes;
+    int ks;           // number of K ranges (grid.y)
+    int ups;          // units per K range
+    int full_rows;    // 1: stage whole rows (the 16-row tile is contiguous)
+    int su;           // units per stage when staging row segments
+};
+
+// Device buffers of the decode path inside a plan's workspace.
+struct GemvBufs {
+    void* img;     // activation operand image
+    float* sc0;    // mode a: 1/row scale [8]; mode b: act block scales [units][8]
+    void* sc1;     // mode a Q4_K: scaled sub-block sums [K/32][8] f32; mode b Q4_K: bsum pairs [units][8][8] i32
+    float* part;   // split-K partials [ks][8][N]
+    int* cnt;      // split-K arrival counters [ceil(N/64)]
+};
+
+// Device buffers of the prefill path.
+struct GemmBufs {
+    _Float16* a0;  // mode a: hi part [M][K]; mode b: quantized activations as f16 [M][K]
+    _Float16* a1;  // mode a: lo part [M][K]
+    float* sc0;    // mode a: 1/row scale [M]; mode b: act block scales [M][K/32 or K/256]
+    void* sc1;     // mode a Q4_K: scaled sub-block sums [M][K/32] f32; mode b Q4_K: bsum pairs [M][K/32] i32
+};
+
+GemvGeom gemv_geom(int fmt, int64_t K);
+bool gemv_supported(int fmt, int64_t K);
+
+hipError_t launch_quantize_act(int act_fmt, const float* x, int64_t M, int64_t K, void* out, hipStream_t s);
+hipError_t launch_quantize_weights(int fmt, const float* w, int64_t N, int64_t K, void* out, hipStream_t s);
+
+hipError_t launch_gemv_prep(int fmt, int mode, const float* x, int M, int64_t K, const GemvBufs& b, hipStream_t s);
+hipError_t launch_gemv(int fmt, int mode, const void* w, int64_t N, int64_t K, int M, const GemvGeom& g,
+                       const GemvBufs& b, float* y, int32_t* sums, hipStream_t s);
+
+hipError_t launch_gemm_prep(int fmt, int mode, const float* x, int64_t M, int64_t K, const GemmBufs& b, hipStream_t s);
+hipError_t launch_gemm(int fmt, int mode, const void* w, int64_t N, int64_t K, int64_t M, const GemmBufs& b,
+                       float* y, int32_t* sums, hipStream_t s);
+
+}  // namespace qmm

@@ -1,0 +1,133 @@
+/*
+ * qmatmul.h -- C ABI of the MI355X (gfx950) GGUF quantized matmul library.
+ *
+ * Computes y[M x N] = x[M x K] . W[N x K]^T where W is stored as GGUF
+ * quantized blocks exactly as a GGUF file stores a weight tensor: N rows, each
+ * row K/QK consecutive blocks cut along K (page "自己量化", section
+ * "2. q、k 投影的行重排": blocks run along a row).  x and y are f32, row-major,
+ * contiguous.  y is overwritten.
+ *
+ * Two numerical modes, the two forms the page "同一个 GGUF，CPU 和 Metal
+ * 生成的文字不一样" (section 出处) contrasts:
+ *   QMM_MODE_F32ACT (a)  activations stay f32; weight blocks are dequantized
+ *                        inside the kernel (the Metal form).  Accurate to f32.
+ *   QMM_MODE_QACT   (b)  each activation row is first quantized on its own
+ *                        (Q8_0 for Q8_0 weights, Q8K for Q4_K weights, per 32 or
+ *                        256 values), then integer block dot products are
+ *                        scaled by the weight and activation block scales (the
+ *                        CPU form).
+ *
+ * Block formats (little-endian; byte sizes fixed by the page "自己量化",
+ * sections 和下载的 Q8_0 逐字节比 and 大小和误差):
+ *   QMM_Q8_0   34 B per 32 values: f16 d, int8 q[32].
+ *   QMM_Q4_K  144 B per 256 values: f16 d, f16 dmin, 12 B packed 6-bit
+ *             sub-block scales and mins, 128 B of 4-bit values.
+ *   QMM_Q8_K  292 B per 256 values (activations only): f32 d, int8 q[256],
+ *             int16 bsums[16].
+ *
+ * Pointers named "device" must be device memory of the current HIP device
+ * (e.g. torch tensor data pointers); `stream` is a hipStream_t (NULL = the
+ * null stream).  Every call that takes a stream is asynchronous: it enqueues
+ * kernels and returns without synchronizing.  No call throws or aborts; each
+ * returns a status code, and qmatmul_last_error() gives a message for the
+ * calling thread.  Argument checks happen on the host before any HIP call.
+ */
+#ifndef QMATMUL_H
+#define QMATMUL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* formats: the GGUF (ggml) type ids */
+#define QMM_Q8_0 8
+#define QMM_Q4_K 12
+#define QMM_Q8_K 15
+
+/* modes */
+#define QMM_MODE_F32ACT 0
+#define QMM_MODE_QACT 1
+
+/* status codes */
+#define QMM_OK 0
+#define QMM_EINVAL 1       /* null pointer, non-positive size, M > M_max, misaligned pointer */
+#define QMM_EBLOCK 2       /* K not a multiple of the format's block size */
+#define QMM_EUNSUPPORTED 3 /* unknown format or mode, or a format/mode pairing not offered */
+#define QMM_ENOMEM 4       /* device allocation failed */
+#define QMM_EHIP 5         /* a HIP runtime call or kernel launch failed */
+
+typedef struct qmm_plan qmm_plan;
+
+/*
+ * Create a plan for one weight shape: format, N output rows, K inputs, up to
+ * M_max activation rows per run, and a mode.  The mode is fixed here, as the
+ * pages' QMatMul fixes its form when it is built (page "同一个 GGUF，CPU 和
+ * Metal 生成的文字不一样", section 修法).  K must be a multiple of 32 (Q8_0)
+ * or 256 (Q4_K), the shape check of page "自己量化", section "3. 量化".
+ * Allocates the plan's device workspace on the current device (hipMalloc).
+ * On success *out receives the plan; on failure *out is set to NULL.
+ */
+int qmatmul_create(qmm_plan** out, int format, int64_t N, int64_t K, int64_t M_max, int mode);
+
+/*
+ * Run y = x . W^T on `stream`.  w_blocks: device, N * qmatmul_row_bytes(format, K)
+ * bytes, 16-byte aligned.  x: device f32 [M x K].  y: device f32 [M x N],
+ * overwritten.  0 <= M <= M_max; M == 0 enqueues nothing.  M <= 8 takes the
+ * decode (GEMV) kernels, larger M the prefill (GEMM) kernels.  The caller owns
+ * w, x and y; the plan keeps no pointer after the call.  The plan's workspace
+ * is shared by its runs: do not run one plan concurrently on two streams.
+ */
+int qmatmul_run(const qmm_plan* plan, const void* w_blocks, const float* x, float* y,
+                int64_t M, void* stream);
+
+/* Free a plan and its workspace (NULL is a no-op).  Synchronizes the device
+ * before freeing, so pending runs of the plan finish first. */
+int qmatmul_destroy(qmm_plan* plan);
+
+/*
+ * Quantize activation rows the way mode (b) does, writing canonical blocks:
+ * act_format QMM_Q8_0 (34 B per 32) or QMM_Q8_K (292 B per 256).  Row-local:
+ * each row depends only on itself (page "自己量化", section 动脑筋答案).
+ * x: device f32 [M x K]; out_blocks: device, M * qmatmul_row_bytes(act_format, K)
+ * bytes.  Bit-identical to the quantization inside qmatmul_run.
+ */
+int qmatmul_quantize_act(int act_format, const float* x, int64_t M, int64_t K,
+                         void* out_blocks, void* stream);
+
+/*
+ * Quantize f32 weights [N x K] (device) into GGUF blocks (device, N *
+ * qmatmul_row_bytes(format, K) bytes), the role of QTensor::quantize on the
+ * page "自己量化" (section "3. 量化").  Q8_0: d = max|w|/127, q = round(w/d).
+ * Q4_K: per 32-value sub-block an affine min/max fit, 6-bit scales and mins
+ * against the super-block maximum / 63, 4-bit values re-quantized against the
+ * stored f16 scales (no importance matrix).
+ */
+int qmatmul_quantize_weights(int format, const float* w, int64_t N, int64_t K,
+                             void* out_blocks, void* stream);
+
+/*
+ * Test hook (mode (b) plans only): the integer parts of the run, from the
+ * same kernels.  sums: device int32 [M x N x qmatmul_block_sums_per_row(format, K)].
+ * Q8_0: S[m][n][b] = sum over block b of qw*qx.  Q4_K: per super-block i ten
+ * values S_0..S_7 (per 32), sumi = sum_j sc_j*S_j, summins = sum_j m_j*(bsums[2j]+bsums[2j+1]).
+ * Same preconditions as qmatmul_run; y is not written.
+ */
+int qmatmul_run_block_sums(const qmm_plan* plan, const void* w_blocks, const float* x,
+                           int32_t* sums, int64_t M, void* stream);
+
+/* Host-only helpers (no HIP calls; safe without a GPU). */
+int qmatmul_check(int format, int64_t N, int64_t K, int64_t M_max, int mode); /* what create validates */
+int64_t qmatmul_row_bytes(int format, int64_t K);           /* bytes of one row of blocks, -1 if invalid */
+int64_t qmatmul_block_sums_per_row(int format, int64_t K);  /* int32 entries per (m, n), -1 if invalid */
+int64_t qmatmul_workspace_bytes(int format, int64_t N, int64_t K, int64_t M_max, int mode); /* -1 if invalid */
+const char* qmatmul_status_string(int status);
+const char* qmatmul_last_error(void); /* message of the calling thread's last failure, "" if none */
+int qmatmul_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QMATMUL_H */

@@ -1,0 +1,118 @@
+"""The C-ABI library on the host (no GPU needed): it loads, exports every
+symbol include/qmatmul.h declares, and rejects bad arguments with the right
+status code before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_quantized_matmul_gguf_amd as qmm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qmatmul.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qmatmul_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_expected_entry_points():
+    names = declared_functions()
+    for must in ("qmatmul_create", "qmatmul_run", "qmatmul_destroy", "qmatmul_quantize_act",
+                 "qmatmul_run_block_sums", "qmatmul_status_string", "qmatmul_last_error"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = qmm.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in qmm.SIGNATURES, f"binding lacks a signature for {name}"
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    consts = dict((k, int(v)) for k, v in re.findall(r"#define (QMM_\w+) (\d+)", text))
+    assert consts["QMM_Q8_0"] == qmm.Q8_0 == 8
+    assert consts["QMM_Q4_K"] == qmm.Q4_K == 12
+    assert consts["QMM_Q8_K"] == qmm.Q8_K == 15
+    assert consts["QMM_MODE_F32ACT"] == qmm.MODE_F32ACT
+    assert consts["QMM_MODE_QACT"] == qmm.MODE_QACT
+    for name, v in (("QMM_OK", qmm.OK), ("QMM_EINVAL", qmm.EINVAL), ("QMM_EBLOCK", qmm.EBLOCK),
+                    ("QMM_EUNSUPPORTED", qmm.EUNSUPPORTED), ("QMM_ENOMEM", qmm.ENOMEM), ("QMM_EHIP", qmm.EHIP)):
+        assert consts[name] == v
+
+
+def test_row_bytes_and_block_sums_sizes():
+    assert qmm.row_bytes(qmm.Q8_0, 576) == 612
+    assert qmm.row_bytes(qmm.Q4_K, 1536) == 864
+    assert qmm.row_bytes(qmm.Q8_K, 4096) == 16 * 292
+    assert qmm.row_bytes(qmm.Q4_K, 576) == -1
+    assert qmm.row_bytes(99, 576) == -1
+    assert qmm.block_sums_per_row(qmm.Q8_0, 576) == 18
+    assert qmm.block_sums_per_row(qmm.Q4_K, 1536) == 60
+
+
+@pytest.mark.parametrize("args,status", [
+    ((qmm.Q4_K, 576, 576, 1, 0), qmm.EBLOCK),        # K-quants need K % 256 == 0
+    ((qmm.Q8_0, 576, 40, 1, 0), qmm.EBLOCK),
+    ((7, 576, 576, 1, 0), qmm.EUNSUPPORTED),          # unknown format
+    ((qmm.Q8_K, 576, 512, 1, 1), qmm.EUNSUPPORTED),   # activation-only format as weights
+    ((qmm.Q8_0, 576, 576, 1, 2), qmm.EUNSUPPORTED),   # unknown mode
+    ((qmm.Q8_0, 0, 576, 1, 0), qmm.EINVAL),
+    ((qmm.Q8_0, 576, 576, 0, 0), qmm.EINVAL),
+    ((qmm.Q8_0, -5, 576, 1, 0), qmm.EINVAL),
+    ((qmm.Q8_0, 576, 576, 307, 1), qmm.OK),
+    ((qmm.Q4_K, 14336, 4096, 512, 0), qmm.OK),
+])
+def test_check_status_codes(args, status):
+    assert qmm.check(*args) == status
+
+
+def test_shape_error_names_the_shape_and_block_size():
+    assert qmm.check(qmm.Q4_K, 576, 576, 1, 0) == qmm.EBLOCK
+    assert qmm.last_error() == "quantized tensor must have their last dim divisible by block size [576, 576] 256"
+
+
+def test_create_rejects_before_touching_the_gpu():
+    lib = qmm.lib()
+    h = ctypes.c_void_p(1234)
+    assert lib.qmatmul_create(ctypes.byref(h), qmm.Q4_K, 576, 576, 1, 0) == qmm.EBLOCK
+    assert h.value is None
+    assert lib.qmatmul_create(None, qmm.Q8_0, 576, 576, 1, 0) == qmm.EINVAL
+
+
+def test_run_rejects_null_plan_and_bad_m():
+    lib = qmm.lib()
+    assert lib.qmatmul_run(None, None, None, None, 1, None) == qmm.EINVAL
+    assert lib.qmatmul_run_block_sums(None, None, None, None, 1, None) == qmm.EINVAL
+    assert lib.qmatmul_destroy(None) == qmm.OK
+
+
+def test_quantize_entry_points_validate_on_host():
+    lib = qmm.lib()
+    assert lib.qmatmul_quantize_act(qmm.Q4_K, None, 1, 256, None, None) == qmm.EUNSUPPORTED
+    assert lib.qmatmul_quantize_act(qmm.Q8_K, None, 1, 300, None, None) == qmm.EBLOCK
+    assert lib.qmatmul_quantize_act(qmm.Q8_0, None, 0, 64, None, None) == qmm.OK   # M = 0: nothing to do
+    assert lib.qmatmul_quantize_act(qmm.Q8_0, None, 2, 64, None, None) == qmm.EINVAL
+    assert lib.qmatmul_quantize_act(qmm.Q8_0, ctypes.c_void_p(8), 2, 64, ctypes.c_void_p(64), None) == qmm.EINVAL
+    assert lib.qmatmul_quantize_weights(qmm.Q8_K, None, 1, 256, None, None) == qmm.EUNSUPPORTED
+    assert lib.qmatmul_quantize_weights(qmm.Q4_K, None, 1, 576, None, None) == qmm.EBLOCK
+
+
+def test_status_strings():
+    for s in range(6):
+        assert qmm.status_string(s)
+    assert qmm.status_string(99) == "unknown status"
+    assert qmm.lib().qmatmul_version() >= 1
+
+
+def test_workspace_sizes_are_modest():
+    # decode-only plans stay small; the prefill activation buffers scale with M_max * K
+    assert 0 < qmm.workspace_bytes(qmm.Q8_0, 49152, 576, 1, 0) < 8 << 20
+    big = qmm.workspace_bytes(qmm.Q4_K, 14336, 4096, 512, 0)
+    assert 4 * 512 * 4096 <= big < 64 << 20
+    assert qmm.workspace_bytes(qmm.Q4_K, 576, 576, 1, 0) == -1

@@ -1,0 +1,209 @@
+"""GPU parity: the HIP kernels, called through the C ABI, against the CPU
+oracle on the same seeded inputs.
+
+Bars: quantized activations, quantized weights and integer block sums are
+bit-exact; outputs satisfy |y - y_ref| <= 1e-5 * sum_k |w_k x_k| per element
+(x = the f32 activations in mode (a), the dequantized quantized activations in
+mode (b)), and y == 0 exactly where that sum is 0.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import block_quantized_matmul_gguf_amd as qmm  # noqa: E402
+
+TOL = 1e-5
+FMT_NAME = {qmm.Q8_0: "Q8_0", qmm.Q4_K: "Q4_K"}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    qmm.lib()  # fails loudly when the library is missing
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def assert_within(y, ref, absacc, what):
+    y = y.astype(np.float64)
+    err = np.abs(y - ref)
+    bound = TOL * absacc
+    bad = (err > bound) | ((absacc == 0) & (y != 0)) | ~np.isfinite(y)
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        rows = [f"(m={i},n={j}) y={y[i, j]!r} ref={ref[i, j]!r} err={err[i, j]:.3e} bound={bound[i, j]:.3e}"
+                for i, j in idx]
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside tolerance; " + "; ".join(rows))
+    return float((err / np.maximum(absacc, 1e-300)).max())
+
+
+def run_plan(fmt, mode, wq, n, k, x, m_max=None):
+    m = x.shape[0]
+    with qmm.Plan(fmt, n, k, m_max or max(m, 1), mode) as p:
+        return host(p.run(dev(wq), dev(x)))
+
+
+def ref(fmt, mode, wq, n, k, x):
+    return (oracle.matmul_a if mode == qmm.MODE_F32ACT else oracle.matmul_b)(fmt, wq, n, k, x)
+
+
+# --------------------------------------------------------- quantizers ----
+
+@pytest.mark.parametrize("m,k", [(1, 576), (3, 1536), (37, 1536), (8, 4096), (307, 576)])
+def test_quantize_act_q8_0_bit_exact(m, k):
+    x = synth.acts_f32(900 + m, m, k)
+    got = host(qmm.quantize_act(qmm.Q8_0, dev(x)))
+    assert np.array_equal(got, oracle.quantize(oracle.Q8_0, x))
+
+
+@pytest.mark.parametrize("m,k", [(1, 1536), (37, 1536), (8, 4096), (5, 256)])
+def test_quantize_act_q8k_bit_exact(m, k):
+    x = synth.acts_f32(910 + m, m, k)
+    got = host(qmm.quantize_act(qmm.Q8_K, dev(x)))
+    assert np.array_equal(got, oracle.quantize(oracle.Q8_K, x))
+
+
+def test_quantize_act_edge_blocks_bit_exact():
+    # zero blocks, ties at x*id = k + 1/2, a +-max tie on |x| (first index wins), subnormal scales
+    k = 512
+    x = np.zeros((4, k), np.float32)
+    x[1, :32] = np.arange(32) - 15.5          # d = 16.5/127: many values near ties
+    x[1, 32:64] = 2.5
+    x[1, 64] = 127.0
+    x[1, 65] = -2.5
+    x[2, 5], x[2, 9] = 2.0, -2.0               # Q8K sign tie: first index decides
+    x[2, 300], x[2, 301] = -3.0, 3.0
+    x[3] = synth.acts_f32(920, 1, k)[0] * 1e-6  # f16 d goes subnormal
+    for fmt in (qmm.Q8_0, qmm.Q8_K):
+        got = host(qmm.quantize_act(fmt, dev(x)))
+        assert np.array_equal(got, oracle.quantize(fmt, x)), FMT_NAME.get(fmt, "Q8K")
+
+
+@pytest.mark.parametrize("fmt,n,k", [(qmm.Q8_0, 96, 576), (qmm.Q4_K, 96, 1536), (qmm.Q4_K, 33, 4096)])
+def test_quantize_weights_bit_exact(fmt, n, k):
+    w = synth.weights_f32(930 + n, n, k)
+    got = host(qmm.quantize_weights(fmt, dev(w)))
+    assert np.array_equal(got, oracle.quantize(fmt, w))
+
+
+def test_activation_quantization_is_row_local_on_gpu():
+    x = synth.acts_f32(940, 37, 1536)
+    full = host(qmm.quantize_act(qmm.Q8_K, dev(x)))
+    one = host(qmm.quantize_act(qmm.Q8_K, dev(x[:1])))
+    assert np.array_equal(one[0], full[0])
+    perm = np.random.default_rng(941).permutation(37)
+    assert np.array_equal(host(qmm.quantize_act(qmm.Q8_K, dev(x[perm]))), full[perm])
+
+
+# ---------------------------------------------------- matmul parity ----
+
+SHAPES = [
+    (qmm.Q8_0, 576, 576),     # q_proj
+    (qmm.Q8_0, 200, 576),     # ragged N (not a multiple of 16 or 64)
+    (qmm.Q8_0, 192, 1536),    # split K, 48 blocks
+    (qmm.Q8_0, 130, 4096),    # split K x4
+    (qmm.Q4_K, 576, 1536),    # ffn_down
+    (qmm.Q4_K, 100, 4096),
+    (qmm.Q4_K, 70, 256),      # one super-block per row
+]
+
+
+@pytest.mark.parametrize("mode", [qmm.MODE_F32ACT, qmm.MODE_QACT], ids=["a", "b"])
+@pytest.mark.parametrize("fmt,n,k", SHAPES, ids=[f"{FMT_NAME[f]}-{n}x{k}" for f, n, k in SHAPES])
+@pytest.mark.parametrize("m", [1, 2, 5, 8, 9, 37, 130])
+def test_matmul_parity(fmt, n, k, mode, m):
+    wq = oracle.quantize(fmt, synth.weights_f32(1000 + n + k, n, k))
+    x = synth.acts_f32(2000 + m, m, k)
+    y = run_plan(fmt, mode, wq, n, k, x)
+    yr, a = ref(fmt, mode, wq, n, k, x)
+    assert_within(y, yr, a, f"{FMT_NAME[fmt]} {n}x{k} M={m} mode={mode}")
+
+
+@pytest.mark.parametrize("mode", [qmm.MODE_F32ACT, qmm.MODE_QACT], ids=["a", "b"])
+@pytest.mark.parametrize("fmt", [qmm.Q8_0, qmm.Q4_K], ids=["Q8_0", "Q4_K"])
+@pytest.mark.parametrize("m", [1, 8, 40])
+def test_integer_special_case_is_exact(fmt, mode, m):
+    # d = 1 weights (Q4_K: sc = m = 1, dmin = 1) and integer activations whose
+    # every block reaches +-127: both modes equal the integer matmul exactly.
+    n, k = 48, 512
+    g = np.random.default_rng(77)
+    if fmt == qmm.Q8_0:
+        q = g.integers(-127, 128, size=(n, k))
+        blk = np.zeros((n, k // 32, 34), np.uint8)
+        blk[..., 0:2] = [0x00, 0x3C]
+        blk[..., 2:] = q.reshape(n, k // 32, 32).astype(np.int8).view(np.uint8)
+        wint = q
+        x = synth.integer_acts(78, m, k, 32)
+    else:
+        q = g.integers(0, 16, size=(n, k))
+        blk = np.zeros((n, k // 256, 144), np.uint8)
+        blk[..., 0:2] = [0x00, 0x3C]
+        blk[..., 2:4] = [0x00, 0x3C]
+        blk[..., 4:12] = 1
+        blk[..., 12:16] = 0x11
+        for e in range(256):
+            c, l = divmod(e, 64)
+            blk[..., 16 + 32 * c + l % 32] |= (q.reshape(n, k // 256, 256)[..., e] << (0 if l < 32 else 4)).astype(np.uint8)
+        wint = q - 1
+        x = synth.integer_acts(78, m, k, 256)
+    exact = (x.astype(np.int64) @ wint.T).astype(np.float64)
+    y = run_plan(fmt, mode, blk, n, k, x)
+    assert np.array_equal(y.astype(np.float64), exact)
+
+
+@pytest.mark.parametrize("fmt,n,k", [(qmm.Q8_0, 200, 576), (qmm.Q8_0, 130, 4096), (qmm.Q4_K, 100, 1536)])
+@pytest.mark.parametrize("m", [1, 3, 8, 20])
+def test_block_sums_bit_exact(fmt, n, k, m):
+    wq = oracle.quantize(fmt, synth.weights_f32(3000 + n, n, k))
+    x = synth.acts_f32(3100 + m, m, k)
+    with qmm.Plan(fmt, n, k, m, qmm.MODE_QACT) as p:
+        got = host(p.block_sums(dev(wq), dev(x))).astype(np.int64)
+    want = oracle.block_sums(fmt, wq, n, k, x)
+    if fmt == qmm.Q4_K and m > qmm.GEMV_MAX_M:
+        # the prefill kernel folds the sub-block scales into its operands, so it
+        # yields sumi and summins per super-block but not the per-32 sums
+        got = got.reshape(m, n, -1, 10)[..., 8:]
+        want = want.reshape(m, n, -1, 10)[..., 8:]
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("fmt,mode,m", [(qmm.Q8_0, 0, 1), (qmm.Q8_0, 1, 8), (qmm.Q4_K, 0, 8),
+                                        (qmm.Q4_K, 1, 1), (qmm.Q8_0, 1, 37), (qmm.Q4_K, 0, 37)])
+def test_runs_are_deterministic_and_reuse_the_plan(fmt, mode, m):
+    n, k = 300, 4096
+    wq = dev(oracle.quantize(fmt, synth.weights_f32(4000, n, k)))
+    x = dev(synth.acts_f32(4001, m, k))
+    x2 = dev(synth.acts_f32(4002, m, k))
+    with qmm.Plan(fmt, n, k, 64, mode) as p:
+        y1 = host(p.run(wq, x))
+        p.run(wq, x2)
+        y2 = host(p.run(wq, x))
+    assert np.array_equal(y1, y2)
+
+
+def test_m_zero_is_a_no_op():
+    with qmm.Plan(qmm.Q8_0, 64, 576, 4, 0) as p:
+        y = torch.full((0, 64), 7.0, device="cuda")
+        p.run(dev(oracle.quantize(oracle.Q8_0, synth.weights_f32(5, 64, 576))), torch.empty((0, 576), device="cuda"), y)
+    torch.cuda.synchronize()
+
+
+def test_run_rejects_m_above_plan_maximum():
+    with qmm.Plan(qmm.Q8_0, 64, 576, 4, 0) as p:
+        wq = dev(oracle.quantize(oracle.Q8_0, synth.weights_f32(6, 64, 576)))
+        with pytest.raises(qmm.QmmError) as e:
+            p.run(wq, dev(synth.acts_f32(7, 5, 576)))
+        assert e.value.status == qmm.EINVAL
