@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Benchmark of the GGUF quantized matmul hot path on one MI355X.
+
+Workload (one "step" = one pass of the whole path over one batch): the
+HBM-resident scale-up, 8 stacked layers of W 14336x4096 (N(0,0.02), seeded),
+each quantized to Q8_0 and to Q4_K (~499 MB and ~264 MB of blocks), activations
+x 512x4096 N(0,1).  Per step, for both formats and both modes (a: f32
+activations, b: quantized activations):
+  * decode: M = 1 and M = 8 (the GEMV kernel), rotating over the 8 layers;
+  * prefill: M = 512 (the GEMM kernel), rotating over the 8 layers.
+
+value = effective weight GB/s of the decode phase (weight bytes streamed /
+decode time), the headline metric's first part; the prefill TOPS (useful
+2*M*N*K per second) is reported beside it.  Every timing comes from HIP events
+recorded on the stream the kernels run on, with inputs resident in HBM.
+
+CPU baseline: the CPU oracle (plain C, f64/int64) timed on the decode phase
+of the same step (M = 1 and 8, both formats and modes, all 8 layers) on the
+host's threads, reported in the same unit.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "quantized GEMV effective weight GB/s (% of 8 TB/s) + prefill GEMM TOPS (% MFMA peak)"
+PEAK_HBM_GBS = 8000.0
+PEAK_F16_TFLOPS = 2500.0
+PEAK_I8_TOPS = 5000.0
+N, K, LAYERS, M_PREFILL = 14336, 4096, 8, 512
+DECODE_M = (1, 8)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-layers", type=int, default=LAYERS, help="layers in the CPU-baseline sample")
+    p.add_argument("--only", default="", help="restrict the step to one part, e.g. gemv:q8_0:b:1 or gemm:q4_k:a "
+                                              "(for profiling one kernel)")
+    return p.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_quantized_matmul_gguf_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(key):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if data.get("source_hash") != kernel_source_hash():
+        return None
+    entry = data.get("kernels", {}).get(key)
+    return None if entry is None else entry.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(layers):
+    """The oracle on the decode phase of the step (M = 1 and 8, both formats,
+    both modes) over the first `layers` layers, all host threads."""
+    import oracle
+    import synth
+
+    want = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    threads = oracle.set_threads(min(want, os.cpu_count() or 1))
+    x = synth.acts_f32(5100, M_PREFILL, K)
+    total_bytes, total_s = 0, 0.0
+    for layer in range(layers):
+        w = synth.weights_f32(5000 + layer, N, K)
+        for fmt in (oracle.Q8_0, oracle.Q4_K):
+            wq = oracle.quantize(fmt, w)
+            for fn in (oracle.matmul_a, oracle.matmul_b):
+                for m in DECODE_M:
+                    t0 = time.perf_counter()
+                    fn(fmt, wq, N, K, x[:m])
+                    total_s += time.perf_counter() - t0
+                    total_bytes += wq.nbytes
+    return {
+        "value": round(total_bytes / total_s / 1e9, 3),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"decode phase of the step on {layers} of {LAYERS} layers: M=1 and M=8, Q8_0 and Q4_K, "
+                  f"modes a and b, N=14336 K=4096; {total_bytes / 1e9:.2f} GB of weight blocks in {total_s:.1f} s",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards over N across GPUs by design but no multi-GPU run is built)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_quantized_matmul_gguf_amd as qmm
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    fmts = {"q8_0": qmm.Q8_0, "q4_k": qmm.Q4_K}
+    modes = {"a": qmm.MODE_F32ACT, "b": qmm.MODE_QACT}
+
+    # ---- inputs: quantized on the GPU by the library's weight quantizer ----
+    t_setup = time.perf_counter()
+    wq = {f: [] for f in fmts}
+    for layer in range(LAYERS):
+        wf = torch.from_numpy(synth.weights_f32(5000 + layer, N, K)).to(dev)
+        for f, code in fmts.items():
+            wq[f].append(qmm.quantize_weights(code, wf))
+        del wf
+    x = torch.from_numpy(synth.acts_f32(5100, M_PREFILL, K)).to(dev)
+    xs = {m: x[:m].contiguous() for m in DECODE_M + (M_PREFILL,)}
+    ys = {m: torch.empty((m, N), dtype=torch.float32, device=dev) for m in DECODE_M + (M_PREFILL,)}
+    plans = {(f, md): qmm.Plan(code, N, K, M_PREFILL, mcode) for f, code in fmts.items() for md, mcode in modes.items()}
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+    layer_bytes = {f: wq[f][0].numel() for f in fmts}
+
+    groups = []  # (kind, fmt, mode, M)
+    for f in fmts:
+        for md in modes:
+            for m in DECODE_M:
+                groups.append(("gemv", f, md, m))
+    for f in fmts:
+        for md in modes:
+            groups.append(("gemm", f, md, M_PREFILL))
+    if args.only:
+        parts = args.only.split(":")
+        groups = [g for g in groups if all(str(v) == p for v, p in zip(g, parts))]
+        assert groups, f"--only {args.only} matches nothing"
+
+    def run_group(g):
+        kind, f, md, m = g
+        p = plans[(f, md)]
+        for layer in range(LAYERS):
+            p.run(wq[f][layer], xs[m], ys[m], stream)
+
+    def step(evs=None):
+        for i, g in enumerate(groups):
+            if evs is not None:
+                evs[i][0].record(stream)
+            run_group(g)
+            if evs is not None:
+                evs[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in groups]
+           for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for s in range(args.steps):
+        step(evs[s])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+
+    group_ms = [sum(evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)) / args.steps
+                for i in range(len(groups))]
+    detail = []
+    gemv_ms = gemv_bytes = gemm_ms = gemm_flops = 0.0
+    for g, ms in zip(groups, group_ms):
+        kind, f, md, m = g
+        us = ms * 1000.0 / LAYERS
+        row = {"kernel": kind, "fmt": f, "mode": md, "M": m, "us_per_launch": round(us, 3)}
+        if kind == "gemv":
+            b = layer_bytes[f]
+            row["weight_GBps"] = round(b / (us * 1e-6) / 1e9, 1)
+            row["frac_hbm"] = round(row["weight_GBps"] / PEAK_HBM_GBS, 4)
+            gemv_ms += ms
+            gemv_bytes += b * LAYERS
+        else:
+            fl = 2.0 * m * N * K
+            row["TOPS"] = round(fl / (us * 1e-6) / 1e12, 1)
+            row["frac_f16_peak"] = round(row["TOPS"] / PEAK_F16_TFLOPS, 4)
+            row["frac_int8_peak"] = round(row["TOPS"] / PEAK_I8_TOPS, 4)
+            gemm_ms += ms
+            gemm_flops += fl * LAYERS
+        detail.append(row)
+
+    def pick(kind, f, md, m):
+        for g, r in zip(groups, detail):
+            if g == (kind, f, md, m):
+                return r
+        return None
+
+    out = {
+        "metric": METRIC,
+        "value": round(gemv_bytes / (gemv_ms * 1e-3) / 1e9, 1) if gemv_ms else None,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8/f16 MFMA, f32 accumulate",
+        "data": "synthetic",
+        "config": {
+            "workload": "HBM-resident scale-up: 8 layers of 14336x4096 GGUF weights (Q8_0 499 MB, Q4_K 264 MB), "
+                        "modes a and b, decode M=1 and 8, prefill M=512, layers rotated",
+            "N": N, "K": K, "layers": LAYERS, "formats": list(fmts), "modes": list(modes),
+            "decode_M": list(DECODE_M), "prefill_M": M_PREFILL,
+            "only": args.only or None,
+        },
+    }
+    if gemm_ms:
+        out["prefill"] = {"TOPS": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 1),
+                          "frac_f16_peak": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4),
+                          "frac_int8_peak": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / PEAK_I8_TOPS, 4)}
+    # roofline of the decode kernel: Q8_0 weights, quantized activations, one token
+    r = pick("gemv", "q8_0", "b", 1) or (detail[0] if detail and detail[0]["kernel"] == "gemv" else None)
+    if r is not None:
+        b = layer_bytes[r["fmt"]]
+        out["roofline"] = {
+            "kernel": f"gemv_kernel {r['fmt']} mode {r['mode']} M={r['M']}",
+            "bound": "hbm", "achieved": r["weight_GBps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": r["frac_hbm"], "algorithmic_bytes_per_launch": b,
+            "traffic": traffic_from_profile(f"gemv:{r['fmt']}:{r['mode']}:{r['M']}"),
+        }
+    rg = pick("gemm", "q8_0", "a", M_PREFILL) or next((d for d in detail if d["kernel"] == "gemm"), None)
+    if rg is not None:
+        out["roofline_gemm"] = {
+            "kernel": f"gemm_kernel {rg['fmt']} mode {rg['mode']} M={rg['M']}",
+            "bound": "mfma", "achieved": rg["TOPS"], "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+            "frac": rg["frac_f16_peak"], "algorithmic_flops_per_launch": 2 * rg["M"] * N * K,
+            "traffic": traffic_from_profile(f"gemm:{rg['fmt']}:{rg['mode']}:{rg['M']}"),
+        }
+    out["detail"] = detail
+    out["wall_s_timed"] = round(wall_s, 3)
+    out["setup_s"] = round(setup_s, 1)
+    out["weights_fit_infinity_cache_256MB"] = {f: layer_bytes[f] * LAYERS <= 256 * 2 ** 20 for f in fmts}
+    if not args.no_cpu_baseline and not args.only:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_layers)
+    for p in plans.values():
+        p.close()
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,112 @@
+// qmm_act.h -- activation arithmetic shared by every kernel that quantizes or
+// splits activations (the standalone quantizer, the prefill preparation and the
+// decode kernel's prologue), so all of them produce identical values.
+#pragma once
+#include "qmm_device.h"
+
+namespace qmm {
+
+// Q8_0 block of 32 values (page "自己量化", section 和下载的 Q8_0 逐字节比: the
+// scale is max|x|/127): d = amax/127 in f32, q = round-half-away(x * (1/d))
+// with the unrounded d, d stored as f16 (nearest even).
+QMM_DEV void q8_0_block(const float a[32], uint16_t& dbits, float& dval, int8_t q[32])
+{
+#pragma clang fp contract(off)
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+        const float t = fabsf(a[j]);
+        amax = t > amax ? t : amax;
+    }
+    const float d = amax / 127.0f;
+    const float id = d != 0.0f ? 1.0f / d : 0.0f;
+    dbits = f16bits(d);
+    dval = f16round(d);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) q[j] = (int8_t)(int)roundf(a[j] * id);
+}
+
+QMM_DEV void load32(const float* __restrict__ v, float a[32])
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float4 t = reinterpret_cast<const float4*>(v)[i];
+        a[4 * i] = t.x; a[4 * i + 1] = t.y; a[4 * i + 2] = t.z; a[4 * i + 3] = t.w;
+    }
+}
+
+// Q8K block of 256 values held by one wave, four per lane (elements
+// 4*lane..4*lane+3).  The signed element of largest |x| (first index on
+// ties) sets iscale = -127/max; q = min(127, round-half-away(iscale*x));
+// d = 1/iscale; an all-zero block gives d = 0, q = 0.  On return lanes
+// 4i..4i+3 hold bsums[i] in s16.
+QMM_DEV void q8k_wave(const float xs[4], int lane, float& d, int q[4], int& s16)
+{
+#pragma clang fp contract(off)
+    float best = -1.0f;
+    int bi = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const float a = fabsf(xs[u]);
+        if (a > best) { best = a; bi = 4 * lane + u; }
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float ob = __shfl_xor(best, off);
+        const int oi = __shfl_xor(bi, off);
+        if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
+    }
+    const int sel = bi & 3;
+    const float mine = sel == 0 ? xs[0] : sel == 1 ? xs[1] : sel == 2 ? xs[2] : xs[3];
+    const float mx = __shfl(mine, bi >> 2);
+    d = 0.0f;
+    q[0] = q[1] = q[2] = q[3] = 0;
+    if (best != 0.0f) {
+        const float iscale = -127.0f / mx;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int v = (int)roundf(iscale * xs[u]);
+            q[u] = v < 127 ? v : 127;
+        }
+        d = 1.0f / iscale;
+    }
+    int s = q[0] + q[1] + q[2] + q[3];
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    s16 = s;
+}
+
+// Mode (a) activation split.  A row (or a row's K range) is scaled by the
+// power of two s = 2^sexp that puts its max|x| in [2^14, 2^15) (exact), then
+// x*s = hi + lo + r with hi = f16(x*s), lo = f16(x*s - hi): |r| <= 2^-22|x*s|
+// while lo is a normal f16.  Weights enter the matrix cores as exact small
+// integers, so their products with hi and lo are exact.
+QMM_DEV int split_exp(float amax)
+{
+    if (amax == 0.0f) return 0;
+    const int e = 14 - ilogbf(amax);
+    return e > 126 ? 126 : e;
+}
+
+QMM_DEV float split_chunk(const float a[32], float s, _Float16 hi[32], _Float16 lo[32])
+{
+#pragma clang fp contract(off)
+    float acc = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+        const float xs = a[c] * s;
+        const _Float16 h = (_Float16)xs;
+        hi[c] = h;
+        lo[c] = (_Float16)(xs - (float)h);
+        acc += xs;
+    }
+    return acc;  // sum of x*s over the chunk (the Q4_K mins term needs it)
+}
+
+QMM_DEV uint32_t pack4(int a, int b, int c, int d)
+{
+    return (uint32_t)(uint8_t)a | ((uint32_t)(uint8_t)b << 8) | ((uint32_t)(uint8_t)c << 16) |
+           ((uint32_t)(uint8_t)d << 24);
+}
+
+}  // namespace qmm

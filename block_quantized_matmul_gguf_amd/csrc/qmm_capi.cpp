@@ -108,7 +108,6 @@ static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 static size_t layout(qmm_plan* p, char* base)
 {
     const int64_t K = p->K, N = p->N;
-    const int64_t mg = p->M_max < GEMV_MAX_M ? p->M_max : GEMV_MAX_M;
     const int64_t units = p->fmt == QMM_Q8_0 ? K / 32 : K / 256;
     const bool a = p->mode == QMM_MODE_F32ACT, q4 = p->fmt == QMM_Q4_K;
     size_t off = 0;
@@ -118,11 +117,7 @@ static size_t layout(qmm_plan* p, char* base)
         return r;
     };
     // decode path
-    p->gv.img = take(a ? 4 * mg * K : mg * K);
-    p->gv.sc0 = (float*)take(a ? 4 * GEMV_MAX_M : 4 * units * GEMV_MAX_M);
-    p->gv.sc1 = take(q4 ? (a ? 4 * (K / 32) * GEMV_MAX_M : 4 * units * 64) : 0);
     p->gv.part = (float*)take(p->geom.ks > 1 ? 4 * (size_t)p->geom.ks * GEMV_MAX_M * N : 0);
-    p->gv.cnt = (int*)take(4 * ((N + GEMV_ROWS - 1) / GEMV_ROWS));
     // prefill path
     if (p->M_max > GEMV_MAX_M) {
         const int64_t M = p->M_max;
@@ -177,14 +172,6 @@ extern "C" int qmatmul_create(qmm_plan** out, int format, int64_t N, int64_t K, 
                     hipGetErrorString(e));
     }
     layout(p, (char*)p->ws);
-    // split-K arrival counters start at zero; the kernel leaves them at zero
-    e = hipMemset(p->gv.cnt, 0, 4 * ((N + GEMV_ROWS - 1) / GEMV_ROWS));
-    if (e == hipSuccess) e = hipDeviceSynchronize();
-    if (e != hipSuccess) {
-        (void)hipFree(p->ws);
-        delete p;
-        return fail(QMM_EHIP, "workspace init: %s", hipGetErrorString(e));
-    }
     *out = p;
     return QMM_OK;
 }
@@ -222,8 +209,7 @@ static int run_impl(const qmm_plan* p, const void* w, const float* x, float* y, 
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
     if (M <= GEMV_MAX_M) {
-        e = launch_gemv_prep(p->fmt, p->mode, x, (int)M, p->K, p->gv, s);
-        if (e == hipSuccess) e = launch_gemv(p->fmt, p->mode, w, p->N, p->K, (int)M, p->geom, p->gv, y, sums, s);
+        e = launch_gemv(p->fmt, p->mode, w, x, p->N, p->K, (int)M, p->geom, p->gv, y, sums, s);
     } else {
         e = launch_gemm_prep(p->fmt, p->mode, x, M, p->K, p->gm, s);
         if (e == hipSuccess) e = launch_gemm(p->fmt, p->mode, w, p->N, p->K, M, p->gm, y, sums, s);

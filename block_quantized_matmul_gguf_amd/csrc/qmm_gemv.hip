@@ -8,7 +8,8 @@
 //   * each wave streams its 16 rows with coalesced 16-byte loads into a
 //     private LDS stage (prefetched one stage ahead in registers), then every
 //     lane reads the weight bytes of one row in the matrix-core operand layout;
-//   * the activation operand image of the K range is staged once into LDS;
+//   * each workgroup prepares the activation operand of its K range in LDS
+//     (mode a: f16 hi/lo split; mode b: Q8_0 / Q8K quantization of each row);
 //   * mode (a): v_mfma_f32_16x16x32_f16 with the weights as exact f16 integers
 //     (q for Q8_0, the 4-bit q for Q4_K) against activation rows 0..7 = f16 hi
 //     part and rows 8..15 = f16 lo part, block scales applied per block in f32;
@@ -16,9 +17,9 @@
 //     0..7 carry the first block, 8..15 the second, zero elsewhere), giving the
 //     int32 block sums; scaled in f32 (Q8_0: dw*dx*S; Q4_K: sub-block scales in
 //     int32, then dx*(d*sumi - dmin*summins));
-//   * split-K partials are combined in a fixed order by the last workgroup of
-//     a row tile to arrive, so results are deterministic.
-#include "qmm_device.h"
+//   * split-K partials go to a workspace and a small second kernel sums them
+//     in a fixed order (deterministic; no cross-workgroup fences).
+#include "qmm_act.h"
 
 namespace qmm {
 
@@ -29,11 +30,8 @@ struct GemvArgs {
     int64_t row_bytes;
     int N, K, M;
     int units, ups, full_rows, su, ks;
-    const uint8_t* img;
-    const float* sc0;
-    const void* sc1;
+    const float* x;
     float* part;
-    int* cnt;
     float* y;
     int32_t* sums;
 };
@@ -59,13 +57,12 @@ __global__ __launch_bounds__(256, 2) void gemv_kernel(GemvArgs a)
 {
     constexpr int UB = FMT == FMT_Q8_0 ? 34 : 144;
     // activation image bytes per weight unit (32-block or 256-super-block) and row M
-    constexpr int IMG_PER_UNIT_M = MODE == MODE_A ? (FMT == FMT_Q8_0 ? 128 : 1024) : (FMT == FMT_Q8_0 ? 32 : 256);
     constexpr int IMG_BYTES = MODE == MODE_A ? 32768 : 8192;
     __shared__ __align__(16) uint8_t s_img[IMG_BYTES];
     __shared__ __align__(16) float s_sc0[256];
     __shared__ __align__(16) int32_t s_sc1[256];
     __shared__ __align__(16) uint8_t s_stage[4][GEMV_STAGE_BYTES];
-    __shared__ int s_last;
+    __shared__ float s_scale[GEMV_MAX_M], s_inv[GEMV_MAX_M];
 
     const int M = a.M, N = a.N;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -75,20 +72,91 @@ __global__ __launch_bounds__(256, 2) void gemv_kernel(GemvArgs a)
     const int u_end = min(u_begin + a.ups, a.units);
     const int nu = u_end - u_begin;
 
-    // ---- stage the activation operand image and scales of this K range ----
+    // ---- build the activation operand of this K range in LDS ----
+    // Mode (a): f16 hi/lo split of x (power-of-two scale per row and K range),
+    // rows 0..M-1 hi and M..2M-1 lo, k in the weight decoder's order.
+    // Mode (b): each row quantized on its own per 32 (Q8_0) or 256 (Q8K) values,
+    // int8 image rows 0..M-1 first block of a pair, M..2M-1 second block.
     {
-        const int bytes = nu * IMG_PER_UNIT_M * M;
-        const uint4* src = reinterpret_cast<const uint4*>(a.img + (int64_t)u_begin * IMG_PER_UNIT_M * M);
-        for (int o = tid; o * 16 < bytes; o += 256) reinterpret_cast<uint4*>(s_img)[o] = src[o];
-        if (MODE == MODE_B) {
-            const int per = FMT == FMT_Q8_0 ? 8 : 8;  // scales [unit][8]
-            for (int o = tid; o < nu * per; o += 256) s_sc0[o] = a.sc0[(int64_t)u_begin * per + o];
-            if (FMT == FMT_Q4_K)
-                for (int o = tid; o < nu * 64; o += 256)
-                    s_sc1[o] = reinterpret_cast<const int32_t*>(a.sc1)[(int64_t)u_begin * 64 + o];
-        } else if (FMT == FMT_Q4_K) {
-            for (int o = tid; o < nu * 64; o += 256)
-                reinterpret_cast<float*>(s_sc1)[o] = reinterpret_cast<const float*>(a.sc1)[(int64_t)u_begin * 64 + o];
+        constexpr int QK = FMT == FMT_Q8_0 ? 32 : 256;
+        const float* xk = a.x + (int64_t)u_begin * QK;
+        if (MODE == MODE_A) {
+            const int n32 = nu * (QK / 32);
+            const bool have = tid < M * n32;  // one 32-value chunk per thread (<= 256)
+            const int cm = have ? tid / n32 : 0, cu = have ? tid - cm * n32 : 0;
+            float v[32];
+            if (have) {
+                load32(xk + (int64_t)cm * a.K + 32 * cu, v);
+                float am = 0.0f;
+#pragma unroll
+                for (int c = 0; c < 32; ++c) am = fmaxf(am, fabsf(v[c]));
+                s_sc0[tid] = am;
+            }
+            __syncthreads();
+            if (tid < M) {
+                float r = 0.0f;
+                for (int c = 0; c < n32; ++c) r = fmaxf(r, s_sc0[tid * n32 + c]);
+                const int e = split_exp(r);
+                s_scale[tid] = ldexpf(1.0f, e);
+                s_inv[tid] = ldexpf(1.0f, -e);
+            }
+            __syncthreads();
+            if (have) {
+                _Float16 hi[32], lo[32];
+                const float sum = split_chunk(v, s_scale[cm], hi, lo);
+                half8_t* img = reinterpret_cast<half8_t*>(s_img);
+#pragma unroll
+                for (int gg = 0; gg < 4; ++gg) {
+                    half8_t vh, vl;
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) {
+                        int k;
+                        if (FMT == FMT_Q8_0) k = (cu & 1) ? 8 * gg + t : q8_even_k(gg, t);
+                        else k = 8 * gg + nib_perm(t);
+                        vh[t] = hi[k];
+                        vl[t] = lo[k];
+                    }
+                    img[(cu * 4 + gg) * 2 * M + cm] = vh;
+                    img[(cu * 4 + gg) * 2 * M + M + cm] = vl;
+                }
+                if (FMT == FMT_Q4_K) reinterpret_cast<float*>(s_sc1)[cu * 8 + cm] = sum;
+            }
+        } else if (FMT == FMT_Q8_0) {
+            if (tid < M * nu) {  // one 32-value block per thread
+                const int cm = tid / nu, cu = tid - cm * nu;
+                float v[32];
+                load32(xk + (int64_t)cm * a.K + 32 * cu, v);
+                uint16_t dbits;
+                float dval;
+                int8_t q[32];
+                q8_0_block(v, dbits, dval, q);
+                const int odd = cu & 1, row = odd ? M + cm : cm;
+#pragma unroll
+                for (int gg = 0; gg < 4; ++gg) {
+                    int sv[8];
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) sv[t] = q[odd ? 8 * gg + t : q8_even_k(gg, t)];
+                    reinterpret_cast<uint2*>(s_img)[((cu >> 1) * 4 + gg) * 2 * M + row] =
+                        make_uint2(pack4(sv[0], sv[1], sv[2], sv[3]), pack4(sv[4], sv[5], sv[6], sv[7]));
+                }
+                s_sc0[cu * 8 + cm] = dval;
+            }
+        } else {
+            for (int b = wave; b < M * nu; b += 4) {  // one 256-value block per wave
+                const int cm = b / nu, cu = b - cm * nu;
+                const float4 xv = reinterpret_cast<const float4*>(xk + (int64_t)cm * a.K + 256 * cu)[lane];
+                const float xs[4] = {xv.x, xv.y, xv.z, xv.w};
+                float d;
+                int q[4], s16;
+                q8k_wave(xs, lane, d, q, s16);
+                const int e = 4 * lane, c = e >> 6, w = e & 63, hf = w >> 5, gg = (w & 31) >> 3, t0 = w & 7;
+                const int row = hf ? M + cm : cm;
+                *reinterpret_cast<uint32_t*>(s_img + ((((cu * 4 + c) * 4 + gg) * 2 * M + row) * 8 + t0)) =
+                    pack4(q[0], q[1], q[2], q[3]);
+                if (lane == 0) s_sc0[cu * 8 + cm] = d;
+                const int pair = s16 + __shfl_down(s16, 4);
+                if ((lane & 7) == 0) s_sc1[(cu * 8 + (lane >> 3)) * 8 + cm] = pair;
+            }
         }
     }
     __syncthreads();
@@ -322,34 +390,24 @@ __global__ __launch_bounds__(256, 2) void gemv_kernel(GemvArgs a)
             const int m = 4 * g + r;
             if (m < M) {
                 float v = acc[r];
-                if (MODE == MODE_A) v *= a.sc0[m];
+                if (MODE == MODE_A) v *= s_inv[m];
                 if (a.ks == 1) a.y[(int64_t)m * N + n] = v;
                 else a.part[((int64_t)split * GEMV_MAX_M + m) * N + n] = v;
             }
         }
     }
-    if (a.ks == 1) return;
+}
 
-    // ---- split-K: the last workgroup of this row tile sums the partials ----
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const int old = atomicAdd(&a.cnt[blockIdx.x], 1);
-        s_last = old == a.ks - 1;
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    for (int idx = tid; idx < M * GEMV_ROWS; idx += 256) {
-        const int m = idx / GEMV_ROWS;
-        const int nn = blockIdx.x * GEMV_ROWS + idx % GEMV_ROWS;
-        if (nn < N) {
-            float s = 0.0f;
-            for (int sp = 0; sp < a.ks; ++sp) s += __builtin_nontemporal_load(&a.part[((int64_t)sp * GEMV_MAX_M + m) * N + nn]);
-            a.y[(int64_t)m * N + nn] = s;
-        }
-    }
-    if (tid == 0) a.cnt[blockIdx.x] = 0;
+// Split-K: y[m][n] = sum over K ranges of the partials, in range order.
+__global__ __launch_bounds__(256) void gemv_reduce_kernel(const float* __restrict__ part, int ks, int M, int N,
+                                                          float* __restrict__ y)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)M * N) return;
+    const int m = (int)(i / N), n = (int)(i - (int64_t)m * N);
+    float s = 0.0f;
+    for (int sp = 0; sp < ks; ++sp) s += part[((int64_t)sp * GEMV_MAX_M + m) * N + n];
+    y[i] = s;
 }
 
 GemvGeom gemv_geom(int fmt, int64_t K)
@@ -395,8 +453,8 @@ static void launch_one(const GemvArgs& a, hipStream_t s)
     hipLaunchKernelGGL((gemv_kernel<FMT, MODE, EMIT>), grid, dim3(256), 0, s, a);
 }
 
-hipError_t launch_gemv(int fmt, int mode, const void* w, int64_t N, int64_t K, int M, const GemvGeom& g,
-                       const GemvBufs& b, float* y, int32_t* sums, hipStream_t s)
+hipError_t launch_gemv(int fmt, int mode, const void* w, const float* x, int64_t N, int64_t K, int M,
+                       const GemvGeom& g, const GemvBufs& b, float* y, int32_t* sums, hipStream_t s)
 {
     GemvArgs a{};
     a.w = (const uint8_t*)w;
@@ -409,11 +467,8 @@ hipError_t launch_gemv(int fmt, int mode, const void* w, int64_t N, int64_t K, i
     a.full_rows = g.full_rows;
     a.su = g.su;
     a.ks = g.ks;
-    a.img = (const uint8_t*)b.img;
-    a.sc0 = b.sc0;
-    a.sc1 = b.sc1;
+    a.x = x;
     a.part = b.part;
-    a.cnt = b.cnt;
     a.y = y;
     a.sums = sums;
     const bool emit = sums != nullptr;
@@ -425,6 +480,11 @@ hipError_t launch_gemv(int fmt, int mode, const void* w, int64_t N, int64_t K, i
         if (mode == MODE_A) launch_one<FMT_Q4_K, MODE_A, false>(a, s);
         else if (emit) launch_one<FMT_Q4_K, MODE_B, true>(a, s);
         else launch_one<FMT_Q4_K, MODE_B, false>(a, s);
+    }
+    if (!emit && g.ks > 1) {
+        const int64_t total = (int64_t)M * N;
+        hipLaunchKernelGGL(gemv_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, b.part, g.ks,
+                           M, (int)N, y);
     }
     return hipGetLastError();
 }

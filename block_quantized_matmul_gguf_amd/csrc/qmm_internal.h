@@ -33,11 +33,7 @@ struct GemvGeom {
 
 // Device buffers of the decode path inside a plan's workspace.
 struct GemvBufs {
-    void* img;     // activation operand image
-    float* sc0;    // mode a: 1/row scale [8]; mode b: act block scales [units][8]
-    void* sc1;     // mode a Q4_K: scaled sub-block sums [K/32][8] f32; mode b Q4_K: bsum pairs [units][8][8] i32
     float* part;   // split-K partials [ks][8][N]
-    int* cnt;      // split-K arrival counters [ceil(N/64)]
 };
 
 // Device buffers of the prefill path.
@@ -54,9 +50,8 @@ bool gemv_supported(int fmt, int64_t K);
 hipError_t launch_quantize_act(int act_fmt, const float* x, int64_t M, int64_t K, void* out, hipStream_t s);
 hipError_t launch_quantize_weights(int fmt, const float* w, int64_t N, int64_t K, void* out, hipStream_t s);
 
-hipError_t launch_gemv_prep(int fmt, int mode, const float* x, int M, int64_t K, const GemvBufs& b, hipStream_t s);
-hipError_t launch_gemv(int fmt, int mode, const void* w, int64_t N, int64_t K, int M, const GemvGeom& g,
-                       const GemvBufs& b, float* y, int32_t* sums, hipStream_t s);
+hipError_t launch_gemv(int fmt, int mode, const void* w, const float* x, int64_t N, int64_t K, int M,
+                       const GemvGeom& g, const GemvBufs& b, float* y, int32_t* sums, hipStream_t s);
 
 hipError_t launch_gemm_prep(int fmt, int mode, const float* x, int64_t M, int64_t K, const GemmBufs& b, hipStream_t s);
 hipError_t launch_gemm(int fmt, int mode, const void* w, int64_t N, int64_t K, int64_t M, const GemmBufs& b,
