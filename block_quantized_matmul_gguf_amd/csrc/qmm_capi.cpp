@@ -18,8 +18,6 @@ struct qmm_plan {
     int fmt, mode;
     int64_t N, K, M_max;
     int device;
-    GemvGeom geom;
-    bool gemv_fast, gemm_fast;
     void* ws;
     size_t ws_bytes;
     GemvBufs gv;
@@ -117,7 +115,8 @@ static size_t layout(qmm_plan* p, char* base)
         return r;
     };
     // decode path
-    p->gv.part = (float*)take(p->geom.ks > 1 ? 4 * (size_t)p->geom.ks * GEMV_MAX_M * N : 0);
+    const int splits = gemv_max_splits(p->fmt, K);
+    p->gv.part = (float*)take(splits > 1 ? 4 * (size_t)splits * GEMV_MAX_M * N : 0);
     // prefill path
     if (p->M_max > GEMV_MAX_M) {
         const int64_t M = p->M_max;
@@ -140,7 +139,6 @@ extern "C" int64_t qmatmul_workspace_bytes(int format, int64_t N, int64_t K, int
     p.N = N;
     p.K = K;
     p.M_max = M_max;
-    p.geom = gemv_geom(format, K);
     return (int64_t)layout(&p, nullptr);
 }
 
@@ -158,7 +156,6 @@ extern "C" int qmatmul_create(qmm_plan** out, int format, int64_t N, int64_t K, 
     p->N = N;
     p->K = K;
     p->M_max = M_max;
-    p->geom = gemv_geom(format, K);
     p->ws_bytes = layout(p, nullptr);
     hipError_t e = hipGetDevice(&p->device);
     if (e != hipSuccess) {
@@ -209,7 +206,7 @@ static int run_impl(const qmm_plan* p, const void* w, const float* x, float* y, 
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
     if (M <= GEMV_MAX_M) {
-        e = launch_gemv(p->fmt, p->mode, w, x, p->N, p->K, (int)M, p->geom, p->gv, y, sums, s);
+        e = launch_gemv(p->fmt, p->mode, w, x, p->N, p->K, (int)M, p->gv, y, sums, s);
     } else {
         e = launch_gemm_prep(p->fmt, p->mode, x, M, p->K, p->gm, s);
         if (e == hipSuccess) e = launch_gemm(p->fmt, p->mode, w, p->N, p->K, M, p->gm, y, sums, s);

@@ -9,11 +9,10 @@ namespace qmm {
 enum { FMT_Q8_0 = 8, FMT_Q4_K = 12, FMT_Q8_K = 15 };
 enum { MODE_A = 0, MODE_B = 1 };
 
-// Decode (GEMV) path: M <= 8 rows, 64 output rows per 256-thread workgroup
-// (four waves of 16), K split into ranges of at most 1024 values.
+// Decode (GEMV) path: M <= 8 rows; 256-thread workgroups of four waves, each
+// wave streaming 16-row tiles of one K split.
 constexpr int GEMV_MAX_M = 8;
-constexpr int GEMV_ROWS = 64;
-constexpr int GEMV_KRANGE = 1024;
+constexpr int GEMV_MAX_SPLITS = 16;
 constexpr int GEMV_STAGE_BYTES = 9792;  // per-wave weight staging buffer (16 rows)
 
 // Prefill (GEMM) path tile.
@@ -25,10 +24,13 @@ struct GemvGeom {
     int units;        // weight blocks per row (Q8_0: 32 values, Q4_K: 256)
     int unit_bytes;   // 34 or 144
     int64_t row_bytes;
-    int ks;           // number of K ranges (grid.y)
-    int ups;          // units per K range
+    int tiles;        // 16-row tiles
+    int ks;           // K splits
+    int ups;          // units per K split
     int full_rows;    // 1: stage whole rows (the 16-row tile is contiguous)
     int su;           // units per stage when staging row segments
+    int upw;          // tiles per wave
+    int grid;         // workgroups
 };
 
 // Device buffers of the decode path inside a plan's workspace.
@@ -44,14 +46,15 @@ struct GemmBufs {
     void* sc1;     // mode a Q4_K: scaled sub-block sums [M][K/32] f32; mode b Q4_K: bsum pairs [M][K/32] i32
 };
 
-GemvGeom gemv_geom(int fmt, int64_t K);
+GemvGeom gemv_geom(int fmt, int mode, int64_t N, int64_t K, int M, int max_wgs);
 bool gemv_supported(int fmt, int64_t K);
+int gemv_max_splits(int fmt, int64_t K);
 
 hipError_t launch_quantize_act(int act_fmt, const float* x, int64_t M, int64_t K, void* out, hipStream_t s);
 hipError_t launch_quantize_weights(int fmt, const float* w, int64_t N, int64_t K, void* out, hipStream_t s);
 
 hipError_t launch_gemv(int fmt, int mode, const void* w, const float* x, int64_t N, int64_t K, int M,
-                       const GemvGeom& g, const GemvBufs& b, float* y, int32_t* sums, hipStream_t s);
+                       const GemvBufs& b, float* y, int32_t* sums, hipStream_t s);
 
 hipError_t launch_gemm_prep(int fmt, int mode, const float* x, int64_t M, int64_t K, const GemmBufs& b, hipStream_t s);
 hipError_t launch_gemm(int fmt, int mode, const void* w, int64_t N, int64_t K, int64_t M, const GemmBufs& b,
