@@ -44,7 +44,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-layers", type=int, default=LAYERS, help="layers in the CPU-baseline sample")
     p.add_argument("--only", default="", help="restrict the step to one part, e.g. gemv:q8_0:b:1 or gemm:q4_k:a "
-                                              "(for profiling one kernel)")
+                                              "(for profiling one kernel); 'copy' times a plain 512 MiB device copy "
+                                              "instead (the calibration for the HBM byte counters)")
     return p.parse_args()
 
 
@@ -102,6 +103,27 @@ def cpu_baseline(layers):
     }
 
 
+def copy_calibration(torch, dev, stream, args):
+    """A plain elementwise copy of 512 MiB of f32 (read 512 MiB, write
+    512 MiB): the known-size kernel against which the FETCH_SIZE and WRITE_SIZE
+    counters are scaled, and the streaming ceiling of the device."""
+    nbytes = 512 * 2 ** 20
+    src = torch.randn(nbytes // 4, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        torch.neg(src, out=dst)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        torch.neg(src, out=dst)
+    end.record(stream)
+    torch.cuda.synchronize()
+    us = start.elapsed_time(end) * 1000.0 / args.steps
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "us_per_copy": round(us, 2),
+                      "GBps_read_plus_write": round(2 * nbytes / (us * 1e-6) / 1e9, 1)}))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -119,6 +141,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
+    if args.only == "copy":
+        copy_calibration(torch, dev, stream, args)
+        return
     fmts = {"q8_0": qmm.Q8_0, "q4_k": qmm.Q4_K}
     modes = {"a": qmm.MODE_F32ACT, "b": qmm.MODE_QACT}
 
