@@ -86,11 +86,9 @@ static int check_shape(int format, int64_t N, int64_t K, int64_t M_max, int mode
     if (N > (1ll << 30) || K > (1ll << 20) || M_max > (1ll << 24) || N * (K / qk) * block_bytes(format) > (1ll << 40))
         return fail(QMM_EINVAL, "shape too large: N=%lld K=%lld M_max=%lld", (long long)N, (long long)K,
                     (long long)M_max);
-    const bool gemv_ok = gemv_supported(format, K);
-    const bool gemm_ok = format == QMM_Q4_K || (K / 32) % 2 == 0;
-    if (!gemv_ok || !gemm_ok)
-        return fail(QMM_EUNSUPPORTED, "K=%lld has no kernel for this format yet (Q8_0 needs K/32 even and K<=576 or K/32 a multiple of 8)",
-                    (long long)K);
+    if (!gemv_supported(format, K))
+        return fail(QMM_EUNSUPPORTED, "K=%lld has no kernel for this format (Q8_0 needs K divisible by 64: the "
+                    "kernels read blocks in pairs)", (long long)K);
     return QMM_OK;
 }
 

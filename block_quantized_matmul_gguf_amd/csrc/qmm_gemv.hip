@@ -3,458 +3,546 @@
 // The weight stream is the cost (the pages' CPU decode step is dominated by
 // it: page "同一个 GGUF，CPU 和 Metal 生成的文字不一样", section 修法, 7 ms
 // Q8_0 vs 15 ms dequantized f32).  Layout of the work:
-//   * the weight matrix is cut into units of 16 rows x one K split; the grid
-//     is sized so every workgroup is resident at once, and each wave owns a
-//     contiguous run of units, streaming them stage by stage with two stages
-//     of 16-byte coalesced loads in flight (across unit boundaries), through a
-//     private LDS stage from which every lane reads one row's bytes in the
-//     matrix-core operand layout;
-//   * all four waves of a workgroup share one K split, whose activation
-//     operand the workgroup prepares once in LDS (mode a: f16 hi/lo split;
-//     mode b: Q8_0 / Q8K quantization of each row);
+//   * a wave owns 16 weight rows (one matrix-core tile) and one slice of K,
+//     streamed in stages of P load units (Q8_0 block pairs or Q4_K
+//     super-blocks).  A stage is read row by row in 16-byte chunks, so four
+//     consecutive lanes always read 64 consecutive bytes of one row (loads
+//     whose lane quads span several rows run at half the rate), two stages in
+//     flight;
+//   * each stage lands in a small per-wave LDS buffer, from which every lane
+//     gathers its matrix-core operand (lane l: row l%16, k-group l/16);
+//   * the activation operand is built once per workgroup, in LDS, in operand
+//     order; lanes whose operand rows are structurally zero (the two-block
+//     trick below, or activation rows >= M) mask their 16 bytes to zero;
+//   * the eight waves of a workgroup split each tile's K range among
+//     themselves (kw waves per tile) and sum their partials through LDS once at
+//     the end, so no second kernel is needed unless the activation operand
+//     exceeds LDS (then K is also split across workgroups and a small kernel
+//     adds the partials in a fixed order);
 //   * mode (a): v_mfma_f32_16x16x32_f16 with the weights as exact f16 integers
 //     (q for Q8_0, the 4-bit q for Q4_K) against activation rows 0..7 = f16 hi
-//     part and rows 8..15 = f16 lo part, block scales applied per block in f32;
-//   * mode (b): v_mfma_i32_16x16x64_i8 over two 32-value blocks at once (A rows
-//     0..7 carry the first block, 8..15 the second, zero elsewhere), giving the
-//     int32 block sums; scaled in f32 (Q8_0: dw*dx*S; Q4_K: sub-block scales in
-//     int32, then dx*(d*sumi - dmin*summins));
-//   * with several K splits, partials go to a workspace and a small second
-//     kernel sums them in a fixed order (deterministic; no cross-workgroup
-//     fences).
+//     part and rows 8..15 = f16 lo part of x*2^e;
+//   * mode (b): v_mfma_i32_16x16x64_i8 over two 32-value (sub-)blocks at once
+//     (A rows 0..7 carry the first, 8..15 the second, zeros elsewhere), giving
+//     the int32 block sums; scaled in f32 (Q8_0: dw*dx*S; Q4_K: sub-block
+//     scales in int32, then dx*(d*sumi - dmin*summins)).
 #include <algorithm>
+#include <map>
 #include <mutex>
+#include <utility>
 
 #include "qmm_act.h"
 
 namespace qmm {
 
-#ifndef QMM_NT_WEIGHTS
-#define QMM_NT_WEIGHTS 1
-#endif
+constexpr int GV_WAVES = 8;
+constexpr int GV_THREADS = 64 * GV_WAVES;
+constexpr int GV_XMAX = 64 * GV_THREADS;  // activation values one workgroup prepares (64 per thread)
+constexpr int GV_GPW_MAX = 4;             // tile groups per workgroup
+constexpr int GV_RED = 128;               // floats per (tile, slice) partial: 8 rows x 16 columns
+constexpr int GV_MISC_BYTES = 128;
+constexpr int GV_LDS_MAX = 160 * 1024;
 
-constexpr int MAXP = 10;          // 16-byte staging pieces per lane and stage
-constexpr int IMG_BYTES = 32768;  // activation operand of one K split
-constexpr int SC_WORDS = 1024;    // per-split activation scales / sums
-constexpr int MAX_RANGE = 4096;   // K values per split
+// Per format and mode: bytes per load unit and row (a Q8_0 block pair or a
+// Q4_K super-block), matrix-core steps per load unit, activation values per
+// unit; per activation-row slot count MS (1 when M == 1, else 8): image
+// bytes per matrix-core step and scale bytes per load unit.
+template <int FMT, int MODE, int MS>
+struct GvFmt {
+    static constexpr int LUB = FMT == FMT_Q8_0 ? 68 : 144;
+    static constexpr int OPS = FMT == FMT_Q8_0 ? (MODE == MODE_A ? 2 : 1) : (MODE == MODE_A ? 8 : 4);
+    static constexpr int VPL = FMT == FMT_Q8_0 ? 64 : 256;
+    static constexpr int OPB = (MODE == MODE_A ? 128 : 64) * MS;
+    static constexpr int SCB = FMT == FMT_Q8_0 ? (MODE == MODE_A ? 0 : 8 * MS) : (MODE == MODE_A ? 64 * MS : 36 * MS);
+};
+
+static void gv_fmt(int fmt, int mode, int ms, int& lub, int& ops, int& vpl, int& opb, int& scb)
+{
+    lub = fmt == FMT_Q8_0 ? 68 : 144;
+    ops = fmt == FMT_Q8_0 ? (mode == MODE_A ? 2 : 1) : (mode == MODE_A ? 8 : 4);
+    vpl = fmt == FMT_Q8_0 ? 64 : 256;
+    opb = (mode == MODE_A ? 128 : 64) * ms;
+    scb = fmt == FMT_Q8_0 ? (mode == MODE_A ? 0 : 8 * ms) : (mode == MODE_A ? 64 * ms : 36 * ms);
+}
+
+// 16-byte chunks per row in a stage of P load units (the last may run past
+// the stage: those bytes are read but not used).
+constexpr int gv_cpr(int fmt, int P) { return fmt == FMT_Q8_0 ? (68 * P + 15) / 16 : 9 * P; }
+// LDS row stride of the stage buffer: an odd number of 16-byte units, so the
+// 16 rows a wave gathers from start in different banks.
+constexpr int gv_rs(int fmt, int P) { return 16 * (gv_cpr(fmt, P) | 1); }
 
 struct GemvArgs {
     const uint8_t* w;
-    int64_t row_bytes;
+    int64_t w_bytes;  // N * row_bytes
+    int row_bytes;
     int N, K, M;
-    int units;      // weight units (32-blocks or 256-super-blocks) per row
-    int ups;        // units per K split
-    int ks;         // K splits
-    int full_rows;  // 1: a stage is whole rows (ks == 1; the 16-row tile is contiguous)
-    int su;         // units per stage otherwise
-    int upw;        // row tiles per wave
-    int tiles;      // ceil(N / 16)
+    int nlu;          // load units per row
+    int lus_split;    // load units per K split
+    int ks;           // K splits (across workgroups)
+    int kw;           // waves per tile (K slices inside the workgroup)
+    int slice;        // load units per wave slice (a multiple of the stage size)
+    int G;            // tiles per workgroup step (GV_WAVES / kw)
+    int groups;       // tile groups per split
+    int gpw;          // tile groups per workgroup
+    int sc_off, red_off, misc_off, stg_off;  // LDS byte offsets
     const float* x;
     float* part;
     float* y;
     int32_t* sums;
 };
 
-#define WAVE_SYNC()                                 \
-    do {                                            \
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);    \
-        __builtin_amdgcn_wave_barrier();            \
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);    \
-    } while (0)
-
-// Weight stream loads: a raw buffer descriptor per (tile, stage) whose record
-// count ends at the last real row, so rows past N read as zeros (the range
-// check is per dword and whole-row stages end on a dword boundary); non-
-// temporal, since every weight byte is used once per run.  Every load path is
-// branch-free, so the in-order load counter waits are exact.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 QMM_DEV rsrc_t make_rsrc(const void* base, uint32_t bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
-QMM_DEV float4 load_x16(rsrc_t r, uint32_t off)
+QMM_DEV u32x4_t ld128(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0); }
+QMM_DEV float4 ldx16(rsrc_t r, uint32_t off)
 {
-    const f32x4_t v = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    const f32x4_t v = __builtin_bit_cast(f32x4_t, ld128(r, off));
     return make_float4(v[0], v[1], v[2], v[3]);
 }
-QMM_DEV uint4 load_w16(rsrc_t r, uint32_t off)
+
+// Eight int8 (two dwords) -> eight exact f16 in order.
+QMM_DEV half8_t i8x8_to_f16(uint32_t d0, uint32_t d1)
 {
-    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, QMM_NT_WEIGHTS ? 2 : 0);
-    return make_uint4(v[0], v[1], v[2], v[3]);
+    uint32_t a0, a1, b0, b1;
+    i8x4_to_f16(d0, a0, a1);
+    i8x4_to_f16(d1, b0, b1);
+    return __builtin_bit_cast(half8_t, u32x4_t{a0, a1, b0, b1});
 }
 
-template <int FMT, int MODE, bool EMIT>
-__global__ __launch_bounds__(256, 2) void gemv_kernel(GemvArgs a)
+QMM_DEV void st16(uint8_t* p, uint32_t a, uint32_t b, uint32_t c, uint32_t d)
 {
-    constexpr int UB = FMT == FMT_Q8_0 ? 34 : 144;
-    constexpr int QK = FMT == FMT_Q8_0 ? 32 : 256;
-    // LDS sized per mode: the f16 hi/lo operand is 4 bytes per value and row,
-    // the int8 one 1; scales [unit][8], Q4_K sums [sub-block or unit][8(x8)]
-    constexpr int IMG = MODE == MODE_A ? IMG_BYTES : IMG_BYTES / 4;
-    constexpr int SC0 = MODE == MODE_A ? 256 : (FMT == FMT_Q8_0 ? SC_WORDS : 128);
-    constexpr int SC1 = FMT == FMT_Q4_K ? SC_WORDS : 4;
-    __shared__ __align__(16) uint8_t s_img[IMG];
-    __shared__ __align__(16) float s_sc0[SC0];
-    __shared__ __align__(16) int32_t s_sc1[SC1];
-    __shared__ __align__(16) uint8_t s_stage[4][GEMV_STAGE_BYTES];
-    __shared__ float s_scale[GEMV_MAX_M], s_inv[GEMV_MAX_M];
+    *reinterpret_cast<u32x4_t*>(p) = u32x4_t{a, b, c, d};
+}
+QMM_DEV uint32_t lds32(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+QMM_DEV u32x2_t lds64(const uint8_t* p) { return *reinterpret_cast<const u32x2_t*>(p); }
+QMM_DEV u32x4_t lds128(const uint8_t* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 
-    const int M = a.M, N = a.N;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int j = lane & 15, g = lane >> 4;
-    const int split = blockIdx.x % a.ks;
-    const int u_begin = split * a.ups;
-    const int nu = min(u_begin + a.ups, a.units) - u_begin;
+// R: activation rows per lane the arithmetic covers (1 when M == 1, else 4:
+// lane l holds output rows 4*(l/16 % 2) + r of its tile column l%16).
+template <int FMT, int MODE, int P, int R, bool EMIT>
+__global__ __launch_bounds__(GV_THREADS, 1) void gemv_kernel(GemvArgs a)
+{
+    constexpr int MS = R == 1 ? 1 : 8;
+    using F = GvFmt<FMT, MODE, MS>;
+    constexpr int LUB = F::LUB, OPS = F::OPS, VPL = F::VPL, OPB = F::OPB, SCB = F::SCB;
+    constexpr int CPR = gv_cpr(FMT, P), RS = gv_rs(FMT, P);
+    constexpr int T = (16 * CPR + 63) / 64;  // load instructions per stage
+    extern __shared__ __align__(16) uint8_t lds[];
+    uint8_t* s_img = lds;
+    float* s_scf = reinterpret_cast<float*>(lds + a.sc_off);
+    int32_t* s_sci = reinterpret_cast<int32_t*>(lds + a.sc_off);
+    float* s_red = reinterpret_cast<float*>(lds + a.red_off);
+    float* s_misc = reinterpret_cast<float*>(lds + a.misc_off);  // mode a: [0,8) 2^e, [8,16) 2^-e, [16,24) amax
 
-    // ---- this wave's units: row tiles t0 .. t0+ntile-1 of split `split` ----
-    const int wv = __builtin_amdgcn_readfirstlane(wave);
-    const int t0 = ((blockIdx.x / a.ks) * 4 + wv) * a.upw;
-    const int ntile = max(0, min(a.upw, a.tiles - t0));
-    const int nstages = a.full_rows ? 1 : nu / a.su;  // su divides the split
-    const int nq = ntile * nstages;                    // stages this wave streams
-    const int SB = a.full_rows ? (int)a.row_bytes : a.su * UB;  // bytes per row and stage
-    uint8_t* stg = s_stage[wave];
-    uint4 pfA[MAXP], pfB[MAXP];
+    const int M = a.M, N = a.N, K = a.K;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 15, g = lane >> 4;
+    const int split = blockIdx.x % a.ks, wgi = blockIdx.x / a.ks;
+    const int lu_beg = split * a.lus_split;
+    const int lu_cnt = min(a.lus_split, a.nlu - lu_beg);  // real load units of this split
+    const int tg = wave / a.kw, sl = wave - tg * a.kw;
+    const int grp0 = wgi * a.gpw;
+    const int ngrp = min(a.gpw, a.groups - grp0);
+    const int sl_lu0 = sl * a.slice;                          // first unit of this wave's slice
+    const int sl_real = max(0, min(a.slice, lu_cnt - sl_lu0));
+    const int S = (sl_real + P - 1) / P;                      // stages per tile
+    const int Q = ngrp * S;                                   // stages this wave streams
+    uint8_t* stg = lds + a.stg_off + wave * (16 * RS);
 
-    // ---- x of this K split, loaded before the weight stream is queued ----
-    // (loads retire in order: issued first, they are not stuck behind the weights)
-    const rsrc_t xr = make_rsrc(a.x, (uint32_t)((int64_t)M * a.K * 4));
-    const uint32_t xbase = (uint32_t)u_begin * QK * 4;
-    float xv[32];
-    int xc = -1;   // chunk of 32 values this thread prepares (mode a, Q8_0 mode b)
-    float4 xq[8];  // Q8K: this lane's 4 values of up to 8 blocks of 256
-    if (MODE == MODE_A || FMT == FMT_Q8_0) {
-        const int n32 = nu * (QK / 32);
-        const int cm = tid / n32, cu = tid - cm * n32;
-        xc = tid < M * n32 ? tid : -1;
-        const uint32_t off = xc >= 0 ? xbase + (uint32_t)(cm * a.K + 32 * cu) * 4 : 0x7ffffff0u;
+    // ---- x of this K split: loaded before the weight stream is queued ----
+    const rsrc_t xr = make_rsrc(a.x, (uint32_t)(M * K * 4));
+    const int k0 = lu_beg * VPL;
+    constexpr bool CHUNKS = MODE == MODE_A || FMT == FMT_Q8_0;  // 32-value chunks, one per thread and pass
+    const int nb32 = lu_cnt * (VPL / 32);
+    float xv[2][32];
+    float4 xq[16];
+    if constexpr (CHUNKS) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float4 t = load_x16(xr, off + 16 * i);
-            xv[4 * i] = t.x; xv[4 * i + 1] = t.y; xv[4 * i + 2] = t.z; xv[4 * i + 3] = t.w;
+        for (int c = 0; c < 2; ++c) {
+            const int t = tid + GV_THREADS * c;
+            const int m = t / nb32, b = t - m * nb32;
+            const uint32_t off = t < M * nb32 ? (uint32_t)(m * K + k0 + 32 * b) * 4 : 0x80000000u;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float4 v = ldx16(xr, off + 16 * i);
+                xv[c][4 * i] = v.x; xv[c][4 * i + 1] = v.y; xv[c][4 * i + 2] = v.z; xv[c][4 * i + 3] = v.w;
+            }
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int b = wave + 4 * i;
-            const int cm = b / nu, cu = b - cm * nu;
-            const uint32_t off = b < M * nu ? xbase + (uint32_t)(cm * a.K + 256 * cu + 4 * lane) * 4 : 0x7ffffff0u;
-            xq[i] = load_x16(xr, off);
+        for (int c = 0; c < 16; ++c) {  // Q8K: one 256-value block per wave and pass, 4 values per lane
+            const int t = wave + GV_WAVES * c;
+            const int m = t / lu_cnt, b = t - m * lu_cnt;
+            const uint32_t off = t < M * lu_cnt ? (uint32_t)(m * K + k0 + 256 * b + 4 * lane) * 4 : 0x80000000u;
+            xq[c] = ldx16(xr, off);
         }
     }
 
-    // ---- the weight stream: per-lane piece offsets, the same for every stage ----
-    uint32_t voff[MAXP];
-    {
-        const int PR = SB >> 4;
-        const uint32_t mg = (65536u + PR - 1) / PR;
+    // ---- the weight stream: chunk f = 64t + lane of a stage is row f/CPR, chunk f%CPR ----
+    uint32_t go[T], lw[T];
 #pragma unroll
-        for (int i = 0; i < MAXP; ++i) {
-            const int p = lane + 64 * i;
-            const int r = a.full_rows ? 0 : (int)(((uint32_t)p * mg) >> 16);
-            const uint32_t off = a.full_rows ? 16u * p : (uint32_t)(r * a.row_bytes + 16 * (p - r * PR));
-            voff[i] = p < SB ? off : 0x7ffffff0u;
-        }
+    for (int t = 0; t < T; ++t) {
+        const int f = 64 * t + lane, r = f / CPR, c = f - r * CPR;
+        go[t] = f < 16 * CPR ? (uint32_t)(r * a.row_bytes + 16 * c) : 0x80000000u;
+        lw[t] = (uint32_t)(r * RS + 16 * c);
     }
-    auto issue = [&](uint4 (&pf)[MAXP], int q) {  // stage q, or zeros past the last one
-        const bool real = q < nq;
-        const int qq = real ? q : 0;
-        const int t = t0 + qq / nstages, s = qq - (qq / nstages) * nstages;
-        const int n0 = 16 * t, rows = max(0, min(16, N - n0));
-        const int64_t col = a.full_rows ? 0 : (int64_t)(u_begin + s * a.su) * UB;
-        const uint8_t* base = a.w + (int64_t)n0 * a.row_bytes + col;
-        const uint32_t nrec = real ? (uint32_t)((int64_t)rows * a.row_bytes - col) : 0u;
-        const rsrc_t rs = make_rsrc(real ? base : a.w, nrec);
+    constexpr int TAIL = 16 * CPR - 64 * (T - 1);  // live lanes of the last load
+
+    int iq = 0, iu = 0, is = 0;  // next stage to queue: index, tile, stage within the tile
+    auto issue = [&](u32x4_t (&r)[T]) {
+        const bool real = iq < Q;
+        const int tile = (grp0 + iu) * a.G + tg;
+        const int64_t t0 = (int64_t)tile * 16 * a.row_bytes;
+        const int64_t left = a.w_bytes - t0;
+        const uint32_t nrec = real && left > 0 ? (uint32_t)min(left, (int64_t)16 * a.row_bytes) : 0u;
+        const rsrc_t wr = make_rsrc(a.w + (real ? t0 : 0), nrec);
+        const uint32_t so = (uint32_t)((lu_beg + sl_lu0 + is * P) * LUB);
+        ++iq;
+        if (++is == S) { is = 0; ++iu; }
 #pragma unroll
-        for (int i = 0; i < MAXP; ++i) pf[i] = load_w16(rs, voff[i]);
+        for (int t = 0; t < T; ++t) r[t] = ld128(wr, go[t] + so);
     };
-    issue(pfA, 0);
-    issue(pfB, 1);
+    u32x4_t rA[T], rB[T];
+    issue(rA);
+    issue(rB);
 
     // ---- the activation operand of this K split, once per workgroup ----
-    // Mode (a): f16 hi/lo split of x (power-of-two scale per row and K split),
-    // image rows 0..M-1 hi and M..2M-1 lo, k in the weight decoder's order.
-    // Mode (b): each row quantized on its own per 32 (Q8_0) or 256 (Q8K) values,
-    // int8 image rows 0..M-1 first block of a pair, M..2M-1 second block.
-    if (MODE == MODE_A) {
-        const int n32 = nu * (QK / 32);
-        if (xc >= 0) {
-            float am = 0.0f;
+    {
+        // zero what the slices may read past the split's last unit, and the partials
+        const u32x4_t z = {0u, 0u, 0u, 0u};
+        const int lu_img = a.kw * a.slice;
+        for (int i = lu_cnt * OPS * OPB / 16 + tid; i < lu_img * OPS * OPB / 16; i += GV_THREADS)
+            reinterpret_cast<u32x4_t*>(s_img)[i] = z;
+        if constexpr (SCB > 0)
+            for (int i = lu_cnt * SCB / 4 + tid; i < lu_img * SCB / 4; i += GV_THREADS) s_sci[i] = 0;
+        for (int i = tid; i < (a.misc_off - a.red_off) / 16; i += GV_THREADS)
+            reinterpret_cast<u32x4_t*>(s_red)[i] = z;
+        if (tid < GV_MISC_BYTES / 4) s_misc[tid] = 0.0f;
+    }
+    __syncthreads();
+    if constexpr (MODE == MODE_A) {
+        // power-of-two scale per row (over this split), then hi/lo f16 split
 #pragma unroll
-            for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(xv[i]));
-            s_sc0[xc] = am;
+        for (int c = 0; c < 2; ++c) {
+            const int t = tid + GV_THREADS * c;
+            if (t < M * nb32) {
+                float am = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(xv[c][i]));
+                atomicMax(reinterpret_cast<unsigned*>(&s_misc[16 + t / nb32]), __float_as_uint(am));
+            }
         }
         __syncthreads();
-        if (tid < M) {
-            float r = 0.0f;
-            for (int c = 0; c < n32; ++c) r = fmaxf(r, s_sc0[tid * n32 + c]);
-            const int e = split_exp(r);
-            s_scale[tid] = ldexpf(1.0f, e);
-            s_inv[tid] = ldexpf(1.0f, -e);
+        if (tid < GEMV_MAX_M) {
+            const int e = split_exp(__uint_as_float(reinterpret_cast<unsigned*>(s_misc)[16 + tid]));
+            s_misc[tid] = ldexpf(1.0f, e);
+            s_misc[8 + tid] = ldexpf(1.0f, -e);
         }
         __syncthreads();
-        if (xc >= 0) {
-            const int cm = xc / n32, cu = xc - cm * n32;
-            _Float16 hi[32], lo[32];
-            const float sum = split_chunk(xv, s_scale[cm], hi, lo);
-            half8_t* img = reinterpret_cast<half8_t*>(s_img);
 #pragma unroll
-            for (int gg = 0; gg < 4; ++gg) {
-                half8_t vh, vl;
+        for (int c = 0; c < 2; ++c) {
+            const int t = tid + GV_THREADS * c;
+            if (t < M * nb32) {
+                const int m = t / nb32, b = t - m * nb32;  // b: matrix-core step (32 values) in this split
+                _Float16 hi[32], lo[32];
+                const float sum = split_chunk(xv[c], s_misc[m], hi, lo);
+                uint8_t* op = s_img + b * OPB;
 #pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    int k;
-                    if (FMT == FMT_Q8_0) k = (cu & 1) ? 8 * gg + t : q8_even_k(gg, t);
-                    else k = 8 * gg + nib_perm(t);
-                    vh[t] = hi[k];
-                    vl[t] = lo[k];
+                for (int kg = 0; kg < 4; ++kg) {
+                    half8_t vh, vl;
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        int k;
+                        if constexpr (FMT == FMT_Q8_0) {
+                            // even block of a pair: groups 0..2 take q[2+8kg ..], group 3 takes
+                            // q26..q31, q0, q1 (the weight side's dword layout); odd block: natural
+                            if (b & 1) k = 8 * kg + u;
+                            else k = kg < 3 ? 2 + 8 * kg + u : (u < 6 ? 26 + u : u - 6);
+                        } else {
+                            k = 8 * kg + nib_perm(u);
+                        }
+                        vh[u] = hi[k];
+                        vl[u] = lo[k];
+                    }
+                    *reinterpret_cast<half8_t*>(op + ((kg * 2) * MS + m) * 16) = vh;
+                    *reinterpret_cast<half8_t*>(op + ((kg * 2 + 1) * MS + m) * 16) = vl;
                 }
-                img[(cu * 4 + gg) * 2 * M + cm] = vh;
-                img[(cu * 4 + gg) * 2 * M + M + cm] = vl;
+                if constexpr (FMT == FMT_Q4_K) {  // mins term: sum of x*2^e (hi rows; lo rows stay 0)
+                    s_scf[b * 2 * MS + m] = sum;
+                    s_scf[b * 2 * MS + MS + m] = 0.0f;
+                }
             }
-            if (FMT == FMT_Q4_K) reinterpret_cast<float*>(s_sc1)[cu * 8 + cm] = sum;
         }
-    } else if (FMT == FMT_Q8_0) {
-        if (xc >= 0) {  // one 32-value block per thread
-            const int cm = xc / nu, cu = xc - cm * nu;
-            uint16_t dbits;
-            float dval;
-            int8_t q[32];
-            q8_0_block(xv, dbits, dval, q);
-            const int odd = cu & 1, row = odd ? M + cm : cm;
+    } else if constexpr (FMT == FMT_Q8_0) {
 #pragma unroll
-            for (int gg = 0; gg < 4; ++gg) {
-                int sv[8];
-#pragma unroll
-                for (int t = 0; t < 8; ++t) sv[t] = q[odd ? 8 * gg + t : q8_even_k(gg, t)];
-                reinterpret_cast<uint2*>(s_img)[((cu >> 1) * 4 + gg) * 2 * M + row] =
-                    make_uint2(pack4(sv[0], sv[1], sv[2], sv[3]), pack4(sv[4], sv[5], sv[6], sv[7]));
+        for (int c = 0; c < 2; ++c) {
+            const int t = tid + GV_THREADS * c;
+            if (t < M * nb32) {
+                const int m = t / nb32, b = t - m * nb32;
+                uint16_t dbits;
+                float dval;
+                int8_t q[32];
+                q8_0_block(xv[c], dbits, dval, q);
+                uint8_t* op = s_img + (b >> 1) * OPB;
+                if (!(b & 1)) {  // k-groups 0, 1 of rows 0..7: q2..q17 | q18..q31, q0, q1
+                    st16(op + m * 16, pack4(q[2], q[3], q[4], q[5]), pack4(q[6], q[7], q[8], q[9]),
+                         pack4(q[10], q[11], q[12], q[13]), pack4(q[14], q[15], q[16], q[17]));
+                    st16(op + (MS + m) * 16, pack4(q[18], q[19], q[20], q[21]), pack4(q[22], q[23], q[24], q[25]),
+                         pack4(q[26], q[27], q[28], q[29]), pack4(q[30], q[31], q[0], q[1]));
+                } else {  // k-groups 2, 3 of rows 8..15: q0..q15 | q16..q31
+                    st16(op + (2 * MS + m) * 16, pack4(q[0], q[1], q[2], q[3]), pack4(q[4], q[5], q[6], q[7]),
+                         pack4(q[8], q[9], q[10], q[11]), pack4(q[12], q[13], q[14], q[15]));
+                    st16(op + (3 * MS + m) * 16, pack4(q[16], q[17], q[18], q[19]), pack4(q[20], q[21], q[22], q[23]),
+                         pack4(q[24], q[25], q[26], q[27]), pack4(q[28], q[29], q[30], q[31]));
+                }
+                s_scf[(b >> 1) * 2 * MS + (b & 1) * MS + m] = dval;
             }
-            s_sc0[cu * 8 + cm] = dval;
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {  // one 256-value block per wave and step
-            const int b = wave + 4 * i;
-            if (b < M * nu) {
-                const int cm = b / nu, cu = b - cm * nu;
-                const float xs[4] = {xq[i].x, xq[i].y, xq[i].z, xq[i].w};
+        for (int c = 0; c < 16; ++c) {
+            const int t = wave + GV_WAVES * c;
+            if (t < M * lu_cnt) {
+                const int m = t / lu_cnt, sb = t - m * lu_cnt;
+                const float xs[4] = {xq[c].x, xq[c].y, xq[c].z, xq[c].w};
                 float d;
                 int q[4], s16;
                 q8k_wave(xs, lane, d, q, s16);
-                const int e = 4 * lane, c = e >> 6, w = e & 63, hf = w >> 5, gg = (w & 31) >> 3, tt = w & 7;
-                const int row = hf ? M + cm : cm;
-                *reinterpret_cast<uint32_t*>(s_img + ((((cu * 4 + c) * 4 + gg) * 2 * M + row) * 8 + tt)) =
-                    pack4(q[0], q[1], q[2], q[3]);
-                if (lane == 0) s_sc0[cu * 8 + cm] = d;
-                const int pair = s16 + __shfl_down(s16, 4);
-                if ((lane & 7) == 0) s_sc1[(cu * 8 + (lane >> 3)) * 8 + cm] = pair;
+                // element e = 4*lane: sub-block j, position tt; step 2*(j/4) + j%2 holds sub-blocks
+                // (4cc+h) in rows 0..7 and (4cc+2+h) in rows 8..15
+                const int e = 4 * lane, j = e >> 5, tt = e & 31;
+                const int isb = (j >> 1) & 1, op = 2 * (j >> 2) + (j & 1);
+                *reinterpret_cast<uint32_t*>(s_img + (sb * 4 + op) * OPB + ((isb * 2 + (tt >> 4)) * MS + m) * 16 +
+                                             (tt & 15)) = pack4(q[0], q[1], q[2], q[3]);
+                if (lane == 0) s_scf[sb * 9 * MS + m] = d;
+                const int pr = s16 + __shfl_down(s16, 4);
+                if ((lane & 7) == 0) s_sci[sb * 9 * MS + MS + (lane >> 3) * MS + m] = pr;
             }
         }
     }
     __syncthreads();
 
+    // ---- main loop ----
+    // activation operand of this lane: slot, and a mask for structurally zero rows
+    int aslot;
+    bool alive;
+    {
+        const int mrow = n & 7;
+        if constexpr (MODE == MODE_A) {
+            aslot = (g * 2 + (n >> 3)) * MS + mrow;
+            alive = mrow < M;
+        } else {
+            aslot = ((g >> 1) * 2 + (g & 1)) * MS + mrow;
+            alive = ((n >> 3) == (g >> 1)) && mrow < M;
+        }
+        if (!alive) aslot = 0;
+    }
+    const uint8_t* aimg = s_img + aslot * 16;
+    const uint32_t amask = alive ? 0xffffffffu : 0u;
+    const int moff = MS == 8 ? 4 * (g & 1) : 0;  // this lane's first output row within the slots
+    const uint8_t* rrow = stg + n * RS;           // this lane's weight row in the stage buffer
+
     f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    // A-operand row of this lane: rows 0..7 -> image row m, rows 8..15 -> image row M+m
-    const int arow = j < 8 ? j : M + (j - 8);
-    const bool alive = (j & 7) < M;
+    const i32x4_t zi = {0, 0, 0, 0};
+    const f32x4_t zf = {0.0f, 0.0f, 0.0f, 0.0f};
+    // Q8_0 mode b: k-group 1 completes its 16 bytes with q0, q1 from the pair's first dword
+    const uint32_t selp = g == 1 ? 0x07060100u : 0x03020100u;
+    // Q8_0 mode a: k-group 3 of the even block takes q30, q31, q0, q1
+    const uint32_t sel3 = g == 3 ? 0x07060100u : 0x03020100u;
+    const int dsh = g < 2 ? 0 : 16;
 
-    auto store = [&](uint4 (&pf)[MAXP]) {
-        WAVE_SYNC();
-#pragma unroll
-        for (int i = 0; i < MAXP; ++i) {
-            const int p = lane + 64 * i;
-            if (p < SB) reinterpret_cast<uint4*>(stg)[p] = pf[i];
-        }
-        WAVE_SYNC();
-    };
+    auto masked = [&](u32x4_t v) { return u32x4_t{v[0] & amask, v[1] & amask, v[2] & amask, v[3] & amask}; };
 
-    // one stage of one unit: rows n0..n0+15, stage s of the split
-    auto compute = [&](int n0, int s) {
-        const uint8_t* rowp = stg + j * SB;
-        const int lu0 = a.full_rows ? 0 : s * a.su;  // first unit of the stage, relative to u_begin
-        if (FMT == FMT_Q8_0) {
-            const int npairs = SB / 68;
-#pragma unroll 4
-            for (int pp = 0; pp < npairs; ++pp) {
-                const uint32_t* L = reinterpret_cast<const uint32_t*>(rowp + 68 * pp);
-                const uint32_t dw0 = L[0], dw8 = L[8];
-                const uint32_t le = L[1 + 2 * g], he_raw = L[2 + 2 * g];
-                const uint32_t lo = L[9 + 2 * g], ho = L[10 + 2 * g];
-                const uint32_t he = g == 3 ? __builtin_amdgcn_alignbyte(he_raw, dw0, 2) : he_raw;
-                const int lb = lu0 + 2 * pp;  // even block, relative to u_begin
-                if (MODE == MODE_A) {
-                    uint32_t t0_, t1_, t2_, t3_;
-                    i8x4_to_f16(le, t0_, t1_);
-                    i8x4_to_f16(he, t2_, t3_);
-                    const half8_t be = __builtin_bit_cast(half8_t, u32x4_t{t0_, t1_, t2_, t3_});
-                    i8x4_to_f16(lo, t0_, t1_);
-                    i8x4_to_f16(ho, t2_, t3_);
-                    const half8_t bo = __builtin_bit_cast(half8_t, u32x4_t{t0_, t1_, t2_, t3_});
-                    const half8_t* img = reinterpret_cast<const half8_t*>(s_img);
-                    half8_t ae = {}, ao = {};
-                    if (alive) {
-                        ae = img[(lb * 4 + g) * 2 * M + arow];
-                        ao = img[((lb + 1) * 4 + g) * 2 * M + arow];
-                    }
-                    const f32x4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
-                    const f32x4_t ce = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, be, z, 0, 0, 0);
-                    const f32x4_t co = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, bo, z, 0, 0, 0);
-                    const float de = f16lo(dw0), dd = f16hi(dw8);
+    auto compute = [&](int lu0, int tile) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[r] += de * ce[r] + dd * co[r];
+        for (int j = 0; j < P; ++j) {
+            const int lu = lu0 + j;  // load unit within the split
+            const uint8_t* rp = rrow + j * LUB;
+            if constexpr (FMT == FMT_Q8_0 && MODE == MODE_B) {
+                const uint8_t* xp = rp + 4 + 16 * g;
+                const uint32_t x0 = lds32(xp), x1 = lds32(xp + 4), x2 = lds32(xp + 8), x3 = lds32(xp + 12);
+                const uint32_t E = lds32(rp + (g < 2 ? 0 : 32));
+                const uint32_t b3 = __builtin_amdgcn_perm(E, x3, selp);
+                const i32x4_t B = {(int)x0, (int)x1, (int)x2, (int)b3};
+                const i32x4_t A = __builtin_bit_cast(i32x4_t, masked(lds128(aimg + lu * OPB)));
+                const i32x4_t C = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, zi, 0, 0, 0);
+                const float dw = (float)__builtin_bit_cast(_Float16, (uint16_t)(E >> dsh));
+                const float* dxp = s_scf + lu * 2 * MS + (g >> 1) * MS + moff;
+                if constexpr (R == 1) {
+                    acc[0] = fmaf((float)C[0], dw * dxp[0], acc[0]);
                 } else {
-                    const i32x4_t bq = {(int)le, (int)he, (int)lo, (int)ho};
-                    uint2 av = make_uint2(0, 0);
-                    if (alive) av = reinterpret_cast<const uint2*>(s_img)[((lb >> 1) * 4 + g) * 2 * M + arow];
-                    const i32x4_t aq = j < 8 ? i32x4_t{(int)av.x, (int)av.y, 0, 0} : i32x4_t{0, 0, (int)av.x, (int)av.y};
-                    const i32x4_t z = {0, 0, 0, 0};
-                    const i32x4_t c = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq, bq, z, 0, 0, 0);
-                    const int blk = lb + (g >> 1);
-                    const float sw = g < 2 ? f16lo(dw0) : f16hi(dw8);
-                    const f32x4_t dx = *reinterpret_cast<const f32x4_t*>(&s_sc0[blk * 8 + 4 * (g & 1)]);
+                    const f32x4_t dx = *reinterpret_cast<const f32x4_t*>(dxp);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[r] += (sw * dx[r]) * (float)c[r];
-                    if (EMIT) {
-                        const int n = n0 + j;
+                    for (int q = 0; q < 4; ++q) acc[q] = fmaf((float)C[q], dw * dx[q], acc[q]);
+                }
+                if constexpr (EMIT) {
+                    const int ng = tile * 16 + n, blk = 2 * (lu_beg + lu) + (g >> 1);
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int m = 4 * (g & 1) + r;
-                            if (m < M && n < N) a.sums[((int64_t)m * N + n) * a.units + u_begin + blk] = c[r];
-                        }
+                    for (int q = 0; q < 4; ++q) {
+                        const int m = 4 * (g & 1) + q;
+                        if (m < M && ng < N) a.sums[((int64_t)m * N + ng) * (2 * a.nlu) + blk] = C[q];
                     }
                 }
-            }
-        } else {  // Q4_K super-blocks
-            const int nsb = SB / 144;
-#pragma unroll 2
-            for (int uu = 0; uu < nsb; ++uu) {
-                const uint8_t* sbp = rowp + 144 * uu;
-                const u32x4_t hdr = *reinterpret_cast<const u32x4_t*>(sbp);
-                const float d = f16lo(hdr[0]), dmin = f16hi(hdr[0]);
-                int sc[8], mn[8];
+            } else if constexpr (FMT == FMT_Q8_0) {
+                const uint32_t E0 = lds32(rp), E8 = lds32(rp + 32);
+                const uint8_t* xe = rp + 4 + 8 * g;
+                const uint8_t* xo = rp + 36 + 8 * g;
+                const half8_t Be = i8x8_to_f16(lds32(xe), __builtin_amdgcn_perm(E0, lds32(xe + 4), sel3));
+                const half8_t Bo = i8x8_to_f16(lds32(xo), lds32(xo + 4));
+                const half8_t Ae = __builtin_bit_cast(half8_t, masked(lds128(aimg + (2 * lu) * OPB)));
+                const half8_t Ao = __builtin_bit_cast(half8_t, masked(lds128(aimg + (2 * lu + 1) * OPB)));
+                const f32x4_t Ce = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ae, Be, zf, 0, 0, 0);
+                const f32x4_t Co = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ao, Bo, zf, 0, 0, 0);
+                const float de = f16lo(E0), dd = f16hi(E8);
 #pragma unroll
-                for (int q = 0; q < 8; ++q) q4k_scale_min(hdr[1], hdr[2], hdr[3], q, sc[q], mn[q]);
-                const int lu = lu0 + uu;  // super-block relative to u_begin
-                if (MODE == MODE_A) {
-                    const half8_t* img = reinterpret_cast<const half8_t*>(s_img);
-                    const float* xs = reinterpret_cast<const float*>(s_sc1);
-                    f32x4_t mins = {0.0f, 0.0f, 0.0f, 0.0f};
+                for (int q = 0; q < R; ++q) acc[q] = fmaf(Co[q], dd, fmaf(Ce[q], de, acc[q]));
+            } else if constexpr (MODE == MODE_B) {
+                const u32x4_t H = lds128(rp);
+                const int ssh = 16 * (g >> 1);  // this lane's sub-blocks: j0 + {0, 1, 4, 5}, j0 = 2*(g>>1)
+                const uint32_t sa = H[1] >> ssh, sb_ = H[2] >> ssh, sc_ = H[3] >> ssh;
+                const uint32_t sc_lo = sa & 0x3f3fu, mn_lo = sb_ & 0x3f3fu;
+                const uint32_t sc_hi = (sc_ & 0x0f0fu) | ((sa >> 2) & 0x3030u);
+                const uint32_t mn_hi = ((sc_ >> 4) & 0x0f0fu) | ((sb_ >> 2) & 0x3030u);
+                i32x4_t sumi = zi;
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const uint2 qv = *reinterpret_cast<const uint2*>(sbp + 16 + 32 * c + 8 * g);
-                        const half8_t b0 = nib8_to_f16(qv.x, qv.y, 0);
-                        const half8_t b1 = nib8_to_f16(qv.x, qv.y, 4);
-                        const int sub0 = lu * 8 + 2 * c;
-                        half8_t a0 = {}, a1 = {};
-                        if (alive) {
-                            a0 = img[(sub0 * 4 + g) * 2 * M + arow];
-                            a1 = img[((sub0 + 1) * 4 + g) * 2 * M + arow];
-                        }
-                        const f32x4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
-                        const f32x4_t c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0, z, 0, 0, 0);
-                        const f32x4_t c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1, z, 0, 0, 0);
-                        const float s0 = d * (float)sc[2 * c], s1 = d * (float)sc[2 * c + 1];
-                        const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(&xs[sub0 * 8 + 4 * (g & 1)]);
-                        const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(&xs[(sub0 + 1) * 8 + 4 * (g & 1)]);
+                for (int cc = 0; cc < 2; ++cc) {
+                    const u32x4_t Qv = lds128(rp + 16 * (1 + 4 * cc + g));
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            acc[r] += s0 * c0[r] + s1 * c1[r];
-                            mins[r] += (float)mn[2 * c] * x0[r] + (float)mn[2 * c + 1] * x1[r];
-                        }
-                    }
-                    const float dm = g < 2 ? dmin : 0.0f;
+                    for (int h = 0; h < 2; ++h) {
+                        const i32x4_t B = {(int)((Qv[0] >> (4 * h)) & 0x0f0f0f0fu), (int)((Qv[1] >> (4 * h)) & 0x0f0f0f0fu),
+                                           (int)((Qv[2] >> (4 * h)) & 0x0f0f0f0fu), (int)((Qv[3] >> (4 * h)) & 0x0f0f0f0fu)};
+                        const i32x4_t A = __builtin_bit_cast(i32x4_t, masked(lds128(aimg + (lu * 4 + 2 * cc + h) * OPB)));
+                        const i32x4_t C = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, zi, 0, 0, 0);
+                        const int scj = (int)(((cc ? sc_hi : sc_lo) >> (8 * h)) & 0xffu);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[r] -= dm * mins[r];
-                } else {
-                    i32x4_t sumi = {0, 0, 0, 0};
-                    const int half = g >> 1;
+                        for (int q = 0; q < R; ++q) sumi[q] += scj * C[q];
+                        if constexpr (EMIT) {
+                            const int ng = tile * 16 + n, jj = 2 * (g >> 1) + 4 * cc + h;
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const uint2 qv = *reinterpret_cast<const uint2*>(sbp + 16 + 32 * c + 8 * g);
-                        const i32x4_t bq = {(int)(qv.x & 0x0f0f0f0fu), (int)(qv.y & 0x0f0f0f0fu),
-                                            (int)((qv.x >> 4) & 0x0f0f0f0fu), (int)((qv.y >> 4) & 0x0f0f0f0fu)};
-                        uint2 av = make_uint2(0, 0);
-                        if (alive) av = reinterpret_cast<const uint2*>(s_img)[((lu * 4 + c) * 4 + g) * 2 * M + arow];
-                        const i32x4_t aq = j < 8 ? i32x4_t{(int)av.x, (int)av.y, 0, 0} : i32x4_t{0, 0, (int)av.x, (int)av.y};
-                        const i32x4_t z = {0, 0, 0, 0};
-                        const i32x4_t cc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq, bq, z, 0, 0, 0);
-                        const int scj = sc[2 * c + half];
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) sumi[r] += scj * cc[r];
-                        if (EMIT) {
-                            const int n = n0 + j;
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                const int m = 4 * (g & 1) + r;
-                                if (m < M && n < N)
-                                    a.sums[(((int64_t)m * N + n) * a.units + u_begin + lu) * 10 + 2 * c + half] = cc[r];
-                            }
-                        }
-                    }
-                    i32x4_t summ = {0, 0, 0, 0};
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const int jq = 2 * c + half;
-                        const i32x4_t bsv = *reinterpret_cast<const i32x4_t*>(&s_sc1[(lu * 8 + jq) * 8 + 4 * (g & 1)]);
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) summ[r] += mn[jq] * bsv[r];
-                    }
-                    const f32x4_t dq = *reinterpret_cast<const f32x4_t*>(&s_sc0[lu * 8 + 4 * (g & 1)]);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[r] += dq[r] * (d * (float)sumi[r] - dmin * (float)summ[r]);
-                    if (EMIT) {
-                        i32x4_t ti, tm;
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            ti[r] = sumi[r] + __shfl_xor(sumi[r], 32);
-                            tm[r] = summ[r] + __shfl_xor(summ[r], 32);
-                        }
-                        const int n = n0 + j;
-                        if (g < 2) {
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                const int m = 4 * g + r;
-                                if (m < M && n < N) {
-                                    int32_t* o = a.sums + (((int64_t)m * N + n) * a.units + u_begin + lu) * 10;
-                                    o[8] = ti[r];
-                                    o[9] = tm[r];
-                                }
+                            for (int q = 0; q < 4; ++q) {
+                                const int m = 4 * (g & 1) + q;
+                                if (m < M && ng < N)
+                                    a.sums[(((int64_t)m * N + ng) * a.nlu + lu_beg + lu) * 10 + jj] = C[q];
                             }
                         }
                     }
                 }
-            }
-        }
-        if (s == nstages - 1 && !EMIT) {  // unit done: combine the two halves, write, reset
+                const int mn0 = mn_lo & 0xff, mn1 = (mn_lo >> 8) & 0xff, mn4 = mn_hi & 0xff, mn5 = (mn_hi >> 8) & 0xff;
+                const int32_t* bsp = s_sci + lu * 9 * MS + MS + 2 * (g >> 1) * MS + moff;
+                const float* dqp = s_scf + lu * 9 * MS + moff;
+                const float d = f16lo(H[0]), dmin = f16hi(H[0]);
+                i32x4_t summ = zi;
+                if constexpr (R == 1) {
+                    summ[0] = mn0 * bsp[0] + mn1 * bsp[MS] + mn4 * bsp[4 * MS] + mn5 * bsp[5 * MS];
+                    acc[0] = fmaf(dqp[0], d * (float)sumi[0] - dmin * (float)summ[0], acc[0]);
+                } else {
+                    const i32x4_t b0 = *reinterpret_cast<const i32x4_t*>(bsp);
+                    const i32x4_t b1 = *reinterpret_cast<const i32x4_t*>(bsp + MS);
+                    const i32x4_t b4 = *reinterpret_cast<const i32x4_t*>(bsp + 4 * MS);
+                    const i32x4_t b5 = *reinterpret_cast<const i32x4_t*>(bsp + 5 * MS);
+                    const f32x4_t dq = *reinterpret_cast<const f32x4_t*>(dqp);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] += __shfl_xor(acc[r], 32);
-            const int n = n0 + j;
-            if (g < 2 && n < N) {
+                    for (int q = 0; q < 4; ++q) {
+                        summ[q] = mn0 * b0[q] + mn1 * b1[q] + mn4 * b4[q] + mn5 * b5[q];
+                        acc[q] = fmaf(dq[q], d * (float)sumi[q] - dmin * (float)summ[q], acc[q]);
+                    }
+                }
+                if constexpr (EMIT) {
+                    const int ng = tile * 16 + n;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int m = 4 * g + r;
-                    if (m < M) {
-                        float v = acc[r];
-                        if (MODE == MODE_A) v *= s_inv[m];
-                        if (a.ks == 1) a.y[(int64_t)m * N + n] = v;
-                        else a.part[((int64_t)split * GEMV_MAX_M + m) * N + n] = v;
+                    for (int q = 0; q < 4; ++q) {
+                        const int ti = sumi[q] + __shfl_xor(sumi[q], 32);
+                        const int tm = summ[q] + __shfl_xor(summ[q], 32);
+                        const int m = 4 * (g & 1) + q;
+                        if (g < 2 && m < M && ng < N) {
+                            int32_t* o = a.sums + (((int64_t)m * N + ng) * a.nlu + lu_beg + lu) * 10;
+                            o[8] = ti;
+                            o[9] = tm;
+                        }
+                    }
+                }
+            } else {
+                const u32x4_t H = lds128(rp);
+                const float d = f16lo(H[0]), dmin = f16hi(H[0]);
+                const uint32_t s0 = H[1], s1 = H[2], s2 = H[3];
+                const uint32_t sc4[2] = {s0 & 0x3f3f3f3fu, (s2 & 0x0f0f0f0fu) | ((s0 >> 2) & 0x30303030u)};
+                const uint32_t mn4[2] = {s1 & 0x3f3f3f3fu, ((s2 >> 4) & 0x0f0f0f0fu) | ((s1 >> 2) & 0x30303030u)};
+                const float* xsp = s_scf + (lu * 8) * 2 * MS + (g >> 1) * MS + moff;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const u32x2_t Qv = lds64(rp + 16 + 32 * c + 8 * g);
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int jj = 2 * c + h;
+                        const half8_t B = nib8_to_f16(Qv[0], Qv[1], 4 * h);
+                        const half8_t A = __builtin_bit_cast(half8_t, masked(lds128(aimg + (lu * 8 + jj) * OPB)));
+                        const f32x4_t C = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, zf, 0, 0, 0);
+                        const float dsc = d * (float)((sc4[jj >> 2] >> (8 * (jj & 3))) & 0xffu);
+                        const float dmm = dmin * (float)((mn4[jj >> 2] >> (8 * (jj & 3))) & 0xffu);
+                        if constexpr (R == 1) {
+                            acc[0] = fmaf(-dmm, xsp[jj * 2 * MS], fmaf(C[0], dsc, acc[0]));
+                        } else {
+                            const f32x4_t xs = *reinterpret_cast<const f32x4_t*>(xsp + jj * 2 * MS);
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) acc[q] = fmaf(-dmm, xs[q], fmaf(C[q], dsc, acc[q]));
+                        }
                     }
                 }
             }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] = 0.0f;
         }
     };
 
-    // two stages in flight: store stage q, queue stage q+2, compute stage q
-    for (int q = 0; q < nq; q += 2) {
-        store(pfA);
-        issue(pfA, q + 2);
-        compute(16 * (t0 + q / nstages), q - (q / nstages) * nstages);
-        store(pfB);
-        issue(pfB, q + 3);
-        if (q + 1 < nq) compute(16 * (t0 + (q + 1) / nstages), (q + 1) - ((q + 1) / nstages) * nstages);
+    int cq = 0, cu = 0, cs = 0;  // next stage to compute: index, tile, stage within the tile
+    auto step = [&](u32x4_t (&r)[T]) {
+        if (cq < Q) {
+            // land the stage in this wave's LDS buffer (the gather below reads other lanes' chunks)
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+                if (t < T - 1 || lane < TAIL) *reinterpret_cast<u32x4_t*>(stg + lw[t]) = r[t];
+            const int tile = (grp0 + cu) * a.G + tg;
+            compute(sl_lu0 + cs * P, tile);
+            if (cs == S - 1) {  // tile done: fold the two lane halves, park the partial in LDS
+#pragma unroll
+                for (int q = 0; q < R; ++q) acc[q] += __shfl_xor(acc[q], 32);
+                if (lane < 32) {
+                    float* o = s_red + ((cu * a.G + tg) * a.kw + sl) * GV_RED + 4 * (lane >> 4) * 16 + n;
+#pragma unroll
+                    for (int q = 0; q < R; ++q) o[16 * q] = acc[q];
+                }
+                acc = zf;
+            }
+        }
+        ++cq;
+        if (++cs == S) { cs = 0; ++cu; }
+        issue(r);
+    };
+    for (int q = 0; q < Q; q += 2) {
+        step(rA);
+        step(rB);
+    }
+    __syncthreads();
+
+    // ---- sum the slices of every tile and write ----
+    if constexpr (!EMIT) {
+        const int per = 16 * M, nout = ngrp * a.G * per;
+        for (int i = tid; i < nout; i += GV_THREADS) {
+            const int slot = i / per, rem = i - slot * per, m = rem >> 4, nn = rem & 15;
+            const int u = slot / a.G, t = slot - u * a.G;
+            const int ng = ((grp0 + u) * a.G + t) * 16 + nn;
+            if (ng < N) {
+                const float* p = s_red + slot * a.kw * GV_RED + m * 16 + nn;
+                float v = 0.0f;
+                for (int s = 0; s < a.kw; ++s) v += p[s * GV_RED];
+                if constexpr (MODE == MODE_A) v *= s_misc[8 + m];
+                if (a.ks == 1) a.y[(int64_t)m * N + ng] = v;
+                else a.part[((int64_t)split * GEMV_MAX_M + m) * N + ng] = v;
+            }
+        }
     }
 }
 
@@ -470,151 +558,194 @@ __global__ __launch_bounds__(256) void gemv_reduce_kernel(const float* __restric
     y[i] = s;
 }
 
-// ------------------------------------------------------------- geometry ----
+// ------------------------------------------------------------- kernels ----
 
-static int unit_values(int fmt) { return fmt == FMT_Q8_0 ? 32 : 256; }
+typedef void (*GvKernel)(GemvArgs);
+
+template <int FMT, int MODE, int P>
+static GvKernel gv_pick_r(int R, bool emit)
+{
+    if constexpr (MODE == MODE_B && P == 1)
+        if (emit) return gemv_kernel<FMT, MODE, 1, 4, true>;
+    return R == 1 ? gemv_kernel<FMT, MODE, P, 1, false> : gemv_kernel<FMT, MODE, P, 4, false>;
+}
+
+// Stage sizes (load units) compiled for each format.
+static const int kStageQ8[3] = {4, 3, 1};
+static const int kStageQ4[3] = {2, 3, 1};
+
+static GvKernel gv_kernel(int fmt, int mode, int P, int R, bool emit)
+{
+    if (fmt == FMT_Q8_0) {
+        if (mode == MODE_A) return P == 4 ? gv_pick_r<FMT_Q8_0, MODE_A, 4>(R, false)
+                                   : P == 3 ? gv_pick_r<FMT_Q8_0, MODE_A, 3>(R, false)
+                                            : gv_pick_r<FMT_Q8_0, MODE_A, 1>(R, false);
+        return P == 4 ? gv_pick_r<FMT_Q8_0, MODE_B, 4>(R, emit)
+             : P == 3 ? gv_pick_r<FMT_Q8_0, MODE_B, 3>(R, emit)
+                      : gv_pick_r<FMT_Q8_0, MODE_B, 1>(R, emit);
+    }
+    if (mode == MODE_A) return P == 2 ? gv_pick_r<FMT_Q4_K, MODE_A, 2>(R, false)
+                               : P == 3 ? gv_pick_r<FMT_Q4_K, MODE_A, 3>(R, false)
+                                        : gv_pick_r<FMT_Q4_K, MODE_A, 1>(R, false);
+    return P == 2 ? gv_pick_r<FMT_Q4_K, MODE_B, 2>(R, emit)
+         : P == 3 ? gv_pick_r<FMT_Q4_K, MODE_B, 3>(R, emit)
+                  : gv_pick_r<FMT_Q4_K, MODE_B, 1>(R, emit);
+}
+
+// Workgroups of one kernel resident at once on the current device with `lds`
+// bytes of LDS each (CUs x workgroups per CU), cached.
+static int resident_wgs(GvKernel k, int lds)
+{
+    static std::map<std::pair<std::pair<int, const void*>, int>, int> cache;
+    static std::mutex mu;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    std::lock_guard<std::mutex> lock(mu);
+    const auto key = std::make_pair(std::make_pair(dev, (const void*)k), lds);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, GV_LDS_MAX);
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, GV_THREADS, lds) != hipSuccess || per_cu < 1)
+        per_cu = 1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 1;
+    (void)hipGetLastError();
+    return cache[key] = per_cu * cus;
+}
+
+// ------------------------------------------------------------- geometry ----
 
 bool gemv_supported(int fmt, int64_t K)
 {
-    if (fmt == FMT_Q4_K) return K % 256 == 0;
-    if (K % 32) return false;
-    const int64_t units = K / 32;
-    const bool whole_rows = 16 * units * 34 <= GEMV_STAGE_BYTES && units % 2 == 0;
-    return whole_rows || units % 8 == 0;
+    return fmt == FMT_Q4_K ? K % 256 == 0 : K % 64 == 0;
 }
 
-// Most K splits a run may use (sizes the split-K workspace): at least enough
-// to keep every split within the LDS activation operand (1024 values for
-// f32 activations at M = 8), at most one split per aligned unit group.
+// LDS bytes of the eight waves' weight stage buffers.
+static int stage_bytes(int fmt, int P) { return GV_WAVES * 16 * (fmt == FMT_Q8_0 ? gv_rs(FMT_Q8_0, P) : gv_rs(FMT_Q4_K, P)); }
+
+// K splits of one run: enough that the activation operand of a split (with
+// the smallest weight stage) fits in LDS and one workgroup prepares at most
+// 64 values per thread.
+static int gemv_splits(int fmt, int mode, int64_t K, int M, int ms, int& lus_split)
+{
+    int lub, ops, vpl, opb, scb;
+    gv_fmt(fmt, mode, ms, lub, ops, vpl, opb, scb);
+    const int64_t nlu = K / vpl;
+    const int64_t per_lu = (int64_t)ops * opb + scb;
+    const int64_t room = GV_LDS_MAX - GV_WAVES * GV_RED * 4 - GV_MISC_BYTES - stage_bytes(fmt, 1);
+    const int64_t lus_max = std::max<int64_t>(1, std::min<int64_t>(room / per_lu, GV_XMAX / ((int64_t)M * vpl)));
+    const int64_t ks = (nlu + lus_max - 1) / lus_max;
+    lus_split = (int)((nlu + ks - 1) / ks);
+    return (int)ks;
+}
+
 int gemv_max_splits(int fmt, int64_t K)
 {
-    const int64_t units = K / unit_values(fmt);
-    if (fmt == FMT_Q8_0 && units % 8) return 1;
-    const int64_t align = fmt == FMT_Q8_0 ? 8 : 1;
-    const int64_t cap = std::max<int64_t>(GEMV_MAX_SPLITS, (K + 1023) / 1024);
-    return (int)std::max<int64_t>(1, std::min<int64_t>(cap, units / align));
+    int l;
+    int ks = 1;
+    for (int mode = 0; mode < 2; ++mode)
+        for (int M = 1; M <= GEMV_MAX_M; ++M) ks = std::max(ks, gemv_splits(fmt, mode, K, M, M == 1 ? 1 : 8, l));
+    return ks;
 }
 
-// K splits, units per wave and grid for one run: every workgroup resident at
-// once (max_wgs = CUs x workgroups per CU), about one unit per wave when the
-// matrix is large, and each K split at most min(4096, 8192/M) values, so one
-// thread (one wave for Q8K) prepares at most one chunk of the activation
-// operand and the operand fits in LDS.  The stage size divides every split.
-GemvGeom gemv_geom(int fmt, int mode, int64_t N, int64_t K, int M, int max_wgs)
+// Geometry of one run: K splits, waves per tile (kw), stage size (P) and tile
+// groups per workgroup, chosen to minimise the bytes the busiest wave loads
+// (plus a per-stage overhead) with every workgroup resident at once; ties go
+// to larger stages, then to fewer waves per tile.
+GemvGeom gemv_geom(int fmt, int mode, int64_t N, int64_t K, int M, bool emit)
 {
-    (void)mode;
     GemvGeom g{};
-    const int qk = unit_values(fmt);
-    g.unit_bytes = fmt == FMT_Q8_0 ? 34 : 144;
-    g.units = (int)(K / qk);
-    g.row_bytes = (int64_t)g.units * g.unit_bytes;
+    g.R = M == 1 && !emit ? 1 : 4;
+    const int ms = g.R == 1 ? 1 : 8;
+    int lub, ops, vpl, opb, scb;
+    gv_fmt(fmt, mode, ms, lub, ops, vpl, opb, scb);
+    g.nlu = (int)(K / vpl);
+    g.row_bytes = (int64_t)g.nlu * lub;
     g.tiles = (int)((N + 15) / 16);
-    const int range = std::min(MAX_RANGE, 8192 / M);
-    const int max_units = std::max(1, range / qk);
-    int ks = std::max((g.units + max_units - 1) / max_units, (4 * max_wgs) / g.tiles);
-    ks = std::max(1, std::min(ks, gemv_max_splits(fmt, K)));
-    if (fmt == FMT_Q8_0 && g.units % 8) {
-        g.ks = 1;
-        g.ups = g.units;
-        g.full_rows = 1;
-        g.su = g.units;
-    } else {
-        int ups = (g.units + ks - 1) / ks;
-        if (fmt == FMT_Q8_0) ups = (ups + 7) / 8 * 8;
-        while (ups > max_units && ups > (fmt == FMT_Q8_0 ? 8 : 1)) ups -= fmt == FMT_Q8_0 ? 8 : 1;
-        g.ups = ups;
-        g.ks = (g.units + ups - 1) / ups;
-        const int last = g.units - (g.ks - 1) * ups;
-        g.full_rows = fmt == FMT_Q8_0 && g.ks == 1 && 16 * g.row_bytes <= GEMV_STAGE_BYTES;
-        if (g.full_rows) {
-            g.su = g.units;
-        } else {
-            const int cand8[2] = {16, 8}, cand4[4] = {4, 3, 2, 1};
-            const int* cand = fmt == FMT_Q8_0 ? cand8 : cand4;
-            const int nc = fmt == FMT_Q8_0 ? 2 : 4;
-            g.su = cand[nc - 1];
-            for (int i = 0; i < nc; ++i)
-                if (ups % cand[i] == 0 && last % cand[i] == 0) {
-                    g.su = cand[i];
-                    break;
-                }
+    g.ks = gemv_splits(fmt, mode, K, M, ms, g.lus_split);
+    const int* stages = fmt == FMT_Q8_0 ? kStageQ8 : kStageQ4;
+    int64_t best = -1;
+    for (int kw = 1; kw <= GV_WAVES; kw *= 2) {
+        for (int si = 0; si < 3; ++si) {
+            const int P = stages[si];
+            if (emit && P != 1) continue;
+            const int raw = (g.lus_split + kw - 1) / kw;
+            const int slice = (raw + P - 1) / P * P;
+            if ((kw - 1) * slice >= g.lus_split) continue;  // an empty slice
+            const int G = GV_WAVES / kw;
+            const int groups = (g.tiles + G - 1) / G;
+            const int img = kw * slice * ops * opb;
+            const int sc = kw * slice * scb;
+            const int stg = stage_bytes(fmt, P);
+            const int fixed = img + sc + GV_MISC_BYTES + stg;  // plus 4 KB of partials per tile group
+            const int gpw_cap = std::min(GV_GPW_MAX, (GV_LDS_MAX - fixed) / (GV_WAVES * GV_RED * 4));
+            if (gpw_cap < 1) continue;
+            // fewest tile groups per workgroup that keep every workgroup resident at once
+            const GvKernel kern = gv_kernel(fmt, mode, P, g.R, emit);
+            int gpw = 1;
+            while (gpw < gpw_cap &&
+                   (int64_t)groups * g.ks > (int64_t)gpw * resident_wgs(kern, fixed + gpw * GV_WAVES * GV_RED * 4))
+                ++gpw;
+            // bytes the busiest wave loads (whole 16-byte chunks) plus a per-stage overhead
+            const int cpr = fmt == FMT_Q8_0 ? gv_cpr(FMT_Q8_0, P) : gv_cpr(FMT_Q4_K, P);
+            const int64_t cost = (int64_t)gpw * (slice / P) * (256 * cpr + 512);
+            if (best < 0 || cost < best || (cost == best && P > g.P)) {
+                best = cost;
+                g.kw = kw;
+                g.slice = slice;
+                g.P = P;
+                g.G = G;
+                g.groups = groups;
+                g.gpw = gpw;
+                g.rs = fmt == FMT_Q8_0 ? gv_rs(FMT_Q8_0, P) : gv_rs(FMT_Q4_K, P);
+                g.sc_off = img;
+                g.red_off = img + sc;
+                g.misc_off = g.red_off + gpw * GV_WAVES * GV_RED * 4;
+                g.stg_off = g.misc_off + GV_MISC_BYTES;
+                g.lds = g.stg_off + stg;
+                g.grid = g.ks * ((groups + gpw - 1) / gpw);
+            }
         }
     }
-    const int64_t units_total = (int64_t)g.tiles * g.ks;
-    g.upw = (int)std::max<int64_t>(1, (units_total + 4 * (int64_t)max_wgs - 1) / (4 * (int64_t)max_wgs));
-    const int wgs_per_split = (int)((g.tiles + 4 * g.upw - 1) / (4 * g.upw));
-    g.grid = wgs_per_split * g.ks;
     return g;
 }
 
 // ------------------------------------------------------------ launchers ----
 
-template <int FMT, int MODE, bool EMIT>
-static int resident_wgs()
-{
-    static int cached[64] = {0};
-    static std::mutex mu;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    std::lock_guard<std::mutex> lock(mu);
-    if (cached[dev] == 0) {
-        int per_cu = 0, cus = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemv_kernel<FMT, MODE, EMIT>, 256, 0) != hipSuccess ||
-            per_cu < 1)
-            per_cu = 1;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 1;
-        cached[dev] = per_cu * cus;
-    }
-    return cached[dev];
-}
-
-int gemv_resident_wgs(int fmt, int mode, bool emit)
-{
-    if (fmt == FMT_Q8_0) {
-        if (mode == MODE_A) return resident_wgs<FMT_Q8_0, MODE_A, false>();
-        return emit ? resident_wgs<FMT_Q8_0, MODE_B, true>() : resident_wgs<FMT_Q8_0, MODE_B, false>();
-    }
-    if (mode == MODE_A) return resident_wgs<FMT_Q4_K, MODE_A, false>();
-    return emit ? resident_wgs<FMT_Q4_K, MODE_B, true>() : resident_wgs<FMT_Q4_K, MODE_B, false>();
-}
-
-template <int FMT, int MODE, bool EMIT>
-static void launch_one(const GemvArgs& a, int grid, hipStream_t s)
-{
-    hipLaunchKernelGGL((gemv_kernel<FMT, MODE, EMIT>), dim3((unsigned)grid), dim3(256), 0, s, a);
-}
-
 hipError_t launch_gemv(int fmt, int mode, const void* w, const float* x, int64_t N, int64_t K, int M,
                        const GemvBufs& b, float* y, int32_t* sums, hipStream_t s)
 {
     const bool emit = sums != nullptr;
-    const GemvGeom g = gemv_geom(fmt, mode, N, K, M, gemv_resident_wgs(fmt, mode, emit));
+    const GemvGeom g = gemv_geom(fmt, mode, N, K, M, emit);
+    if (g.grid <= 0) return hipErrorInvalidConfiguration;
     GemvArgs a{};
     a.w = (const uint8_t*)w;
-    a.row_bytes = g.row_bytes;
+    a.w_bytes = N * g.row_bytes;
+    a.row_bytes = (int)g.row_bytes;
     a.N = (int)N;
     a.K = (int)K;
     a.M = M;
-    a.units = g.units;
-    a.ups = g.ups;
+    a.nlu = g.nlu;
+    a.lus_split = g.lus_split;
     a.ks = g.ks;
-    a.full_rows = g.full_rows;
-    a.su = g.su;
-    a.upw = g.upw;
-    a.tiles = g.tiles;
+    a.kw = g.kw;
+    a.slice = g.slice;
+    a.G = g.G;
+    a.groups = g.groups;
+    a.gpw = g.gpw;
+    a.sc_off = g.sc_off;
+    a.red_off = g.red_off;
+    a.misc_off = g.misc_off;
+    a.stg_off = g.stg_off;
     a.x = x;
     a.part = b.part;
     a.y = y;
     a.sums = sums;
-    if (fmt == FMT_Q8_0) {
-        if (mode == MODE_A) launch_one<FMT_Q8_0, MODE_A, false>(a, g.grid, s);
-        else if (emit) launch_one<FMT_Q8_0, MODE_B, true>(a, g.grid, s);
-        else launch_one<FMT_Q8_0, MODE_B, false>(a, g.grid, s);
-    } else {
-        if (mode == MODE_A) launch_one<FMT_Q4_K, MODE_A, false>(a, g.grid, s);
-        else if (emit) launch_one<FMT_Q4_K, MODE_B, true>(a, g.grid, s);
-        else launch_one<FMT_Q4_K, MODE_B, false>(a, g.grid, s);
-    }
+    GvKernel k = gv_kernel(fmt, mode, g.P, g.R, emit);
+    (void)resident_wgs(k, g.lds);  // sets the kernel's LDS limit on this device
+    void* args[] = {&a};
+    hipError_t e = hipLaunchKernel((const void*)k, dim3(g.grid), dim3(GV_THREADS), args, g.lds, s);
+    if (e != hipSuccess) return e;
     if (!emit && g.ks > 1) {
         const int64_t total = (int64_t)M * N;
         hipLaunchKernelGGL(gemv_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, b.part, g.ks,

@@ -9,11 +9,9 @@ namespace qmm {
 enum { FMT_Q8_0 = 8, FMT_Q4_K = 12, FMT_Q8_K = 15 };
 enum { MODE_A = 0, MODE_B = 1 };
 
-// Decode (GEMV) path: M <= 8 rows; 256-thread workgroups of four waves, each
-// wave streaming 16-row tiles of one K split.
+// Decode (GEMV) path: M <= 8 rows; 512-thread workgroups of eight waves,
+// each wave streaming 16-row tiles over one slice of K.
 constexpr int GEMV_MAX_M = 8;
-constexpr int GEMV_MAX_SPLITS = 16;
-constexpr int GEMV_STAGE_BYTES = 9792;  // per-wave weight staging buffer (16 rows)
 
 // Prefill (GEMM) path tile.
 constexpr int GEMM_BM = 128;
@@ -21,15 +19,20 @@ constexpr int GEMM_BN = 128;
 constexpr int GEMM_KS = 64;
 
 struct GemvGeom {
-    int units;        // weight blocks per row (Q8_0: 32 values, Q4_K: 256)
-    int unit_bytes;   // 34 or 144
+    int nlu;          // load units per row (Q8_0 block pairs or Q4_K super-blocks)
     int64_t row_bytes;
     int tiles;        // 16-row tiles
-    int ks;           // K splits
-    int ups;          // units per K split
-    int full_rows;    // 1: stage whole rows (the 16-row tile is contiguous)
-    int su;           // units per stage when staging row segments
-    int upw;          // tiles per wave
+    int ks;           // K splits across workgroups
+    int lus_split;    // load units per split
+    int kw;           // waves per tile (K slices inside a workgroup)
+    int slice;        // load units per wave slice
+    int P;            // load units per stage
+    int R;            // activation rows per lane the arithmetic covers (1 or 4)
+    int G;            // tiles per workgroup step
+    int groups;       // tile groups per split
+    int gpw;          // tile groups per workgroup
+    int rs;           // LDS row stride of the per-wave weight stage buffer (bytes)
+    int sc_off, red_off, misc_off, stg_off, lds;  // LDS layout (bytes)
     int grid;         // workgroups
 };
 
@@ -46,7 +49,7 @@ struct GemmBufs {
     void* sc1;     // mode a Q4_K: scaled sub-block sums [M][K/32] f32; mode b Q4_K: bsum pairs [M][K/32] i32
 };
 
-GemvGeom gemv_geom(int fmt, int mode, int64_t N, int64_t K, int M, int max_wgs);
+GemvGeom gemv_geom(int fmt, int mode, int64_t N, int64_t K, int M, bool emit);
 bool gemv_supported(int fmt, int64_t K);
 int gemv_max_splits(int fmt, int64_t K);
 
