@@ -6,24 +6,58 @@
 
 namespace qmm {
 
-// Q8_0 block of 32 values (page "自己量化", section 和下载的 Q8_0 逐字节比: the
-// scale is max|x|/127): d = amax/127 in f32, q = round-half-away(x * (1/d))
-// with the unrounded d, d stored as f16 (nearest even).
-QMM_DEV void q8_0_block(const float a[32], uint16_t& dbits, float& dval, int8_t q[32])
+// Q8_0 scale of a block of 32 values from its max|x| (page "自己量化", section
+// 和下载的 Q8_0 逐字节比: the scale is max|x|/127): d = amax/127 in f32, the
+// quantizer multiplies by id = 1/d (0 for an all-zero block), d is stored as
+// f16 (nearest even).  Every Q8_0 activation quantizer goes through this and
+// q8_0_q, so all of them produce identical blocks.
+QMM_DEV void q8_0_scale(float amax, float& id, uint16_t& dbits, float& dval)
 {
 #pragma clang fp contract(off)
-    float amax = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-        const float t = fabsf(a[j]);
-        amax = t > amax ? t : amax;
-    }
     const float d = amax / 127.0f;
-    const float id = d != 0.0f ? 1.0f / d : 0.0f;
+    id = d != 0.0f ? 1.0f / d : 0.0f;
     dbits = f16bits(d);
     dval = f16round(d);
+}
+// q = round-half-away(x * id) with the unrounded scale.
+QMM_DEV int q8_0_q(float x, float id)
+{
+#pragma clang fp contract(off)
+    return (int)roundf(x * id);
+}
+
+QMM_DEV void q8_0_block(const float a[32], uint16_t& dbits, float& dval, int8_t q[32])
+{
+    float amax = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 32; ++j) q[j] = (int8_t)(int)roundf(a[j] * id);
+    for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(a[j]));
+    float id;
+    q8_0_scale(amax, id, dbits, dval);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) q[j] = (int8_t)q8_0_q(a[j], id);
+}
+
+// Q8K: the signed element of largest |x| picks the scale, the first index
+// winning ties; q8k_better says whether candidate (ob, oi) beats (best, bi).
+QMM_DEV bool q8k_better(float ob, int oi, float best, int bi) { return ob > best || (ob == best && oi < bi); }
+// From that element mx (and its |mx| = best): iscale = -127/mx, d = 1/iscale;
+// an all-zero block gives iscale = d = 0.
+QMM_DEV void q8k_scale(float mx, float best, float& iscale, float& d)
+{
+#pragma clang fp contract(off)
+    iscale = 0.0f;
+    d = 0.0f;
+    if (best != 0.0f) {
+        iscale = -127.0f / mx;
+        d = 1.0f / iscale;
+    }
+}
+// q = min(127, round-half-away(iscale * x)).
+QMM_DEV int q8k_q(float x, float iscale)
+{
+#pragma clang fp contract(off)
+    const int v = (int)roundf(iscale * x);
+    return v < 127 ? v : 127;
 }
 
 QMM_DEV void load32(const float* __restrict__ v, float a[32])
@@ -42,7 +76,6 @@ QMM_DEV void load32(const float* __restrict__ v, float a[32])
 // 4i..4i+3 hold bsums[i] in s16.
 QMM_DEV void q8k_wave(const float xs[4], int lane, float& d, int q[4], int& s16)
 {
-#pragma clang fp contract(off)
     float best = -1.0f;
     int bi = 0;
 #pragma unroll
@@ -54,22 +87,15 @@ QMM_DEV void q8k_wave(const float xs[4], int lane, float& d, int q[4], int& s16)
     for (int off = 1; off < 64; off <<= 1) {
         const float ob = __shfl_xor(best, off);
         const int oi = __shfl_xor(bi, off);
-        if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
+        if (q8k_better(ob, oi, best, bi)) { best = ob; bi = oi; }
     }
     const int sel = bi & 3;
     const float mine = sel == 0 ? xs[0] : sel == 1 ? xs[1] : sel == 2 ? xs[2] : xs[3];
     const float mx = __shfl(mine, bi >> 2);
-    d = 0.0f;
-    q[0] = q[1] = q[2] = q[3] = 0;
-    if (best != 0.0f) {
-        const float iscale = -127.0f / mx;
+    float iscale;
+    q8k_scale(mx, best, iscale, d);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int v = (int)roundf(iscale * xs[u]);
-            q[u] = v < 127 ? v : 127;
-        }
-        d = 1.0f / iscale;
-    }
+    for (int u = 0; u < 4; ++u) q[u] = q8k_q(xs[u], iscale);
     int s = q[0] + q[1] + q[2] + q[3];
     s += __shfl_xor(s, 1);
     s += __shfl_xor(s, 2);
@@ -86,6 +112,14 @@ QMM_DEV int split_exp(float amax)
     if (amax == 0.0f) return 0;
     const int e = 14 - ilogbf(amax);
     return e > 126 ? 126 : e;
+}
+
+QMM_DEV void split_one(float x, float s, _Float16& hi, _Float16& lo, float& xs)
+{
+#pragma clang fp contract(off)
+    xs = x * s;
+    hi = (_Float16)xs;
+    lo = (_Float16)(xs - (float)hi);
 }
 
 QMM_DEV float split_chunk(const float a[32], float s, _Float16 hi[32], _Float16 lo[32])

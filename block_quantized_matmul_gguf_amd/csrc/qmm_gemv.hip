@@ -124,7 +124,7 @@ QMM_DEV u32x4_t lds128(const uint8_t* p) { return *reinterpret_cast<const u32x4_
 // R: activation rows per lane the arithmetic covers (1 when M == 1, else 4:
 // lane l holds output rows 4*(l/16 % 2) + r of its tile column l%16).
 template <int FMT, int MODE, int P, int R, bool EMIT>
-__global__ __launch_bounds__(GV_THREADS, 1) void gemv_kernel(GemvArgs a)
+__global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
 {
     constexpr int MS = R == 1 ? 1 : 8;
     using F = GvFmt<FMT, MODE, MS>;
@@ -154,35 +154,6 @@ __global__ __launch_bounds__(GV_THREADS, 1) void gemv_kernel(GemvArgs a)
     const int Q = ngrp * S;                                   // stages this wave streams
     uint8_t* stg = lds + a.stg_off + wave * (16 * RS);
 
-    // ---- x of this K split: loaded before the weight stream is queued ----
-    const rsrc_t xr = make_rsrc(a.x, (uint32_t)(M * K * 4));
-    const int k0 = lu_beg * VPL;
-    constexpr bool CHUNKS = MODE == MODE_A || FMT == FMT_Q8_0;  // 32-value chunks, one per thread and pass
-    const int nb32 = lu_cnt * (VPL / 32);
-    float xv[2][32];
-    float4 xq[16];
-    if constexpr (CHUNKS) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const int t = tid + GV_THREADS * c;
-            const int m = t / nb32, b = t - m * nb32;
-            const uint32_t off = t < M * nb32 ? (uint32_t)(m * K + k0 + 32 * b) * 4 : 0x80000000u;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float4 v = ldx16(xr, off + 16 * i);
-                xv[c][4 * i] = v.x; xv[c][4 * i + 1] = v.y; xv[c][4 * i + 2] = v.z; xv[c][4 * i + 3] = v.w;
-            }
-        }
-    } else {
-#pragma unroll
-        for (int c = 0; c < 16; ++c) {  // Q8K: one 256-value block per wave and pass, 4 values per lane
-            const int t = wave + GV_WAVES * c;
-            const int m = t / lu_cnt, b = t - m * lu_cnt;
-            const uint32_t off = t < M * lu_cnt ? (uint32_t)(m * K + k0 + 256 * b + 4 * lane) * 4 : 0x80000000u;
-            xq[c] = ldx16(xr, off);
-        }
-    }
-
     // ---- the weight stream: chunk f = 64t + lane of a stage is row f/CPR, chunk f%CPR ----
     uint32_t go[T], lw[T];
 #pragma unroll
@@ -208,10 +179,87 @@ __global__ __launch_bounds__(GV_THREADS, 1) void gemv_kernel(GemvArgs a)
         for (int t = 0; t < T; ++t) r[t] = ld128(wr, go[t] + so);
     };
     u32x4_t rA[T], rB[T];
-    issue(rA);
-    issue(rB);
 
     // ---- the activation operand of this K split, once per workgroup ----
+    // Each task fills one 16-byte operand slot (mode b: 16 int8 of one half of a
+    // (sub-)block; mode a: 8 values of one k-group as f16 hi and lo) from exactly
+    // the x values that slot holds, in slot order; the lanes of one block meet
+    // through shuffles for its scale.  Waves with no task queue their weight
+    // stages at once; the others after their slots are written.
+    constexpr int VT = MODE == MODE_A ? 8 : 16;   // x values per task
+    constexpr int NTPT = MODE == MODE_A ? 8 : 4;  // tasks per thread at most (64 values)
+    const int nb32 = lu_cnt * (VPL / 32);         // 32-value blocks in this split
+    const int ntasks = MODE == MODE_A ? M * nb32 * 4 : (FMT == FMT_Q8_0 ? M * nb32 * 2 : M * lu_cnt * 16);
+    const bool xw = 64 * wave < ntasks;
+    const rsrc_t xr = make_rsrc(a.x, (uint32_t)(M * K * 4));
+    const int k0 = lu_beg * VPL;
+    float xv[NTPT][VT];
+    if (xw) {
+#pragma unroll
+        for (int c = 0; c < NTPT; ++c) {
+            if (64 * wave + GV_THREADS * c >= ntasks) break;  // uniform per wave
+            const int t = tid + GV_THREADS * c;
+            const bool live = t < ntasks;
+            const int per_row = ntasks / M;
+            const int m = t / per_row, r = t - m * per_row;
+            uint32_t o[4];  // float offsets of the slot's values: 4 + 4 + 4 + 4, or 4 + 2 + 2 (mode a)
+            if constexpr (MODE == MODE_A) {
+                const int b = r >> 2, kg = r & 3;
+                const int base = m * K + k0 + 32 * b;
+                int o0 = 8 * kg, o2 = 8 * kg + 6;
+                if (FMT == FMT_Q8_0 && !(b & 1)) {  // even block: q[2+8kg ..]; group 3: q26..q31, q0, q1
+                    o0 = kg < 3 ? 2 + 8 * kg : 26;
+                    o2 = kg < 3 ? o0 + 6 : 0;
+                }
+                o[0] = base + o0; o[1] = base + o0 + 4; o[2] = base + o2; o[3] = 0;
+            } else if constexpr (FMT == FMT_Q8_0) {
+                const int b = r >> 1, h = r & 1;
+                const int base = m * K + k0 + 32 * b;
+                // even block: half 0 = q2..q17, half 1 = q18..q31, q0, q1; odd block: natural
+                const int s0 = (b & 1) ? 16 * h : 2 + 16 * h;
+                o[0] = base + s0; o[1] = base + s0 + 4; o[2] = base + s0 + 8;
+                o[3] = base + ((b & 1) || !h ? s0 + 12 : 28);  // 4 values; the last 2 of half 1 (even) wrap
+            } else {
+                const int sb = r >> 4, sl16 = r & 15;
+                const int base = m * K + k0 + 256 * sb + 16 * sl16;
+                o[0] = base; o[1] = base + 4; o[2] = base + 8; o[3] = base + 12;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = live ? o[i] * 4 : 0x80000000u;
+            if constexpr (MODE == MODE_A) {
+                const float4 v0 = ldx16(xr, o[0]);
+                const u32x2_t v1 = __builtin_amdgcn_raw_buffer_load_b64(xr, o[1], 0, 0);
+                const u32x2_t v2 = __builtin_amdgcn_raw_buffer_load_b64(xr, o[2], 0, 0);
+                xv[c][0] = v0.x; xv[c][1] = v0.y; xv[c][2] = v0.z; xv[c][3] = v0.w;
+                xv[c][4] = __uint_as_float(v1[0]); xv[c][5] = __uint_as_float(v1[1]);
+                xv[c][6] = __uint_as_float(v2[0]); xv[c][7] = __uint_as_float(v2[1]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 3; ++i) {
+                    const float4 v = ldx16(xr, o[i]);
+                    xv[c][4 * i] = v.x; xv[c][4 * i + 1] = v.y; xv[c][4 * i + 2] = v.z; xv[c][4 * i + 3] = v.w;
+                }
+                if constexpr (FMT == FMT_Q8_0) {
+                    // last 4 values: the slot's q12..q15 (halves of odd blocks, half 0 of even
+                    // blocks) or q30, q31, q0, q1 (half 1 of an even block)
+                    const int r2 = r & 3;  // (b & 1) << 1 | h
+                    const bool wrap = r2 == 1;
+                    const u32x2_t lo = __builtin_amdgcn_raw_buffer_load_b64(xr, wrap ? o[3] + 8 : o[3], 0, 0);
+                    const u32x2_t hi2 = __builtin_amdgcn_raw_buffer_load_b64(
+                        xr, wrap ? (live ? (uint32_t)((t / per_row) * K + k0 + 32 * (r >> 1)) * 4 : 0x80000000u)
+                                 : o[3] + 8, 0, 0);
+                    xv[c][12] = __uint_as_float(lo[0]); xv[c][13] = __uint_as_float(lo[1]);
+                    xv[c][14] = __uint_as_float(hi2[0]); xv[c][15] = __uint_as_float(hi2[1]);
+                } else {
+                    const float4 v = ldx16(xr, o[3]);
+                    xv[c][12] = v.x; xv[c][13] = v.y; xv[c][14] = v.z; xv[c][15] = v.w;
+                }
+            }
+        }
+    } else {
+        issue(rA);
+        issue(rB);
+    }
     {
         // zero what the slices may read past the split's last unit, and the partials
         const u32x4_t z = {0u, 0u, 0u, 0u};
@@ -224,17 +272,18 @@ __global__ __launch_bounds__(GV_THREADS, 1) void gemv_kernel(GemvArgs a)
             reinterpret_cast<u32x4_t*>(s_red)[i] = z;
         if (tid < GV_MISC_BYTES / 4) s_misc[tid] = 0.0f;
     }
-    __syncthreads();
     if constexpr (MODE == MODE_A) {
-        // power-of-two scale per row (over this split), then hi/lo f16 split
+        // power-of-two scale per row over this split, then the hi/lo f16 split
+        __syncthreads();
+        if (xw) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const int t = tid + GV_THREADS * c;
-            if (t < M * nb32) {
+            for (int c = 0; c < NTPT; ++c) {
+                if (64 * wave + GV_THREADS * c >= ntasks) break;
+                const int t = tid + GV_THREADS * c;
                 float am = 0.0f;
 #pragma unroll
-                for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(xv[c][i]));
-                atomicMax(reinterpret_cast<unsigned*>(&s_misc[16 + t / nb32]), __float_as_uint(am));
+                for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(xv[c][i]));
+                if (t < ntasks) atomicMax(reinterpret_cast<unsigned*>(&s_misc[16 + t / (ntasks / M)]), __float_as_uint(am));
             }
         }
         __syncthreads();
@@ -244,86 +293,103 @@ __global__ __launch_bounds__(GV_THREADS, 1) void gemv_kernel(GemvArgs a)
             s_misc[8 + tid] = ldexpf(1.0f, -e);
         }
         __syncthreads();
+    }
+    if (xw) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int c = 0; c < NTPT; ++c) {
+            if (64 * wave + GV_THREADS * c >= ntasks) break;
             const int t = tid + GV_THREADS * c;
-            if (t < M * nb32) {
-                const int m = t / nb32, b = t - m * nb32;  // b: matrix-core step (32 values) in this split
-                _Float16 hi[32], lo[32];
-                const float sum = split_chunk(xv[c], s_misc[m], hi, lo);
-                uint8_t* op = s_img + b * OPB;
+            const bool live = t < ntasks;
+            const int per_row = ntasks / M;
+            const int m = t / per_row, r = t - m * per_row;
+            if constexpr (MODE == MODE_A) {
+                const int b = r >> 2, kg = r & 3;
+                const float sc = s_misc[live ? m : 0];
+                half8_t vh, vl;
+                float sum = 0.0f;
 #pragma unroll
-                for (int kg = 0; kg < 4; ++kg) {
-                    half8_t vh, vl;
-#pragma unroll
-                    for (int u = 0; u < 8; ++u) {
-                        int k;
-                        if constexpr (FMT == FMT_Q8_0) {
-                            // even block of a pair: groups 0..2 take q[2+8kg ..], group 3 takes
-                            // q26..q31, q0, q1 (the weight side's dword layout); odd block: natural
-                            if (b & 1) k = 8 * kg + u;
-                            else k = kg < 3 ? 2 + 8 * kg + u : (u < 6 ? 26 + u : u - 6);
-                        } else {
-                            k = 8 * kg + nib_perm(u);
-                        }
-                        vh[u] = hi[k];
-                        vl[u] = lo[k];
-                    }
+                for (int u = 0; u < 8; ++u) {
+                    // Q4_K: the nibble decoder yields k-group elements in order {0,2,1,3,4,6,5,7}
+                    const int k = FMT == FMT_Q4_K ? nib_perm(u) : u;
+                    _Float16 h, l;
+                    float xs;
+                    split_one(xv[c][k], sc, h, l, xs);
+                    vh[u] = h;
+                    vl[u] = l;
+                    sum += xs;
+                }
+                if (live) {
+                    uint8_t* op = s_img + b * OPB;
                     *reinterpret_cast<half8_t*>(op + ((kg * 2) * MS + m) * 16) = vh;
                     *reinterpret_cast<half8_t*>(op + ((kg * 2 + 1) * MS + m) * 16) = vl;
                 }
-                if constexpr (FMT == FMT_Q4_K) {  // mins term: sum of x*2^e (hi rows; lo rows stay 0)
-                    s_scf[b * 2 * MS + m] = sum;
-                    s_scf[b * 2 * MS + MS + m] = 0.0f;
+                if constexpr (FMT == FMT_Q4_K) {  // mins term: sum of x*2^e over the 32 values (hi rows)
+                    sum += __shfl_xor(sum, 1);
+                    sum += __shfl_xor(sum, 2);
+                    if (live && kg == 0) {
+                        s_scf[b * 2 * MS + m] = sum;
+                        s_scf[b * 2 * MS + MS + m] = 0.0f;
+                    }
                 }
-            }
-        }
-    } else if constexpr (FMT == FMT_Q8_0) {
+            } else if constexpr (FMT == FMT_Q8_0) {
+                const int b = r >> 1, h = r & 1;
+                float am = 0.0f;
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const int t = tid + GV_THREADS * c;
-            if (t < M * nb32) {
-                const int m = t / nb32, b = t - m * nb32;
+                for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(xv[c][i]));
+                am = fmaxf(am, __shfl_xor(am, 1));  // the block's other half
+                float id, dval;
                 uint16_t dbits;
-                float dval;
-                int8_t q[32];
-                q8_0_block(xv[c], dbits, dval, q);
-                uint8_t* op = s_img + (b >> 1) * OPB;
-                if (!(b & 1)) {  // k-groups 0, 1 of rows 0..7: q2..q17 | q18..q31, q0, q1
-                    st16(op + m * 16, pack4(q[2], q[3], q[4], q[5]), pack4(q[6], q[7], q[8], q[9]),
-                         pack4(q[10], q[11], q[12], q[13]), pack4(q[14], q[15], q[16], q[17]));
-                    st16(op + (MS + m) * 16, pack4(q[18], q[19], q[20], q[21]), pack4(q[22], q[23], q[24], q[25]),
-                         pack4(q[26], q[27], q[28], q[29]), pack4(q[30], q[31], q[0], q[1]));
-                } else {  // k-groups 2, 3 of rows 8..15: q0..q15 | q16..q31
-                    st16(op + (2 * MS + m) * 16, pack4(q[0], q[1], q[2], q[3]), pack4(q[4], q[5], q[6], q[7]),
-                         pack4(q[8], q[9], q[10], q[11]), pack4(q[12], q[13], q[14], q[15]));
-                    st16(op + (3 * MS + m) * 16, pack4(q[16], q[17], q[18], q[19]), pack4(q[20], q[21], q[22], q[23]),
-                         pack4(q[24], q[25], q[26], q[27]), pack4(q[28], q[29], q[30], q[31]));
-                }
-                s_scf[(b >> 1) * 2 * MS + (b & 1) * MS + m] = dval;
-            }
-        }
-    } else {
+                q8_0_scale(am, id, dbits, dval);
+                int q[16];
 #pragma unroll
-        for (int c = 0; c < 16; ++c) {
-            const int t = wave + GV_WAVES * c;
-            if (t < M * lu_cnt) {
-                const int m = t / lu_cnt, sb = t - m * lu_cnt;
-                const float xs[4] = {xq[c].x, xq[c].y, xq[c].z, xq[c].w};
-                float d;
-                int q[4], s16;
-                q8k_wave(xs, lane, d, q, s16);
-                // element e = 4*lane: sub-block j, position tt; step 2*(j/4) + j%2 holds sub-blocks
-                // (4cc+h) in rows 0..7 and (4cc+2+h) in rows 8..15
-                const int e = 4 * lane, j = e >> 5, tt = e & 31;
-                const int isb = (j >> 1) & 1, op = 2 * (j >> 2) + (j & 1);
-                *reinterpret_cast<uint32_t*>(s_img + (sb * 4 + op) * OPB + ((isb * 2 + (tt >> 4)) * MS + m) * 16 +
-                                             (tt & 15)) = pack4(q[0], q[1], q[2], q[3]);
-                if (lane == 0) s_scf[sb * 9 * MS + m] = d;
-                const int pr = s16 + __shfl_down(s16, 4);
-                if ((lane & 7) == 0) s_sci[sb * 9 * MS + MS + (lane >> 3) * MS + m] = pr;
+                for (int i = 0; i < 16; ++i) q[i] = q8_0_q(xv[c][i], id);
+                if (live) {
+                    const int par = b & 1;
+                    *reinterpret_cast<u32x4_t*>(s_img + (b >> 1) * OPB + ((par * 2 + h) * MS + m) * 16) =
+                        u32x4_t{pack4(q[0], q[1], q[2], q[3]), pack4(q[4], q[5], q[6], q[7]),
+                                pack4(q[8], q[9], q[10], q[11]), pack4(q[12], q[13], q[14], q[15])};
+                    if (h == 0) s_scf[(b >> 1) * 2 * MS + par * MS + m] = dval;
+                }
+            } else {
+                const int sb = r >> 4, sl16 = r & 15;
+                // the super-block's signed element of largest |x|, first index on ties
+                float best = -1.0f, bv = 0.0f;
+                int bi = 0;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float av = fabsf(xv[c][i]);
+                    if (av > best) { best = av; bv = xv[c][i]; bi = 16 * sl16 + i; }
+                }
+#pragma unroll
+                for (int off = 1; off < 16; off <<= 1) {
+                    const float ob = __shfl_xor(best, off), ov = __shfl_xor(bv, off);
+                    const int oi = __shfl_xor(bi, off);
+                    if (q8k_better(ob, oi, best, bi)) { best = ob; bv = ov; bi = oi; }
+                }
+                float iscale, d;
+                q8k_scale(bv, best, iscale, d);
+                int q[16], s16 = 0;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    q[i] = q8k_q(xv[c][i], iscale);
+                    s16 += q[i];
+                }
+                const int pr = s16 + __shfl_xor(s16, 1);  // the sub-block's two halves
+                if (live) {
+                    // slot sl16 = sub-block j (two halves); step 2*(j/4) + j%2 holds sub-blocks
+                    // (4cc+h) in rows 0..7 and (4cc+2+h) in rows 8..15
+                    const int j = sl16 >> 1, half = sl16 & 1;
+                    const int isb = (j >> 1) & 1, op = 2 * (j >> 2) + (j & 1);
+                    *reinterpret_cast<u32x4_t*>(s_img + (sb * 4 + op) * OPB + ((isb * 2 + half) * MS + m) * 16) =
+                        u32x4_t{pack4(q[0], q[1], q[2], q[3]), pack4(q[4], q[5], q[6], q[7]),
+                                pack4(q[8], q[9], q[10], q[11]), pack4(q[12], q[13], q[14], q[15])};
+                    if (sl16 == 0) s_scf[sb * 9 * MS + m] = d;
+                    if (half == 0) s_sci[sb * 9 * MS + MS + j * MS + m] = pr;
+                }
             }
         }
+        issue(rA);
+        issue(rB);
     }
     __syncthreads();
 
