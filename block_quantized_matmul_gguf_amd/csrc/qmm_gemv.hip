@@ -38,8 +38,9 @@ namespace qmm {
 constexpr int GV_WAVES = 8;
 constexpr int GV_THREADS = 64 * GV_WAVES;
 constexpr int GV_XMAX = 64 * GV_THREADS;  // activation values one workgroup prepares (64 per thread)
-constexpr int GV_GPW_MAX = 4;             // tile groups per workgroup
+constexpr int GV_GPW_MAX = 16;            // tile groups per workgroup
 constexpr int GV_RED = 128;               // floats per (tile, slice) partial: 8 rows x 16 columns
+constexpr int GV_RED_BYTES = GV_WAVES * GV_RED * 4;  // partials of one tile group
 constexpr int GV_MISC_BYTES = 128;
 constexpr int GV_LDS_MAX = 160 * 1024;
 
@@ -150,8 +151,11 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
     const int ngrp = min(a.gpw, a.groups - grp0);
     const int sl_lu0 = sl * a.slice;                          // first unit of this wave's slice
     const int sl_real = max(0, min(a.slice, lu_cnt - sl_lu0));
-    const int S = (sl_real + P - 1) / P;                      // stages per tile
-    const int Q = ngrp * S;                                   // stages this wave streams
+    // every wave runs S stages per tile, so the waves reach each tile's end together;
+    // the stages of a short last slice past its real units load nothing
+    const int S = a.slice / P;
+    const int S_real = (sl_real + P - 1) / P;
+    const int Q = ngrp * S;                                   // stages per wave
     uint8_t* stg = lds + a.stg_off + wave * (16 * RS);
 
     // ---- the weight stream: chunk f = 64t + lane of a stage is row f/CPR, chunk f%CPR ----
@@ -166,7 +170,7 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
 
     int iq = 0, iu = 0, is = 0;  // next stage to queue: index, tile, stage within the tile
     auto issue = [&](u32x4_t (&r)[T]) {
-        const bool real = iq < Q;
+        const bool real = iq < Q && is < S_real;
         const int tile = (grp0 + iu) * a.G + tg;
         const int64_t t0 = (int64_t)tile * 16 * a.row_bytes;
         const int64_t left = a.w_bytes - t0;
@@ -268,8 +272,7 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
             reinterpret_cast<u32x4_t*>(s_img)[i] = z;
         if constexpr (SCB > 0)
             for (int i = lu_cnt * SCB / 4 + tid; i < lu_img * SCB / 4; i += GV_THREADS) s_sci[i] = 0;
-        for (int i = tid; i < (a.misc_off - a.red_off) / 16; i += GV_THREADS)
-            reinterpret_cast<u32x4_t*>(s_red)[i] = z;
+        for (int i = tid; i < GV_RED_BYTES / 16; i += GV_THREADS) reinterpret_cast<u32x4_t*>(s_red)[i] = z;
         if (tid < GV_MISC_BYTES / 4) s_misc[tid] = 0.0f;
     }
     if constexpr (MODE == MODE_A) {
@@ -563,24 +566,45 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
         }
     };
 
-    int cq = 0, cu = 0, cs = 0;  // next stage to compute: index, tile, stage within the tile
+    int cq = 0, cu = 0, cs = 0;  // next stage to compute: index, tile group, stage within the tile
     auto step = [&](u32x4_t (&r)[T]) {
         if (cq < Q) {
-            // land the stage in this wave's LDS buffer (the gather below reads other lanes' chunks)
+            if (cs < S_real) {
+                // land the stage in this wave's LDS buffer (the gather below reads other lanes' chunks)
 #pragma unroll
-            for (int t = 0; t < T; ++t)
-                if (t < T - 1 || lane < TAIL) *reinterpret_cast<u32x4_t*>(stg + lw[t]) = r[t];
-            const int tile = (grp0 + cu) * a.G + tg;
-            compute(sl_lu0 + cs * P, tile);
-            if (cs == S - 1) {  // tile done: fold the two lane halves, park the partial in LDS
+                for (int t = 0; t < T; ++t)
+                    if (t < T - 1 || lane < TAIL) *reinterpret_cast<u32x4_t*>(stg + lw[t]) = r[t];
+                compute(sl_lu0 + cs * P, (grp0 + cu) * a.G + tg);
+            }
+            if (cs == S - 1) {
+                // the tile group is done in every wave: fold the two lane halves, park the
+                // partials in LDS, sum the slices, and free the buffer for the next group
+                float* red = s_red;
 #pragma unroll
                 for (int q = 0; q < R; ++q) acc[q] += __shfl_xor(acc[q], 32);
                 if (lane < 32) {
-                    float* o = s_red + ((cu * a.G + tg) * a.kw + sl) * GV_RED + 4 * (lane >> 4) * 16 + n;
+                    float* o = red + (tg * a.kw + sl) * GV_RED + 4 * (lane >> 4) * 16 + n;
 #pragma unroll
                     for (int q = 0; q < R; ++q) o[16 * q] = acc[q];
                 }
                 acc = zf;
+                __syncthreads();
+                if constexpr (!EMIT) {
+                    const int per = 16 * M;
+                    for (int i = tid; i < a.G * per; i += GV_THREADS) {
+                        const int t = i / per, rem = i - t * per, m = rem >> 4, nn = rem & 15;
+                        const int ng = ((grp0 + cu) * a.G + t) * 16 + nn;
+                        if (ng < N) {
+                            const float* p = red + t * a.kw * GV_RED + m * 16 + nn;
+                            float v = 0.0f;
+                            for (int sl2 = 0; sl2 < a.kw; ++sl2) v += p[sl2 * GV_RED];
+                            if constexpr (MODE == MODE_A) v *= s_misc[8 + m];
+                            if (a.ks == 1) a.y[(int64_t)m * N + ng] = v;
+                            else a.part[((int64_t)split * GEMV_MAX_M + m) * N + ng] = v;
+                        }
+                    }
+                }
+                __syncthreads();
             }
         }
         ++cq;
@@ -590,25 +614,6 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
     for (int q = 0; q < Q; q += 2) {
         step(rA);
         step(rB);
-    }
-    __syncthreads();
-
-    // ---- sum the slices of every tile and write ----
-    if constexpr (!EMIT) {
-        const int per = 16 * M, nout = ngrp * a.G * per;
-        for (int i = tid; i < nout; i += GV_THREADS) {
-            const int slot = i / per, rem = i - slot * per, m = rem >> 4, nn = rem & 15;
-            const int u = slot / a.G, t = slot - u * a.G;
-            const int ng = ((grp0 + u) * a.G + t) * 16 + nn;
-            if (ng < N) {
-                const float* p = s_red + slot * a.kw * GV_RED + m * 16 + nn;
-                float v = 0.0f;
-                for (int s = 0; s < a.kw; ++s) v += p[s * GV_RED];
-                if constexpr (MODE == MODE_A) v *= s_misc[8 + m];
-                if (a.ks == 1) a.y[(int64_t)m * N + ng] = v;
-                else a.part[((int64_t)split * GEMV_MAX_M + m) * N + ng] = v;
-            }
-        }
     }
 }
 
@@ -637,17 +642,20 @@ static GvKernel gv_pick_r(int R, bool emit)
 }
 
 // Stage sizes (load units) compiled for each format.
-static const int kStageQ8[3] = {4, 3, 1};
-static const int kStageQ4[3] = {2, 3, 1};
+static const int kStageQ8[] = {4, 3, 2, 1};
+static const int kStageQ4[] = {2, 3, 1};
+static const int kNStageQ8 = 4, kNStageQ4 = 3;
 
 static GvKernel gv_kernel(int fmt, int mode, int P, int R, bool emit)
 {
     if (fmt == FMT_Q8_0) {
         if (mode == MODE_A) return P == 4 ? gv_pick_r<FMT_Q8_0, MODE_A, 4>(R, false)
                                    : P == 3 ? gv_pick_r<FMT_Q8_0, MODE_A, 3>(R, false)
+                                   : P == 2 ? gv_pick_r<FMT_Q8_0, MODE_A, 2>(R, false)
                                             : gv_pick_r<FMT_Q8_0, MODE_A, 1>(R, false);
         return P == 4 ? gv_pick_r<FMT_Q8_0, MODE_B, 4>(R, emit)
              : P == 3 ? gv_pick_r<FMT_Q8_0, MODE_B, 3>(R, emit)
+             : P == 2 ? gv_pick_r<FMT_Q8_0, MODE_B, 2>(R, emit)
                       : gv_pick_r<FMT_Q8_0, MODE_B, 1>(R, emit);
     }
     if (mode == MODE_A) return P == 2 ? gv_pick_r<FMT_Q4_K, MODE_A, 2>(R, false)
@@ -698,7 +706,7 @@ static int gemv_splits(int fmt, int mode, int64_t K, int M, int ms, int& lus_spl
     gv_fmt(fmt, mode, ms, lub, ops, vpl, opb, scb);
     const int64_t nlu = K / vpl;
     const int64_t per_lu = (int64_t)ops * opb + scb;
-    const int64_t room = GV_LDS_MAX - GV_WAVES * GV_RED * 4 - GV_MISC_BYTES - stage_bytes(fmt, 1);
+    const int64_t room = GV_LDS_MAX - GV_RED_BYTES - GV_MISC_BYTES - stage_bytes(fmt, 1);
     const int64_t lus_max = std::max<int64_t>(1, std::min<int64_t>(room / per_lu, GV_XMAX / ((int64_t)M * vpl)));
     const int64_t ks = (nlu + lus_max - 1) / lus_max;
     lus_split = (int)((nlu + ks - 1) / ks);
@@ -730,9 +738,10 @@ GemvGeom gemv_geom(int fmt, int mode, int64_t N, int64_t K, int M, bool emit)
     g.tiles = (int)((N + 15) / 16);
     g.ks = gemv_splits(fmt, mode, K, M, ms, g.lus_split);
     const int* stages = fmt == FMT_Q8_0 ? kStageQ8 : kStageQ4;
+    const int nstages = fmt == FMT_Q8_0 ? kNStageQ8 : kNStageQ4;
     int64_t best = -1;
     for (int kw = 1; kw <= GV_WAVES; kw *= 2) {
-        for (int si = 0; si < 3; ++si) {
+        for (int si = 0; si < nstages; ++si) {
             const int P = stages[si];
             if (emit && P != 1) continue;
             const int raw = (g.lus_split + kw - 1) / kw;
@@ -743,15 +752,11 @@ GemvGeom gemv_geom(int fmt, int mode, int64_t N, int64_t K, int M, bool emit)
             const int img = kw * slice * ops * opb;
             const int sc = kw * slice * scb;
             const int stg = stage_bytes(fmt, P);
-            const int fixed = img + sc + GV_MISC_BYTES + stg;  // plus 4 KB of partials per tile group
-            const int gpw_cap = std::min(GV_GPW_MAX, (GV_LDS_MAX - fixed) / (GV_WAVES * GV_RED * 4));
-            if (gpw_cap < 1) continue;
+            const int lds = img + sc + GV_RED_BYTES + GV_MISC_BYTES + stg;
+            if (lds > GV_LDS_MAX) continue;
             // fewest tile groups per workgroup that keep every workgroup resident at once
-            const GvKernel kern = gv_kernel(fmt, mode, P, g.R, emit);
-            int gpw = 1;
-            while (gpw < gpw_cap &&
-                   (int64_t)groups * g.ks > (int64_t)gpw * resident_wgs(kern, fixed + gpw * GV_WAVES * GV_RED * 4))
-                ++gpw;
+            const int rwg = resident_wgs(gv_kernel(fmt, mode, P, g.R, emit), lds);
+            const int gpw = (int)std::min<int64_t>(GV_GPW_MAX, ((int64_t)groups * g.ks + rwg - 1) / rwg);
             // bytes the busiest wave loads (whole 16-byte chunks) plus a per-stage overhead
             const int cpr = fmt == FMT_Q8_0 ? gv_cpr(FMT_Q8_0, P) : gv_cpr(FMT_Q4_K, P);
             const int64_t cost = (int64_t)gpw * (slice / P) * (256 * cpr + 512);
@@ -766,9 +771,9 @@ GemvGeom gemv_geom(int fmt, int mode, int64_t N, int64_t K, int M, bool emit)
                 g.rs = fmt == FMT_Q8_0 ? gv_rs(FMT_Q8_0, P) : gv_rs(FMT_Q4_K, P);
                 g.sc_off = img;
                 g.red_off = img + sc;
-                g.misc_off = g.red_off + gpw * GV_WAVES * GV_RED * 4;
+                g.misc_off = g.red_off + GV_RED_BYTES;
                 g.stg_off = g.misc_off + GV_MISC_BYTES;
-                g.lds = g.stg_off + stg;
+                g.lds = lds;
                 g.grid = g.ks * ((groups + gpw - 1) / gpw);
             }
         }
