@@ -29,6 +29,7 @@
 #include <algorithm>
 #include <map>
 #include <mutex>
+#include <set>
 #include <utility>
 
 #include "qmm_act.h"
@@ -122,6 +123,22 @@ QMM_DEV uint32_t lds32(const uint8_t* p) { return *reinterpret_cast<const uint32
 QMM_DEV u32x2_t lds64(const uint8_t* p) { return *reinterpret_cast<const u32x2_t*>(p); }
 QMM_DEV u32x4_t lds128(const uint8_t* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 
+// Workgroup counters in LDS that let some waves wait for others without a
+// full barrier (waves still queueing weight loads do not hold the rest up).
+// The wait is bounded, so a wave can never spin forever.
+QMM_DEV void wg_signal(int* c, bool release)
+{
+    if (release) __hip_atomic_fetch_add(c, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    else __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+QMM_DEV void wg_wait(int* c, int target)
+{
+    for (int spin = 0; spin < (1 << 22); ++spin) {
+        if (__hip_atomic_load(c, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
 // R: activation rows per lane the arithmetic covers (1 when M == 1, else 4:
 // lane l holds output rows 4*(l/16 % 2) + r of its tile column l%16).
 template <int FMT, int MODE, int P, int R, bool EMIT>
@@ -194,7 +211,9 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
     constexpr int NTPT = MODE == MODE_A ? 8 : 4;  // tasks per thread at most (64 values)
     const int nb32 = lu_cnt * (VPL / 32);         // 32-value blocks in this split
     const int ntasks = MODE == MODE_A ? M * nb32 * 4 : (FMT == FMT_Q8_0 ? M * nb32 * 2 : M * lu_cnt * 16);
-    const bool xw = 64 * wave < ntasks;
+    const int npw = min(GV_WAVES, (ntasks + 63) / 64);  // waves with tasks (the first npw)
+    const bool xw = wave < npw;
+    int* s_sync = reinterpret_cast<int*>(s_misc) + 24;  // row maxima in, operand ready
     const rsrc_t xr = make_rsrc(a.x, (uint32_t)(M * K * 4));
     const int k0 = lu_beg * VPL;
     float xv[NTPT][VT];
@@ -260,42 +279,47 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
                 }
             }
         }
+    }
+    // the barrier orders every x load before any weight load, so x is not stuck behind the stream
+    if (tid < GV_MISC_BYTES / 4) s_misc[tid] = 0.0f;
+    __syncthreads();
+    if (xw) {
+        // zero what the slices may read past the split's last unit, and the partials
+        const u32x4_t z = {0u, 0u, 0u, 0u};
+        const int lu_img = a.kw * a.slice, pthreads = 64 * npw;
+        for (int i = lu_cnt * OPS * OPB / 16 + tid; i < lu_img * OPS * OPB / 16; i += pthreads)
+            reinterpret_cast<u32x4_t*>(s_img)[i] = z;
+        if constexpr (SCB > 0)
+            for (int i = lu_cnt * SCB / 4 + tid; i < lu_img * SCB / 4; i += pthreads) s_sci[i] = 0;
+        for (int i = tid; i < GV_RED_BYTES / 16; i += pthreads) reinterpret_cast<u32x4_t*>(s_red)[i] = z;
     } else {
         issue(rA);
         issue(rB);
     }
-    {
-        // zero what the slices may read past the split's last unit, and the partials
-        const u32x4_t z = {0u, 0u, 0u, 0u};
-        const int lu_img = a.kw * a.slice;
-        for (int i = lu_cnt * OPS * OPB / 16 + tid; i < lu_img * OPS * OPB / 16; i += GV_THREADS)
-            reinterpret_cast<u32x4_t*>(s_img)[i] = z;
-        if constexpr (SCB > 0)
-            for (int i = lu_cnt * SCB / 4 + tid; i < lu_img * SCB / 4; i += GV_THREADS) s_sci[i] = 0;
-        for (int i = tid; i < GV_RED_BYTES / 16; i += GV_THREADS) reinterpret_cast<u32x4_t*>(s_red)[i] = z;
-        if (tid < GV_MISC_BYTES / 4) s_misc[tid] = 0.0f;
-    }
     if constexpr (MODE == MODE_A) {
-        // power-of-two scale per row over this split, then the hi/lo f16 split
-        __syncthreads();
+        // power-of-two scale per row over this split, then the hi/lo f16 split; a wave
+        // whose tasks share a row reduces its maximum first (one LDS atomic per wave)
         if (xw) {
+            const int per_row = ntasks / M;
 #pragma unroll
             for (int c = 0; c < NTPT; ++c) {
                 if (64 * wave + GV_THREADS * c >= ntasks) break;
-                const int t = tid + GV_THREADS * c;
+                const int t = tid + GV_THREADS * c, t0 = 64 * wave + GV_THREADS * c;
                 float am = 0.0f;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(xv[c][i]));
-                if (t < ntasks) atomicMax(reinterpret_cast<unsigned*>(&s_misc[16 + t / (ntasks / M)]), __float_as_uint(am));
+                const int m0 = t0 / per_row;
+                if (min(t0 + 63, ntasks - 1) / per_row == m0) {
+#pragma unroll
+                    for (int off = 32; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
+                    if (lane == 0) atomicMax(reinterpret_cast<unsigned*>(&s_misc[16 + m0]), __float_as_uint(am));
+                } else if (t < ntasks) {
+                    atomicMax(reinterpret_cast<unsigned*>(&s_misc[16 + t / per_row]), __float_as_uint(am));
+                }
             }
+            if (lane == 0) wg_signal(&s_sync[1], true);
+            wg_wait(&s_sync[1], npw);
         }
-        __syncthreads();
-        if (tid < GEMV_MAX_M) {
-            const int e = split_exp(__uint_as_float(reinterpret_cast<unsigned*>(s_misc)[16 + tid]));
-            s_misc[tid] = ldexpf(1.0f, e);
-            s_misc[8 + tid] = ldexpf(1.0f, -e);
-        }
-        __syncthreads();
     }
     if (xw) {
 #pragma unroll
@@ -307,7 +331,7 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
             const int m = t / per_row, r = t - m * per_row;
             if constexpr (MODE == MODE_A) {
                 const int b = r >> 2, kg = r & 3;
-                const float sc = s_misc[live ? m : 0];
+                const float sc = ldexpf(1.0f, split_exp(__uint_as_float(reinterpret_cast<const unsigned*>(s_misc)[16 + (live ? m : 0)])));
                 half8_t vh, vl;
                 float sum = 0.0f;
 #pragma unroll
@@ -391,10 +415,11 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
                 }
             }
         }
+        if (lane == 0) wg_signal(&s_sync[2], true);  // this wave's slots are written
         issue(rA);
         issue(rB);
     }
-    __syncthreads();
+    wg_wait(&s_sync[2], npw);  // the whole operand is in place
 
     // ---- main loop ----
     // activation operand of this lane: slot, and a mask for structurally zero rows
@@ -598,7 +623,8 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
                             const float* p = red + t * a.kw * GV_RED + m * 16 + nn;
                             float v = 0.0f;
                             for (int sl2 = 0; sl2 < a.kw; ++sl2) v += p[sl2 * GV_RED];
-                            if constexpr (MODE == MODE_A) v *= s_misc[8 + m];
+                            if constexpr (MODE == MODE_A)
+                                v *= ldexpf(1.0f, -split_exp(__uint_as_float(reinterpret_cast<const unsigned*>(s_misc)[16 + m])));
                             if (a.ks == 1) a.y[(int64_t)m * N + ng] = v;
                             else a.part[((int64_t)split * GEMV_MAX_M + m) * N + ng] = v;
                         }
@@ -666,25 +692,33 @@ static GvKernel gv_kernel(int fmt, int mode, int P, int R, bool emit)
                   : gv_pick_r<FMT_Q4_K, MODE_B, 1>(R, emit);
 }
 
-// Workgroups of one kernel resident at once on the current device with `lds`
-// bytes of LDS each (CUs x workgroups per CU), cached.
-static int resident_wgs(GvKernel k, int lds)
+// Compute units of the current device, cached per device.
+static int device_cus()
 {
-    static std::map<std::pair<std::pair<int, const void*>, int>, int> cache;
+    static std::map<int, int> cache;
     static std::mutex mu;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) dev = 0;
     std::lock_guard<std::mutex> lock(mu);
-    const auto key = std::make_pair(std::make_pair(dev, (const void*)k), lds);
-    auto it = cache.find(key);
+    auto it = cache.find(dev);
     if (it != cache.end()) return it->second;
-    (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, GV_LDS_MAX);
-    int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, GV_THREADS, lds) != hipSuccess || per_cu < 1)
-        per_cu = 1;
+    int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 1;
     (void)hipGetLastError();
-    return cache[key] = per_cu * cus;
+    return cache[dev] = cus;
+}
+
+// Raises a kernel's dynamic LDS limit to the full 160 KB, once per device.
+static void allow_full_lds(GvKernel k)
+{
+    static std::set<std::pair<int, const void*>> done;
+    static std::mutex mu;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!done.insert(std::make_pair(dev, (const void*)k)).second) return;
+    (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, GV_LDS_MAX);
+    (void)hipGetLastError();
 }
 
 // ------------------------------------------------------------- geometry ----
@@ -723,9 +757,12 @@ int gemv_max_splits(int fmt, int64_t K)
 }
 
 // Geometry of one run: K splits, waves per tile (kw), stage size (P) and tile
-// groups per workgroup, chosen to minimise the bytes the busiest wave loads
-// (plus a per-stage overhead) with every workgroup resident at once; ties go
-// to larger stages, then to fewer waves per tile.
+// groups per workgroup (gpw), chosen to minimise the work of the busiest
+// compute unit: the workgroups it runs times (the prologue, which loads and
+// prepares the activations once per workgroup, plus the busiest wave's stages,
+// priced by the 16-byte chunks they load plus a fixed overhead).  The prologue
+// term makes one workgroup per compute unit beat two half-sized ones.  Ties go
+// to larger stages, then to fewer waves per tile, then to more workgroups.
 GemvGeom gemv_geom(int fmt, int mode, int64_t N, int64_t K, int M, bool emit)
 {
     GemvGeom g{};
@@ -739,6 +776,9 @@ GemvGeom gemv_geom(int fmt, int mode, int64_t N, int64_t K, int M, bool emit)
     g.ks = gemv_splits(fmt, mode, K, M, ms, g.lus_split);
     const int* stages = fmt == FMT_Q8_0 ? kStageQ8 : kStageQ4;
     const int nstages = fmt == FMT_Q8_0 ? kNStageQ8 : kNStageQ4;
+    const int64_t cus = device_cus();
+    // prologue price: a fixed part plus one unit per activation value it prepares
+    const int64_t pro = 8192 + (int64_t)M * g.lus_split * vpl;
     int64_t best = -1;
     for (int kw = 1; kw <= GV_WAVES; kw *= 2) {
         for (int si = 0; si < nstages; ++si) {
@@ -754,13 +794,12 @@ GemvGeom gemv_geom(int fmt, int mode, int64_t N, int64_t K, int M, bool emit)
             const int stg = stage_bytes(fmt, P);
             const int lds = img + sc + GV_RED_BYTES + GV_MISC_BYTES + stg;
             if (lds > GV_LDS_MAX) continue;
-            // fewest tile groups per workgroup that keep every workgroup resident at once
-            const int rwg = resident_wgs(gv_kernel(fmt, mode, P, g.R, emit), lds);
-            const int gpw = (int)std::min<int64_t>(GV_GPW_MAX, ((int64_t)groups * g.ks + rwg - 1) / rwg);
-            // bytes the busiest wave loads (whole 16-byte chunks) plus a per-stage overhead
             const int cpr = fmt == FMT_Q8_0 ? gv_cpr(FMT_Q8_0, P) : gv_cpr(FMT_Q4_K, P);
-            const int64_t cost = (int64_t)gpw * (slice / P) * (256 * cpr + 512);
-            if (best < 0 || cost < best || (cost == best && P > g.P)) {
+            const int64_t loop = (int64_t)(slice / P) * (256 * cpr + 512);
+            for (int gpw = 1; gpw <= GV_GPW_MAX; ++gpw) {
+                const int64_t grid = (int64_t)g.ks * ((groups + gpw - 1) / gpw);
+                const int64_t cost = (grid + cus - 1) / cus * (pro + gpw * loop);
+                if (best >= 0 && !(cost < best || (cost == best && P > g.P))) continue;
                 best = cost;
                 g.kw = kw;
                 g.slice = slice;
@@ -813,7 +852,7 @@ hipError_t launch_gemv(int fmt, int mode, const void* w, const float* x, int64_t
     a.y = y;
     a.sums = sums;
     GvKernel k = gv_kernel(fmt, mode, g.P, g.R, emit);
-    (void)resident_wgs(k, g.lds);  // sets the kernel's LDS limit on this device
+    allow_full_lds(k);
     void* args[] = {&a};
     hipError_t e = hipLaunchKernel((const void*)k, dim3(g.grid), dim3(GV_THREADS), args, g.lds, s);
     if (e != hipSuccess) return e;
