@@ -119,9 +119,11 @@ static size_t layout(qmm_plan* p, char* base)
     if (p->M_max > GEMV_MAX_M) {
         const int64_t M = p->M_max;
         p->gm.a0 = (_Float16*)take(2 * M * K);
-        p->gm.a1 = (_Float16*)take(a ? 2 * M * K : 0);
-        p->gm.sc0 = (float*)take(a ? 4 * M : 4 * M * units);
-        p->gm.sc1 = take(q4 ? 4 * M * (K / 32) : 0);
+        p->gm.a1 = (_Float16*)take(2 * M * K);
+        p->gm.rs = (float*)take(4 * M);
+        p->gm.xs = (_Float16*)take(q4 ? 2 * M * (K / 256) * 16 : 0);
+        p->gm.sd = (float*)take(a ? 0 : 4 * M * units);
+        p->gm.sbs = (int32_t*)take(q4 && !a ? 4 * M * (K / 32) : 0);
     } else {
         p->gm = GemmBufs{};
     }
@@ -206,7 +208,7 @@ static int run_impl(const qmm_plan* p, const void* w, const float* x, float* y, 
     if (M <= GEMV_MAX_M) {
         e = launch_gemv(p->fmt, p->mode, w, x, p->N, p->K, (int)M, p->gv, y, sums, s);
     } else {
-        e = launch_gemm_prep(p->fmt, p->mode, x, M, p->K, p->gm, s);
+        e = launch_gemm_prep(p->fmt, p->mode, x, M, p->K, p->gm, sums != nullptr, s);
         if (e == hipSuccess) e = launch_gemm(p->fmt, p->mode, w, p->N, p->K, M, p->gm, y, sums, s);
     }
     if (e != hipSuccess) return fail(QMM_EHIP, "kernel launch: %s", hipGetErrorString(e));

@@ -15,6 +15,14 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 #define QMM_DEV __device__ __forceinline__
 
+// Raw buffer resource over `bytes` bytes from `base`: loads at offsets past
+// the end return zeros.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+QMM_DEV rsrc_t make_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 QMM_DEV float f16lo(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xffffu)); }
 QMM_DEV float f16hi(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16)); }
 QMM_DEV uint16_t f16bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }

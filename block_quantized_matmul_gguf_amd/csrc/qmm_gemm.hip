@@ -1,20 +1,38 @@
 // qmm_gemm.hip -- prefill kernel (M > 8) for y = x . W^T on GGUF blocks.
 //
-// 128x128 output tile per 256-thread workgroup; each wave owns 64x64 as 2x2
-// v_mfma_f32_32x32x16_f16 tiles.  K advances 64 values per stage: the weight
-// rows of the stage are decoded once into LDS as exact f16 integers (Q8_0: q;
-// Q4_K: sc_j*q <= 945), shared by all waves; the next stage's raw bytes are
-// prefetched into registers while the current one computes.
-//   mode (a): activations arrive as an exact f16 hi/lo split of a power-of-two
-//     scaled row (two MFMA passes); per-block f32 epilogue acc += d*C (Q8_0
-//     every 32 values; Q4_K once per 256 with the mins term
-//     -dmin*sum_j m_j*sum(x over sub-block j));
-//   mode (b): activations arrive as their quantized integers in f16; the MFMA
-//     sums are exact integers (Q8_0 block sums |S| <= 516128; Q4_K half
-//     super-block sums of sc_j*q*q8 < 2^24), scaled in f32: Q8_0 acc +=
-//     dw*dx*S per block, Q4_K acc += dx*d*sumi per 128 values and
-//     -dx*dmin*summins per super-block (page "同一个 GGUF，CPU 和 Metal
-//     生成的文字不一样", section 出处: integer dot, then the scales).
+// Every (format, mode) pair runs one contraction on the matrix cores.  The
+// activation row, scaled by the power of two s that puts its largest value in
+// [2^14, 2^15), enters as an f16 pair hi + lo: in mode (a) x*s itself, in
+// mode (b) the dequantized quantized activation d_x*q_x*s (page "同一个
+// GGUF，CPU 和 Metal 生成的文字不一样", section 出处: the CPU path quantizes
+// the activations, then takes integer block dots scaled by both block
+// scales).  A Q8_0 activation d_x*q_x (an f16 scale times a 7-bit integer) is
+// exact in the pair, so mode (b) reaches sum_b d_w*d_x*S_b with only f32
+// accumulation rounding.  The weights enter as exact f16 integers (Q8_0: q;
+// Q4_K: sc_j*q <= 945).  Two v_mfma_f32_16x16x32_f16 passes (hi, lo) per 32
+// values give sum q*x*s; the weight scales follow in f32:
+//   Q8_0: acc += d * C after every 32-value block;
+//   Q4_K: acc += d * C - dmin * Cmin after every super-block, where
+//         Cmin = sum_j m_j * (s * sum of x over sub-block j) is one more MFMA
+//         whose 32-deep operands hold the eight sub-block sums' hi parts and
+//         lo parts against m_j twice.
+// y = acc / s.
+//
+// A 256-thread workgroup owns a (32*TM) x (32*TN) output tile, four waves in
+// 2 x 2, each (16*TM) x (16*TN) as TM x TN MFMA tiles.  K advances 64 values
+// per stage through two LDS buffers: while a stage computes, the next stage's
+// activation pairs and raw weight bytes are in flight to registers; after the
+// compute they are decoded (weights to exact f16) into the other buffer, and
+// one barrier per stage hands it over.
+//
+// The block-sums test hook (mode (b), integer sums out) keeps its own kernel,
+// gemm_sums_kernel, which runs the MFMA on the quantized integers.
+#include <map>
+#include <mutex>
+#include <set>
+#include <type_traits>
+#include <utility>
+
 #include "qmm_device.h"
 
 namespace qmm {
@@ -23,329 +41,691 @@ struct GemmArgs {
     const uint8_t* w;
     int64_t row_bytes;
     int N, K, M;
-    const _Float16* a0;
-    const _Float16* a1;
-    const float* sc0;
-    const void* sc1;
+    int nm;              // row blocks of the output (tiles along M)
+    int remap;           // 1: give each XCD a contiguous run of tiles
+    const _Float16* hi;
+    const _Float16* lo;
+    const float* rs;     // 1/s per row
+    const _Float16* xs;  // Q4_K: [M][K/256][16] sub-block sums * s / 32, hi then lo
     float* y;
-    int32_t* sums;
 };
 
-constexpr int LDA = GEMM_KS + 8;  // halves per LDS row (16-byte pad against bank conflicts)
+// LDS rows hold 64 values (128 bytes) as 8 chunks of 16 bytes; chunk c of row
+// r sits in slot c ^ (r & 7), so that the 16-byte MFMA operand reads and the
+// 16-byte staging writes hit distinct banks.
+constexpr int G_ROW = 128;
+QMM_DEV uint32_t swz(int row, int chunk) { return (uint32_t)(row * G_ROW + ((chunk ^ (row & 7)) << 4)); }
 
-template <int FMT, int MODE, bool EMIT>
-__global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a)
+// WM x WN waves, each owning TM x TN tiles of 16 x 16 outputs.
+template <int FMT, int WM, int WN, int TM, int TN>
+struct GemmCfg {
+    static constexpr int NT = 64 * WM * WN;
+    static constexpr int BM = 16 * TM * WM, BN = 16 * TN * WN;
+    static constexpr int A_HALF = BM * G_ROW;  // hi (or lo) of one stage, bytes
+    static constexpr int A_BYTES = 2 * A_HALF;
+    static constexpr int B_BYTES = BN * G_ROW;
+    static constexpr int OFF_B = 2 * A_BYTES;
+    static constexpr int OFF_S = OFF_B + 2 * B_BYTES;
+    // Q8_0: block scales [2 stages][2 blocks][BN] f32.
+    // Q4_K, by super-block parity: {d, dmin, -, -} [2][BN] (16 B each), 32*m_j
+    // [2][BN][8] f16, activation sub-block sums [2][BM][16] f16.
+    static constexpr int OFF_DD = OFF_S;
+    static constexpr int OFF_MJ = OFF_DD + 2 * BN * 16;
+    static constexpr int OFF_X = OFF_MJ + 2 * BN * 16;
+    static constexpr int BYTES = FMT == FMT_Q8_0 ? OFF_S + 2 * 2 * BN * 4 : OFF_X + 2 * BM * 32;
+    static constexpr int AU = 16 * BM / NT;            // 16-byte activation chunks per thread per stage
+    static constexpr int BU = (2 * BN + NT - 1) / NT;  // weight units (row, half) per thread per stage
+    static constexpr int XU = (2 * BM + NT - 1) / NT;  // Q4_K sub-block-sum chunks per thread
+    static_assert((8 * BM) % NT == 0, "activation chunks must split evenly between hi and lo");
+};
+
+QMM_DEV uint32_t clamp_u32(int64_t v) { return v > 0xffffffffll ? 0xffffffffu : (uint32_t)v; }
+
+template <int FMT, int WM, int WN, int TM, int TN>
+__global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_kernel(GemmArgs a)
 {
-    constexpr bool TWO = MODE == MODE_A;
-    __shared__ __align__(16) _Float16 sA0[GEMM_BM * LDA];
-    __shared__ __align__(16) _Float16 sA1[TWO ? GEMM_BM * LDA : 8];
-    __shared__ __align__(16) _Float16 sB[GEMM_BN * LDA];
-    __shared__ __align__(16) float sWd[2][GEMM_BN];   // Q8_0: weight block scales; Q4_K: [0]=d, [1]=dmin
-    __shared__ __align__(16) float sXd[2][GEMM_BM];   // Q8_0 mode b: act block scales; Q4_K mode b: [0]=dx
-    __shared__ __align__(16) int sQm[8][GEMM_BN];     // Q4_K sub-block mins m_j
-    __shared__ __align__(16) float sXs[8][GEMM_BM];   // Q4_K: mode a sub-block sums of x*s; mode b bsum pairs
+    using C = GemmCfg<FMT, WM, WN, TM, TN>;
+    constexpr int NT = C::NT, BM = C::BM, BN = C::BN, AU = C::AU, BU = C::BU, XU = C::XU;
+    constexpr bool Q8 = FMT == FMT_Q8_0;
+    extern __shared__ __align__(16) uint8_t lds[];
 
     const int M = a.M, N = a.N, K = a.K;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int m0 = blockIdx.y * GEMM_BM, n0 = blockIdx.x * GEMM_BN;
-    const int wm = (wave & 1) * 64, wn = (wave >> 1) * 64;
-    const int nst = K / GEMM_KS;
-    const int nb = K / 32;
+    int t = blockIdx.x;
+    if (a.remap) {
+        const int per = (int)gridDim.x >> 3;
+        t = (t & 7) * per + (t >> 3);
+    }
+    const int m0 = (t % a.nm) * BM, n0 = (t / a.nm) * BN;
+    const int wm = (wave % WM) * 16 * TM, wn = (wave / WM) * 16 * TN;
+    const int nst = K / 64;
+    const int li = lane & 15, kg = lane >> 4;
 
-    // ---- per-thread load roles ----
-    const int br = tid >> 1, bpart = tid & 1;  // weight row and half of the stage
+    // Resources over this workgroup's rows: loads past the last row return zeros.
+    const int64_t rb = a.row_bytes;
+    const rsrc_t rhi = make_rsrc(a.hi + (int64_t)m0 * K, clamp_u32((int64_t)(M - m0) * K * 2));
+    const rsrc_t rlo = make_rsrc(a.lo + (int64_t)m0 * K, clamp_u32((int64_t)(M - m0) * K * 2));
+    const rsrc_t rw = make_rsrc(a.w + (int64_t)n0 * rb, clamp_u32((int64_t)(N - n0) * rb));
+    const rsrc_t rx = make_rsrc(Q8 ? a.hi : a.xs + (int64_t)m0 * (K / 256) * 16,
+                                clamp_u32((int64_t)(M - m0) * (K / 256) * 32));
+
+    // ---- per-thread staging roles, fixed for the whole K loop ----
+    // activation chunk idx over [hi, lo][BM rows][8 chunks]
+    uint32_t ag[AU], as_[AU];
+#pragma unroll
+    for (int i = 0; i < AU; ++i) {
+        const int idx = (tid + NT * i) % (8 * BM), row = idx >> 3, ch = idx & 7;
+        ag[i] = (uint32_t)(row * K * 2 + ch * 16);
+        as_[i] = (uint32_t)((i < AU / 2 ? 0 : C::A_HALF) + swz(row, ch));
+    }
+    // weight unit (row, half): Q8_0 half = block of the stage, Q4_K half = low
+    // or high nibbles (values 0-31 or 32-63 of the stage).  Each unit writes
+    // chunks 4*half .. 4*half+3 of its row.  Threads past 2*BN units repeat
+    // earlier units (same values to the same places).
+    uint32_t bg[BU], bsel[BU], bsh[BU], brow[BU], bst[BU][4];
+#pragma unroll
+    for (int i = 0; i < BU; ++i) {
+        const int u = (tid + NT * i) % (2 * BN), row = u >> 1, sub = u & 1;
+        bg[i] = (uint32_t)(Q8 ? row * rb + 32 * sub : row * rb);
+        bsel[i] = sub ? 0x07060504u : 0x05040302u;  // Q8_0: byte selector of the block's values
+        bsh[i] = (uint32_t)sub;
+        brow[i] = (uint32_t)row;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bst[i][e] = swz(row, 4 * sub + e);
+    }
+    uint32_t xg[XU], xs_[XU];
+#pragma unroll
+    for (int i = 0; i < XU; ++i) {
+        const int u = (tid + NT * i) % (2 * BM);
+        xg[i] = (uint32_t)((u >> 1) * (K / 256) * 32 + 16 * (u & 1));
+        xs_[i] = (uint32_t)((u >> 1) * 32 + 16 * (u & 1));
+    }
+    // MFMA operand reads: row wm + 16 i + li (A) or wn + 16 j + li (B), chunk 4 s + kg
+    uint32_t afr[2], bfr[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        afr[s] = swz(wm + li, 4 * s + kg);
+        bfr[s] = swz(wn + li, 4 * s + kg);
+    }
+
+    // ---- staging registers, two sets (stage parity) ----
+    uint4 ra[2][AU];
+    uint32_t rq8[2][Q8 ? BU : 1][9];
+    uint4 rhd[2][Q8 ? 1 : BU], rqa[2][Q8 ? 1 : BU], rqb[2][Q8 ? 1 : BU];
+    uint4 rxv[XU];
+
+    auto load = [&](int st, auto setc, auto csc) {
+        constexpr int SET = decltype(setc)::value;
+        constexpr int CS = decltype(csc)::value;  // stage within the super-block (Q4_K)
+#pragma unroll
+        for (int i = 0; i < AU; ++i)
+            ra[SET][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(i < AU / 2 ? rhi : rlo, ag[i], 128 * st, 0));
+        if constexpr (Q8) {
+#pragma unroll
+            for (int i = 0; i < BU; ++i) {
+                const u32x4_t v0 = __builtin_amdgcn_raw_buffer_load_b128(rw, bg[i], 68 * st, 0);
+                const u32x4_t v1 = __builtin_amdgcn_raw_buffer_load_b128(rw, bg[i] + 16, 68 * st, 0);
+                const uint32_t v2 = __builtin_amdgcn_raw_buffer_load_b32(rw, bg[i] + 32, 68 * st, 0);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) { rq8[SET][i][k] = v0[k]; rq8[SET][i][4 + k] = v1[k]; }
+                rq8[SET][i][8] = v2;
+            }
+        } else {
+            const int sb = st >> 2;
+#pragma unroll
+            for (int i = 0; i < BU; ++i) {
+                rhd[SET][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, bg[i], 144 * sb, 0));
+                rqa[SET][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, bg[i] + 16 + 32 * CS, 144 * sb, 0));
+                rqb[SET][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, bg[i] + 32 + 32 * CS, 144 * sb, 0));
+            }
+            if (CS == 0) {
+#pragma unroll
+                for (int i = 0; i < XU; ++i)
+                    rxv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, xg[i], 32 * sb, 0));
+            }
+        }
+    };
+
+    // ---- staging items: registers of one set -> LDS buffer P ----
+    // Items: activation chunks, then per weight unit four 8-value chunks and
+    // its scales.  `item` runs one of them; the compute loop spreads them over
+    // its MFMA groups.
+    constexpr int NI = AU + BU * 5 + (Q8 ? 0 : XU);
+    half2_t qs_s[BU], qs_b[BU];  // Q4_K: sc and -1024*sc of the unit's sub-block
+    auto item = [&](int w, int st, auto setc, auto pc, auto csc) {
+        constexpr int SET = decltype(setc)::value;
+        constexpr int P = decltype(pc)::value;
+        constexpr int CS = decltype(csc)::value;
+        if (w < AU) {
+            *reinterpret_cast<uint4*>(lds + P * C::A_BYTES + as_[w]) = ra[SET][w];
+            return;
+        }
+        w -= AU;
+        if (w < 5 * BU) {
+            const int i = w / 5, e = w % 5;
+            uint8_t* bbase = lds + C::OFF_B + P * C::B_BYTES;
+            if constexpr (Q8) {
+                if (e < 4) {
+                    uint32_t h[4];
+                    i8x4_to_f16(__builtin_amdgcn_perm(rq8[SET][i][2 * e + 1], rq8[SET][i][2 * e], bsel[i]), h[0], h[1]);
+                    i8x4_to_f16(__builtin_amdgcn_perm(rq8[SET][i][2 * e + 2], rq8[SET][i][2 * e + 1], bsel[i]), h[2], h[3]);
+                    *reinterpret_cast<uint4*>(bbase + bst[i][e]) = make_uint4(h[0], h[1], h[2], h[3]);
+                } else {
+                    const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)(rq8[SET][i][0] >> (16 * bsh[i])));
+                    reinterpret_cast<float*>(lds + C::OFF_S)[(P * 2 + bsh[i]) * BN + brow[i]] = d;
+                }
+            } else {
+                const uint4 hd = rhd[SET][i];
+                if (e == 0) {
+                    int sc0, mn0, sc1, mn1;
+                    q4k_scale_min(hd.y, hd.z, hd.w, 2 * CS, sc0, mn0);
+                    q4k_scale_min(hd.y, hd.z, hd.w, 2 * CS + 1, sc1, mn1);
+                    const int sc = bsh[i] ? sc1 : sc0;
+                    const _Float16 f = (_Float16)(float)sc, g = (_Float16)(-1024.0f * (float)sc);
+                    qs_s[i] = half2_t{f, f};
+                    qs_b[i] = half2_t{g, g};
+                }
+                if (e < 4) {
+                    // values 8e .. 8e+7 of the half: bytes 8e .. 8e+7 of the 32 stage bytes
+                    const uint32_t d0 = e < 2 ? (e == 0 ? rqa[SET][i].x : rqa[SET][i].z) : (e == 2 ? rqb[SET][i].x : rqb[SET][i].z);
+                    const uint32_t d1 = e < 2 ? (e == 0 ? rqa[SET][i].y : rqa[SET][i].w) : (e == 2 ? rqb[SET][i].y : rqb[SET][i].w);
+                    const uint32_t n0_ = (d0 >> (4 * bsh[i])) & 0x0f0f0f0fu, n1_ = (d1 >> (4 * bsh[i])) & 0x0f0f0f0fu;
+                    uint32_t h[4];
+                    h[0] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, n0_, 0x05010400u)), qs_s[i], qs_b[i]));
+                    h[1] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, n0_, 0x07030602u)), qs_s[i], qs_b[i]));
+                    h[2] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, n1_, 0x05010400u)), qs_s[i], qs_b[i]));
+                    h[3] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, n1_, 0x07030602u)), qs_s[i], qs_b[i]));
+                    *reinterpret_cast<uint4*>(bbase + bst[i][e]) = make_uint4(h[0], h[1], h[2], h[3]);
+                } else if (CS == 0) {
+                    // the (row, 0) unit stores {d, dmin}, the (row, 1) unit the mins 32*m_j
+                    const int sp = (st >> 2) & 1;
+                    uint32_t mj[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        int s_, ma, mb;
+                        q4k_scale_min(hd.y, hd.z, hd.w, 2 * j, s_, ma);
+                        q4k_scale_min(hd.y, hd.z, hd.w, 2 * j + 1, s_, mb);
+                        mj[j] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)(float)(32 * ma), (_Float16)(float)(32 * mb)});
+                    }
+                    const uint4 v = bsh[i] ? make_uint4(mj[0], mj[1], mj[2], mj[3])
+                                           : make_uint4(__float_as_uint(f16lo(hd.x)), __float_as_uint(f16hi(hd.x)), 0u, 0u);
+                    *reinterpret_cast<uint4*>(lds + (bsh[i] ? C::OFF_MJ : C::OFF_DD) + (sp * BN + brow[i]) * 16) = v;
+                }
+            }
+            return;
+        }
+        w -= 5 * BU;
+        if constexpr (!Q8) {
+            if (CS == 0 && w < XU) {
+                const int sp = (st >> 2) & 1;
+                *reinterpret_cast<uint4*>(lds + C::OFF_X + sp * BM * 32 + xs_[w]) = rxv[w];
+            }
+        }
+    };
+
+    f32x4_t acc[TM][TN], csb[Q8 ? 1 : TM][Q8 ? 1 : TN];
+    const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = zero;
+
+    // ---- one stage: MFMAs out of buffer P, interleaved with staging stage st+1
+    // (register set SET ^ 1) into buffer P ^ 1 when STORE ----
+    auto iter = [&](int st, auto pc, auto csc, auto ldc, auto stc) {
+        constexpr int P = decltype(pc)::value;
+        constexpr int CS = decltype(csc)::value;
+        constexpr bool LOAD = decltype(ldc)::value, STORE = decltype(stc)::value;
+        using IP = std::integral_constant<int, P>;
+        using IQ = std::integral_constant<int, P ^ 1>;
+        using ICS1 = std::integral_constant<int, (CS + 1) & 3>;
+        using ICS2 = std::integral_constant<int, (CS + 2) & 3>;
+        if (LOAD) load(st + 2, IP{}, ICS2{});
+        const uint8_t* sa = lds + P * C::A_BYTES;
+        const uint8_t* sbb = lds + C::OFF_B + P * C::B_BYTES;
+        f32x4_t cvp[TM];
+        float dwp = 0.0f;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            half8_t ah[TM], al[TM];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                ah[i] = *reinterpret_cast<const half8_t*>(sa + afr[s] + 16 * G_ROW * i);
+                al[i] = *reinterpret_cast<const half8_t*>(sa + C::A_HALF + afr[s] + 16 * G_ROW * i);
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const half8_t bw = *reinterpret_cast<const half8_t*>(sbb + bfr[s] + 16 * G_ROW * j);
+                if constexpr (Q8) {
+                    const float dw = reinterpret_cast<const float*>(lds + C::OFF_S)[(P * 2 + s) * BN + wn + 16 * j + li];
+                    f32x4_t cv[TM];
+#pragma unroll
+                    for (int i = 0; i < TM; ++i) cv[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[i], bw, zero, 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < TM; ++i) cv[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[i], bw, cv[i], 0, 0, 0);
+                    // scale the previous column while this one is in the matrix cores
+                    if (s > 0 || j > 0) {
+                        const int jp = j > 0 ? j - 1 : TN - 1;
+#pragma unroll
+                        for (int i = 0; i < TM; ++i)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) acc[i][jp][r] = __builtin_fmaf(dwp, cvp[i][r], acc[i][jp][r]);
+                    }
+#pragma unroll
+                    for (int i = 0; i < TM; ++i) cvp[i] = cv[i];
+                    dwp = dw;
+                } else {
+#pragma unroll
+                    for (int i = 0; i < TM; ++i)
+                        csb[Q8 ? 0 : i][Q8 ? 0 : j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            ah[i], bw, (CS == 0 && s == 0) ? zero : csb[Q8 ? 0 : i][Q8 ? 0 : j], 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < TM; ++i)
+                        csb[Q8 ? 0 : i][Q8 ? 0 : j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            al[i], bw, csb[Q8 ? 0 : i][Q8 ? 0 : j], 0, 0, 0);
+                }
+                if (STORE) {
+                    constexpr int R = 2 * TN;
+                    const int rg = s * TN + j;
+#pragma unroll
+                    for (int w = 0; w < NI; ++w)
+                        if ((w * R) / NI == rg) item(w, st + 1, IQ{}, IQ{}, ICS1{});
+                }
+            }
+        }
+        if constexpr (Q8) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[i][TN - 1][r] = __builtin_fmaf(dwp, cvp[i][r], acc[i][TN - 1][r]);
+        } else if (CS == 3) {
+            const int sp = (st >> 2) & 1;
+            const half8_t hz = {};
+            half8_t ax[TM];
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                ax[i] = kg < 2 ? *reinterpret_cast<const half8_t*>(lds + C::OFF_X + (sp * BM + wm + 16 * i + li) * 32 + 16 * kg) : hz;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int nl = wn + 16 * j + li;
+                const half8_t bm = kg < 2 ? *reinterpret_cast<const half8_t*>(lds + C::OFF_MJ + (sp * BN + nl) * 16) : hz;
+                const float2 dd = *reinterpret_cast<const float2*>(lds + C::OFF_DD + (sp * BN + nl) * 16);
+#pragma unroll
+                for (int i = 0; i < TM; ++i) {
+                    const f32x4_t cm = __builtin_amdgcn_mfma_f32_16x16x32_f16(ax[i], bm, zero, 0, 0, 0);
+                    const f32x4_t& cs = csb[Q8 ? 0 : i][Q8 ? 0 : j];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        acc[i][j][r] = __builtin_fmaf(-dd.y, cm[r], __builtin_fmaf(dd.x, cs[r], acc[i][j][r]));
+                }
+            }
+        }
+        __syncthreads();
+    };
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+
+    // prologue: stages 0 and 1 in flight, stage 0 staged into buffer 0
+    load(0, I0{}, I0{});
+    if (nst > 1) load(1, I1{}, I1{});
+#pragma unroll
+    for (int w = 0; w < NI; ++w) item(w, 0, I0{}, I0{}, I0{});
+    __syncthreads();
+
+    if constexpr (Q8) {
+        int st = 0;
+        for (; st + 3 < nst; st += 2) {
+            iter(st, I0{}, I0{}, T_{}, T_{});
+            iter(st + 1, I1{}, I0{}, T_{}, T_{});
+        }
+        const int rem = nst - st;
+        if (rem == 3) {
+            iter(st, I0{}, I0{}, T_{}, T_{});
+            iter(st + 1, I1{}, I0{}, F_{}, T_{});
+            iter(st + 2, I0{}, I0{}, F_{}, F_{});
+        } else if (rem == 2) {
+            iter(st, I0{}, I0{}, F_{}, T_{});
+            iter(st + 1, I1{}, I0{}, F_{}, F_{});
+        } else {
+            iter(st, I0{}, I0{}, F_{}, F_{});
+        }
+    } else {
+        const int nsb = nst >> 2;
+        for (int sb = 0; sb + 1 < nsb; ++sb) {
+            const int st = 4 * sb;
+            iter(st, I0{}, I0{}, T_{}, T_{});
+            iter(st + 1, I1{}, I1{}, T_{}, T_{});
+            iter(st + 2, I0{}, I2{}, T_{}, T_{});
+            iter(st + 3, I1{}, I3{}, T_{}, T_{});
+        }
+        const int st = nst - 4;
+        iter(st, I0{}, I0{}, T_{}, T_{});
+        iter(st + 1, I1{}, I1{}, T_{}, T_{});
+        iter(st + 2, I0{}, I2{}, F_{}, T_{});
+        iter(st + 3, I1{}, I3{}, F_{}, F_{});
+    }
+
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        float rsv[4];
+        int mrow[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            mrow[r] = m0 + wm + 16 * i + 4 * kg + r;
+            rsv[r] = mrow[r] < M ? a.rs[mrow[r]] : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int n = n0 + wn + 16 * j + li;
+            if (n >= N) continue;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (mrow[r] < M) a.y[(int64_t)mrow[r] * N + n] = acc[i][j][r] * rsv[r];
+        }
+    }
+}
+
+// ---------------------------------------------------- block-sums hook ----
+//
+// Mode (b) integer block sums for M > 8: 128 x 128 tiles, activations as
+// their quantized integers in f16, weights as exact f16 integers (Q8_0: q;
+// Q4_K: sc_j*q); v_mfma_f32_32x32x16_f16 sums of 32 (Q8_0) or 128 (Q4_K)
+// products are exact integers below 2^24.  Writes Q8_0 S[m][n][b]; Q4_K
+// sumi and summins per super-block (the per-32 sums are folded into sumi).
+
+struct SumsArgs {
+    const uint8_t* w;
+    int64_t row_bytes;
+    int N, K, M;
+    const _Float16* q;   // quantized activations as f16 [M][K]
+    const float* sd;     // unused by the sums; kept for the layout
+    const int32_t* bsp;  // Q4_K: bsum pairs [M][K/32]
+    int32_t* sums;
+};
+
+constexpr int S_BM = 128, S_BN = 128, S_LDA = 72;
+
+template <int FMT>
+__global__ __launch_bounds__(256, 1) void gemm_sums_kernel(SumsArgs a)
+{
+    __shared__ __align__(16) _Float16 sA0[S_BM * S_LDA];
+    __shared__ __align__(16) _Float16 sB[S_BN * S_LDA];
+    __shared__ __align__(16) int sQm[8][S_BN];
+    __shared__ __align__(16) int sBs[8][S_BM];
+
+    const int M = a.M, N = a.N, K = a.K;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int m0 = blockIdx.y * S_BM, n0 = blockIdx.x * S_BN;
+    const int wm = (wave & 1) * 64, wn = (wave >> 1) * 64;
+    const int nst = K / 64;
+    const int nb = K / 32;
+    const int br = tid >> 1, bpart = tid & 1;
     const bool brow_ok = n0 + br < N;
     const uint8_t* wrow = a.w + (int64_t)(n0 + (brow_ok ? br : 0)) * a.row_bytes;
 
-    uint4 ra0[4], ra1[TWO ? 4 : 1];
-    uint32_t rb[9];
-    float rx[2];
+    f32x16_t cb[2][2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int yv = 0; yv < 2; ++yv)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) cb[x][yv][r] = 0.0f;
+    int32_t half0[2][2][16];
 
-    auto load_stage = [&](int st) {
+    const int li = lane & 31, lk = 8 * (lane >> 5);
+    auto crow = [&](int r) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); };
+
+    for (int st = 0; st < nst; ++st) {
+        __syncthreads();
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int idx = tid + 256 * i, row = idx >> 3, c16 = idx & 7;
-            const int m = m0 + row;
-            if (m < M) {
-                const int64_t off = (int64_t)m * K + st * GEMM_KS + 8 * c16;
-                ra0[i] = *reinterpret_cast<const uint4*>(a.a0 + off);
-                if (TWO) ra1[i] = *reinterpret_cast<const uint4*>(a.a1 + off);
-            } else {
-                ra0[i] = make_uint4(0, 0, 0, 0);
-                if (TWO) ra1[i] = make_uint4(0, 0, 0, 0);
-            }
+            const int idx = tid + 256 * i, row = idx >> 3, c16 = idx & 7, m = m0 + row;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (m < M) v = *reinterpret_cast<const uint4*>(a.q + (int64_t)m * K + st * 64 + 8 * c16);
+            *reinterpret_cast<uint4*>(&sA0[row * S_LDA + 8 * c16]) = v;
         }
         if (FMT == FMT_Q8_0) {
             const uint32_t* p = reinterpret_cast<const uint32_t*>(wrow + 68 * st) + 8 * bpart;
+            uint32_t rb[9];
 #pragma unroll
             for (int i = 0; i < 9; ++i) rb[i] = brow_ok ? p[i] : 0u;
-            if (MODE == MODE_B) {
-                if (tid < GEMM_BM) {
-                    const int m = m0 + tid;
-                    const float2 v = m < M ? *reinterpret_cast<const float2*>(a.sc0 + (int64_t)m * nb + 2 * st)
-                                           : make_float2(0.0f, 0.0f);
-                    rx[0] = v.x;
-                    rx[1] = v.y;
-                }
+            uint32_t q[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) q[i] = bpart == 0 ? __builtin_amdgcn_alignbyte(rb[i + 1], rb[i], 2) : rb[i + 1];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint32_t t0, t1, t2, t3;
+                i8x4_to_f16(q[2 * i], t0, t1);
+                i8x4_to_f16(q[2 * i + 1], t2, t3);
+                *reinterpret_cast<uint4*>(&sB[br * S_LDA + 32 * bpart + 8 * i]) = make_uint4(t0, t1, t2, t3);
             }
         } else {
             const int sb = st >> 2, c = st & 3;
             const uint4 hdr = brow_ok ? *reinterpret_cast<const uint4*>(wrow + 144 * sb) : make_uint4(0, 0, 0, 0);
             const uint4 qv = brow_ok ? *reinterpret_cast<const uint4*>(wrow + 144 * sb + 16 + 32 * c + 16 * bpart)
                                      : make_uint4(0, 0, 0, 0);
-            rb[0] = hdr.x; rb[1] = hdr.y; rb[2] = hdr.z; rb[3] = hdr.w;
-            rb[4] = qv.x; rb[5] = qv.y; rb[6] = qv.z; rb[7] = qv.w;
-        }
-    };
-
-    auto store_stage = [&](int st) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int idx = tid + 256 * i, row = idx >> 3, c16 = idx & 7;
-            *reinterpret_cast<uint4*>(&sA0[row * LDA + 8 * c16]) = ra0[i];
-            if (TWO) *reinterpret_cast<uint4*>(&sA1[row * LDA + 8 * c16]) = ra1[i];
-        }
-        if (FMT == FMT_Q8_0) {
-            uint32_t q[8];
-            float d;
-            if (bpart == 0) {
-                d = f16lo(rb[0]);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) q[i] = __builtin_amdgcn_alignbyte(rb[i + 1], rb[i], 2);
-            } else {
-                d = f16hi(rb[0]);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) q[i] = rb[i + 1];
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                uint32_t t0, t1, t2, t3;
-                i8x4_to_f16(q[2 * i], t0, t1);
-                i8x4_to_f16(q[2 * i + 1], t2, t3);
-                *reinterpret_cast<uint4*>(&sB[br * LDA + 32 * bpart + 8 * i]) = make_uint4(t0, t1, t2, t3);
-            }
-            sWd[bpart][br] = brow_ok ? d : 0.0f;
-            if (MODE == MODE_B && tid < GEMM_BM) {
-                sXd[0][tid] = rx[0];
-                sXd[1][tid] = rx[1];
-            }
-        } else {
-            const int c = st & 3;
+            const uint32_t qd[4] = {qv.x, qv.y, qv.z, qv.w};
             int sc0, mn0, sc1, mn1;
-            q4k_scale_min(rb[1], rb[2], rb[3], 2 * c, sc0, mn0);
-            q4k_scale_min(rb[1], rb[2], rb[3], 2 * c + 1, sc1, mn1);
-            const _Float16 f0 = (_Float16)(float)sc0, f1 = (_Float16)(float)sc1;
+            q4k_scale_min(hdr.y, hdr.z, hdr.w, 2 * c, sc0, mn0);
+            q4k_scale_min(hdr.y, hdr.z, hdr.w, 2 * c + 1, sc1, mn1);
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {  // 8 bytes at a time
+            for (int hh = 0; hh < 2; ++hh) {
                 half8_t lo, hi;
 #pragma unroll
-                for (int b = 0; b < 8; ++b) {
-                    const uint32_t byte = (rb[4 + 2 * h + (b >> 2)] >> (8 * (b & 3))) & 0xffu;
-                    lo[b] = (_Float16)(float)(byte & 15u) * f0;
-                    hi[b] = (_Float16)(float)(byte >> 4) * f1;
+                for (int bb = 0; bb < 8; ++bb) {
+                    const uint32_t byte = (qd[2 * hh + (bb >> 2)] >> (8 * (bb & 3))) & 0xffu;
+                    lo[bb] = (_Float16)(float)((int)(byte & 15u) * sc0);
+                    hi[bb] = (_Float16)(float)((int)(byte >> 4) * sc1);
                 }
-                *reinterpret_cast<half8_t*>(&sB[br * LDA + 16 * bpart + 8 * h]) = lo;
-                *reinterpret_cast<half8_t*>(&sB[br * LDA + 32 + 16 * bpart + 8 * h]) = hi;
+                *reinterpret_cast<half8_t*>(&sB[br * S_LDA + 16 * bpart + 8 * hh]) = lo;
+                *reinterpret_cast<half8_t*>(&sB[br * S_LDA + 32 + 16 * bpart + 8 * hh]) = hi;
             }
             if (c == 0 && bpart == 0) {
-                sWd[0][br] = brow_ok ? f16lo(rb[0]) : 0.0f;
-                sWd[1][br] = brow_ok ? f16hi(rb[0]) : 0.0f;
 #pragma unroll
                 for (int jq = 0; jq < 8; ++jq) {
                     int s_, m_;
-                    q4k_scale_min(rb[1], rb[2], rb[3], jq, s_, m_);
-                    sQm[jq][br] = m_;
+                    q4k_scale_min(hdr.y, hdr.z, hdr.w, jq, s_, m_);
+                    sQm[jq][br] = brow_ok ? m_ : 0;
                 }
             }
-            if (c == 0) {  // per-row activation data of the super-block
-                const int sb = st >> 2;
-                for (int idx = tid; idx < GEMM_BM * 8; idx += 256) {
+            if (c == 0)
+                for (int idx = tid; idx < S_BM * 8; idx += 256) {
                     const int row = idx >> 3, jq = idx & 7, m = m0 + row;
-                    if (MODE == MODE_A) {
-                        sXs[jq][row] = m < M ? reinterpret_cast<const float*>(a.sc1)[(int64_t)m * (K / 32) + 8 * sb + jq] : 0.0f;
-                    } else {
-                        const int v = m < M ? reinterpret_cast<const int32_t*>(a.sc1)[(int64_t)m * (K / 32) + 8 * sb + jq] : 0;
-                        sXs[jq][row] = __builtin_bit_cast(float, v);
-                    }
+                    sBs[jq][row] = m < M ? a.bsp[(int64_t)m * (K / 32) + 8 * sb + jq] : 0;
                 }
-                if (MODE == MODE_B)
-                    for (int row = tid; row < GEMM_BM; row += 256)
-                        sXd[0][row] = m0 + row < M ? a.sc0[(int64_t)(m0 + row) * (K / 256) + sb] : 0.0f;
-            }
         }
-    };
-
-    f32x16_t acc[2][2], cb[2][2];
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int yv = 0; yv < 2; ++yv)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) { acc[x][yv][r] = 0.0f; cb[x][yv][r] = 0.0f; }
-    int32_t half0[2][2][16];  // Q4_K mode b block-sums hook: first-half sumi
-
-    const int li = lane & 31, lk = 8 * (lane >> 5);
-    // C layout: lane column j = li; register r holds row 8*(r/4) + 4*(lane/32) + (r%4)
-    auto crow = [&](int r) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); };
-
-    load_stage(0);
-    for (int st = 0; st < nst; ++st) {
         __syncthreads();
-        store_stage(st);
-        __syncthreads();
-        if (st + 1 < nst) load_stage(st + 1);
 
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            half8_t A0[2], A1[2], B[2];
+            half8_t A0[2], B[2];
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                A0[t] = *reinterpret_cast<const half8_t*>(&sA0[(wm + 32 * t + li) * LDA + 16 * kk + lk]);
-                if (TWO) A1[t] = *reinterpret_cast<const half8_t*>(&sA1[(wm + 32 * t + li) * LDA + 16 * kk + lk]);
-                B[t] = *reinterpret_cast<const half8_t*>(&sB[(wn + 32 * t + li) * LDA + 16 * kk + lk]);
+            for (int t2 = 0; t2 < 2; ++t2) {
+                A0[t2] = *reinterpret_cast<const half8_t*>(&sA0[(wm + 32 * t2 + li) * S_LDA + 16 * kk + lk]);
+                B[t2] = *reinterpret_cast<const half8_t*>(&sB[(wn + 32 * t2 + li) * S_LDA + 16 * kk + lk]);
             }
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
+                for (int nt = 0; nt < 2; ++nt)
                     cb[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A0[mt], B[nt], cb[mt][nt], 0, 0, 0);
-                    if (TWO) cb[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A1[mt], B[nt], cb[mt][nt], 0, 0, 0);
-                }
-
             if (FMT == FMT_Q8_0 && (kk & 1)) {  // end of a 32-value block
                 const int blk = kk >> 1;
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) {
-                        const float dw = sWd[blk][wn + 32 * nt + li];
+                    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
-                            float s = dw;
-                            if (MODE == MODE_B) s *= sXd[blk][wm + 32 * mt + crow(r)];
-                            acc[mt][nt][r] += s * cb[mt][nt][r];
-                            if (EMIT) {
-                                const int m = m0 + wm + 32 * mt + crow(r), n = n0 + wn + 32 * nt + li;
-                                if (m < M && n < N) a.sums[((int64_t)m * N + n) * nb + 2 * st + blk] = (int32_t)cb[mt][nt][r];
-                            }
+                            const int m = m0 + wm + 32 * mt + crow(r), n = n0 + wn + 32 * nt + li;
+                            if (m < M && n < N) a.sums[((int64_t)m * N + n) * nb + 2 * st + blk] = (int32_t)cb[mt][nt][r];
                             cb[mt][nt][r] = 0.0f;
                         }
-                    }
             }
         }
-
         if (FMT == FMT_Q4_K) {
             const int c = st & 3;
-            if (MODE == MODE_B && (c & 1)) {  // end of a 128-value half super-block
+            if (c & 1) {  // end of a 128-value half super-block
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) {
-                        const float d = sWd[0][wn + 32 * nt + li];
+                    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
-                            const float dx = sXd[0][wm + 32 * mt + crow(r)];
-                            acc[mt][nt][r] += (dx * d) * cb[mt][nt][r];
-                            if (EMIT) {
-                                if (c == 1) half0[mt][nt][r] = (int32_t)cb[mt][nt][r];
-                                else half0[mt][nt][r] += (int32_t)cb[mt][nt][r];
-                            }
+                            if (c == 1) half0[mt][nt][r] = (int32_t)cb[mt][nt][r];
+                            else half0[mt][nt][r] += (int32_t)cb[mt][nt][r];
                             cb[mt][nt][r] = 0.0f;
                         }
-                    }
             }
-            if (c == 3) {  // end of the super-block: scale (mode a) and mins term
+            if (c == 3) {
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                     for (int nt = 0; nt < 2; ++nt) {
                         const int nl = wn + 32 * nt + li;
-                        const float d = sWd[0][nl], dmin = sWd[1][nl];
-                        int mj[8];
-#pragma unroll
-                        for (int jq = 0; jq < 8; ++jq) mj[jq] = sQm[jq][nl];
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
                             const int ml = wm + 32 * mt + crow(r);
-                            if (MODE == MODE_A) {
-                                float mins = 0.0f;
+                            int summ = 0;
 #pragma unroll
-                                for (int jq = 0; jq < 8; ++jq) mins += (float)mj[jq] * sXs[jq][ml];
-                                acc[mt][nt][r] += d * cb[mt][nt][r] - dmin * mins;
-                                cb[mt][nt][r] = 0.0f;
-                            } else {
-                                int summ = 0;
+                            for (int jq = 0; jq < 8; ++jq) summ += sQm[jq][nl] * sBs[jq][ml];
+                            const int m = m0 + ml, n = n0 + nl;
+                            if (m < M && n < N) {
+                                int32_t* o = a.sums + (((int64_t)m * N + n) * (K / 256) + (st >> 2)) * 10;
 #pragma unroll
-                                for (int jq = 0; jq < 8; ++jq) summ += mj[jq] * __builtin_bit_cast(int, sXs[jq][ml]);
-                                acc[mt][nt][r] -= sXd[0][ml] * dmin * (float)summ;
-                                if (EMIT) {
-                                    const int m = m0 + ml, n = n0 + nl;
-                                    if (m < M && n < N) {
-                                        int32_t* o = a.sums + (((int64_t)m * N + n) * (K / 256) + (st >> 2)) * 10;
-#pragma unroll
-                                        for (int jq = 0; jq < 8; ++jq) o[jq] = INT32_MIN;
-                                        o[8] = half0[mt][nt][r];
-                                        o[9] = summ;
-                                    }
-                                }
+                                for (int jq = 0; jq < 8; ++jq) o[jq] = INT32_MIN;
+                                o[8] = half0[mt][nt][r];
+                                o[9] = summ;
                             }
                         }
                     }
             }
         }
     }
-
-    if (EMIT) return;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            const int n = n0 + wn + 32 * nt + li;
-            if (n >= N) continue;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = m0 + wm + 32 * mt + crow(r);
-                if (m < M) {
-                    float v = acc[mt][nt][r];
-                    if (MODE == MODE_A) v *= a.sc0[m];
-                    a.y[(int64_t)m * N + n] = v;
-                }
-            }
-        }
 }
 
-template <int FMT, int MODE, bool EMIT>
-static void launch_one(const GemmArgs& a, hipStream_t s)
+// ------------------------------------------------------------ launchers ----
+
+typedef void (*GemmKernel)(GemmArgs);
+
+// Raises a kernel's dynamic LDS limit to what it needs, once per device.
+static void allow_lds(const void* k, int bytes)
 {
-    const dim3 grid((unsigned)((a.N + GEMM_BN - 1) / GEMM_BN), (unsigned)((a.M + GEMM_BM - 1) / GEMM_BM));
-    hipLaunchKernelGGL((gemm_kernel<FMT, MODE, EMIT>), grid, dim3(256), 0, s, a);
+    static std::set<std::pair<int, const void*>> done;
+    static std::mutex mu;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!done.insert(std::make_pair(dev, k)).second) return;
+    (void)hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    (void)hipGetLastError();
+}
+
+static int cu_count()
+{
+    static std::map<int, int> cache;
+    static std::mutex mu;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(dev);
+    if (it != cache.end()) return it->second;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 1;
+    (void)hipGetLastError();
+    return cache[dev] = cus;
+}
+
+struct GemmTile {
+    int wm, wn, tm, tn;
+};
+// Tile shapes, largest first: 128 x 224 fills 256 compute units exactly on
+// 512 x 14336; the smaller ones keep short or narrow problems spread out.
+static const GemmTile kTiles[] = {{4, 2, 2, 7}, {4, 2, 2, 4}, {2, 2, 2, 4}};
+
+// The tile whose busiest compute unit does the least work: rounds of tiles
+// over the compute units times the tile's area, weighted by its operand
+// traffic per output (activation pairs over BN, weight bytes over BM).
+static GemmTile pick_tile(int64_t M, int64_t N)
+{
+    const int64_t cus = cu_count();
+    GemmTile best = kTiles[0];
+    double bc = -1.0;
+    for (const GemmTile& t : kTiles) {
+        const int64_t bm = 16 * t.tm * t.wm, bn = 16 * t.tn * t.wn;
+        const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+        const double cost = (double)((tiles + cus - 1) / cus) * (double)(bm * bn) * (1.0 + 16.0 / bm + 64.0 / bn);
+        if (bc < 0 || cost < bc) {
+            bc = cost;
+            best = t;
+        }
+    }
+    return best;
+}
+
+template <int FMT, int WM, int WN, int TM, int TN>
+static hipError_t launch_tile(GemmArgs a, hipStream_t s)
+{
+    using C = GemmCfg<FMT, WM, WN, TM, TN>;
+    const int nm = (a.M + C::BM - 1) / C::BM, nn = (a.N + C::BN - 1) / C::BN;
+    const int64_t grid = (int64_t)nm * nn;
+    if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    a.nm = nm;
+    a.remap = grid % 8 == 0 ? 1 : 0;
+    GemmKernel k = gemm_kernel<FMT, WM, WN, TM, TN>;
+    allow_lds((const void*)k, C::BYTES);
+    void* args[] = {&a};
+    return hipLaunchKernel((const void*)k, dim3((unsigned)grid), dim3(C::NT), args, C::BYTES, s);
+}
+
+template <int FMT>
+static hipError_t launch_fmt(const GemmArgs& a, GemmTile t, hipStream_t s)
+{
+    if (t.wm == 4 && t.tn == 7) return launch_tile<FMT, 4, 2, 2, 7>(a, s);
+    if (t.wm == 4 && t.tn == 4) return launch_tile<FMT, 4, 2, 2, 4>(a, s);
+    return launch_tile<FMT, 2, 2, 2, 4>(a, s);
 }
 
 hipError_t launch_gemm(int fmt, int mode, const void* w, int64_t N, int64_t K, int64_t M, const GemmBufs& b,
                        float* y, int32_t* sums, hipStream_t s)
 {
+    const int64_t row_bytes = fmt == FMT_Q8_0 ? (K / 32) * 34 : (K / 256) * 144;
+    if (sums) {
+        if (mode != MODE_B) return hipErrorInvalidValue;
+        SumsArgs a{};
+        a.w = (const uint8_t*)w;
+        a.row_bytes = row_bytes;
+        a.N = (int)N;
+        a.K = (int)K;
+        a.M = (int)M;
+        a.q = b.a0;
+        a.sd = b.sd;
+        a.bsp = b.sbs;
+        a.sums = sums;
+        const dim3 grid((unsigned)((N + S_BN - 1) / S_BN), (unsigned)((M + S_BM - 1) / S_BM));
+        if (fmt == FMT_Q8_0) hipLaunchKernelGGL(gemm_sums_kernel<FMT_Q8_0>, grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL(gemm_sums_kernel<FMT_Q4_K>, grid, dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
     GemmArgs a{};
     a.w = (const uint8_t*)w;
-    a.row_bytes = fmt == FMT_Q8_0 ? (K / 32) * 34 : (K / 256) * 144;
+    a.row_bytes = row_bytes;
     a.N = (int)N;
     a.K = (int)K;
     a.M = (int)M;
-    a.a0 = b.a0;
-    a.a1 = b.a1;
-    a.sc0 = b.sc0;
-    a.sc1 = b.sc1;
+    a.hi = b.a0;
+    a.lo = b.a1;
+    a.rs = b.rs;
+    a.xs = b.xs;
     a.y = y;
-    a.sums = sums;
-    const bool emit = sums != nullptr;
-    if (fmt == FMT_Q8_0) {
-        if (mode == MODE_A) launch_one<FMT_Q8_0, MODE_A, false>(a, s);
-        else if (emit) launch_one<FMT_Q8_0, MODE_B, true>(a, s);
-        else launch_one<FMT_Q8_0, MODE_B, false>(a, s);
-    } else {
-        if (mode == MODE_A) launch_one<FMT_Q4_K, MODE_A, false>(a, s);
-        else if (emit) launch_one<FMT_Q4_K, MODE_B, true>(a, s);
-        else launch_one<FMT_Q4_K, MODE_B, false>(a, s);
-    }
+    const GemmTile t = pick_tile(M, N);
+    hipError_t e = fmt == FMT_Q8_0 ? launch_fmt<FMT_Q8_0>(a, t, s) : launch_fmt<FMT_Q4_K>(a, t, s);
+    if (e != hipSuccess) return e;
     return hipGetLastError();
 }
 

@@ -94,11 +94,6 @@ struct GemvArgs {
     int32_t* sums;
 };
 
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-QMM_DEV rsrc_t make_rsrc(const void* base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
 QMM_DEV u32x4_t ld128(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0); }
 QMM_DEV float4 ldx16(rsrc_t r, uint32_t off)
 {

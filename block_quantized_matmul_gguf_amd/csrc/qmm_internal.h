@@ -13,11 +13,6 @@ enum { MODE_A = 0, MODE_B = 1 };
 // each wave streaming 16-row tiles over one slice of K.
 constexpr int GEMV_MAX_M = 8;
 
-// Prefill (GEMM) path tile.
-constexpr int GEMM_BM = 128;
-constexpr int GEMM_BN = 128;
-constexpr int GEMM_KS = 64;
-
 struct GemvGeom {
     int nlu;          // load units per row (Q8_0 block pairs or Q4_K super-blocks)
     int64_t row_bytes;
@@ -43,10 +38,12 @@ struct GemvBufs {
 
 // Device buffers of the prefill path.
 struct GemmBufs {
-    _Float16* a0;  // mode a: hi part [M][K]; mode b: quantized activations as f16 [M][K]
-    _Float16* a1;  // mode a: lo part [M][K]
-    float* sc0;    // mode a: 1/row scale [M]; mode b: act block scales [M][K/32 or K/256]
-    void* sc1;     // mode a Q4_K: scaled sub-block sums [M][K/32] f32; mode b Q4_K: bsum pairs [M][K/32] i32
+    _Float16* a0;   // hi part of the scaled activation rows [M][K] (block-sums hook: quantized values as f16)
+    _Float16* a1;   // lo part [M][K]
+    float* rs;      // 1/s per row [M]
+    _Float16* xs;   // Q4_K: hi and lo of s * (sub-block sums) / 32, [M][K/256][16]
+    float* sd;      // block-sums hook: activation block scales [M][K/32 or K/256]
+    int32_t* sbs;   // block-sums hook, Q4_K: sums of 32 quantized values [M][K/32]
 };
 
 GemvGeom gemv_geom(int fmt, int mode, int64_t N, int64_t K, int M, bool emit);
@@ -59,7 +56,8 @@ hipError_t launch_quantize_weights(int fmt, const float* w, int64_t N, int64_t K
 hipError_t launch_gemv(int fmt, int mode, const void* w, const float* x, int64_t N, int64_t K, int M,
                        const GemvBufs& b, float* y, int32_t* sums, hipStream_t s);
 
-hipError_t launch_gemm_prep(int fmt, int mode, const float* x, int64_t M, int64_t K, const GemmBufs& b, hipStream_t s);
+hipError_t launch_gemm_prep(int fmt, int mode, const float* x, int64_t M, int64_t K, const GemmBufs& b, bool sums,
+                            hipStream_t s);
 hipError_t launch_gemm(int fmt, int mode, const void* w, int64_t N, int64_t K, int64_t M, const GemmBufs& b,
                        float* y, int32_t* sums, hipStream_t s);
 

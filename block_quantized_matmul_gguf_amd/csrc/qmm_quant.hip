@@ -1,5 +1,5 @@
 // qmm_quant.hip -- the standalone activation quantizer (canonical Q8_0 / Q8K
-// blocks), the prefill kernel's activation preparation, and the weight
+// blocks), the prefill kernels' activation preparation, and the weight
 // quantizers.  The block arithmetic lives in qmm_act.h and is shared with the
 // decode kernel's prologue.  Every activation row is quantized on its own
 // (page "自己量化", section 动脑筋答案).
@@ -76,45 +76,118 @@ __global__ __launch_bounds__(256) void quantize_q8k_kernel(const float* __restri
     }
 }
 
-// Mode (a) prefill preparation: one workgroup per row; whole-row power-of-two
-// scale; hi [M][K], lo [M][K] (f16), 1/scale [M], and (Q4_K) the sums of x*s
-// over every 32 values [M][K/32].
-template <int FMT>
-__global__ __launch_bounds__(256) void split_x_kernel(const float* __restrict__ x, int M, int K,
-                                                      _Float16* __restrict__ o0, _Float16* __restrict__ o1,
-                                                      float* __restrict__ sc0, float* __restrict__ sums)
+// Prefill preparation, one workgroup per row.  The row's effective
+// activation -- mode (a): x; mode (b): the dequantized quantized value, Q8_0
+// f16(d)*q (exact in f32) or Q8K d*q -- is scaled by the power of two s that
+// puts its largest magnitude in [2^14, 2^15) and split into f16 hi + lo;
+// rs = 1/s.  Q4_K also gets the sums of value*s over every 32 values, divided
+// by 32 so that they stay below 2^15, split the same way and laid out
+// [M][K/256][8 hi, 8 lo].
+template <int FMT, int MODE>
+__global__ __launch_bounds__(256) void gemm_prep_kernel(const float* __restrict__ x, int M, int K,
+                                                        _Float16* __restrict__ hi, _Float16* __restrict__ lo,
+                                                        float* __restrict__ rs, _Float16* __restrict__ xs)
 {
+    constexpr bool WAVE = FMT == FMT_Q4_K && MODE == MODE_B;  // Q8K blocks of 256 values, one wave each
     __shared__ float red[4];
     const int m = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const float* v = x + (int64_t)m * K;
+    const int n32 = K / 32, nsb = K / 256;
+
+    auto chunk = [&](int u, float e[32]) {  // 32 effective values (mode (a), or Q8_0 mode (b))
+        load32(v + 32 * u, e);
+        if (MODE == MODE_B) {
+            uint16_t dbits;
+            float dval;
+            int8_t q[32];
+            q8_0_block(e, dbits, dval, q);
+#pragma unroll
+            for (int j = 0; j < 32; ++j) e[j] = dval * (float)q[j];
+        }
+    };
+    auto block4 = [&](int sb, float e[4]) {  // this lane's 4 effective values of Q8K block sb
+        const float4 t = reinterpret_cast<const float4*>(v + 256 * sb)[lane];
+        const float xv[4] = {t.x, t.y, t.z, t.w};
+        float d;
+        int q[4], s16;
+        q8k_wave(xv, lane, d, q, s16);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) e[u] = d * (float)q[u];
+    };
+
     float am = 0.0f;
-    for (int k = 4 * threadIdx.x; k < K; k += 1024) {
-        const float4 t = *reinterpret_cast<const float4*>(v + k);
-        am = fmaxf(am, fmaxf(fmaxf(fabsf(t.x), fabsf(t.y)), fmaxf(fabsf(t.z), fabsf(t.w))));
+    if (WAVE) {
+        for (int sb = wave; sb < nsb; sb += 4) {
+            float e[4];
+            block4(sb, e);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) am = fmaxf(am, fabsf(e[u]));
+        }
+    } else {
+        for (int u = threadIdx.x; u < n32; u += 256) {
+            float e[32];
+            chunk(u, e);
+#pragma unroll
+            for (int j = 0; j < 32; ++j) am = fmaxf(am, fabsf(e[j]));
+        }
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = am;
+    if (lane == 0) red[wave] = am;
     __syncthreads();
     am = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     const int sexp = split_exp(am);
     const float s = ldexpf(1.0f, sexp);
-    if (threadIdx.x == 0) sc0[m] = ldexpf(1.0f, -sexp);
-    const int n32 = K / 32;
-    for (int u = threadIdx.x; u < n32; u += 256) {
-        float a[32];
-        _Float16 hi[32], lo[32];
-        load32(v + 32 * u, a);
-        const float acc = split_chunk(a, s, hi, lo);
+    if (threadIdx.x == 0) rs[m] = ldexpf(1.0f, -sexp);
+
+    _Float16* oh = hi + (int64_t)m * K;
+    _Float16* ol = lo + (int64_t)m * K;
+    _Float16* ox = FMT == FMT_Q4_K ? xs + (int64_t)m * nsb * 16 : nullptr;
+    auto put_sum = [&](int sb, int j, float sum) {
+        _Float16 h, l;
+        float t;
+        split_one(sum, 0.03125f, h, l, t);
+        ox[16 * sb + j] = h;
+        ox[16 * sb + 8 + j] = l;
+    };
+    if (WAVE) {
+        for (int sb = wave; sb < nsb; sb += 4) {
+            float e[4];
+            block4(sb, e);
+            _Float16 h[4], l[4];
+            float sum = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            half8_t vh, vl;
-#pragma unroll
-            for (int t = 0; t < 8; ++t) { vh[t] = hi[8 * i + t]; vl[t] = lo[8 * i + t]; }
-            reinterpret_cast<half8_t*>(o0 + (int64_t)m * K + 32 * u)[i] = vh;
-            reinterpret_cast<half8_t*>(o1 + (int64_t)m * K + 32 * u)[i] = vl;
+            for (int u = 0; u < 4; ++u) {
+                float t;
+                split_one(e[u], s, h[u], l[u], t);
+                sum += t;
+            }
+            const int k = 256 * sb + 4 * lane;
+            const half2_t h01 = {h[0], h[1]}, h23 = {h[2], h[3]}, l01 = {l[0], l[1]}, l23 = {l[2], l[3]};
+            *reinterpret_cast<u32x2_t*>(oh + k) = u32x2_t{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
+            *reinterpret_cast<u32x2_t*>(ol + k) = u32x2_t{__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23)};
+            sum += __shfl_xor(sum, 1);
+            sum += __shfl_xor(sum, 2);
+            sum += __shfl_xor(sum, 4);
+            if ((lane & 7) == 0) put_sum(sb, lane >> 3, sum);
         }
-        if (FMT == FMT_Q4_K) sums[(int64_t)m * n32 + u] = acc;
+    } else {
+        for (int u = threadIdx.x; u < n32; u += 256) {
+            float e[32];
+            _Float16 h[32], l[32];
+            chunk(u, e);
+            const float sum = split_chunk(e, s, h, l);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                half8_t vh, vl;
+#pragma unroll
+                for (int t = 0; t < 8; ++t) { vh[t] = h[8 * i + t]; vl[t] = l[8 * i + t]; }
+                reinterpret_cast<half8_t*>(oh + 32 * u)[i] = vh;
+                reinterpret_cast<half8_t*>(ol + 32 * u)[i] = vl;
+            }
+            if (FMT == FMT_Q4_K) put_sum(u >> 3, u & 7, sum);
+        }
     }
 }
 
@@ -206,22 +279,27 @@ hipError_t launch_quantize_weights(int fmt, const float* w, int64_t N, int64_t K
     return hipGetLastError();
 }
 
-hipError_t launch_gemm_prep(int fmt, int mode, const float* x, int64_t M, int64_t K, const GemmBufs& b, hipStream_t s)
+hipError_t launch_gemm_prep(int fmt, int mode, const float* x, int64_t M, int64_t K, const GemmBufs& b, bool sums,
+                            hipStream_t s)
 {
-    if (mode == MODE_A) {
+    if (sums) {  // block-sums hook: quantized values as f16 and their scales
         if (fmt == FMT_Q8_0)
-            hipLaunchKernelGGL((split_x_kernel<FMT_Q8_0>), dim3((unsigned)M), dim3(256), 0, s, x, (int)M, (int)K,
-                               b.a0, b.a1, b.sc0, (float*)nullptr);
+            hipLaunchKernelGGL(quantize_q8_0_kernel<LAY_GEMM>, dim3(nblocks(M * (K / 32), 256)), dim3(256), 0, s,
+                               x, (int)M, (int)K, (uint8_t*)b.a0, b.sd);
         else
-            hipLaunchKernelGGL((split_x_kernel<FMT_Q4_K>), dim3((unsigned)M), dim3(256), 0, s, x, (int)M, (int)K,
-                               b.a0, b.a1, b.sc0, (float*)b.sc1);
-    } else if (fmt == FMT_Q8_0) {
-        hipLaunchKernelGGL(quantize_q8_0_kernel<LAY_GEMM>, dim3(nblocks(M * (K / 32), 256)), dim3(256), 0, s,
-                           x, (int)M, (int)K, (uint8_t*)b.a0, b.sc0);
-    } else {
-        hipLaunchKernelGGL(quantize_q8k_kernel<LAY_GEMM>, dim3(nblocks(M * (K / 256), 4)), dim3(256), 0, s,
-                           x, (int)M, (int)K, (uint8_t*)b.a0, b.sc0, (int32_t*)b.sc1);
+            hipLaunchKernelGGL(quantize_q8k_kernel<LAY_GEMM>, dim3(nblocks(M * (K / 256), 4)), dim3(256), 0, s,
+                               x, (int)M, (int)K, (uint8_t*)b.a0, b.sd, b.sbs);
+        return hipGetLastError();
     }
+    const dim3 grid((unsigned)M), block(256);
+    if (fmt == FMT_Q8_0 && mode == MODE_A)
+        hipLaunchKernelGGL((gemm_prep_kernel<FMT_Q8_0, MODE_A>), grid, block, 0, s, x, (int)M, (int)K, b.a0, b.a1, b.rs, b.xs);
+    else if (fmt == FMT_Q8_0)
+        hipLaunchKernelGGL((gemm_prep_kernel<FMT_Q8_0, MODE_B>), grid, block, 0, s, x, (int)M, (int)K, b.a0, b.a1, b.rs, b.xs);
+    else if (mode == MODE_A)
+        hipLaunchKernelGGL((gemm_prep_kernel<FMT_Q4_K, MODE_A>), grid, block, 0, s, x, (int)M, (int)K, b.a0, b.a1, b.rs, b.xs);
+    else
+        hipLaunchKernelGGL((gemm_prep_kernel<FMT_Q4_K, MODE_B>), grid, block, 0, s, x, (int)M, (int)K, b.a0, b.a1, b.rs, b.xs);
     return hipGetLastError();
 }
 
