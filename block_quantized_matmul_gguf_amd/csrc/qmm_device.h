@@ -23,6 +23,28 @@ QMM_DEV rsrc_t make_rsrc(const void* base, uint32_t bytes)
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// Lane exchanges inside the vector ALU (DPP), for reductions that must not
+// wait on the LDS crossbar: quad_perm [1,0,3,2] (lane ^ 1), [2,3,0,1]
+// (lane ^ 2), row_half_mirror (lane i <-> 7 - i within 8 lanes), row_mirror
+// (i <-> 15 - i within 16).  Applied in this order, an associative and
+// commutative combine leaves the result of a 16-lane row in every lane of it.
+enum { DPP_X1 = 0xB1, DPP_X2 = 0x4E, DPP_HMIRROR = 0x141, DPP_MIRROR = 0x140 };
+template <int CTRL>
+QMM_DEV int dpp_i(int v) { return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false); }
+template <int CTRL>
+QMM_DEV float dpp_f(float v) { return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, v))); }
+// max over the wave, the same value in every lane
+QMM_DEV float wave_max(float v)
+{
+    v = fmaxf(v, dpp_f<DPP_X1>(v));
+    v = fmaxf(v, dpp_f<DPP_X2>(v));
+    v = fmaxf(v, dpp_f<DPP_HMIRROR>(v));
+    v = fmaxf(v, dpp_f<DPP_MIRROR>(v));
+    const int b = __builtin_bit_cast(int, v);
+    return fmaxf(fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)), __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16))),
+                 fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)), __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48))));
+}
+
 QMM_DEV float f16lo(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xffffu)); }
 QMM_DEV float f16hi(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16)); }
 QMM_DEV uint16_t f16bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }

@@ -305,8 +305,7 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
                 for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(xv[c][i]));
                 const int m0 = t0 / per_row;
                 if (min(t0 + 63, ntasks - 1) / per_row == m0) {
-#pragma unroll
-                    for (int off = 32; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
+                    am = wave_max(am);
                     if (lane == 0) atomicMax(reinterpret_cast<unsigned*>(&s_misc[16 + m0]), __float_as_uint(am));
                 } else if (t < ntasks) {
                     atomicMax(reinterpret_cast<unsigned*>(&s_misc[16 + t / per_row]), __float_as_uint(am));
@@ -346,8 +345,8 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
                     *reinterpret_cast<half8_t*>(op + ((kg * 2 + 1) * MS + m) * 16) = vl;
                 }
                 if constexpr (FMT == FMT_Q4_K) {  // mins term: sum of x*2^e over the 32 values (hi rows)
-                    sum += __shfl_xor(sum, 1);
-                    sum += __shfl_xor(sum, 2);
+                    sum += dpp_f<DPP_X1>(sum);
+                    sum += dpp_f<DPP_X2>(sum);
                     if (live && kg == 0) {
                         s_scf[b * 2 * MS + m] = sum;
                         s_scf[b * 2 * MS + MS + m] = 0.0f;
@@ -358,7 +357,7 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
                 float am = 0.0f;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(xv[c][i]));
-                am = fmaxf(am, __shfl_xor(am, 1));  // the block's other half
+                am = fmaxf(am, dpp_f<DPP_X1>(am));  // the block's other half
                 float id, dval;
                 uint16_t dbits;
                 q8_0_scale(am, id, dbits, dval);
@@ -382,12 +381,14 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
                     const float av = fabsf(xv[c][i]);
                     if (av > best) { best = av; bv = xv[c][i]; bi = 16 * sl16 + i; }
                 }
-#pragma unroll
-                for (int off = 1; off < 16; off <<= 1) {
-                    const float ob = __shfl_xor(best, off), ov = __shfl_xor(bv, off);
-                    const int oi = __shfl_xor(bi, off);
+                // over the 16 lanes of the super-block (the order of the combine does not matter)
+                auto pick = [&](float ob, float ov, int oi) {
                     if (q8k_better(ob, oi, best, bi)) { best = ob; bv = ov; bi = oi; }
-                }
+                };
+                pick(dpp_f<DPP_X1>(best), dpp_f<DPP_X1>(bv), dpp_i<DPP_X1>(bi));
+                pick(dpp_f<DPP_X2>(best), dpp_f<DPP_X2>(bv), dpp_i<DPP_X2>(bi));
+                pick(dpp_f<DPP_HMIRROR>(best), dpp_f<DPP_HMIRROR>(bv), dpp_i<DPP_HMIRROR>(bi));
+                pick(dpp_f<DPP_MIRROR>(best), dpp_f<DPP_MIRROR>(bv), dpp_i<DPP_MIRROR>(bi));
                 float iscale, d;
                 q8k_scale(bv, best, iscale, d);
                 int q[16], s16 = 0;
@@ -396,7 +397,7 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
                     q[i] = q8k_q(xv[c][i], iscale);
                     s16 += q[i];
                 }
-                const int pr = s16 + __shfl_xor(s16, 1);  // the sub-block's two halves
+                const int pr = s16 + dpp_i<DPP_X1>(s16);  // the sub-block's two halves
                 if (live) {
                     // slot sl16 = sub-block j (two halves); step 2*(j/4) + j%2 holds sub-blocks
                     // (4cc+h) in rows 0..7 and (4cc+2+h) in rows 8..15
