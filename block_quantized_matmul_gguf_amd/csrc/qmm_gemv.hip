@@ -54,7 +54,10 @@ struct GvFmt {
     static constexpr int LUB = FMT == FMT_Q8_0 ? 68 : 144;
     static constexpr int OPS = FMT == FMT_Q8_0 ? (MODE == MODE_A ? 2 : 1) : (MODE == MODE_A ? 8 : 4);
     static constexpr int VPL = FMT == FMT_Q8_0 ? 64 : 256;
-    static constexpr int OPB = (MODE == MODE_A ? 128 : 64) * MS;
+    // one zero slot closes each matrix-core step when some lanes' operand rows are
+    // structurally zero (mode b's two-block trick, and M == 1): those lanes read it
+    static constexpr int ZS = MODE == MODE_B || MS == 1 ? 16 : 0;
+    static constexpr int OPB = (MODE == MODE_A ? 128 : 64) * MS + ZS;
     static constexpr int SCB = FMT == FMT_Q8_0 ? (MODE == MODE_A ? 0 : 8 * MS) : (MODE == MODE_A ? 64 * MS : 36 * MS);
 };
 
@@ -63,7 +66,7 @@ static void gv_fmt(int fmt, int mode, int ms, int& lub, int& ops, int& vpl, int&
     lub = fmt == FMT_Q8_0 ? 68 : 144;
     ops = fmt == FMT_Q8_0 ? (mode == MODE_A ? 2 : 1) : (mode == MODE_A ? 8 : 4);
     vpl = fmt == FMT_Q8_0 ? 64 : 256;
-    opb = (mode == MODE_A ? 128 : 64) * ms;
+    opb = (mode == MODE_A ? 128 : 64) * ms + (mode == MODE_B || ms == 1 ? 16 : 0);
     scb = fmt == FMT_Q8_0 ? (mode == MODE_A ? 0 : 8 * ms) : (mode == MODE_A ? 64 * ms : 36 * ms);
 }
 
@@ -287,6 +290,15 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
         if constexpr (SCB > 0)
             for (int i = lu_cnt * SCB / 4 + tid; i < lu_img * SCB / 4; i += pthreads) s_sci[i] = 0;
         for (int i = tid; i < GV_RED_BYTES / 16; i += pthreads) reinterpret_cast<u32x4_t*>(s_red)[i] = z;
+        if constexpr (F::ZS > 0) {
+            for (int i = tid; i < lu_cnt * OPS; i += pthreads) *reinterpret_cast<u32x4_t*>(s_img + i * OPB + OPB - 16) = z;
+        } else if (M < MS) {  // mode (a), 2 <= M < 8: the slots of rows M..7 read as zero
+            const int dead = MS - M;
+            for (int i = tid; i < lu_cnt * OPS * 8 * dead; i += pthreads) {
+                const int st = i / (8 * dead), rem = i - st * 8 * dead, sl = rem / dead, m = M + (rem - sl * dead);
+                *reinterpret_cast<u32x4_t*>(s_img + st * OPB + (sl * MS + m) * 16) = z;
+            }
+        }
     } else {
         issue(rA);
         issue(rB);
@@ -418,11 +430,12 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
     wg_wait(&s_sync[2], npw);  // the whole operand is in place
 
     // ---- main loop ----
-    // activation operand of this lane: slot, and a mask for structurally zero rows
+    // activation operand of this lane: its slot, or the step's zero slot for rows that
+    // are structurally zero (mode a with M >= 2 zeroes rows M..7 in place instead)
     int aslot;
-    bool alive;
     {
         const int mrow = n & 7;
+        bool alive;
         if constexpr (MODE == MODE_A) {
             aslot = (g * 2 + (n >> 3)) * MS + mrow;
             alive = mrow < M;
@@ -430,10 +443,9 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
             aslot = ((g >> 1) * 2 + (g & 1)) * MS + mrow;
             alive = ((n >> 3) == (g >> 1)) && mrow < M;
         }
-        if (!alive) aslot = 0;
+        if (!alive && F::ZS > 0) aslot = (OPB - 16) / 16;
     }
     const uint8_t* aimg = s_img + aslot * 16;
-    const uint32_t amask = alive ? 0xffffffffu : 0u;
     const int moff = MS == 8 ? 4 * (g & 1) : 0;  // this lane's first output row within the slots
     const uint8_t* rrow = stg + n * RS;           // this lane's weight row in the stage buffer
 
@@ -446,7 +458,6 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
     const uint32_t sel3 = g == 3 ? 0x07060100u : 0x03020100u;
     const int dsh = g < 2 ? 0 : 16;
 
-    auto masked = [&](u32x4_t v) { return u32x4_t{v[0] & amask, v[1] & amask, v[2] & amask, v[3] & amask}; };
 
     auto compute = [&](int lu0, int tile) {
 #pragma unroll
@@ -459,7 +470,7 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
                 const uint32_t E = lds32(rp + (g < 2 ? 0 : 32));
                 const uint32_t b3 = __builtin_amdgcn_perm(E, x3, selp);
                 const i32x4_t B = {(int)x0, (int)x1, (int)x2, (int)b3};
-                const i32x4_t A = __builtin_bit_cast(i32x4_t, masked(lds128(aimg + lu * OPB)));
+                const i32x4_t A = __builtin_bit_cast(i32x4_t, lds128(aimg + lu * OPB));
                 const i32x4_t C = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, zi, 0, 0, 0);
                 const float dw = (float)__builtin_bit_cast(_Float16, (uint16_t)(E >> dsh));
                 const float* dxp = s_scf + lu * 2 * MS + (g >> 1) * MS + moff;
@@ -484,8 +495,8 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
                 const uint8_t* xo = rp + 36 + 8 * g;
                 const half8_t Be = i8x8_to_f16(lds32(xe), __builtin_amdgcn_perm(E0, lds32(xe + 4), sel3));
                 const half8_t Bo = i8x8_to_f16(lds32(xo), lds32(xo + 4));
-                const half8_t Ae = __builtin_bit_cast(half8_t, masked(lds128(aimg + (2 * lu) * OPB)));
-                const half8_t Ao = __builtin_bit_cast(half8_t, masked(lds128(aimg + (2 * lu + 1) * OPB)));
+                const half8_t Ae = __builtin_bit_cast(half8_t, lds128(aimg + (2 * lu) * OPB));
+                const half8_t Ao = __builtin_bit_cast(half8_t, lds128(aimg + (2 * lu + 1) * OPB));
                 const f32x4_t Ce = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ae, Be, zf, 0, 0, 0);
                 const f32x4_t Co = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ao, Bo, zf, 0, 0, 0);
                 const float de = f16lo(E0), dd = f16hi(E8);
@@ -506,7 +517,7 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
                     for (int h = 0; h < 2; ++h) {
                         const i32x4_t B = {(int)((Qv[0] >> (4 * h)) & 0x0f0f0f0fu), (int)((Qv[1] >> (4 * h)) & 0x0f0f0f0fu),
                                            (int)((Qv[2] >> (4 * h)) & 0x0f0f0f0fu), (int)((Qv[3] >> (4 * h)) & 0x0f0f0f0fu)};
-                        const i32x4_t A = __builtin_bit_cast(i32x4_t, masked(lds128(aimg + (lu * 4 + 2 * cc + h) * OPB)));
+                        const i32x4_t A = __builtin_bit_cast(i32x4_t, lds128(aimg + (lu * 4 + 2 * cc + h) * OPB));
                         const i32x4_t C = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, zi, 0, 0, 0);
                         const int scj = (int)(((cc ? sc_hi : sc_lo) >> (8 * h)) & 0xffu);
 #pragma unroll
@@ -570,7 +581,7 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
                     for (int h = 0; h < 2; ++h) {
                         const int jj = 2 * c + h;
                         const half8_t B = nib8_to_f16(Qv[0], Qv[1], 4 * h);
-                        const half8_t A = __builtin_bit_cast(half8_t, masked(lds128(aimg + (lu * 8 + jj) * OPB)));
+                        const half8_t A = __builtin_bit_cast(half8_t, lds128(aimg + (lu * 8 + jj) * OPB));
                         const f32x4_t C = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, zf, 0, 0, 0);
                         const float dsc = d * (float)((sc4[jj >> 2] >> (8 * (jj & 3))) & 0xffu);
                         const float dmm = dmin * (float)((mn4[jj >> 2] >> (8 * (jj & 3))) & 0xffu);
