@@ -65,14 +65,17 @@ QMM_DEV void i8x4_to_f16(uint32_t d, uint32_t& p01, uint32_t& p23)
 
 // Eight 4-bit values selected by `shift` (0: low nibbles, 4: high nibbles) of
 // the bytes of (d0, d1) -> eight exact f16, element order [0,2,1,3,4,6,5,7].
-QMM_DEV half8_t nib8_to_f16(uint32_t d0, uint32_t d1, int shift)
+// The caller keeps m = 0x000f000f and c = 0x64006400 in registers, so each
+// pair of values is one bit-field insert (f16 bits 0x640N = 1024 + N) and one
+// packed subtraction of 1024.
+QMM_DEV half8_t nib8_to_f16(uint32_t d0, uint32_t d1, int shift, uint32_t m, uint32_t c)
 {
     const half2_t bias = {(_Float16)-1024.0f, (_Float16)-1024.0f};
-    uint32_t s0 = d0 >> shift, s1 = d1 >> shift;
-    uint32_t w0 = (s0 & 0x000f000fu) | 0x64006400u;
-    uint32_t w1 = ((s0 >> 8) & 0x000f000fu) | 0x64006400u;
-    uint32_t w2 = (s1 & 0x000f000fu) | 0x64006400u;
-    uint32_t w3 = ((s1 >> 8) & 0x000f000fu) | 0x64006400u;
+    const uint32_t s0 = d0 >> shift, s1 = d1 >> shift;
+    const uint32_t w0 = (s0 & m) | (c & ~m);
+    const uint32_t w1 = ((s0 >> 8) & m) | (c & ~m);
+    const uint32_t w2 = (s1 & m) | (c & ~m);
+    const uint32_t w3 = ((s1 >> 8) & m) | (c & ~m);
     half2_t h0 = __builtin_bit_cast(half2_t, w0) + bias;
     half2_t h1 = __builtin_bit_cast(half2_t, w1) + bias;
     half2_t h2 = __builtin_bit_cast(half2_t, w2) + bias;

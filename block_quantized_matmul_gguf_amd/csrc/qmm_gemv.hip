@@ -457,6 +457,9 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
     // Q8_0 mode a: k-group 3 of the even block takes q30, q31, q0, q1
     const uint32_t sel3 = g == 3 ? 0x07060100u : 0x03020100u;
     const int dsh = g < 2 ? 0 : 16;
+    // Q4_K mode a: nibble decode constants, held in registers (opaque to constant folding)
+    uint32_t nibm = 0x000f000fu, nibc = 0x64006400u;
+    asm volatile("" : "+v"(nibm), "+v"(nibc));
 
 
     auto compute = [&](int lu0, int tile) {
@@ -580,7 +583,7 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
                         const int jj = 2 * c + h;
-                        const half8_t B = nib8_to_f16(Qv[0], Qv[1], 4 * h);
+                        const half8_t B = nib8_to_f16(Qv[0], Qv[1], 4 * h, nibm, nibc);
                         const half8_t A = __builtin_bit_cast(half8_t, lds128(aimg + (lu * 8 + jj) * OPB));
                         const f32x4_t C = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, zf, 0, 0, 0);
                         const float dsc = d * (float)((sc4[jj >> 2] >> (8 * (jj & 3))) & 0xffu);
