@@ -118,9 +118,9 @@ static size_t layout(qmm_plan* p, char* base)
     // prefill path
     if (p->M_max > GEMV_MAX_M) {
         const int64_t M = p->M_max;
-        p->gm.a0 = (_Float16*)take(2 * M * K);
-        p->gm.a1 = (_Float16*)take(2 * M * K);
-        p->gm.rs = (float*)take(4 * M);
+        p->gm.a0 = (_Float16*)take(2 * M * K);  // mode (b): int8 values, or f16 for the block sums
+        p->gm.a1 = (_Float16*)take(a ? 2 * M * K : 0);
+        p->gm.rs = (float*)take(a ? 4 * M : 0);
         p->gm.xs = (_Float16*)take(q4 ? 2 * M * (K / 256) * 16 : 0);
         p->gm.sd = (float*)take(a ? 0 : 4 * M * units);
         p->gm.sbs = (int32_t*)take(q4 && !a ? 4 * M * (K / 32) : 0);

@@ -79,8 +79,6 @@ struct GemmCfg {
     static_assert((8 * BM) % NT == 0, "activation chunks must split evenly between hi and lo");
 };
 
-QMM_DEV uint32_t clamp_u32(int64_t v) { return v > 0xffffffffll ? 0xffffffffu : (uint32_t)v; }
-
 template <int FMT, int WM, int WN, int TM, int TN>
 __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_kernel(GemmArgs a)
 {
@@ -712,6 +710,7 @@ hipError_t launch_gemm(int fmt, int mode, const void* w, int64_t N, int64_t K, i
         else hipLaunchKernelGGL(gemm_sums_kernel<FMT_Q4_K>, grid, dim3(256), 0, s, a);
         return hipGetLastError();
     }
+    if (mode == MODE_B) return launch_gemm_q(fmt, w, N, K, M, b, y, s);
     GemmArgs a{};
     a.w = (const uint8_t*)w;
     a.row_bytes = row_bytes;

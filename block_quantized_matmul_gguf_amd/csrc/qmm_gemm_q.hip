@@ -1,0 +1,461 @@
+// qmm_gemm_q.hip -- prefill kernel (M > 8) for mode (b) on the int8 matrix cores.
+//
+// Mode (b) quantizes every activation row first (Q8_0 blocks of 32 values for
+// Q8_0 weights, Q8K blocks of 256 for Q4_K) and sums integer products block by
+// block, each integer block sum scaled by the weight and activation block
+// scales (page "同一个 GGUF，CPU 和 Metal 生成的文字不一样", section 出处).
+// Here every 32-value block is one v_mfma_i32_32x32x32_i8: int8 activations
+// against int8 weights (Q8_0: q; Q4_K: the 4-bit values 0..15) give the exact
+// int32 block sums S of a 32 x 32 output tile, which are scaled in f32:
+//   Q8_0: acc += (d_x * d_w) * S                  for every block;
+//   Q4_K: acc += (d_x * d * sc_j) * S_j           for every sub-block j,
+//         acc -= (d_x * dmin) * sum_j m_j * bsum_j once per super-block.
+// The mins term is one v_mfma_f32_32x32x16_f16 on exact f16 operands: m_j
+// against the activation's 32-value sums bsum_j, each split into a multiple
+// of 64 and a remainder in [0, 63] (exact f16 integers), so the f32 result is
+// the exact integer sum.
+//
+// A 256-thread workgroup owns a 64 x (32*TN) output tile; two run on each
+// compute unit.  Its four waves are two row halves times two K groups: K
+// advances 64 values (two blocks) per stage, group g takes block g of every
+// stage over all 32*TN columns, and the two groups' partial sums are added
+// through LDS at the end.  A stage's activation bytes, raw weight bytes and
+// scales are loaded to registers two stages ahead and written to the idle LDS
+// buffer at the start of the next stage; one barrier per stage.  Consecutive
+// lanes load consecutive 16-byte pieces of one weight row, so that a load
+// instruction touches few rows; the Q8_0 blocks (two bytes of scale before
+// their values) are realigned in registers with one lane exchange and a byte
+// permute per dword.
+#include <map>
+#include <mutex>
+#include <set>
+#include <type_traits>
+#include <utility>
+
+#include "qmm_device.h"
+
+namespace qmm {
+
+struct QGemmArgs {
+    const uint8_t* w;
+    int64_t row_bytes;
+    int N, K, M;
+    int nm;               // row tiles of the output
+    int remap;            // 1: give each XCD a contiguous run of tiles
+    const int8_t* q;      // quantized activations [M][K]
+    const float* dx;      // activation block scales, block-major: Q8_0 [K/32][M], Q8K [K/256][M]
+    const _Float16* bsx;  // Q8K: [K/256][M][16] sub-block sums, multiples of 64 then remainders
+    float* y;
+};
+
+
+// An LDS row of one block: 32 int8 as two 16-byte halves; half h of row r
+// sits in slot h ^ ((r >> 3) & 1), so the 16 rows an MFMA operand read
+// touches at once cover all banks.
+QMM_DEV uint32_t qswz(int row, int h) { return (uint32_t)(row * 32 + ((h ^ ((row >> 3) & 1)) << 4)); }
+
+// MW waves of 32 rows per K group: BM = 32*MW rows, 128*MW threads.
+template <int FMT, int MW, int TN>
+struct QCfg {
+    static constexpr bool Q8 = FMT == FMT_Q8_0;
+    static constexpr int Q_BM = 32 * MW, Q_NT = 128 * MW;
+    static constexpr int BN = 32 * TN;
+    static constexpr int A_BLK = Q_BM * 32;  // one block of the activation tile, bytes
+    static constexpr int B_BLK = BN * 32;
+    // [buffer][block] images of the activation and weight tiles and d_x
+    // [buffer][block][BM] f32.  Column scales: Q8_0 d_w [buffer][block][BN]
+    // f32; Q4_K, by super-block parity, d * sc_j [2][8][BN] f32, dmin [2][BN]
+    // f32, m_j [2][BN][8] f16 and the activation sub-block sums [2][BM][16] f16.
+    static constexpr int OFF_A = 0;
+    static constexpr int OFF_B = OFF_A + 4 * A_BLK;
+    static constexpr int OFF_DX = OFF_B + 4 * B_BLK;
+    static constexpr int OFF_DW = OFF_DX + 4 * Q_BM * 4;
+    static constexpr int OFF_DMIN = OFF_DW + (Q8 ? 4 : 16) * BN * 4;
+    static constexpr int OFF_MJ = OFF_DMIN + 2 * BN * 4;
+    static constexpr int OFF_BSX = OFF_MJ + 2 * BN * 16;
+    static constexpr int STAGE_BYTES = Q8 ? OFF_DMIN : OFF_BSX + 2 * Q_BM * 32;
+    static constexpr int RED_BYTES = Q_BM * BN * 4;  // the K groups' sum
+    static constexpr int BYTES = STAGE_BYTES > RED_BYTES ? STAGE_BYTES : RED_BYTES;
+    // weight load units per thread: Q8_0 (row, 16-byte quarter of the stage's
+    // 64 bytes); Q4_K (row, 16-byte half of the stage's 32 nibble bytes)
+    static constexpr int UNITS = (Q8 ? 4 : 2) * BN;
+    static constexpr int BU = (UNITS + Q_NT - 1) / Q_NT;
+};
+
+template <int FMT, int MW, int TN>
+__global__ __launch_bounds__(128 * MW, 2) void gemm_q_kernel(QGemmArgs a)
+{
+    using C = QCfg<FMT, MW, TN>;
+    constexpr int BN = C::BN, BU = C::BU, Q_BM = C::Q_BM, Q_NT = C::Q_NT;
+    constexpr bool Q8 = C::Q8;
+    extern __shared__ __align__(16) uint8_t lds[];
+
+    const int M = a.M, N = a.N, K = a.K;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    int t = blockIdx.x;
+    if (a.remap) {
+        const int per = (int)gridDim.x >> 3;
+        t = (t & 7) * per + (t >> 3);
+    }
+    const int m0 = (t % a.nm) * Q_BM, n0 = (t / a.nm) * BN;
+    const int wm = (wave % MW) * 32, g = wave / MW;
+    const int l32 = lane & 31, hl = lane >> 5;
+    const int nst = K / 64;
+    const int nsc = Q8 ? K / 32 : K / 256;  // activation scales per row
+    const int64_t rb = a.row_bytes;
+
+    // Loads past the end of a resource return zeros.  The block-major scale
+    // arrays are covered whole: a row past M reads another row's (finite)
+    // values, which reach only that row's discarded outputs.
+    const rsrc_t rq = make_rsrc(a.q + (int64_t)m0 * K, clamp_u32((int64_t)(M - m0) * K));
+    const rsrc_t rdxs = make_rsrc(a.dx, clamp_u32((int64_t)nsc * M * 4));
+    const rsrc_t rw = make_rsrc(a.w + (int64_t)n0 * rb, clamp_u32((int64_t)(N - n0) * rb));
+    const rsrc_t rbs = make_rsrc(Q8 ? nullptr : a.bsx, Q8 ? 0u : clamp_u32((int64_t)(K / 256) * M * 32));
+
+    // ---- staging roles, fixed for the whole K loop ----
+    // activations: (row, 16-byte part of the stage's 64 bytes)
+    const int arow = tid >> 2, apart = tid & 3;
+    const uint32_t ag = (uint32_t)(arow * K + 16 * apart);
+    const uint32_t as_ = (uint32_t)((apart >> 1) * C::A_BLK + qswz(arow, apart & 1));
+    // activation scales (waves 0..MW/2-1): one row per lane
+    const int drow = tid & (Q_BM - 1);
+    const uint32_t dg = (uint32_t)((m0 + drow) * 4);
+    // weight units, consecutive lanes along a row so that a load instruction
+    // touches few rows; threads past the last unit repeat earlier ones (same
+    // values to the same places)
+    uint32_t bg[BU];
+    int brow[BU];
+    const int bp = Q8 ? (tid & 3) : (tid & 1);  // the unit's part of its row
+#pragma unroll
+    for (int i = 0; i < BU; ++i) {
+        const int u = (tid + Q_NT * i) % C::UNITS;
+        brow[i] = Q8 ? u >> 2 : u >> 1;
+        bg[i] = (uint32_t)(brow[i] * rb + (Q8 ? 16 * bp : 0));
+    }
+    // Q8_0 realignment: a stage's 68 bytes are d0 q0..q31 d1 q0..q31; quarter
+    // p holds bytes 16p..16p+15 and needs the next dword (the next quarter's
+    // first; bytes 64..67 for the last): parts 0, 1 shift by 2 bytes (block 0,
+    // halves 0 and 1), parts 2, 3 by 4 (block 1).
+    const uint32_t psel = bp < 2 ? 0x05040302u : 0x07060504u;
+    // Q4_K activation sub-block sums (waves 0..MW-1): (row, half)
+    const int xrow = (tid >> 1) & (Q_BM - 1), xpart = tid & 1;
+    const uint32_t xg = (uint32_t)(((m0 + xrow) * 16 + 8 * xpart) * 2);
+
+    // ---- staging registers ----
+    uint4 ra;
+    u32x2_t rdx;
+    uint4 rw4[BU];
+    uint32_t rtail[Q8 ? BU : 1];
+    uint4 rhd[Q8 ? 1 : BU];
+    uint4 rbx;
+
+    auto load = [&](int st) {
+        ra = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, ag, 64 * st, 0));
+        if (wave < MW / 2) {
+            if constexpr (Q8) {
+                rdx[0] = __builtin_amdgcn_raw_buffer_load_b32(rdxs, dg, 2 * st * M * 4, 0);
+                rdx[1] = __builtin_amdgcn_raw_buffer_load_b32(rdxs, dg, (2 * st + 1) * M * 4, 0);
+            } else {
+                rdx[0] = __builtin_amdgcn_raw_buffer_load_b32(rdxs, dg, (st >> 2) * M * 4, 0);
+            }
+        }
+        if constexpr (Q8) {
+#pragma unroll
+            for (int i = 0; i < BU; ++i) {
+                rw4[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, bg[i], 68 * st, 0));
+                if (bp == 3) rtail[i] = __builtin_amdgcn_raw_buffer_load_b32(rw, bg[i] + 16, 68 * st, 0);
+            }
+        } else {
+            const int sb = st >> 2, c = st & 3;
+#pragma unroll
+            for (int i = 0; i < BU; ++i) {
+                rw4[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, bg[i] + 16 + 32 * c + 16 * bp, 144 * sb, 0));
+                if (c == 0) rhd[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, bg[i], 144 * sb, 0));
+            }
+            if (c == 0 && wave < MW)
+                rbx = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rbs, xg, sb * M * 32, 0));
+        }
+    };
+
+    // registers of stage st -> LDS buffer P
+    auto store = [&](int st, auto pc) {
+        constexpr int P = decltype(pc)::value;
+        *reinterpret_cast<uint4*>(lds + C::OFF_A + P * 2 * C::A_BLK + as_) = ra;
+        if (wave < MW / 2) {
+            float* sdx = reinterpret_cast<float*>(lds + C::OFF_DX) + P * 2 * Q_BM;
+            sdx[drow] = __uint_as_float(rdx[0]);
+            sdx[Q_BM + drow] = __uint_as_float(Q8 ? rdx[1] : rdx[0]);
+        }
+        uint8_t* sb_ = lds + C::OFF_B + P * 2 * C::B_BLK;
+        if constexpr (Q8) {
+            float* sdw = reinterpret_cast<float*>(lds + C::OFF_DW) + P * 2 * BN;
+#pragma unroll
+            for (int i = 0; i < BU; ++i) {
+                const uint4 v = rw4[i];
+                const uint32_t nx = (uint32_t)__builtin_amdgcn_update_dpp((int)v.x, (int)v.x, 0xF9, 0xF, 0xF, false);
+                const uint32_t e = bp == 3 ? rtail[i] : nx;
+                const uint4 o = make_uint4(__builtin_amdgcn_perm(v.y, v.x, psel), __builtin_amdgcn_perm(v.z, v.y, psel),
+                                           __builtin_amdgcn_perm(v.w, v.z, psel), __builtin_amdgcn_perm(e, v.w, psel));
+                *reinterpret_cast<uint4*>(sb_ + (bp >> 1) * C::B_BLK + qswz(brow[i], bp & 1)) = o;
+                if (bp == 0) sdw[brow[i]] = f16lo(v.x);
+                if (bp == 2) sdw[BN + brow[i]] = f16hi(v.x);
+            }
+        } else {
+            const int sb = st >> 2, c = st & 3, par = sb & 1;
+#pragma unroll
+            for (int i = 0; i < BU; ++i) {
+                const uint4 nb = rw4[i];
+                const uint32_t mk = 0x0f0f0f0fu;
+                // low nibbles: sub-block 2c (block 0 of the stage); high: 2c+1
+                *reinterpret_cast<uint4*>(sb_ + qswz(brow[i], bp)) = make_uint4(nb.x & mk, nb.y & mk, nb.z & mk, nb.w & mk);
+                *reinterpret_cast<uint4*>(sb_ + C::B_BLK + qswz(brow[i], bp)) =
+                    make_uint4((nb.x >> 4) & mk, (nb.y >> 4) & mk, (nb.z >> 4) & mk, (nb.w >> 4) & mk);
+                if (c == 0) {
+                    const uint4 hd = rhd[i];
+                    if (bp == 0) {  // d * sc_j for the eight sub-blocks
+                        const float d = f16lo(hd.x);
+                        float* sds = reinterpret_cast<float*>(lds + C::OFF_DW) + par * 8 * BN + brow[i];
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            int sc, mn;
+                            q4k_scale_min(hd.y, hd.z, hd.w, j, sc, mn);
+                            sds[j * BN] = d * (float)sc;
+                        }
+                    } else {  // dmin and the mins m_j
+                        reinterpret_cast<float*>(lds + C::OFF_DMIN)[par * BN + brow[i]] = f16hi(hd.x);
+                        half8_t mj;
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            int sc, mn;
+                            q4k_scale_min(hd.y, hd.z, hd.w, j, sc, mn);
+                            mj[j] = (_Float16)(float)mn;
+                        }
+                        *reinterpret_cast<half8_t*>(lds + C::OFF_MJ + (par * BN + brow[i]) * 16) = mj;
+                    }
+                }
+            }
+            if (c == 0 && wave < MW)
+                *reinterpret_cast<uint4*>(lds + C::OFF_BSX + par * Q_BM * 32 + qswz(xrow, xpart)) = rbx;
+        }
+    };
+
+    f32x16_t acc[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
+    const i32x16_t izero = {};
+    const f32x16_t fzero = {};
+
+    // block g of stage st out of buffer P
+    auto compute = [&](int st, auto pc) {
+        constexpr int P = decltype(pc)::value;
+        const uint8_t* sa = lds + C::OFF_A + (P * 2 + g) * C::A_BLK;
+        const uint8_t* sbb = lds + C::OFF_B + (P * 2 + g) * C::B_BLK;
+        const i32x4_t af = *reinterpret_cast<const i32x4_t*>(sa + qswz(wm + l32, hl));
+        const float* sdw = reinterpret_cast<const float*>(lds + C::OFF_DW) + l32 +
+                           (Q8 ? (P * 2 + g) * BN : (((st >> 2) & 1) * 8 + 2 * (st & 3) + g) * BN);
+        i32x4_t bn = *reinterpret_cast<const i32x4_t*>(sbb + qswz(l32, hl));
+        float dwn = sdw[0];
+        // d_x of this lane's 16 output rows wm + 8q + 4hl + (0..3)
+        float dxv[16];
+        const float* sdx = reinterpret_cast<const float*>(lds + C::OFF_DX) + (P * 2 + g) * Q_BM + wm + 4 * hl;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 v = *reinterpret_cast<const float4*>(sdx + 8 * q);
+            dxv[4 * q] = v.x; dxv[4 * q + 1] = v.y; dxv[4 * q + 2] = v.z; dxv[4 * q + 3] = v.w;
+        }
+        i32x16_t cp;
+        float dwp = 0.0f;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const i32x4_t bf = bn;
+            const float dw = dwn;
+            const i32x16_t cv = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bf, izero, 0, 0, 0);
+            // next tile's operand while this one is in the matrix cores
+            if (j + 1 < TN) {
+                bn = *reinterpret_cast<const i32x4_t*>(sbb + qswz(32 * (j + 1) + l32, hl));
+                dwn = sdw[32 * (j + 1)];
+            }
+            // scale the previous tile's sums
+            if (j > 0) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[j - 1][r] = __builtin_fmaf(dxv[r] * dwp, (float)cp[r], acc[j - 1][r]);
+                asm volatile("" : "+v"(acc[j - 1]));  // done here, not sunk past the staging
+            }
+            cp = cv;
+            dwp = dw;
+            // keep one tile's sums in flight: hoisting the MFMAs ahead would
+            // hold all TN results at once
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[TN - 1][r] = __builtin_fmaf(dxv[r] * dwp, (float)cp[r], acc[TN - 1][r]);
+        asm volatile("" : "+v"(acc[TN - 1]));
+
+        if constexpr (!Q8) {
+            if ((st & 3) == 3) {  // end of a super-block: the mins term, tiles of this group's parity
+                const int par = (st >> 2) & 1;
+                const half8_t ax = *reinterpret_cast<const half8_t*>(lds + C::OFF_BSX + par * Q_BM * 32 + qswz(wm + l32, hl));
+                const float* sdm = reinterpret_cast<const float*>(lds + C::OFF_DMIN) + par * BN + l32;
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    if ((j & 1) != g) continue;
+                    const half8_t bm = *reinterpret_cast<const half8_t*>(lds + C::OFF_MJ + (par * BN + 32 * j + l32) * 16);
+                    const float dm = sdm[32 * j];
+                    const f32x16_t cm = __builtin_amdgcn_mfma_f32_32x32x16_f16(ax, bm, fzero, 0, 0, 0);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[j][r] = __builtin_fmaf(-dxv[r] * dm, cm[r], acc[j][r]);
+                }
+            }
+        }
+    };
+
+    // The registers hold the stage after the one in LDS: each iteration first
+    // writes them to the idle buffer, then loads the stage after that, so a
+    // load has a whole stage of MFMAs to arrive.  Past the end the last stage
+    // is restaged into the idle buffer rather than branch.
+    const int last = nst - 1;
+    load(0);
+    store(0, std::integral_constant<int, 0>{});
+    load(nst > 1 ? 1 : 0);
+    __syncthreads();
+    auto iter = [&](int st, auto pc) {
+        constexpr int P = decltype(pc)::value;
+        store(st + 1 < nst ? st + 1 : last, std::integral_constant<int, P ^ 1>{});
+        load(st + 2 < nst ? st + 2 : last);
+        compute(st, pc);
+        __syncthreads();
+    };
+    int st = 0;
+    for (; st + 1 < nst; st += 2) {
+        iter(st, std::integral_constant<int, 0>{});
+        iter(st + 1, std::integral_constant<int, 1>{});
+    }
+    if (st < nst) iter(st, std::integral_constant<int, 0>{});
+
+    // group 1 hands its sums to group 0 through LDS, which writes the tile
+    float* red = reinterpret_cast<float*>(lds);
+    auto crow = [&](int r) { return wm + 8 * (r >> 2) + 4 * hl + (r & 3); };
+    if (g == 1) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) red[crow(r) * BN + 32 * j + l32] = acc[j][r];
+    }
+    __syncthreads();
+    if (g == 0) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int n = n0 + 32 * j + l32;
+            if (n >= N) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = m0 + crow(r);
+                if (m < M) a.y[(int64_t)m * N + n] = acc[j][r] + red[crow(r) * BN + 32 * j + l32];
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------ launchers ----
+
+// Raises a kernel's dynamic LDS limit to what it needs, once per device.
+static void allow_lds_q(const void* k, int bytes)
+{
+    static std::set<std::pair<int, const void*>> done;
+    static std::mutex mu;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!done.insert(std::make_pair(dev, k)).second) return;
+    (void)hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    (void)hipGetLastError();
+}
+
+static int cu_count_q()
+{
+    static std::map<int, int> cache;
+    static std::mutex mu;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(dev);
+    if (it != cache.end()) return it->second;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 1;
+    (void)hipGetLastError();
+    return cache[dev] = cus;
+}
+
+struct QTile {
+    int mw, tn;
+};
+// Tiles, (32*MW) x (32*TN): 64 x 224 puts two tiles on each of 256 compute
+// units on 512 x 14336, 128 x 224 one.
+static const QTile kQTiles[] = {{4, 7}, {2, 7}, {2, 4}, {2, 2}};
+
+// The tile whose busiest compute unit does the least work: rounds times the
+// tile's area, weighted by its operand reads per output.
+static QTile pick_qtile(int64_t M, int64_t N)
+{
+    const int64_t cus = cu_count_q();
+    QTile best = kQTiles[0];
+    double bc = -1.0;
+    for (const QTile& t : kQTiles) {
+        const int64_t bm = 32 * t.mw, bn = 32 * t.tn, slots = cus * (t.mw == 4 ? 1 : 2);
+        const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+        const double cost = (double)((tiles + slots - 1) / slots) * (double)(bm * bn) * (t.mw == 4 ? 0.5 : 1.0) *
+                            (1.0 + 8.0 / bn + 16.0 / bm);
+        if (bc < 0 || cost < bc) {
+            bc = cost;
+            best = t;
+        }
+    }
+    return best;
+}
+
+template <int FMT, int MW, int TN>
+static hipError_t launch_q(QGemmArgs a, hipStream_t s)
+{
+    using C = QCfg<FMT, MW, TN>;
+    const int nm = (a.M + C::Q_BM - 1) / C::Q_BM, nn = (a.N + C::BN - 1) / C::BN;
+    const int64_t grid = (int64_t)nm * nn;
+    if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    a.nm = nm;
+    a.remap = grid % 8 == 0 ? 1 : 0;
+    const void* k = (const void*)gemm_q_kernel<FMT, MW, TN>;
+    allow_lds_q(k, C::BYTES);
+    void* args[] = {&a};
+    return hipLaunchKernel(k, dim3((unsigned)grid), dim3(C::Q_NT), args, C::BYTES, s);
+}
+
+template <int FMT>
+static hipError_t launch_q_fmt(const QGemmArgs& a, QTile t, hipStream_t s)
+{
+    if (t.mw == 4) return launch_q<FMT, 4, 7>(a, s);
+    if (t.tn == 7) return launch_q<FMT, 2, 7>(a, s);
+    if (t.tn == 4) return launch_q<FMT, 2, 4>(a, s);
+    return launch_q<FMT, 2, 2>(a, s);
+}
+
+hipError_t launch_gemm_q(int fmt, const void* w, int64_t N, int64_t K, int64_t M, const GemmBufs& b, float* y,
+                         hipStream_t s)
+{
+    QGemmArgs a{};
+    a.w = (const uint8_t*)w;
+    a.row_bytes = fmt == FMT_Q8_0 ? (K / 32) * 34 : (K / 256) * 144;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.M = (int)M;
+    a.q = (const int8_t*)b.a0;
+    a.dx = b.sd;
+    a.bsx = b.xs;
+    a.y = y;
+    const QTile t = pick_qtile(M, N);
+    const hipError_t e = fmt == FMT_Q8_0 ? launch_q_fmt<FMT_Q8_0>(a, t, s) : launch_q_fmt<FMT_Q4_K>(a, t, s);
+    if (e != hipSuccess) return e;
+    return hipGetLastError();
+}
+
+}  // namespace qmm

@@ -38,11 +38,13 @@ struct GemvBufs {
 
 // Device buffers of the prefill path.
 struct GemmBufs {
-    _Float16* a0;   // hi part of the scaled activation rows [M][K] (block-sums hook: quantized values as f16)
+    _Float16* a0;   // mode (a): hi part of the scaled activation rows [M][K]; mode (b): the quantized
+                    // activations as int8 [M][K] (block-sums hook: as f16)
     _Float16* a1;   // lo part [M][K]
     float* rs;      // 1/s per row [M]
-    _Float16* xs;   // Q4_K: hi and lo of s * (sub-block sums) / 32, [M][K/256][16]
-    float* sd;      // block-sums hook: activation block scales [M][K/32 or K/256]
+    _Float16* xs;   // Q4_K mode (a): hi and lo of s * (sub-block sums) / 32; mode (b): the Q8K
+                    // sub-block sums as multiples of 64 and remainders; [M][K/256][16]
+    float* sd;      // mode (b): activation block scales [M][K/32 or K/256]
     int32_t* sbs;   // block-sums hook, Q4_K: sums of 32 quantized values [M][K/32]
 };
 
@@ -60,5 +62,7 @@ hipError_t launch_gemm_prep(int fmt, int mode, const float* x, int64_t M, int64_
                             hipStream_t s);
 hipError_t launch_gemm(int fmt, int mode, const void* w, int64_t N, int64_t K, int64_t M, const GemmBufs& b,
                        float* y, int32_t* sums, hipStream_t s);
+hipError_t launch_gemm_q(int fmt, const void* w, int64_t N, int64_t K, int64_t M, const GemmBufs& b, float* y,
+                         hipStream_t s);
 
 }  // namespace qmm

@@ -7,10 +7,11 @@
 
 namespace qmm {
 
-enum { LAY_AOS = 0, LAY_GEMM = 2 };
+enum { LAY_AOS = 0, LAY_GEMM = 2, LAY_I8 = 3 };
 
 // One thread per 32-value block.  LAY_AOS: canonical 34-byte blocks.
-// LAY_GEMM: the values as f16 [M][K] plus f32 scales [M][K/32].
+// LAY_GEMM: the values as f16 [M][K] plus f32 scales [M][K/32].  LAY_I8: the
+// values as int8 [M][K] plus f32 scales block-major [K/32][M].
 template <int LAY>
 __global__ __launch_bounds__(256) void quantize_q8_0_kernel(const float* __restrict__ x, int M, int K,
                                                             uint8_t* __restrict__ out, float* __restrict__ sc)
@@ -30,6 +31,15 @@ __global__ __launch_bounds__(256) void quantize_q8_0_kernel(const float* __restr
         o[0] = dbits;
 #pragma unroll
         for (int j = 0; j < 16; ++j) o[1 + j] = (uint16_t)((uint8_t)q[2 * j] | ((uint16_t)(uint8_t)q[2 * j + 1] << 8));
+    } else if (LAY == LAY_I8) {
+        uint4* o = reinterpret_cast<uint4*>(out + (int64_t)m * K + 32 * b);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            o[i] = make_uint4(pack4(q[16 * i], q[16 * i + 1], q[16 * i + 2], q[16 * i + 3]),
+                              pack4(q[16 * i + 4], q[16 * i + 5], q[16 * i + 6], q[16 * i + 7]),
+                              pack4(q[16 * i + 8], q[16 * i + 9], q[16 * i + 10], q[16 * i + 11]),
+                              pack4(q[16 * i + 12], q[16 * i + 13], q[16 * i + 14], q[16 * i + 15]));
+        sc[(int64_t)b * M + m] = dval;
     } else {
         _Float16* o = reinterpret_cast<_Float16*>(out) + (int64_t)m * K + 32 * b;
 #pragma unroll
@@ -45,11 +55,14 @@ __global__ __launch_bounds__(256) void quantize_q8_0_kernel(const float* __restr
 
 // One wave per 256-value block, four blocks per workgroup.  LAY_AOS: canonical
 // 292-byte blocks.  LAY_GEMM: values as f16 [M][K], f32 scales [M][K/256],
-// int32 sums of 32 consecutive values [M][K/32].
+// int32 sums of 32 consecutive values [M][K/32].  LAY_I8: values as int8
+// [M][K], f32 scales block-major [K/256][M], and per block the eight sums of
+// 32 consecutive values as f16 [K/256][M][16]: first each sum rounded down to
+// a multiple of 64, then the remainders (0..63), all exact.
 template <int LAY>
 __global__ __launch_bounds__(256) void quantize_q8k_kernel(const float* __restrict__ x, int M, int K,
                                                            uint8_t* __restrict__ out, float* __restrict__ sc,
-                                                           int32_t* __restrict__ bs)
+                                                           void* __restrict__ bs)
 {
     const int nsb = K / 256;
     const int lane = threadIdx.x & 63;
@@ -66,13 +79,23 @@ __global__ __launch_bounds__(256) void quantize_q8k_kernel(const float* __restri
         if (lane == 0) *reinterpret_cast<float*>(o) = d;
         *reinterpret_cast<uint32_t*>(o + 4 + 4 * lane) = pack4(q[0], q[1], q[2], q[3]);
         if ((lane & 3) == 0) *reinterpret_cast<int16_t*>(o + 260 + 2 * (lane >> 2)) = (int16_t)s16;
+    } else if (LAY == LAY_I8) {
+        const int pair = s16 + __shfl_down(s16, 4);  // lane 8j: bsums[2j] + bsums[2j+1]
+        *reinterpret_cast<uint32_t*>(out + (int64_t)m * K + 256 * sb + 4 * lane) = pack4(q[0], q[1], q[2], q[3]);
+        if (lane == 0) sc[(int64_t)sb * M + m] = d;
+        if ((lane & 7) == 0) {
+            _Float16* o = reinterpret_cast<_Float16*>(bs) + ((int64_t)sb * M + m) * 16 + (lane >> 3);
+            const int hi = (pair >> 6) * 64;
+            o[0] = (_Float16)(float)hi;
+            o[8] = (_Float16)(float)(pair - hi);
+        }
     } else {
         const int pair = s16 + __shfl_down(s16, 4);  // lane 8j: bsums[2j] + bsums[2j+1]
         _Float16* o = reinterpret_cast<_Float16*>(out) + (int64_t)m * K + 256 * sb + 4 * lane;
         o[0] = (_Float16)(float)q[0]; o[1] = (_Float16)(float)q[1];
         o[2] = (_Float16)(float)q[2]; o[3] = (_Float16)(float)q[3];
         if (lane == 0) sc[(int64_t)m * nsb + sb] = d;
-        if ((lane & 7) == 0) bs[(int64_t)m * (K / 32) + 8 * sb + (lane >> 3)] = pair;
+        if ((lane & 7) == 0) reinterpret_cast<int32_t*>(bs)[(int64_t)m * (K / 32) + 8 * sb + (lane >> 3)] = pair;
     }
 }
 
@@ -266,7 +289,7 @@ hipError_t launch_quantize_act(int act_fmt, const float* x, int64_t M, int64_t K
                            x, (int)M, (int)K, (uint8_t*)out, (float*)nullptr);
     } else {
         hipLaunchKernelGGL(quantize_q8k_kernel<LAY_AOS>, dim3(nblocks(M * (K / 256), 4)), dim3(256), 0, s,
-                           x, (int)M, (int)K, (uint8_t*)out, (float*)nullptr, (int32_t*)nullptr);
+                           x, (int)M, (int)K, (uint8_t*)out, (float*)nullptr, (void*)nullptr);
     }
     return hipGetLastError();
 }
@@ -289,6 +312,15 @@ hipError_t launch_gemm_prep(int fmt, int mode, const float* x, int64_t M, int64_
         else
             hipLaunchKernelGGL(quantize_q8k_kernel<LAY_GEMM>, dim3(nblocks(M * (K / 256), 4)), dim3(256), 0, s,
                                x, (int)M, (int)K, (uint8_t*)b.a0, b.sd, b.sbs);
+        return hipGetLastError();
+    }
+    if (mode == MODE_B) {  // int8 values, block scales (and Q8K sub-block sums) for the int8 kernel
+        if (fmt == FMT_Q8_0)
+            hipLaunchKernelGGL(quantize_q8_0_kernel<LAY_I8>, dim3(nblocks(M * (K / 32), 256)), dim3(256), 0, s,
+                               x, (int)M, (int)K, (uint8_t*)b.a0, b.sd);
+        else
+            hipLaunchKernelGGL(quantize_q8k_kernel<LAY_I8>, dim3(nblocks(M * (K / 256), 4)), dim3(256), 0, s,
+                               x, (int)M, (int)K, (uint8_t*)b.a0, b.sd, (void*)b.xs);
         return hipGetLastError();
     }
     const dim3 grid((unsigned)M), block(256);
