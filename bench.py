@@ -286,6 +286,14 @@ def main():
             "frac": rg["frac_f16_peak"], "algorithmic_flops_per_launch": 2 * rg["M"] * N * K,
             "traffic": traffic_from_profile(f"gemm:{rg['fmt']}:{rg['mode']}:{rg['M']}"),
         }
+    rb = pick("gemm", "q8_0", "b", M_PREFILL)
+    if rb is not None:  # mode (b) prefill runs on the int8 matrix cores
+        out["roofline_gemm_int8"] = {
+            "kernel": f"gemm_q_kernel {rb['fmt']} mode {rb['mode']} M={rb['M']}",
+            "bound": "mfma", "achieved": rb["TOPS"], "peak": PEAK_I8_TOPS, "unit": "TOP/s",
+            "frac": rb["frac_int8_peak"], "algorithmic_ops_per_launch": 2 * rb["M"] * N * K,
+            "traffic": traffic_from_profile(f"gemm:{rb['fmt']}:{rb['mode']}:{rb['M']}"),
+        }
     out["detail"] = detail
     out["wall_s_timed"] = round(wall_s, 3)
     out["setup_s"] = round(setup_s, 1)

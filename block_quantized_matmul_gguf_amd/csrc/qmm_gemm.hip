@@ -1,16 +1,14 @@
-// qmm_gemm.hip -- prefill kernel (M > 8) for y = x . W^T on GGUF blocks.
+// qmm_gemm.hip -- prefill kernel (M > 8) for y = x . W^T on GGUF blocks in
+// mode (a), f32 activations; mode (b) runs on the int8 matrix cores
+// (qmm_gemm_q.hip).
 //
-// Every (format, mode) pair runs one contraction on the matrix cores.  The
-// activation row, scaled by the power of two s that puts its largest value in
-// [2^14, 2^15), enters as an f16 pair hi + lo: in mode (a) x*s itself, in
-// mode (b) the dequantized quantized activation d_x*q_x*s (page "同一个
-// GGUF，CPU 和 Metal 生成的文字不一样", section 出处: the CPU path quantizes
-// the activations, then takes integer block dots scaled by both block
-// scales).  A Q8_0 activation d_x*q_x (an f16 scale times a 7-bit integer) is
-// exact in the pair, so mode (b) reaches sum_b d_w*d_x*S_b with only f32
-// accumulation rounding.  The weights enter as exact f16 integers (Q8_0: q;
-// Q4_K: sc_j*q <= 945).  Two v_mfma_f32_16x16x32_f16 passes (hi, lo) per 32
-// values give sum q*x*s; the weight scales follow in f32:
+// The activation row, scaled by the power of two s that puts its largest
+// value in [2^14, 2^15), enters as an exact f16 pair hi + lo of x*s (page
+// "同一个 GGUF，CPU 和 Metal 生成的文字不一样", section 出处: the Metal path
+// keeps the activations in f32 and dequantizes the weights in the kernel).
+// The weights enter as exact f16 integers (Q8_0: q; Q4_K: sc_j*q <= 945).
+// Two v_mfma_f32_16x16x32_f16 passes (hi, lo) per 32 values give sum q*x*s;
+// the weight scales follow in f32:
 //   Q8_0: acc += d * C after every 32-value block;
 //   Q4_K: acc += d * C - dmin * Cmin after every super-block, where
 //         Cmin = sum_j m_j * (s * sum of x over sub-block j) is one more MFMA

@@ -54,12 +54,15 @@ struct QGemmArgs {
 // touches at once cover all banks.
 QMM_DEV uint32_t qswz(int row, int h) { return (uint32_t)(row * 32 + ((h ^ ((row >> 3) & 1)) << 4)); }
 
-// MW waves of 32 rows per K group: BM = 32*MW rows, 128*MW threads.
-template <int FMT, int MW, int TN>
+// MW waves of 32 rows per K group: BM = 32*MW rows, 128*MW threads.  A
+// stage is KB block pairs, 64*KB values: group g takes blocks g, g+2, ...
+template <int FMT, int MW, int TN, int KB>
 struct QCfg {
     static constexpr bool Q8 = FMT == FMT_Q8_0;
     static constexpr int Q_BM = 32 * MW, Q_NT = 128 * MW;
     static constexpr int BN = 32 * TN;
+    static constexpr int SB = 2 * KB;        // blocks per stage
+    static constexpr int SV = 32 * SB;       // values per stage
     static constexpr int A_BLK = Q_BM * 32;  // one block of the activation tile, bytes
     static constexpr int B_BLK = BN * 32;
     // [buffer][block] images of the activation and weight tiles and d_x
@@ -67,26 +70,30 @@ struct QCfg {
     // f32; Q4_K, by super-block parity, d * sc_j [2][8][BN] f32, dmin [2][BN]
     // f32, m_j [2][BN][8] f16 and the activation sub-block sums [2][BM][16] f16.
     static constexpr int OFF_A = 0;
-    static constexpr int OFF_B = OFF_A + 4 * A_BLK;
-    static constexpr int OFF_DX = OFF_B + 4 * B_BLK;
-    static constexpr int OFF_DW = OFF_DX + 4 * Q_BM * 4;
-    static constexpr int OFF_DMIN = OFF_DW + (Q8 ? 4 : 16) * BN * 4;
+    static constexpr int OFF_B = OFF_A + 2 * SB * A_BLK;
+    static constexpr int OFF_DX = OFF_B + 2 * SB * B_BLK;
+    static constexpr int OFF_DW = OFF_DX + 2 * SB * Q_BM * 4;
+    static constexpr int OFF_DMIN = OFF_DW + (Q8 ? 2 * SB : 16) * BN * 4;
     static constexpr int OFF_MJ = OFF_DMIN + 2 * BN * 4;
     static constexpr int OFF_BSX = OFF_MJ + 2 * BN * 16;
     static constexpr int STAGE_BYTES = Q8 ? OFF_DMIN : OFF_BSX + 2 * Q_BM * 32;
     static constexpr int RED_BYTES = Q_BM * BN * 4;  // the K groups' sum
     static constexpr int BYTES = STAGE_BYTES > RED_BYTES ? STAGE_BYTES : RED_BYTES;
-    // weight load units per thread: Q8_0 (row, 16-byte quarter of the stage's
-    // 64 bytes); Q4_K (row, 16-byte half of the stage's 32 nibble bytes)
-    static constexpr int UNITS = (Q8 ? 4 : 2) * BN;
+    static constexpr int AU = Q_BM * 2 * SB / Q_NT;  // 16-byte activation pieces per thread
+    // weight load units: Q8_0 (row, block pair, 16-byte quarter of its 64
+    // bytes); Q4_K (row, 32-byte chunk, 16-byte half)
+    static constexpr int UPR = Q8 ? 4 * KB : 2 * KB;  // units per row
+    static constexpr int UNITS = UPR * BN;
     static constexpr int BU = (UNITS + Q_NT - 1) / Q_NT;
+    static_assert(AU * Q_NT == Q_BM * 2 * SB, "activation pieces must split evenly");
+    static_assert(Q8 || 256 % SV == 0, "a Q4_K stage must not cross a super-block");
 };
 
-template <int FMT, int MW, int TN>
+template <int FMT, int MW, int TN, int KB>
 __global__ __launch_bounds__(128 * MW, 2) void gemm_q_kernel(QGemmArgs a)
 {
-    using C = QCfg<FMT, MW, TN>;
-    constexpr int BN = C::BN, BU = C::BU, Q_BM = C::Q_BM, Q_NT = C::Q_NT;
+    using C = QCfg<FMT, MW, TN, KB>;
+    constexpr int BN = C::BN, BU = C::BU, AU = C::AU, Q_BM = C::Q_BM, Q_NT = C::Q_NT, SB = C::SB, SV = C::SV;
     constexpr bool Q8 = C::Q8;
     extern __shared__ __align__(16) uint8_t lds[];
 
@@ -100,143 +107,167 @@ __global__ __launch_bounds__(128 * MW, 2) void gemm_q_kernel(QGemmArgs a)
     const int m0 = (t % a.nm) * Q_BM, n0 = (t / a.nm) * BN;
     const int wm = (wave % MW) * 32, g = wave / MW;
     const int l32 = lane & 31, hl = lane >> 5;
-    const int nst = K / 64;
-    const int nsc = Q8 ? K / 32 : K / 256;  // activation scales per row
+    const int nst = (K + SV - 1) / SV;
+    const int kb_last = ((K - (nst - 1) * SV) / 32) >> 1;  // block pairs in the last stage
+    const int nsc = Q8 ? K / 32 : K / 256;                // activation scales per row
     const int64_t rb = a.row_bytes;
 
     // Loads past the end of a resource return zeros.  The block-major scale
     // arrays are covered whole: a row past M reads another row's (finite)
-    // values, which reach only that row's discarded outputs.
+    // values, which reach only that row's discarded outputs.  Past the end of
+    // a ragged last stage, the staging reads the next row's bytes into blocks
+    // that are never multiplied.
     const rsrc_t rq = make_rsrc(a.q + (int64_t)m0 * K, clamp_u32((int64_t)(M - m0) * K));
     const rsrc_t rdxs = make_rsrc(a.dx, clamp_u32((int64_t)nsc * M * 4));
     const rsrc_t rw = make_rsrc(a.w + (int64_t)n0 * rb, clamp_u32((int64_t)(N - n0) * rb));
     const rsrc_t rbs = make_rsrc(Q8 ? nullptr : a.bsx, Q8 ? 0u : clamp_u32((int64_t)(K / 256) * M * 32));
 
     // ---- staging roles, fixed for the whole K loop ----
-    // activations: (row, 16-byte part of the stage's 64 bytes)
-    const int arow = tid >> 2, apart = tid & 3;
-    const uint32_t ag = (uint32_t)(arow * K + 16 * apart);
-    const uint32_t as_ = (uint32_t)((apart >> 1) * C::A_BLK + qswz(arow, apart & 1));
+    // activations: (row, 16-byte piece of the stage's SV bytes)
+    uint32_t ag[AU], as_[AU];
+#pragma unroll
+    for (int i = 0; i < AU; ++i) {
+        const int idx = tid + Q_NT * i, row = idx / (2 * SB), part = idx % (2 * SB);
+        ag[i] = (uint32_t)(row * K + 16 * part);
+        as_[i] = (uint32_t)((part >> 1) * C::A_BLK + qswz(row, part & 1));
+    }
     // activation scales (waves 0..MW/2-1): one row per lane
     const int drow = tid & (Q_BM - 1);
     const uint32_t dg = (uint32_t)((m0 + drow) * 4);
     // weight units, consecutive lanes along a row so that a load instruction
     // touches few rows; threads past the last unit repeat earlier ones (same
     // values to the same places)
+    constexpr int UPR = C::UPR;
     uint32_t bg[BU];
     int brow[BU];
-    const int bp = Q8 ? (tid & 3) : (tid & 1);  // the unit's part of its row
+    const int bp = Q8 ? (tid & 3) : (tid & 1);                 // quarter (Q8_0) or half (Q4_K)
+    const int bpair = Q8 ? (tid >> 2) % KB : (tid >> 1) % KB;  // block pair (Q8_0) or chunk (Q4_K) in the stage
 #pragma unroll
     for (int i = 0; i < BU; ++i) {
         const int u = (tid + Q_NT * i) % C::UNITS;
-        brow[i] = Q8 ? u >> 2 : u >> 1;
-        bg[i] = (uint32_t)(brow[i] * rb + (Q8 ? 16 * bp : 0));
+        brow[i] = u / UPR;
+        bg[i] = (uint32_t)(brow[i] * rb + (Q8 ? 68 * bpair + 16 * bp : 32 * bpair + 16 * bp));
     }
-    // Q8_0 realignment: a stage's 68 bytes are d0 q0..q31 d1 q0..q31; quarter
-    // p holds bytes 16p..16p+15 and needs the next dword (the next quarter's
-    // first; bytes 64..67 for the last): parts 0, 1 shift by 2 bytes (block 0,
-    // halves 0 and 1), parts 2, 3 by 4 (block 1).
+    // Q8_0 realignment: a block pair's 68 bytes are d0 q0..q31 d1 q0..q31;
+    // quarter p holds bytes 16p..16p+15 and needs the next dword (the next
+    // quarter's first; bytes 64..67 for the last): quarters 0, 1 shift by 2
+    // bytes (the pair's first block, halves 0 and 1), 2, 3 by 4 (its second).
     const uint32_t psel = bp < 2 ? 0x05040302u : 0x07060504u;
     // Q4_K activation sub-block sums (waves 0..MW-1): (row, half)
     const int xrow = (tid >> 1) & (Q_BM - 1), xpart = tid & 1;
     const uint32_t xg = (uint32_t)(((m0 + xrow) * 16 + 8 * xpart) * 2);
 
     // ---- staging registers ----
-    uint4 ra;
-    u32x2_t rdx;
+    uint4 ra[AU];
+    float rdx[Q8 ? SB : 1];
     uint4 rw4[BU];
     uint32_t rtail[Q8 ? BU : 1];
     uint4 rhd[Q8 ? 1 : BU];
     uint4 rbx;
 
     auto load = [&](int st) {
-        ra = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, ag, 64 * st, 0));
+#pragma unroll
+        for (int i = 0; i < AU; ++i)
+            ra[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, ag[i], SV * st, 0));
         if (wave < MW / 2) {
             if constexpr (Q8) {
-                rdx[0] = __builtin_amdgcn_raw_buffer_load_b32(rdxs, dg, 2 * st * M * 4, 0);
-                rdx[1] = __builtin_amdgcn_raw_buffer_load_b32(rdxs, dg, (2 * st + 1) * M * 4, 0);
+#pragma unroll
+                for (int b = 0; b < SB; ++b)
+                    rdx[b] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdxs, dg, (SB * st + b) * M * 4, 0));
             } else {
-                rdx[0] = __builtin_amdgcn_raw_buffer_load_b32(rdxs, dg, (st >> 2) * M * 4, 0);
+                rdx[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdxs, dg, (SV * st / 256) * M * 4, 0));
             }
         }
         if constexpr (Q8) {
 #pragma unroll
             for (int i = 0; i < BU; ++i) {
-                rw4[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, bg[i], 68 * st, 0));
-                if (bp == 3) rtail[i] = __builtin_amdgcn_raw_buffer_load_b32(rw, bg[i] + 16, 68 * st, 0);
+                rw4[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, bg[i], 68 * KB * st, 0));
+                if (bp == 3) rtail[i] = __builtin_amdgcn_raw_buffer_load_b32(rw, bg[i] + 16, 68 * KB * st, 0);
             }
         } else {
-            const int sb = st >> 2, c = st & 3;
+            const int sb = SV * st / 256, c0 = (SV * st % 256) / 64;
 #pragma unroll
             for (int i = 0; i < BU; ++i) {
-                rw4[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, bg[i] + 16 + 32 * c + 16 * bp, 144 * sb, 0));
-                if (c == 0) rhd[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, bg[i], 144 * sb, 0));
+                rw4[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, bg[i] + 16 + 32 * c0, 144 * sb, 0));
+                if (c0 == 0)
+                    rhd[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, brow[i] * (uint32_t)rb, 144 * sb, 0));
             }
-            if (c == 0 && wave < MW)
+            if (c0 == 0 && wave < MW)
                 rbx = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rbs, xg, sb * M * 32, 0));
         }
     };
 
-    // registers of stage st -> LDS buffer P
-    auto store = [&](int st, auto pc) {
+    // registers of stage st -> LDS buffer P, as NI items that the compute
+    // loop spreads over its MFMAs: item 0 the activation pieces and scales,
+    // item 1 + i weight unit i
+    constexpr int NI = 1 + BU;
+    static_assert(NI <= TN, "the staging items must fit in one block's MFMAs");
+    auto store_item = [&](int w, int st, auto pc) {
         constexpr int P = decltype(pc)::value;
-        *reinterpret_cast<uint4*>(lds + C::OFF_A + P * 2 * C::A_BLK + as_) = ra;
-        if (wave < MW / 2) {
-            float* sdx = reinterpret_cast<float*>(lds + C::OFF_DX) + P * 2 * Q_BM;
-            sdx[drow] = __uint_as_float(rdx[0]);
-            sdx[Q_BM + drow] = __uint_as_float(Q8 ? rdx[1] : rdx[0]);
-        }
-        uint8_t* sb_ = lds + C::OFF_B + P * 2 * C::B_BLK;
-        if constexpr (Q8) {
-            float* sdw = reinterpret_cast<float*>(lds + C::OFF_DW) + P * 2 * BN;
+        uint8_t* sb_ = lds + C::OFF_B + P * SB * C::B_BLK;
+        const int sb = SV * st / 256, c0 = (SV * st % 256) / 64, par = sb & 1;  // Q4_K position
+        if (w == 0) {
 #pragma unroll
-            for (int i = 0; i < BU; ++i) {
-                const uint4 v = rw4[i];
-                const uint32_t nx = (uint32_t)__builtin_amdgcn_update_dpp((int)v.x, (int)v.x, 0xF9, 0xF, 0xF, false);
-                const uint32_t e = bp == 3 ? rtail[i] : nx;
-                const uint4 o = make_uint4(__builtin_amdgcn_perm(v.y, v.x, psel), __builtin_amdgcn_perm(v.z, v.y, psel),
-                                           __builtin_amdgcn_perm(v.w, v.z, psel), __builtin_amdgcn_perm(e, v.w, psel));
-                *reinterpret_cast<uint4*>(sb_ + (bp >> 1) * C::B_BLK + qswz(brow[i], bp & 1)) = o;
-                if (bp == 0) sdw[brow[i]] = f16lo(v.x);
-                if (bp == 2) sdw[BN + brow[i]] = f16hi(v.x);
+            for (int i = 0; i < AU; ++i) *reinterpret_cast<uint4*>(lds + C::OFF_A + P * SB * C::A_BLK + as_[i]) = ra[i];
+            if (wave < MW / 2) {
+                float* sdx = reinterpret_cast<float*>(lds + C::OFF_DX) + P * SB * Q_BM + drow;
+#pragma unroll
+                for (int b = 0; b < SB; ++b) sdx[b * Q_BM] = Q8 ? rdx[Q8 ? b : 0] : rdx[0];
             }
+            if constexpr (!Q8) {
+                if (c0 == 0 && wave < MW)
+                    *reinterpret_cast<uint4*>(lds + C::OFF_BSX + par * Q_BM * 32 + qswz(xrow, xpart)) = rbx;
+            }
+            return;
+        }
+        const int i = w - 1;
+        if constexpr (Q8) {
+            float* sdw = reinterpret_cast<float*>(lds + C::OFF_DW) + P * SB * BN;
+            const uint4 v = rw4[i];
+            const uint32_t nx = (uint32_t)__builtin_amdgcn_update_dpp((int)v.x, (int)v.x, 0xF9, 0xF, 0xF, false);
+            const uint32_t e = bp == 3 ? rtail[i] : nx;
+            const uint4 o = make_uint4(__builtin_amdgcn_perm(v.y, v.x, psel), __builtin_amdgcn_perm(v.z, v.y, psel),
+                                       __builtin_amdgcn_perm(v.w, v.z, psel), __builtin_amdgcn_perm(e, v.w, psel));
+            const int blk = 2 * bpair + (bp >> 1);
+            *reinterpret_cast<uint4*>(sb_ + blk * C::B_BLK + qswz(brow[i], bp & 1)) = o;
+            if (bp == 0) sdw[blk * BN + brow[i]] = f16lo(v.x);
+            if (bp == 2) sdw[blk * BN + brow[i]] = f16hi(v.x);
         } else {
-            const int sb = st >> 2, c = st & 3, par = sb & 1;
+            const uint4 nb = rw4[i];
+            const uint32_t mk = 0x0f0f0f0fu;
+            // low nibbles of chunk c: sub-block 2c (stage block 2*bpair); high: 2c+1
+            *reinterpret_cast<uint4*>(sb_ + 2 * bpair * C::B_BLK + qswz(brow[i], bp)) =
+                make_uint4(nb.x & mk, nb.y & mk, nb.z & mk, nb.w & mk);
+            *reinterpret_cast<uint4*>(sb_ + (2 * bpair + 1) * C::B_BLK + qswz(brow[i], bp)) =
+                make_uint4((nb.x >> 4) & mk, (nb.y >> 4) & mk, (nb.z >> 4) & mk, (nb.w >> 4) & mk);
+            if (c0 == 0 && bpair == 0) {
+                const uint4 hd = rhd[i];
+                if (bp == 0) {  // d * sc_j for the eight sub-blocks
+                    const float d = f16lo(hd.x);
+                    float* sds = reinterpret_cast<float*>(lds + C::OFF_DW) + par * 8 * BN + brow[i];
 #pragma unroll
-            for (int i = 0; i < BU; ++i) {
-                const uint4 nb = rw4[i];
-                const uint32_t mk = 0x0f0f0f0fu;
-                // low nibbles: sub-block 2c (block 0 of the stage); high: 2c+1
-                *reinterpret_cast<uint4*>(sb_ + qswz(brow[i], bp)) = make_uint4(nb.x & mk, nb.y & mk, nb.z & mk, nb.w & mk);
-                *reinterpret_cast<uint4*>(sb_ + C::B_BLK + qswz(brow[i], bp)) =
-                    make_uint4((nb.x >> 4) & mk, (nb.y >> 4) & mk, (nb.z >> 4) & mk, (nb.w >> 4) & mk);
-                if (c == 0) {
-                    const uint4 hd = rhd[i];
-                    if (bp == 0) {  // d * sc_j for the eight sub-blocks
-                        const float d = f16lo(hd.x);
-                        float* sds = reinterpret_cast<float*>(lds + C::OFF_DW) + par * 8 * BN + brow[i];
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) {
-                            int sc, mn;
-                            q4k_scale_min(hd.y, hd.z, hd.w, j, sc, mn);
-                            sds[j * BN] = d * (float)sc;
-                        }
-                    } else {  // dmin and the mins m_j
-                        reinterpret_cast<float*>(lds + C::OFF_DMIN)[par * BN + brow[i]] = f16hi(hd.x);
-                        half8_t mj;
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) {
-                            int sc, mn;
-                            q4k_scale_min(hd.y, hd.z, hd.w, j, sc, mn);
-                            mj[j] = (_Float16)(float)mn;
-                        }
-                        *reinterpret_cast<half8_t*>(lds + C::OFF_MJ + (par * BN + brow[i]) * 16) = mj;
+                    for (int j = 0; j < 8; ++j) {
+                        int sc, mn;
+                        q4k_scale_min(hd.y, hd.z, hd.w, j, sc, mn);
+                        sds[j * BN] = d * (float)sc;
                     }
+                } else {  // dmin and the mins m_j
+                    reinterpret_cast<float*>(lds + C::OFF_DMIN)[par * BN + brow[i]] = f16hi(hd.x);
+                    half8_t mj;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        int sc, mn;
+                        q4k_scale_min(hd.y, hd.z, hd.w, j, sc, mn);
+                        mj[j] = (_Float16)(float)mn;
+                    }
+                    *reinterpret_cast<half8_t*>(lds + C::OFF_MJ + (par * BN + brow[i]) * 16) = mj;
                 }
             }
-            if (c == 0 && wave < MW)
-                *reinterpret_cast<uint4*>(lds + C::OFF_BSX + par * Q_BM * 32 + qswz(xrow, xpart)) = rbx;
         }
+    };
+    auto store = [&](int st, auto pc) {
+#pragma unroll
+        for (int w = 0; w < NI; ++w) store_item(w, st, pc);
     };
 
     f32x16_t acc[TN];
@@ -246,56 +277,75 @@ __global__ __launch_bounds__(128 * MW, 2) void gemm_q_kernel(QGemmArgs a)
         for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
     const i32x16_t izero = {};
     const f32x16_t fzero = {};
+    const f32x32_t fzero32 = {};
 
-    // block g of stage st out of buffer P
-    auto compute = [&](int st, auto pc) {
+    // block blk of stage st out of buffer P
+    auto block = [&](int st, int blk, auto pc, auto hook) {
         constexpr int P = decltype(pc)::value;
-        const uint8_t* sa = lds + C::OFF_A + (P * 2 + g) * C::A_BLK;
-        const uint8_t* sbb = lds + C::OFF_B + (P * 2 + g) * C::B_BLK;
+        constexpr int NPAIR = (TN + 1) / 2;
+        const uint8_t* sa = lds + C::OFF_A + (P * SB + blk) * C::A_BLK;
+        const uint8_t* sbb = lds + C::OFF_B + (P * SB + blk) * C::B_BLK;
         const i32x4_t af = *reinterpret_cast<const i32x4_t*>(sa + qswz(wm + l32, hl));
+        const int sub = 2 * ((SV * st % 256) / 64) + blk;  // Q4_K sub-block
         const float* sdw = reinterpret_cast<const float*>(lds + C::OFF_DW) + l32 +
-                           (Q8 ? (P * 2 + g) * BN : (((st >> 2) & 1) * 8 + 2 * (st & 3) + g) * BN);
+                           (Q8 ? (P * SB + blk) * BN : (((SV * st / 256) & 1) * 8 + sub) * BN);
         i32x4_t bn = *reinterpret_cast<const i32x4_t*>(sbb + qswz(l32, hl));
-        float dwn = sdw[0];
-        // d_x of this lane's 16 output rows wm + 8q + 4hl + (0..3)
-        float dxv[16];
-        const float* sdx = reinterpret_cast<const float*>(lds + C::OFF_DX) + (P * 2 + g) * Q_BM + wm + 4 * hl;
+        // outer-product operands: d_x of row wm + l32 in both halves, the
+        // column scale of tile 2p + hl (the last tile repeated for odd TN)
+        const float dxa = reinterpret_cast<const float*>(lds + C::OFF_DX)[(P * SB + blk) * Q_BM + wm + l32];
+        float dwb[NPAIR];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float4 v = *reinterpret_cast<const float4*>(sdx + 8 * q);
-            dxv[4 * q] = v.x; dxv[4 * q + 1] = v.y; dxv[4 * q + 2] = v.z; dxv[4 * q + 3] = v.w;
-        }
+        for (int q = 0; q < NPAIR; ++q) dwb[q] = sdw[32 * (2 * q + 1 < TN ? 2 * q + hl : 2 * q)];
+        f32x32_t s2;
         i32x16_t cp;
-        float dwp = 0.0f;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const i32x4_t bf = bn;
-            const float dw = dwn;
             const i32x16_t cv = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bf, izero, 0, 0, 0);
+            // issue the MFMA before the previous tile's scaling, which then
+            // runs while the matrix cores work (never waits on this result)
+            __builtin_amdgcn_sched_barrier(0);
+            hook(j);
             // next tile's operand while this one is in the matrix cores
-            if (j + 1 < TN) {
-                bn = *reinterpret_cast<const i32x4_t*>(sbb + qswz(32 * (j + 1) + l32, hl));
-                dwn = sdw[32 * (j + 1)];
-            }
-            // scale the previous tile's sums
+            if (j + 1 < TN) bn = *reinterpret_cast<const i32x4_t*>(sbb + qswz(32 * (j + 1) + l32, hl));
+            // scale the previous tile's sums: acc += (d_x d_w) * S
             if (j > 0) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[j - 1][r] = __builtin_fmaf(dxv[r] * dwp, (float)cp[r], acc[j - 1][r]);
+                for (int r = 0; r < 16; ++r)
+                    acc[j - 1][r] = __builtin_fmaf(s2[16 * ((j - 1) & 1) + r], (float)cp[r], acc[j - 1][r]);
                 asm volatile("" : "+v"(acc[j - 1]));  // done here, not sunk past the staging
             }
+            // the d_x d_w tiles of tiles j, j+1 (32x32 outer products, two per MFMA)
+            if ((j & 1) == 0) s2 = __builtin_amdgcn_mfma_f32_32x32x1f32(dxa, dwb[j / 2], fzero32, 0, 0, 0);
             cp = cv;
-            dwp = dw;
             // keep one tile's sums in flight: hoisting the MFMAs ahead would
             // hold all TN results at once
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[TN - 1][r] = __builtin_fmaf(dxv[r] * dwp, (float)cp[r], acc[TN - 1][r]);
+        for (int r = 0; r < 16; ++r) acc[TN - 1][r] = __builtin_fmaf(s2[16 * ((TN - 1) & 1) + r], (float)cp[r], acc[TN - 1][r]);
         asm volatile("" : "+v"(acc[TN - 1]));
+    };
 
+    // the group's blocks of stage st, then (Q4_K) the mins term at the end of
+    // a super-block, over the tiles of this group's parity
+    auto compute = [&](int st, auto pc, int kb, auto hook) {
+        constexpr int P_LAST = decltype(pc)::value;
+        block(st, g, pc, hook);  // every stage has at least one block pair
+#pragma unroll
+        for (int k = 1; k < KB; ++k)
+            if (k < kb) block(st, 2 * k + g, pc, [](int) {});
         if constexpr (!Q8) {
-            if ((st & 3) == 3) {  // end of a super-block: the mins term, tiles of this group's parity
-                const int par = (st >> 2) & 1;
+            if ((SV * (st + 1)) % 256 == 0) {
+                const int par = (SV * st / 256) & 1;
+                // d_x of this lane's 16 output rows wm + 8q + 4hl + (0..3)
+                float dxv[16];
+                const float* sdx = reinterpret_cast<const float*>(lds + C::OFF_DX) + P_LAST * SB * Q_BM + wm + 4 * hl;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 v = *reinterpret_cast<const float4*>(sdx + 8 * q);
+                    dxv[4 * q] = v.x; dxv[4 * q + 1] = v.y; dxv[4 * q + 2] = v.z; dxv[4 * q + 3] = v.w;
+                }
                 const half8_t ax = *reinterpret_cast<const half8_t*>(lds + C::OFF_BSX + par * Q_BM * 32 + qswz(wm + l32, hl));
                 const float* sdm = reinterpret_cast<const float*>(lds + C::OFF_DMIN) + par * BN + l32;
 #pragma unroll
@@ -311,10 +361,11 @@ __global__ __launch_bounds__(128 * MW, 2) void gemm_q_kernel(QGemmArgs a)
         }
     };
 
-    // The registers hold the stage after the one in LDS: each iteration first
-    // writes them to the idle buffer, then loads the stage after that, so a
-    // load has a whole stage of MFMAs to arrive.  Past the end the last stage
-    // is restaged into the idle buffer rather than branch.
+    // The registers hold the stage after the one in LDS: while a stage's first
+    // MFMAs run they are written to the idle buffer, one item per MFMA, then
+    // the stage after that is loaded, so a load has about a stage of MFMAs to
+    // arrive.  Past the end the last stage is restaged into the idle buffer
+    // rather than branch.
     const int last = nst - 1;
     load(0);
     store(0, std::integral_constant<int, 0>{});
@@ -322,9 +373,11 @@ __global__ __launch_bounds__(128 * MW, 2) void gemm_q_kernel(QGemmArgs a)
     __syncthreads();
     auto iter = [&](int st, auto pc) {
         constexpr int P = decltype(pc)::value;
-        store(st + 1 < nst ? st + 1 : last, std::integral_constant<int, P ^ 1>{});
-        load(st + 2 < nst ? st + 2 : last);
-        compute(st, pc);
+        const int nx = st + 1 < nst ? st + 1 : last, nx2 = st + 2 < nst ? st + 2 : last;
+        compute(st, pc, st == last ? kb_last : KB, [&](int j) {
+            if (j < NI) store_item(j, nx, std::integral_constant<int, P ^ 1>{});
+            if (j == (NI < TN ? NI : TN - 1)) load(nx2);
+        });
         __syncthreads();
     };
     int st = 0;
@@ -388,6 +441,8 @@ static int cu_count_q()
     return cache[dev] = cus;
 }
 
+constexpr int Q_KB = 1;  // block pairs per stage: 64 values
+
 struct QTile {
     int mw, tn;
 };
@@ -418,13 +473,13 @@ static QTile pick_qtile(int64_t M, int64_t N)
 template <int FMT, int MW, int TN>
 static hipError_t launch_q(QGemmArgs a, hipStream_t s)
 {
-    using C = QCfg<FMT, MW, TN>;
+    using C = QCfg<FMT, MW, TN, Q_KB>;
     const int nm = (a.M + C::Q_BM - 1) / C::Q_BM, nn = (a.N + C::BN - 1) / C::BN;
     const int64_t grid = (int64_t)nm * nn;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     a.nm = nm;
     a.remap = grid % 8 == 0 ? 1 : 0;
-    const void* k = (const void*)gemm_q_kernel<FMT, MW, TN>;
+    const void* k = (const void*)gemm_q_kernel<FMT, MW, TN, Q_KB>;
     allow_lds_q(k, C::BYTES);
     void* args[] = {&a};
     return hipLaunchKernel(k, dim3((unsigned)grid), dim3(C::Q_NT), args, C::BYTES, s);

@@ -99,61 +99,28 @@ __global__ __launch_bounds__(256) void quantize_q8k_kernel(const float* __restri
     }
 }
 
-// Prefill preparation, one workgroup per row.  The row's effective
-// activation -- mode (a): x; mode (b): the dequantized quantized value, Q8_0
-// f16(d)*q (exact in f32) or Q8K d*q -- is scaled by the power of two s that
-// puts its largest magnitude in [2^14, 2^15) and split into f16 hi + lo;
-// rs = 1/s.  Q4_K also gets the sums of value*s over every 32 values, divided
-// by 32 so that they stay below 2^15, split the same way and laid out
-// [M][K/256][8 hi, 8 lo].
-template <int FMT, int MODE>
+// Mode (a) prefill preparation, one workgroup per row.  The row x is scaled
+// by the power of two s that puts its largest magnitude in [2^14, 2^15) and
+// split into f16 hi + lo; rs = 1/s.  Q4_K also gets the sums of x*s over every
+// 32 values, divided by 32 so that they stay below 2^15, split the same way
+// and laid out [M][K/256][8 hi, 8 lo].
+template <int FMT>
 __global__ __launch_bounds__(256) void gemm_prep_kernel(const float* __restrict__ x, int M, int K,
                                                         _Float16* __restrict__ hi, _Float16* __restrict__ lo,
                                                         float* __restrict__ rs, _Float16* __restrict__ xs)
 {
-    constexpr bool WAVE = FMT == FMT_Q4_K && MODE == MODE_B;  // Q8K blocks of 256 values, one wave each
     __shared__ float red[4];
     const int m = blockIdx.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const float* v = x + (int64_t)m * K;
     const int n32 = K / 32, nsb = K / 256;
 
-    auto chunk = [&](int u, float e[32]) {  // 32 effective values (mode (a), or Q8_0 mode (b))
-        load32(v + 32 * u, e);
-        if (MODE == MODE_B) {
-            uint16_t dbits;
-            float dval;
-            int8_t q[32];
-            q8_0_block(e, dbits, dval, q);
-#pragma unroll
-            for (int j = 0; j < 32; ++j) e[j] = dval * (float)q[j];
-        }
-    };
-    auto block4 = [&](int sb, float e[4]) {  // this lane's 4 effective values of Q8K block sb
-        const float4 t = reinterpret_cast<const float4*>(v + 256 * sb)[lane];
-        const float xv[4] = {t.x, t.y, t.z, t.w};
-        float d;
-        int q[4], s16;
-        q8k_wave(xv, lane, d, q, s16);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) e[u] = d * (float)q[u];
-    };
-
     float am = 0.0f;
-    if (WAVE) {
-        for (int sb = wave; sb < nsb; sb += 4) {
-            float e[4];
-            block4(sb, e);
+    for (int u = threadIdx.x; u < n32; u += 256) {
+        float e[32];
+        load32(v + 32 * u, e);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) am = fmaxf(am, fabsf(e[u]));
-        }
-    } else {
-        for (int u = threadIdx.x; u < n32; u += 256) {
-            float e[32];
-            chunk(u, e);
-#pragma unroll
-            for (int j = 0; j < 32; ++j) am = fmaxf(am, fabsf(e[j]));
-        }
+        for (int j = 0; j < 32; ++j) am = fmaxf(am, fabsf(e[j]));
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
@@ -167,49 +134,25 @@ __global__ __launch_bounds__(256) void gemm_prep_kernel(const float* __restrict_
     _Float16* oh = hi + (int64_t)m * K;
     _Float16* ol = lo + (int64_t)m * K;
     _Float16* ox = FMT == FMT_Q4_K ? xs + (int64_t)m * nsb * 16 : nullptr;
-    auto put_sum = [&](int sb, int j, float sum) {
-        _Float16 h, l;
-        float t;
-        split_one(sum, 0.03125f, h, l, t);
-        ox[16 * sb + j] = h;
-        ox[16 * sb + 8 + j] = l;
-    };
-    if (WAVE) {
-        for (int sb = wave; sb < nsb; sb += 4) {
-            float e[4];
-            block4(sb, e);
-            _Float16 h[4], l[4];
-            float sum = 0.0f;
+    for (int u = threadIdx.x; u < n32; u += 256) {
+        float e[32];
+        _Float16 h[32], l[32];
+        load32(v + 32 * u, e);
+        const float sum = split_chunk(e, s, h, l);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                float t;
-                split_one(e[u], s, h[u], l[u], t);
-                sum += t;
-            }
-            const int k = 256 * sb + 4 * lane;
-            const half2_t h01 = {h[0], h[1]}, h23 = {h[2], h[3]}, l01 = {l[0], l[1]}, l23 = {l[2], l[3]};
-            *reinterpret_cast<u32x2_t*>(oh + k) = u32x2_t{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
-            *reinterpret_cast<u32x2_t*>(ol + k) = u32x2_t{__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23)};
-            sum += __shfl_xor(sum, 1);
-            sum += __shfl_xor(sum, 2);
-            sum += __shfl_xor(sum, 4);
-            if ((lane & 7) == 0) put_sum(sb, lane >> 3, sum);
+        for (int i = 0; i < 4; ++i) {
+            half8_t vh, vl;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) { vh[t] = h[8 * i + t]; vl[t] = l[8 * i + t]; }
+            reinterpret_cast<half8_t*>(oh + 32 * u)[i] = vh;
+            reinterpret_cast<half8_t*>(ol + 32 * u)[i] = vl;
         }
-    } else {
-        for (int u = threadIdx.x; u < n32; u += 256) {
-            float e[32];
-            _Float16 h[32], l[32];
-            chunk(u, e);
-            const float sum = split_chunk(e, s, h, l);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                half8_t vh, vl;
-#pragma unroll
-                for (int t = 0; t < 8; ++t) { vh[t] = h[8 * i + t]; vl[t] = l[8 * i + t]; }
-                reinterpret_cast<half8_t*>(oh + 32 * u)[i] = vh;
-                reinterpret_cast<half8_t*>(ol + 32 * u)[i] = vl;
-            }
-            if (FMT == FMT_Q4_K) put_sum(u >> 3, u & 7, sum);
+        if (FMT == FMT_Q4_K) {
+            _Float16 sh, sl;
+            float t;
+            split_one(sum, 0.03125f, sh, sl, t);
+            ox[16 * (u >> 3) + (u & 7)] = sh;
+            ox[16 * (u >> 3) + 8 + (u & 7)] = sl;
         }
     }
 }
@@ -324,14 +267,10 @@ hipError_t launch_gemm_prep(int fmt, int mode, const float* x, int64_t M, int64_
         return hipGetLastError();
     }
     const dim3 grid((unsigned)M), block(256);
-    if (fmt == FMT_Q8_0 && mode == MODE_A)
-        hipLaunchKernelGGL((gemm_prep_kernel<FMT_Q8_0, MODE_A>), grid, block, 0, s, x, (int)M, (int)K, b.a0, b.a1, b.rs, b.xs);
-    else if (fmt == FMT_Q8_0)
-        hipLaunchKernelGGL((gemm_prep_kernel<FMT_Q8_0, MODE_B>), grid, block, 0, s, x, (int)M, (int)K, b.a0, b.a1, b.rs, b.xs);
-    else if (mode == MODE_A)
-        hipLaunchKernelGGL((gemm_prep_kernel<FMT_Q4_K, MODE_A>), grid, block, 0, s, x, (int)M, (int)K, b.a0, b.a1, b.rs, b.xs);
+    if (fmt == FMT_Q8_0)
+        hipLaunchKernelGGL(gemm_prep_kernel<FMT_Q8_0>, grid, block, 0, s, x, (int)M, (int)K, b.a0, b.a1, b.rs, b.xs);
     else
-        hipLaunchKernelGGL((gemm_prep_kernel<FMT_Q4_K, MODE_B>), grid, block, 0, s, x, (int)M, (int)K, b.a0, b.a1, b.rs, b.xs);
+        hipLaunchKernelGGL(gemm_prep_kernel<FMT_Q4_K>, grid, block, 0, s, x, (int)M, (int)K, b.a0, b.a1, b.rs, b.xs);
     return hipGetLastError();
 }
 
