@@ -17,6 +17,11 @@ recorded on the stream the kernels run on, with inputs resident in HBM.
 CPU baseline: the CPU oracle (plain C, f64/int64) timed on the decode phase
 of the same step (M = 1 and 8, both formats and modes, all 8 layers) on the
 host's threads, reported in the same unit.
+
+Context, outside the step and the value: the dequantize-all form (weights
+decoded to f32 once, then the library f32 GEMM), timed on the same layers and
+M, as the page "同一个 GGUF，CPU 和 Metal 生成的文字不一样" (section 修法)
+compares it with the quantized forms.
 """
 import argparse
 import hashlib
@@ -43,6 +48,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-layers", type=int, default=LAYERS, help="layers in the CPU-baseline sample")
+    p.add_argument("--no-dequant", action="store_true", help="skip the dequantize-all context rows")
     p.add_argument("--only", default="", help="restrict the step to one part, e.g. gemv:q8_0:b:1 or gemm:q4_k:a "
                                               "(for profiling one kernel); 'copy' times a plain 512 MiB device copy "
                                               "instead (the calibration for the HBM byte counters)")
@@ -108,6 +114,45 @@ def cpu_baseline(layers, min_seconds=10.0):
                   f"modes a and b, N=14336 K=4096), repeated {reps} times: {total_bytes / 1e9:.2f} GB of weight "
                   f"blocks in {total_s:.1f} s",
     }
+
+
+def dequant_context(qmm, torch, wq, xs, ys, fmts, stream, args):
+    """The dequantize-all form on the step's layers: the one-time decode of
+    each layer to f32, then y = x . W^T with the f32 weights for M = 1, 8 and
+    512 (HIP events on the launch stream, per launch = group time / layers)."""
+    out = {}
+    for f, code in fmts.items():
+        plan = qmm.Plan(code, N, K, M_PREFILL, qmm.MODE_DEQUANT)
+        wf = [torch.empty((N, K), dtype=torch.float32, device=xs[1].device) for _ in range(LAYERS)]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+        def timed(fn):
+            for _ in range(max(1, args.warmup)):
+                fn()
+            torch.cuda.synchronize()
+            ev[0].record(stream)
+            for _ in range(args.steps):
+                fn()
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            return ev[0].elapsed_time(ev[1]) * 1000.0 / (args.steps * LAYERS)
+
+        row = {"dequantize_us_per_layer": round(timed(lambda: [qmm.dequantize_weights(code, wq[f][l], N, K, wf[l], stream)
+                                                               for l in range(LAYERS)]), 2)}
+        f32_bytes = N * K * 4
+        for m in DECODE_M + (M_PREFILL,):
+            us = timed(lambda: [plan.run_dequantized(wf[l], xs[m], ys[m], stream) for l in range(LAYERS)])
+            r = {"us_per_launch": round(us, 3)}
+            if m in DECODE_M:
+                r["f32_weight_GBps"] = round(f32_bytes / (us * 1e-6) / 1e9, 1)
+            else:
+                r["TFLOPS"] = round(2.0 * m * N * K / (us * 1e-6) / 1e12, 1)
+            row[f"M={m}"] = r
+        out[f] = row
+        plan.close()
+        del wf
+        torch.cuda.synchronize()
+    return out
 
 
 def copy_calibration(torch, dev, stream, args):
@@ -295,6 +340,8 @@ def main():
             "traffic": traffic_from_profile(f"gemm:{rb['fmt']}:{rb['mode']}:{rb['M']}"),
         }
     out["detail"] = detail
+    if not args.only and not args.no_dequant:
+        out["dequantize_all"] = dequant_context(qmm, torch, wq, xs, ys, fmts, stream, args)
     out["wall_s_timed"] = round(wall_s, 3)
     out["setup_s"] = round(setup_s, 1)
     out["weights_fit_infinity_cache_256MB"] = {f: layer_bytes[f] * LAYERS <= 256 * 2 ** 20 for f in fmts}

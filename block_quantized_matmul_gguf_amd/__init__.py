@@ -5,7 +5,10 @@ forms of the page "同一个 GGUF，CPU 和 Metal 生成的文字不一样" (sec
 
 * ``MODE_F32ACT`` (a): f32 activations, weight blocks dequantized in-kernel;
 * ``MODE_QACT`` (b): activation rows quantized to Q8_0 / Q8K first, integer
-  block dot products scaled by the block scales.
+  block dot products scaled by the block scales;
+* ``MODE_DEQUANT``: the same page's third form (section 修法, the
+  CANDLE_DEQUANTIZE_ALL switch): weights decoded to f32 once
+  (``dequantize_weights``), then a plain f32 matmul (``Plan.run_dequantized``).
 
 This module only marshals arguments: it checks dtypes, devices, contiguity and
 sizes of torch tensors, then calls the C ABI (``include/qmatmul.h``) with their
@@ -19,7 +22,7 @@ import ctypes
 import os
 
 Q8_0, Q4_K, Q8_K = 8, 12, 15
-MODE_F32ACT, MODE_QACT = 0, 1
+MODE_F32ACT, MODE_QACT, MODE_DEQUANT = 0, 1, 2
 OK, EINVAL, EBLOCK, EUNSUPPORTED, ENOMEM, EHIP = 0, 1, 2, 3, 4, 5
 BLOCK_VALUES = {Q8_0: 32, Q4_K: 256, Q8_K: 256}
 BLOCK_BYTES = {Q8_0: 34, Q4_K: 144, Q8_K: 292}
@@ -39,6 +42,8 @@ SIGNATURES = {
     "qmatmul_quantize_act": (_int, [_int, _p, _i64, _i64, _p, _p]),
     "qmatmul_quantize_weights": (_int, [_int, _p, _i64, _i64, _p, _p]),
     "qmatmul_run_block_sums": (_int, [_p, _p, _p, _p, _i64, _p]),
+    "qmatmul_dequantize_weights": (_int, [_int, _p, _i64, _i64, _p, _p]),
+    "qmatmul_run_dequantized": (_int, [_p, _p, _p, _p, _i64, _p]),
     "qmatmul_check": (_int, [_int, _i64, _i64, _i64, _int]),
     "qmatmul_row_bytes": (_i64, [_int, _i64]),
     "qmatmul_block_sums_per_row": (_i64, [_int, _i64]),
@@ -171,6 +176,22 @@ class Plan:
         _check(lib().qmatmul_run(self._h, _ptr(w), _ptr(x), _ptr(y), m, _stream(stream)), "qmatmul_run")
         return y
 
+    def run_dequantized(self, w_f32, x, y=None, stream=None):
+        """Dequantize-all plans: y = x . W^T with W the f32 [N, K] matrix from
+        ``dequantize_weights``."""
+        torch = _torch()
+        _need(w_f32, torch.float32, (self.n, self.k), "w_f32")
+        _need(x, torch.float32, None, "x")
+        if x.dim() != 2 or x.shape[1] != self.k:
+            raise ValueError(f"x must be [M, {self.k}], got {tuple(x.shape)}")
+        m = x.shape[0]
+        if y is None:
+            y = torch.empty((m, self.n), dtype=torch.float32, device=x.device)
+        _need(y, torch.float32, (m, self.n), "y")
+        _check(lib().qmatmul_run_dequantized(self._h, _ptr(w_f32), _ptr(x), _ptr(y), m, _stream(stream)),
+               "qmatmul_run_dequantized")
+        return y
+
     def block_sums(self, w, x, out=None, stream=None):
         torch = _torch()
         m = self._args(w, x)
@@ -229,4 +250,22 @@ def quantize_weights(fmt: int, w, out=None, stream=None):
         out = torch.empty((n, rb), dtype=torch.uint8, device=w.device)
     _need(out, torch.uint8, (n, rb), "out")
     _check(lib().qmatmul_quantize_weights(fmt, _ptr(w), n, k, _ptr(out), _stream(stream)), "qmatmul_quantize_weights")
+    return out
+
+
+def dequantize_weights(fmt: int, w, n: int, k: int, out=None, stream=None):
+    """f32 [N, K] of GGUF weight blocks w (uint8, N*row_bytes(fmt, K) bytes, on
+    the GPU): the exact dequantized values rounded once to f32."""
+    torch = _torch()
+    _need(w, torch.uint8, None, "w")
+    rb = row_bytes(fmt, k)
+    if rb < 0:
+        raise ValueError(f"K={k} is not a multiple of the block size of format {fmt}")
+    if w.numel() != n * rb:
+        raise ValueError(f"w has {w.numel()} bytes, expected {n * rb}")
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.float32, device=w.device)
+    _need(out, torch.float32, (n, k), "out")
+    _check(lib().qmatmul_dequantize_weights(fmt, _ptr(w), n, k, _ptr(out), _stream(stream)),
+           "qmatmul_dequantize_weights")
     return out

@@ -6,7 +6,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqmatmul.so")
-SOURCES = ["qmm_capi.cpp", "qmm_quant.hip", "qmm_gemv.hip", "qmm_gemm.hip", "qmm_gemm_q.hip"]
+SOURCES = ["qmm_capi.cpp", "qmm_quant.hip", "qmm_gemv.hip", "qmm_gemm.hip", "qmm_gemm_q.hip", "qmm_dequant.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -15,9 +15,13 @@ FLAGS = [
 ]
 
 
+# rocBLAS: the plain f32 GEMM of the dequantize-all form
+LIBS = ["-L/opt/rocm/lib", "-lrocblas", "-Wl,-rpath,/opt/rocm/lib"]
+
+
 def build(verbose: bool = False, extra=()) -> str:
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    cmd = [HIPCC, *FLAGS, *extra, *srcs, "-o", LIB + ".tmp"]
+    cmd = [HIPCC, *FLAGS, *extra, *srcs, *LIBS, "-o", LIB + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)

@@ -22,6 +22,8 @@ struct qmm_plan {
     size_t ws_bytes;
     GemvBufs gv;
     GemmBufs gm;
+    float* wdeq;   // dequantize-all plans: the decoded weights [N][K]
+    void* dense;   // dequantize-all plans: the f32 GEMM handle
 };
 
 static thread_local char g_err[512];
@@ -74,8 +76,10 @@ static int check_shape(int format, int64_t N, int64_t K, int64_t M_max, int mode
     if (format != QMM_Q8_0 && format != QMM_Q4_K)
         return fail(QMM_EUNSUPPORTED, "unsupported weight format %d (expected %d Q8_0 or %d Q4_K)", format, QMM_Q8_0,
                     QMM_Q4_K);
-    if (mode != QMM_MODE_F32ACT && mode != QMM_MODE_QACT)
-        return fail(QMM_EUNSUPPORTED, "unsupported mode %d (expected 0 f32 activations or 1 quantized activations)", mode);
+    if (mode != QMM_MODE_F32ACT && mode != QMM_MODE_QACT && mode != QMM_MODE_DEQUANT)
+        return fail(QMM_EUNSUPPORTED,
+                    "unsupported mode %d (expected 0 f32 activations, 1 quantized activations or 2 dequantize-all)",
+                    mode);
     if (N <= 0 || K <= 0 || M_max <= 0)
         return fail(QMM_EINVAL, "sizes must be positive: N=%lld K=%lld M_max=%lld", (long long)N, (long long)K,
                     (long long)M_max);
@@ -112,6 +116,12 @@ static size_t layout(qmm_plan* p, char* base)
         off += align256(bytes ? bytes : 16);
         return r;
     };
+    if (p->mode == QMM_MODE_DEQUANT) {  // the decoded weights only
+        p->wdeq = (float*)take(4 * (size_t)N * K);
+        p->gv = GemvBufs{};
+        p->gm = GemmBufs{};
+        return off;
+    }
     // decode path
     const int splits = gemv_max_splits(p->fmt, K);
     p->gv.part = (float*)take(splits > 1 ? 4 * (size_t)splits * GEMV_MAX_M * N : 0);
@@ -169,6 +179,11 @@ extern "C" int qmatmul_create(qmm_plan** out, int format, int64_t N, int64_t K, 
                     hipGetErrorString(e));
     }
     layout(p, (char*)p->ws);
+    if (mode == QMM_MODE_DEQUANT && dense_create(&p->dense) != 0) {
+        (void)hipFree(p->ws);
+        delete p;
+        return fail(QMM_EHIP, "rocblas_create_handle failed");
+    }
     *out = p;
     return QMM_OK;
 }
@@ -178,6 +193,7 @@ extern "C" int qmatmul_destroy(qmm_plan* p)
     g_err[0] = 0;
     if (!p) return QMM_OK;
     hipError_t e = hipDeviceSynchronize();
+    dense_destroy(p->dense);
     hipError_t f = hipFree(p->ws);
     delete p;
     if (e != hipSuccess) return fail(QMM_EHIP, "hipDeviceSynchronize: %s", hipGetErrorString(e));
@@ -205,6 +221,13 @@ static int run_impl(const qmm_plan* p, const void* w, const float* x, float* y, 
 {
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
+    if (p->mode == QMM_MODE_DEQUANT) {
+        e = launch_dequantize(p->fmt, w, p->N, p->K, p->wdeq, s);
+        if (e != hipSuccess) return fail(QMM_EHIP, "kernel launch: %s", hipGetErrorString(e));
+        const int st = dense_gemm(p->dense, p->wdeq, x, y, M, p->N, p->K, s);
+        if (st != 0) return fail(QMM_EHIP, "rocblas_sgemm: status %d", st);
+        return QMM_OK;
+    }
     if (M <= GEMV_MAX_M) {
         e = launch_gemv(p->fmt, p->mode, w, x, p->N, p->K, (int)M, p->gv, y, sums, s);
     } else {
@@ -231,6 +254,37 @@ extern "C" int qmatmul_run_block_sums(const qmm_plan* p, const void* w, const fl
     if (st != QMM_OK || M == 0) return st;
     if (p->mode != QMM_MODE_QACT) return fail(QMM_EUNSUPPORTED, "block sums exist only for quantized activations (mode 1)");
     return run_impl(p, w, x, nullptr, sums, M, stream);
+}
+
+extern "C" int qmatmul_run_dequantized(const qmm_plan* p, const float* w, const float* x, float* y, int64_t M,
+                                       void* stream)
+{
+    g_err[0] = 0;
+    int st = check_run(p, w, x, y, M);
+    if (st != QMM_OK || M == 0) return st;
+    if (p->mode != QMM_MODE_DEQUANT)
+        return fail(QMM_EUNSUPPORTED, "f32 weights need a dequantize-all plan (mode 2)");
+    st = dense_gemm(p->dense, w, x, y, M, p->N, p->K, (hipStream_t)stream);
+    if (st != 0) return fail(QMM_EHIP, "rocblas_sgemm: status %d", st);
+    return QMM_OK;
+}
+
+extern "C" int qmatmul_dequantize_weights(int format, const void* w, int64_t N, int64_t K, float* out, void* stream)
+{
+    g_err[0] = 0;
+    if (format != QMM_Q8_0 && format != QMM_Q4_K)
+        return fail(QMM_EUNSUPPORTED, "unsupported weight format %d", format);
+    if (N < 0 || K <= 0) return fail(QMM_EINVAL, "bad sizes N=%lld K=%lld", (long long)N, (long long)K);
+    if (K % block_values(format))
+        return fail(QMM_EBLOCK, "quantized tensor must have their last dim divisible by block size [%lld, %lld] %lld",
+                    (long long)N, (long long)K, (long long)block_values(format));
+    if (N == 0) return QMM_OK;
+    if (!w || !out) return fail(QMM_EINVAL, "null pointer");
+    if (!aligned(w, 16)) return fail(QMM_EINVAL, "w_blocks must be 16-byte aligned");
+    if (!aligned(out, 16)) return fail(QMM_EINVAL, "out must be 16-byte aligned");
+    hipError_t e = launch_dequantize(format, w, N, K, out, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(QMM_EHIP, "kernel launch: %s", hipGetErrorString(e));
+    return QMM_OK;
 }
 
 extern "C" int qmatmul_quantize_act(int act_format, const float* x, int64_t M, int64_t K, void* out, void* stream)

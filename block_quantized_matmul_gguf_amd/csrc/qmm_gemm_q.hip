@@ -446,9 +446,10 @@ constexpr int Q_KB = 1;  // block pairs per stage: 64 values
 struct QTile {
     int mw, tn;
 };
-// Tiles, (32*MW) x (32*TN): 64 x 224 puts two tiles on each of 256 compute
-// units on 512 x 14336, 128 x 224 one.
-static const QTile kQTiles[] = {{4, 7}, {2, 7}, {2, 4}, {2, 2}};
+// Tiles, (32*MW) x (32*TN): 128 x 224 puts one tile on each of 256 compute
+// units on 512 x 14336; 64 x 128 and 64 x 64 (two workgroups per compute
+// unit) keep narrow or short problems spread out.
+static const QTile kQTiles[] = {{4, 7}, {2, 4}, {2, 2}};
 
 // The tile whose busiest compute unit does the least work: rounds times the
 // tile's area, weighted by its operand reads per output.
@@ -489,7 +490,6 @@ template <int FMT>
 static hipError_t launch_q_fmt(const QGemmArgs& a, QTile t, hipStream_t s)
 {
     if (t.mw == 4) return launch_q<FMT, 4, 7>(a, s);
-    if (t.tn == 7) return launch_q<FMT, 2, 7>(a, s);
     if (t.tn == 4) return launch_q<FMT, 2, 4>(a, s);
     return launch_q<FMT, 2, 2>(a, s);
 }

@@ -7,7 +7,7 @@
 namespace qmm {
 
 enum { FMT_Q8_0 = 8, FMT_Q4_K = 12, FMT_Q8_K = 15 };
-enum { MODE_A = 0, MODE_B = 1 };
+enum { MODE_A = 0, MODE_B = 1, MODE_DEQ = 2 };
 
 // Decode (GEMV) path: M <= 8 rows; 512-thread workgroups of eight waves,
 // each wave streaming 16-row tiles over one slice of K.
@@ -64,5 +64,13 @@ hipError_t launch_gemm(int fmt, int mode, const void* w, int64_t N, int64_t K, i
                        float* y, int32_t* sums, hipStream_t s);
 hipError_t launch_gemm_q(int fmt, const void* w, int64_t N, int64_t K, int64_t M, const GemmBufs& b, float* y,
                          hipStream_t s);
+
+// Dequantize-all form: GGUF blocks -> f32 [N][K], and the plain f32 GEMM
+// (rocBLAS) behind an opaque handle; dense_* return 0 on success.
+hipError_t launch_dequantize(int fmt, const void* w, int64_t N, int64_t K, float* out, hipStream_t s);
+int dense_create(void** handle);
+void dense_destroy(void* handle);
+int dense_gemm(void* handle, const float* w, const float* x, float* y, int64_t M, int64_t N, int64_t K,
+               hipStream_t s);
 
 }  // namespace qmm

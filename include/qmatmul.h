@@ -16,6 +16,10 @@
  *                        256 values), then integer block dot products are
  *                        scaled by the weight and activation block scales (the
  *                        CPU form).
+ * and the third form the same page (section 修法) sets against them:
+ *   QMM_MODE_DEQUANT     every weight block decoded to f32 once, then a plain
+ *                        f32 matmul (CANDLE_DEQUANTIZE_ALL): no activation
+ *                        quantization, f32-sized weights.
  *
  * Block formats (little-endian; byte sizes fixed by the page "自己量化",
  * sections 和下载的 Q8_0 逐字节比 and 大小和误差):
@@ -50,6 +54,7 @@ extern "C" {
 /* modes */
 #define QMM_MODE_F32ACT 0
 #define QMM_MODE_QACT 1
+#define QMM_MODE_DEQUANT 2
 
 /* status codes */
 #define QMM_OK 0
@@ -86,6 +91,28 @@ int qmatmul_run(const qmm_plan* plan, const void* w_blocks, const float* x, floa
 /* Free a plan and its workspace (NULL is a no-op).  Synchronizes the device
  * before freeing, so pending runs of the plan finish first. */
 int qmatmul_destroy(qmm_plan* plan);
+
+/*
+ * Dequantize-all form (page "同一个 GGUF，CPU 和 Metal 生成的文字不一样",
+ * section 修法: CANDLE_DEQUANTIZE_ALL decodes every quantized weight to f32 at
+ * load, then both devices run a plain f32 matmul).
+ *
+ * qmatmul_dequantize_weights: GGUF blocks (device, N * qmatmul_row_bytes(format,
+ * K) bytes, 16-byte aligned) -> f32 [N x K] (device, 16-byte aligned, caller
+ * owned).  Every value is the exact dequantized weight (Q8_0 d*q; Q4_K
+ * d*sc_j*q - dmin*m_j) rounded once to f32.
+ *
+ * qmatmul_run_dequantized (QMM_MODE_DEQUANT plans only): y = x . W^T with W
+ * given as that f32 [N x K] matrix; x, y as in qmatmul_run.  The product is the
+ * library f32 GEMM (rocBLAS), deterministic.  qmatmul_run on a QMM_MODE_DEQUANT
+ * plan decodes w_blocks into the plan's workspace (N*K*4 bytes) first and then
+ * does the same; load-once callers decode with qmatmul_dequantize_weights and
+ * call qmatmul_run_dequantized.
+ */
+int qmatmul_dequantize_weights(int format, const void* w_blocks, int64_t N, int64_t K, float* out,
+                               void* stream);
+int qmatmul_run_dequantized(const qmm_plan* plan, const float* w_f32, const float* x, float* y,
+                            int64_t M, void* stream);
 
 /*
  * Quantize activation rows the way mode (b) does, writing canonical blocks:

@@ -41,6 +41,7 @@ def test_header_constants_match_binding():
     assert consts["QMM_Q8_K"] == qmm.Q8_K == 15
     assert consts["QMM_MODE_F32ACT"] == qmm.MODE_F32ACT
     assert consts["QMM_MODE_QACT"] == qmm.MODE_QACT
+    assert consts["QMM_MODE_DEQUANT"] == qmm.MODE_DEQUANT == 2
     for name, v in (("QMM_OK", qmm.OK), ("QMM_EINVAL", qmm.EINVAL), ("QMM_EBLOCK", qmm.EBLOCK),
                     ("QMM_EUNSUPPORTED", qmm.EUNSUPPORTED), ("QMM_ENOMEM", qmm.ENOMEM), ("QMM_EHIP", qmm.EHIP)):
         assert consts[name] == v
@@ -61,7 +62,9 @@ def test_row_bytes_and_block_sums_sizes():
     ((qmm.Q8_0, 576, 40, 1, 0), qmm.EBLOCK),
     ((7, 576, 576, 1, 0), qmm.EUNSUPPORTED),          # unknown format
     ((qmm.Q8_K, 576, 512, 1, 1), qmm.EUNSUPPORTED),   # activation-only format as weights
-    ((qmm.Q8_0, 576, 576, 1, 2), qmm.EUNSUPPORTED),   # unknown mode
+    ((qmm.Q8_0, 576, 576, 1, 3), qmm.EUNSUPPORTED),   # unknown mode
+    ((qmm.Q8_0, 576, 576, 1, 2), qmm.OK),             # dequantize-all
+    ((qmm.Q4_K, 576, 576, 1, 2), qmm.EBLOCK),
     ((qmm.Q8_0, 0, 576, 1, 0), qmm.EINVAL),
     ((qmm.Q8_0, 576, 576, 0, 0), qmm.EINVAL),
     ((qmm.Q8_0, -5, 576, 1, 0), qmm.EINVAL),
@@ -89,6 +92,7 @@ def test_run_rejects_null_plan_and_bad_m():
     lib = qmm.lib()
     assert lib.qmatmul_run(None, None, None, None, 1, None) == qmm.EINVAL
     assert lib.qmatmul_run_block_sums(None, None, None, None, 1, None) == qmm.EINVAL
+    assert lib.qmatmul_run_dequantized(None, None, None, None, 1, None) == qmm.EINVAL
     assert lib.qmatmul_destroy(None) == qmm.OK
 
 
@@ -101,6 +105,11 @@ def test_quantize_entry_points_validate_on_host():
     assert lib.qmatmul_quantize_act(qmm.Q8_0, ctypes.c_void_p(8), 2, 64, ctypes.c_void_p(64), None) == qmm.EINVAL
     assert lib.qmatmul_quantize_weights(qmm.Q8_K, None, 1, 256, None, None) == qmm.EUNSUPPORTED
     assert lib.qmatmul_quantize_weights(qmm.Q4_K, None, 1, 576, None, None) == qmm.EBLOCK
+    assert lib.qmatmul_dequantize_weights(qmm.Q8_K, None, 1, 256, None, None) == qmm.EUNSUPPORTED
+    assert lib.qmatmul_dequantize_weights(qmm.Q4_K, None, 1, 576, None, None) == qmm.EBLOCK
+    assert lib.qmatmul_dequantize_weights(qmm.Q8_0, None, 0, 64, None, None) == qmm.OK   # N = 0
+    assert lib.qmatmul_dequantize_weights(qmm.Q8_0, None, 2, 64, None, None) == qmm.EINVAL
+    assert lib.qmatmul_dequantize_weights(qmm.Q8_0, ctypes.c_void_p(16), 2, 64, ctypes.c_void_p(8), None) == qmm.EINVAL
 
 
 def test_status_strings():
@@ -116,3 +125,5 @@ def test_workspace_sizes_are_modest():
     big = qmm.workspace_bytes(qmm.Q4_K, 14336, 4096, 512, 0)
     assert 4 * 512 * 4096 <= big < 64 << 20
     assert qmm.workspace_bytes(qmm.Q4_K, 576, 576, 1, 0) == -1
+    # dequantize-all plans hold the decoded f32 weights
+    assert qmm.workspace_bytes(qmm.Q8_0, 576, 576, 1, 2) == 4 * 576 * 576
