@@ -49,6 +49,10 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-layers", type=int, default=LAYERS, help="layers in the CPU-baseline sample")
     p.add_argument("--no-dequant", action="store_true", help="skip the dequantize-all context rows")
+    p.add_argument("--workload", default="c5", choices=["c1", "c2", "c3", "c4", "c5"],
+                   help="c5 (default): the step above.  c1-c4: the pages' smaller workloads as context lines "
+                        "(q_proj GEMV, lm_head GEMV warm and cold, ffn_down Q4_K at M=1 and 37, the 30-layer "
+                        "SmolLM2 prefill at M=307 on a stream and as a HIP graph)")
     p.add_argument("--only", default="", help="restrict the step to one part, e.g. gemv:q8_0:b:1 or gemm:q4_k:a "
                                               "(for profiling one kernel); 'copy' times a plain 512 MiB device copy "
                                               "instead (the calibration for the HBM byte counters)")
@@ -155,6 +159,124 @@ def dequant_context(qmm, torch, wq, xs, ys, fmts, stream, args):
     return out
 
 
+def small_workload(args, qmm, torch, synth, stream):
+    """One JSON line for c1-c4: per-launch times from HIP events on the launch
+    stream (no weight rotation: these shapes live in the L2 or Infinity Cache,
+    as the line says), c2 also cold (a 512 MiB write between launches), c4 the
+    whole 211-projection prefill pass on a stream and replayed as a HIP graph
+    (every replay checked bit-for-bit against the stream pass first)."""
+    import numpy as np
+    dev = torch.device("cuda:0")
+    modes = {"a": qmm.MODE_F32ACT, "b": qmm.MODE_QACT}
+    fmt_code = {"q8_0": qmm.Q8_0, "q4_k": qmm.Q4_K}
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def timed(fn, reps):
+        for _ in range(max(3, args.warmup)):
+            fn()
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for _ in range(reps):
+            fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) * 1000.0 / reps  # us
+
+    def weights(prob, fmt):
+        return qmm.quantize_weights(fmt_code[fmt], torch.from_numpy(prob.weights()).to(dev))
+
+    rows = []
+    wl = args.workload
+    if wl in ("c1", "c2", "c3"):
+        probs = {"c1": [("q8_0", synth.c1_q_proj())], "c2": [("q8_0", synth.c2_lm_head())],
+                 "c3": [("q4_k", synth.c3_ffn_down(1)), ("q4_k", synth.c3_ffn_down(37))]}[wl]
+        flush = torch.empty(128 * 2 ** 20, dtype=torch.float32, device=dev) if wl == "c2" else None
+        for fmt, prob in probs:
+            w = weights(prob, fmt)
+            x = torch.from_numpy(prob.acts()).to(dev)
+            y = torch.empty((prob.m, prob.n), dtype=torch.float32, device=dev)
+            for md, mcode in modes.items():
+                with qmm.Plan(fmt_code[fmt], prob.n, prob.k, prob.m, mcode) as plan:
+                    us = timed(lambda: plan.run(w, x, y, stream), 1000 if prob.m <= 8 else 200)
+                    r = {"problem": prob.name, "fmt": fmt, "mode": md, "M": prob.m, "us_per_launch": round(us, 3),
+                         "weight_GBps": round(w.numel() / (us * 1e-6) / 1e9, 1)}
+                    if prob.m > 8:
+                        r["TOPS"] = round(2.0 * prob.m * prob.n * prob.k / (us * 1e-6) / 1e12, 2)
+                    if flush is not None:  # cold: the weights evicted by a 512 MiB write before each launch
+                        cold = []
+                        for _ in range(30):
+                            flush.fill_(1.0)
+                            ev[0].record(stream)
+                            plan.run(w, x, y, stream)
+                            ev[1].record(stream)
+                            torch.cuda.synchronize()
+                            cold.append(ev[0].elapsed_time(ev[1]) * 1000.0)
+                        cu = float(np.median(cold))
+                        r["cold_us_per_launch"] = round(cu, 3)
+                        r["cold_weight_GBps"] = round(w.numel() / (cu * 1e-6) / 1e9, 1)
+                    rows.append(r)
+        resid = {"c1": "L2-resident (352 KB of blocks)", "c2": "warm: Infinity-Cache/L2-resident (30 MB); cold: "
+                 "after a 512 MiB write", "c3": "L2-resident (498 KB of blocks); M=37 takes the prefill kernel"}[wl]
+        out = {"workload": wl, "note": resid, "rows": rows}
+    else:  # c4
+        probs = synth.c4_prefill()
+        xp = [torch.from_numpy(p.acts()).to(dev) for p in probs]
+        yp = [torch.empty((p.m, p.n), dtype=torch.float32, device=dev) for p in probs]
+        # the decode step of the same model: every projection at M = 1 (the first token's row)
+        xd = [t[:1].contiguous() for t in xp]
+        yd = [torch.empty((1, p.n), dtype=torch.float32, device=dev) for p in probs]
+        passes = {"q8_0": ["q8_0"] * len(probs),
+                  "down_q4_k": ["q4_k" if p.name.split()[0].endswith(".down") else "q8_0" for p in probs]}
+        wcache = {}
+        out = {"workload": "c4", "problems": len(probs), "M_prefill": probs[0].m, "M_decode": 1, "passes": {}}
+        total_flop = sum(2.0 * p.m * p.n * p.k for p in probs)
+        for pname, fmts in passes.items():
+            w = []
+            for p, f in zip(probs, fmts):
+                if (p.name, f) not in wcache:
+                    wcache[(p.name, f)] = weights(p, f)
+                w.append(wcache[(p.name, f)])
+            for (md, mcode), phase in [(mm, ph) for mm in modes.items() for ph in ("prefill", "decode")]:
+                x, y = (xp, yp) if phase == "prefill" else (xd, yd)
+                plans = {}
+                for p, f in zip(probs, fmts):
+                    key = (f, p.n, p.k)
+                    if key not in plans:
+                        plans[key] = qmm.Plan(fmt_code[f], p.n, p.k, p.m, mcode)
+
+                def one_pass():
+                    for i, (p, f) in enumerate(zip(probs, fmts)):
+                        plans[(f, p.n, p.k)].run(w[i], x[i], y[i], stream)
+
+                us = timed(one_pass, 10)
+                ref = [t.clone() for t in y]
+                # the same pass captured once as a HIP graph, each replay checked against the stream pass
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    cap = torch.cuda.current_stream()
+                    for i, (p, f) in enumerate(zip(probs, fmts)):
+                        plans[(f, p.n, p.k)].run(w[i], x[i], y[i], cap)
+                for rep in range(3):
+                    for t in y:
+                        t.zero_()
+                    torch.cuda.synchronize()
+                    g.replay()
+                    torch.cuda.synchronize()
+                    assert all(torch.equal(a, b) for a, b in zip(y, ref)), f"graph replay {rep} differs"
+                gus = timed(g.replay, 10)
+                flop = total_flop if phase == "prefill" else total_flop / probs[0].m
+                out["passes"][f"{phase}:{pname}:{md}"] = {
+                    "ms_per_pass_stream": round(us / 1000.0, 3), "ms_per_pass_graph": round(gus / 1000.0, 3),
+                    "TOPS_stream": round(flop / (us * 1e-6) / 1e12, 3),
+                    "TOPS_graph": round(flop / (gus * 1e-6) / 1e12, 3),
+                    "launches": len(probs)}
+                del g
+                for pl in plans.values():
+                    pl.close()
+        out["GFLOP_per_prefill_pass"] = round(total_flop / 1e9, 2)
+    print(json.dumps(out))
+
+
 def copy_calibration(torch, dev, stream, args):
     """A plain elementwise copy of 512 MiB of f32 (read 512 MiB, write
     512 MiB): the known-size kernel against which the FETCH_SIZE and WRITE_SIZE
@@ -195,6 +317,9 @@ def main():
     stream = torch.cuda.current_stream()
     if args.only == "copy":
         copy_calibration(torch, dev, stream, args)
+        return
+    if args.workload != "c5":
+        small_workload(args, qmm, torch, synth, stream)
         return
     fmts = {"q8_0": qmm.Q8_0, "q4_k": qmm.Q4_K}
     modes = {"a": qmm.MODE_F32ACT, "b": qmm.MODE_QACT}
