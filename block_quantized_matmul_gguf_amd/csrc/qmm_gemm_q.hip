@@ -109,18 +109,17 @@ __global__ __launch_bounds__(128 * MW, 2) void gemm_q_kernel(QGemmArgs a)
     const int l32 = lane & 31, hl = lane >> 5;
     const int nst = (K + SV - 1) / SV;
     const int kb_last = ((K - (nst - 1) * SV) / 32) >> 1;  // block pairs in the last stage
-    const int nsc = Q8 ? K / 32 : K / 256;                // activation scales per row
     const int64_t rb = a.row_bytes;
 
-    // Loads past the end of a resource return zeros.  The block-major scale
-    // arrays are covered whole: a row past M reads another row's (finite)
-    // values, which reach only that row's discarded outputs.  Past the end of
-    // a ragged last stage, the staging reads the next row's bytes into blocks
-    // that are never multiplied.
+    // Loads past the end of a resource return zeros: rows past M or N read
+    // zeros.  The block-major scale arrays get a resource per block row,
+    // starting at this tile's first row, so their offsets stay small at any
+    // M and K.  Past the end of a ragged last stage, the staging reads the
+    // next row's bytes into blocks that are never multiplied.
     const rsrc_t rq = make_rsrc(a.q + (int64_t)m0 * K, clamp_u32((int64_t)(M - m0) * K));
-    const rsrc_t rdxs = make_rsrc(a.dx, clamp_u32((int64_t)nsc * M * 4));
     const rsrc_t rw = make_rsrc(a.w + (int64_t)n0 * rb, clamp_u32((int64_t)(N - n0) * rb));
-    const rsrc_t rbs = make_rsrc(Q8 ? nullptr : a.bsx, Q8 ? 0u : clamp_u32((int64_t)(K / 256) * M * 32));
+    const uint32_t dx_bytes = clamp_u32((int64_t)(M - m0) * 4), bsx_bytes = clamp_u32((int64_t)(M - m0) * 32);
+    auto rdx_of = [&](int blk) { return make_rsrc(a.dx + (int64_t)blk * M + m0, dx_bytes); };
 
     // ---- staging roles, fixed for the whole K loop ----
     // activations: (row, 16-byte piece of the stage's SV bytes)
@@ -133,7 +132,7 @@ __global__ __launch_bounds__(128 * MW, 2) void gemm_q_kernel(QGemmArgs a)
     }
     // activation scales (waves 0..MW/2-1): one row per lane
     const int drow = tid & (Q_BM - 1);
-    const uint32_t dg = (uint32_t)((m0 + drow) * 4);
+    const uint32_t dg = (uint32_t)(drow * 4);
     // weight units, consecutive lanes along a row so that a load instruction
     // touches few rows; threads past the last unit repeat earlier ones (same
     // values to the same places)
@@ -155,7 +154,7 @@ __global__ __launch_bounds__(128 * MW, 2) void gemm_q_kernel(QGemmArgs a)
     const uint32_t psel = bp < 2 ? 0x05040302u : 0x07060504u;
     // Q4_K activation sub-block sums (waves 0..MW-1): (row, half)
     const int xrow = (tid >> 1) & (Q_BM - 1), xpart = tid & 1;
-    const uint32_t xg = (uint32_t)(((m0 + xrow) * 16 + 8 * xpart) * 2);
+    const uint32_t xg = (uint32_t)((xrow * 16 + 8 * xpart) * 2);
 
     // ---- staging registers ----
     uint4 ra[AU];
@@ -173,9 +172,9 @@ __global__ __launch_bounds__(128 * MW, 2) void gemm_q_kernel(QGemmArgs a)
             if constexpr (Q8) {
 #pragma unroll
                 for (int b = 0; b < SB; ++b)
-                    rdx[b] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdxs, dg, (SB * st + b) * M * 4, 0));
+                    rdx[b] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdx_of(SB * st + b), dg, 0, 0));
             } else {
-                rdx[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdxs, dg, (SV * st / 256) * M * 4, 0));
+                rdx[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdx_of(SV * st / 256), dg, 0, 0));
             }
         }
         if constexpr (Q8) {
@@ -193,7 +192,8 @@ __global__ __launch_bounds__(128 * MW, 2) void gemm_q_kernel(QGemmArgs a)
                     rhd[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, brow[i] * (uint32_t)rb, 144 * sb, 0));
             }
             if (c0 == 0 && wave < MW)
-                rbx = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rbs, xg, sb * M * 32, 0));
+                rbx = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                    make_rsrc(a.bsx + ((int64_t)sb * M + m0) * 16, bsx_bytes), xg, 0, 0));
         }
     };
 
