@@ -84,6 +84,10 @@ int qmatmul_create(qmm_plan** out, int format, int64_t N, int64_t K, int64_t M_m
  * decode (GEMV) kernels, larger M the prefill (GEMM) kernels.  The caller owns
  * w, x and y; the plan keeps no pointer after the call.  The plan's workspace
  * is shared by its runs: do not run one plan concurrently on two streams.
+ * A run only enqueues kernels (no allocation, memset or synchronization), so
+ * runs may be captured in a HIP graph once each kernel has run eagerly (its
+ * launch attributes are set on first use); the exception is a
+ * QMM_MODE_DEQUANT plan at M > 8, whose product is a rocBLAS call.
  */
 int qmatmul_run(const qmm_plan* plan, const void* w_blocks, const float* x, float* y,
                 int64_t M, void* stream);

@@ -1,0 +1,56 @@
+"""Runs captured in a HIP graph: qmatmul_run enqueues kernels only (no device
+allocation, no memset, no synchronization), so a captured sequence of runs
+replays to the same bits as the eager runs.  Each replay is checked against
+the eager result, with eager work on the same buffers between replays."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import block_quantized_matmul_gguf_amd as qmm  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    qmm.lib()
+
+
+CASES = [(qmm.Q8_0, qmm.MODE_F32ACT, 1), (qmm.Q8_0, qmm.MODE_QACT, 8), (qmm.Q4_K, qmm.MODE_QACT, 1),
+         (qmm.Q8_0, qmm.MODE_QACT, 96), (qmm.Q4_K, qmm.MODE_F32ACT, 96), (qmm.Q8_0, qmm.MODE_DEQUANT, 4)]
+
+
+@pytest.mark.parametrize("fmt,mode,m", CASES, ids=[f"fmt{f}-mode{md}-M{m}" for f, md, m in CASES])
+def test_graph_replays_match_eager_runs(fmt, mode, m):
+    n, k = 640, 1536 if fmt == qmm.Q4_K else 576
+    dev = torch.device("cuda")
+    w = [torch.from_numpy(oracle.quantize(fmt, synth.weights_f32(7000 + i, n, k))).to(dev) for i in range(3)]
+    x = torch.from_numpy(synth.acts_f32(7100 + m, m, k)).to(dev)
+    ys = [torch.empty((m, n), dtype=torch.float32, device=dev) for _ in w]
+    with qmm.Plan(fmt, n, k, m, mode) as p:
+        stream = torch.cuda.current_stream()
+        for wi, yi in zip(w, ys):  # eager runs (also set the kernels' launch attributes before capture)
+            p.run(wi, x, yi, stream)
+        torch.cuda.synchronize()
+        ref = [t.clone() for t in ys]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cap = torch.cuda.current_stream()
+            for wi, yi in zip(w, ys):
+                p.run(wi, x, yi, cap)
+        for rep in range(4):
+            for t in ys:
+                t.fill_(float("nan"))
+            p.run(w[0], x, ys[0], stream)  # eager work on the same plan and buffers between replays
+            torch.cuda.synchronize()
+            assert torch.equal(ys[0], ref[0])
+            g.replay()
+            torch.cuda.synchronize()
+            for i, (a, b) in enumerate(zip(ys, ref)):
+                assert torch.equal(a, b), f"replay {rep}, run {i} differs from the eager run"
+        del g
