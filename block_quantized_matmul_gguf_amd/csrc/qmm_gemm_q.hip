@@ -130,7 +130,8 @@ __global__ __launch_bounds__(128 * MW, 2) void gemm_q_kernel(QGemmArgs a)
         ag[i] = (uint32_t)(row * K + 16 * part);
         as_[i] = (uint32_t)((part >> 1) * C::A_BLK + qswz(row, part & 1));
     }
-    // activation scales (waves 0..MW/2-1): one row per lane
+    // activation scales (waves 0..DW-1): one row per lane
+    constexpr int DW = MW / 2 > 0 ? MW / 2 : 1;
     const int drow = tid & (Q_BM - 1);
     const uint32_t dg = (uint32_t)(drow * 4);
     // weight units, consecutive lanes along a row so that a load instruction
@@ -168,7 +169,7 @@ __global__ __launch_bounds__(128 * MW, 2) void gemm_q_kernel(QGemmArgs a)
 #pragma unroll
         for (int i = 0; i < AU; ++i)
             ra[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, ag[i], SV * st, 0));
-        if (wave < MW / 2) {
+        if (wave < DW) {
             if constexpr (Q8) {
 #pragma unroll
                 for (int b = 0; b < SB; ++b)
@@ -201,7 +202,6 @@ __global__ __launch_bounds__(128 * MW, 2) void gemm_q_kernel(QGemmArgs a)
     // loop spreads over its MFMAs: item 0 the activation pieces and scales,
     // item 1 + i weight unit i
     constexpr int NI = 1 + BU;
-    static_assert(NI <= TN, "the staging items must fit in one block's MFMAs");
     auto store_item = [&](int w, int st, auto pc) {
         constexpr int P = decltype(pc)::value;
         uint8_t* sb_ = lds + C::OFF_B + P * SB * C::B_BLK;
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(128 * MW, 2) void gemm_q_kernel(QGemmArgs a)
         if (w == 0) {
 #pragma unroll
             for (int i = 0; i < AU; ++i) *reinterpret_cast<uint4*>(lds + C::OFF_A + P * SB * C::A_BLK + as_[i]) = ra[i];
-            if (wave < MW / 2) {
+            if (wave < DW) {
                 float* sdx = reinterpret_cast<float*>(lds + C::OFF_DX) + P * SB * Q_BM + drow;
 #pragma unroll
                 for (int b = 0; b < SB; ++b) sdx[b * Q_BM] = Q8 ? rdx[Q8 ? b : 0] : rdx[0];
@@ -375,7 +375,10 @@ __global__ __launch_bounds__(128 * MW, 2) void gemm_q_kernel(QGemmArgs a)
         constexpr int P = decltype(pc)::value;
         const int nx = st + 1 < nst ? st + 1 : last, nx2 = st + 2 < nst ? st + 2 : last;
         compute(st, pc, st == last ? kb_last : KB, [&](int j) {
-            if (j < NI) store_item(j, nx, std::integral_constant<int, P ^ 1>{});
+            // item j after MFMA j; a narrow tile runs the rest after its last MFMA
+#pragma unroll
+            for (int w = 0; w < NI; ++w)
+                if (w == j || (j == TN - 1 && w > j)) store_item(w, nx, std::integral_constant<int, P ^ 1>{});
             if (j == (NI < TN ? NI : TN - 1)) load(nx2);
         });
         __syncthreads();
@@ -447,22 +450,25 @@ struct QTile {
     int mw, tn;
 };
 // Tiles, (32*MW) x (32*TN): 128 x 224 puts one tile on each of 256 compute
-// units on 512 x 14336; 64 x 128 and 64 x 64 (two workgroups per compute
-// unit) keep narrow or short problems spread out.
+// units on 512 x 14336; 64 x 128 and 64 x 64 (two or more workgroups per
+// compute unit) keep narrow or short problems spread out.  (A 32 x 64 tile
+// measured slower than 64 x 64 on every shape tried.)
 static const QTile kQTiles[] = {{4, 7}, {2, 4}, {2, 2}};
 
-// The tile whose busiest compute unit does the least work: rounds times the
-// tile's area, weighted by its operand reads per output.
+// The tile whose busiest compute unit finishes first: its tiles times a
+// tile's area, over the SIMDs its waves keep busy (a tile has 2*MW waves, a
+// compute unit 4 SIMDs), weighted by the operand reads per output.
 static QTile pick_qtile(int64_t M, int64_t N)
 {
     const int64_t cus = cu_count_q();
     QTile best = kQTiles[0];
     double bc = -1.0;
     for (const QTile& t : kQTiles) {
-        const int64_t bm = 32 * t.mw, bn = 32 * t.tn, slots = cus * (t.mw == 4 ? 1 : 2);
+        const int64_t bm = 32 * t.mw, bn = 32 * t.tn;
         const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
-        const double cost = (double)((tiles + slots - 1) / slots) * (double)(bm * bn) * (t.mw == 4 ? 0.5 : 1.0) *
-                            (1.0 + 8.0 / bn + 16.0 / bm);
+        const int64_t per_cu = (tiles + cus - 1) / cus;
+        const int64_t simds = 2 * t.mw * per_cu < 4 ? 2 * t.mw * per_cu : 4;
+        const double cost = (double)per_cu * (double)(bm * bn) / (double)simds * (1.0 + 8.0 / bn + 16.0 / bm);
         if (bc < 0 || cost < bc) {
             bc = cost;
             best = t;
