@@ -47,6 +47,28 @@ QMM_DEV float wave_max(float v)
                  fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)), __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48))));
 }
 
+// Waits until at most N of this wave's vector memory operations are
+// outstanding.  They retire in issue order, so after vm_wait<k*T> every stage
+// but the last k issued has landed.  The compiler does not track loads that
+// write LDS directly, hence the explicit waits ("memory" keeps LDS reads after).
+template <int N>
+QMM_DEV void vm_wait()
+{
+    static_assert(N >= 0 && N <= 63, "vmcnt holds 0..63");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// vm_wait<ahead*T> for a wave-uniform ahead in [0, I].
+template <int T, int I>
+QMM_DEV void vm_wait_ahead(int ahead)
+{
+    if constexpr (I == 0) {
+        vm_wait<0>();
+    } else {
+        if (ahead >= I) vm_wait<I * T>();
+        else vm_wait_ahead<T, I - 1>(ahead);
+    }
+}
+QMM_DEV void lgkm_wait0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 // Byte count for a buffer resource, saturated to its 32-bit field.
 QMM_DEV uint32_t clamp_u32(int64_t v) { return v > 0xffffffffll ? 0xffffffffu : (uint32_t)v; }
 

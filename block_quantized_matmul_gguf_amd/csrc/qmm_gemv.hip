@@ -73,6 +73,9 @@ static void gv_fmt(int fmt, int mode, int ms, int& lub, int& ops, int& vpl, int&
 // 16-byte chunks per row in a stage of P load units (the last may run past
 // the stage: those bytes are read but not used).
 constexpr int gv_cpr(int fmt, int P) { return fmt == FMT_Q8_0 ? (68 * P + 15) / 16 : 9 * P; }
+constexpr bool gv_ring_ok(int fmt, int P) { return (gv_cpr(fmt, P) & 1) == 1; }
+constexpr int kRingMax = 3;  // LDS-direct stage buffers per wave at most (4 measured slower)
+constexpr int kRingMin = 2;  // fewer than this fit: register staging
 // LDS row stride of the stage buffer: an odd number of 16-byte units, so the
 // 16 rows a wave gathers from start in different banks.
 constexpr int gv_rs(int fmt, int P) { return 16 * (gv_cpr(fmt, P) | 1); }
@@ -129,17 +132,35 @@ QMM_DEV void wg_signal(int* c, bool release)
     if (release) __hip_atomic_fetch_add(c, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     else __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
+// The counters and the data they guard are in LDS, whose reads a wave performs
+// in order, and the signalling wave's LDS writes are complete before its
+// release add: a relaxed read plus a compiler barrier orders the reads after
+// the wait.  (An acquire read would also wait for every outstanding global
+// load, the weight stream's prefetch included.)
 QMM_DEV void wg_wait(int* c, int target)
 {
     for (int spin = 0; spin < (1 << 22); ++spin) {
-        if (__hip_atomic_load(c, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+        if (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
         __builtin_amdgcn_s_sleep(1);
     }
+    asm volatile("" ::: "memory");
+}
+
+// 16 bytes per lane from the buffer at voff into LDS at dst + 16 * lane (dst wave-uniform)
+QMM_DEV void ld128_lds(rsrc_t r, uint8_t* dst, uint32_t voff)
+{
+    typedef __attribute__((address_space(3))) void* lds_ptr_t;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 16, voff, 0, 0, 0);
 }
 
 // R: activation rows per lane the arithmetic covers (1 when M == 1, else 4:
 // lane l holds output rows 4*(l/16 % 2) + r of its tile column l%16).
-template <int FMT, int MODE, int P, int R, bool EMIT>
+// D: 0 = each stage is loaded into registers (two stages in flight) and
+// written to one LDS buffer per wave; D >= 2 = a ring of D stage buffers per
+// wave filled by 16-byte loads that write LDS directly (lane i of a load lands
+// at its base + 16 i, so the stage keeps the row-major chunk layout), D
+// stages in flight and no registers or LDS writes spent on the stream.
+template <int FMT, int MODE, int P, int R, bool EMIT, int D>
 __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
 {
     constexpr int MS = R == 1 ? 1 : 8;
@@ -147,6 +168,9 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
     constexpr int LUB = F::LUB, OPS = F::OPS, VPL = F::VPL, OPB = F::OPB, SCB = F::SCB;
     constexpr int CPR = gv_cpr(FMT, P), RS = gv_rs(FMT, P);
     constexpr int T = (16 * CPR + 63) / 64;  // load instructions per stage
+    static_assert(D == 0 || (D >= 2 && !EMIT && (D - 1) * T <= 63), "ring of LDS-direct stages");
+    constexpr int RSW = D > 0 ? 16 * CPR : RS;  // stage row stride in LDS (direct loads: unpadded)
+    constexpr int SBY = 16 * RSW;               // bytes of one stage buffer
     extern __shared__ __align__(16) uint8_t lds[];
     uint8_t* s_img = lds;
     float* s_scf = reinterpret_cast<float*>(lds + a.sc_off);
@@ -171,7 +195,7 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
     const int S = a.slice / P;
     const int S_real = (sl_real + P - 1) / P;
     const int Q = ngrp * S;                                   // stages per wave
-    uint8_t* stg = lds + a.stg_off + wave * (16 * RS);
+    uint8_t* stg = lds + a.stg_off + wave * ((D > 0 ? D : 1) * SBY);
 
     // ---- the weight stream: chunk f = 64t + lane of a stage is row f/CPR, chunk f%CPR ----
     uint32_t go[T], lw[T];
@@ -184,20 +208,50 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
     constexpr int TAIL = 16 * CPR - 64 * (T - 1);  // live lanes of the last load
 
     int iq = 0, iu = 0, is = 0;  // next stage to queue: index, tile, stage within the tile
-    auto issue = [&](u32x4_t (&r)[T]) {
+    // the next stage's source: the tile's rows as a buffer (rows past N, and stages
+    // past the wave's real units, read as zero) and the stage's byte offset in a row
+    auto next_src = [&](rsrc_t& wr, uint32_t& so) {
         const bool real = iq < Q && is < S_real;
         const int tile = (grp0 + iu) * a.G + tg;
         const int64_t t0 = (int64_t)tile * 16 * a.row_bytes;
         const int64_t left = a.w_bytes - t0;
         const uint32_t nrec = real && left > 0 ? (uint32_t)min(left, (int64_t)16 * a.row_bytes) : 0u;
-        const rsrc_t wr = make_rsrc(a.w + (real ? t0 : 0), nrec);
-        const uint32_t so = (uint32_t)((lu_beg + sl_lu0 + is * P) * LUB);
+        wr = make_rsrc(a.w + (real ? t0 : 0), nrec);
+        so = (uint32_t)((lu_beg + sl_lu0 + is * P) * LUB);
         ++iq;
         if (++is == S) { is = 0; ++iu; }
+    };
+    auto issue = [&](u32x4_t (&r)[T]) {
+        rsrc_t wr;
+        uint32_t so;
+        next_src(wr, so);
 #pragma unroll
         for (int t = 0; t < T; ++t) r[t] = ld128(wr, go[t] + so);
     };
-    u32x4_t rA[T], rB[T];
+    // LDS-direct form: the next stage into ring buffer `slot` (lanes past the
+    // stage's last chunk stay off, so nothing lands beyond the buffer)
+    auto issue_lds = [&](int slot) {
+        rsrc_t wr;
+        uint32_t so;
+        next_src(wr, so);
+        uint8_t* buf = stg + slot * SBY;
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+            if (t < T - 1 || lane < TAIL)
+                ld128_lds(wr, buf + 1024 * t, go[t] + so);
+    };
+    u32x4_t rA[D > 0 ? 1 : T], rB[D > 0 ? 1 : T];
+    // the first stages of the stream: two into registers, or the whole ring
+    auto prime = [&]() {
+        if constexpr (D > 0) {
+#pragma unroll
+            for (int i = 0; i < D; ++i)
+                if (iq < Q) issue_lds(i);
+        } else {
+            issue(rA);
+            issue(rB);
+        }
+    };
 
     // ---- the activation operand of this K split, once per workgroup ----
     // Each task fills one 16-byte operand slot (mode b: 16 int8 of one half of a
@@ -300,8 +354,7 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
             }
         }
     } else {
-        issue(rA);
-        issue(rB);
+        prime();
     }
     if constexpr (MODE == MODE_A) {
         // power-of-two scale per row over this split, then the hi/lo f16 split; a wave
@@ -424,8 +477,7 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
             }
         }
         if (lane == 0) wg_signal(&s_sync[2], true);  // this wave's slots are written
-        issue(rA);
-        issue(rB);
+        prime();
     }
     wg_wait(&s_sync[2], npw);  // the whole operand is in place
 
@@ -447,7 +499,6 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
     }
     const uint8_t* aimg = s_img + aslot * 16;
     const int moff = MS == 8 ? 4 * (g & 1) : 0;  // this lane's first output row within the slots
-    const uint8_t* rrow = stg + n * RS;           // this lane's weight row in the stage buffer
 
     f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
     const i32x4_t zi = {0, 0, 0, 0};
@@ -462,7 +513,8 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
     asm volatile("" : "+v"(nibm), "+v"(nibc));
 
 
-    auto compute = [&](int lu0, int tile) {
+    auto compute = [&](const uint8_t* sbuf, int lu0, int tile) {
+        const uint8_t* rrow = sbuf + n * RSW;  // this lane's weight row in the stage buffer
 #pragma unroll
         for (int j = 0; j < P; ++j) {
             const int lu = lu0 + j;  // load unit within the split
@@ -602,14 +654,17 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
     };
 
     int cq = 0, cu = 0, cs = 0;  // next stage to compute: index, tile group, stage within the tile
-    auto step = [&](u32x4_t (&r)[T]) {
-        if (cq < Q) {
+    // computes stage cq from sbuf (r: its registers, to land first) and closes its tile group
+    auto consume = [&](const uint8_t* sbuf, const u32x4_t* r) {
+        {
             if (cs < S_real) {
-                // land the stage in this wave's LDS buffer (the gather below reads other lanes' chunks)
+                if constexpr (D == 0) {
+                    // land the stage in this wave's LDS buffer (the gather below reads other lanes' chunks)
 #pragma unroll
-                for (int t = 0; t < T; ++t)
-                    if (t < T - 1 || lane < TAIL) *reinterpret_cast<u32x4_t*>(stg + lw[t]) = r[t];
-                compute(sl_lu0 + cs * P, (grp0 + cu) * a.G + tg);
+                    for (int t = 0; t < T; ++t)
+                        if (t < T - 1 || lane < TAIL) *reinterpret_cast<u32x4_t*>(stg + lw[t]) = r[t];
+                }
+                compute(sbuf, sl_lu0 + cs * P, (grp0 + cu) * a.G + tg);
             }
             if (cs == S - 1) {
                 // the tile group is done in every wave: fold the two lane halves, park the
@@ -645,11 +700,33 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
         }
         ++cq;
         if (++cs == S) { cs = 0; ++cu; }
-        issue(r);
     };
-    for (int q = 0; q < Q; q += 2) {
-        step(rA);
-        step(rB);
+    if constexpr (D == 0) {
+        auto step = [&](u32x4_t (&r)[T]) {
+            if (cq < Q) {
+                consume(stg, r);
+            } else {
+                ++cq;
+                if (++cs == S) { cs = 0; ++cu; }
+            }
+            issue(r);
+        };
+        for (int q = 0; q < Q; q += 2) {
+            step(rA);
+            step(rB);
+        }
+    } else {
+        // stage q sits in ring buffer q % D; once it is consumed, stage q + D takes its place
+        int slot = 0;
+        for (int q = 0; q < Q; ++q) {
+            vm_wait_ahead<T, D - 1>(min(D - 1, Q - 1 - q));  // stage q has landed
+            consume(stg + slot * SBY, nullptr);
+            if (iq < Q) {
+                lgkm_wait0();  // this buffer's reads are done before it is refilled
+                issue_lds(slot);
+            }
+            slot = slot == D - 1 ? 0 : slot + 1;
+        }
     }
 }
 
@@ -669,41 +746,55 @@ __global__ __launch_bounds__(256) void gemv_reduce_kernel(const float* __restric
 
 typedef void (*GvKernel)(GemvArgs);
 
-template <int FMT, int MODE, int P>
-static GvKernel gv_pick_r(int R, bool emit)
+// (stage sizes without the ring map every depth to register staging)
+template <int FMT, int MODE, int P, int R>
+static GvKernel gv_pick_d(int D)
 {
-    if constexpr (MODE == MODE_B && P == 1)
-        if (emit) return gemv_kernel<FMT, MODE, 1, 4, true>;
-    return R == 1 ? gemv_kernel<FMT, MODE, P, 1, false> : gemv_kernel<FMT, MODE, P, 4, false>;
+    constexpr bool ok = gv_ring_ok(FMT, P);
+    if (D == 4) return gemv_kernel<FMT, MODE, P, R, false, ok ? 4 : 0>;
+    if (D == 3) return gemv_kernel<FMT, MODE, P, R, false, ok ? 3 : 0>;
+    if (D == 2) return gemv_kernel<FMT, MODE, P, R, false, ok ? 2 : 0>;
+    return gemv_kernel<FMT, MODE, P, R, false, 0>;
 }
 
-// Stage sizes (load units) compiled for each format.
+template <int FMT, int MODE, int P>
+static GvKernel gv_pick_r(int R, bool emit, int D)
+{
+    if constexpr (MODE == MODE_B && P == 1)
+        if (emit) return gemv_kernel<FMT, MODE, 1, 4, true, 0>;
+    return R == 1 ? gv_pick_d<FMT, MODE, P, 1>(D) : gv_pick_d<FMT, MODE, P, 4>(D);
+}
+
+// Stage sizes (load units) compiled for each format.  The LDS-direct ring
+// (up to kRingMax stage buffers per wave) is compiled for the stage sizes whose
+// rows are an odd number of 16-byte chunks: then the unpadded row-major stage
+// layout starts the 16 rows in different banks, as the padded one does.
 static const int kStageQ8[] = {4, 3, 2, 1};
 static const int kStageQ4[] = {2, 3, 1};
 static const int kNStageQ8 = 4, kNStageQ4 = 3;
 
-static GvKernel gv_kernel(int fmt, int mode, int P, int R, bool emit)
+static GvKernel gv_kernel(int fmt, int mode, int P, int R, bool emit, int D)
 {
     if (fmt == FMT_Q8_0) {
-        if (mode == MODE_A) return P == 4 ? gv_pick_r<FMT_Q8_0, MODE_A, 4>(R, false)
-                                   : P == 3 ? gv_pick_r<FMT_Q8_0, MODE_A, 3>(R, false)
-                                   : P == 2 ? gv_pick_r<FMT_Q8_0, MODE_A, 2>(R, false)
-                                            : gv_pick_r<FMT_Q8_0, MODE_A, 1>(R, false);
-        return P == 4 ? gv_pick_r<FMT_Q8_0, MODE_B, 4>(R, emit)
-             : P == 3 ? gv_pick_r<FMT_Q8_0, MODE_B, 3>(R, emit)
-             : P == 2 ? gv_pick_r<FMT_Q8_0, MODE_B, 2>(R, emit)
-                      : gv_pick_r<FMT_Q8_0, MODE_B, 1>(R, emit);
+        if (mode == MODE_A) return P == 4 ? gv_pick_r<FMT_Q8_0, MODE_A, 4>(R, false, D)
+                                   : P == 3 ? gv_pick_r<FMT_Q8_0, MODE_A, 3>(R, false, D)
+                                   : P == 2 ? gv_pick_r<FMT_Q8_0, MODE_A, 2>(R, false, D)
+                                            : gv_pick_r<FMT_Q8_0, MODE_A, 1>(R, false, D);
+        return P == 4 ? gv_pick_r<FMT_Q8_0, MODE_B, 4>(R, emit, D)
+             : P == 3 ? gv_pick_r<FMT_Q8_0, MODE_B, 3>(R, emit, D)
+             : P == 2 ? gv_pick_r<FMT_Q8_0, MODE_B, 2>(R, emit, D)
+                      : gv_pick_r<FMT_Q8_0, MODE_B, 1>(R, emit, D);
     }
-    if (mode == MODE_A) return P == 2 ? gv_pick_r<FMT_Q4_K, MODE_A, 2>(R, false)
-                               : P == 3 ? gv_pick_r<FMT_Q4_K, MODE_A, 3>(R, false)
-                                        : gv_pick_r<FMT_Q4_K, MODE_A, 1>(R, false);
-    return P == 2 ? gv_pick_r<FMT_Q4_K, MODE_B, 2>(R, emit)
-         : P == 3 ? gv_pick_r<FMT_Q4_K, MODE_B, 3>(R, emit)
-                  : gv_pick_r<FMT_Q4_K, MODE_B, 1>(R, emit);
+    if (mode == MODE_A) return P == 2 ? gv_pick_r<FMT_Q4_K, MODE_A, 2>(R, false, D)
+                               : P == 3 ? gv_pick_r<FMT_Q4_K, MODE_A, 3>(R, false, D)
+                                        : gv_pick_r<FMT_Q4_K, MODE_A, 1>(R, false, D);
+    return P == 2 ? gv_pick_r<FMT_Q4_K, MODE_B, 2>(R, emit, D)
+         : P == 3 ? gv_pick_r<FMT_Q4_K, MODE_B, 3>(R, emit, D)
+                  : gv_pick_r<FMT_Q4_K, MODE_B, 1>(R, emit, D);
 }
 
 // Compute units of the current device, cached per device.
-static int device_cus()
+int device_cus()
 {
     static std::map<int, int> cache;
     static std::mutex mu;
@@ -738,7 +829,7 @@ bool gemv_supported(int fmt, int64_t K)
     return fmt == FMT_Q4_K ? K % 256 == 0 : K % 64 == 0;
 }
 
-// LDS bytes of the eight waves' weight stage buffers.
+// LDS bytes of the eight waves' weight stage buffers (one each, register staging).
 static int stage_bytes(int fmt, int P) { return GV_WAVES * 16 * (fmt == FMT_Q8_0 ? gv_rs(FMT_Q8_0, P) : gv_rs(FMT_Q4_K, P)); }
 
 // K splits of one run: enough that the activation operand of a split (with
@@ -801,8 +892,13 @@ GemvGeom gemv_geom(int fmt, int mode, int64_t N, int64_t K, int M, bool emit)
             const int groups = (g.tiles + G - 1) / G;
             const int img = kw * slice * ops * opb;
             const int sc = kw * slice * scb;
-            const int stg = stage_bytes(fmt, P);
-            const int lds = img + sc + GV_RED_BYTES + GV_MISC_BYTES + stg;
+            const int fixed = img + sc + GV_RED_BYTES + GV_MISC_BYTES;
+            // the deepest LDS-direct ring that fits, else one register-staged buffer per wave
+            int D = 0;
+            if (!emit && gv_ring_ok(fmt, P))
+                for (int d = kRingMax; d >= kRingMin && !D; --d)
+                    if (fixed + d * stage_bytes(fmt, P) <= GV_LDS_MAX) D = d;
+            const int lds = fixed + (D > 0 ? D : 1) * stage_bytes(fmt, P);
             if (lds > GV_LDS_MAX) continue;
             const int cpr = fmt == FMT_Q8_0 ? gv_cpr(FMT_Q8_0, P) : gv_cpr(FMT_Q4_K, P);
             const int64_t loop = (int64_t)(slice / P) * (256 * cpr + 512);
@@ -818,6 +914,7 @@ GemvGeom gemv_geom(int fmt, int mode, int64_t N, int64_t K, int M, bool emit)
                 g.groups = groups;
                 g.gpw = gpw;
                 g.rs = fmt == FMT_Q8_0 ? gv_rs(FMT_Q8_0, P) : gv_rs(FMT_Q4_K, P);
+                g.D = D;
                 g.sc_off = img;
                 g.red_off = img + sc;
                 g.misc_off = g.red_off + GV_RED_BYTES;
@@ -836,6 +933,7 @@ hipError_t launch_gemv(int fmt, int mode, const void* w, const float* x, int64_t
                        const GemvBufs& b, float* y, int32_t* sums, hipStream_t s)
 {
     const bool emit = sums != nullptr;
+    if (gemv_row_supported(fmt, mode, M, K, emit)) return launch_gemv_row(fmt, w, x, N, K, y, s);
     const GemvGeom g = gemv_geom(fmt, mode, N, K, M, emit);
     if (g.grid <= 0) return hipErrorInvalidConfiguration;
     GemvArgs a{};
@@ -861,7 +959,7 @@ hipError_t launch_gemv(int fmt, int mode, const void* w, const float* x, int64_t
     a.part = b.part;
     a.y = y;
     a.sums = sums;
-    GvKernel k = gv_kernel(fmt, mode, g.P, g.R, emit);
+    GvKernel k = gv_kernel(fmt, mode, g.P, g.R, emit, g.D);
     allow_full_lds(k);
     void* args[] = {&a};
     hipError_t e = hipLaunchKernel((const void*)k, dim3(g.grid), dim3(GV_THREADS), args, g.lds, s);

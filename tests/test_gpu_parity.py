@@ -132,6 +132,33 @@ def test_matmul_parity(fmt, n, k, mode, m):
     assert_within(y, yr, a, f"{FMT_NAME[fmt]} {n}x{k} M={m} mode={mode}")
 
 
+# One activation row streams weight rows whole, in segments of 64 block pairs
+# (Q8_0) or 8 super-blocks (Q4_K), several rows per wave: rows longer than one
+# segment with a short last segment, one-pair last segments, more rows than
+# waves by far (outputs leave a wave 64 at a time), fewer rows than waves, and
+# rows past the segment limit (the tile kernel takes those).
+ROW_SHAPES = [
+    (qmm.Q8_0, 70, 14336),    # four segments, the last 32 pairs
+    (qmm.Q8_0, 33, 8256),     # three segments, the last one pair
+    (qmm.Q8_0, 5, 576),       # fewer rows than waves
+    (qmm.Q8_0, 140000, 64),   # about 69 rows per wave
+    (qmm.Q8_0, 24, 16448),    # past the segment limit
+    (qmm.Q4_K, 70, 14336),    # seven segments of super-blocks
+    (qmm.Q4_K, 37, 2304),     # one short segment
+    (qmm.Q4_K, 140000, 256),  # one super-block per row, about 69 rows per wave
+]
+
+
+@pytest.mark.parametrize("mode", [qmm.MODE_F32ACT, qmm.MODE_QACT], ids=["a", "b"])
+@pytest.mark.parametrize("fmt,n,k", ROW_SHAPES, ids=[f"{FMT_NAME[f]}-{n}x{k}" for f, n, k in ROW_SHAPES])
+def test_single_row_decode_shapes(fmt, n, k, mode):
+    wq = oracle.quantize(fmt, synth.weights_f32(6000 + n + k, n, k))
+    x = synth.acts_f32(6001 + k, 1, k)
+    y = run_plan(fmt, mode, wq, n, k, x)
+    yr, a = ref(fmt, mode, wq, n, k, x)
+    assert_within(y, yr, a, f"{FMT_NAME[fmt]} {n}x{k} M=1 mode={mode}")
+
+
 @pytest.mark.parametrize("mode", [qmm.MODE_F32ACT, qmm.MODE_QACT], ids=["a", "b"])
 @pytest.mark.parametrize("fmt", [qmm.Q8_0, qmm.Q4_K], ids=["Q8_0", "Q4_K"])
 @pytest.mark.parametrize("m", [1, 8, 40])
