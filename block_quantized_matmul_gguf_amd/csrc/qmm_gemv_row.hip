@@ -1,6 +1,9 @@
-// qmm_gemv_row.hip -- decode kernel for one activation row (M == 1) in mode
-// (b), Q8_0 and Q4_K weights.
+// qmm_gemv_row.hip -- decode kernel for one activation row (M == 1), Q8_0 and
+// Q4_K weights, modes (a) and (b).
 //
+// Mode (a) is the Metal form of the same page and section: f32 activations
+// against the dequantized weights, y[n] = sum_k w[n][k] x[k], w = d q (Q8_0)
+// or d sc_j q - dmin m_j (Q4_K, sub-block j).
 // Mode (b) is the CPU form of page "同一个 GGUF，CPU 和 Metal 生成的文字不一样"
 // (section 出处): the activation row is quantized on its own, per 32 values to
 // Q8_0 for Q8_0 weights (page "自己量化", section 和下载的 Q8_0 逐字节比) and per
@@ -29,16 +32,22 @@
 //     dot products are v_dot4 against activation values the lane holds in
 //     registers; a Q4_K super-block's four lanes add their scaled integer
 //     sums exactly before the f32 step.
-//   * Each wave has a ring of two segment buffers, so the next segment's
-//     loads are in flight while the current one is summed (deeper rings
-//     measured slower, for either format).  Every segment issues the
+//   * Each wave keeps two segments in flight (deeper measured slower, for
+//     either format).  With three segment buffers (where LDS allows) segment
+//     u + 2 is issued before segment u is summed, so the stream never waits
+//     on the arithmetic; with two it is issued after.  Every segment issues the
 //     same number of load instructions with every lane on (lanes past the
 //     segment re-read its first bytes into the buffer's tail), which keeps the
 //     explicit waits exact and the issue free of branches.
-//   * The activation row is brought into LDS ahead of the stream and
-//     quantized once per workgroup with the device functions every other
-//     activation quantizer uses, so its blocks are the same bytes; each lane
-//     then holds its activation values in registers for all of its rows.
+//   * The activation row is brought into LDS ahead of the stream.  Mode (b)
+//     quantizes it once per workgroup with the device functions every other
+//     activation quantizer uses, so its blocks are the same bytes; mode (a)
+//     keeps it f32.  Each lane then holds its activation values in registers
+//     for all of its rows (mode (a): 64 f32, so rows of one segment only).
+//   * Mode (a) decodes the lane's weights to exact f32 integers (signed bytes,
+//     nibbles) and forms per-block sums of q x with fused multiply-adds; the
+//     block then scales them: Q8_0 d S, Q4_K (d sc_j) S_j - (dmin m_j) sum x
+//     over the sub-block (the decomposition the tile kernel uses too).
 //   * A row's per-lane f32 sums are added across the wave in a fixed order:
 //     a run is deterministic.
 #include <algorithm>
@@ -110,11 +119,13 @@ QMM_DEV float wave_sum(float v)
 
 // LPU: load instructions per segment, ceil(min(row bytes, segment bytes) / 1024);
 // a segment buffer holds LPU KB.  NSEG: segments per row.  RING: segment
-// buffers per wave (a power of two).  Every global load of the kernel writes
-// LDS directly, so all waits on them are the explicit ones.
-template <int FMT, int LPU, int NSEG, int RING>
+// buffers per wave (2 or 3); two segments are in flight either way.  Every
+// global load of the kernel writes LDS directly, so all waits on them are the
+// explicit ones.
+template <int FMT, int MODE, int LPU, int NSEG, int RING>
 __global__ __launch_bounds__(GR_THREADS) void gemv_row_kernel(GemvRowArgs a)
 {
+    static_assert(MODE == MODE_B || NSEG == 1, "mode (a) holds one segment's activations");
     using F = GrFmt<FMT>;
     constexpr int SLOT = 1024 * LPU;
     extern __shared__ __align__(16) uint8_t lds[];
@@ -128,7 +139,8 @@ __global__ __launch_bounds__(GR_THREADS) void gemv_row_kernel(GemvRowArgs a)
     const int N = a.N, K = a.K;
     const int nrows = gw < N ? (N - 1 - gw) / nw + 1 : 0;  // rows gw, gw + nw, ...
     const int U = nrows * NSEG;                             // segments this wave streams
-    static_assert(RING == 2 || RING == 4, "ring of 2 or 4 segment buffers");
+    static_assert(RING == 2 || RING == 3, "ring of 2 or 3 segment buffers");
+    constexpr int AHEAD = 2;  // segments in flight
     uint8_t* ring = lds + a.ring_off + wave * (RING * SLOT);
 
     // ---- x (f32) into LDS first, so it is not queued behind the stream ----
@@ -159,13 +171,14 @@ __global__ __launch_bounds__(GR_THREADS) void gemv_row_kernel(GemvRowArgs a)
         }
     };
 #pragma unroll
-    for (int u = 0; u < RING; ++u) issue(u < U ? u : max(U - 1, 0), u);
+    for (int u = 0; u < AHEAD; ++u) issue(u < U ? u : max(U - 1, 0), u);
 
-    vm_wait<RING * LPU>();  // this wave's share of x has landed (loads retire in order)
+    vm_wait<AHEAD * LPU>();  // this wave's share of x has landed (loads retire in order)
     asm volatile("s_barrier" ::: "memory");  // ... and every other wave's
 
-    // ---- quantize x into LDS ----
-    if constexpr (FMT == FMT_Q8_0) {
+    // ---- quantize x into LDS (mode b) ----
+    if constexpr (MODE == MODE_A) {
+    } else if constexpr (FMT == FMT_Q8_0) {
         // 8 values per task, the four tasks of a 32-value block a lane quad
         for (int t = tid; t < K / 8; t += GR_THREADS) {
             const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(s_xf + 8 * t);
@@ -225,17 +238,41 @@ __global__ __launch_bounds__(GR_THREADS) void gemv_row_kernel(GemvRowArgs a)
             if (part == 0) s_xd[sb] = d;
         }
     }
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if constexpr (MODE == MODE_B) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-    // ---- this lane's activation values for each segment, held for every row ----
+    // ---- mode (a): this lane's 64 f32 activation values (and Q4_K's sub-block sums) ----
+    float XF[MODE == MODE_A ? 64 : 1];
+    float XS[2] = {0.0f, 0.0f};
+    if constexpr (MODE == MODE_A) {
+        const int unit = min(lane / F::LANES_PER_UNIT, a.nunit - 1);
+        const f32x4_t* q = reinterpret_cast<const f32x4_t*>(s_xf + F::UNIT_VALUES * unit + 64 * (lane % F::LANES_PER_UNIT));
+#pragma unroll
+        for (int cc = 0; cc < 16; ++cc) {
+            const f32x4_t v = q[cc];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) XF[4 * cc + e] = v[e];
+        }
+        if constexpr (FMT == FMT_Q4_K) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                float t = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 32; ++i) t += XF[32 * h + i];
+                XS[h] = t;
+            }
+        }
+    }
+
+    // ---- mode (b): this lane's activation values for each segment, held for every row ----
     // Q8_0: pair p = 64 sg + lane (two blocks, their scales).  Q4_K: values
     // 64c..64c+63 of super-block sb = 16 sg + lane/4, c = lane % 4, the sums of
     // its two sub-blocks and the super-block's scale.
-    int X[NSEG][16];
-    float DX[NSEG][2];
-    int XB[NSEG][2];
+    constexpr int NB = MODE == MODE_B ? NSEG : 1;
+    int X[NB][16];
+    float DX[NB][2];
+    int XB[NB][2];
 #pragma unroll
-    for (int sg = 0; sg < NSEG; ++sg) {
+    for (int sg = 0; sg < NB && MODE == MODE_B; ++sg) {
         const int unit = min(sg * F::SEG_UNITS + lane / F::LANES_PER_UNIT, a.nunit - 1);
         const int c = lane % F::LANES_PER_UNIT;
         const u32x4_t* q = reinterpret_cast<const u32x4_t*>(s_xq + F::UNIT_VALUES * unit + 64 * c);
@@ -258,16 +295,78 @@ __global__ __launch_bounds__(GR_THREADS) void gemv_row_kernel(GemvRowArgs a)
 
     // ---- the stream ----
     float yv = 0.0f;
-    int u = 0;
+    int u = 0, slot = 0;
     for (int j = 0; j < nrows; ++j) {
         float acc = 0.0f;
 #pragma unroll
         for (int sg = 0; sg < NSEG; ++sg, ++u) {
-            const int slot = u & (RING - 1);
-            vm_wait_ahead<LPU, RING - 1>(min(RING - 1, U - 1 - u));  // segment u has landed
+            vm_wait_ahead<LPU, AHEAD - 1>(min(AHEAD - 1, U - 1 - u));  // segment u has landed
+            const int nslot = slot + AHEAD >= RING ? slot + AHEAD - RING : slot + AHEAD;  // segment u + 2's buffer
+            if (RING > AHEAD && u + AHEAD < U) {
+                lgkm_wait0();  // segment u - 1's reads of that buffer are done
+                issue(u + AHEAD, nslot);
+            }
             const int units = min(F::SEG_UNITS, a.nunit - sg * F::SEG_UNITS);
             const uint8_t* sbuf = ring + slot * SLOT;
-            if constexpr (FMT == FMT_Q8_0) {
+            if constexpr (MODE == MODE_A && FMT == FMT_Q8_0) {
+                if (lane < units) {
+                    const uint32_t* wp = reinterpret_cast<const uint32_t*>(sbuf + 68 * lane);
+                    uint32_t W[17];
+#pragma unroll
+                    for (int k = 0; k < 17; ++k) W[k] = wp[k];
+                    // even block: values in bytes 2-33; odd block: values in bytes 36-67
+                    float s0a = 0.0f, s0b = 0.0f, s1a = 0.0f, s1b = 0.0f;
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        const uint32_t e = __builtin_amdgcn_alignbyte(W[k + 1], W[k], 2), o = W[9 + k];
+#pragma unroll
+                        for (int b = 0; b < 4; ++b) {
+                            const float qe = (float)(int8_t)(e >> (8 * b)), qo = (float)(int8_t)(o >> (8 * b));
+                            if (b < 2) {
+                                s0a = fmaf(qe, XF[4 * k + b], s0a);
+                                s1a = fmaf(qo, XF[32 + 4 * k + b], s1a);
+                            } else {
+                                s0b = fmaf(qe, XF[4 * k + b], s0b);
+                                s1b = fmaf(qo, XF[32 + 4 * k + b], s1b);
+                            }
+                        }
+                    }
+                    acc = fmaf(s0a + s0b, f16lo(W[0]), acc);
+                    acc = fmaf(s1a + s1b, f16hi(W[8]), acc);
+                }
+            } else if constexpr (MODE == MODE_A) {
+                if (lane < 4 * units) {
+                    const int c = lane & 3;
+                    const uint8_t* sp = sbuf + 144 * (lane >> 2);
+                    const u32x4_t H = *reinterpret_cast<const u32x4_t*>(sp);  // d | dmin, 12 scale bytes
+                    const u32x4_t Qa = *reinterpret_cast<const u32x4_t*>(sp + 16 + 32 * c);
+                    const u32x4_t Qb = *reinterpret_cast<const u32x4_t*>(sp + 32 + 32 * c);
+                    const uint32_t Q[8] = {Qa[0], Qa[1], Qa[2], Qa[3], Qb[0], Qb[1], Qb[2], Qb[3]};
+                    // sub-block 2c: low nibbles against values 0-31; 2c + 1: high nibbles against 32-63
+                    float s0a = 0.0f, s0b = 0.0f, s1a = 0.0f, s1b = 0.0f;
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        const uint32_t lo = Q[k] & 0x0f0f0f0fu, hi = (Q[k] >> 4) & 0x0f0f0f0fu;
+#pragma unroll
+                        for (int b = 0; b < 4; ++b) {
+                            const float ql = (float)((lo >> (8 * b)) & 0xffu), qh = (float)((hi >> (8 * b)) & 0xffu);
+                            if (b < 2) {
+                                s0a = fmaf(ql, XF[4 * k + b], s0a);
+                                s1a = fmaf(qh, XF[32 + 4 * k + b], s1a);
+                            } else {
+                                s0b = fmaf(ql, XF[4 * k + b], s0b);
+                                s1b = fmaf(qh, XF[32 + 4 * k + b], s1b);
+                            }
+                        }
+                    }
+                    int sc0, m0, sc1, m1;
+                    q4k_scale_min(H[1], H[2], H[3], 2 * c, sc0, m0);
+                    q4k_scale_min(H[1], H[2], H[3], 2 * c + 1, sc1, m1);
+                    const float d = f16lo(H[0]), dmin = f16hi(H[0]);
+                    acc = fmaf(-(dmin * (float)m0), XS[0], fmaf(s0a + s0b, d * (float)sc0, acc));
+                    acc = fmaf(-(dmin * (float)m1), XS[1], fmaf(s1a + s1b, d * (float)sc1, acc));
+                }
+            } else if constexpr (FMT == FMT_Q8_0) {
                 if (lane < units) {
                     const uint32_t* wp = reinterpret_cast<const uint32_t*>(sbuf + 68 * lane);
                     uint32_t W[17];
@@ -310,10 +409,11 @@ __global__ __launch_bounds__(GR_THREADS) void gemv_row_kernel(GemvRowArgs a)
                 sm += dpp_i<DPP_X2>(sm);
                 if (live && c == 0) acc = fmaf(DX[sg][0], f16lo(H[0]) * (float)si - f16hi(H[0]) * (float)sm, acc);
             }
-            if (u + RING < U) {
+            if (RING == AHEAD && u + AHEAD < U) {
                 lgkm_wait0();  // this buffer's reads are done before it is refilled
-                issue(u + RING, slot);
+                issue(u + AHEAD, nslot);
             }
+            slot = slot + 1 == RING ? 0 : slot + 1;
         }
         // the row is complete: add the lanes' sums (fixed order), park it in lane j % 64;
         // outputs leave 64 rows at a time, or after the last row
@@ -328,26 +428,35 @@ __global__ __launch_bounds__(GR_THREADS) void gemv_row_kernel(GemvRowArgs a)
 
 typedef void (*GrKernel)(GemvRowArgs);
 
-template <int FMT, int RING>
+template <int FMT, int MODE, int RING>
 static GrKernel gr_kernel_ring(int lpu, int nseg)
 {
     constexpr int L = GrFmt<FMT>::LPU_MAX;
-    if (nseg == 4) return gemv_row_kernel<FMT, L, 4, RING>;
-    if (nseg == 3) return gemv_row_kernel<FMT, L, 3, RING>;
-    if (nseg == 2) return gemv_row_kernel<FMT, L, 2, RING>;
+    if constexpr (MODE == MODE_B) {
+        if (nseg == 4) return gemv_row_kernel<FMT, MODE, L, 4, RING>;
+        if (nseg == 3) return gemv_row_kernel<FMT, MODE, L, 3, RING>;
+        if (nseg == 2) return gemv_row_kernel<FMT, MODE, L, 2, RING>;
+    }
     switch (lpu) {
-    case 1: return gemv_row_kernel<FMT, 1, 1, RING>;
-    case 2: return gemv_row_kernel<FMT, (2 < L ? 2 : L), 1, RING>;
-    case 3: return gemv_row_kernel<FMT, (3 < L ? 3 : L), 1, RING>;
-    case 4: return gemv_row_kernel<FMT, (4 < L ? 4 : L), 1, RING>;
-    default: return gemv_row_kernel<FMT, L, 1, RING>;
+    case 1: return gemv_row_kernel<FMT, MODE, 1, 1, RING>;
+    case 2: return gemv_row_kernel<FMT, MODE, (2 < L ? 2 : L), 1, RING>;
+    case 3: return gemv_row_kernel<FMT, MODE, (3 < L ? 3 : L), 1, RING>;
+    case 4: return gemv_row_kernel<FMT, MODE, (4 < L ? 4 : L), 1, RING>;
+    default: return gemv_row_kernel<FMT, MODE, L, 1, RING>;
     }
 }
 
-static GrKernel gr_kernel(int fmt, int lpu, int nseg, int ring)
+template <int FMT, int MODE>
+static GrKernel gr_kernel_mode(int lpu, int nseg, int ring)
 {
-    if (fmt == FMT_Q8_0) return gr_kernel_ring<FMT_Q8_0, 2>(lpu, nseg);
-    return ring == 4 ? gr_kernel_ring<FMT_Q4_K, 4>(lpu, nseg) : gr_kernel_ring<FMT_Q4_K, 2>(lpu, nseg);
+    return ring == 3 ? gr_kernel_ring<FMT, MODE, 3>(lpu, nseg) : gr_kernel_ring<FMT, MODE, 2>(lpu, nseg);
+}
+
+static GrKernel gr_kernel(int fmt, int mode, int lpu, int nseg, int ring)
+{
+    if (fmt == FMT_Q8_0)
+        return mode == MODE_A ? gr_kernel_mode<FMT_Q8_0, MODE_A>(lpu, nseg, ring) : gr_kernel_mode<FMT_Q8_0, MODE_B>(lpu, nseg, ring);
+    return mode == MODE_A ? gr_kernel_mode<FMT_Q4_K, MODE_A>(lpu, nseg, ring) : gr_kernel_mode<FMT_Q4_K, MODE_B>(lpu, nseg, ring);
 }
 
 // LDS layout: x as f32 (padded to whole 1 KB loads), x quantized (int8), its
@@ -368,26 +477,24 @@ static GrLayout gr_layout(int fmt, int64_t K, int ring)
     return l;
 }
 
-// Two segment buffers per wave (four, for Q4_K's 2304-byte segments, measured
-// slower: 9.1 us against 8.4 us on 14336 x 4096).
+// Three segment buffers per wave where they fit, else two.
 static int gr_ring(int fmt, int64_t K)
 {
-    (void)fmt;
-    (void)K;
-    return 2;
+    return gr_layout(fmt, K, 3).bytes <= GR_LDS_MAX ? 3 : 2;
 }
 
 bool gemv_row_supported(int fmt, int mode, int M, int64_t K, bool emit)
 {
-    if (mode != MODE_B || M != 1 || emit || (fmt != FMT_Q8_0 && fmt != FMT_Q4_K)) return false;
+    if ((mode != MODE_A && mode != MODE_B) || M != 1 || emit || (fmt != FMT_Q8_0 && fmt != FMT_Q4_K)) return false;
     const int vpu = gr_unit_values(fmt);
-    return K % vpu == 0 && K / vpu <= (int64_t)GR_NSEG_MAX * gr_seg_units(fmt) &&
+    const int nseg_max = mode == MODE_A ? 1 : GR_NSEG_MAX;  // mode (a) holds one segment's f32 activations
+    return K % vpu == 0 && K / vpu <= (int64_t)nseg_max * gr_seg_units(fmt) &&
            gr_layout(fmt, K, gr_ring(fmt, K)).bytes <= GR_LDS_MAX;
 }
 
-hipError_t launch_gemv_row(int fmt, const void* w, const float* x, int64_t N, int64_t K, float* y, hipStream_t s)
+hipError_t launch_gemv_row(int fmt, int mode, const void* w, const float* x, int64_t N, int64_t K, float* y, hipStream_t s)
 {
-    if (!gemv_row_supported(fmt, MODE_B, 1, K, false) || N <= 0 || N > 0x7fffffff) return hipErrorInvalidValue;
+    if (!gemv_row_supported(fmt, mode, 1, K, false) || N <= 0 || N > 0x7fffffff) return hipErrorInvalidValue;
     const int ring = gr_ring(fmt, K);
     const GrLayout l = gr_layout(fmt, K, ring);
     GemvRowArgs a{};
@@ -410,7 +517,7 @@ hipError_t launch_gemv_row(int fmt, const void* w, const float* x, int64_t N, in
     const int64_t cus = device_cus();
     const int64_t rpw = (N + GR_WAVES * cus - 1) / (GR_WAVES * cus);
     const int64_t grid = (N + GR_WAVES * rpw - 1) / (GR_WAVES * rpw);
-    const GrKernel k = gr_kernel(fmt, lpu, nseg, ring);
+    const GrKernel k = gr_kernel(fmt, mode, lpu, nseg, ring);
     static std::set<std::pair<int, const void*>> done;  // dynamic LDS above 64 KB, once per device
     static std::mutex mu;
     {
