@@ -443,7 +443,7 @@ def main():
     if r is not None:
         b = layer_bytes[r["fmt"]]
         out["roofline"] = {
-            "kernel": f"gemv_kernel {r['fmt']} mode {r['mode']} M={r['M']}",
+            "kernel": f"{'gemv_row_kernel' if r['M'] == 1 else 'gemv_kernel'} {r['fmt']} mode {r['mode']} M={r['M']}",
             "bound": "hbm", "achieved": r["weight_GBps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": r["frac_hbm"], "algorithmic_bytes_per_launch": b,
             "traffic": traffic_from_profile(f"gemv:{r['fmt']}:{r['mode']}:{r['M']}"),
