@@ -933,7 +933,7 @@ hipError_t launch_gemv(int fmt, int mode, const void* w, const float* x, int64_t
                        const GemvBufs& b, float* y, int32_t* sums, hipStream_t s)
 {
     const bool emit = sums != nullptr;
-    if (gemv_row_supported(fmt, mode, M, K, emit)) return launch_gemv_row(fmt, mode, w, x, N, K, y, s);
+    if (gemv_row_supported(fmt, mode, M, N, K, emit)) return launch_gemv_row(fmt, mode, w, x, N, K, y, s);
     const GemvGeom g = gemv_geom(fmt, mode, N, K, M, emit);
     if (g.grid <= 0) return hipErrorInvalidConfiguration;
     GemvArgs a{};

@@ -33,12 +33,13 @@
 //     registers; a Q4_K super-block's four lanes add their scaled integer
 //     sums exactly before the f32 step.
 //   * Each wave keeps two segments in flight (deeper measured slower, for
-//     either format).  With three segment buffers (where LDS allows) segment
-//     u + 2 is issued before segment u is summed, so the stream never waits
-//     on the arithmetic; with two it is issued after.  Every segment issues the
-//     same number of load instructions with every lane on (lanes past the
-//     segment re-read its first bytes into the buffer's tail), which keeps the
-//     explicit waits exact and the issue free of branches.
+//     either format, also when only the prologue runs deeper).  With three
+//     segment buffers (where LDS allows) segment u + 2 is issued before
+//     segment u is summed, so the stream never waits on the arithmetic; with
+//     two it is issued after.  Every segment issues the same number of load
+//     instructions with every lane on (lanes past the segment re-read its
+//     first bytes into the buffer's tail), which keeps the explicit waits
+//     exact and the issue free of branches.
 //   * The activation row is brought into LDS ahead of the stream.  Mode (b)
 //     quantizes it once per workgroup with the device functions every other
 //     activation quantizer uses, so its blocks are the same bytes; mode (a)
@@ -302,7 +303,8 @@ __global__ __launch_bounds__(GR_THREADS) void gemv_row_kernel(GemvRowArgs a)
         for (int sg = 0; sg < NSEG; ++sg, ++u) {
             vm_wait_ahead<LPU, AHEAD - 1>(min(AHEAD - 1, U - 1 - u));  // segment u has landed
             const int nslot = slot + AHEAD >= RING ? slot + AHEAD - RING : slot + AHEAD;  // segment u + 2's buffer
-            if (RING > AHEAD && u + AHEAD < U) {
+            const bool refill = u + AHEAD < U;
+            if (RING > AHEAD && refill) {
                 lgkm_wait0();  // segment u - 1's reads of that buffer are done
                 issue(u + AHEAD, nslot);
             }
@@ -409,7 +411,7 @@ __global__ __launch_bounds__(GR_THREADS) void gemv_row_kernel(GemvRowArgs a)
                 sm += dpp_i<DPP_X2>(sm);
                 if (live && c == 0) acc = fmaf(DX[sg][0], f16lo(H[0]) * (float)si - f16hi(H[0]) * (float)sm, acc);
             }
-            if (RING == AHEAD && u + AHEAD < U) {
+            if (RING == AHEAD && refill) {
                 lgkm_wait0();  // this buffer's reads are done before it is refilled
                 issue(u + AHEAD, nslot);
             }
@@ -483,18 +485,28 @@ static int gr_ring(int fmt, int64_t K)
     return gr_layout(fmt, K, 3).bytes <= GR_LDS_MAX ? 3 : 2;
 }
 
-bool gemv_row_supported(int fmt, int mode, int M, int64_t K, bool emit)
+// Rows shorter than a segment leave lanes idle while mode (a)'s per-row
+// arithmetic still costs the whole wave: with fewer than half the lanes busy
+// and more than four rows per wave, mode (a) stays on the tile kernel (the
+// 49152 x 576 lm_head: 21.6 us here against 8.5 us there; 576-row shapes run
+// faster here).
+bool gemv_row_supported(int fmt, int mode, int M, int64_t N, int64_t K, bool emit)
 {
     if ((mode != MODE_A && mode != MODE_B) || M != 1 || emit || (fmt != FMT_Q8_0 && fmt != FMT_Q4_K)) return false;
     const int vpu = gr_unit_values(fmt);
     const int nseg_max = mode == MODE_A ? 1 : GR_NSEG_MAX;  // mode (a) holds one segment's f32 activations
-    return K % vpu == 0 && K / vpu <= (int64_t)nseg_max * gr_seg_units(fmt) &&
-           gr_layout(fmt, K, gr_ring(fmt, K)).bytes <= GR_LDS_MAX;
+    if (K % vpu != 0 || K / vpu > (int64_t)nseg_max * gr_seg_units(fmt)) return false;
+    if (mode == MODE_A) {
+        const int64_t lanes = (K / vpu) * (fmt == FMT_Q8_0 ? 1 : 4);
+        const int64_t rows_per_wave = (N + GR_WAVES * (int64_t)device_cus() - 1) / (GR_WAVES * (int64_t)device_cus());
+        if (lanes < 32 && rows_per_wave > 4) return false;
+    }
+    return gr_layout(fmt, K, gr_ring(fmt, K)).bytes <= GR_LDS_MAX;
 }
 
 hipError_t launch_gemv_row(int fmt, int mode, const void* w, const float* x, int64_t N, int64_t K, float* y, hipStream_t s)
 {
-    if (!gemv_row_supported(fmt, mode, 1, K, false) || N <= 0 || N > 0x7fffffff) return hipErrorInvalidValue;
+    if (!gemv_row_supported(fmt, mode, 1, N, K, false) || N <= 0 || N > 0x7fffffff) return hipErrorInvalidValue;
     const int ring = gr_ring(fmt, K);
     const GrLayout l = gr_layout(fmt, K, ring);
     GemvRowArgs a{};

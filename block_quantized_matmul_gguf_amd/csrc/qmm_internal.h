@@ -53,7 +53,7 @@ GemvGeom gemv_geom(int fmt, int mode, int64_t N, int64_t K, int M, bool emit);
 int device_cus();  // compute units of the current device (cached per device)
 
 // Decode with one activation row, weights streamed row by row.
-bool gemv_row_supported(int fmt, int mode, int M, int64_t K, bool emit);
+bool gemv_row_supported(int fmt, int mode, int M, int64_t N, int64_t K, bool emit);
 hipError_t launch_gemv_row(int fmt, int mode, const void* w, const float* x, int64_t N, int64_t K, float* y, hipStream_t s);
 bool gemv_supported(int fmt, int64_t K);
 int gemv_max_splits(int fmt, int64_t K);
