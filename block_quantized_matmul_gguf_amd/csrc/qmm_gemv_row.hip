@@ -348,7 +348,10 @@ __global__ __launch_bounds__(GR_THREADS) void gemv_row_kernel(GemvRowArgs a)
                     float s0a = 0.0f, s0b = 0.0f, s1a = 0.0f, s1b = 0.0f;
 #pragma unroll
                     for (int k = 0; k < 8; ++k) {
-                        const uint32_t lo = Q[k] & 0x0f0f0f0fu, hi = (Q[k] >> 4) & 0x0f0f0f0fu;
+                        uint32_t lo = Q[k] & 0x0f0f0f0fu, hi = (Q[k] >> 4) & 0x0f0f0f0fu;
+                        // opaque to the combiner, so each byte converts with one v_cvt_f32_ubyteN
+                        // instead of a bit-field extract and a convert
+                        asm volatile("" : "+v"(lo), "+v"(hi));
 #pragma unroll
                         for (int b = 0; b < 4; ++b) {
                             const float ql = (float)((lo >> (8 * b)) & 0xffu), qh = (float)((hi >> (8 * b)) & 0xffu);
