@@ -149,6 +149,24 @@ ROW_SHAPES = [
 ]
 
 
+# Every row length the one-row kernel compiles for: 1 to 5 load instructions per
+# segment (Q8_0 rows of 64 to 4352 bytes, Q4_K of 144 to 2304), 1 to 4 segments
+# per row, two or three segment buffers per wave.
+ROW_K = [(qmm.Q8_0, k) for k in (64, 960, 1600, 2048, 3072, 4032, 4096, 4160, 8192, 12352, 16384)] + \
+        [(qmm.Q4_K, k) for k in (256, 1792, 2304, 2560, 4352, 8192, 12288, 16384)]
+
+
+@pytest.mark.parametrize("mode", [qmm.MODE_F32ACT, qmm.MODE_QACT], ids=["a", "b"])
+@pytest.mark.parametrize("fmt,k", ROW_K, ids=[f"{FMT_NAME[f]}-{k}" for f, k in ROW_K])
+def test_single_row_decode_row_lengths(fmt, k, mode):
+    n = 41
+    wq = oracle.quantize(fmt, synth.weights_f32(7000 + k, n, k))
+    x = synth.acts_f32(7001 + k, 1, k)
+    y = run_plan(fmt, mode, wq, n, k, x)
+    yr, a = ref(fmt, mode, wq, n, k, x)
+    assert_within(y, yr, a, f"{FMT_NAME[fmt]} {n}x{k} M=1 mode={mode}")
+
+
 @pytest.mark.parametrize("mode", [qmm.MODE_F32ACT, qmm.MODE_QACT], ids=["a", "b"])
 @pytest.mark.parametrize("fmt,n,k", ROW_SHAPES, ids=[f"{FMT_NAME[f]}-{n}x{k}" for f, n, k in ROW_SHAPES])
 def test_single_row_decode_shapes(fmt, n, k, mode):
