@@ -271,6 +271,42 @@ def small_workload(args, qmm, torch, synth, stream):
                     "TOPS_graph": round(flop / (gus * 1e-6) / 1e12, 3),
                     "launches": len(probs)}
                 del g
+                if phase == "decode":
+                    # the same step with each layer's q/k/v and gate/up as one grouped run on
+                    # one activation row (that of q, or gate), the others as before
+                    groups = []
+                    for base in range(0, len(probs) - 1, 7):  # q k v o gate up down
+                        groups += [[base, base + 1, base + 2], [base + 3], [base + 4, base + 5], [base + 6]]
+                    groups.append([len(probs) - 1])
+
+                    def grouped_pass(st):
+                        for grp in groups:
+                            if len(grp) == 1:
+                                i = grp[0]
+                                plans[(fmts[i], probs[i].n, probs[i].k)].run(w[i], x[i], y[i], st)
+                            else:
+                                qmm.run_group([plans[(fmts[i], probs[i].n, probs[i].k)] for i in grp],
+                                              [w[i] for i in grp], x[grp[0]], [y[i] for i in grp], st)
+
+                    us = timed(lambda: grouped_pass(stream), 10)
+                    ref = [t.clone() for t in y]
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g):
+                        grouped_pass(torch.cuda.current_stream())
+                    for rep in range(3):
+                        for t in y:
+                            t.zero_()
+                        torch.cuda.synchronize()
+                        g.replay()
+                        torch.cuda.synchronize()
+                        assert all(torch.equal(a, b) for a, b in zip(y, ref)), f"grouped graph replay {rep} differs"
+                    gus = timed(g.replay, 10)
+                    out["passes"][f"decode_grouped:{pname}:{md}"] = {
+                        "ms_per_pass_stream": round(us / 1000.0, 3), "ms_per_pass_graph": round(gus / 1000.0, 3),
+                        "TOPS_stream": round(flop / (us * 1e-6) / 1e12, 3),
+                        "TOPS_graph": round(flop / (gus * 1e-6) / 1e12, 3),
+                        "launches": len(groups)}
+                    del g
                 for pl in plans.values():
                     pl.close()
         out["GFLOP_per_prefill_pass"] = round(total_flop / 1e9, 2)

@@ -44,6 +44,7 @@ SIGNATURES = {
     "qmatmul_run_block_sums": (_int, [_p, _p, _p, _p, _i64, _p]),
     "qmatmul_dequantize_weights": (_int, [_int, _p, _i64, _i64, _p, _p]),
     "qmatmul_run_dequantized": (_int, [_p, _p, _p, _p, _i64, _p]),
+    "qmatmul_run_group": (_int, [ctypes.POINTER(_p), _int, ctypes.POINTER(_p), _p, ctypes.POINTER(_p), _i64, _p]),
     "qmatmul_check": (_int, [_int, _i64, _i64, _i64, _int]),
     "qmatmul_row_bytes": (_i64, [_int, _i64]),
     "qmatmul_block_sums_per_row": (_i64, [_int, _i64]),
@@ -220,6 +221,31 @@ class Plan:
 
     def __exit__(self, *exc):
         self.close()
+
+
+GROUP_MAX = 8
+
+
+def run_group(plans, ws, x, ys=None, stream=None):
+    """y[i] = x . W[i]^T for plans sharing format, K and mode (one launch per
+    four plans at M = 1 where the one-row kernel takes the rows); returns the
+    list of outputs."""
+    torch = _torch()
+    if not 1 <= len(plans) <= GROUP_MAX or len(ws) != len(plans):
+        raise ValueError(f"need 1..{GROUP_MAX} plans and as many weight tensors, got {len(plans)} and {len(ws)}")
+    m = plans[0]._args(ws[0], x)
+    for p, w in zip(plans[1:], ws[1:]):
+        p._args(w, x)
+    if ys is None:
+        ys = [torch.empty((m, p.n), dtype=torch.float32, device=x.device) for p in plans]
+    for p, y in zip(plans, ys):
+        _need(y, torch.float32, (m, p.n), "y")
+    n = len(plans)
+    harr = (_p * n)(*[p._h for p in plans])
+    warr = (_p * n)(*[_ptr(w) for w in ws])
+    yarr = (_p * n)(*[_ptr(y) for y in ys])
+    _check(lib().qmatmul_run_group(harr, n, warr, _ptr(x), yarr, m, _stream(stream)), "qmatmul_run_group")
+    return ys
 
 
 def quantize_act(act_fmt: int, x, out=None, stream=None):

@@ -246,6 +246,46 @@ extern "C" int qmatmul_run(const qmm_plan* p, const void* w, const float* x, flo
     return run_impl(p, w, x, y, nullptr, M, stream);
 }
 
+extern "C" int qmatmul_run_group(const qmm_plan* const* plans, int count, const void* const* w, const float* x,
+                                 float* const* y, int64_t M, void* stream)
+{
+    g_err[0] = 0;
+    if (!plans || !w || !y) return fail(QMM_EINVAL, "null array: plans=%p w=%p y=%p", (const void*)plans,
+                                        (const void*)w, (const void*)y);
+    if (count < 1 || count > QMM_GROUP_MAX) return fail(QMM_EINVAL, "count=%d outside [1, %d]", count, QMM_GROUP_MAX);
+    for (int i = 0; i < count; ++i) {
+        const int st = check_run(plans[i], w[i], x, y[i], M);
+        if (st != QMM_OK) return st;
+        if (plans[i]->fmt != plans[0]->fmt || plans[i]->K != plans[0]->K || plans[i]->mode != plans[0]->mode)
+            return fail(QMM_EINVAL, "the plans of a group must share format, K and mode (plan %d differs from plan 0)",
+                        i);
+    }
+    if (M == 0) return QMM_OK;
+    const qmm_plan* p0 = plans[0];
+    const hipStream_t s = (hipStream_t)stream;
+    if (M == 1 && p0->mode != QMM_MODE_DEQUANT) {
+        // one launch per gemv_row_group_max() plans, when the one-row kernel takes their rows
+        int64_t total = 0;
+        for (int i = 0; i < count; ++i) total += plans[i]->N;
+        if (gemv_row_supported(p0->fmt, p0->mode, 1, total, p0->K, false)) {
+            const int gmax = gemv_row_group_max();
+            for (int i = 0; i < count; i += gmax) {
+                const int c = count - i < gmax ? count - i : gmax;
+                int64_t Ns[QMM_GROUP_MAX];
+                for (int j = 0; j < c; ++j) Ns[j] = plans[i + j]->N;
+                const hipError_t e = launch_gemv_row_group(p0->fmt, p0->mode, c, w + i, Ns, y + i, x, p0->K, s);
+                if (e != hipSuccess) return fail(QMM_EHIP, "kernel launch: %s", hipGetErrorString(e));
+            }
+            return QMM_OK;
+        }
+    }
+    for (int i = 0; i < count; ++i) {
+        const int st = run_impl(plans[i], w[i], x, y[i], nullptr, M, stream);
+        if (st != QMM_OK) return st;
+    }
+    return QMM_OK;
+}
+
 extern "C" int qmatmul_run_block_sums(const qmm_plan* p, const void* w, const float* x, int32_t* sums, int64_t M,
                                       void* stream)
 {

@@ -83,11 +83,17 @@ constexpr int gr_unit_values(int fmt) { return fmt == FMT_Q8_0 ? 64 : 256; }
 constexpr int gr_unit_bytes(int fmt) { return fmt == FMT_Q8_0 ? 68 : 144; }
 constexpr int gr_seg_units(int fmt) { return fmt == FMT_Q8_0 ? 64 : 16; }
 
+constexpr int GR_GROUP_MAX = 4;  // problems sharing x in one launch
+
+// Problems p = 0..groups-1 share x and K; their rows are numbered end to end:
+// global row r belongs to the last p with row0[p] <= r, local row r - row0[p].
 struct GemvRowArgs {
-    const uint8_t* w;
+    const uint8_t* w[GR_GROUP_MAX];
+    float* y[GR_GROUP_MAX];
+    int row0[GR_GROUP_MAX + 1];
+    int groups;
     const float* x;
-    float* y;
-    int N, K;
+    int N, K;  // N: rows of all problems
     int row_bytes;  // units x unit bytes
     int nunit;      // units per row (Q8_0 block pairs, Q4_K super-blocks)
     int nxi;        // 1 KB load instructions that bring x into LDS
@@ -143,6 +149,14 @@ __global__ __launch_bounds__(GR_THREADS) void gemv_row_kernel(GemvRowArgs a)
     static_assert(RING == 2 || RING == 3, "ring of 2 or 3 segment buffers");
     constexpr int AHEAD = 2;  // segments in flight
     uint8_t* ring = lds + a.ring_off + wave * (RING * SLOT);
+    // problem of global row r (wave-uniform r) and its local row
+    auto locate = [&](int r, int& p) {
+        p = 0;
+#pragma unroll
+        for (int q = 1; q < GR_GROUP_MAX; ++q)
+            if (q < a.groups && r >= a.row0[q]) p = q;
+        return r - a.row0[p];
+    };
 
     // ---- x (f32) into LDS first, so it is not queued behind the stream ----
     {
@@ -161,8 +175,9 @@ __global__ __launch_bounds__(GR_THREADS) void gemv_row_kernel(GemvRowArgs a)
     // buffer's tail, so each segment is exactly LPU instructions.
     auto issue = [&](int u, int slot) {
         const int j = u / NSEG, sg = u - j * NSEG;
-        const int row = min(gw + nw * j, N - 1);
-        const uint8_t* src = a.w + (int64_t)row * a.row_bytes + sg * F::SEG_BYTES;
+        int p;
+        const int row = locate(min(gw + nw * j, N - 1), p);
+        const uint8_t* src = a.w[p] + (int64_t)row * a.row_bytes + sg * F::SEG_BYTES;
         const int bytes = min(F::SEG_BYTES, a.row_bytes - sg * F::SEG_BYTES);
         uint8_t* dst = ring + slot * SLOT;
 #pragma unroll
@@ -426,7 +441,15 @@ __global__ __launch_bounds__(GR_THREADS) void gemv_row_kernel(GemvRowArgs a)
         if (lane == (j & 63)) yv = t;
         if ((j & 63) == 63 || j == nrows - 1) {
             const int j0 = j & ~63;
-            if (lane <= (j & 63)) a.y[gw + nw * (j0 + lane)] = yv;
+            if (lane <= (j & 63)) {
+                const int r = gw + nw * (j0 + lane);  // this lane's row (differs per lane)
+                float* yp = a.y[0];
+                int r0 = 0;
+#pragma unroll
+                for (int q = 1; q < GR_GROUP_MAX; ++q)
+                    if (q < a.groups && r >= a.row0[q]) { yp = a.y[q]; r0 = a.row0[q]; }
+                yp[r - r0] = yv;
+            }
         }
     }
 }
@@ -507,15 +530,28 @@ bool gemv_row_supported(int fmt, int mode, int M, int64_t N, int64_t K, bool emi
     return gr_layout(fmt, K, gr_ring(fmt, K)).bytes <= GR_LDS_MAX;
 }
 
-hipError_t launch_gemv_row(int fmt, int mode, const void* w, const float* x, int64_t N, int64_t K, float* y, hipStream_t s)
+int gemv_row_group_max() { return GR_GROUP_MAX; }
+
+hipError_t launch_gemv_row_group(int fmt, int mode, int count, const void* const* w, const int64_t* Ns, float* const* y,
+                                 const float* x, int64_t K, hipStream_t s)
 {
-    if (!gemv_row_supported(fmt, mode, 1, N, K, false) || N <= 0 || N > 0x7fffffff) return hipErrorInvalidValue;
+    if (count < 1 || count > GR_GROUP_MAX) return hipErrorInvalidValue;
+    int64_t N = 0;
+    for (int i = 0; i < count; ++i) {
+        if (Ns[i] <= 0) return hipErrorInvalidValue;
+        N += Ns[i];
+    }
+    if (!gemv_row_supported(fmt, mode, 1, N, K, false) || N > 0x7fffffff) return hipErrorInvalidValue;
     const int ring = gr_ring(fmt, K);
     const GrLayout l = gr_layout(fmt, K, ring);
     GemvRowArgs a{};
-    a.w = (const uint8_t*)w;
+    a.groups = count;
+    for (int i = 0; i < count; ++i) {
+        a.w[i] = (const uint8_t*)w[i];
+        a.y[i] = y[i];
+        a.row0[i + 1] = a.row0[i] + (int)Ns[i];
+    }
     a.x = x;
-    a.y = y;
     a.N = (int)N;
     a.K = (int)K;
     a.nunit = (int)(K / gr_unit_values(fmt));
@@ -547,6 +583,11 @@ hipError_t launch_gemv_row(int fmt, int mode, const void* w, const float* x, int
     void* args[] = {&a};
     const hipError_t e = hipLaunchKernel((const void*)k, dim3((unsigned)grid), dim3(GR_THREADS), args, l.bytes, s);
     return e != hipSuccess ? e : hipGetLastError();
+}
+
+hipError_t launch_gemv_row(int fmt, int mode, const void* w, const float* x, int64_t N, int64_t K, float* y, hipStream_t s)
+{
+    return launch_gemv_row_group(fmt, mode, 1, &w, &N, &y, x, K, s);
 }
 
 }  // namespace qmm

@@ -55,6 +55,11 @@ int device_cus();  // compute units of the current device (cached per device)
 // Decode with one activation row, weights streamed row by row.
 bool gemv_row_supported(int fmt, int mode, int M, int64_t N, int64_t K, bool emit);
 hipError_t launch_gemv_row(int fmt, int mode, const void* w, const float* x, int64_t N, int64_t K, float* y, hipStream_t s);
+// Several problems sharing x and K (their rows end to end) in one launch; at
+// most gemv_row_group_max() of them.
+int gemv_row_group_max();
+hipError_t launch_gemv_row_group(int fmt, int mode, int count, const void* const* w, const int64_t* Ns, float* const* y,
+                                 const float* x, int64_t K, hipStream_t s);
 bool gemv_supported(int fmt, int64_t K);
 int gemv_max_splits(int fmt, int64_t K);
 

@@ -92,6 +92,25 @@ int qmatmul_create(qmm_plan** out, int format, int64_t N, int64_t K, int64_t M_m
 int qmatmul_run(const qmm_plan* plan, const void* w_blocks, const float* x, float* y,
                 int64_t M, void* stream);
 
+/*
+ * Grouped run: y[i] = x . W[i]^T for count plans that share format, K and mode
+ * and one activation matrix x (M x K), such as the q, k and v (or gate and up)
+ * projections of one layer; each product is the one qmatmul_run computes
+ * (page "同一个 GGUF，CPU 和 Metal 生成的文字不一样", section 出处).  plans,
+ * w_blocks and y are host arrays of count entries (1 <= count <=
+ * QMM_GROUP_MAX) holding each plan's device pointers, with qmatmul_run's
+ * sizes and alignment; 0 <= M <= every plan's M_max.  At M == 1, where the
+ * one-row decode kernel takes the rows, the plans' rows go to one launch per
+ * four plans (the activations are loaded and quantized once per workgroup for
+ * all of them), giving bit-for-bit the values separate one-row runs give;
+ * otherwise the plans run one after another as with qmatmul_run.  Errors: as
+ * qmatmul_run for each plan, and QMM_EINVAL for null arrays, count out of
+ * range or plans that differ in format, K or mode.
+ */
+#define QMM_GROUP_MAX 8
+int qmatmul_run_group(const qmm_plan* const* plans, int count, const void* const* w_blocks, const float* x,
+                      float* const* y, int64_t M, void* stream);
+
 /* Free a plan and its workspace (NULL is a no-op).  Synchronizes the device
  * before freeing, so pending runs of the plan finish first. */
 int qmatmul_destroy(qmm_plan* plan);

@@ -94,6 +94,11 @@ def test_run_rejects_null_plan_and_bad_m():
     assert lib.qmatmul_run_block_sums(None, None, None, None, 1, None) == qmm.EINVAL
     assert lib.qmatmul_run_dequantized(None, None, None, None, 1, None) == qmm.EINVAL
     assert lib.qmatmul_destroy(None) == qmm.OK
+    arr = (ctypes.c_void_p * 2)()  # null plans, null pointers
+    assert lib.qmatmul_run_group(None, 1, None, None, None, 1, None) == qmm.EINVAL
+    assert lib.qmatmul_run_group(arr, 0, arr, None, arr, 1, None) == qmm.EINVAL   # count out of range
+    assert lib.qmatmul_run_group(arr, qmm.GROUP_MAX + 1, arr, None, arr, 1, None) == qmm.EINVAL
+    assert lib.qmatmul_run_group(arr, 2, arr, None, arr, 1, None) == qmm.EINVAL   # null plan
 
 
 def test_quantize_entry_points_validate_on_host():

@@ -239,6 +239,50 @@ def test_runs_are_deterministic_and_reuse_the_plan(fmt, mode, m):
     assert np.array_equal(y1, y2)
 
 
+# Grouped runs: plans sharing format, K and mode and one x.  At M = 1 the
+# one-row kernel takes all of their rows in one launch (per four plans) and
+# must give what separate runs give, bit for bit; other M run the plans in turn.
+GROUPS = [
+    (qmm.Q8_0, 576, [576, 192, 192]),             # q, k, v of a SmolLM2 layer
+    (qmm.Q8_0, 576, [1536, 1536]),                # gate, up
+    (qmm.Q8_0, 4096, [300, 77, 41, 129, 64]),     # five plans: two launches
+    (qmm.Q4_K, 1536, [576, 100]),
+]
+
+
+@pytest.mark.parametrize("m", [1, 3])
+@pytest.mark.parametrize("mode", [qmm.MODE_F32ACT, qmm.MODE_QACT], ids=["a", "b"])
+@pytest.mark.parametrize("fmt,k,ns", GROUPS, ids=[f"{FMT_NAME[f]}-{k}-{len(ns)}" for f, k, ns in GROUPS])
+def test_grouped_run_equals_separate_runs(fmt, k, ns, mode, m):
+    x = synth.acts_f32(8000 + k + m, m, k)
+    wqs = [oracle.quantize(fmt, synth.weights_f32(8100 + i + n, n, k)) for i, n in enumerate(ns)]
+    plans = [qmm.Plan(fmt, n, k, 8, mode) for n in ns]
+    try:
+        xg, wg = dev(x), [dev(w) for w in wqs]
+        sep = [host(p.run(w, xg)) for p, w in zip(plans, wg)]
+        grp = [host(y) for y in qmm.run_group(plans, wg, xg)]
+    finally:
+        for p in plans:
+            p.close()
+    for i, (n, wq) in enumerate(zip(ns, wqs)):
+        assert np.array_equal(grp[i], sep[i]), f"plan {i} ({n} rows)"
+        yr, a = ref(fmt, mode, wq, n, k, x)
+        assert_within(grp[i], yr, a, f"group plan {i} {FMT_NAME[fmt]} {n}x{k} M={m} mode={mode}")
+
+
+def test_grouped_run_rejects_mixed_plans():
+    x = dev(synth.acts_f32(8200, 1, 576))
+    w = dev(oracle.quantize(oracle.Q8_0, synth.weights_f32(8201, 64, 576)))
+    y = [torch.empty((1, 64), device="cuda") for _ in range(2)]
+    with qmm.Plan(qmm.Q8_0, 64, 576, 1, qmm.MODE_QACT) as p1, qmm.Plan(qmm.Q8_0, 64, 1536, 1, qmm.MODE_QACT) as p2, \
+            qmm.Plan(qmm.Q8_0, 64, 576, 1, qmm.MODE_F32ACT) as p3:
+        for other in (p2, p3):  # another K, another mode
+            harr = (qmm._p * 2)(p1._h, other._h)
+            warr = (qmm._p * 2)(qmm._ptr(w), qmm._ptr(w))
+            yarr = (qmm._p * 2)(qmm._ptr(y[0]), qmm._ptr(y[1]))
+            assert qmm.lib().qmatmul_run_group(harr, 2, warr, qmm._ptr(x), yarr, 1, None) == qmm.EINVAL
+
+
 def test_m_zero_is_a_no_op():
     with qmm.Plan(qmm.Q8_0, 64, 576, 4, 0) as p:
         y = torch.full((0, 64), 7.0, device="cuda")
