@@ -13,9 +13,11 @@ import os
 
 import numpy as np
 
-Q8_0, Q4_K, Q8_K = 8, 12, 15
-BLOCK = {Q8_0: (32, 34), Q4_K: (256, 144), Q8_K: (256, 292)}  # (values, bytes)
-ACT_FORMAT = {Q8_0: Q8_0, Q4_K: Q8_K}
+Q4_0, Q5_0, Q8_0, Q4_K, Q6_K, Q8_K = 2, 6, 8, 12, 14, 15
+BLOCK = {Q8_0: (32, 34), Q4_K: (256, 144), Q8_K: (256, 292),
+         Q4_0: (32, 18), Q5_0: (32, 22), Q6_K: (256, 210)}  # (values, bytes)
+ACT_FORMAT = {Q8_0: Q8_0, Q4_K: Q8_K, Q4_0: Q8_0, Q5_0: Q8_0, Q6_K: Q8_K}
+WEIGHT_FORMATS = (Q8_0, Q4_K, Q4_0, Q5_0, Q6_K)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
@@ -37,7 +39,8 @@ def _load():
     lib.orc_f32_to_f16.restype = ctypes.c_uint16
     lib.orc_f16_to_f64.argtypes = [ctypes.c_uint16]
     lib.orc_f16_to_f64.restype = ctypes.c_double
-    for name in ("orc_quantize_q8_0", "orc_quantize_q8k", "orc_quantize_q4_k"):
+    for name in ("orc_quantize_q8_0", "orc_quantize_q8k", "orc_quantize_q4_k", "orc_quantize_q4_0",
+                 "orc_quantize_q5_0", "orc_quantize_q6_k"):
         getattr(lib, name).argtypes = [_p, _i64, _i64, _p]
         getattr(lib, name).restype = None
     for name in ("orc_quantize_q8_0_v", "orc_quantize_q8k_v"):
@@ -104,9 +107,11 @@ def quantize(fmt: int, x, variant: int = 0) -> np.ndarray:
         lib.orc_quantize_q8_0_v(_ptr(x), r, k, _ptr(out), variant)
     elif fmt == Q8_K:
         lib.orc_quantize_q8k_v(_ptr(x), r, k, _ptr(out), variant)
-    elif fmt == Q4_K:
+    elif fmt in (Q4_K, Q4_0, Q5_0, Q6_K):
         assert variant == 0
-        lib.orc_quantize_q4_k(_ptr(x), r, k, _ptr(out))
+        name = {Q4_K: "orc_quantize_q4_k", Q4_0: "orc_quantize_q4_0", Q5_0: "orc_quantize_q5_0",
+                Q6_K: "orc_quantize_q6_k"}[fmt]
+        getattr(lib, name)(_ptr(x), r, k, _ptr(out))
     else:
         raise ValueError(fmt)
     return out
@@ -153,8 +158,9 @@ def sums_per_row(fmt: int, k: int) -> int:
 
 
 def block_sums(fmt: int, w: np.ndarray, n: int, k: int, x) -> np.ndarray:
-    """Integer block sums, int64 (M, N, sums_per_row).  Q8_0: S per 32-block.
-    Q4_K: per super-block S_0..S_7, sumi, summins."""
+    """Integer block sums, int64 (M, N, sums_per_row).  Q8_0, Q4_0, Q5_0: S per
+    32-block (signed weight values).  Q4_K: per super-block S_0..S_7, sumi,
+    summins.  Q6_K: per super-block S_0..S_15 (per 16), sumi."""
     x = _f32(x)
     m = x.shape[0]
     w = np.ascontiguousarray(w, dtype=np.uint8)

@@ -24,11 +24,17 @@
  *   Q4_K 144 B per 256 weights: f16 d, f16 dmin, 12 B of 6-bit sub-block
  *         scales/mins, 128 B of 4-bit values; w = d*sc_j*q - dmin*m_j.
  *   Q8K  292 B per 256 activations: f32 d, int8 q[256], int16 bsums[16].
- * The byte sizes are fixed by the pages' byte counts (page "自己量化", sections
- * 和下载的 Q8_0 逐字节比 and 大小和误差).  The pages do not print the field
- * order or the Q4_K bit packing; this file uses the public GGUF layout.  The
- * Q4_K packing is therefore pinned only by hand-built blocks in the tests
- * (parity of the packing unpinned by the pages themselves).
+ *   Q4_0  18 B per 32 weights: f16 d, 16 B of 4-bit values; w = d*(q - 8).
+ *   Q5_0  22 B per 32 weights: f16 d, 4 B of fifth bits, 16 B of 4-bit values;
+ *         w = d*(q - 16).
+ *   Q6_K 210 B per 256 weights: 128 B low 4 bits, 64 B high 2 bits, int8
+ *         scales[16] (one per 16 values), f16 d; w = d*sc_j*(q - 32).
+ * The byte sizes of Q8_0, Q4_K, Q4_0 and Q5_0 are fixed by the pages' byte
+ * counts (page "自己量化", sections 和下载的 Q8_0 逐字节比 and 大小和误差);
+ * Q6_K's is not.  The pages do not print the field order or any bit packing;
+ * this file uses the public GGUF layout.  The packings are therefore pinned
+ * only by hand-built blocks in the tests (parity of the packings unpinned by
+ * the pages themselves).
  *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fopenmp -shared -fPIC.
  * No fast-math: every float operation below is one IEEE-754 binary32 or
@@ -42,8 +48,11 @@
 #include <omp.h>
 #endif
 
+#define ORC_Q4_0 2
+#define ORC_Q5_0 6
 #define ORC_Q8_0 8
 #define ORC_Q4_K 12
+#define ORC_Q6_K 14
 #define ORC_Q8_K 15
 
 #define Q8_0_QK 32
@@ -51,6 +60,9 @@
 #define QK_K 256
 #define Q4_K_BYTES 144
 #define Q8_K_BYTES 292
+#define Q4_0_BYTES 18
+#define Q5_0_BYTES 22
+#define Q6_K_BYTES 210
 
 /* ---------------------------------------------------------------- f16 ---- */
 
@@ -274,6 +286,154 @@ void orc_quantize_q4_k(const float* w, int64_t rows, int64_t K, uint8_t* out)
     }
 }
 
+/* The signed element of largest |x| among n (first index on ties); 0 if all 0. */
+static float signed_absmax(const float* v, int n)
+{
+    float amax = 0.0f, mx = 0.0f;
+    for (int j = 0; j < n; ++j) {
+        float a = fabsf(v[j]);
+        if (a > amax) { amax = a; mx = v[j]; }
+    }
+    return mx;
+}
+
+/*
+ * Q4_0 (offset 8) and Q5_0 (offset 16) weights, 32 values per block, for
+ * synthetic inputs: the page "自己量化" (section 3. 量化) names
+ * QTensor::quantize to Q4_0, and to Q5_0 for rows K-quants cannot take, but
+ * not the rule.  Rule used: the signed element of largest |x| maps to the
+ * most negative code, d = max / -offset, q = floor(x * (1/d) + offset + 1/2)
+ * capped at 2*offset - 1 (the public GGUF reference rule); d stored as f16.
+ * Element j < 16 is the low nibble of value byte j, element j + 16 its high
+ * nibble; Q5_0 keeps bit 4 of element j in bit j of a little-endian u32.
+ */
+static void quantize_q4_q5_0(const float* w, int64_t rows, int64_t K, uint8_t* out, int five)
+{
+    const int64_t nb = K / 32;
+    const int bytes = five ? Q5_0_BYTES : Q4_0_BYTES;
+    const float off = five ? 16.0f : 8.0f;
+    const int qmax = five ? 31 : 15;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const float* v = w + r * K + b * 32;
+            uint8_t* blk = out + (r * nb + b) * bytes;
+            float mx = signed_absmax(v, 32);
+            float d = mx / -off;
+            float id = d != 0.0f ? 1.0f / d : 0.0f;
+            wr16(blk, orc_f32_to_f16(d));
+            uint8_t* qs = blk + (five ? 6 : 2);
+            uint32_t qh = 0;
+            memset(qs, 0, 16);
+            for (int j = 0; j < 32; ++j) {
+                float t = v[j] * id;
+                t = t + (off + 0.5f);
+                int q = (int)t; /* t > 0 here, so truncation is floor */
+                if (q > qmax) q = qmax;
+                qs[j % 16] |= (uint8_t)((q & 15) << (j < 16 ? 0 : 4));
+                qh |= (uint32_t)((q >> 4) & 1) << j;
+            }
+            if (five) {
+                blk[2] = (uint8_t)qh;
+                blk[3] = (uint8_t)(qh >> 8);
+                blk[4] = (uint8_t)(qh >> 16);
+                blk[5] = (uint8_t)(qh >> 24);
+            }
+        }
+    }
+}
+
+void orc_quantize_q4_0(const float* w, int64_t rows, int64_t K, uint8_t* out)
+{
+    quantize_q4_q5_0(w, rows, K, out, 0);
+}
+
+void orc_quantize_q5_0(const float* w, int64_t rows, int64_t K, uint8_t* out)
+{
+    quantize_q4_q5_0(w, rows, K, out, 1);
+}
+
+/* Byte offsets of element e (0..255) of a Q6_K super-block: the low-bits
+ * byte (nibble *nib: 0 low, 1 high) and the high-bits byte (bit pair *pair). */
+static void q6k_where(int e, int* lo_byte, int* nib, int* hi_byte, int* pair)
+{
+    int half = e / 128, el = e % 128, g = el / 32, l = el % 32;
+    *lo_byte = 64 * half + 32 * (g & 1) + l;
+    *nib = g >> 1;
+    *hi_byte = 128 + 32 * half + l;
+    *pair = g;
+}
+
+/* 6-bit value (0..63) of element e of a Q6_K super-block. */
+static int q6k_value(const uint8_t* blk, int e)
+{
+    int lb, nib, hb, pair;
+    q6k_where(e, &lb, &nib, &hb, &pair);
+    int lo = nib ? (blk[lb] >> 4) : (blk[lb] & 15);
+    int hi = (blk[hb] >> (2 * pair)) & 3;
+    return lo | (hi << 4);
+}
+
+/*
+ * Q6_K weights for synthetic inputs (the pages name Q6K tensors of a
+ * downloaded file, page "自己量化", section 和下载的 Q8_0 逐字节比, but no
+ * quantizer).  Plain rule: per 16-value sub-block j the signed element of
+ * largest |x| gives s_j = max / -32; over the super-block the signed s_j of
+ * largest |s_j| gives d = s / -128; sc_j = min(127, round(s_j / d)); each
+ * value q = clamp(round(x / (d*sc_j)), -32, 31) + 32 against the stored f16 d
+ * (q = 32 where d*sc_j is 0).
+ */
+void orc_quantize_q6_k(const float* w, int64_t rows, int64_t K, uint8_t* out)
+{
+    const int64_t nb = K / QK_K;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const float* v = w + r * K + b * QK_K;
+            uint8_t* blk = out + (r * nb + b) * Q6_K_BYTES;
+            float s[16];
+            for (int j = 0; j < 16; ++j) s[j] = signed_absmax(v + 16 * j, 16) / -32.0f;
+            float smax = signed_absmax(s, 16);
+            float d = smax / -128.0f;
+            uint16_t dh = orc_f32_to_f16(d);
+            float dq = (float)orc_f16_to_f64(dh);
+            memset(blk, 0, Q6_K_BYTES);
+            int sc[16];
+            for (int j = 0; j < 16; ++j) {
+                int c = d != 0.0f ? (int)roundf(s[j] / d) : 0;
+                sc[j] = c > 127 ? 127 : c;
+                blk[192 + j] = (uint8_t)(int8_t)sc[j];
+            }
+            wr16(blk + 208, dh);
+            for (int e = 0; e < QK_K; ++e) {
+                float de = dq * (float)sc[e / 16];
+                int q = 0;
+                if (de != 0.0f) {
+                    q = (int)roundf(v[e] / de);
+                    if (q < -32) q = -32;
+                    if (q > 31) q = 31;
+                }
+                q += 32;
+                int lb, nib, hb, pair;
+                q6k_where(e, &lb, &nib, &hb, &pair);
+                blk[lb] |= (uint8_t)((q & 15) << (4 * nib));
+                blk[hb] |= (uint8_t)((q >> 4) << (2 * pair));
+            }
+        }
+    }
+}
+
+/* 5-bit value (0..31) of element j of a Q5_0 block, 4-bit of a Q4_0 block. */
+static int q5_0_value(const uint8_t* blk, int j)
+{
+    uint32_t qh = (uint32_t)blk[2] | ((uint32_t)blk[3] << 8) | ((uint32_t)blk[4] << 16) | ((uint32_t)blk[5] << 24);
+    int lo = j < 16 ? (blk[6 + j] & 15) : (blk[6 + j - 16] >> 4);
+    return lo | (int)(((qh >> j) & 1u) << 4);
+}
+
+static int q4_0_value(const uint8_t* blk, int j)
+{
+    return j < 16 ? (blk[2 + j] & 15) : (blk[2 + j - 16] >> 4);
+}
+
 /* ------------------------------------------------------------ decoders -- */
 
 static int64_t row_bytes(int fmt, int64_t K)
@@ -281,6 +441,9 @@ static int64_t row_bytes(int fmt, int64_t K)
     if (fmt == ORC_Q8_0) return (K / Q8_0_QK) * Q8_0_BYTES;
     if (fmt == ORC_Q4_K) return (K / QK_K) * Q4_K_BYTES;
     if (fmt == ORC_Q8_K) return (K / QK_K) * Q8_K_BYTES;
+    if (fmt == ORC_Q4_0) return (K / 32) * Q4_0_BYTES;
+    if (fmt == ORC_Q5_0) return (K / 32) * Q5_0_BYTES;
+    if (fmt == ORC_Q6_K) return (K / QK_K) * Q6_K_BYTES;
     return -1;
 }
 
@@ -311,6 +474,21 @@ static void dequant_row(int fmt, const uint8_t* row, int64_t K, double* out)
             const uint8_t* blk = row + b * Q8_K_BYTES;
             double d = (double)rdf32(blk);
             for (int j = 0; j < QK_K; ++j) out[b * QK_K + j] = d * (double)(int8_t)blk[4 + j];
+        }
+    } else if (fmt == ORC_Q4_0 || fmt == ORC_Q5_0) {
+        const int five = fmt == ORC_Q5_0, bytes = five ? Q5_0_BYTES : Q4_0_BYTES;
+        for (int64_t b = 0; b < K / 32; ++b) {
+            const uint8_t* blk = row + b * bytes;
+            double d = orc_f16_to_f64(rd16(blk));
+            for (int j = 0; j < 32; ++j)
+                out[b * 32 + j] = d * (double)(five ? q5_0_value(blk, j) - 16 : q4_0_value(blk, j) - 8);
+        }
+    } else if (fmt == ORC_Q6_K) {
+        for (int64_t b = 0; b < K / QK_K; ++b) {
+            const uint8_t* blk = row + b * Q6_K_BYTES;
+            double d = orc_f16_to_f64(rd16(blk + 208));
+            for (int e = 0; e < QK_K; ++e)
+                out[b * QK_K + e] = d * (double)(int8_t)blk[192 + e / 16] * (double)(q6k_value(blk, e) - 32);
         }
     }
 }
@@ -357,28 +535,65 @@ void orc_matmul_a(int fmt, const uint8_t* w, int64_t N, int64_t K,
 
 /* ------------------------------------------------------------- mode (b) -- */
 
-static int act_format(int wfmt) { return wfmt == ORC_Q8_0 ? ORC_Q8_0 : ORC_Q8_K; }
+/* Q8_0, Q4_0 and Q5_0 weights take Q8_0 activations, K-quants Q8K (page
+ * "同一个 GGUF，CPU 和 Metal 生成的文字不一样", section 出处). */
+static int act_format(int wfmt)
+{
+    return (wfmt == ORC_Q8_0 || wfmt == ORC_Q4_0 || wfmt == ORC_Q5_0) ? ORC_Q8_0 : ORC_Q8_K;
+}
 
 static void quantize_act(int wfmt, const float* x, int64_t M, int64_t K, uint8_t* xq)
 {
-    if (wfmt == ORC_Q8_0) orc_quantize_q8_0(x, M, K, xq);
+    if (act_format(wfmt) == ORC_Q8_0) orc_quantize_q8_0(x, M, K, xq);
     else orc_quantize_q8k(x, M, K, xq);
+}
+
+/* Signed integer weight value of element j of a 32-value block (Q8_0, Q4_0, Q5_0). */
+static int int_weight32(int fmt, const uint8_t* blk, int j)
+{
+    if (fmt == ORC_Q8_0) return (int8_t)blk[2 + j];
+    if (fmt == ORC_Q4_0) return q4_0_value(blk, j) - 8;
+    return q5_0_value(blk, j) - 16;
+}
+
+static int64_t weight_block_bytes(int fmt)
+{
+    return fmt == ORC_Q8_0 ? Q8_0_BYTES : fmt == ORC_Q4_0 ? Q4_0_BYTES : fmt == ORC_Q5_0 ? Q5_0_BYTES
+         : fmt == ORC_Q4_K ? Q4_K_BYTES : Q6_K_BYTES;
 }
 
 /*
  * Integer block sums of one weight row against one quantized activation row.
- * Q8_0: S[b] = sum_{j<32} qw*qx.  Q4_K: per super-block i, 10 values:
+ * Q8_0, Q4_0, Q5_0: S[b] = sum_{j<32} qw*qx with qw the signed weight value
+ * (q - 8 for Q4_0, q - 16 for Q5_0).  Q4_K: per super-block i, 10 values:
  * S_0..S_7 (per 32), sumi = sum_j sc_j*S_j, summins = sum_j m_j*(bsums[2j]+bsums[2j+1]).
+ * Q6_K: per super-block 17 values: S_0..S_15 (per 16, weights q - 32) and
+ * sumi = sum_j sc_j*S_j.
  */
 static void row_block_sums(int fmt, const uint8_t* wrow, const uint8_t* xrow, int64_t K, int64_t* out)
 {
-    if (fmt == ORC_Q8_0) {
+    if (fmt == ORC_Q8_0 || fmt == ORC_Q4_0 || fmt == ORC_Q5_0) {
+        const int64_t wb = weight_block_bytes(fmt);
         for (int64_t b = 0; b < K / Q8_0_QK; ++b) {
-            const int8_t* qw = (const int8_t*)(wrow + b * Q8_0_BYTES + 2);
+            const uint8_t* blk = wrow + b * wb;
             const int8_t* qx = (const int8_t*)(xrow + b * Q8_0_BYTES + 2);
             int64_t s = 0;
-            for (int j = 0; j < Q8_0_QK; ++j) s += (int64_t)qw[j] * qx[j];
+            for (int j = 0; j < Q8_0_QK; ++j) s += (int64_t)int_weight32(fmt, blk, j) * qx[j];
             out[b] = s;
+        }
+    } else if (fmt == ORC_Q6_K) {
+        for (int64_t i = 0; i < K / QK_K; ++i) {
+            const uint8_t* wb = wrow + i * Q6_K_BYTES;
+            const int8_t* q8 = (const int8_t*)(xrow + i * Q8_K_BYTES + 4);
+            int64_t* o = out + i * 17;
+            int64_t sumi = 0;
+            for (int j = 0; j < 16; ++j) {
+                int64_t s = 0;
+                for (int l = 0; l < 16; ++l) s += (int64_t)(q6k_value(wb, 16 * j + l) - 32) * q8[16 * j + l];
+                o[j] = s;
+                sumi += (int64_t)(int8_t)wb[192 + j] * s;
+            }
+            o[16] = sumi;
         }
     } else {
         for (int64_t i = 0; i < K / QK_K; ++i) {
@@ -406,7 +621,8 @@ static void row_block_sums(int fmt, const uint8_t* wrow, const uint8_t* xrow, in
 
 static int64_t sums_per_row(int fmt, int64_t K)
 {
-    return fmt == ORC_Q8_0 ? K / Q8_0_QK : (K / QK_K) * 10;
+    if (fmt == ORC_Q8_0 || fmt == ORC_Q4_0 || fmt == ORC_Q5_0) return K / Q8_0_QK;
+    return (K / QK_K) * (fmt == ORC_Q6_K ? 17 : 10);
 }
 
 int64_t orc_sums_per_row(int fmt, int64_t K) { return sums_per_row(fmt, K); }
@@ -427,10 +643,11 @@ void orc_block_sums(int fmt, const uint8_t* w, int64_t N, int64_t K,
 }
 
 /*
- * Mode (b): quantize each activation row (Q8_0 with Q8_0 weights, Q8K with
- * Q4_K weights), form the integer block sums, then
- *   Q8_0: y = sum_b dw_b * dx_b * S_b
+ * Mode (b): quantize each activation row (Q8_0 with Q8_0, Q4_0 and Q5_0
+ * weights, Q8K with K-quant weights), form the integer block sums, then
+ *   Q8_0, Q4_0, Q5_0: y = sum_b dw_b * dx_b * S_b
  *   Q4_K: y = sum_i dx_i * (d_i * sumi_i - dmin_i * summins_i)
+ *   Q6_K: y = sum_i dx_i * d_i * sumi_i
  * in double.  absacc = sum_k |w^_k * x~_k| with x~ the dequantized quantized
  * activation (the quantities actually multiplied).
  */
@@ -455,11 +672,18 @@ void orc_matmul_b(int fmt, const uint8_t* w, int64_t N, int64_t K,
                 const uint8_t* xrow = xq + m * xb;
                 row_block_sums(fmt, wrow, xrow, K, s);
                 double acc = 0.0;
-                if (fmt == ORC_Q8_0) {
+                if (fmt == ORC_Q8_0 || fmt == ORC_Q4_0 || fmt == ORC_Q5_0) {
+                    const int64_t wb = weight_block_bytes(fmt);
                     for (int64_t b = 0; b < K / Q8_0_QK; ++b) {
-                        double dw = orc_f16_to_f64(rd16(wrow + b * Q8_0_BYTES));
+                        double dw = orc_f16_to_f64(rd16(wrow + b * wb));
                         double dx = orc_f16_to_f64(rd16(xrow + b * Q8_0_BYTES));
                         acc += dw * dx * (double)s[b];
+                    }
+                } else if (fmt == ORC_Q6_K) {
+                    for (int64_t i = 0; i < K / QK_K; ++i) {
+                        double d = orc_f16_to_f64(rd16(wrow + i * Q6_K_BYTES + 208));
+                        double dx = (double)rdf32(xrow + i * Q8_K_BYTES);
+                        acc += dx * d * (double)s[i * 17 + 16];
                     }
                 } else {
                     for (int64_t i = 0; i < K / QK_K; ++i) {

@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import synth
-from oracle import Q4_K, Q8_0, Q8_K
+from oracle import Q4_0, Q4_K, Q5_0, Q6_K, Q8_0, Q8_K
 
 GOLD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -63,7 +63,7 @@ def test_f16_encode_is_round_to_nearest_even():
 def test_block_sizes_reproduce_the_pages_byte_counts():
     g = gold("page_byte_counts.json")
     for t in g["tensor_type_totals"]:
-        fmt = {"Q8_0": Q8_0, "Q4_K": Q4_K}[t["fmt"]]
+        fmt = {"Q8_0": Q8_0, "Q4_K": Q4_K, "Q5_0": Q5_0}[t["fmt"]]
         q = oracle.quantize(fmt, synth.weights_f32(7, t["n"], t["k"]))
         assert q.nbytes * t["tensors"] == t["bytes"], t["what"]
     f = g["whole_files"]
@@ -76,6 +76,16 @@ def test_block_sizes_reproduce_the_pages_byte_counts():
     overhead = f["f32_bytes"] - payload_f32
     assert 0 < overhead < 1 << 20
     assert f["q8_0_bytes"] - payload_q8 == overhead
+    # the Q4_0 file: every matrix Q4_0; the Q4K file: K-quants only where K is a
+    # multiple of 256 (ffn_down, K = 1536), Q5_0 for the rest
+    payload_q4_0 = (synth.SMOLLM2_LAYERS * sum(n * oracle.row_bytes(Q4_0, k) for n, k in layer)
+                    + vocab * oracle.row_bytes(Q4_0, hidden) + norms)
+    assert f["q4_0_bytes"] - payload_q4_0 == overhead
+    fallback = [(n, oracle.row_bytes(Q4_K if k % 256 == 0 else Q5_0, k)) for n, k in layer]
+    assert sum(k % 256 == 0 for _, _, k in synth.SMOLLM2_LAYER) == 1
+    payload_q4k = (synth.SMOLLM2_LAYERS * sum(n * rb for n, rb in fallback)
+                   + vocab * oracle.row_bytes(Q5_0, hidden) + norms)
+    assert f["q4k_q5_0_bytes"] - payload_q4k == overhead
 
 
 # ------------------------------------------------------------------ Q8_0 --
@@ -308,7 +318,7 @@ def test_integer_case_q4_k_both_modes_exact(dmin):
 
 # -------------------------------------------------------- mode relations --
 
-@pytest.mark.parametrize("fmt,k", [(Q8_0, 576), (Q4_K, 1536)])
+@pytest.mark.parametrize("fmt,k", [(Q8_0, 576), (Q4_K, 1536), (Q4_0, 576), (Q5_0, 576), (Q6_K, 1536)])
 def test_mode_a_is_the_matmul_of_the_dequantized_weights(fmt, k):
     n, m = 48, 5
     w = oracle.quantize(fmt, synth.weights_f32(51, n, k))
@@ -319,7 +329,7 @@ def test_mode_a_is_the_matmul_of_the_dequantized_weights(fmt, k):
     assert np.allclose(a, np.abs(x.astype(np.float64)) @ np.abs(oracle.dequantize(fmt, w, k)).T, rtol=1e-12)
 
 
-@pytest.mark.parametrize("fmt,k", [(Q8_0, 576), (Q4_K, 1536)])
+@pytest.mark.parametrize("fmt,k", [(Q8_0, 576), (Q4_K, 1536), (Q4_0, 576), (Q5_0, 576), (Q6_K, 1536)])
 def test_mode_b_is_the_matmul_of_requantized_activations(fmt, k):
     # sum_b dw*dx*S_b (and the Q4_K sumi/summins combination) equals, in exact
     # arithmetic, the plain product of the dequantized weights with the
@@ -381,3 +391,245 @@ def test_shape_check_rejects_k_not_divisible_by_block():
         oracle.quantize(Q4_K, np.zeros((2, 576), np.float32))
     with pytest.raises(ValueError):
         oracle.quantize(Q8_0, np.zeros((2, 40), np.float32))
+
+
+# ---------------------------------------------------------- Q4_0 and Q5_0 --
+
+def handbuilt_q4_q5():
+    g = gold("q4_0_q5_0_handbuilt.json")
+    qs = [i | ((15 - i) << 4) for i in range(16)]
+    b4 = np.array(le16(g["q4_0"]["d_bits"]) + qs, np.uint8)
+    b5 = np.array(le16(g["q5_0"]["d_bits"]) + g["q5_0"]["qh_bytes"] + qs, np.uint8)
+    return g, b4, b5
+
+
+def py_q4_q5_decode(blk, five):
+    """A direct reading of one Q4_0 / Q5_0 block: (values, codes)."""
+    d = f16val(int(blk[0]) | (int(blk[1]) << 8))
+    qs = blk[6:22] if five else blk[2:18]
+    qh = int.from_bytes(bytes(blk[2:6]), "little") if five else 0
+    codes = []
+    for j in range(32):
+        lo = int(qs[j]) & 15 if j < 16 else int(qs[j - 16]) >> 4
+        codes.append(lo | (((qh >> j) & 1) << 4))
+    off = 16 if five else 8
+    return np.array([d * (c - off) for c in codes]), codes
+
+
+def test_q4_0_q5_0_handbuilt_blocks_decode_to_hand_worked_values():
+    g, b4, b5 = handbuilt_q4_q5()
+    for fmt, blk, key, five in ((Q4_0, b4, "q4_0", False), (Q5_0, b5, "q5_0", True)):
+        w = oracle.dequantize(fmt, blk, 32)[0]
+        _, codes = py_q4_q5_decode(blk, five)
+        for el in g[key]["elements"]:
+            assert w[el["e"]] == el["w"], (key, el)
+            assert codes[el["e"]] == el["q"], (key, el)
+
+
+def test_q4_0_q5_0_handbuilt_quantization():
+    j = np.arange(32)
+    for case in gold("q4_0_q5_0_handbuilt.json")["quantize"]:
+        x = {"x[j] = j - 16": j - 16, "x[j] = 16 - j": 16 - j, "x[j] = 0": 0 * j}[case["x_rule"]]
+        five = case["fmt"] == "Q5_0"
+        blk = oracle.quantize(Q5_0 if five else Q4_0, x.astype(np.float32)[None, :])[0]
+        assert list(blk[0:2]) == le16(case["d_bits"]), case["why"]
+        _, codes = py_q4_q5_decode(blk, five)
+        assert codes == case["q"], case["why"]
+        if five:
+            assert list(blk[2:6]) == case["qh_bytes"], case["why"]
+
+
+@pytest.mark.parametrize("fmt", [Q4_0, Q5_0])
+def test_q4_0_q5_0_random_bytes_decode_like_a_direct_reading(fmt):
+    five = fmt == Q5_0
+    nbytes = 22 if five else 18
+    g = np.random.default_rng(33 + fmt)
+    blk = g.integers(0, 256, size=(8, nbytes), dtype=np.uint8)
+    blk[:, 1] &= 0x7B  # finite f16 d
+    got = oracle.dequantize(fmt, blk, 32 * 8).reshape(8, 32)
+    for r in range(8):
+        assert np.array_equal(got[r], py_q4_q5_decode(blk[r], five)[0])
+
+
+@pytest.mark.parametrize("fmt", [Q4_0, Q5_0])
+def test_q4_0_q5_0_quantizer_scale_rule_and_round_trip(fmt):
+    # d = (signed absmax) / -offset stored as f16; the absmax element takes
+    # code 0; unclamped values round to within half a step of the stored d
+    five = fmt == Q5_0
+    off, qmax = (16, 31) if five else (8, 15)
+    w = synth.weights_f32(81 + fmt, 16, 576)
+    blk = oracle.quantize(fmt, w).reshape(16, 18, 22 if five else 18)
+    for r in range(16):
+        for b in range(18):
+            x = w[r, 32 * b:32 * b + 32]
+            mx = x[np.argmax(np.abs(x))]
+            d_bits = int(blk[r, b, 0]) | (int(blk[r, b, 1]) << 8)
+            assert d_bits == int(np.array([np.float32(mx) / np.float32(-off)], np.float32)
+                                 .astype(np.float16).view(np.uint16)[0])
+            deq, codes = py_q4_q5_decode(blk[r, b], five)
+            codes = np.array(codes)
+            assert codes[np.argmax(np.abs(x))] == 0
+            # codes are rounded against the f32 d and decoded with the f16 d
+            d32 = float(np.float32(mx) / np.float32(-off))
+            drift = off * abs(d32 - f16val(d_bits))
+            inside = codes < qmax
+            err = np.abs(x.astype(np.float64) - deq)
+            assert np.all(err[inside] <= 0.5 * abs(d32) * (1 + 1e-6) + drift)
+            # the one-sided range: only values near +-|max| on the far side clamp
+            assert np.all(err <= abs(d32) * (1 + 1e-6) + drift)
+
+
+# ------------------------------------------------------------------ Q6_K --
+
+def handbuilt_q6k():
+    g = gold("q6_k_handbuilt.json")
+    blk = np.zeros(210, np.uint8)
+    blk[:128] = [(37 * i + 11) % 256 for i in range(128)]
+    blk[128:192] = [(53 * i + 7) % 256 for i in range(64)]
+    blk[192:208] = np.array(g["scales"], np.int8).view(np.uint8)
+    blk[208:210] = le16(g["d_bits"])
+    return g, blk
+
+
+def py_q6k_decode(blk):
+    """A direct reading of one Q6_K super-block: (values, codes, scales, d)."""
+    d = f16val(int(blk[208]) | (int(blk[209]) << 8))
+    sc = blk[192:208].view(np.int8).astype(int)
+    codes = []
+    for e in range(256):
+        n, el = divmod(e, 128)
+        g, l = divmod(el, 32)
+        lo_byte = int(blk[64 * n + 32 * (g & 1) + l])
+        lo = (lo_byte >> 4) if g >= 2 else (lo_byte & 15)
+        hi = (int(blk[128 + 32 * n + l]) >> (2 * g)) & 3
+        codes.append(lo | (hi << 4))
+    vals = np.array([d * sc[e // 16] * (codes[e] - 32) for e in range(256)])
+    return vals, codes, sc, d
+
+
+def test_q6_k_handbuilt_block_decodes_to_hand_worked_values():
+    g, blk = handbuilt_q6k()
+    w = oracle.dequantize(Q6_K, blk, 256)[0]
+    _, codes, _, _ = py_q6k_decode(blk)
+    for el in g["elements"]:
+        assert w[el["e"]] == el["w"], el
+        assert codes[el["e"]] == el["q"], el
+
+
+def test_q6_k_handbuilt_quantization():
+    case = gold("q6_k_handbuilt.json")["quantize"]
+    e = np.arange(256)
+    x = (e % 16 - 8).astype(np.float32)[None, :]
+    blk = oracle.quantize(Q6_K, x)[0]
+    assert list(blk[208:210]) == le16(case["d_bits"]), case["why"]
+    assert list(blk[192:208].view(np.int8)) == case["scales"], case["why"]
+    vals, codes, _, _ = py_q6k_decode(blk)
+    assert codes == list(4 * (e % 16)), case["why"]
+    assert np.array_equal(vals, x[0].astype(np.float64)), case["why"]
+
+
+def test_q6_k_random_bytes_decode_like_a_direct_reading():
+    g = np.random.default_rng(35)
+    blk = g.integers(0, 256, size=(4, 210), dtype=np.uint8)
+    blk[:, 209] &= 0x7B
+    got = oracle.dequantize(Q6_K, blk, 256 * 4).reshape(4, 256)
+    for r in range(4):
+        assert np.array_equal(got[r], py_q6k_decode(blk[r])[0])
+
+
+def test_q6_k_quantizer_round_trip_bound():
+    w = synth.weights_f32(37, 12, 1536)
+    blk = oracle.quantize(Q6_K, w).reshape(12, 6, 210)
+    for r in range(12):
+        for b in range(6):
+            deq, codes, sc, d = py_q6k_decode(blk[r, b])
+            x = w[r, 256 * b:256 * (b + 1)].astype(np.float64)
+            step = np.abs(np.repeat(d * sc, 16))
+            codes = np.array(codes)
+            inside = (codes > 0) & (codes < 63)
+            err = np.abs(x - deq)
+            assert np.all(err[inside] <= 0.5 * step[inside] * (1 + 1e-5))
+            assert np.all(sc <= 127) and np.all(sc >= -128)
+
+
+# -------------------------------- integer special cases, other formats --
+
+@pytest.mark.parametrize("fmt", [Q4_0, Q5_0])
+def test_integer_case_q4_0_q5_0_both_modes_exact(fmt):
+    # d = 1: w = q - offset.  Integer activations with a +-127 in every
+    # 32-block make their Q8_0 quantization lossless.
+    five = fmt == Q5_0
+    n, k, m = 24, 256, 3
+    g = np.random.default_rng(15 + fmt)
+    q = g.integers(0, 32 if five else 16, size=(n, k // 32, 32))
+    blk = np.zeros((n, k // 32, 22 if five else 18), np.uint8)
+    blk[..., 0:2] = le16(0x3C00)
+    base = 6 if five else 2
+    blk[..., base:base + 16] = (q[..., :16] & 15) | ((q[..., 16:] & 15) << 4)
+    if five:
+        qh = ((q >> 4) << np.arange(32)).sum(-1)
+        for t in range(4):
+            blk[..., 2 + t] = (qh >> (8 * t)) & 255
+    x = synth.integer_acts(16 + fmt, m, k, 32)
+    ref = x.astype(np.int64) @ (q.reshape(n, k) - (16 if five else 8)).T
+    ya, _ = oracle.matmul_a(fmt, blk, n, k, x)
+    yb, _ = oracle.matmul_b(fmt, blk, n, k, x)
+    assert np.array_equal(ya, ref) and np.array_equal(yb, ref)
+    assert np.array_equal(oracle.block_sums(fmt, blk, n, k, x).sum(-1), ref)
+
+
+def test_integer_case_q6_k_both_modes_exact():
+    # d = 1 and sc_j = 1: w = q - 32; Q8K lossless on integer activations
+    # with a +-127 in every 256-block.
+    n, k, m = 16, 512, 3
+    g = np.random.default_rng(17)
+    q = g.integers(0, 64, size=(n, k // 256, 256))
+    blk = np.zeros((n, k // 256, 210), np.uint8)
+    for e in range(256):
+        half, el = divmod(e, 128)
+        gg, l = divmod(el, 32)
+        lo = (q[..., e] & 15) << (4 if gg >= 2 else 0)
+        blk[..., 64 * half + 32 * (gg & 1) + l] |= lo.astype(np.uint8)
+        blk[..., 128 + 32 * half + l] |= ((q[..., e] >> 4) << (2 * gg)).astype(np.uint8)
+    blk[..., 192:208] = 1
+    blk[..., 208:210] = le16(0x3C00)
+    x = synth.integer_acts(18, m, k, 256)
+    ref = x.astype(np.int64) @ (q.reshape(n, k) - 32).T
+    ya, _ = oracle.matmul_a(Q6_K, blk, n, k, x)
+    yb, _ = oracle.matmul_b(Q6_K, blk, n, k, x)
+    assert np.array_equal(ya, ref) and np.array_equal(yb, ref)
+
+
+def test_q6_k_block_sums_by_brute_force():
+    n, k, m = 3, 512, 2
+    w = oracle.quantize(Q6_K, synth.weights_f32(63, n, k))
+    x = synth.acts_f32(64, m, k)
+    s = oracle.block_sums(Q6_K, w, n, k, x)
+    xq = oracle.quantize(Q8_K, x).reshape(m, k // 256, 292)
+    wb = w.reshape(n, k // 256, 210)
+    for mi in range(m):
+        for ni in range(n):
+            for i in range(k // 256):
+                _, codes, sc, _ = py_q6k_decode(wb[ni, i])
+                q8 = xq[mi, i, 4:260].view(np.int8).astype(int)
+                S = [sum((codes[16 * j + l] - 32) * q8[16 * j + l] for l in range(16)) for j in range(16)]
+                sumi = sum(int(sc[j]) * S[j] for j in range(16))
+                assert list(s[mi, ni, 17 * i:17 * i + 17]) == S + [sumi]
+
+
+def test_q4_0_q5_0_block_sums_by_brute_force():
+    n, k, m = 3, 128, 2
+    x = synth.acts_f32(66, m, k)
+    xq = oracle.quantize(Q8_0, x).reshape(m, k // 32, 34)
+    for fmt in (Q4_0, Q5_0):
+        five = fmt == Q5_0
+        w = oracle.quantize(fmt, synth.weights_f32(65, n, k))
+        s = oracle.block_sums(fmt, w, n, k, x)
+        wb = w.reshape(n, k // 32, 22 if five else 18)
+        for mi in range(m):
+            for ni in range(n):
+                for b in range(k // 32):
+                    _, codes = py_q4_q5_decode(wb[ni, b], five)
+                    q8 = xq[mi, b, 2:].view(np.int8).astype(int)
+                    off = 16 if five else 8
+                    assert s[mi, ni, b] == sum((codes[j] - off) * q8[j] for j in range(32))
