@@ -1,6 +1,6 @@
 """GGUF quantized matmul for MI355X (gfx950): thin binding over libqmatmul.so.
 
-y = x . W^T with W stored as GGUF Q8_0 or Q4_K blocks, in the two numerical
+y = x . W^T with W stored as GGUF Q8_0, Q4_K, Q4_0, Q5_0 or Q6_K blocks, in the two numerical
 forms of the page "同一个 GGUF，CPU 和 Metal 生成的文字不一样" (section 出处):
 
 * ``MODE_F32ACT`` (a): f32 activations, weight blocks dequantized in-kernel;
@@ -21,12 +21,13 @@ from __future__ import annotations
 import ctypes
 import os
 
-Q8_0, Q4_K, Q8_K = 8, 12, 15
+Q4_0, Q5_0, Q8_0, Q4_K, Q6_K, Q8_K = 2, 6, 8, 12, 14, 15
+WEIGHT_FORMATS = (Q8_0, Q4_K, Q4_0, Q5_0, Q6_K)
 MODE_F32ACT, MODE_QACT, MODE_DEQUANT = 0, 1, 2
 OK, EINVAL, EBLOCK, EUNSUPPORTED, ENOMEM, EHIP = 0, 1, 2, 3, 4, 5
-BLOCK_VALUES = {Q8_0: 32, Q4_K: 256, Q8_K: 256}
-BLOCK_BYTES = {Q8_0: 34, Q4_K: 144, Q8_K: 292}
-ACT_FORMAT = {Q8_0: Q8_0, Q4_K: Q8_K}
+BLOCK_VALUES = {Q8_0: 32, Q4_K: 256, Q8_K: 256, Q4_0: 32, Q5_0: 32, Q6_K: 256}
+BLOCK_BYTES = {Q8_0: 34, Q4_K: 144, Q8_K: 292, Q4_0: 18, Q5_0: 22, Q6_K: 210}
+ACT_FORMAT = {Q8_0: Q8_0, Q4_K: Q8_K, Q4_0: Q8_0, Q5_0: Q8_0, Q6_K: Q8_K}
 GEMV_MAX_M = 8
 
 _HERE = os.path.dirname(os.path.abspath(__file__))

@@ -6,7 +6,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqmatmul.so")
-SOURCES = ["qmm_capi.cpp", "qmm_quant.hip", "qmm_gemv.hip", "qmm_gemv_row.hip", "qmm_gemm.hip", "qmm_gemm_q.hip", "qmm_dequant.hip"]
+SOURCES = ["qmm_capi.cpp", "qmm_quant.hip", "qmm_gemv.hip", "qmm_gemv_row.hip", "qmm_gemm.hip", "qmm_gemm_q.hip", "qmm_dequant.hip", "qmm_ext.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 #include <new>
 
 #include "../../include/qmatmul.h"
@@ -22,6 +23,7 @@ struct qmm_plan {
     size_t ws_bytes;
     GemvBufs gv;
     GemmBufs gm;
+    ExtBufs ex;    // Q4_0, Q5_0, Q6_K
     float* wdeq;   // dequantize-all plans: the decoded weights [N][K]
     void* dense;   // dequantize-all plans: the f32 GEMM handle
 };
@@ -43,6 +45,9 @@ static int64_t block_values(int fmt)
     case QMM_Q8_0: return 32;
     case QMM_Q4_K: return 256;
     case QMM_Q8_K: return 256;
+    case QMM_Q4_0: return 32;
+    case QMM_Q5_0: return 32;
+    case QMM_Q6_K: return 256;
     default: return -1;
     }
 }
@@ -53,6 +58,9 @@ static int64_t block_bytes(int fmt)
     case QMM_Q8_0: return 34;
     case QMM_Q4_K: return 144;
     case QMM_Q8_K: return 292;
+    case QMM_Q4_0: return 18;
+    case QMM_Q5_0: return 22;
+    case QMM_Q6_K: return 210;
     default: return -1;
     }
 }
@@ -66,16 +74,23 @@ extern "C" int64_t qmatmul_row_bytes(int format, int64_t K)
 
 extern "C" int64_t qmatmul_block_sums_per_row(int format, int64_t K)
 {
-    if (format == QMM_Q8_0 && K > 0 && K % 32 == 0) return K / 32;
+    if ((format == QMM_Q8_0 || format == QMM_Q4_0 || format == QMM_Q5_0) && K > 0 && K % 32 == 0) return K / 32;
     if (format == QMM_Q4_K && K > 0 && K % 256 == 0) return K / 256 * 10;
+    if (format == QMM_Q6_K && K > 0 && K % 256 == 0) return K / 256 * 17;
     return -1;
+}
+
+static bool weight_format(int f)
+{
+    return f == QMM_Q8_0 || f == QMM_Q4_K || f == QMM_Q4_0 || f == QMM_Q5_0 || f == QMM_Q6_K;
 }
 
 static int check_shape(int format, int64_t N, int64_t K, int64_t M_max, int mode)
 {
-    if (format != QMM_Q8_0 && format != QMM_Q4_K)
-        return fail(QMM_EUNSUPPORTED, "unsupported weight format %d (expected %d Q8_0 or %d Q4_K)", format, QMM_Q8_0,
-                    QMM_Q4_K);
+    if (!weight_format(format))
+        return fail(QMM_EUNSUPPORTED,
+                    "unsupported weight format %d (expected %d Q4_0, %d Q5_0, %d Q8_0, %d Q4_K or %d Q6_K)", format,
+                    QMM_Q4_0, QMM_Q5_0, QMM_Q8_0, QMM_Q4_K, QMM_Q6_K);
     if (mode != QMM_MODE_F32ACT && mode != QMM_MODE_QACT && mode != QMM_MODE_DEQUANT)
         return fail(QMM_EUNSUPPORTED,
                     "unsupported mode %d (expected 0 f32 activations, 1 quantized activations or 2 dequantize-all)",
@@ -91,8 +106,8 @@ static int check_shape(int format, int64_t N, int64_t K, int64_t M_max, int mode
         return fail(QMM_EINVAL, "shape too large: N=%lld K=%lld M_max=%lld", (long long)N, (long long)K,
                     (long long)M_max);
     if (!gemv_supported(format, K))
-        return fail(QMM_EUNSUPPORTED, "K=%lld has no kernel for this format (Q8_0 needs K divisible by 64: the "
-                    "kernels read blocks in pairs)", (long long)K);
+        return fail(QMM_EUNSUPPORTED, "K=%lld has no kernel for this format (Q8_0, Q4_0 and Q5_0 need K divisible "
+                    "by 64: the kernels read blocks in pairs)", (long long)K);
     return QMM_OK;
 }
 
@@ -108,7 +123,7 @@ static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 static size_t layout(qmm_plan* p, char* base)
 {
     const int64_t K = p->K, N = p->N;
-    const int64_t units = p->fmt == QMM_Q8_0 ? K / 32 : K / 256;
+    const int64_t units = p->fmt == QMM_Q4_K ? K / 256 : K / 32;
     const bool a = p->mode == QMM_MODE_F32ACT, q4 = p->fmt == QMM_Q4_K;
     size_t off = 0;
     auto take = [&](size_t bytes) -> char* {
@@ -116,10 +131,35 @@ static size_t layout(qmm_plan* p, char* base)
         off += align256(bytes ? bytes : 16);
         return r;
     };
+    p->ex = ExtBufs{};
     if (p->mode == QMM_MODE_DEQUANT) {  // the decoded weights only
         p->wdeq = (float*)take(4 * (size_t)N * K);
         p->gv = GemvBufs{};
         p->gm = GemmBufs{};
+        return off;
+    }
+    if (is_ext_format(p->fmt)) {
+        // Q6_K: every run takes the ext kernels; Q4_0/Q5_0: decode runs do, and
+        // prefill runs take the Q8_0 kernels on transcoded weights.
+        const bool q6 = p->fmt == QMM_Q6_K, pre = !q6 && p->M_max > GEMV_MAX_M;
+        const int64_t Mx = q6 ? p->M_max : std::min<int64_t>(p->M_max, GEMV_MAX_M);
+        p->gv = GemvBufs{};
+        p->gm = GemmBufs{};
+        if (!a) {
+            p->ex.xq = (int8_t*)take((size_t)Mx * K);
+            p->ex.xd = (float*)take(4 * (size_t)Mx * (q6 ? K / 256 : K / 32));
+            p->ex.xs = (int32_t*)take(4 * (size_t)Mx * (q6 ? K / 16 : K / 32));
+        }
+        if (pre) {
+            p->ex.tw = (uint8_t*)take((size_t)N * (K / 32) * 34);
+            const int64_t M = p->M_max;
+            p->gm.a0 = (_Float16*)take(2 * M * K);
+            p->gm.a1 = (_Float16*)take(a ? 2 * M * K : 0);
+            p->gm.rs = (float*)take(a ? 4 * M : 0);
+            p->gm.xs = nullptr;
+            p->gm.sd = (float*)take(a ? 0 : 4 * M * (K / 32));
+            p->gm.sbs = nullptr;
+        }
         return off;
     }
     // decode path
@@ -222,13 +262,22 @@ static int run_impl(const qmm_plan* p, const void* w, const float* x, float* y, 
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
     if (p->mode == QMM_MODE_DEQUANT) {
-        e = launch_dequantize(p->fmt, w, p->N, p->K, p->wdeq, s);
+        e = is_ext_format(p->fmt) ? launch_ext_dequantize(p->fmt, w, p->N, p->K, p->wdeq, s)
+                                  : launch_dequantize(p->fmt, w, p->N, p->K, p->wdeq, s);
         if (e != hipSuccess) return fail(QMM_EHIP, "kernel launch: %s", hipGetErrorString(e));
         const int st = dense_gemm(p->dense, p->wdeq, x, y, M, p->N, p->K, s);
         if (st != 0) return fail(QMM_EHIP, "rocblas_sgemm: status %d", st);
         return QMM_OK;
     }
-    if (M <= GEMV_MAX_M) {
+    if (is_ext_format(p->fmt)) {
+        if (M <= GEMV_MAX_M || p->fmt == QMM_Q6_K) {
+            e = launch_ext_run(p->fmt, p->mode, w, x, p->N, p->K, M, p->ex, y, sums, s);
+        } else {
+            e = launch_ext_to_q8_0(p->fmt, w, p->N, p->K, p->ex.tw, s);
+            if (e == hipSuccess) e = launch_gemm_prep(FMT_Q8_0, p->mode, x, M, p->K, p->gm, sums != nullptr, s);
+            if (e == hipSuccess) e = launch_gemm(FMT_Q8_0, p->mode, p->ex.tw, p->N, p->K, M, p->gm, y, sums, s);
+        }
+    } else if (M <= GEMV_MAX_M) {
         e = launch_gemv(p->fmt, p->mode, w, x, p->N, p->K, (int)M, p->gv, y, sums, s);
     } else {
         e = launch_gemm_prep(p->fmt, p->mode, x, M, p->K, p->gm, sums != nullptr, s);
@@ -312,17 +361,20 @@ extern "C" int qmatmul_run_dequantized(const qmm_plan* p, const float* w, const 
 extern "C" int qmatmul_dequantize_weights(int format, const void* w, int64_t N, int64_t K, float* out, void* stream)
 {
     g_err[0] = 0;
-    if (format != QMM_Q8_0 && format != QMM_Q4_K)
-        return fail(QMM_EUNSUPPORTED, "unsupported weight format %d", format);
+    if (!weight_format(format)) return fail(QMM_EUNSUPPORTED, "unsupported weight format %d", format);
     if (N < 0 || K <= 0) return fail(QMM_EINVAL, "bad sizes N=%lld K=%lld", (long long)N, (long long)K);
     if (K % block_values(format))
         return fail(QMM_EBLOCK, "quantized tensor must have their last dim divisible by block size [%lld, %lld] %lld",
                     (long long)N, (long long)K, (long long)block_values(format));
+    if ((format == QMM_Q4_0 || format == QMM_Q5_0) && K % 64)
+        return fail(QMM_EUNSUPPORTED, "K=%lld: Q4_0 and Q5_0 rows are decoded in block pairs (K divisible by 64)",
+                    (long long)K);
     if (N == 0) return QMM_OK;
     if (!w || !out) return fail(QMM_EINVAL, "null pointer");
     if (!aligned(w, 16)) return fail(QMM_EINVAL, "w_blocks must be 16-byte aligned");
     if (!aligned(out, 16)) return fail(QMM_EINVAL, "out must be 16-byte aligned");
-    hipError_t e = launch_dequantize(format, w, N, K, out, (hipStream_t)stream);
+    hipError_t e = is_ext_format(format) ? launch_ext_dequantize(format, w, N, K, out, (hipStream_t)stream)
+                                         : launch_dequantize(format, w, N, K, out, (hipStream_t)stream);
     if (e != hipSuccess) return fail(QMM_EHIP, "kernel launch: %s", hipGetErrorString(e));
     return QMM_OK;
 }
@@ -349,8 +401,7 @@ extern "C" int qmatmul_quantize_act(int act_format, const float* x, int64_t M, i
 extern "C" int qmatmul_quantize_weights(int format, const float* w, int64_t N, int64_t K, void* out, void* stream)
 {
     g_err[0] = 0;
-    if (format != QMM_Q8_0 && format != QMM_Q4_K)
-        return fail(QMM_EUNSUPPORTED, "unsupported weight format %d", format);
+    if (!weight_format(format)) return fail(QMM_EUNSUPPORTED, "unsupported weight format %d", format);
     if (N < 0 || K <= 0) return fail(QMM_EINVAL, "bad sizes N=%lld K=%lld", (long long)N, (long long)K);
     if (K % block_values(format))
         return fail(QMM_EBLOCK, "quantized tensor must have their last dim divisible by block size [%lld, %lld] %lld",
@@ -359,7 +410,8 @@ extern "C" int qmatmul_quantize_weights(int format, const float* w, int64_t N, i
     if (!w || !out) return fail(QMM_EINVAL, "null pointer");
     if (!aligned(w, 16)) return fail(QMM_EINVAL, "w must be 16-byte aligned");
     if (!aligned(out, 16)) return fail(QMM_EINVAL, "out_blocks must be 16-byte aligned");
-    hipError_t e = launch_quantize_weights(format, w, N, K, out, (hipStream_t)stream);
+    hipError_t e = is_ext_format(format) ? launch_ext_quantize_weights(format, w, N, K, out, (hipStream_t)stream)
+                                         : launch_quantize_weights(format, w, N, K, out, (hipStream_t)stream);
     if (e != hipSuccess) return fail(QMM_EHIP, "kernel launch: %s", hipGetErrorString(e));
     return QMM_OK;
 }

@@ -1,0 +1,672 @@
+// qmm_ext.hip -- Q4_0, Q5_0 and Q6_K weights: decode (M <= 8) kernels for both
+// numerical forms, their activation preparation, the Q4_0/Q5_0 -> Q8_0
+// transcode that lets the prefill take the Q8_0 kernels, dequantize-all and
+// the weight quantizers.
+//
+// Formats (page "自己量化": Q4_0 18 B and Q5_0 22 B per 32 values by the byte
+// counts of sections 和下载的 Q8_0 逐字节比 and 大小和误差; Q6_K, which the same
+// page names among the downloaded file's tensors, 210 B per 256; field order
+// and packing are the public GGUF layout, which the pages do not print):
+//   Q4_0  f16 d, 16 B of nibbles (element j < 16 low nibble of byte j, element
+//         j + 16 its high nibble); w = d*(q - 8).
+//   Q5_0  f16 d, u32 of fifth bits (bit j for element j), 16 B of nibbles as
+//         Q4_0; w = d*(q - 16).
+//   Q6_K  ql[128], qh[64], int8 scales[16], f16 d; element e of half n = e/128,
+//         group g = (e%128)/32, l = e%32: low 4 bits in ql[64n + 32(g&1) + l]
+//         (high nibble for g >= 2), high 2 bits = bit pair g of qh[32n + l];
+//         w = d*sc[e/16]*(q - 32).
+// Mode (b) pairs Q4_0 and Q5_0 with Q8_0 activations and Q6_K with Q8K (page
+// "同一个 GGUF，CPU 和 Metal 生成的文字不一样", section 出处).
+#include <algorithm>
+
+#include "qmm_act.h"
+
+namespace qmm {
+
+template <int FMT>
+struct Ext;
+template <>
+struct Ext<FMT_Q4_0> {
+    static constexpr int BYTES = 18, OFF = 8, UNIT = 64;  // a unit is a 4-byte-aligned pair of blocks
+};
+template <>
+struct Ext<FMT_Q5_0> {
+    static constexpr int BYTES = 22, OFF = 16, UNIT = 64;
+};
+template <>
+struct Ext<FMT_Q6_K> {
+    static constexpr int BYTES = 210, OFF = 32, UNIT = 32;  // a unit is a 32-value piece of a super-block
+};
+
+// ------------------------------------------------------------- loads -------
+// Q6_K super-blocks (210 B) are only 2-byte aligned.  The loads below read
+// 4-byte-aligned dwords, each holding at least one byte of the requested
+// range, so no access leaves the pages the weight buffer occupies.
+
+// ND dwords of the bytes at p (2-byte aligned): r[t] = bytes p+4t .. p+4t+3.
+template <int ND>
+QMM_DEV void load_bytes(const uint8_t* p, uint32_t r[ND])
+{
+    const uintptr_t a = (uintptr_t)p;
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(a & ~(uintptr_t)3);
+    const uint32_t sh = (uint32_t)(a & 3);
+    uint32_t raw[ND + 1];
+#pragma unroll
+    for (int i = 0; i < ND; ++i) raw[i] = q[i];
+    raw[ND] = sh ? q[ND] : 0u;
+#pragma unroll
+    for (int t = 0; t < ND; ++t) r[t] = __builtin_amdgcn_alignbyte(raw[t + 1], raw[t], sh);
+}
+
+// The two bytes at p (2-byte aligned) as the low half of the result.
+QMM_DEV uint32_t load_u16(const uint8_t* p)
+{
+    const uintptr_t a = (uintptr_t)p;
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(a & ~(uintptr_t)3);
+    return (w >> (8 * (uint32_t)(a & 3))) & 0xffffu;
+}
+
+// Bits 0..3 of h, one per byte, moved to bit 4 of bytes 0..3.
+QMM_DEV uint32_t spread4(uint32_t h) { return ((h * 0x00204081u) & 0x01010101u) << 4; }
+
+// Codes (0..2*OFF-1), one per byte, of one 32-value block: v[t] holds
+// elements 4t..4t+3.  qs: the 16 nibble bytes; qh: Q5_0's fifth bits.
+template <int FMT>
+QMM_DEV void block_codes(const uint32_t qs[4], uint32_t qh, uint32_t v[8])
+{
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        v[t] = qs[t] & 0x0f0f0f0fu;
+        v[4 + t] = (qs[t] >> 4) & 0x0f0f0f0fu;
+    }
+    if constexpr (FMT == FMT_Q5_0) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) v[t] |= spread4((qh >> (4 * t)) & 15u);
+    }
+}
+
+// A pair of Q4_0 / Q5_0 blocks at p (4-byte aligned): codes and scales.
+template <int FMT>
+QMM_DEV void pair_codes(const uint8_t* p, uint32_t v[2][8], float d[2])
+{
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+    if constexpr (FMT == FMT_Q4_0) {
+        uint32_t r[9];
+#pragma unroll
+        for (int i = 0; i < 9; ++i) r[i] = q[i];
+        uint32_t a[4], b[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            a[t] = __builtin_amdgcn_alignbyte(r[t + 1], r[t], 2);  // bytes 2..17
+            b[t] = r[5 + t];                                       // bytes 20..35
+        }
+        d[0] = f16lo(r[0]);
+        d[1] = f16hi(r[4]);
+        block_codes<FMT>(a, 0u, v[0]);
+        block_codes<FMT>(b, 0u, v[1]);
+    } else {
+        uint32_t r[11];
+#pragma unroll
+        for (int i = 0; i < 11; ++i) r[i] = q[i];
+        uint32_t a[4], b[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            a[t] = __builtin_amdgcn_alignbyte(r[t + 2], r[t + 1], 2);  // bytes 6..21
+            b[t] = r[7 + t];                                           // bytes 28..43
+        }
+        d[0] = f16lo(r[0]);
+        d[1] = f16hi(r[5]);
+        block_codes<FMT>(a, __builtin_amdgcn_alignbyte(r[1], r[0], 2), v[0]);  // bytes 2..5
+        block_codes<FMT>(b, r[6], v[1]);                                        // bytes 24..27
+    }
+}
+
+// Piece `pc` (0..7, values 32pc..32pc+31) of the Q6_K super-block at s: codes
+// (0..63, v[t] = elements 4t..4t+3 of the piece), the two sub-block scales and d.
+QMM_DEV void q6k_piece(const uint8_t* s, int pc, uint32_t v[8], int& sc0, int& sc1, float& d)
+{
+    const int n = pc >> 2, g = pc & 3;
+    uint32_t lo[8], hi[8];
+    load_bytes<8>(s + 64 * n + 32 * (g & 1), lo);
+    load_bytes<8>(s + 128 + 32 * n, hi);
+    const int ls = 4 * (g >> 1), hs = 2 * g;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) v[t] = ((lo[t] >> ls) & 0x0f0f0f0fu) | (((hi[t] >> hs) & 0x03030303u) << 4);
+    const uint32_t scw = load_u16(s + 192 + 2 * pc);
+    sc0 = (int)(int8_t)(scw & 0xffu);
+    sc1 = (int)(int8_t)(scw >> 8);
+    d = (float)__builtin_bit_cast(_Float16, (uint16_t)load_u16(s + 208));
+}
+
+// sum over a block of (code - off) * x, the codes converted exactly.
+template <int NT>
+QMM_DEV float dot_codes_f32(const uint32_t* v, const float* x, float off)
+{
+    float s = 0.0f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) s = fmaf((float)((v[t] >> (8 * c)) & 0xffu) - off, x[4 * t + c], s);
+    }
+    return s;
+}
+
+template <int NT>
+QMM_DEV int dot_codes_i8(const uint32_t* v, const uint32_t* xq)
+{
+    int s = 0;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) s = __builtin_amdgcn_sdot4((int)v[t], (int)xq[t], s, false);
+    return s;
+}
+
+QMM_DEV void load_x(const float* p, int n, float* out)
+{
+    for (int i = 0; i < n / 4; ++i) {
+        const float4 t = reinterpret_cast<const float4*>(p)[i];
+        out[4 * i] = t.x; out[4 * i + 1] = t.y; out[4 * i + 2] = t.z; out[4 * i + 3] = t.w;
+    }
+}
+
+QMM_DEV void load_q(const int8_t* p, uint32_t out[8])
+{
+    const uint4 a = reinterpret_cast<const uint4*>(p)[0], b = reinterpret_cast<const uint4*>(p)[1];
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+}
+
+// ------------------------------------------------------- decode kernel ----
+
+struct ExtArgs {
+    const uint8_t* w;
+    int64_t row_bytes;
+    const float* x;    // mode (a): f32 [M][K]
+    const int8_t* xq;  // mode (b): quantized activations int8 [M][K]
+    const float* xd;   //   their scales [M][K/32] (Q8_0) or [M][K/256] (Q8K)
+    const int32_t* xs; //   sums of their values [M][K/32] (Q8_0) or [M][K/16] (Q8K bsums)
+    float* y;          // [M][N]
+    int32_t* sums;     // block-sums hook (mode (b)): written instead of y when not null
+    int N, K, M, m0;   // this launch: activation rows m0 + MT*blockIdx.y .. + MT - 1 of M
+    int units;         // units per row
+    int lpr_log2;      // log2 of the lanes per row
+};
+
+// One wave per 64/L rows (L = lanes per row, a power of two covering the
+// row's units up to 64); each lane walks units lane, lane + L, ...; the row
+// sums meet by butterfly inside the L lanes.  Activation rows m0..m0+MT-1.
+template <int FMT, int MODE, int MT>
+__global__ __launch_bounds__(256) void ext_gemv_kernel(ExtArgs a)
+{
+    using F = Ext<FMT>;
+    const int lane = threadIdx.x & 63;
+    const int L = 1 << a.lpr_log2;
+    const int64_t n = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 >> a.lpr_log2) + (lane >> a.lpr_log2);
+    const int sub = lane & (L - 1);
+    const bool live = n < a.N;
+    const uint8_t* row = a.w + (live ? n : 0) * a.row_bytes;
+    const int spr = FMT == FMT_Q6_K ? (a.K / 256) * 17 : a.K / 32;  // block sums per (m, n)
+    const int mb = a.m0 + (int)blockIdx.y * MT;                       // first activation row here
+
+    float acc[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
+
+#pragma unroll 1
+    for (int u = sub; live && u < a.units; u += L) {
+        if constexpr (FMT == FMT_Q6_K) {
+            const int i = u >> 3, pc = u & 7;
+            uint32_t v[8];
+            int sc0, sc1;
+            float d;
+            q6k_piece(row + (int64_t)i * F::BYTES, pc, v, sc0, sc1, d);
+            const int k0 = 32 * u;
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const int mm = mb + m;
+                if (mm >= a.M) break;
+                if constexpr (MODE == MODE_A) {
+                    float x[32];
+                    load_x(a.x + (int64_t)mm * a.K + k0, 32, x);
+                    const float s0 = dot_codes_f32<4>(v, x, 32.0f);
+                    const float s1 = dot_codes_f32<4>(v + 4, x + 16, 32.0f);
+                    acc[m] = fmaf(d, (float)sc0 * s0 + (float)sc1 * s1, acc[m]);
+                    if (MT > 1) asm volatile("" ::: "memory");  // one row's activations live at a time
+                } else {
+                    uint32_t xq[8];
+                    load_q(a.xq + (int64_t)mm * a.K + k0, xq);
+                    const int32_t* bs = a.xs + (int64_t)mm * (a.K / 16) + 2 * u;
+                    const int S0 = dot_codes_i8<4>(v, xq) - 32 * bs[0];
+                    const int S1 = dot_codes_i8<4>(v + 4, xq + 4) - 32 * bs[1];
+                    const int part = sc0 * S0 + sc1 * S1;
+                    if (a.sums) {
+                        int32_t* o = a.sums + ((int64_t)mm * a.N + n) * spr + 17 * i;
+                        o[2 * pc] = S0;
+                        o[2 * pc + 1] = S1;
+                        int t = part;  // sumi: the eight pieces of the super-block are lanes 8k..8k+7
+                        t += __shfl_xor(t, 1);
+                        t += __shfl_xor(t, 2);
+                        t += __shfl_xor(t, 4);
+                        if (pc == 0) o[16] = t;
+                    } else {
+                        const float dx = a.xd[(int64_t)mm * (a.K / 256) + i];
+                        acc[m] = fmaf(d * dx, (float)part, acc[m]);
+                    }
+                }
+            }
+        } else {
+            uint32_t v[2][8];
+            float d[2];
+            pair_codes<FMT>(row + (int64_t)u * (2 * F::BYTES), v, d);
+            const int k0 = 64 * u;
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const int mm = mb + m;
+                if (mm >= a.M) break;
+                if constexpr (MODE == MODE_A) {
+                    float x[32];
+                    load_x(a.x + (int64_t)mm * a.K + k0, 32, x);
+                    const float s0 = dot_codes_f32<8>(v[0], x, (float)F::OFF);
+                    load_x(a.x + (int64_t)mm * a.K + k0 + 32, 32, x);
+                    const float s1 = dot_codes_f32<8>(v[1], x, (float)F::OFF);
+                    acc[m] = fmaf(d[0], s0, fmaf(d[1], s1, acc[m]));
+                    if (MT > 1) asm volatile("" ::: "memory");  // one row's activations live at a time
+                } else {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int b = 2 * u + h;
+                        uint32_t xq[8];
+                        load_q(a.xq + (int64_t)mm * a.K + k0 + 32 * h, xq);
+                        const int S = dot_codes_i8<8>(v[h], xq) - F::OFF * a.xs[(int64_t)mm * (a.K / 32) + b];
+                        if (a.sums) {
+                            a.sums[((int64_t)mm * a.N + n) * spr + b] = S;
+                        } else {
+                            const float dx = a.xd[(int64_t)mm * (a.K / 32) + b];
+                            acc[m] = fmaf(d[h] * dx, (float)S, acc[m]);
+                        }
+                    }
+                }
+            }
+        }
+    }
+    if (MODE == MODE_B && a.sums) return;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        float s = acc[m];
+        for (int off = L >> 1; off > 0; off >>= 1) s += __shfl_xor(s, off);
+        if (live && sub == 0 && mb + m < a.M) a.y[(int64_t)(mb + m) * a.N + n] = s;
+    }
+}
+
+// ------------------------------------------- mode (b) activation prep ------
+
+// Q8_0 activations for Q4_0 / Q5_0 weights, one thread per 32 values: the
+// values int8 [M][K], the f16-rounded scale [M][K/32] and the sum of the
+// values [M][K/32] (which carries the weight offset).
+__global__ __launch_bounds__(256) void ext_prep_q8_0_kernel(const float* __restrict__ x, int M, int K,
+                                                            int8_t* __restrict__ xq, float* __restrict__ xd,
+                                                            int32_t* __restrict__ xs)
+{
+    const int nb = K / 32;
+    const int64_t blk = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (blk >= (int64_t)M * nb) return;
+    const int m = (int)(blk / nb), b = (int)(blk % nb);
+    float v[32];
+    load32(x + (int64_t)m * K + 32 * b, v);
+    uint16_t dbits;
+    float dval;
+    int8_t q[32];
+    q8_0_block(v, dbits, dval, q);
+    int s = 0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) s += q[j];
+    uint4* o = reinterpret_cast<uint4*>(xq + (int64_t)m * K + 32 * b);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        o[i] = make_uint4(pack4(q[16 * i], q[16 * i + 1], q[16 * i + 2], q[16 * i + 3]),
+                          pack4(q[16 * i + 4], q[16 * i + 5], q[16 * i + 6], q[16 * i + 7]),
+                          pack4(q[16 * i + 8], q[16 * i + 9], q[16 * i + 10], q[16 * i + 11]),
+                          pack4(q[16 * i + 12], q[16 * i + 13], q[16 * i + 14], q[16 * i + 15]));
+    xd[blk] = dval;
+    xs[blk] = s;
+}
+
+// Q8K activations for Q6_K weights, one wave per 256 values: int8 [M][K],
+// d [M][K/256], bsums [M][K/16].
+__global__ __launch_bounds__(256) void ext_prep_q8k_kernel(const float* __restrict__ x, int M, int K,
+                                                           int8_t* __restrict__ xq, float* __restrict__ xd,
+                                                           int32_t* __restrict__ xs)
+{
+    const int nsb = K / 256;
+    const int lane = threadIdx.x & 63;
+    const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (blk >= (int64_t)M * nsb) return;  // the whole wave leaves together
+    const int m = (int)(blk / nsb), sb = (int)(blk % nsb);
+    const float4 xv = reinterpret_cast<const float4*>(x + (int64_t)m * K + 256 * sb)[lane];
+    const float v[4] = {xv.x, xv.y, xv.z, xv.w};
+    float d;
+    int q[4], s16;
+    q8k_wave(v, lane, d, q, s16);
+    *reinterpret_cast<uint32_t*>(xq + (int64_t)m * K + 256 * sb + 4 * lane) = pack4(q[0], q[1], q[2], q[3]);
+    if (lane == 0) xd[blk] = d;
+    if ((lane & 3) == 0) xs[blk * 16 + (lane >> 2)] = s16;
+}
+
+// --------------------------------------------------- Q4_0/Q5_0 -> Q8_0 -----
+
+// One thread per block: Q8_0 block with the same d and q' = q - offset, whose
+// dequantized values d*q' equal the source's exactly (the prefill then runs
+// the Q8_0 kernels, whose block sums are the same integers).
+template <int FMT>
+__global__ __launch_bounds__(256) void ext_to_q8_0_kernel(const uint8_t* __restrict__ w, int64_t blocks,
+                                                          uint8_t* __restrict__ out)
+{
+    using F = Ext<FMT>;
+    const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (b >= blocks) return;
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(w + b * F::BYTES);
+    uint32_t qs[4], qh = 0;
+    const int qo = FMT == FMT_Q5_0 ? 3 : 1;  // u16 index of the nibbles
+#pragma unroll
+    for (int t = 0; t < 4; ++t) qs[t] = (uint32_t)src[qo + 2 * t] | ((uint32_t)src[qo + 2 * t + 1] << 16);
+    if (FMT == FMT_Q5_0) qh = (uint32_t)src[1] | ((uint32_t)src[2] << 16);
+    uint32_t v[8];
+    block_codes<FMT>(qs, qh, v);
+    uint16_t* o = reinterpret_cast<uint16_t*>(out + b * 34);
+    o[0] = src[0];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        // bytes minus the offset (no borrow: each byte is >= 0 before and the
+        // result is taken per byte)
+        uint32_t r = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) r |= (uint32_t)(uint8_t)((int)((v[t] >> (8 * c)) & 0xffu) - F::OFF) << (8 * c);
+        o[1 + 2 * t] = (uint16_t)(r & 0xffffu);
+        o[2 + 2 * t] = (uint16_t)(r >> 16);
+    }
+}
+
+// ------------------------------------------------------- dequantize -------
+
+// One thread per 32 values: f32 [N][K], each value d*(q - 8), d*(q - 16) or
+// (d*sc)*(q - 32) rounded once (d*sc is exact in f32).
+template <int FMT>
+__global__ __launch_bounds__(256) void ext_dequant_kernel(const uint8_t* __restrict__ w, int64_t N, int K,
+                                                          int64_t row_bytes, float* __restrict__ out)
+{
+    const int n32 = K / 32;
+    const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (u >= N * n32) return;
+    const int64_t n = u / n32;
+    const int p = (int)(u % n32);
+    const uint8_t* row = w + n * row_bytes;
+    float val[32];
+    if constexpr (FMT == FMT_Q6_K) {
+        uint32_t v[8];
+        int sc0, sc1;
+        float d;
+        q6k_piece(row + (int64_t)(p >> 3) * 210, p & 7, v, sc0, sc1, d);
+        const float e0 = d * (float)sc0, e1 = d * (float)sc1;
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                val[4 * t + c] = (t < 4 ? e0 : e1) * ((float)((v[t] >> (8 * c)) & 0xffu) - 32.0f);
+    } else {
+        using F = Ext<FMT>;
+        uint32_t v[2][8];
+        float d[2];
+        pair_codes<FMT>(row + (int64_t)(p >> 1) * (2 * F::BYTES), v, d);
+        const int h = p & 1;
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) val[4 * t + c] = d[h] * ((float)((v[h][t] >> (8 * c)) & 0xffu) - (float)F::OFF);
+    }
+    float4* o = reinterpret_cast<float4*>(out + n * K + 32 * p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = make_float4(val[4 * i], val[4 * i + 1], val[4 * i + 2], val[4 * i + 3]);
+}
+
+// ------------------------------------------------- weight quantizers ------
+
+// The value itself, hidden from the optimizer: keeps max * (-1/8) and its
+// f16 conversion two roundings (the compiler would otherwise fuse them into one
+// mixed-precision fma with a +0 addend, which turns the -0 scale of an
+// all-zero block into +0).
+QMM_DEV float opaque(float v)
+{
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+// Q4_0 / Q5_0, one thread per 32 values (the pages name QTensor::quantize to
+// Q4_0 and its Q5_0 fallback, page "自己量化", section 3. 量化, not the rule):
+// the signed element of largest |x| (first index on ties) takes the most
+// negative code, d = max / -offset, q = floor(x*(1/d) + offset + 1/2) capped
+// at 2*offset - 1, d stored as f16.
+template <int FMT>
+__global__ __launch_bounds__(256) void ext_quantize_q4_q5_kernel(const float* __restrict__ w, int64_t blocks,
+                                                                 uint8_t* __restrict__ out)
+{
+#pragma clang fp contract(off)
+    using F = Ext<FMT>;
+    const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (b >= blocks) return;
+    float v[32];
+    load32(w + b * 32, v);
+    float amax = 0.0f, mx = 0.0f;
+    for (int j = 0; j < 32; ++j) {
+        const float t = fabsf(v[j]);
+        if (t > amax) { amax = t; mx = v[j]; }
+    }
+    const float d = mx / -(float)F::OFF;
+    const float id = d != 0.0f ? 1.0f / d : 0.0f;
+    uint32_t qs[4] = {0u, 0u, 0u, 0u}, qh = 0u;
+    for (int j = 0; j < 32; ++j) {
+        float t = v[j] * id;
+        t = t + ((float)F::OFF + 0.5f);
+        int q = (int)t;
+        q = q > 2 * F::OFF - 1 ? 2 * F::OFF - 1 : q;
+        const int byte = j & 15;
+        qs[byte >> 2] |= (uint32_t)(q & 15) << (8 * (byte & 3) + (j < 16 ? 0 : 4));
+        qh |= (uint32_t)((q >> 4) & 1) << j;
+    }
+    uint16_t* o = reinterpret_cast<uint16_t*>(out + b * F::BYTES);
+    o[0] = f16bits(opaque(d));
+    int at = 1;
+    if (FMT == FMT_Q5_0) {
+        o[1] = (uint16_t)(qh & 0xffffu);
+        o[2] = (uint16_t)(qh >> 16);
+        at = 3;
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        o[at + 2 * t] = (uint16_t)(qs[t] & 0xffffu);
+        o[at + 2 * t + 1] = (uint16_t)(qs[t] >> 16);
+    }
+}
+
+// Q6_K, one thread per 256 values (no quantizer is described on the pages):
+// per 16 values s_j = (signed max) / -32; d = (signed s_j of largest |s_j|) /
+// -128; sc_j = min(127, round(s_j / d)); q = clamp(round(x / (d*sc_j)), -32,
+// 31) + 32 against the stored f16 d (q = 32 where d*sc_j is 0).
+__global__ __launch_bounds__(256) void ext_quantize_q6_k_kernel(const float* __restrict__ w, int64_t blocks,
+                                                                uint8_t* __restrict__ out)
+{
+#pragma clang fp contract(off)
+    const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (b >= blocks) return;
+    const float* v = w + b * 256;
+    float s[16];
+    float smx = 0.0f, sam = 0.0f;
+    for (int j = 0; j < 16; ++j) {
+        float am = 0.0f, mx = 0.0f;
+        for (int l = 0; l < 16; ++l) {
+            const float t = fabsf(v[16 * j + l]);
+            if (t > am) { am = t; mx = v[16 * j + l]; }
+        }
+        s[j] = mx / -32.0f;
+        if (fabsf(s[j]) > sam) { sam = fabsf(s[j]); smx = s[j]; }
+    }
+    const float d = smx / -128.0f;
+    const uint16_t dh = f16bits(opaque(d));
+    const float dq = (float)__builtin_bit_cast(_Float16, dh);
+    uint32_t word[53];
+    for (int i = 0; i < 53; ++i) word[i] = 0u;
+    int sc[16];
+    for (int j = 0; j < 16; ++j) {
+        const int c = d != 0.0f ? (int)roundf(s[j] / d) : 0;
+        sc[j] = c > 127 ? 127 : c;
+        word[(192 + j) >> 2] |= (uint32_t)(uint8_t)(int8_t)sc[j] << (8 * ((192 + j) & 3));
+    }
+    word[52] |= (uint32_t)dh;  // bytes 208..209
+    for (int e = 0; e < 256; ++e) {
+        const float de = dq * (float)sc[e >> 4];
+        int q = 0;
+        if (de != 0.0f) {
+            q = (int)roundf(v[e] / de);
+            q = q < -32 ? -32 : (q > 31 ? 31 : q);
+        }
+        q += 32;
+        const int half = e >> 7, el = e & 127, g = el >> 5, l = el & 31;
+        const int lb = 64 * half + 32 * (g & 1) + l, hb = 128 + 32 * half + l;
+        word[lb >> 2] |= (uint32_t)((q & 15) << (4 * (g >> 1))) << (8 * (lb & 3));
+        word[hb >> 2] |= (uint32_t)((q >> 4) << (2 * g)) << (8 * (hb & 3));
+    }
+    uint16_t* o = reinterpret_cast<uint16_t*>(out + b * 210);
+    for (int i = 0; i < 105; ++i) o[i] = (uint16_t)(word[i >> 1] >> (16 * (i & 1)));
+}
+
+// ----------------------------------------------------------- launchers ----
+
+static unsigned ext_blocks(int64_t items, int per) { return (unsigned)((items + per - 1) / per); }
+
+bool is_ext_format(int fmt) { return fmt == FMT_Q4_0 || fmt == FMT_Q5_0 || fmt == FMT_Q6_K; }
+
+int64_t ext_block_bytes(int fmt) { return fmt == FMT_Q4_0 ? 18 : fmt == FMT_Q5_0 ? 22 : 210; }
+
+template <int FMT, int MODE, int MT>
+static void launch_one(const ExtArgs& a, unsigned gx, unsigned gy, hipStream_t s)
+{
+    hipLaunchKernelGGL((ext_gemv_kernel<FMT, MODE, MT>), dim3(gx, gy), dim3(256), 0, s, a);
+}
+
+template <int FMT, int MODE>
+static void launch_mt(int mt, const ExtArgs& a, unsigned gx, unsigned gy, hipStream_t s)
+{
+    if (mt == 1) launch_one<FMT, MODE, 1>(a, gx, gy, s);
+    else if (MODE == MODE_B && mt == 2) launch_one<FMT, MODE, 2>(a, gx, gy, s);
+    else if (MODE == MODE_B && mt == 4) launch_one<FMT, MODE, 4>(a, gx, gy, s);
+    else launch_one<FMT, MODE, 8>(a, gx, gy, s);
+}
+
+// The decode kernel over activation rows m0.. in one launch per 65535 * 8 rows.
+static hipError_t ext_gemv(int fmt, int mode, ExtArgs a, hipStream_t s)
+{
+    // activation rows per launch row: mode (a) keeps the one- and eight-row
+    // instances (the two- and four-row ones hold every decoded value and
+    // activation at once and need over 200 registers)
+    const int mt = a.M == 1 ? 1 : mode == MODE_A ? 8 : a.M == 2 ? 2 : a.M <= 4 ? 4 : 8;
+    int lg = 0;
+    while ((1 << lg) < a.units && lg < 6) ++lg;
+    a.lpr_log2 = lg;
+    const int64_t rows_per_wg = 4 * (64 >> lg);
+    const unsigned gx = (unsigned)((a.N + rows_per_wg - 1) / rows_per_wg);
+    const int64_t chunk = 65535ll * mt;
+    for (int64_t m0 = 0; m0 < a.M; m0 += chunk) {
+        a.m0 = (int)m0;
+        const unsigned gy = (unsigned)std::min<int64_t>(65535, (a.M - m0 + mt - 1) / mt);
+        if (fmt == FMT_Q4_0) {
+            if (mode == MODE_A) launch_mt<FMT_Q4_0, MODE_A>(mt, a, gx, gy, s);
+            else launch_mt<FMT_Q4_0, MODE_B>(mt, a, gx, gy, s);
+        } else if (fmt == FMT_Q5_0) {
+            if (mode == MODE_A) launch_mt<FMT_Q5_0, MODE_A>(mt, a, gx, gy, s);
+            else launch_mt<FMT_Q5_0, MODE_B>(mt, a, gx, gy, s);
+        } else {
+            if (mode == MODE_A) launch_mt<FMT_Q6_K, MODE_A>(mt, a, gx, gy, s);
+            else launch_mt<FMT_Q6_K, MODE_B>(mt, a, gx, gy, s);
+        }
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_ext_prep(int fmt, const float* x, int64_t M, int64_t K, const ExtBufs& b, hipStream_t s)
+{
+    if (fmt == FMT_Q6_K)
+        hipLaunchKernelGGL(ext_prep_q8k_kernel, dim3(ext_blocks(M * (K / 256), 4)), dim3(256), 0, s, x, (int)M, (int)K,
+                           b.xq, b.xd, b.xs);
+    else
+        hipLaunchKernelGGL(ext_prep_q8_0_kernel, dim3(ext_blocks(M * (K / 32), 256)), dim3(256), 0, s, x, (int)M,
+                           (int)K, b.xq, b.xd, b.xs);
+    return hipGetLastError();
+}
+
+hipError_t launch_ext_run(int fmt, int mode, const void* w, const float* x, int64_t N, int64_t K, int64_t M,
+                          const ExtBufs& b, float* y, int32_t* sums, hipStream_t s)
+{
+    ExtArgs a{};
+    a.w = (const uint8_t*)w;
+    a.row_bytes = fmt == FMT_Q6_K ? (K / 256) * 210 : (K / 32) * ext_block_bytes(fmt);
+    a.x = x;
+    a.xq = b.xq;
+    a.xd = b.xd;
+    a.xs = b.xs;
+    a.y = y;
+    a.sums = sums;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.M = (int)M;
+    a.units = fmt == FMT_Q6_K ? (int)(K / 32) : (int)(K / 64);
+    if (mode == MODE_B) {
+        const hipError_t e = launch_ext_prep(fmt, x, M, K, b, s);
+        if (e != hipSuccess) return e;
+    }
+    return ext_gemv(fmt, mode, a, s);
+}
+
+hipError_t launch_ext_to_q8_0(int fmt, const void* w, int64_t N, int64_t K, void* out, hipStream_t s)
+{
+    const int64_t blocks = N * (K / 32);
+    if (fmt == FMT_Q4_0)
+        hipLaunchKernelGGL(ext_to_q8_0_kernel<FMT_Q4_0>, dim3(ext_blocks(blocks, 256)), dim3(256), 0, s,
+                           (const uint8_t*)w, blocks, (uint8_t*)out);
+    else
+        hipLaunchKernelGGL(ext_to_q8_0_kernel<FMT_Q5_0>, dim3(ext_blocks(blocks, 256)), dim3(256), 0, s,
+                           (const uint8_t*)w, blocks, (uint8_t*)out);
+    return hipGetLastError();
+}
+
+hipError_t launch_ext_dequantize(int fmt, const void* w, int64_t N, int64_t K, float* out, hipStream_t s)
+{
+    const unsigned grid = ext_blocks(N * (K / 32), 256);
+    const int64_t rb = fmt == FMT_Q6_K ? (K / 256) * 210 : (K / 32) * ext_block_bytes(fmt);
+    if (fmt == FMT_Q4_0)
+        hipLaunchKernelGGL(ext_dequant_kernel<FMT_Q4_0>, dim3(grid), dim3(256), 0, s, (const uint8_t*)w, N, (int)K, rb, out);
+    else if (fmt == FMT_Q5_0)
+        hipLaunchKernelGGL(ext_dequant_kernel<FMT_Q5_0>, dim3(grid), dim3(256), 0, s, (const uint8_t*)w, N, (int)K, rb, out);
+    else
+        hipLaunchKernelGGL(ext_dequant_kernel<FMT_Q6_K>, dim3(grid), dim3(256), 0, s, (const uint8_t*)w, N, (int)K, rb, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_ext_quantize_weights(int fmt, const float* w, int64_t N, int64_t K, void* out, hipStream_t s)
+{
+    if (fmt == FMT_Q6_K) {
+        const int64_t blocks = N * (K / 256);
+        hipLaunchKernelGGL(ext_quantize_q6_k_kernel, dim3(ext_blocks(blocks, 256)), dim3(256), 0, s, w, blocks,
+                           (uint8_t*)out);
+    } else {
+        const int64_t blocks = N * (K / 32);
+        if (fmt == FMT_Q4_0)
+            hipLaunchKernelGGL(ext_quantize_q4_q5_kernel<FMT_Q4_0>, dim3(ext_blocks(blocks, 256)), dim3(256), 0, s, w,
+                               blocks, (uint8_t*)out);
+        else
+            hipLaunchKernelGGL(ext_quantize_q4_q5_kernel<FMT_Q5_0>, dim3(ext_blocks(blocks, 256)), dim3(256), 0, s, w,
+                               blocks, (uint8_t*)out);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace qmm

@@ -826,7 +826,7 @@ static void allow_full_lds(GvKernel k)
 
 bool gemv_supported(int fmt, int64_t K)
 {
-    return fmt == FMT_Q4_K ? K % 256 == 0 : K % 64 == 0;
+    return (fmt == FMT_Q4_K || fmt == FMT_Q6_K) ? K % 256 == 0 : K % 64 == 0;
 }
 
 // LDS bytes of the eight waves' weight stage buffers (one each, register staging).

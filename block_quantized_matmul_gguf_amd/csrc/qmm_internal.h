@@ -6,7 +6,7 @@
 
 namespace qmm {
 
-enum { FMT_Q8_0 = 8, FMT_Q4_K = 12, FMT_Q8_K = 15 };
+enum { FMT_Q4_0 = 2, FMT_Q5_0 = 6, FMT_Q8_0 = 8, FMT_Q4_K = 12, FMT_Q6_K = 14, FMT_Q8_K = 15 };
 enum { MODE_A = 0, MODE_B = 1, MODE_DEQ = 2 };
 
 // Decode (GEMV) path: M <= 8 rows; 512-thread workgroups of eight waves,
@@ -75,6 +75,24 @@ hipError_t launch_gemm(int fmt, int mode, const void* w, int64_t N, int64_t K, i
                        float* y, int32_t* sums, hipStream_t s);
 hipError_t launch_gemm_q(int fmt, const void* w, int64_t N, int64_t K, int64_t M, const GemmBufs& b, float* y,
                          hipStream_t s);
+
+// Q4_0, Q5_0 and Q6_K weights.  Decode runs (and every Q6_K run) take the
+// ext kernels; Q4_0/Q5_0 prefill transcodes the weights to Q8_0 blocks (same
+// dequantized values, same integer block sums) and runs the Q8_0 kernels.
+struct ExtBufs {
+    int8_t* xq;   // mode (b): quantized activations int8 [M][K]
+    float* xd;    // their scales [M][K/32] or [M][K/256]
+    int32_t* xs;  // sums of their values [M][K/32] or [M][K/16]
+    uint8_t* tw;  // Q4_0/Q5_0 prefill: the weights as Q8_0 blocks [N][K/32][34]
+};
+bool is_ext_format(int fmt);
+int64_t ext_block_bytes(int fmt);
+hipError_t launch_ext_prep(int fmt, const float* x, int64_t M, int64_t K, const ExtBufs& b, hipStream_t s);
+hipError_t launch_ext_run(int fmt, int mode, const void* w, const float* x, int64_t N, int64_t K, int64_t M,
+                          const ExtBufs& b, float* y, int32_t* sums, hipStream_t s);
+hipError_t launch_ext_to_q8_0(int fmt, const void* w, int64_t N, int64_t K, void* out, hipStream_t s);
+hipError_t launch_ext_dequantize(int fmt, const void* w, int64_t N, int64_t K, float* out, hipStream_t s);
+hipError_t launch_ext_quantize_weights(int fmt, const float* w, int64_t N, int64_t K, void* out, hipStream_t s);
 
 // Dequantize-all form: GGUF blocks -> f32 [N][K], and the plain f32 GEMM
 // (rocBLAS) behind an opaque handle; dense_* return 0 on success.

@@ -28,6 +28,21 @@
  *             sub-block scales and mins, 128 B of 4-bit values.
  *   QMM_Q8_K  292 B per 256 values (activations only): f32 d, int8 q[256],
  *             int16 bsums[16].
+ * and the other formats of the pages' files (Q4_0 and Q5_0 sizes fixed by the
+ * same page's byte counts, section 大小和误差 and the Q5_0 tensor totals of
+ * 和下载的 Q8_0 逐字节比; Q6_K named there among the downloaded file's
+ * tensors; the packings are the public GGUF layout, not printed by the pages):
+ *   QMM_Q4_0   18 B per 32 values: f16 d, 16 B of 4-bit values (element j < 16
+ *             in the low nibble of byte j, element j+16 in its high nibble);
+ *             w = d*(q - 8).
+ *   QMM_Q5_0   22 B per 32 values: f16 d, u32 of fifth bits (bit j of element
+ *             j), 16 B of 4-bit values as Q4_0; w = d*(q - 16).
+ *   QMM_Q6_K  210 B per 256 values: 128 B low 4 bits, 64 B high 2 bits, int8
+ *             scales[16] (one per 16 values), f16 d; w = d*sc*(q - 32).
+ * Mode (b) pairs Q4_0 and Q5_0 with Q8_0 activations and Q6_K with Q8K (page
+ * "同一个 GGUF，CPU 和 Metal 生成的文字不一样", section 出处).  Q8_0, Q4_0 and
+ * Q5_0 need K divisible by 64 (their kernels read blocks in pairs), the
+ * K-quants K divisible by 256.
  *
  * Pointers named "device" must be device memory of the current HIP device
  * (e.g. torch tensor data pointers); `stream` is a hipStream_t (NULL = the
@@ -47,8 +62,11 @@ extern "C" {
 #endif
 
 /* formats: the GGUF (ggml) type ids */
+#define QMM_Q4_0 2
+#define QMM_Q5_0 6
 #define QMM_Q8_0 8
 #define QMM_Q4_K 12
+#define QMM_Q6_K 14
 #define QMM_Q8_K 15
 
 /* modes */
@@ -70,8 +88,10 @@ typedef struct qmm_plan qmm_plan;
  * Create a plan for one weight shape: format, N output rows, K inputs, up to
  * M_max activation rows per run, and a mode.  The mode is fixed here, as the
  * pages' QMatMul fixes its form when it is built (page "同一个 GGUF，CPU 和
- * Metal 生成的文字不一样", section 修法).  K must be a multiple of 32 (Q8_0)
- * or 256 (Q4_K), the shape check of page "自己量化", section "3. 量化".
+ * Metal 生成的文字不一样", section 修法).  K must be a multiple of the block
+ * size, 32 (Q8_0, Q4_0, Q5_0) or 256 (Q4_K, Q6_K), the shape check of page
+ * "自己量化", section "3. 量化" (QMM_EBLOCK), and of 64 for the 32-value
+ * formats (QMM_EUNSUPPORTED).
  * Allocates the plan's device workspace on the current device (hipMalloc).
  * On success *out receives the plan; on failure *out is set to NULL.
  */
@@ -84,6 +104,10 @@ int qmatmul_create(qmm_plan** out, int format, int64_t N, int64_t K, int64_t M_m
  * decode (GEMV) kernels, larger M the prefill (GEMM) kernels.  The caller owns
  * w, x and y; the plan keeps no pointer after the call.  The plan's workspace
  * is shared by its runs: do not run one plan concurrently on two streams.
+ * Q4_0 and Q5_0 runs with M > 8 first rewrite the weights as Q8_0 blocks
+ * (the same dequantized values) in the plan's workspace and take the Q8_0
+ * prefill kernels; Q6_K runs with M > 8 take the decode kernels eight
+ * activation rows at a time (correct, not tuned for throughput).
  * A run only enqueues kernels (no allocation, memset or synchronization), so
  * runs may be captured in a HIP graph once each kernel has run eagerly (its
  * launch attributes are set on first use); the exception is a
@@ -153,7 +177,12 @@ int qmatmul_quantize_act(int act_format, const float* x, int64_t M, int64_t K,
  * page "自己量化" (section "3. 量化").  Q8_0: d = max|w|/127, q = round(w/d).
  * Q4_K: per 32-value sub-block an affine min/max fit, 6-bit scales and mins
  * against the super-block maximum / 63, 4-bit values re-quantized against the
- * stored f16 scales (no importance matrix).
+ * stored f16 scales (no importance matrix).  Q4_0 / Q5_0: the signed value of
+ * largest magnitude takes the most negative code, d = max/-8 (-16), q =
+ * floor(w/d + 8.5) (+ 16.5) capped at 15 (31).  Q6_K: per 16 values s = (signed
+ * max)/-32, d = (signed s of largest magnitude)/-128, scales round(s/d) capped
+ * at 127, q = clamp(round(w/(d*sc)), -32, 31) + 32.  w and out_blocks
+ * 16-byte aligned.
  */
 int qmatmul_quantize_weights(int format, const float* w, int64_t N, int64_t K,
                              void* out_blocks, void* stream);
@@ -161,8 +190,11 @@ int qmatmul_quantize_weights(int format, const float* w, int64_t N, int64_t K,
 /*
  * Test hook (mode (b) plans only): the integer parts of the run, from the
  * same kernels.  sums: device int32 [M x N x qmatmul_block_sums_per_row(format, K)].
- * Q8_0: S[m][n][b] = sum over block b of qw*qx.  Q4_K: per super-block i ten
+ * Q8_0, Q4_0, Q5_0: S[m][n][b] = sum over block b of qw*qx with qw the signed
+ * weight value (q - 8, q - 16 for Q4_0, Q5_0).  Q4_K: per super-block i ten
  * values S_0..S_7 (per 32), sumi = sum_j sc_j*S_j, summins = sum_j m_j*(bsums[2j]+bsums[2j+1]).
+ * Q6_K: per super-block 17 values S_0..S_15 (per 16, qw = q - 32) and
+ * sumi = sum_j sc_j*S_j.
  * Same preconditions as qmatmul_run; y is not written.
  */
 int qmatmul_run_block_sums(const qmm_plan* plan, const void* w_blocks, const float* x,

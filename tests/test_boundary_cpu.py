@@ -39,6 +39,9 @@ def test_header_constants_match_binding():
     assert consts["QMM_Q8_0"] == qmm.Q8_0 == 8
     assert consts["QMM_Q4_K"] == qmm.Q4_K == 12
     assert consts["QMM_Q8_K"] == qmm.Q8_K == 15
+    assert consts["QMM_Q4_0"] == qmm.Q4_0 == 2
+    assert consts["QMM_Q5_0"] == qmm.Q5_0 == 6
+    assert consts["QMM_Q6_K"] == qmm.Q6_K == 14
     assert consts["QMM_MODE_F32ACT"] == qmm.MODE_F32ACT
     assert consts["QMM_MODE_QACT"] == qmm.MODE_QACT
     assert consts["QMM_MODE_DEQUANT"] == qmm.MODE_DEQUANT == 2
@@ -55,6 +58,13 @@ def test_row_bytes_and_block_sums_sizes():
     assert qmm.row_bytes(99, 576) == -1
     assert qmm.block_sums_per_row(qmm.Q8_0, 576) == 18
     assert qmm.block_sums_per_row(qmm.Q4_K, 1536) == 60
+    # the pages' byte counts: Q5_0 attn_k 192 x 576 is 76,032 B per tensor
+    assert 192 * qmm.row_bytes(qmm.Q5_0, 576) == 2280960 // 30
+    assert qmm.row_bytes(qmm.Q4_0, 576) == 324
+    assert qmm.row_bytes(qmm.Q6_K, 1536) == 1260
+    assert qmm.row_bytes(qmm.Q6_K, 576) == -1
+    assert qmm.block_sums_per_row(qmm.Q5_0, 576) == 18
+    assert qmm.block_sums_per_row(qmm.Q6_K, 1536) == 6 * 17
 
 
 @pytest.mark.parametrize("args,status", [
@@ -70,6 +80,12 @@ def test_row_bytes_and_block_sums_sizes():
     ((qmm.Q8_0, -5, 576, 1, 0), qmm.EINVAL),
     ((qmm.Q8_0, 576, 576, 307, 1), qmm.OK),
     ((qmm.Q4_K, 14336, 4096, 512, 0), qmm.OK),
+    ((qmm.Q5_0, 192, 576, 307, 1), qmm.OK),
+    ((qmm.Q4_0, 576, 96, 1, 0), qmm.EUNSUPPORTED),  # 32-value formats need K % 64 == 0
+    ((qmm.Q4_0, 576, 40, 1, 0), qmm.EBLOCK),
+    ((qmm.Q6_K, 576, 576, 1, 1), qmm.EBLOCK),
+    ((qmm.Q6_K, 576, 768, 512, 0), qmm.OK),
+    ((qmm.Q6_K, 576, 1536, 1, 2), qmm.OK),
 ])
 def test_check_status_codes(args, status):
     assert qmm.check(*args) == status
@@ -110,6 +126,9 @@ def test_quantize_entry_points_validate_on_host():
     assert lib.qmatmul_quantize_act(qmm.Q8_0, ctypes.c_void_p(8), 2, 64, ctypes.c_void_p(64), None) == qmm.EINVAL
     assert lib.qmatmul_quantize_weights(qmm.Q8_K, None, 1, 256, None, None) == qmm.EUNSUPPORTED
     assert lib.qmatmul_quantize_weights(qmm.Q4_K, None, 1, 576, None, None) == qmm.EBLOCK
+    assert lib.qmatmul_quantize_weights(qmm.Q6_K, None, 1, 576, None, None) == qmm.EBLOCK
+    assert lib.qmatmul_quantize_weights(qmm.Q5_0, None, 2, 64, None, None) == qmm.EINVAL
+    assert lib.qmatmul_dequantize_weights(qmm.Q4_0, None, 2, 96, None, None) == qmm.EUNSUPPORTED  # pairs
     assert lib.qmatmul_dequantize_weights(qmm.Q8_K, None, 1, 256, None, None) == qmm.EUNSUPPORTED
     assert lib.qmatmul_dequantize_weights(qmm.Q4_K, None, 1, 576, None, None) == qmm.EBLOCK
     assert lib.qmatmul_dequantize_weights(qmm.Q8_0, None, 0, 64, None, None) == qmm.OK   # N = 0
@@ -130,5 +149,10 @@ def test_workspace_sizes_are_modest():
     big = qmm.workspace_bytes(qmm.Q4_K, 14336, 4096, 512, 0)
     assert 4 * 512 * 4096 <= big < 64 << 20
     assert qmm.workspace_bytes(qmm.Q4_K, 576, 576, 1, 0) == -1
+    # Q4_0 decode plans keep only the quantized activations; prefill plans add
+    # the weights as Q8_0 blocks
+    small = qmm.workspace_bytes(qmm.Q4_0, 14336, 4096, 8, 1)
+    assert 0 < small < 1 << 20
+    assert qmm.workspace_bytes(qmm.Q4_0, 14336, 4096, 512, 1) >= 14336 * 128 * 34
     # dequantize-all plans hold the decoded f32 weights
     assert qmm.workspace_bytes(qmm.Q8_0, 576, 576, 1, 2) == 4 * 576 * 576

@@ -1,0 +1,200 @@
+"""GPU parity of the Q4_0, Q5_0 and Q6_K weight formats: the HIP kernels,
+called through the C ABI, against the CPU oracle on the same seeded inputs.
+
+The formats are the other types of the pages' files (page "自己量化": the Q4_0
+file, the Q5_0 fallback for rows K-quants cannot take, the downloaded file's
+Q6K tensors); mode (b) pairs Q4_0 and Q5_0 with Q8_0 activations and Q6_K with
+Q8K (page "同一个 GGUF，CPU 和 Metal 生成的文字不一样", section 出处).
+
+Bars as for Q8_0 and Q4_K: quantized weights, decoded weights and integer
+block sums bit-exact; outputs within |y - y_ref| <= 1e-5 * sum_k |w_k x_k|,
+and y == 0 exactly where that sum is 0.  M <= 8 takes the decode kernels;
+Q4_0/Q5_0 at M > 8 take the Q8_0 prefill kernels on weights rewritten as
+Q8_0 blocks; Q6_K at M > 8 takes the decode kernels eight rows at a time.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import block_quantized_matmul_gguf_amd as qmm  # noqa: E402
+
+from test_gpu_parity import assert_within, dev, host  # noqa: E402
+
+NAME = {qmm.Q4_0: "Q4_0", qmm.Q5_0: "Q5_0", qmm.Q6_K: "Q6_K"}
+BYTES = {qmm.Q4_0: 18, qmm.Q5_0: 22, qmm.Q6_K: 210}
+MODES = [qmm.MODE_F32ACT, qmm.MODE_QACT]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    qmm.lib()
+
+
+def random_blocks(fmt, n, k, seed):
+    """Every byte random except a finite f16 scale: every code and bit pattern."""
+    g = np.random.default_rng(seed)
+    nb = k // (256 if fmt == qmm.Q6_K else 32)
+    blk = g.integers(0, 256, size=(n, nb, BYTES[fmt]), dtype=np.uint8)
+    dpos = 209 if fmt == qmm.Q6_K else 1          # high byte of d
+    blk[..., dpos] &= 0x1F                         # |d| below 2^-8: keeps sums modest
+    return blk.reshape(n, -1)
+
+
+def run(fmt, mode, wq, n, k, x, m_max=None):
+    with qmm.Plan(fmt, n, k, m_max or max(x.shape[0], 1), mode) as p:
+        return host(p.run(dev(wq), dev(x)))
+
+
+def ref(fmt, mode, wq, n, k, x):
+    return (oracle.matmul_a if mode == qmm.MODE_F32ACT else oracle.matmul_b)(fmt, wq, n, k, x)
+
+
+# ------------------------------------------------------ weight codecs ----
+
+@pytest.mark.parametrize("fmt,n,k", [(qmm.Q4_0, 96, 576), (qmm.Q5_0, 200, 576), (qmm.Q5_0, 33, 4096),
+                                     (qmm.Q6_K, 64, 1536), (qmm.Q6_K, 7, 768)])
+def test_quantize_weights_bit_exact(fmt, n, k):
+    w = synth.weights_f32(7000 + n + k, n, k)
+    w[0, :32] = 0.0                                # an all-zero block
+    w[1, :32] = np.arange(32) - 16.0               # exact ties at x/d + offset + 1/2
+    w[2, 40] = -w[2, 32:64].__abs__().max()        # sign of the block maximum
+    got = host(qmm.quantize_weights(fmt, dev(w)))
+    assert np.array_equal(got, oracle.quantize(fmt, w)), NAME[fmt]
+
+
+@pytest.mark.parametrize("fmt,n,k", [(qmm.Q4_0, 70, 576), (qmm.Q5_0, 70, 4160), (qmm.Q6_K, 33, 768),
+                                     (qmm.Q6_K, 20, 4096)])
+def test_dequantized_weights_bit_exact_on_random_bytes(fmt, n, k):
+    # Q6_K K = 768: three super-blocks per row, so every other row starts at
+    # an address that is 2 mod 4
+    wq = random_blocks(fmt, n, k, 7100 + k)
+    got = host(qmm.dequantize_weights(fmt, dev(wq), n, k))
+    want = oracle.dequantize(fmt, wq, k).astype(np.float32)  # exact value, rounded once
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), NAME[fmt]
+
+
+# ----------------------------------------------------- matmul parity ----
+
+SHAPES = [
+    (qmm.Q4_0, 576, 576),
+    (qmm.Q4_0, 200, 576),     # ragged N
+    (qmm.Q4_0, 130, 4096),
+    (qmm.Q5_0, 192, 576),     # attn_k
+    (qmm.Q5_0, 1536, 576),    # ffn_gate
+    (qmm.Q5_0, 100, 4160),    # 65 block pairs: a second pass over the lanes
+    (qmm.Q6_K, 576, 1536),    # ffn_down
+    (qmm.Q6_K, 70, 256),      # one super-block per row
+    (qmm.Q6_K, 45, 768),      # odd super-block count: misaligned rows
+    (qmm.Q6_K, 33, 4352),     # 17 super-blocks, 136 pieces: three passes
+]
+
+
+@pytest.mark.parametrize("mode", MODES, ids=["a", "b"])
+@pytest.mark.parametrize("fmt,n,k", SHAPES, ids=[f"{NAME[f]}-{n}x{k}" for f, n, k in SHAPES])
+@pytest.mark.parametrize("m", [1, 2, 3, 5, 8, 9, 37])
+def test_matmul_parity(fmt, n, k, mode, m):
+    wq = oracle.quantize(fmt, synth.weights_f32(7200 + n + k, n, k))
+    x = synth.acts_f32(7300 + m, m, k)
+    y = run(fmt, mode, wq, n, k, x)
+    yr, a = ref(fmt, mode, wq, n, k, x)
+    assert_within(y, yr, a, f"{NAME[fmt]} {n}x{k} M={m} mode={mode}")
+
+
+@pytest.mark.parametrize("mode", MODES, ids=["a", "b"])
+@pytest.mark.parametrize("fmt,k", [(qmm.Q4_0, 1536), (qmm.Q5_0, 576), (qmm.Q6_K, 768)])
+@pytest.mark.parametrize("m", [1, 4, 12])
+def test_matmul_parity_on_random_bytes(fmt, k, mode, m):
+    n = 50
+    wq = random_blocks(fmt, n, k, 7400 + k + m)
+    x = synth.acts_f32(7500 + m, m, k)
+    y = run(fmt, mode, wq, n, k, x)
+    yr, a = ref(fmt, mode, wq, n, k, x)
+    assert_within(y, yr, a, f"{NAME[fmt]} random bytes M={m} mode={mode}")
+
+
+@pytest.mark.parametrize("fmt,n,k", [(qmm.Q4_0, 40, 256), (qmm.Q5_0, 40, 256), (qmm.Q6_K, 24, 512)])
+@pytest.mark.parametrize("mode", MODES, ids=["a", "b"])
+@pytest.mark.parametrize("m", [1, 3, 10])
+def test_integer_special_case_is_exact(fmt, n, k, mode, m):
+    # d = 1 (and Q6_K scales 1): weights are q - offset; integer activations
+    # with a +-127 in every block quantize losslessly, and every partial sum is
+    # an integer below 2^24: both modes must equal the integer matmul exactly
+    g = np.random.default_rng(7600 + fmt + m)
+    if fmt == qmm.Q6_K:
+        blk = random_blocks(fmt, n, k, 7601).reshape(n, k // 256, 210)
+        blk[..., 192:208] = 1
+        blk[..., 208:210] = [0x00, 0x3C]
+        wq = blk.reshape(n, -1)
+        x = synth.integer_acts(7602 + m, m, k, 256)
+    else:
+        blk = random_blocks(fmt, n, k, 7603).reshape(n, k // 32, BYTES[fmt])
+        blk[..., 0:2] = [0x00, 0x3C]
+        wq = blk.reshape(n, -1)
+        x = synth.integer_acts(7604 + m, m, k, 32)
+    want = x.astype(np.int64) @ np.rint(oracle.dequantize(fmt, wq, k)).astype(np.int64).T
+    y = run(fmt, mode, wq, n, k, x)
+    assert np.array_equal(y, want.astype(np.float32)), (NAME[fmt], mode, m)
+    assert g is not None
+
+
+@pytest.mark.parametrize("fmt,n,k", [(qmm.Q4_0, 70, 576), (qmm.Q5_0, 33, 1536), (qmm.Q6_K, 45, 768)])
+@pytest.mark.parametrize("m", [1, 3, 8, 11])
+def test_block_sums_bit_exact(fmt, n, k, m):
+    wq = oracle.quantize(fmt, synth.weights_f32(7700 + n, n, k))
+    x = synth.acts_f32(7701 + m, m, k)
+    want = oracle.block_sums(fmt, wq, n, k, x)
+    with qmm.Plan(fmt, n, k, m, qmm.MODE_QACT) as p:
+        got = host(p.block_sums(dev(wq), dev(x))).astype(np.int64)
+    assert np.array_equal(got.reshape(want.shape), want), (NAME[fmt], m)
+
+
+@pytest.mark.parametrize("fmt,n,k", [(qmm.Q4_0, 200, 576), (qmm.Q6_K, 45, 768)])
+@pytest.mark.parametrize("m", [1, 5, 37])
+def test_dequant_form_parity(fmt, n, k, m):
+    wq = oracle.quantize(fmt, synth.weights_f32(7800 + n, n, k))
+    x = synth.acts_f32(7801 + m, m, k)
+    y = run(fmt, qmm.MODE_DEQUANT, wq, n, k, x)
+    yr, a = oracle.matmul_a(fmt, wq, n, k, x)
+    assert_within(y, yr, a, f"{NAME[fmt]} dequantize-all M={m}")
+
+
+@pytest.mark.parametrize("fmt", [qmm.Q4_0, qmm.Q5_0, qmm.Q6_K], ids=["Q4_0", "Q5_0", "Q6_K"])
+@pytest.mark.parametrize("mode", MODES, ids=["a", "b"])
+def test_runs_are_deterministic_and_m_below_plan_maximum(fmt, mode):
+    n, k = 96, 1536
+    wq = dev(oracle.quantize(fmt, synth.weights_f32(7900, n, k)))
+    x = synth.acts_f32(7901, 12, k)
+    with qmm.Plan(fmt, n, k, 12, mode) as p:
+        y12 = host(p.run(wq, dev(x)))
+        y3 = host(p.run(wq, dev(x[:3])))
+        y12b = host(p.run(wq, dev(x)))
+    assert np.array_equal(y12, y12b)
+    yr, a = ref(fmt, mode, oracle.quantize(fmt, synth.weights_f32(7900, n, k)), n, k, x[:3])
+    assert_within(y3, yr, a, f"{NAME[fmt]} M=3 on a plan for 12")
+
+
+# ------------------------------------------------- full-size, sampled ----
+
+@pytest.mark.parametrize("fmt", [qmm.Q4_0, qmm.Q5_0, qmm.Q6_K], ids=["Q4_0", "Q5_0", "Q6_K"])
+@pytest.mark.parametrize("mode", MODES, ids=["a", "b"])
+@pytest.mark.parametrize("m", [1, 8])
+def test_scaleup_shape_sampled_rows(fmt, mode, m):
+    # 14336 x 4096 (the scale-up projection), every output computed on the
+    # GPU, 64 sampled weight rows checked against the oracle
+    n, k = 14336, 4096
+    w = synth.weights_f32(5000, n, k)
+    x = synth.acts_f32(5100, 512, k)[:m]
+    wg = qmm.quantize_weights(fmt, dev(w))
+    y = run(fmt, mode, host(wg), n, k, x)
+    rows = np.random.default_rng(7950 + m).choice(n, 64, replace=False)
+    wq = oracle.quantize(fmt, w[rows])
+    assert np.array_equal(host(wg)[rows], wq)
+    yr, a = ref(fmt, mode, wq, 64, k, x)
+    assert_within(y[:, rows], yr, a, f"{NAME[fmt]} 14336x4096 M={m} mode={mode}")
