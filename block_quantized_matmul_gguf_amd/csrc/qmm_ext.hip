@@ -38,34 +38,6 @@ struct Ext<FMT_Q6_K> {
     static constexpr int BYTES = 210, OFF = 32, UNIT = 32;  // a unit is a 32-value piece of a super-block
 };
 
-// ------------------------------------------------------------- loads -------
-// Q6_K super-blocks (210 B) are only 2-byte aligned.  The loads below read
-// 4-byte-aligned dwords, each holding at least one byte of the requested
-// range, so no access leaves the pages the weight buffer occupies.
-
-// ND dwords of the bytes at p (2-byte aligned): r[t] = bytes p+4t .. p+4t+3.
-template <int ND>
-QMM_DEV void load_bytes(const uint8_t* p, uint32_t r[ND])
-{
-    const uintptr_t a = (uintptr_t)p;
-    const uint32_t* q = reinterpret_cast<const uint32_t*>(a & ~(uintptr_t)3);
-    const uint32_t sh = (uint32_t)(a & 3);
-    uint32_t raw[ND + 1];
-#pragma unroll
-    for (int i = 0; i < ND; ++i) raw[i] = q[i];
-    raw[ND] = sh ? q[ND] : 0u;
-#pragma unroll
-    for (int t = 0; t < ND; ++t) r[t] = __builtin_amdgcn_alignbyte(raw[t + 1], raw[t], sh);
-}
-
-// The two bytes at p (2-byte aligned) as the low half of the result.
-QMM_DEV uint32_t load_u16(const uint8_t* p)
-{
-    const uintptr_t a = (uintptr_t)p;
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(a & ~(uintptr_t)3);
-    return (w >> (8 * (uint32_t)(a & 3))) & 0xffffu;
-}
-
 // Bits 0..3 of h, one per byte, moved to bit 4 of bytes 0..3.
 QMM_DEV uint32_t spread4(uint32_t h) { return ((h * 0x00204081u) & 0x01010101u) << 4; }
 
@@ -83,59 +55,6 @@ QMM_DEV void block_codes(const uint32_t qs[4], uint32_t qh, uint32_t v[8])
 #pragma unroll
         for (int t = 0; t < 8; ++t) v[t] |= spread4((qh >> (4 * t)) & 15u);
     }
-}
-
-// A pair of Q4_0 / Q5_0 blocks at p (4-byte aligned): codes and scales.
-template <int FMT>
-QMM_DEV void pair_codes(const uint8_t* p, uint32_t v[2][8], float d[2])
-{
-    const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
-    if constexpr (FMT == FMT_Q4_0) {
-        uint32_t r[9];
-#pragma unroll
-        for (int i = 0; i < 9; ++i) r[i] = q[i];
-        uint32_t a[4], b[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            a[t] = __builtin_amdgcn_alignbyte(r[t + 1], r[t], 2);  // bytes 2..17
-            b[t] = r[5 + t];                                       // bytes 20..35
-        }
-        d[0] = f16lo(r[0]);
-        d[1] = f16hi(r[4]);
-        block_codes<FMT>(a, 0u, v[0]);
-        block_codes<FMT>(b, 0u, v[1]);
-    } else {
-        uint32_t r[11];
-#pragma unroll
-        for (int i = 0; i < 11; ++i) r[i] = q[i];
-        uint32_t a[4], b[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            a[t] = __builtin_amdgcn_alignbyte(r[t + 2], r[t + 1], 2);  // bytes 6..21
-            b[t] = r[7 + t];                                           // bytes 28..43
-        }
-        d[0] = f16lo(r[0]);
-        d[1] = f16hi(r[5]);
-        block_codes<FMT>(a, __builtin_amdgcn_alignbyte(r[1], r[0], 2), v[0]);  // bytes 2..5
-        block_codes<FMT>(b, r[6], v[1]);                                        // bytes 24..27
-    }
-}
-
-// Piece `pc` (0..7, values 32pc..32pc+31) of the Q6_K super-block at s: codes
-// (0..63, v[t] = elements 4t..4t+3 of the piece), the two sub-block scales and d.
-QMM_DEV void q6k_piece(const uint8_t* s, int pc, uint32_t v[8], int& sc0, int& sc1, float& d)
-{
-    const int n = pc >> 2, g = pc & 3;
-    uint32_t lo[8], hi[8];
-    load_bytes<8>(s + 64 * n + 32 * (g & 1), lo);
-    load_bytes<8>(s + 128 + 32 * n, hi);
-    const int ls = 4 * (g >> 1), hs = 2 * g;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) v[t] = ((lo[t] >> ls) & 0x0f0f0f0fu) | (((hi[t] >> hs) & 0x03030303u) << 4);
-    const uint32_t scw = load_u16(s + 192 + 2 * pc);
-    sc0 = (int)(int8_t)(scw & 0xffu);
-    sc1 = (int)(int8_t)(scw >> 8);
-    d = (float)__builtin_bit_cast(_Float16, (uint16_t)load_u16(s + 208));
 }
 
 // sum over a block of (code - off) * x, the codes converted exactly.
@@ -185,115 +104,282 @@ struct ExtArgs {
     const float* xd;   //   their scales [M][K/32] (Q8_0) or [M][K/256] (Q8K)
     const int32_t* xs; //   sums of their values [M][K/32] (Q8_0) or [M][K/16] (Q8K bsums)
     float* y;          // [M][N]
-    int32_t* sums;     // block-sums hook (mode (b)): written instead of y when not null
+    int32_t* sums;     // block-sums hook (mode (b)): written instead of y when not null (HOOK instances)
     int N, K, M, m0;   // this launch: activation rows m0 + MT*blockIdx.y .. + MT - 1 of M
     int units;         // units per row
     int lpr_log2;      // log2 of the lanes per row
 };
 
-// One wave per 64/L rows (L = lanes per row, a power of two covering the
-// row's units up to 64); each lane walks units lane, lane + L, ...; the row
-// sums meet by butterfly inside the L lanes.  Activation rows m0..m0+MT-1.
+// Activations staged in LDS: per activation row, one slot per unit holding
+// the unit's values (f32 in mode (a), int8 in mode (b)) plus 16 bytes of
+// padding, so that the 16-byte reads of 16 lanes at consecutive units fall in
+// distinct banks.
+template <int FMT, int MODE>
+QMM_DEV constexpr int xl_stride() { return Ext<FMT>::UNIT * (MODE == MODE_A ? 4 : 1) + 16; }
+
+// Rows of activations [mb, mb + rows) as the kernel reads them: from LDS
+// (XL) or from global memory.
+template <int FMT, int MODE, bool XL>
+QMM_DEV const uint8_t* x_unit(const ExtArgs& a, const uint8_t* xl, int m, int mm, int u)
+{
+    if constexpr (XL) return xl + ((int64_t)m * a.units + u) * xl_stride<FMT, MODE>();
+    if constexpr (MODE == MODE_A) return reinterpret_cast<const uint8_t*>(a.x + (int64_t)mm * a.K + Ext<FMT>::UNIT * u);
+    return reinterpret_cast<const uint8_t*>(a.xq + (int64_t)mm * a.K + Ext<FMT>::UNIT * u);
+}
+
+// The weight bytes of one unit as loaded (raw dwords), then decoded.
+template <int FMT>
+struct Raw {
+    // a 4-byte-aligned pair of blocks
+    static constexpr int ND = FMT == FMT_Q4_0 ? 9 : 11;
+    uint32_t r[ND];
+    QMM_DEV void load(const uint8_t* row, int u)
+    {
+        const uint32_t* q = reinterpret_cast<const uint32_t*>(row + (int64_t)u * (2 * Ext<FMT>::BYTES));
+#pragma unroll
+        for (int i = 0; i < ND; ++i) r[i] = q[i];
+    }
+};
+template <>
+struct Raw<FMT_Q6_K> {
+    // piece pc of super-block i: the dwords under its 32 low-bit bytes and 32
+    // high-bit bytes (one more when the super-block starts at 2 mod 4), the
+    // dword holding its two scales and the one holding d.  Q6_K super-blocks
+    // (210 B) are only 2-byte aligned; every load is a 4-byte-aligned dword
+    // that holds at least one byte of the super-block, so no access leaves the
+    // pages the weight buffer occupies.
+    uint32_t lo[9], hi[9], scw, dw, sh;
+    QMM_DEV void load(const uint8_t* row, int u)
+    {
+        const int i = u >> 3, pc = u & 7, nn = pc >> 2, g = pc & 3;
+        const uint8_t* s = row + (int64_t)i * 210;
+        sh = (uint32_t)((uintptr_t)s & 3);
+        // rounded down by pointer arithmetic (an integer round trip would
+        // lose the global address space and give flat loads)
+        const uint32_t* pl = reinterpret_cast<const uint32_t*>(s + 64 * nn + 32 * (g & 1) - sh);
+        const uint32_t* ph = reinterpret_cast<const uint32_t*>(s + 128 + 32 * nn - sh);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            lo[t] = pl[t];
+            hi[t] = ph[t];
+        }
+        // the ninth dwords: the last two bytes when the super-block starts at
+        // 2 mod 4, else the bytes that follow inside the super-block (the
+        // high bits after the low bits, the scales after the high bits)
+        lo[8] = pl[8];
+        hi[8] = ph[8];
+        scw = *reinterpret_cast<const uint32_t*>(s + 192 + 2 * pc - ((sh + 2 * pc) & 3));
+        dw = *reinterpret_cast<const uint32_t*>(s + 208 - sh);
+    }
+};
+
+// Codes (0..63, v[t] = elements 4t..4t+3 of the piece), the two sub-block
+// scales and d of Q6_K piece pc (values 32pc..32pc+31 of its super-block).
+QMM_DEV void q6k_decode(const Raw<FMT_Q6_K>& w, int pc, uint32_t v[8], int& sc0, int& sc1, float& d)
+{
+    const int g = pc & 3, ls = 4 * (g >> 1), hs = 2 * g;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const uint32_t l = __builtin_amdgcn_alignbyte(w.lo[t + 1], w.lo[t], w.sh);
+        const uint32_t h = __builtin_amdgcn_alignbyte(w.hi[t + 1], w.hi[t], w.sh);
+        v[t] = ((l >> ls) & 0x0f0f0f0fu) | (((h >> hs) & 0x03030303u) << 4);
+    }
+    const uint32_t scb = w.scw >> (8 * ((w.sh + 2 * pc) & 3));
+    sc0 = (int)(int8_t)(scb & 0xffu);
+    sc1 = (int)(int8_t)((scb >> 8) & 0xffu);
+    d = (float)__builtin_bit_cast(_Float16, (uint16_t)((w.dw >> (8 * w.sh)) & 0xffffu));
+}
+
+// Codes and scales of a pair of Q4_0 / Q5_0 blocks (4-byte aligned).
+template <int FMT>
+QMM_DEV void pair_decode(const Raw<FMT>& w, uint32_t v[2][8], float d[2])
+{
+    const uint32_t* r = w.r;
+    uint32_t a[4], b[4];
+    if constexpr (FMT == FMT_Q4_0) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            a[t] = __builtin_amdgcn_alignbyte(r[t + 1], r[t], 2);  // bytes 2..17
+            b[t] = r[5 + t];                                       // bytes 20..35
+        }
+        d[0] = f16lo(r[0]);
+        d[1] = f16hi(r[4]);
+        block_codes<FMT>(a, 0u, v[0]);
+        block_codes<FMT>(b, 0u, v[1]);
+    } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            a[t] = __builtin_amdgcn_alignbyte(r[t + 2], r[t + 1], 2);  // bytes 6..21
+            b[t] = r[7 + t];                                           // bytes 28..43
+        }
+        d[0] = f16lo(r[0]);
+        d[1] = f16hi(r[5]);
+        block_codes<FMT>(a, __builtin_amdgcn_alignbyte(r[1], r[0], 2), v[0]);  // bytes 2..5
+        block_codes<FMT>(b, r[6], v[1]);                                        // bytes 24..27
+    }
+}
+
+// Mode (b) LDS layout after the activation slots of MT rows: the block
+// scales [MT][K/32 or K/256] (f32), then the value sums [MT][K/32 or K/16].
 template <int FMT, int MODE, int MT>
-__global__ __launch_bounds__(256) void ext_gemv_kernel(ExtArgs a)
+QMM_DEV int xl_extra_off(const ExtArgs& a) { return MT * a.units * xl_stride<FMT, MODE>(); }
+template <int FMT>
+QMM_DEV int xd_per_row(int K) { return FMT == FMT_Q6_K ? K / 256 : K / 32; }
+template <int FMT>
+QMM_DEV int xs_per_row(int K) { return FMT == FMT_Q6_K ? K / 16 : K / 32; }
+
+// The arithmetic of one unit u of row n against activation rows mb ..
+// mb + mrows - 1: into acc, or (block-sums hook) into a.sums.
+template <int FMT, int MODE, int MT, bool XL, bool HOOK>
+QMM_DEV void unit_math(const ExtArgs& a, const uint8_t* xl, const Raw<FMT>& w, int u, int64_t n, int mb, int mrows,
+                       int spr, float acc[MT])
 {
     using F = Ext<FMT>;
-    const int lane = threadIdx.x & 63;
-    const int L = 1 << a.lpr_log2;
-    const int64_t n = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 >> a.lpr_log2) + (lane >> a.lpr_log2);
-    const int sub = lane & (L - 1);
-    const bool live = n < a.N;
-    const uint8_t* row = a.w + (live ? n : 0) * a.row_bytes;
-    const int spr = FMT == FMT_Q6_K ? (a.K / 256) * 17 : a.K / 32;  // block sums per (m, n)
-    const int mb = a.m0 + (int)blockIdx.y * MT;                       // first activation row here
-
-    float acc[MT];
+    auto xl_scales = [&](const ExtArgs& aa, const uint8_t* p) {
+        return reinterpret_cast<const float*>(p + xl_extra_off<FMT, MODE, MT>(aa));
+    };
+    auto xl_sums = [&](const ExtArgs& aa, const uint8_t* p) {
+        return reinterpret_cast<const int32_t*>(p + xl_extra_off<FMT, MODE, MT>(aa)) + MT * xd_per_row<FMT>(aa.K);
+    };
+    if constexpr (FMT == FMT_Q6_K) {
+        const int i = u >> 3, pc = u & 7;
+        uint32_t v[8];
+        int sc0, sc1;
+        float d;
+        q6k_decode(w, pc, v, sc0, sc1, d);
 #pragma unroll
-    for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
-
-#pragma unroll 1
-    for (int u = sub; live && u < a.units; u += L) {
-        if constexpr (FMT == FMT_Q6_K) {
-            const int i = u >> 3, pc = u & 7;
-            uint32_t v[8];
-            int sc0, sc1;
-            float d;
-            q6k_piece(row + (int64_t)i * F::BYTES, pc, v, sc0, sc1, d);
-            const int k0 = 32 * u;
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                const int mm = mb + m;
-                if (mm >= a.M) break;
-                if constexpr (MODE == MODE_A) {
-                    float x[32];
-                    load_x(a.x + (int64_t)mm * a.K + k0, 32, x);
-                    const float s0 = dot_codes_f32<4>(v, x, 32.0f);
-                    const float s1 = dot_codes_f32<4>(v + 4, x + 16, 32.0f);
-                    acc[m] = fmaf(d, (float)sc0 * s0 + (float)sc1 * s1, acc[m]);
-                    if (MT > 1) asm volatile("" ::: "memory");  // one row's activations live at a time
+        for (int m = 0; m < MT; ++m) {
+            if (MT > 1 && m >= mrows) break;  // a one-row instance always has its row
+            const int mm = mb + m;
+            const uint8_t* xp = x_unit<FMT, MODE, XL>(a, xl, m, mm, u);
+            if constexpr (MODE == MODE_A) {
+                float x[32];
+                load_x(reinterpret_cast<const float*>(xp), 32, x);
+                const float s0 = dot_codes_f32<4>(v, x, 32.0f);
+                const float s1 = dot_codes_f32<4>(v + 4, x + 16, 32.0f);
+                acc[m] = fmaf(d, (float)sc0 * s0 + (float)sc1 * s1, acc[m]);
+                if (MT > 1) asm volatile("" ::: "memory");  // one row's activations live at a time
+            } else {
+                uint32_t xq[8];
+                load_q(reinterpret_cast<const int8_t*>(xp), xq);
+                const int32_t* bs = (XL ? xl_sums(a, xl) + (int64_t)m * (a.K / 16) : a.xs + (int64_t)mm * (a.K / 16)) + 2 * u;
+                const int S0 = dot_codes_i8<4>(v, xq) - 32 * bs[0];
+                const int S1 = dot_codes_i8<4>(v + 4, xq + 4) - 32 * bs[1];
+                const int part = sc0 * S0 + sc1 * S1;
+                if constexpr (HOOK) {
+                    int32_t* o = a.sums + ((int64_t)mm * a.N + n) * spr + 17 * i;
+                    o[2 * pc] = S0;
+                    o[2 * pc + 1] = S1;
+                    int t = part;  // sumi: the eight pieces of the super-block are lanes 8k..8k+7
+                    t += __shfl_xor(t, 1);
+                    t += __shfl_xor(t, 2);
+                    t += __shfl_xor(t, 4);
+                    if (pc == 0) o[16] = t;
                 } else {
-                    uint32_t xq[8];
-                    load_q(a.xq + (int64_t)mm * a.K + k0, xq);
-                    const int32_t* bs = a.xs + (int64_t)mm * (a.K / 16) + 2 * u;
-                    const int S0 = dot_codes_i8<4>(v, xq) - 32 * bs[0];
-                    const int S1 = dot_codes_i8<4>(v + 4, xq + 4) - 32 * bs[1];
-                    const int part = sc0 * S0 + sc1 * S1;
-                    if (a.sums) {
-                        int32_t* o = a.sums + ((int64_t)mm * a.N + n) * spr + 17 * i;
-                        o[2 * pc] = S0;
-                        o[2 * pc + 1] = S1;
-                        int t = part;  // sumi: the eight pieces of the super-block are lanes 8k..8k+7
-                        t += __shfl_xor(t, 1);
-                        t += __shfl_xor(t, 2);
-                        t += __shfl_xor(t, 4);
-                        if (pc == 0) o[16] = t;
-                    } else {
-                        const float dx = a.xd[(int64_t)mm * (a.K / 256) + i];
-                        acc[m] = fmaf(d * dx, (float)part, acc[m]);
-                    }
+                    const float dx = XL ? xl_scales(a, xl)[(int64_t)m * (a.K / 256) + i] : a.xd[(int64_t)mm * (a.K / 256) + i];
+                    acc[m] = fmaf(d * dx, (float)part, acc[m]);
                 }
             }
-        } else {
-            uint32_t v[2][8];
-            float d[2];
-            pair_codes<FMT>(row + (int64_t)u * (2 * F::BYTES), v, d);
-            const int k0 = 64 * u;
+        }
+    } else {
+        uint32_t v[2][8];
+        float d[2];
+        pair_decode<FMT>(w, v, d);
 #pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                const int mm = mb + m;
-                if (mm >= a.M) break;
-                if constexpr (MODE == MODE_A) {
-                    float x[32];
-                    load_x(a.x + (int64_t)mm * a.K + k0, 32, x);
-                    const float s0 = dot_codes_f32<8>(v[0], x, (float)F::OFF);
-                    load_x(a.x + (int64_t)mm * a.K + k0 + 32, 32, x);
-                    const float s1 = dot_codes_f32<8>(v[1], x, (float)F::OFF);
-                    acc[m] = fmaf(d[0], s0, fmaf(d[1], s1, acc[m]));
-                    if (MT > 1) asm volatile("" ::: "memory");  // one row's activations live at a time
-                } else {
+        for (int m = 0; m < MT; ++m) {
+            if (MT > 1 && m >= mrows) break;  // a one-row instance always has its row
+            const int mm = mb + m;
+            const uint8_t* xp = x_unit<FMT, MODE, XL>(a, xl, m, mm, u);
+            if constexpr (MODE == MODE_A) {
+                float x[32];
+                load_x(reinterpret_cast<const float*>(xp), 32, x);
+                const float s0 = dot_codes_f32<8>(v[0], x, (float)F::OFF);
+                load_x(reinterpret_cast<const float*>(xp) + 32, 32, x);
+                const float s1 = dot_codes_f32<8>(v[1], x, (float)F::OFF);
+                acc[m] = fmaf(d[0], s0, fmaf(d[1], s1, acc[m]));
+                if (MT > 1) asm volatile("" ::: "memory");  // one row's activations live at a time
+            } else {
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const int b = 2 * u + h;
-                        uint32_t xq[8];
-                        load_q(a.xq + (int64_t)mm * a.K + k0 + 32 * h, xq);
-                        const int S = dot_codes_i8<8>(v[h], xq) - F::OFF * a.xs[(int64_t)mm * (a.K / 32) + b];
-                        if (a.sums) {
-                            a.sums[((int64_t)mm * a.N + n) * spr + b] = S;
-                        } else {
-                            const float dx = a.xd[(int64_t)mm * (a.K / 32) + b];
-                            acc[m] = fmaf(d[h] * dx, (float)S, acc[m]);
-                        }
+                for (int h = 0; h < 2; ++h) {
+                    const int b = 2 * u + h;
+                    uint32_t xq[8];
+                    load_q(reinterpret_cast<const int8_t*>(xp) + 32 * h, xq);
+                    const int32_t sx = XL ? xl_sums(a, xl)[(int64_t)m * (a.K / 32) + b] : a.xs[(int64_t)mm * (a.K / 32) + b];
+                    const int S = dot_codes_i8<8>(v[h], xq) - F::OFF * sx;
+                    if constexpr (HOOK) {
+                        a.sums[((int64_t)mm * a.N + n) * spr + b] = S;
+                    } else {
+                        const float dx = XL ? xl_scales(a, xl)[(int64_t)m * (a.K / 32) + b] : a.xd[(int64_t)mm * (a.K / 32) + b];
+                        acc[m] = fmaf(d[h] * dx, (float)S, acc[m]);
                     }
                 }
             }
         }
     }
-    if (MODE == MODE_B && a.sums) return;
+}
+
+// Each wave takes 64/L rows at a time (L = lanes per row, a power of two
+// covering the row's units up to 64) and strides over the row groups; each
+// lane walks units lane, lane + L, ... of its row, and the row sums meet by
+// butterfly inside the L lanes.  Activation rows mb .. mb + MT - 1, staged in
+// LDS once per workgroup when XL.  HOOK: the block-sums test hook (mode (b))
+// writes the integer sums instead of y.
+template <int FMT, int MODE, int MT, bool XL, bool HOOK>
+__global__ __launch_bounds__(256) void ext_gemv_kernel(ExtArgs a)
+{
+    using F = Ext<FMT>;
+    extern __shared__ __align__(16) uint8_t xl[];
+    const int lane = threadIdx.x & 63;
+    const int L = 1 << a.lpr_log2;
+    const int sub = lane & (L - 1);
+    const int spr = FMT == FMT_Q6_K ? (a.K / 256) * 17 : a.K / 32;  // block sums per (m, n)
+    const int mb = a.m0 + (int)blockIdx.y * MT;                       // first activation row here
+    const int mrows = min(MT, a.M - mb);
+
+    if constexpr (XL) {
+        constexpr int ub = F::UNIT * (MODE == MODE_A ? 4 : 1), st = xl_stride<FMT, MODE>();
+        const int per_row = a.units * (ub / 16);
+        const uint8_t* src = MODE == MODE_A ? reinterpret_cast<const uint8_t*>(a.x) : reinterpret_cast<const uint8_t*>(a.xq);
+        const int64_t row_b = (int64_t)a.K * (MODE == MODE_A ? 4 : 1);
+        for (int c = threadIdx.x; c < mrows * per_row; c += 256) {
+            const int m = c / per_row, cc = c % per_row;
+            const int u = cc / (ub / 16), w = cc % (ub / 16);
+            const uint4 t = *reinterpret_cast<const uint4*>(src + (int64_t)(mb + m) * row_b + 16 * (int64_t)cc);
+            *reinterpret_cast<uint4*>(xl + ((int64_t)m * a.units + u) * st + 16 * w) = t;
+        }
+        if constexpr (MODE == MODE_B) {
+            const int nd = xd_per_row<FMT>(a.K), ns = xs_per_row<FMT>(a.K);
+            float* ld = reinterpret_cast<float*>(xl + xl_extra_off<FMT, MODE, MT>(a));
+            int32_t* ls = reinterpret_cast<int32_t*>(ld + MT * nd);
+            for (int c = threadIdx.x; c < mrows * nd; c += 256) ld[c] = a.xd[(int64_t)mb * nd + c];
+            for (int c = threadIdx.x; c < mrows * ns; c += 256) ls[c] = a.xs[(int64_t)mb * ns + c];
+        }
+        __syncthreads();
+    }
+
+    const int rpw = 64 >> a.lpr_log2;
+    const int64_t groups = ((int64_t)a.N + rpw - 1) / rpw;
+    for (int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); g < groups; g += (int64_t)gridDim.x * 4) {
+        const int64_t n = g * rpw + (lane >> a.lpr_log2);
+        const bool live = n < a.N;
+        const uint8_t* row = a.w + (live ? n : 0) * a.row_bytes;
+
+        float acc[MT];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        float s = acc[m];
-        for (int off = L >> 1; off > 0; off >>= 1) s += __shfl_xor(s, off);
-        if (live && sub == 0 && mb + m < a.M) a.y[(int64_t)(mb + m) * a.N + n] = s;
+        for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
+        Raw<FMT> r;
+#pragma unroll 1
+        for (int u = sub; live && u < a.units; u += L) {
+            r.load(row, u);
+            unit_math<FMT, MODE, MT, XL, HOOK>(a, xl, r, u, n, mb, mrows, spr, acc);
+        }
+        if constexpr (HOOK) continue;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            float t = acc[m];
+            for (int off = L >> 1; off > 0; off >>= 1) t += __shfl_xor(t, off);
+            if (live && sub == 0 && m < mrows) a.y[(int64_t)(mb + m) * a.N + n] = t;
+        }
     }
 }
 
@@ -400,11 +486,13 @@ __global__ __launch_bounds__(256) void ext_dequant_kernel(const uint8_t* __restr
     const int p = (int)(u % n32);
     const uint8_t* row = w + n * row_bytes;
     float val[32];
+    Raw<FMT> raw;
     if constexpr (FMT == FMT_Q6_K) {
         uint32_t v[8];
         int sc0, sc1;
         float d;
-        q6k_piece(row + (int64_t)(p >> 3) * 210, p & 7, v, sc0, sc1, d);
+        raw.load(row, p);
+        q6k_decode(raw, p & 7, v, sc0, sc1, d);
         const float e0 = d * (float)sc0, e1 = d * (float)sc1;
 #pragma unroll
         for (int t = 0; t < 8; ++t)
@@ -415,7 +503,8 @@ __global__ __launch_bounds__(256) void ext_dequant_kernel(const uint8_t* __restr
         using F = Ext<FMT>;
         uint32_t v[2][8];
         float d[2];
-        pair_codes<FMT>(row + (int64_t)(p >> 1) * (2 * F::BYTES), v, d);
+        raw.load(row, p >> 1);
+        pair_decode<FMT>(raw, v, d);
         const int h = p & 1;
 #pragma unroll
         for (int t = 0; t < 8; ++t)
@@ -546,45 +635,77 @@ bool is_ext_format(int fmt) { return fmt == FMT_Q4_0 || fmt == FMT_Q5_0 || fmt =
 int64_t ext_block_bytes(int fmt) { return fmt == FMT_Q4_0 ? 18 : fmt == FMT_Q5_0 ? 22 : 210; }
 
 template <int FMT, int MODE, int MT>
-static void launch_one(const ExtArgs& a, unsigned gx, unsigned gy, hipStream_t s)
+static void launch_one(bool xl, const ExtArgs& a, unsigned gx, unsigned gy, int lds, hipStream_t s)
 {
-    hipLaunchKernelGGL((ext_gemv_kernel<FMT, MODE, MT>), dim3(gx, gy), dim3(256), 0, s, a);
+    const dim3 grid(gx, gy), block(256);
+    if constexpr (MODE == MODE_B) {
+        if (a.sums) {  // the block-sums hook: activations from global memory
+            hipLaunchKernelGGL((ext_gemv_kernel<FMT, MODE, MT, false, true>), grid, block, 0, s, a);
+            return;
+        }
+    }
+    if (xl) hipLaunchKernelGGL((ext_gemv_kernel<FMT, MODE, MT, true, false>), grid, block, lds, s, a);
+    else hipLaunchKernelGGL((ext_gemv_kernel<FMT, MODE, MT, false, false>), grid, block, 0, s, a);
 }
 
 template <int FMT, int MODE>
-static void launch_mt(int mt, const ExtArgs& a, unsigned gx, unsigned gy, hipStream_t s)
+static void launch_mt(int mt, bool xl, const ExtArgs& a, unsigned gx, unsigned gy, int lds, hipStream_t s)
 {
-    if (mt == 1) launch_one<FMT, MODE, 1>(a, gx, gy, s);
-    else if (MODE == MODE_B && mt == 2) launch_one<FMT, MODE, 2>(a, gx, gy, s);
-    else if (MODE == MODE_B && mt == 4) launch_one<FMT, MODE, 4>(a, gx, gy, s);
-    else launch_one<FMT, MODE, 8>(a, gx, gy, s);
+    if (mt == 1) {
+        launch_one<FMT, MODE, 1>(xl, a, gx, gy, lds, s);
+        return;
+    }
+    if constexpr (MODE == MODE_B) {
+        if (mt == 2) return launch_one<FMT, MODE, 2>(xl, a, gx, gy, lds, s);
+        if (mt == 4) return launch_one<FMT, MODE, 4>(xl, a, gx, gy, lds, s);
+    }
+    launch_one<FMT, MODE, 8>(xl, a, gx, gy, lds, s);
 }
 
-// The decode kernel over activation rows m0.. in one launch per 65535 * 8 rows.
+// LDS bytes of the staged activations: MT rows of units * stride, and in
+// mode (b) the rows' block scales and value sums.
+static int ext_xl_bytes(int fmt, int mode, int units, int K, int mt)
+{
+    const int unit = fmt == FMT_Q6_K ? 32 : 64;
+    int bytes = mt * units * (unit * (mode == MODE_A ? 4 : 1) + 16);
+    if (mode == MODE_B) bytes += 4 * mt * (fmt == FMT_Q6_K ? K / 256 + K / 16 : 2 * (K / 32));
+    return bytes;
+}
+constexpr int EXT_XL_MAX = 64 * 1024;  // the default LDS limit; above it the kernel reads activations from global memory
+
+// The decode kernel over activation rows m0.. in one launch per 65535 * MT rows.
 static hipError_t ext_gemv(int fmt, int mode, ExtArgs a, hipStream_t s)
 {
     // activation rows per launch row: mode (a) keeps the one- and eight-row
     // instances (the two- and four-row ones hold every decoded value and
     // activation at once and need over 200 registers)
     const int mt = a.M == 1 ? 1 : mode == MODE_A ? 8 : a.M == 2 ? 2 : a.M <= 4 ? 4 : 8;
+    const int lds = ext_xl_bytes(fmt, mode, a.units, a.K, mt);
+    const bool xl = lds <= EXT_XL_MAX && !a.sums;
     int lg = 0;
     while ((1 << lg) < a.units && lg < 6) ++lg;
     a.lpr_log2 = lg;
-    const int64_t rows_per_wg = 4 * (64 >> lg);
-    const unsigned gx = (unsigned)((a.N + rows_per_wg - 1) / rows_per_wg);
+    // workgroups: enough to cover the row groups once, at most what the
+    // compute units hold at once by LDS (so that each workgroup's staged
+    // activations serve several rows)
+    const int64_t groups = ((int64_t)a.N + (64 >> lg) - 1) / (64 >> lg);
+    const int slot = mt * a.units * ((fmt == FMT_Q6_K ? 32 : 64) * (mode == MODE_A ? 4 : 1) + 16);
+    const int per_cu = xl ? std::max(1, std::min(8, (160 * 1024) / slot)) : 8;
+    const int64_t cap = (int64_t)device_cus() * per_cu;
+    const unsigned gx = (unsigned)std::min<int64_t>((groups + 3) / 4, cap);
     const int64_t chunk = 65535ll * mt;
     for (int64_t m0 = 0; m0 < a.M; m0 += chunk) {
         a.m0 = (int)m0;
         const unsigned gy = (unsigned)std::min<int64_t>(65535, (a.M - m0 + mt - 1) / mt);
         if (fmt == FMT_Q4_0) {
-            if (mode == MODE_A) launch_mt<FMT_Q4_0, MODE_A>(mt, a, gx, gy, s);
-            else launch_mt<FMT_Q4_0, MODE_B>(mt, a, gx, gy, s);
+            if (mode == MODE_A) launch_mt<FMT_Q4_0, MODE_A>(mt, xl, a, gx, gy, lds, s);
+            else launch_mt<FMT_Q4_0, MODE_B>(mt, xl, a, gx, gy, lds, s);
         } else if (fmt == FMT_Q5_0) {
-            if (mode == MODE_A) launch_mt<FMT_Q5_0, MODE_A>(mt, a, gx, gy, s);
-            else launch_mt<FMT_Q5_0, MODE_B>(mt, a, gx, gy, s);
+            if (mode == MODE_A) launch_mt<FMT_Q5_0, MODE_A>(mt, xl, a, gx, gy, lds, s);
+            else launch_mt<FMT_Q5_0, MODE_B>(mt, xl, a, gx, gy, lds, s);
         } else {
-            if (mode == MODE_A) launch_mt<FMT_Q6_K, MODE_A>(mt, a, gx, gy, s);
-            else launch_mt<FMT_Q6_K, MODE_B>(mt, a, gx, gy, s);
+            if (mode == MODE_A) launch_mt<FMT_Q6_K, MODE_A>(mt, xl, a, gx, gy, lds, s);
+            else launch_mt<FMT_Q6_K, MODE_B>(mt, xl, a, gx, gy, lds, s);
         }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

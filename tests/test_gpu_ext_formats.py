@@ -198,3 +198,19 @@ def test_scaleup_shape_sampled_rows(fmt, mode, m):
     assert np.array_equal(host(wg)[rows], wq)
     yr, a = ref(fmt, mode, wq, 64, k, x)
     assert_within(y[:, rows], yr, a, f"{NAME[fmt]} 14336x4096 M={m} mode={mode}")
+
+
+# Long rows: more units than two per lane (each lane walks its units), and
+# activations too large to stage in LDS (read from global memory).
+LONG = [(qmm.Q4_0, 40, 16384), (qmm.Q5_0, 24, 9216), (qmm.Q6_K, 40, 14336)]
+
+
+@pytest.mark.parametrize("mode", MODES, ids=["a", "b"])
+@pytest.mark.parametrize("fmt,n,k", LONG, ids=[f"{NAME[f]}-{n}x{k}" for f, n, k in LONG])
+@pytest.mark.parametrize("m", [1, 3, 8])
+def test_long_rows(fmt, n, k, mode, m):
+    wq = oracle.quantize(fmt, synth.weights_f32(8000 + k, n, k))
+    x = synth.acts_f32(8001 + m, m, k)
+    y = run(fmt, mode, wq, n, k, x)
+    yr, a = ref(fmt, mode, wq, n, k, x)
+    assert_within(y, yr, a, f"{NAME[fmt]} {n}x{k} M={m} mode={mode}")
