@@ -324,8 +324,10 @@ QMM_DEV void unit_math(const ExtArgs& a, const uint8_t* xl, const Raw<FMT>& w, i
 // butterfly inside the L lanes.  Activation rows mb .. mb + MT - 1, staged in
 // LDS once per workgroup when XL.  HOOK: the block-sums test hook (mode (b))
 // writes the integer sums instead of y.
+constexpr int EXT_WAVES = 8, EXT_THREADS = 64 * EXT_WAVES;  // decode workgroup: eight waves share the staged activations
+
 template <int FMT, int MODE, int MT, bool XL, bool HOOK>
-__global__ __launch_bounds__(256) void ext_gemv_kernel(ExtArgs a)
+__global__ __launch_bounds__(EXT_THREADS) void ext_gemv_kernel(ExtArgs a)
 {
     using F = Ext<FMT>;
     extern __shared__ __align__(16) uint8_t xl[];
@@ -341,7 +343,7 @@ __global__ __launch_bounds__(256) void ext_gemv_kernel(ExtArgs a)
         const int per_row = a.units * (ub / 16);
         const uint8_t* src = MODE == MODE_A ? reinterpret_cast<const uint8_t*>(a.x) : reinterpret_cast<const uint8_t*>(a.xq);
         const int64_t row_b = (int64_t)a.K * (MODE == MODE_A ? 4 : 1);
-        for (int c = threadIdx.x; c < mrows * per_row; c += 256) {
+        for (int c = threadIdx.x; c < mrows * per_row; c += EXT_THREADS) {
             const int m = c / per_row, cc = c % per_row;
             const int u = cc / (ub / 16), w = cc % (ub / 16);
             const uint4 t = *reinterpret_cast<const uint4*>(src + (int64_t)(mb + m) * row_b + 16 * (int64_t)cc);
@@ -351,15 +353,15 @@ __global__ __launch_bounds__(256) void ext_gemv_kernel(ExtArgs a)
             const int nd = xd_per_row<FMT>(a.K), ns = xs_per_row<FMT>(a.K);
             float* ld = reinterpret_cast<float*>(xl + xl_extra_off<FMT, MODE, MT>(a));
             int32_t* ls = reinterpret_cast<int32_t*>(ld + MT * nd);
-            for (int c = threadIdx.x; c < mrows * nd; c += 256) ld[c] = a.xd[(int64_t)mb * nd + c];
-            for (int c = threadIdx.x; c < mrows * ns; c += 256) ls[c] = a.xs[(int64_t)mb * ns + c];
+            for (int c = threadIdx.x; c < mrows * nd; c += EXT_THREADS) ld[c] = a.xd[(int64_t)mb * nd + c];
+            for (int c = threadIdx.x; c < mrows * ns; c += EXT_THREADS) ls[c] = a.xs[(int64_t)mb * ns + c];
         }
         __syncthreads();
     }
 
     const int rpw = 64 >> a.lpr_log2;
     const int64_t groups = ((int64_t)a.N + rpw - 1) / rpw;
-    for (int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); g < groups; g += (int64_t)gridDim.x * 4) {
+    for (int64_t g = (int64_t)blockIdx.x * EXT_WAVES + (threadIdx.x >> 6); g < groups; g += (int64_t)gridDim.x * EXT_WAVES) {
         const int64_t n = g * rpw + (lane >> a.lpr_log2);
         const bool live = n < a.N;
         const uint8_t* row = a.w + (live ? n : 0) * a.row_bytes;
@@ -634,18 +636,31 @@ bool is_ext_format(int fmt) { return fmt == FMT_Q4_0 || fmt == FMT_Q5_0 || fmt =
 
 int64_t ext_block_bytes(int fmt) { return fmt == FMT_Q4_0 ? 18 : fmt == FMT_Q5_0 ? 22 : 210; }
 
+constexpr int EXT_XL_MAX = 160 * 1024;  // LDS of a compute unit; above it the kernel reads activations from global memory
+
 template <int FMT, int MODE, int MT>
 static void launch_one(bool xl, const ExtArgs& a, unsigned gx, unsigned gy, int lds, hipStream_t s)
 {
-    const dim3 grid(gx, gy), block(256);
+    const dim3 grid(gx, gy), block(EXT_THREADS);
     if constexpr (MODE == MODE_B) {
         if (a.sums) {  // the block-sums hook: activations from global memory
             hipLaunchKernelGGL((ext_gemv_kernel<FMT, MODE, MT, false, true>), grid, block, 0, s, a);
             return;
         }
     }
-    if (xl) hipLaunchKernelGGL((ext_gemv_kernel<FMT, MODE, MT, true, false>), grid, block, lds, s, a);
-    else hipLaunchKernelGGL((ext_gemv_kernel<FMT, MODE, MT, false, false>), grid, block, 0, s, a);
+    if (xl) {
+        if (lds > 64 * 1024) {
+            // above the default dynamic LDS limit: raised once per kernel (the
+            // call is host-side, before any capture of a run)
+            static const hipError_t raised = hipFuncSetAttribute(
+                reinterpret_cast<const void*>(&ext_gemv_kernel<FMT, MODE, MT, true, false>),
+                hipFuncAttributeMaxDynamicSharedMemorySize, EXT_XL_MAX);
+            (void)raised;
+        }
+        hipLaunchKernelGGL((ext_gemv_kernel<FMT, MODE, MT, true, false>), grid, block, lds, s, a);
+    } else {
+        hipLaunchKernelGGL((ext_gemv_kernel<FMT, MODE, MT, false, false>), grid, block, 0, s, a);
+    }
 }
 
 template <int FMT, int MODE>
@@ -671,7 +686,6 @@ static int ext_xl_bytes(int fmt, int mode, int units, int K, int mt)
     if (mode == MODE_B) bytes += 4 * mt * (fmt == FMT_Q6_K ? K / 256 + K / 16 : 2 * (K / 32));
     return bytes;
 }
-constexpr int EXT_XL_MAX = 64 * 1024;  // the default LDS limit; above it the kernel reads activations from global memory
 
 // The decode kernel over activation rows m0.. in one launch per 65535 * MT rows.
 static hipError_t ext_gemv(int fmt, int mode, ExtArgs a, hipStream_t s)
@@ -690,9 +704,9 @@ static hipError_t ext_gemv(int fmt, int mode, ExtArgs a, hipStream_t s)
     // activations serve several rows)
     const int64_t groups = ((int64_t)a.N + (64 >> lg) - 1) / (64 >> lg);
     const int slot = mt * a.units * ((fmt == FMT_Q6_K ? 32 : 64) * (mode == MODE_A ? 4 : 1) + 16);
-    const int per_cu = xl ? std::max(1, std::min(8, (160 * 1024) / slot)) : 8;
+    const int per_cu = xl ? std::max(1, std::min(4, (160 * 1024) / slot)) : 4;
     const int64_t cap = (int64_t)device_cus() * per_cu;
-    const unsigned gx = (unsigned)std::min<int64_t>((groups + 3) / 4, cap);
+    const unsigned gx = (unsigned)std::min<int64_t>((groups + EXT_WAVES - 1) / EXT_WAVES, cap);
     const int64_t chunk = 65535ll * mt;
     for (int64_t m0 = 0; m0 < a.M; m0 += chunk) {
         a.m0 = (int)m0;
