@@ -49,10 +49,11 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-layers", type=int, default=LAYERS, help="layers in the CPU-baseline sample")
     p.add_argument("--no-dequant", action="store_true", help="skip the dequantize-all context rows")
-    p.add_argument("--workload", default="c5", choices=["c1", "c2", "c3", "c4", "c5"],
+    p.add_argument("--workload", default="c5", choices=["c1", "c2", "c3", "c4", "c5", "c6"],
                    help="c5 (default): the step above.  c1-c4: the pages' smaller workloads as context lines "
                         "(q_proj GEMV, lm_head GEMV warm and cold, ffn_down Q4_K at M=1 and 37, the 30-layer "
-                        "SmolLM2 prefill at M=307 on a stream and as a HIP graph)")
+                        "SmolLM2 prefill at M=307 on a stream and as a HIP graph).  c6: the step's layers in "
+                        "the other formats of the pages' files (Q4_0, Q5_0, Q6_K)")
     p.add_argument("--only", default="", help="restrict the step to one part, e.g. gemv:q8_0:b:1 or gemm:q4_k:a "
                                               "(for profiling one kernel); 'copy' times a plain 512 MiB device copy "
                                               "instead (the calibration for the HBM byte counters)")
@@ -168,7 +169,7 @@ def small_workload(args, qmm, torch, synth, stream):
     import numpy as np
     dev = torch.device("cuda:0")
     modes = {"a": qmm.MODE_F32ACT, "b": qmm.MODE_QACT}
-    fmt_code = {"q8_0": qmm.Q8_0, "q4_k": qmm.Q4_K}
+    fmt_code = {"q8_0": qmm.Q8_0, "q4_k": qmm.Q4_K, "q5_0": qmm.Q5_0}
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
 
     def timed(fn, reps):
@@ -225,8 +226,11 @@ def small_workload(args, qmm, torch, synth, stream):
         # the decode step of the same model: every projection at M = 1 (the first token's row)
         xd = [t[:1].contiguous() for t in xp]
         yd = [torch.empty((1, p.n), dtype=torch.float32, device=dev) for p in probs]
+        # the page's own Q4K file: K-quants only where K divides by 256 (ffn_down),
+        # every other matrix Q5_0 (page "自己量化", section 3. 量化)
         passes = {"q8_0": ["q8_0"] * len(probs),
-                  "down_q4_k": ["q4_k" if p.name.split()[0].endswith(".down") else "q8_0" for p in probs]}
+                  "down_q4_k": ["q4_k" if p.name.split()[0].endswith(".down") else "q8_0" for p in probs],
+                  "q4k_file": ["q4_k" if p.name.split()[0].endswith(".down") else "q5_0" for p in probs]}
         wcache = {}
         out = {"workload": "c4", "problems": len(probs), "M_prefill": probs[0].m, "M_decode": 1, "passes": {}}
         total_flop = sum(2.0 * p.m * p.n * p.k for p in probs)
@@ -313,6 +317,56 @@ def small_workload(args, qmm, torch, synth, stream):
     print(json.dumps(out))
 
 
+def formats_workload(args, qmm, torch, synth, stream):
+    """c6: the step's 8 layers of 14336x4096 weights (the same seeds) in Q4_0,
+    Q5_0 and Q6_K, quantized by the library, rotated per launch (264, 323 and
+    385 MB: HBM-resident), both modes, M = 1 and 8 (decode) and 512 (prefill:
+    Q4_0/Q5_0 rewrite the weights as Q8_0 blocks and take the Q8_0 kernels,
+    Q6_K takes the decode kernels eight rows at a time).  Per-launch times
+    from HIP events on the launch stream."""
+    dev = torch.device("cuda:0")
+    fmts = {"q4_0": qmm.Q4_0, "q5_0": qmm.Q5_0, "q6_k": qmm.Q6_K}
+    modes = {"a": qmm.MODE_F32ACT, "b": qmm.MODE_QACT}
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    x = torch.from_numpy(synth.acts_f32(5100, M_PREFILL, K)).to(dev)
+    xs = {m: x[:m].contiguous() for m in DECODE_M + (M_PREFILL,)}
+    ys = {m: torch.empty((m, N), dtype=torch.float32, device=dev) for m in DECODE_M + (M_PREFILL,)}
+    rows = []
+    for f, code in fmts.items():
+        wq = []
+        for layer in range(LAYERS):
+            wf = torch.from_numpy(synth.weights_f32(5000 + layer, N, K)).to(dev)
+            wq.append(qmm.quantize_weights(code, wf))
+            del wf
+        b = wq[0].numel()
+        for md, mcode in modes.items():
+            with qmm.Plan(code, N, K, M_PREFILL, mcode) as plan:
+                for m in DECODE_M + (M_PREFILL,):
+                    reps = args.steps if m <= 8 else max(2, args.steps // 4)
+                    for _ in range(max(1, args.warmup)):
+                        for l in range(LAYERS):
+                            plan.run(wq[l], xs[m], ys[m], stream)
+                    torch.cuda.synchronize()
+                    ev[0].record(stream)
+                    for _ in range(reps):
+                        for l in range(LAYERS):
+                            plan.run(wq[l], xs[m], ys[m], stream)
+                    ev[1].record(stream)
+                    torch.cuda.synchronize()
+                    us = ev[0].elapsed_time(ev[1]) * 1000.0 / (reps * LAYERS)
+                    r = {"fmt": f, "mode": md, "M": m, "us_per_launch": round(us, 3),
+                         "weight_GBps": round(b / (us * 1e-6) / 1e9, 1)}
+                    if m <= 8:
+                        r["frac_hbm"] = round(b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+                    else:
+                        r["TOPS"] = round(2.0 * m * N * K / (us * 1e-6) / 1e12, 1)
+                    rows.append(r)
+        del wq
+        torch.cuda.synchronize()
+    print(json.dumps({"workload": "c6", "note": "8 layers of 14336x4096 rotated per launch (HBM-resident); weight "
+                      "bytes per layer: Q4_0 33.0 MB, Q5_0 40.4 MB, Q6_K 48.2 MB", "rows": rows}))
+
+
 def copy_calibration(torch, dev, stream, args):
     """A plain elementwise copy of 512 MiB of f32 (read 512 MiB, write
     512 MiB): the known-size kernel against which the FETCH_SIZE and WRITE_SIZE
@@ -353,6 +407,9 @@ def main():
     stream = torch.cuda.current_stream()
     if args.only == "copy":
         copy_calibration(torch, dev, stream, args)
+        return
+    if args.workload == "c6":
+        formats_workload(args, qmm, torch, synth, stream)
         return
     if args.workload != "c5":
         small_workload(args, qmm, torch, synth, stream)

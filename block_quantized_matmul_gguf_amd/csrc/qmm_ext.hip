@@ -99,8 +99,8 @@ QMM_DEV void load_q(const int8_t* p, uint32_t out[8])
 struct ExtArgs {
     const uint8_t* w;
     int64_t row_bytes;
-    const float* x;    // mode (a): f32 [M][K]
-    const int8_t* xq;  // mode (b): quantized activations int8 [M][K]
+    const float* x;    // f32 activations [M][K]
+    const int8_t* xq;  // mode (b): quantized activations int8 [M][K] (null: quantized in the kernel)
     const float* xd;   //   their scales [M][K/32] (Q8_0) or [M][K/256] (Q8K)
     const int32_t* xs; //   sums of their values [M][K/32] (Q8_0) or [M][K/16] (Q8K bsums)
     float* y;          // [M][N]
@@ -338,23 +338,76 @@ __global__ __launch_bounds__(EXT_THREADS) void ext_gemv_kernel(ExtArgs a)
     const int mb = a.m0 + (int)blockIdx.y * MT;                       // first activation row here
     const int mrows = min(MT, a.M - mb);
 
-    if constexpr (XL) {
-        constexpr int ub = F::UNIT * (MODE == MODE_A ? 4 : 1), st = xl_stride<FMT, MODE>();
+    if constexpr (XL && MODE == MODE_A) {
+        // f32 activations copied into their slots
+        constexpr int ub = F::UNIT * 4, st = xl_stride<FMT, MODE>();
         const int per_row = a.units * (ub / 16);
-        const uint8_t* src = MODE == MODE_A ? reinterpret_cast<const uint8_t*>(a.x) : reinterpret_cast<const uint8_t*>(a.xq);
-        const int64_t row_b = (int64_t)a.K * (MODE == MODE_A ? 4 : 1);
         for (int c = threadIdx.x; c < mrows * per_row; c += EXT_THREADS) {
             const int m = c / per_row, cc = c % per_row;
             const int u = cc / (ub / 16), w = cc % (ub / 16);
-            const uint4 t = *reinterpret_cast<const uint4*>(src + (int64_t)(mb + m) * row_b + 16 * (int64_t)cc);
-            *reinterpret_cast<uint4*>(xl + ((int64_t)m * a.units + u) * st + 16 * w) = t;
+            const float4 t = *reinterpret_cast<const float4*>(a.x + (int64_t)(mb + m) * a.K + 4 * (int64_t)cc);
+            *reinterpret_cast<float4*>(xl + ((int64_t)m * a.units + u) * st + 16 * w) = t;
         }
-        if constexpr (MODE == MODE_B) {
-            const int nd = xd_per_row<FMT>(a.K), ns = xs_per_row<FMT>(a.K);
-            float* ld = reinterpret_cast<float*>(xl + xl_extra_off<FMT, MODE, MT>(a));
-            int32_t* ls = reinterpret_cast<int32_t*>(ld + MT * nd);
+        __syncthreads();
+    }
+    if constexpr (XL && MODE == MODE_B) {
+        constexpr int st = xl_stride<FMT, MODE>();
+        const int nd = xd_per_row<FMT>(a.K);
+        float* ld = reinterpret_cast<float*>(xl + xl_extra_off<FMT, MODE, MT>(a));
+        int32_t* ls = reinterpret_cast<int32_t*>(ld + MT * nd);
+        if (a.xq) {
+            // quantized by the separate launch: copied into their slots
+            constexpr int ub = F::UNIT;
+            const int per_row = a.units * (ub / 16), ns = xs_per_row<FMT>(a.K);
+            for (int c = threadIdx.x; c < mrows * per_row; c += EXT_THREADS) {
+                const int m = c / per_row, cc = c % per_row;
+                const int u = cc / (ub / 16), w = cc % (ub / 16);
+                const uint4 t = *reinterpret_cast<const uint4*>(a.xq + (int64_t)(mb + m) * a.K + 16 * (int64_t)cc);
+                *reinterpret_cast<uint4*>(xl + ((int64_t)m * a.units + u) * st + 16 * w) = t;
+            }
             for (int c = threadIdx.x; c < mrows * nd; c += EXT_THREADS) ld[c] = a.xd[(int64_t)mb * nd + c];
             for (int c = threadIdx.x; c < mrows * ns; c += EXT_THREADS) ls[c] = a.xs[(int64_t)mb * ns + c];
+        } else if constexpr (FMT == FMT_Q6_K) {
+            // quantized here, with the arithmetic of the standalone quantizer
+            // (so bit-identical to it).  Q8K: one wave per 256 values.
+            // Q8K: one wave per 256 values, four per lane
+            const int lane_ = threadIdx.x & 63, nsb = a.K / 256;
+            for (int blk = threadIdx.x >> 6; blk < mrows * nsb; blk += EXT_WAVES) {
+                const int m = blk / nsb, sb = blk % nsb;
+                const float4 xv = reinterpret_cast<const float4*>(a.x + (int64_t)(mb + m) * a.K + 256 * sb)[lane_];
+                const float v[4] = {xv.x, xv.y, xv.z, xv.w};
+                float d;
+                int q[4], s16;
+                q8k_wave(v, lane_, d, q, s16);
+                const int u = 8 * sb + (lane_ >> 3);  // the 32-value unit of elements 4*lane..4*lane+3
+                *reinterpret_cast<uint32_t*>(xl + ((int64_t)m * a.units + u) * st + 4 * (lane_ & 7)) =
+                    pack4(q[0], q[1], q[2], q[3]);
+                if (lane_ == 0) ld[m * nd + sb] = d;
+                if ((lane_ & 3) == 0) ls[m * (a.K / 16) + 16 * sb + (lane_ >> 2)] = s16;
+            }
+        } else {
+            // quantized here; Q8_0: one thread per 32 values
+            for (int blk = threadIdx.x; blk < mrows * nd; blk += EXT_THREADS) {
+                const int m = blk / nd, b = blk % nd;
+                float v[32];
+                load32(a.x + (int64_t)(mb + m) * a.K + 32 * b, v);
+                uint16_t dbits;
+                float dval;
+                int8_t q[32];
+                q8_0_block(v, dbits, dval, q);
+                int sum = 0;
+#pragma unroll
+                for (int j = 0; j < 32; ++j) sum += q[j];
+                uint4* o = reinterpret_cast<uint4*>(xl + ((int64_t)m * a.units + (b >> 1)) * st + 32 * (b & 1));
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    o[i] = make_uint4(pack4(q[16 * i], q[16 * i + 1], q[16 * i + 2], q[16 * i + 3]),
+                                      pack4(q[16 * i + 4], q[16 * i + 5], q[16 * i + 6], q[16 * i + 7]),
+                                      pack4(q[16 * i + 8], q[16 * i + 9], q[16 * i + 10], q[16 * i + 11]),
+                                      pack4(q[16 * i + 12], q[16 * i + 13], q[16 * i + 14], q[16 * i + 15]));
+                ld[m * nd + b] = dval;
+                ls[m * nd + b] = sum;
+            }
         }
         __syncthreads();
     }
@@ -687,15 +740,24 @@ static int ext_xl_bytes(int fmt, int mode, int units, int K, int mt)
     return bytes;
 }
 
+// Activation rows per launch row: mode (a) keeps the one- and eight-row
+// instances (the two- and four-row ones hold every decoded value and
+// activation at once and need over 200 registers).
+static int ext_mt(int mode, int M) { return M == 1 ? 1 : mode == MODE_A ? 8 : M == 2 ? 2 : M <= 4 ? 4 : 8; }
+
+// Whether a run stages its activations in LDS (and, in mode (b), quantizes
+// them there): not for the block-sums hook, nor when they exceed the LDS.
+static bool ext_staged(int fmt, int mode, int units, int K, int mt, bool hook)
+{
+    return !hook && ext_xl_bytes(fmt, mode, units, K, mt) <= EXT_XL_MAX;
+}
+
 // The decode kernel over activation rows m0.. in one launch per 65535 * MT rows.
 static hipError_t ext_gemv(int fmt, int mode, ExtArgs a, hipStream_t s)
 {
-    // activation rows per launch row: mode (a) keeps the one- and eight-row
-    // instances (the two- and four-row ones hold every decoded value and
-    // activation at once and need over 200 registers)
-    const int mt = a.M == 1 ? 1 : mode == MODE_A ? 8 : a.M == 2 ? 2 : a.M <= 4 ? 4 : 8;
+    const int mt = ext_mt(mode, a.M);
     const int lds = ext_xl_bytes(fmt, mode, a.units, a.K, mt);
-    const bool xl = lds <= EXT_XL_MAX && !a.sums;
+    const bool xl = ext_staged(fmt, mode, a.units, a.K, mt, a.sums != nullptr);
     int lg = 0;
     while ((1 << lg) < a.units && lg < 6) ++lg;
     a.lpr_log2 = lg;
@@ -741,6 +803,10 @@ hipError_t launch_ext_prep(int fmt, const float* x, int64_t M, int64_t K, const 
 hipError_t launch_ext_run(int fmt, int mode, const void* w, const float* x, int64_t N, int64_t K, int64_t M,
                           const ExtBufs& b, float* y, int32_t* sums, hipStream_t s)
 {
+    // mode (b) with one or two activation rows staged in LDS quantizes them
+    // inside the decode kernel (a.xq null); otherwise a separate launch
+    // writes them to the workspace first (with more rows every workgroup
+    // quantizing them all costs more than that launch)
     ExtArgs a{};
     a.w = (const uint8_t*)w;
     a.row_bytes = fmt == FMT_Q6_K ? (K / 256) * 210 : (K / 32) * ext_block_bytes(fmt);
@@ -755,8 +821,13 @@ hipError_t launch_ext_run(int fmt, int mode, const void* w, const float* x, int6
     a.M = (int)M;
     a.units = fmt == FMT_Q6_K ? (int)(K / 32) : (int)(K / 64);
     if (mode == MODE_B) {
-        const hipError_t e = launch_ext_prep(fmt, x, M, K, b, s);
-        if (e != hipSuccess) return e;
+        const int mt = ext_mt(mode, (int)M);
+        if (mt <= 2 && ext_staged(fmt, mode, a.units, (int)K, mt, sums != nullptr)) {
+            a.xq = nullptr;
+        } else {
+            const hipError_t e = launch_ext_prep(fmt, x, M, K, b, s);
+            if (e != hipSuccess) return e;
+        }
     }
     return ext_gemv(fmt, mode, a, s);
 }
