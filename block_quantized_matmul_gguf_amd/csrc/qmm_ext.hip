@@ -96,16 +96,23 @@ QMM_DEV void load_q(const int8_t* p, uint32_t out[8])
 
 // ------------------------------------------------------- decode kernel ----
 
+constexpr int EXT_GROUP_MAX = 4;  // problems per launch of a grouped run
+
 struct ExtArgs {
-    const uint8_t* w;
+    // problems sharing K, mode and the activations, their rows end to end:
+    // problem p holds rows row0[p] .. row0[p+1]-1 of the N, weights w[p],
+    // outputs y[p] [M][row0[p+1]-row0[p]]
+    const uint8_t* w[EXT_GROUP_MAX];
+    float* y[EXT_GROUP_MAX];
+    int row0[EXT_GROUP_MAX + 1];  // N <= 2^30
+    int groups;
     int64_t row_bytes;
     const float* x;    // f32 activations [M][K]
     const int8_t* xq;  // mode (b): quantized activations int8 [M][K] (null: quantized in the kernel)
     const float* xd;   //   their scales [M][K/32] (Q8_0) or [M][K/256] (Q8K)
     const int32_t* xs; //   sums of their values [M][K/32] (Q8_0) or [M][K/16] (Q8K bsums)
-    float* y;          // [M][N]
     int32_t* sums;     // block-sums hook (mode (b)): written instead of y when not null (HOOK instances)
-    int N, K, M, m0;   // this launch: activation rows m0 + MT*blockIdx.y .. + MT - 1 of M
+    int N, K, M, m0;   // N: rows of all problems; this launch: activation rows m0 + MT*blockIdx.y .. + MT - 1 of M
     int units;         // units per row
     int lpr_log2;      // log2 of the lanes per row
 };
@@ -228,6 +235,31 @@ QMM_DEV int xd_per_row(int K) { return FMT == FMT_Q6_K ? K / 256 : K / 32; }
 template <int FMT>
 QMM_DEV int xs_per_row(int K) { return FMT == FMT_Q6_K ? K / 16 : K / 32; }
 
+// The problem of global row n (0 <= n < N) and the row within it: a chain of
+// selects over the few problems, no indexed access to the argument arrays.
+QMM_DEV int ext_problem(const ExtArgs& a, int n)
+{
+    int p = 0;
+#pragma unroll
+    for (int q = 1; q < EXT_GROUP_MAX; ++q) p = (q < a.groups && n >= a.row0[q]) ? q : p;
+    return p;
+}
+template <typename T>
+QMM_DEV T ext_pick(T const (&arr)[EXT_GROUP_MAX], int p)
+{
+    T v = arr[0];
+#pragma unroll
+    for (int q = 1; q < EXT_GROUP_MAX; ++q) v = p == q ? arr[q] : v;
+    return v;
+}
+QMM_DEV int ext_row0(const ExtArgs& a, int p)  // 0 <= p <= groups
+{
+    int v = a.row0[0];
+#pragma unroll
+    for (int q = 1; q <= EXT_GROUP_MAX; ++q) v = p == q ? a.row0[q] : v;
+    return v;
+}
+
 // The arithmetic of one unit u of row n against activation rows mb ..
 // mb + mrows - 1: into acc, or (block-sums hook) into a.sums.
 template <int FMT, int MODE, int MT, bool XL, bool HOOK>
@@ -326,7 +358,7 @@ QMM_DEV void unit_math(const ExtArgs& a, const uint8_t* xl, const Raw<FMT>& w, i
 // writes the integer sums instead of y.
 constexpr int EXT_WAVES = 8, EXT_THREADS = 64 * EXT_WAVES;  // decode workgroup: eight waves share the staged activations
 
-template <int FMT, int MODE, int MT, bool XL, bool HOOK>
+template <int FMT, int MODE, int MT, bool XL, bool HOOK, bool GRP>
 __global__ __launch_bounds__(EXT_THREADS) void ext_gemv_kernel(ExtArgs a)
 {
     using F = Ext<FMT>;
@@ -417,7 +449,10 @@ __global__ __launch_bounds__(EXT_THREADS) void ext_gemv_kernel(ExtArgs a)
     for (int64_t g = (int64_t)blockIdx.x * EXT_WAVES + (threadIdx.x >> 6); g < groups; g += (int64_t)gridDim.x * EXT_WAVES) {
         const int64_t n = g * rpw + (lane >> a.lpr_log2);
         const bool live = n < a.N;
-        const uint8_t* row = a.w + (live ? n : 0) * a.row_bytes;
+        // GRP: the row's problem (a single-problem launch skips the lookup)
+        const int p = GRP ? ext_problem(a, live ? (int)n : 0) : 0;
+        const int ln = (live ? (int)n : 0) - (GRP ? ext_row0(a, p) : 0);  // row within its problem
+        const uint8_t* row = (GRP ? ext_pick(a.w, p) : a.w[0]) + (int64_t)ln * a.row_bytes;
 
         float acc[MT];
 #pragma unroll
@@ -433,7 +468,10 @@ __global__ __launch_bounds__(EXT_THREADS) void ext_gemv_kernel(ExtArgs a)
         for (int m = 0; m < MT; ++m) {
             float t = acc[m];
             for (int off = L >> 1; off > 0; off >>= 1) t += __shfl_xor(t, off);
-            if (live && sub == 0 && m < mrows) a.y[(int64_t)(mb + m) * a.N + n] = t;
+            if (live && sub == 0 && m < mrows) {
+                if constexpr (GRP) ext_pick(a.y, p)[(int64_t)(mb + m) * (ext_row0(a, p + 1) - ext_row0(a, p)) + ln] = t;
+                else a.y[0][(int64_t)(mb + m) * a.N + ln] = t;
+            }
         }
     }
 }
@@ -691,29 +729,35 @@ int64_t ext_block_bytes(int fmt) { return fmt == FMT_Q4_0 ? 18 : fmt == FMT_Q5_0
 
 constexpr int EXT_XL_MAX = 160 * 1024;  // LDS of a compute unit; above it the kernel reads activations from global memory
 
+template <int FMT, int MODE, int MT, bool GRP>
+static void launch_staged(const ExtArgs& a, dim3 grid, dim3 block, int lds, hipStream_t s)
+{
+    if (lds > 64 * 1024) {
+        // above the default dynamic LDS limit: raised once per kernel (the
+        // call is host-side, before any capture of a run)
+        static const hipError_t raised = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&ext_gemv_kernel<FMT, MODE, MT, true, false, GRP>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, EXT_XL_MAX);
+        (void)raised;
+    }
+    hipLaunchKernelGGL((ext_gemv_kernel<FMT, MODE, MT, true, false, GRP>), grid, block, lds, s, a);
+}
+
+// Grouped launches (a.groups > 1) always stage their activations (the host
+// groups only runs that do).
 template <int FMT, int MODE, int MT>
 static void launch_one(bool xl, const ExtArgs& a, unsigned gx, unsigned gy, int lds, hipStream_t s)
 {
     const dim3 grid(gx, gy), block(EXT_THREADS);
     if constexpr (MODE == MODE_B) {
         if (a.sums) {  // the block-sums hook: activations from global memory
-            hipLaunchKernelGGL((ext_gemv_kernel<FMT, MODE, MT, false, true>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((ext_gemv_kernel<FMT, MODE, MT, false, true, false>), grid, block, 0, s, a);
             return;
         }
     }
-    if (xl) {
-        if (lds > 64 * 1024) {
-            // above the default dynamic LDS limit: raised once per kernel (the
-            // call is host-side, before any capture of a run)
-            static const hipError_t raised = hipFuncSetAttribute(
-                reinterpret_cast<const void*>(&ext_gemv_kernel<FMT, MODE, MT, true, false>),
-                hipFuncAttributeMaxDynamicSharedMemorySize, EXT_XL_MAX);
-            (void)raised;
-        }
-        hipLaunchKernelGGL((ext_gemv_kernel<FMT, MODE, MT, true, false>), grid, block, lds, s, a);
-    } else {
-        hipLaunchKernelGGL((ext_gemv_kernel<FMT, MODE, MT, false, false>), grid, block, 0, s, a);
-    }
+    if (a.groups > 1) launch_staged<FMT, MODE, MT, true>(a, grid, block, lds, s);
+    else if (xl) launch_staged<FMT, MODE, MT, false>(a, grid, block, lds, s);
+    else hipLaunchKernelGGL((ext_gemv_kernel<FMT, MODE, MT, false, false, false>), grid, block, 0, s, a);
 }
 
 template <int FMT, int MODE>
@@ -808,13 +852,16 @@ hipError_t launch_ext_run(int fmt, int mode, const void* w, const float* x, int6
     // writes them to the workspace first (with more rows every workgroup
     // quantizing them all costs more than that launch)
     ExtArgs a{};
-    a.w = (const uint8_t*)w;
+    a.w[0] = (const uint8_t*)w;
+    a.y[0] = y;
+    a.row0[0] = 0;
+    for (int p = 1; p <= EXT_GROUP_MAX; ++p) a.row0[p] = (int)N;
+    a.groups = 1;
     a.row_bytes = fmt == FMT_Q6_K ? (K / 256) * 210 : (K / 32) * ext_block_bytes(fmt);
     a.x = x;
     a.xq = b.xq;
     a.xd = b.xd;
     a.xs = b.xs;
-    a.y = y;
     a.sums = sums;
     a.N = (int)N;
     a.K = (int)K;
@@ -823,6 +870,58 @@ hipError_t launch_ext_run(int fmt, int mode, const void* w, const float* x, int6
     if (mode == MODE_B) {
         const int mt = ext_mt(mode, (int)M);
         if (mt <= 2 && ext_staged(fmt, mode, a.units, (int)K, mt, sums != nullptr)) {
+            a.xq = nullptr;
+        } else {
+            const hipError_t e = launch_ext_prep(fmt, x, M, K, b, s);
+            if (e != hipSuccess) return e;
+        }
+    }
+    return ext_gemv(fmt, mode, a, s);
+}
+
+int ext_group_max() { return EXT_GROUP_MAX; }
+
+bool ext_group_supported(int fmt, int mode, int64_t K, int64_t M)
+{
+    if (mode != MODE_A && mode != MODE_B) return false;
+    if (M < 1 || M > GEMV_MAX_M) return false;
+    const int units = fmt == FMT_Q6_K ? (int)(K / 32) : (int)(K / 64);
+    return ext_staged(fmt, mode, units, (int)K, ext_mt(mode, (int)M), false);
+}
+
+// Up to EXT_GROUP_MAX problems sharing K, mode and x in one launch (their
+// rows end to end); each row's arithmetic is that of a separate run.  b: the
+// workspace of the first problem's plan (the activations are shared).
+hipError_t launch_ext_group(int fmt, int mode, int count, const void* const* w, const int64_t* Ns, float* const* y,
+                            const float* x, int64_t K, int64_t M, const ExtBufs& b, hipStream_t s)
+{
+    ExtArgs a{};
+    int64_t rows = 0;
+    for (int p = 0; p < count; ++p) {
+        a.w[p] = (const uint8_t*)w[p];
+        a.y[p] = y[p];
+        a.row0[p] = (int)rows;
+        rows += Ns[p];
+    }
+    for (int p = count; p <= EXT_GROUP_MAX; ++p) a.row0[p] = (int)rows;
+    for (int p = count; p < EXT_GROUP_MAX; ++p) {
+        a.w[p] = a.w[0];
+        a.y[p] = a.y[0];
+    }
+    a.groups = count;
+    a.row_bytes = fmt == FMT_Q6_K ? (K / 256) * 210 : (K / 32) * ext_block_bytes(fmt);
+    a.x = x;
+    a.xq = b.xq;
+    a.xd = b.xd;
+    a.xs = b.xs;
+    a.sums = nullptr;
+    a.N = (int)rows;
+    a.K = (int)K;
+    a.M = (int)M;
+    a.units = fmt == FMT_Q6_K ? (int)(K / 32) : (int)(K / 64);
+    if (mode == MODE_B) {
+        const int mt = ext_mt(mode, (int)M);
+        if (mt <= 2 && ext_staged(fmt, mode, a.units, (int)K, mt, false)) {
             a.xq = nullptr;
         } else {
             const hipError_t e = launch_ext_prep(fmt, x, M, K, b, s);

@@ -90,6 +90,12 @@ int64_t ext_block_bytes(int fmt);
 hipError_t launch_ext_prep(int fmt, const float* x, int64_t M, int64_t K, const ExtBufs& b, hipStream_t s);
 hipError_t launch_ext_run(int fmt, int mode, const void* w, const float* x, int64_t N, int64_t K, int64_t M,
                           const ExtBufs& b, float* y, int32_t* sums, hipStream_t s);
+// Grouped decode (M <= 8): up to ext_group_max() problems sharing K, mode and
+// x in one launch; b is the first problem's workspace.
+int ext_group_max();
+bool ext_group_supported(int fmt, int mode, int64_t K, int64_t M);  // the activations fit in LDS
+hipError_t launch_ext_group(int fmt, int mode, int count, const void* const* w, const int64_t* Ns, float* const* y,
+                            const float* x, int64_t K, int64_t M, const ExtBufs& b, hipStream_t s);
 hipError_t launch_ext_to_q8_0(int fmt, const void* w, int64_t N, int64_t K, void* out, hipStream_t s);
 hipError_t launch_ext_dequantize(int fmt, const void* w, int64_t N, int64_t K, float* out, hipStream_t s);
 hipError_t launch_ext_quantize_weights(int fmt, const float* w, int64_t N, int64_t K, void* out, hipStream_t s);

@@ -123,11 +123,13 @@ int qmatmul_run(const qmm_plan* plan, const void* w_blocks, const float* x, floa
  * (page "同一个 GGUF，CPU 和 Metal 生成的文字不一样", section 出处).  plans,
  * w_blocks and y are host arrays of count entries (1 <= count <=
  * QMM_GROUP_MAX) holding each plan's device pointers, with qmatmul_run's
- * sizes and alignment; 0 <= M <= every plan's M_max.  At M == 1, where the
- * one-row decode kernel takes the rows, the plans' rows go to one launch per
- * four plans (the activations are loaded and quantized once per workgroup for
- * all of them), giving bit-for-bit the values separate one-row runs give;
- * otherwise the plans run one after another as with qmatmul_run.  Errors: as
+ * sizes and alignment; 0 <= M <= every plan's M_max.  At M == 1 for Q8_0 and
+ * Q4_K (where the one-row decode kernel takes the rows), and at M <= 8 for
+ * Q4_0, Q5_0 and Q6_K (where their activations fit in LDS), the plans' rows
+ * go to one launch per four plans (the activations are loaded and quantized
+ * once per workgroup for all of them), giving bit-for-bit the values
+ * separate runs give; otherwise the plans run one after another as with
+ * qmatmul_run.  Errors: as
  * qmatmul_run for each plan, and QMM_EINVAL for null arrays, count out of
  * range or plans that differ in format, K or mode.
  */

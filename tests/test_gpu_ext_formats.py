@@ -214,3 +214,34 @@ def test_long_rows(fmt, n, k, mode, m):
     y = run(fmt, mode, wq, n, k, x)
     yr, a = ref(fmt, mode, wq, n, k, x)
     assert_within(y, yr, a, f"{NAME[fmt]} {n}x{k} M={m} mode={mode}")
+
+
+# Grouped runs: up to four plans sharing format, K, mode and x in one decode
+# launch, their rows end to end; each output must equal its separate run bit
+# for bit (the same per-row arithmetic), and the oracle within the bar.
+GROUPS = [
+    (qmm.Q5_0, 576, [576, 192, 192]),            # q, k, v of a SmolLM2 layer in the page's Q4K file
+    (qmm.Q5_0, 576, [1536, 1536]),               # gate, up
+    (qmm.Q4_0, 1536, [96, 200, 64, 130, 50]),    # five plans: two launches
+    (qmm.Q6_K, 768, [45, 70]),                   # misaligned super-blocks
+]
+
+
+@pytest.mark.parametrize("m", [1, 3, 8])
+@pytest.mark.parametrize("mode", MODES, ids=["a", "b"])
+@pytest.mark.parametrize("fmt,k,ns", GROUPS, ids=[f"{NAME[f]}-{k}-{len(ns)}" for f, k, ns in GROUPS])
+def test_grouped_run_equals_separate_runs(fmt, k, ns, mode, m):
+    x = synth.acts_f32(8300 + k + m, m, k)
+    wqs = [oracle.quantize(fmt, synth.weights_f32(8400 + i + n, n, k)) for i, n in enumerate(ns)]
+    plans = [qmm.Plan(fmt, n, k, 8, mode) for n in ns]
+    try:
+        xg, wg = dev(x), [dev(w) for w in wqs]
+        sep = [host(p.run(w, xg)) for p, w in zip(plans, wg)]
+        grp = [host(y) for y in qmm.run_group(plans, wg, xg)]
+    finally:
+        for p in plans:
+            p.close()
+    for i, (n, wq) in enumerate(zip(ns, wqs)):
+        assert np.array_equal(grp[i], sep[i]), f"plan {i} ({n} rows)"
+        yr, a = ref(fmt, mode, wq, n, k, x)
+        assert_within(grp[i], yr, a, f"group plan {i} {NAME[fmt]} {n}x{k} M={m} mode={mode}")
