@@ -150,6 +150,10 @@ static size_t layout(qmm_plan* p, char* base)
             p->ex.xd = (float*)take(4 * (size_t)Mx * (q6 ? K / 256 : K / 32));
             p->ex.xs = (int32_t*)take(4 * (size_t)Mx * (q6 ? K / 16 : K / 32));
         }
+        if (q6 && a && p->M_max > GEMV_MAX_M) {
+            // Q6_K mode (a) prefill: the weights decoded to f32, then the f32 GEMM
+            p->wdeq = (float*)take(4 * (size_t)N * K);
+        }
         if (pre) {
             p->ex.tw = (uint8_t*)take((size_t)N * (K / 32) * 34);
             const int64_t M = p->M_max;
@@ -219,7 +223,8 @@ extern "C" int qmatmul_create(qmm_plan** out, int format, int64_t N, int64_t K, 
                     hipGetErrorString(e));
     }
     layout(p, (char*)p->ws);
-    if (mode == QMM_MODE_DEQUANT && dense_create(&p->dense) != 0) {
+    const bool dense = mode == QMM_MODE_DEQUANT || (format == QMM_Q6_K && mode == QMM_MODE_F32ACT && M_max > GEMV_MAX_M);
+    if (dense && dense_create(&p->dense) != 0) {
         (void)hipFree(p->ws);
         delete p;
         return fail(QMM_EHIP, "rocblas_create_handle failed");
@@ -264,6 +269,14 @@ static int run_impl(const qmm_plan* p, const void* w, const float* x, float* y, 
     if (p->mode == QMM_MODE_DEQUANT) {
         e = is_ext_format(p->fmt) ? launch_ext_dequantize(p->fmt, w, p->N, p->K, p->wdeq, s)
                                   : launch_dequantize(p->fmt, w, p->N, p->K, p->wdeq, s);
+        if (e != hipSuccess) return fail(QMM_EHIP, "kernel launch: %s", hipGetErrorString(e));
+        const int st = dense_gemm(p->dense, p->wdeq, x, y, M, p->N, p->K, s);
+        if (st != 0) return fail(QMM_EHIP, "rocblas_sgemm: status %d", st);
+        return QMM_OK;
+    }
+    if (p->fmt == QMM_Q6_K && p->mode == QMM_MODE_F32ACT && M > GEMV_MAX_M && sums == nullptr) {
+        // mode (a) prefill: the f32 product of the exactly decoded weights
+        e = launch_ext_dequantize(p->fmt, w, p->N, p->K, p->wdeq, s);
         if (e != hipSuccess) return fail(QMM_EHIP, "kernel launch: %s", hipGetErrorString(e));
         const int st = dense_gemm(p->dense, p->wdeq, x, y, M, p->N, p->K, s);
         if (st != 0) return fail(QMM_EHIP, "rocblas_sgemm: status %d", st);

@@ -106,12 +106,15 @@ int qmatmul_create(qmm_plan** out, int format, int64_t N, int64_t K, int64_t M_m
  * is shared by its runs: do not run one plan concurrently on two streams.
  * Q4_0 and Q5_0 runs with M > 8 first rewrite the weights as Q8_0 blocks
  * (the same dequantized values) in the plan's workspace and take the Q8_0
- * prefill kernels; Q6_K runs with M > 8 take the decode kernels eight
- * activation rows at a time (correct, not tuned for throughput).
+ * prefill kernels; Q6_K runs with M > 8 decode the weights to f32 in the
+ * workspace (N*K*4 bytes) and take the library f32 GEMM in mode (a), and take
+ * the decode kernels eight activation rows at a time in mode (b) (correct,
+ * not tuned for throughput).
  * A run only enqueues kernels (no allocation, memset or synchronization), so
  * runs may be captured in a HIP graph once each kernel has run eagerly (its
- * launch attributes are set on first use); the exception is a
- * QMM_MODE_DEQUANT plan at M > 8, whose product is a rocBLAS call.
+ * launch attributes are set on first use); the exceptions are a
+ * QMM_MODE_DEQUANT plan and a Q6_K mode (a) plan at M > 8, whose product is a
+ * rocBLAS call.
  */
 int qmatmul_run(const qmm_plan* plan, const void* w_blocks, const float* x, float* y,
                 int64_t M, void* stream);
