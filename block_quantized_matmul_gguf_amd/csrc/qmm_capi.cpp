@@ -283,7 +283,9 @@ static int run_impl(const qmm_plan* p, const void* w, const float* x, float* y, 
         return QMM_OK;
     }
     if (is_ext_format(p->fmt)) {
-        if (M <= GEMV_MAX_M || p->fmt == QMM_Q6_K) {
+        if (M == 1 && sums == nullptr && gemv_row_supported(p->fmt, p->mode, 1, p->N, p->K, false)) {
+            e = launch_gemv_row(p->fmt, p->mode, w, x, p->N, p->K, y, s);  // Q4_0, Q5_0: the one-row kernel
+        } else if (M <= GEMV_MAX_M || p->fmt == QMM_Q6_K) {
             e = launch_ext_run(p->fmt, p->mode, w, x, p->N, p->K, M, p->ex, y, sums, s);
         } else {
             e = launch_ext_to_q8_0(p->fmt, w, p->N, p->K, p->ex.tw, s);
@@ -325,23 +327,6 @@ extern "C" int qmatmul_run_group(const qmm_plan* const* plans, int count, const 
     if (M == 0) return QMM_OK;
     const qmm_plan* p0 = plans[0];
     const hipStream_t s = (hipStream_t)stream;
-    if (is_ext_format(p0->fmt) && ext_group_supported(p0->fmt, p0->mode, p0->K, M)) {
-        // Q4_0, Q5_0, Q6_K decode: one launch per ext_group_max() plans
-        int64_t total = 0;
-        for (int i = 0; i < count; ++i) total += plans[i]->N;
-        if (total <= (1ll << 30)) {
-            const int gmax = ext_group_max();
-            for (int i = 0; i < count; i += gmax) {
-                const int c = count - i < gmax ? count - i : gmax;
-                int64_t Ns[QMM_GROUP_MAX];
-                for (int j = 0; j < c; ++j) Ns[j] = plans[i + j]->N;
-                const hipError_t e =
-                    launch_ext_group(p0->fmt, p0->mode, c, w + i, Ns, y + i, x, p0->K, M, plans[i]->ex, s);
-                if (e != hipSuccess) return fail(QMM_EHIP, "kernel launch: %s", hipGetErrorString(e));
-            }
-            return QMM_OK;
-        }
-    }
     if (M == 1 && p0->mode != QMM_MODE_DEQUANT) {
         // one launch per gemv_row_group_max() plans, when the one-row kernel takes their rows
         int64_t total = 0;
@@ -353,6 +338,29 @@ extern "C" int qmatmul_run_group(const qmm_plan* const* plans, int count, const 
                 int64_t Ns[QMM_GROUP_MAX];
                 for (int j = 0; j < c; ++j) Ns[j] = plans[i + j]->N;
                 const hipError_t e = launch_gemv_row_group(p0->fmt, p0->mode, c, w + i, Ns, y + i, x, p0->K, s);
+                if (e != hipSuccess) return fail(QMM_EHIP, "kernel launch: %s", hipGetErrorString(e));
+            }
+            return QMM_OK;
+        }
+    }
+    if (is_ext_format(p0->fmt) && ext_group_supported(p0->fmt, p0->mode, p0->K, M)) {
+        // Q4_0, Q5_0, Q6_K decode: one launch per ext_group_max() plans, unless
+        // a plan's separate run would take the one-row kernel (the grouped
+        // values must be those of the separate runs)
+        int64_t total = 0;
+        bool row_alone = false;
+        for (int i = 0; i < count; ++i) {
+            total += plans[i]->N;
+            row_alone = row_alone || (M == 1 && gemv_row_supported(p0->fmt, p0->mode, 1, plans[i]->N, p0->K, false));
+        }
+        if (total <= (1ll << 30) && !row_alone) {
+            const int gmax = ext_group_max();
+            for (int i = 0; i < count; i += gmax) {
+                const int c = count - i < gmax ? count - i : gmax;
+                int64_t Ns[QMM_GROUP_MAX];
+                for (int j = 0; j < c; ++j) Ns[j] = plans[i + j]->N;
+                const hipError_t e =
+                    launch_ext_group(p0->fmt, p0->mode, c, w + i, Ns, y + i, x, p0->K, M, plans[i]->ex, s);
                 if (e != hipSuccess) return fail(QMM_EHIP, "kernel launch: %s", hipGetErrorString(e));
             }
             return QMM_OK;

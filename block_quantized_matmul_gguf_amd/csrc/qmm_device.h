@@ -132,6 +132,59 @@ QMM_DEV void q4k_scale_min(uint32_t s0, uint32_t s1, uint32_t s2, int j, int& sc
     }
 }
 
+// Q4_0 / Q5_0 (page "自己量化": 18 and 22 bytes per 32 values; the public GGUF
+// layout: f16 d, Q5_0's u32 of fifth bits, 16 bytes of nibbles with element
+// j < 16 in the low nibble of byte j and element j + 16 in its high nibble).
+// Bits 0..3 of h, one per byte, moved to bit 4 of bytes 0..3.
+QMM_DEV uint32_t spread4(uint32_t h) { return ((h * 0x00204081u) & 0x01010101u) << 4; }
+
+// Codes (0..15 or 0..31), one per byte, of one 32-value block: v[t] holds
+// elements 4t..4t+3.  qs: the 16 nibble bytes; qh: Q5_0's fifth bits.
+template <int FMT>
+QMM_DEV void block_codes(const uint32_t qs[4], uint32_t qh, uint32_t v[8])
+{
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        v[t] = qs[t] & 0x0f0f0f0fu;
+        v[4 + t] = (qs[t] >> 4) & 0x0f0f0f0fu;
+    }
+    if constexpr (FMT == qmm::FMT_Q5_0) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) v[t] |= spread4((qh >> (4 * t)) & 15u);
+    }
+}
+
+// Codes and scales of a 4-byte-aligned pair of Q4_0 (9 dwords) or Q5_0 (11
+// dwords) blocks held in r: the first block's fields start two bytes into a
+// dword and are realigned by a byte shift, the second block's nibbles are
+// dword-aligned.
+template <int FMT>
+QMM_DEV void pair_codes(const uint32_t* r, uint32_t v[2][8], float d[2])
+{
+    uint32_t a[4], b[4];
+    if constexpr (FMT == qmm::FMT_Q4_0) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            a[t] = __builtin_amdgcn_alignbyte(r[t + 1], r[t], 2);  // bytes 2..17
+            b[t] = r[5 + t];                                       // bytes 20..35
+        }
+        d[0] = f16lo(r[0]);
+        d[1] = f16hi(r[4]);
+        block_codes<FMT>(a, 0u, v[0]);
+        block_codes<FMT>(b, 0u, v[1]);
+    } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            a[t] = __builtin_amdgcn_alignbyte(r[t + 2], r[t + 1], 2);  // bytes 6..21
+            b[t] = r[7 + t];                                           // bytes 28..43
+        }
+        d[0] = f16lo(r[0]);
+        d[1] = f16hi(r[5]);
+        block_codes<FMT>(a, __builtin_amdgcn_alignbyte(r[1], r[0], 2), v[0]);  // bytes 2..5
+        block_codes<FMT>(b, r[6], v[1]);                                        // bytes 24..27
+    }
+}
+
 // Q8_0 GEMV block-pair k permutation.  Inside a 4-byte-aligned pair of
 // blocks (68 bytes), lane group g (0..3) of the MFMA operand takes the 8
 // weight bytes at dwords (1+2g, 2+2g) of the even block; group 3 takes dword

@@ -38,25 +38,6 @@ struct Ext<FMT_Q6_K> {
     static constexpr int BYTES = 210, OFF = 32, UNIT = 32;  // a unit is a 32-value piece of a super-block
 };
 
-// Bits 0..3 of h, one per byte, moved to bit 4 of bytes 0..3.
-QMM_DEV uint32_t spread4(uint32_t h) { return ((h * 0x00204081u) & 0x01010101u) << 4; }
-
-// Codes (0..2*OFF-1), one per byte, of one 32-value block: v[t] holds
-// elements 4t..4t+3.  qs: the 16 nibble bytes; qh: Q5_0's fifth bits.
-template <int FMT>
-QMM_DEV void block_codes(const uint32_t qs[4], uint32_t qh, uint32_t v[8])
-{
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        v[t] = qs[t] & 0x0f0f0f0fu;
-        v[4 + t] = (qs[t] >> 4) & 0x0f0f0f0fu;
-    }
-    if constexpr (FMT == FMT_Q5_0) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) v[t] |= spread4((qh >> (4 * t)) & 15u);
-    }
-}
-
 // sum over a block of (code - off) * x, the codes converted exactly.
 template <int NT>
 QMM_DEV float dot_codes_f32(const uint32_t* v, const float* x, float off)
@@ -197,33 +178,11 @@ QMM_DEV void q6k_decode(const Raw<FMT_Q6_K>& w, int pc, uint32_t v[8], int& sc0,
     d = (float)__builtin_bit_cast(_Float16, (uint16_t)((w.dw >> (8 * w.sh)) & 0xffffu));
 }
 
-// Codes and scales of a pair of Q4_0 / Q5_0 blocks (4-byte aligned).
+// Codes and scales of a pair of Q4_0 / Q5_0 blocks from its raw dwords.
 template <int FMT>
 QMM_DEV void pair_decode(const Raw<FMT>& w, uint32_t v[2][8], float d[2])
 {
-    const uint32_t* r = w.r;
-    uint32_t a[4], b[4];
-    if constexpr (FMT == FMT_Q4_0) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            a[t] = __builtin_amdgcn_alignbyte(r[t + 1], r[t], 2);  // bytes 2..17
-            b[t] = r[5 + t];                                       // bytes 20..35
-        }
-        d[0] = f16lo(r[0]);
-        d[1] = f16hi(r[4]);
-        block_codes<FMT>(a, 0u, v[0]);
-        block_codes<FMT>(b, 0u, v[1]);
-    } else {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            a[t] = __builtin_amdgcn_alignbyte(r[t + 2], r[t + 1], 2);  // bytes 6..21
-            b[t] = r[7 + t];                                           // bytes 28..43
-        }
-        d[0] = f16lo(r[0]);
-        d[1] = f16hi(r[5]);
-        block_codes<FMT>(a, __builtin_amdgcn_alignbyte(r[1], r[0], 2), v[0]);  // bytes 2..5
-        block_codes<FMT>(b, r[6], v[1]);                                        // bytes 24..27
-    }
+    pair_codes<FMT>(w.r, v, d);
 }
 
 // Mode (b) LDS layout after the activation slots of MT rows: the block

@@ -245,3 +245,19 @@ def test_grouped_run_equals_separate_runs(fmt, k, ns, mode, m):
         assert np.array_equal(grp[i], sep[i]), f"plan {i} ({n} rows)"
         yr, a = ref(fmt, mode, wq, n, k, x)
         assert_within(grp[i], yr, a, f"group plan {i} {NAME[fmt]} {n}x{k} M={m} mode={mode}")
+
+
+# M = 1 on the one-row kernel (Q4_0, Q5_0): rows of one to four 64-pair
+# segments, short last segments, and (mode (a)) past its one-segment limit.
+ROW_K = [(f, k) for f in (qmm.Q4_0, qmm.Q5_0) for k in (64, 960, 2048, 4096, 4160, 8192, 12352, 16384)]
+
+
+@pytest.mark.parametrize("mode", MODES, ids=["a", "b"])
+@pytest.mark.parametrize("fmt,k", ROW_K, ids=[f"{NAME[f]}-{k}" for f, k in ROW_K])
+def test_single_row_decode_row_lengths(fmt, k, mode):
+    n = 300
+    wq = oracle.quantize(fmt, synth.weights_f32(8500 + k, n, k))
+    x = synth.acts_f32(8501 + k, 1, k)
+    y = run(fmt, mode, wq, n, k, x)
+    yr, a = ref(fmt, mode, wq, n, k, x)
+    assert_within(y, yr, a, f"{NAME[fmt]} {n}x{k} M=1 mode={mode}")
