@@ -18,6 +18,9 @@
 // Mode (b) pairs Q4_0 and Q5_0 with Q8_0 activations and Q6_K with Q8K (page
 // "同一个 GGUF，CPU 和 Metal 生成的文字不一样", section 出处).
 #include <algorithm>
+#include <mutex>
+#include <set>
+#include <utility>
 
 #include "qmm_act.h"
 
@@ -688,17 +691,25 @@ int64_t ext_block_bytes(int fmt) { return fmt == FMT_Q4_0 ? 18 : fmt == FMT_Q5_0
 
 constexpr int EXT_XL_MAX = 160 * 1024;  // LDS of a compute unit; above it the kernel reads activations from global memory
 
+// Dynamic LDS above the default 64 KB: the kernel's limit raised once per
+// device (host-side, before any capture of a run).
+static void ext_allow_lds(const void* kernel)
+{
+    static std::set<std::pair<int, const void*>> done;
+    static std::mutex mu;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    std::lock_guard<std::mutex> lock(mu);
+    if (done.insert(std::make_pair(dev, kernel)).second) {
+        (void)hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, EXT_XL_MAX);
+        (void)hipGetLastError();
+    }
+}
+
 template <int FMT, int MODE, int MT, bool GRP>
 static void launch_staged(const ExtArgs& a, dim3 grid, dim3 block, int lds, hipStream_t s)
 {
-    if (lds > 64 * 1024) {
-        // above the default dynamic LDS limit: raised once per kernel (the
-        // call is host-side, before any capture of a run)
-        static const hipError_t raised = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&ext_gemv_kernel<FMT, MODE, MT, true, false, GRP>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, EXT_XL_MAX);
-        (void)raised;
-    }
+    if (lds > 64 * 1024) ext_allow_lds(reinterpret_cast<const void*>(&ext_gemv_kernel<FMT, MODE, MT, true, false, GRP>));
     hipLaunchKernelGGL((ext_gemv_kernel<FMT, MODE, MT, true, false, GRP>), grid, block, lds, s, a);
 }
 
