@@ -152,7 +152,8 @@ int qmatmul_destroy(qmm_plan* plan);
  * qmatmul_dequantize_weights: GGUF blocks (device, N * qmatmul_row_bytes(format,
  * K) bytes, 16-byte aligned) -> f32 [N x K] (device, 16-byte aligned, caller
  * owned).  Every value is the exact dequantized weight (Q8_0 d*q; Q4_K
- * d*sc_j*q - dmin*m_j) rounded once to f32.
+ * d*sc_j*q - dmin*m_j; Q4_0 d*(q-8); Q5_0 d*(q-16); Q6_K d*sc*(q-32)) rounded
+ * once to f32.  Q4_0 and Q5_0 need K divisible by 64 (QMM_EUNSUPPORTED).
  *
  * qmatmul_run_dequantized (QMM_MODE_DEQUANT plans only): y = x . W^T with W
  * given as that f32 [N x K] matrix; x, y as in qmatmul_run.  The product is the

@@ -22,12 +22,16 @@ def _gpu():
 
 
 CASES = [(qmm.Q8_0, qmm.MODE_F32ACT, 1), (qmm.Q8_0, qmm.MODE_QACT, 8), (qmm.Q4_K, qmm.MODE_QACT, 1),
-         (qmm.Q8_0, qmm.MODE_QACT, 96), (qmm.Q4_K, qmm.MODE_F32ACT, 96), (qmm.Q8_0, qmm.MODE_DEQUANT, 4)]
+         (qmm.Q8_0, qmm.MODE_QACT, 96), (qmm.Q4_K, qmm.MODE_F32ACT, 96), (qmm.Q8_0, qmm.MODE_DEQUANT, 4),
+         # the other formats: one-row kernel, staged decode (in-kernel and separate activation
+         # quantization), the Q8_0 rewrite for the prefill, Q6_K's eight-row launches
+         (qmm.Q5_0, qmm.MODE_QACT, 1), (qmm.Q5_0, qmm.MODE_F32ACT, 1), (qmm.Q4_0, qmm.MODE_QACT, 8),
+         (qmm.Q4_0, qmm.MODE_F32ACT, 96), (qmm.Q6_K, qmm.MODE_QACT, 1), (qmm.Q6_K, qmm.MODE_QACT, 12)]
 
 
 @pytest.mark.parametrize("fmt,mode,m", CASES, ids=[f"fmt{f}-mode{md}-M{m}" for f, md, m in CASES])
 def test_graph_replays_match_eager_runs(fmt, mode, m):
-    n, k = 640, 1536 if fmt == qmm.Q4_K else 576
+    n, k = 640, 1536 if fmt in (qmm.Q4_K, qmm.Q6_K) else 576
     dev = torch.device("cuda")
     w = [torch.from_numpy(oracle.quantize(fmt, synth.weights_f32(7000 + i, n, k))).to(dev) for i in range(3)]
     x = torch.from_numpy(synth.acts_f32(7100 + m, m, k)).to(dev)
