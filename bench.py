@@ -21,7 +21,10 @@ host's threads, reported in the same unit.
 Context, outside the step and the value: the dequantize-all form (weights
 decoded to f32 once, then the library f32 GEMM), timed on the same layers and
 M, as the page "同一个 GGUF，CPU 和 Metal 生成的文字不一样" (section 修法)
-compares it with the quantized forms.
+compares it with the quantized forms; and the decode (M = 1 and 8, both
+modes) of the same layers in the other formats of the pages' files (Q4_0,
+Q5_0, Q6_K: the page "自己量化" quantizes to Q4_0 and falls back to Q5_0, the
+downloaded file holds Q6K tensors).
 """
 import argparse
 import hashlib
@@ -49,6 +52,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-layers", type=int, default=LAYERS, help="layers in the CPU-baseline sample")
     p.add_argument("--no-dequant", action="store_true", help="skip the dequantize-all context rows")
+    p.add_argument("--no-other-formats", action="store_true", help="skip the Q4_0/Q5_0/Q6_K decode context rows")
     p.add_argument("--workload", default="c5", choices=["c1", "c2", "c3", "c4", "c5", "c6"],
                    help="c5 (default): the step above.  c1-c4: the pages' smaller workloads as context lines "
                         "(q_proj GEMV, lm_head GEMV warm and cold, ffn_down Q4_K at M=1 and 37, the 30-layer "
@@ -119,6 +123,35 @@ def cpu_baseline(layers, min_seconds=10.0):
                   f"modes a and b, N=14336 K=4096), repeated {reps} times: {total_bytes / 1e9:.2f} GB of weight "
                   f"blocks in {total_s:.1f} s",
     }
+
+
+def other_formats_decode(qmm, torch, wq, others, modes, xs, ys, stream, args):
+    """Decode (M = 1 and 8) of the same 8 layers in Q4_0, Q5_0 and Q6_K (the
+    other formats of the pages' files), both modes, layers rotated (HBM
+    streams), HIP events on the launch stream; per launch = group time /
+    launches.  Context beside the step, not part of its value."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    rows = []
+    for f, code in others.items():
+        b = wq[f][0].numel()
+        for md, mcode in modes.items():
+            with qmm.Plan(code, N, K, max(DECODE_M), mcode) as plan:
+                for m in DECODE_M:
+                    for _ in range(max(1, args.warmup)):
+                        for l in range(LAYERS):
+                            plan.run(wq[f][l], xs[m], ys[m], stream)
+                    torch.cuda.synchronize()
+                    ev[0].record(stream)
+                    for _ in range(args.steps):
+                        for l in range(LAYERS):
+                            plan.run(wq[f][l], xs[m], ys[m], stream)
+                    ev[1].record(stream)
+                    torch.cuda.synchronize()
+                    us = ev[0].elapsed_time(ev[1]) * 1000.0 / (args.steps * LAYERS)
+                    rows.append({"fmt": f, "mode": md, "M": m, "us_per_launch": round(us, 3),
+                                 "weight_GBps": round(b / (us * 1e-6) / 1e9, 1),
+                                 "frac_hbm": round(b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)})
+    return {"layer_bytes": {f: wq[f][0].numel() for f in others}, "rows": rows}
 
 
 def dequant_context(qmm, torch, wq, xs, ys, fmts, stream, args):
@@ -417,12 +450,15 @@ def main():
     fmts = {"q8_0": qmm.Q8_0, "q4_k": qmm.Q4_K}
     modes = {"a": qmm.MODE_F32ACT, "b": qmm.MODE_QACT}
 
+    # the other formats of the pages' files, decode only, outside the step and its value
+    others = {} if (args.only or args.no_other_formats) else {"q4_0": qmm.Q4_0, "q5_0": qmm.Q5_0, "q6_k": qmm.Q6_K}
+
     # ---- inputs: quantized on the GPU by the library's weight quantizer ----
     t_setup = time.perf_counter()
-    wq = {f: [] for f in fmts}
+    wq = {f: [] for f in list(fmts) + list(others)}
     for layer in range(LAYERS):
         wf = torch.from_numpy(synth.weights_f32(5000 + layer, N, K)).to(dev)
-        for f, code in fmts.items():
+        for f, code in list(fmts.items()) + list(others.items()):
             wq[f].append(qmm.quantize_weights(code, wf))
         del wf
     x = torch.from_numpy(synth.acts_f32(5100, M_PREFILL, K)).to(dev)
@@ -558,6 +594,8 @@ def main():
             "traffic": traffic_from_profile(f"gemm:{rb['fmt']}:{rb['mode']}:{rb['M']}"),
         }
     out["detail"] = detail
+    if others:
+        out["other_formats"] = other_formats_decode(qmm, torch, wq, others, modes, xs, ys, stream, args)
     if not args.only and not args.no_dequant:
         out["dequantize_all"] = dequant_context(qmm, torch, wq, xs, ys, fmts, stream, args)
     out["wall_s_timed"] = round(wall_s, 3)
