@@ -117,6 +117,15 @@ QMM_DEV void ldg16_lds(const uint8_t* src, uint8_t* dst)
     __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)dst, 16, 0, AUX);
 }
 
+// 16 bytes per lane from a buffer resource at byte offset voff to LDS at
+// dst + 16 * lane: offsets past the resource's bytes read no memory (the
+// weight rows need not be a multiple of 16 bytes long).  AUX 2: non-temporal.
+template <int AUX>
+QMM_DEV void buf16_lds(rsrc_t r, uint8_t* dst, uint32_t voff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lptr_t)dst, 16, voff, 0, 0, AUX);
+}
+
 // Sum over the wave in a fixed order, the same value in every lane: within each
 // 16-lane row by lane exchanges, then the four rows.
 QMM_DEV float wave_sum(float v)
@@ -177,8 +186,8 @@ __global__ __launch_bounds__(GR_THREADS) void gemv_row_kernel(GemvRowArgs a)
     // ---- the first segments of the stream (they need no activations) ----
     // segment u of this wave into ring buffer `slot`; a wave with fewer than two
     // segments loads its last row (or the matrix's) again for the missing ones.
-    // Every lane loads: lanes past the segment re-read its first bytes into the
-    // buffer's tail, so each segment is exactly LPU instructions.
+    // Every lane loads (lanes past the segment read no memory and write zeros
+    // into the buffer's tail), so each segment is exactly LPU instructions.
     auto issue = [&](int u, int slot) {
         const int j = u / NSEG, sg = u - j * NSEG;
         int p;
@@ -186,11 +195,11 @@ __global__ __launch_bounds__(GR_THREADS) void gemv_row_kernel(GemvRowArgs a)
         const uint8_t* src = a.w[p] + (int64_t)row * a.row_bytes + sg * F::SEG_BYTES;
         const int bytes = min(F::SEG_BYTES, a.row_bytes - sg * F::SEG_BYTES);
         uint8_t* dst = ring + slot * SLOT;
+        // a resource over the segment's bytes: the load that straddles the end of a
+        // row (a length not a multiple of 16) reads nothing past it
+        const rsrc_t r = make_rsrc(src, (uint32_t)bytes);
 #pragma unroll
-        for (int t = 0; t < LPU; ++t) {
-            const int off = 1024 * t + 16 * lane;
-            ldg16_lds<2>(src + (off < bytes ? off : 0), dst + 1024 * t);
-        }
+        for (int t = 0; t < LPU; ++t) buf16_lds<2>(r, dst + 1024 * t, (uint32_t)(1024 * t + 16 * lane));
     };
 #pragma unroll
     for (int u = 0; u < AHEAD; ++u) issue(u < U ? u : max(U - 1, 0), u);
