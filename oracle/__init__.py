@@ -20,7 +20,9 @@ ACT_FORMAT = {Q8_0: Q8_0, Q4_K: Q8_K, Q4_0: Q8_0, Q5_0: Q8_0, Q6_K: Q8_K}
 WEIGHT_FORMATS = (Q8_0, Q4_K, Q4_0, Q5_0, Q6_K)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# QMM_ORACLE_LIB names another build of this oracle's C source: the test that
+# plants mistakes in a copy of that source loads its builds this way.
+_LIB_PATH = os.environ.get("QMM_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 _p = ctypes.c_void_p

@@ -439,6 +439,25 @@ def test_q4_0_q5_0_handbuilt_quantization():
             assert list(blk[2:6]) == case["qh_bytes"], case["why"]
 
 
+def test_q4_0_q5_0_signed_maximum_ties_take_the_first():
+    # x = [4, -4, 0, ...]: both ends have magnitude 4 and the first one met
+    # (+4) is the signed maximum, so d = 4 / -offset is negative.  Worked by
+    # hand from the scale and rounding rule (truncate v/d + offset + 1/2,
+    # capped at the top code):
+    #   Q4_0: d = -0.5 (f16 0xB800), codes 0, 15 (16.5 capped), 8 for the zeros;
+    #         bytes j = c[j] | c[j + 16] << 4: 0x80, 0x8F, then 0x88.
+    #   Q5_0: d = -0.25 (f16 0xB400), codes 0, 31 (32.5 capped), 16 for the zeros;
+    #         fifth bits: all but element 0; low nibbles 0, 15, 0, ...
+    # Taking the last of the tied magnitudes (-4) would flip d's sign and
+    # every code.
+    x = np.zeros((1, 32), dtype=np.float32)
+    x[0, 0], x[0, 1] = 4.0, -4.0
+    q4 = oracle.quantize(Q4_0, x)[0]
+    assert list(q4) == [0x00, 0xB8, 0x80, 0x8F] + [0x88] * 14
+    q5 = oracle.quantize(Q5_0, x)[0]
+    assert list(q5) == [0x00, 0xB4, 0xFE, 0xFF, 0xFF, 0xFF, 0x00, 0x0F] + [0x00] * 14
+
+
 @pytest.mark.parametrize("fmt", [Q4_0, Q5_0])
 def test_q4_0_q5_0_random_bytes_decode_like_a_direct_reading(fmt):
     five = fmt == Q5_0
