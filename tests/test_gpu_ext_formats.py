@@ -65,6 +65,9 @@ def test_quantize_weights_bit_exact(fmt, n, k):
     w[0, :32] = 0.0                                # an all-zero block
     w[1, :32] = np.arange(32) - 16.0               # exact ties at x/d + offset + 1/2
     w[2, 40] = -w[2, 32:64].__abs__().max()        # sign of the block maximum
+    w[3, :] = np.random.default_rng(n + k).integers(-4, 5, k)  # magnitude ties of both signs everywhere
+    w[4, :32] = 0.0
+    w[4, 0], w[4, 1] = 4.0, -4.0                   # the first of the tied maxima sets d's sign
     got = host(qmm.quantize_weights(fmt, dev(w)))
     assert np.array_equal(got, oracle.quantize(fmt, w)), NAME[fmt]
 
