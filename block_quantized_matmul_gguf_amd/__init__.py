@@ -46,6 +46,7 @@ SIGNATURES = {
     "qmatmul_dequantize_weights": (_int, [_int, _p, _i64, _i64, _p, _p]),
     "qmatmul_run_dequantized": (_int, [_p, _p, _p, _p, _i64, _p]),
     "qmatmul_run_group": (_int, [ctypes.POINTER(_p), _int, ctypes.POINTER(_p), _p, ctypes.POINTER(_p), _i64, _p]),
+    "qmatmul_run_noalloc": (_int, [_int, _i64, _i64, _i64, _int, _p, _p, _p, _p]),
     "qmatmul_check": (_int, [_int, _i64, _i64, _i64, _int]),
     "qmatmul_row_bytes": (_i64, [_int, _i64]),
     "qmatmul_block_sums_per_row": (_i64, [_int, _i64]),
@@ -247,6 +248,32 @@ def run_group(plans, ws, x, ys=None, stream=None):
     yarr = (_p * n)(*[_ptr(y) for y in ys])
     _check(lib().qmatmul_run_group(harr, n, warr, _ptr(x), yarr, m, _stream(stream)), "qmatmul_run_group")
     return ys
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def run_noalloc(fmt: int, n: int, k: int, mode: int, w, x, y=None, stream=None):
+    """y = x . W^T without a plan and without device allocation in the library
+    (its workspace is a static device array of NOALLOC_SCRATCH_BYTES per GPU;
+    calls that overlap on one GPU race).  Same arguments and values as
+    ``Plan(fmt, n, k, M, mode).run(w, x)``; allocates ``y`` here only when it is
+    not given."""
+    torch = _torch()
+    _need(w, torch.uint8, None, "w")
+    rb = row_bytes(fmt, k)
+    if rb < 0 or w.numel() != n * rb:
+        raise ValueError(f"w has {w.numel()} bytes, expected {n} rows of {rb}")
+    _need(x, torch.float32, None, "x")
+    if x.dim() != 2 or x.shape[1] != k:
+        raise ValueError(f"x must be [M, {k}], got {tuple(x.shape)}")
+    m = x.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _need(y, torch.float32, (m, n), "y")
+    _check(lib().qmatmul_run_noalloc(fmt, n, k, m, mode, _ptr(w), _ptr(x), _ptr(y), _stream(stream)),
+           "qmatmul_run_noalloc")
+    return y
 
 
 def quantize_act(act_fmt: int, x, out=None, stream=None):

@@ -310,6 +310,50 @@ extern "C" int qmatmul_run(const qmm_plan* p, const void* w, const float* x, flo
     return run_impl(p, w, x, y, nullptr, M, stream);
 }
 
+// The plan-free run of the no-allocation entry point (qmm_noalloc.hip): the
+// same checks and kernels as create + run, with the workspace laid out in the
+// caller's device memory `scratch` of `scratch_bytes` bytes.  dry_run: the
+// checks only (no HIP call).
+int qmm::run_on_scratch(int format, int64_t N, int64_t K, int64_t M, int mode, const void* w, const float* x,
+                        float* y, void* scratch, size_t scratch_bytes, void* stream, bool dry_run)
+{
+    g_err[0] = 0;
+    int st = check_shape(format, N, K, M > 0 ? M : 1, mode);
+    if (st != QMM_OK) return st;
+    if (M < 0) return fail(QMM_EINVAL, "M=%lld is negative", (long long)M);
+    if (M == 0) return QMM_OK;
+    if (mode == QMM_MODE_DEQUANT)
+        return fail(QMM_EUNSUPPORTED, "the dequantize-all form (mode 2) takes a library GEMM that allocates; "
+                    "use qmatmul_create and qmatmul_run");
+    if (format == QMM_Q6_K && mode == QMM_MODE_F32ACT && M > GEMV_MAX_M)
+        return fail(QMM_EUNSUPPORTED, "Q6_K mode (a) at M > %d takes a library GEMM that allocates; use "
+                    "qmatmul_create and qmatmul_run", GEMV_MAX_M);
+    qmm_plan p{};
+    p.fmt = format;
+    p.mode = mode;
+    p.N = N;
+    p.K = K;
+    p.M_max = M;
+    p.ws_bytes = layout(&p, nullptr);
+    if (p.ws_bytes > scratch_bytes)
+        return fail(QMM_EINVAL, "format %d N=%lld K=%lld M=%lld mode %d needs %zu bytes of scratch, more than the "
+                    "%zu bytes of the static scratch buffer", format, (long long)N, (long long)K, (long long)M,
+                    mode, p.ws_bytes, scratch_bytes);
+    st = check_run(&p, w, x, y, M);
+    if (st != QMM_OK || dry_run) return st;
+    if (!scratch) return fail(QMM_EINVAL, "scratch is NULL");
+    hipError_t e = hipGetDevice(&p.device);
+    if (e != hipSuccess) return fail(QMM_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    p.ws = scratch;
+    layout(&p, (char*)scratch);
+    return run_impl(&p, w, x, y, nullptr, M, stream);
+}
+
+int qmm::set_error(int code, const char* msg)
+{
+    return fail(code, "%s", msg);
+}
+
 extern "C" int qmatmul_run_group(const qmm_plan* const* plans, int count, const void* const* w, const float* x,
                                  float* const* y, int64_t M, void* stream)
 {

@@ -108,4 +108,11 @@ void dense_destroy(void* handle);
 int dense_gemm(void* handle, const float* w, const float* x, float* y, int64_t M, int64_t N, int64_t K,
                hipStream_t s);
 
+// Plan-free run on caller-provided device memory (the no-allocation entry
+// point; dry_run: the argument checks only, no HIP call), and setting the
+// calling thread's error message.
+int run_on_scratch(int format, int64_t N, int64_t K, int64_t M, int mode, const void* w, const float* x, float* y,
+                   void* scratch, size_t scratch_bytes, void* stream, bool dry_run);
+int set_error(int code, const char* msg);
+
 }  // namespace qmm

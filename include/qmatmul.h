@@ -140,6 +140,29 @@ int qmatmul_run(const qmm_plan* plan, const void* w_blocks, const float* x, floa
 int qmatmul_run_group(const qmm_plan* const* plans, int count, const void* const* w_blocks, const float* x,
                       float* const* y, int64_t M, void* stream);
 
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Computes
+ * what qmatmul_create(format, N, K, M, mode) followed by qmatmul_run(..., M,
+ * stream) computes, with the same kernels and the same values, but without a
+ * plan and without allocating: the workspace lives in a static device array
+ * of QMM_NOALLOC_SCRATCH_BYTES that each GPU holds from the library's first
+ * use on it until the process ends (qmatmul_workspace_bytes(format, N, K, M,
+ * mode) says what a shape needs).  w_blocks, x, y: device, as in qmatmul_run.
+ * Errors: those of qmatmul_create and qmatmul_run; QMM_EINVAL when the shape
+ * needs more scratch than the array holds; QMM_EUNSUPPORTED for
+ * QMM_MODE_DEQUANT and for Q6_K mode (a) with M > 8 (their product is a
+ * library GEMM that allocates).  Every call on a GPU uses that GPU's one
+ * array: calls that overlap on one GPU (on two streams, or from two host
+ * threads) race and must be serialized by the caller.  The first call on
+ * each device looks up the array's address (no allocation); its kernels set
+ * their launch attributes on first use, so capture a call in a HIP graph only
+ * after one eager call of the same shape.
+ */
+#define QMM_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int qmatmul_run_noalloc(int format, int64_t N, int64_t K, int64_t M, int mode, const void* w_blocks,
+                        const float* x, float* y, void* stream);
+
 /* Free a plan and its workspace (NULL is a no-op).  Synchronizes the device
  * before freeing, so pending runs of the plan finish first. */
 int qmatmul_destroy(qmm_plan* plan);
