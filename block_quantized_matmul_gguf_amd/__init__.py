@@ -43,6 +43,7 @@ SIGNATURES = {
     "qmatmul_quantize_act": (_int, [_int, _p, _i64, _i64, _p, _p]),
     "qmatmul_quantize_weights": (_int, [_int, _p, _i64, _i64, _p, _p]),
     "qmatmul_run_block_sums": (_int, [_p, _p, _p, _p, _i64, _p]),
+    "qmatmul_run_traced": (_int, [_p, _p, _p, _p, _p, _p, _i64, _p]),
     "qmatmul_dequantize_weights": (_int, [_int, _p, _i64, _i64, _p, _p]),
     "qmatmul_run_dequantized": (_int, [_p, _p, _p, _p, _i64, _p]),
     "qmatmul_run_group": (_int, [ctypes.POINTER(_p), _int, ctypes.POINTER(_p), _p, ctypes.POINTER(_p), _i64, _p]),
@@ -205,6 +206,21 @@ class Plan:
         _check(lib().qmatmul_run_block_sums(self._h, _ptr(w), _ptr(x), _ptr(out), m, _stream(stream)),
                "qmatmul_run_block_sums")
         return out
+
+    def run_traced(self, w, x, stream=None):
+        """Mode (b): the run's own kernels with their integer parts written out.
+        Returns (y, sums, act): y float32 [M, N] (bit-equal to ``run``), sums
+        int32 [M, N, block_sums_per_row], act uint8 [M, row_bytes of the
+        activation format] (canonical Q8_0 or Q8K blocks)."""
+        torch = _torch()
+        m = self._args(w, x)
+        spr = block_sums_per_row(self.fmt, self.k)
+        y = torch.empty((m, self.n), dtype=torch.float32, device=x.device)
+        sums = torch.empty((m, self.n, spr), dtype=torch.int32, device=x.device)
+        act = torch.empty((m, row_bytes(ACT_FORMAT[self.fmt], self.k)), dtype=torch.uint8, device=x.device)
+        _check(lib().qmatmul_run_traced(self._h, _ptr(w), _ptr(x), _ptr(y), _ptr(sums), _ptr(act), m,
+                                        _stream(stream)), "qmatmul_run_traced")
+        return y, sums, act
 
     def close(self):
         if self._h:

@@ -143,4 +143,24 @@ QMM_DEV uint32_t pack4(int a, int b, int c, int d)
            ((uint32_t)(uint8_t)d << 24);
 }
 
+// Canonical activation blocks, as the standalone quantizer writes them (and
+// the traced runs copy out of the kernels that quantize): Q8_0 34 bytes
+// (2-byte aligned): f16 d, int8 q[32].
+QMM_DEV void store_q8_0_block(uint8_t* o, uint16_t dbits, const int8_t q[32])
+{
+    uint16_t* h = reinterpret_cast<uint16_t*>(o);
+    h[0] = dbits;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) h[1 + j] = (uint16_t)((uint8_t)q[2 * j] | ((uint16_t)(uint8_t)q[2 * j + 1] << 8));
+}
+// Q8K 292 bytes (4-byte aligned): f32 d, int8 q[256], int16 bsums[16]; the
+// part held by one lane of the wave that quantized the block (q8k_wave: values
+// 4*lane..4*lane+3, lanes 4i hold bsums[i]).
+QMM_DEV void store_q8k_lane(uint8_t* o, int lane, float d, const int q[4], int s16)
+{
+    if (lane == 0) *reinterpret_cast<float*>(o) = d;
+    *reinterpret_cast<uint32_t*>(o + 4 + 4 * lane) = pack4(q[0], q[1], q[2], q[3]);
+    if ((lane & 3) == 0) *reinterpret_cast<int16_t*>(o + 260 + 2 * (lane >> 2)) = (int16_t)s16;
+}
+
 }  // namespace qmm

@@ -157,12 +157,11 @@ static size_t layout(qmm_plan* p, char* base)
         if (pre) {
             p->ex.tw = (uint8_t*)take((size_t)N * (K / 32) * 34);
             const int64_t M = p->M_max;
-            p->gm.a0 = (_Float16*)take(2 * M * K);
+            p->gm.a0 = (_Float16*)take(a ? 2 * M * K : M * K);
             p->gm.a1 = (_Float16*)take(a ? 2 * M * K : 0);
             p->gm.rs = (float*)take(a ? 4 * M : 0);
             p->gm.xs = nullptr;
             p->gm.sd = (float*)take(a ? 0 : 4 * M * (K / 32));
-            p->gm.sbs = nullptr;
         }
         return off;
     }
@@ -172,12 +171,11 @@ static size_t layout(qmm_plan* p, char* base)
     // prefill path
     if (p->M_max > GEMV_MAX_M) {
         const int64_t M = p->M_max;
-        p->gm.a0 = (_Float16*)take(2 * M * K);  // mode (b): int8 values, or f16 for the block sums
+        p->gm.a0 = (_Float16*)take(a ? 2 * M * K : M * K);  // mode (b): int8 values
         p->gm.a1 = (_Float16*)take(a ? 2 * M * K : 0);
         p->gm.rs = (float*)take(a ? 4 * M : 0);
         p->gm.xs = (_Float16*)take(q4 ? 2 * M * (K / 256) * 16 : 0);
         p->gm.sd = (float*)take(a ? 0 : 4 * M * units);
-        p->gm.sbs = (int32_t*)take(q4 && !a ? 4 * M * (K / 32) : 0);
     } else {
         p->gm = GemmBufs{};
     }
@@ -261,7 +259,9 @@ static int check_run(const qmm_plan* p, const void* w, const float* x, const voi
     return QMM_OK;
 }
 
-static int run_impl(const qmm_plan* p, const void* w, const float* x, float* y, int32_t* sums, int64_t M,
+// tr: a traced run (mode (b)), whose kernels also write their integer parts;
+// y may then be null.
+static int run_impl(const qmm_plan* p, const void* w, const float* x, float* y, const Trace* tr, int64_t M,
                     void* stream)
 {
     hipStream_t s = (hipStream_t)stream;
@@ -274,7 +274,7 @@ static int run_impl(const qmm_plan* p, const void* w, const float* x, float* y, 
         if (st != 0) return fail(QMM_EHIP, "rocblas_sgemm: status %d", st);
         return QMM_OK;
     }
-    if (p->fmt == QMM_Q6_K && p->mode == QMM_MODE_F32ACT && M > GEMV_MAX_M && sums == nullptr) {
+    if (p->fmt == QMM_Q6_K && p->mode == QMM_MODE_F32ACT && M > GEMV_MAX_M) {
         // mode (a) prefill: the f32 product of the exactly decoded weights
         e = launch_ext_dequantize(p->fmt, w, p->N, p->K, p->wdeq, s);
         if (e != hipSuccess) return fail(QMM_EHIP, "kernel launch: %s", hipGetErrorString(e));
@@ -282,21 +282,23 @@ static int run_impl(const qmm_plan* p, const void* w, const float* x, float* y, 
         if (st != 0) return fail(QMM_EHIP, "rocblas_sgemm: status %d", st);
         return QMM_OK;
     }
+    uint8_t* act = tr ? tr->act : nullptr;
+    int32_t* sums = tr ? tr->sums : nullptr;
     if (is_ext_format(p->fmt)) {
-        if (M == 1 && sums == nullptr && gemv_row_supported(p->fmt, p->mode, 1, p->N, p->K, false)) {
-            e = launch_gemv_row(p->fmt, p->mode, w, x, p->N, p->K, y, s);  // Q4_0, Q5_0: the one-row kernel
+        if (M == 1 && gemv_row_supported(p->fmt, p->mode, 1, p->N, p->K, tr != nullptr)) {
+            e = launch_gemv_row(p->fmt, p->mode, w, x, p->N, p->K, y, s, tr);  // Q4_0, Q5_0: the one-row kernel
         } else if (M <= GEMV_MAX_M || p->fmt == QMM_Q6_K) {
-            e = launch_ext_run(p->fmt, p->mode, w, x, p->N, p->K, M, p->ex, y, sums, s);
+            e = launch_ext_run(p->fmt, p->mode, w, x, p->N, p->K, M, p->ex, y, s, tr);
         } else {
             e = launch_ext_to_q8_0(p->fmt, w, p->N, p->K, p->ex.tw, s);
-            if (e == hipSuccess) e = launch_gemm_prep(FMT_Q8_0, p->mode, x, M, p->K, p->gm, sums != nullptr, s);
-            if (e == hipSuccess) e = launch_gemm(FMT_Q8_0, p->mode, p->ex.tw, p->N, p->K, M, p->gm, y, sums, s);
+            if (e == hipSuccess) e = launch_gemm_prep(FMT_Q8_0, p->mode, x, M, p->K, p->gm, s, act);
+            if (e == hipSuccess) e = launch_gemm(FMT_Q8_0, p->mode, p->ex.tw, p->N, p->K, M, p->gm, y, s, sums);
         }
     } else if (M <= GEMV_MAX_M) {
-        e = launch_gemv(p->fmt, p->mode, w, x, p->N, p->K, (int)M, p->gv, y, sums, s);
+        e = launch_gemv(p->fmt, p->mode, w, x, p->N, p->K, (int)M, p->gv, y, s, tr);
     } else {
-        e = launch_gemm_prep(p->fmt, p->mode, x, M, p->K, p->gm, sums != nullptr, s);
-        if (e == hipSuccess) e = launch_gemm(p->fmt, p->mode, w, p->N, p->K, M, p->gm, y, sums, s);
+        e = launch_gemm_prep(p->fmt, p->mode, x, M, p->K, p->gm, s, act);
+        if (e == hipSuccess) e = launch_gemm(p->fmt, p->mode, w, p->N, p->K, M, p->gm, y, s, sums);
     }
     if (e != hipSuccess) return fail(QMM_EHIP, "kernel launch: %s", hipGetErrorString(e));
     return QMM_OK;
@@ -417,14 +419,23 @@ extern "C" int qmatmul_run_group(const qmm_plan* const* plans, int count, const 
     return QMM_OK;
 }
 
-extern "C" int qmatmul_run_block_sums(const qmm_plan* p, const void* w, const float* x, int32_t* sums, int64_t M,
-                                      void* stream)
+extern "C" int qmatmul_run_traced(const qmm_plan* p, const void* w, const float* x, float* y, int32_t* sums,
+                                  void* act_blocks, int64_t M, void* stream)
 {
     g_err[0] = 0;
     int st = check_run(p, w, x, sums, M);
     if (st != QMM_OK || M == 0) return st;
     if (p->mode != QMM_MODE_QACT) return fail(QMM_EUNSUPPORTED, "block sums exist only for quantized activations (mode 1)");
-    return run_impl(p, w, x, nullptr, sums, M, stream);
+    if (y && !aligned(y, 4)) return fail(QMM_EINVAL, "y must be 4-byte aligned");
+    if (act_blocks && !aligned(act_blocks, 4)) return fail(QMM_EINVAL, "act_blocks must be 4-byte aligned");
+    const Trace tr{sums, (uint8_t*)act_blocks};
+    return run_impl(p, w, x, y, &tr, M, stream);
+}
+
+extern "C" int qmatmul_run_block_sums(const qmm_plan* p, const void* w, const float* x, int32_t* sums, int64_t M,
+                                      void* stream)
+{
+    return qmatmul_run_traced(p, w, x, nullptr, sums, nullptr, M, stream);
 }
 
 extern "C" int qmatmul_run_dequantized(const qmm_plan* p, const float* w, const float* x, float* y, int64_t M,

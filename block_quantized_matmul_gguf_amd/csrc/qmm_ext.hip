@@ -95,7 +95,9 @@ struct ExtArgs {
     const int8_t* xq;  // mode (b): quantized activations int8 [M][K] (null: quantized in the kernel)
     const float* xd;   //   their scales [M][K/32] (Q8_0) or [M][K/256] (Q8K)
     const int32_t* xs; //   sums of their values [M][K/32] (Q8_0) or [M][K/16] (Q8K bsums)
-    int32_t* sums;     // block-sums hook (mode (b)): written instead of y when not null (HOOK instances)
+    int32_t* sums;     // traced runs (HOOK instances, mode (b)): the integer block sums, written beside y
+    uint8_t* act;      //   and the canonical quantized activation blocks, where the kernel quantizes them
+    int nxblk;         //   activation blocks per row (K/32 or K/256)
     int N, K, M, m0;   // N: rows of all problems; this launch: activation rows m0 + MT*blockIdx.y .. + MT - 1 of M
     int units;         // units per row
     int lpr_log2;      // log2 of the lanes per row
@@ -269,10 +271,9 @@ QMM_DEV void unit_math(const ExtArgs& a, const uint8_t* xl, const Raw<FMT>& w, i
                     t += __shfl_xor(t, 2);
                     t += __shfl_xor(t, 4);
                     if (pc == 0) o[16] = t;
-                } else {
-                    const float dx = XL ? xl_scales(a, xl)[(int64_t)m * (a.K / 256) + i] : a.xd[(int64_t)mm * (a.K / 256) + i];
-                    acc[m] = fmaf(d * dx, (float)part, acc[m]);
                 }
+                const float dx = XL ? xl_scales(a, xl)[(int64_t)m * (a.K / 256) + i] : a.xd[(int64_t)mm * (a.K / 256) + i];
+                acc[m] = fmaf(d * dx, (float)part, acc[m]);
             }
         }
     } else {
@@ -300,12 +301,9 @@ QMM_DEV void unit_math(const ExtArgs& a, const uint8_t* xl, const Raw<FMT>& w, i
                     load_q(reinterpret_cast<const int8_t*>(xp) + 32 * h, xq);
                     const int32_t sx = XL ? xl_sums(a, xl)[(int64_t)m * (a.K / 32) + b] : a.xs[(int64_t)mm * (a.K / 32) + b];
                     const int S = dot_codes_i8<8>(v[h], xq) - F::OFF * sx;
-                    if constexpr (HOOK) {
-                        a.sums[((int64_t)mm * a.N + n) * spr + b] = S;
-                    } else {
-                        const float dx = XL ? xl_scales(a, xl)[(int64_t)m * (a.K / 32) + b] : a.xd[(int64_t)mm * (a.K / 32) + b];
-                        acc[m] = fmaf(d[h] * dx, (float)S, acc[m]);
-                    }
+                    if constexpr (HOOK) a.sums[((int64_t)mm * a.N + n) * spr + b] = S;
+                    const float dx = XL ? xl_scales(a, xl)[(int64_t)m * (a.K / 32) + b] : a.xd[(int64_t)mm * (a.K / 32) + b];
+                    acc[m] = fmaf(d[h] * dx, (float)S, acc[m]);
                 }
             }
         }
@@ -316,8 +314,9 @@ QMM_DEV void unit_math(const ExtArgs& a, const uint8_t* xl, const Raw<FMT>& w, i
 // covering the row's units up to 64) and strides over the row groups; each
 // lane walks units lane, lane + L, ... of its row, and the row sums meet by
 // butterfly inside the L lanes.  Activation rows mb .. mb + MT - 1, staged in
-// LDS once per workgroup when XL.  HOOK: the block-sums test hook (mode (b))
-// writes the integer sums instead of y.
+// LDS once per workgroup when XL.  HOOK (mode (b), the traced run): the same
+// run, which also writes the integer block sums it forms and, where it
+// quantizes the activations itself, those blocks; y may then be null.
 constexpr int EXT_WAVES = 8, EXT_THREADS = 64 * EXT_WAVES;  // decode workgroup: eight waves share the staged activations
 
 template <int FMT, int MODE, int MT, bool XL, bool HOOK, bool GRP>
@@ -373,6 +372,8 @@ __global__ __launch_bounds__(EXT_THREADS) void ext_gemv_kernel(ExtArgs a)
                 float d;
                 int q[4], s16;
                 q8k_wave(v, lane_, d, q, s16);
+                if (HOOK && a.act && blockIdx.x == 0)
+                    store_q8k_lane(a.act + ((int64_t)(mb + m) * a.nxblk + sb) * 292, lane_, d, q, s16);
                 const int u = 8 * sb + (lane_ >> 3);  // the 32-value unit of elements 4*lane..4*lane+3
                 *reinterpret_cast<uint32_t*>(xl + ((int64_t)m * a.units + u) * st + 4 * (lane_ & 7)) =
                     pack4(q[0], q[1], q[2], q[3]);
@@ -389,6 +390,7 @@ __global__ __launch_bounds__(EXT_THREADS) void ext_gemv_kernel(ExtArgs a)
                 float dval;
                 int8_t q[32];
                 q8_0_block(v, dbits, dval, q);
+                if (HOOK && a.act && blockIdx.x == 0) store_q8_0_block(a.act + ((int64_t)(mb + m) * a.nxblk + b) * 34, dbits, q);
                 int sum = 0;
 #pragma unroll
                 for (int j = 0; j < 32; ++j) sum += q[j];
@@ -425,7 +427,7 @@ __global__ __launch_bounds__(EXT_THREADS) void ext_gemv_kernel(ExtArgs a)
             r.load(row, u);
             unit_math<FMT, MODE, MT, XL, HOOK>(a, xl, r, u, n, mb, mrows, spr, acc);
         }
-        if constexpr (HOOK) continue;
+        if (HOOK && a.y[0] == nullptr) continue;
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             float t = acc[m];
@@ -445,7 +447,7 @@ __global__ __launch_bounds__(EXT_THREADS) void ext_gemv_kernel(ExtArgs a)
 // values [M][K/32] (which carries the weight offset).
 __global__ __launch_bounds__(256) void ext_prep_q8_0_kernel(const float* __restrict__ x, int M, int K,
                                                             int8_t* __restrict__ xq, float* __restrict__ xd,
-                                                            int32_t* __restrict__ xs)
+                                                            int32_t* __restrict__ xs, uint8_t* __restrict__ act)
 {
     const int nb = K / 32;
     const int64_t blk = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -457,6 +459,7 @@ __global__ __launch_bounds__(256) void ext_prep_q8_0_kernel(const float* __restr
     float dval;
     int8_t q[32];
     q8_0_block(v, dbits, dval, q);
+    if (act) store_q8_0_block(act + blk * 34, dbits, q);  // traced runs
     int s = 0;
 #pragma unroll
     for (int j = 0; j < 32; ++j) s += q[j];
@@ -475,7 +478,7 @@ __global__ __launch_bounds__(256) void ext_prep_q8_0_kernel(const float* __restr
 // d [M][K/256], bsums [M][K/16].
 __global__ __launch_bounds__(256) void ext_prep_q8k_kernel(const float* __restrict__ x, int M, int K,
                                                            int8_t* __restrict__ xq, float* __restrict__ xd,
-                                                           int32_t* __restrict__ xs)
+                                                           int32_t* __restrict__ xs, uint8_t* __restrict__ act)
 {
     const int nsb = K / 256;
     const int lane = threadIdx.x & 63;
@@ -487,6 +490,7 @@ __global__ __launch_bounds__(256) void ext_prep_q8k_kernel(const float* __restri
     float d;
     int q[4], s16;
     q8k_wave(v, lane, d, q, s16);
+    if (act) store_q8k_lane(act + blk * 292, lane, d, q, s16);  // traced runs
     *reinterpret_cast<uint32_t*>(xq + (int64_t)m * K + 256 * sb + 4 * lane) = pack4(q[0], q[1], q[2], q[3]);
     if (lane == 0) xd[blk] = d;
     if ((lane & 3) == 0) xs[blk * 16 + (lane >> 2)] = s16;
@@ -706,11 +710,11 @@ static void ext_allow_lds(const void* kernel)
     }
 }
 
-template <int FMT, int MODE, int MT, bool GRP>
+template <int FMT, int MODE, int MT, bool HOOK, bool GRP>
 static void launch_staged(const ExtArgs& a, dim3 grid, dim3 block, int lds, hipStream_t s)
 {
-    if (lds > 64 * 1024) ext_allow_lds(reinterpret_cast<const void*>(&ext_gemv_kernel<FMT, MODE, MT, true, false, GRP>));
-    hipLaunchKernelGGL((ext_gemv_kernel<FMT, MODE, MT, true, false, GRP>), grid, block, lds, s, a);
+    if (lds > 64 * 1024) ext_allow_lds(reinterpret_cast<const void*>(&ext_gemv_kernel<FMT, MODE, MT, true, HOOK, GRP>));
+    hipLaunchKernelGGL((ext_gemv_kernel<FMT, MODE, MT, true, HOOK, GRP>), grid, block, lds, s, a);
 }
 
 // Grouped launches (a.groups > 1) always stage their activations (the host
@@ -720,13 +724,14 @@ static void launch_one(bool xl, const ExtArgs& a, unsigned gx, unsigned gy, int 
 {
     const dim3 grid(gx, gy), block(EXT_THREADS);
     if constexpr (MODE == MODE_B) {
-        if (a.sums) {  // the block-sums hook: activations from global memory
-            hipLaunchKernelGGL((ext_gemv_kernel<FMT, MODE, MT, false, true, false>), grid, block, 0, s, a);
+        if (a.sums) {  // the traced run: the same staging choice as the plain run
+            if (xl) launch_staged<FMT, MODE, MT, true, false>(a, grid, block, lds, s);
+            else hipLaunchKernelGGL((ext_gemv_kernel<FMT, MODE, MT, false, true, false>), grid, block, 0, s, a);
             return;
         }
     }
-    if (a.groups > 1) launch_staged<FMT, MODE, MT, true>(a, grid, block, lds, s);
-    else if (xl) launch_staged<FMT, MODE, MT, false>(a, grid, block, lds, s);
+    if (a.groups > 1) launch_staged<FMT, MODE, MT, false, true>(a, grid, block, lds, s);
+    else if (xl) launch_staged<FMT, MODE, MT, false, false>(a, grid, block, lds, s);
     else hipLaunchKernelGGL((ext_gemv_kernel<FMT, MODE, MT, false, false, false>), grid, block, 0, s, a);
 }
 
@@ -760,10 +765,10 @@ static int ext_xl_bytes(int fmt, int mode, int units, int K, int mt)
 static int ext_mt(int mode, int M) { return M == 1 ? 1 : mode == MODE_A ? 8 : M == 2 ? 2 : M <= 4 ? 4 : 8; }
 
 // Whether a run stages its activations in LDS (and, in mode (b), quantizes
-// them there): not for the block-sums hook, nor when they exceed the LDS.
-static bool ext_staged(int fmt, int mode, int units, int K, int mt, bool hook)
+// them there): unless they exceed the LDS.
+static bool ext_staged(int fmt, int mode, int units, int K, int mt)
 {
-    return !hook && ext_xl_bytes(fmt, mode, units, K, mt) <= EXT_XL_MAX;
+    return ext_xl_bytes(fmt, mode, units, K, mt) <= EXT_XL_MAX;
 }
 
 // The decode kernel over activation rows m0.. in one launch per 65535 * MT rows.
@@ -771,7 +776,7 @@ static hipError_t ext_gemv(int fmt, int mode, ExtArgs a, hipStream_t s)
 {
     const int mt = ext_mt(mode, a.M);
     const int lds = ext_xl_bytes(fmt, mode, a.units, a.K, mt);
-    const bool xl = ext_staged(fmt, mode, a.units, a.K, mt, a.sums != nullptr);
+    const bool xl = ext_staged(fmt, mode, a.units, a.K, mt);
     int lg = 0;
     while ((1 << lg) < a.units && lg < 6) ++lg;
     a.lpr_log2 = lg;
@@ -803,20 +808,22 @@ static hipError_t ext_gemv(int fmt, int mode, ExtArgs a, hipStream_t s)
     return hipSuccess;
 }
 
-hipError_t launch_ext_prep(int fmt, const float* x, int64_t M, int64_t K, const ExtBufs& b, hipStream_t s)
+hipError_t launch_ext_prep(int fmt, const float* x, int64_t M, int64_t K, const ExtBufs& b, hipStream_t s,
+                           uint8_t* act)
 {
     if (fmt == FMT_Q6_K)
         hipLaunchKernelGGL(ext_prep_q8k_kernel, dim3(ext_blocks(M * (K / 256), 4)), dim3(256), 0, s, x, (int)M, (int)K,
-                           b.xq, b.xd, b.xs);
+                           b.xq, b.xd, b.xs, act);
     else
         hipLaunchKernelGGL(ext_prep_q8_0_kernel, dim3(ext_blocks(M * (K / 32), 256)), dim3(256), 0, s, x, (int)M,
-                           (int)K, b.xq, b.xd, b.xs);
+                           (int)K, b.xq, b.xd, b.xs, act);
     return hipGetLastError();
 }
 
 hipError_t launch_ext_run(int fmt, int mode, const void* w, const float* x, int64_t N, int64_t K, int64_t M,
-                          const ExtBufs& b, float* y, int32_t* sums, hipStream_t s)
+                          const ExtBufs& b, float* y, hipStream_t s, const Trace* tr)
 {
+    if (tr && mode != MODE_B) return hipErrorInvalidValue;
     // mode (b) with one or two activation rows staged in LDS quantizes them
     // inside the decode kernel (a.xq null); otherwise a separate launch
     // writes them to the workspace first (with more rows every workgroup
@@ -832,17 +839,19 @@ hipError_t launch_ext_run(int fmt, int mode, const void* w, const float* x, int6
     a.xq = b.xq;
     a.xd = b.xd;
     a.xs = b.xs;
-    a.sums = sums;
+    a.sums = tr ? tr->sums : nullptr;
+    a.act = tr ? tr->act : nullptr;
+    a.nxblk = fmt == FMT_Q6_K ? (int)(K / 256) : (int)(K / 32);
     a.N = (int)N;
     a.K = (int)K;
     a.M = (int)M;
     a.units = fmt == FMT_Q6_K ? (int)(K / 32) : (int)(K / 64);
     if (mode == MODE_B) {
         const int mt = ext_mt(mode, (int)M);
-        if (mt <= 2 && ext_staged(fmt, mode, a.units, (int)K, mt, sums != nullptr)) {
+        if (mt <= 2 && ext_staged(fmt, mode, a.units, (int)K, mt)) {
             a.xq = nullptr;
         } else {
-            const hipError_t e = launch_ext_prep(fmt, x, M, K, b, s);
+            const hipError_t e = launch_ext_prep(fmt, x, M, K, b, s, a.act);
             if (e != hipSuccess) return e;
         }
     }
@@ -856,7 +865,7 @@ bool ext_group_supported(int fmt, int mode, int64_t K, int64_t M)
     if (mode != MODE_A && mode != MODE_B) return false;
     if (M < 1 || M > GEMV_MAX_M) return false;
     const int units = fmt == FMT_Q6_K ? (int)(K / 32) : (int)(K / 64);
-    return ext_staged(fmt, mode, units, (int)K, ext_mt(mode, (int)M), false);
+    return ext_staged(fmt, mode, units, (int)K, ext_mt(mode, (int)M));
 }
 
 // Up to EXT_GROUP_MAX problems sharing K, mode and x in one launch (their
@@ -891,10 +900,10 @@ hipError_t launch_ext_group(int fmt, int mode, int count, const void* const* w, 
     a.units = fmt == FMT_Q6_K ? (int)(K / 32) : (int)(K / 64);
     if (mode == MODE_B) {
         const int mt = ext_mt(mode, (int)M);
-        if (mt <= 2 && ext_staged(fmt, mode, a.units, (int)K, mt, false)) {
+        if (mt <= 2 && ext_staged(fmt, mode, a.units, (int)K, mt)) {
             a.xq = nullptr;
         } else {
-            const hipError_t e = launch_ext_prep(fmt, x, M, K, b, s);
+            const hipError_t e = launch_ext_prep(fmt, x, M, K, b, s, nullptr);
             if (e != hipSuccess) return e;
         }
     }

@@ -22,9 +22,6 @@
 // activation pairs and raw weight bytes are in flight to registers; after the
 // compute they are decoded (weights to exact f16) into the other buffer, and
 // one barrier per stage hands it over.
-//
-// The block-sums test hook (mode (b), integer sums out) keeps its own kernel,
-// gemm_sums_kernel, which runs the MFMA on the quantized integers.
 #include <map>
 #include <mutex>
 #include <set>
@@ -426,185 +423,6 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_kernel(GemmArg
     }
 }
 
-// ---------------------------------------------------- block-sums hook ----
-//
-// Mode (b) integer block sums for M > 8: 128 x 128 tiles, activations as
-// their quantized integers in f16, weights as exact f16 integers (Q8_0: q;
-// Q4_K: sc_j*q); v_mfma_f32_32x32x16_f16 sums of 32 (Q8_0) or 128 (Q4_K)
-// products are exact integers below 2^24.  Writes Q8_0 S[m][n][b]; Q4_K
-// sumi and summins per super-block (the per-32 sums are folded into sumi).
-
-struct SumsArgs {
-    const uint8_t* w;
-    int64_t row_bytes;
-    int N, K, M;
-    const _Float16* q;   // quantized activations as f16 [M][K]
-    const float* sd;     // unused by the sums; kept for the layout
-    const int32_t* bsp;  // Q4_K: bsum pairs [M][K/32]
-    int32_t* sums;
-};
-
-constexpr int S_BM = 128, S_BN = 128, S_LDA = 72;
-
-template <int FMT>
-__global__ __launch_bounds__(256, 1) void gemm_sums_kernel(SumsArgs a)
-{
-    __shared__ __align__(16) _Float16 sA0[S_BM * S_LDA];
-    __shared__ __align__(16) _Float16 sB[S_BN * S_LDA];
-    __shared__ __align__(16) int sQm[8][S_BN];
-    __shared__ __align__(16) int sBs[8][S_BM];
-
-    const int M = a.M, N = a.N, K = a.K;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int m0 = blockIdx.y * S_BM, n0 = blockIdx.x * S_BN;
-    const int wm = (wave & 1) * 64, wn = (wave >> 1) * 64;
-    const int nst = K / 64;
-    const int nb = K / 32;
-    const int br = tid >> 1, bpart = tid & 1;
-    const bool brow_ok = n0 + br < N;
-    const uint8_t* wrow = a.w + (int64_t)(n0 + (brow_ok ? br : 0)) * a.row_bytes;
-
-    f32x16_t cb[2][2];
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int yv = 0; yv < 2; ++yv)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) cb[x][yv][r] = 0.0f;
-    int32_t half0[2][2][16];
-
-    const int li = lane & 31, lk = 8 * (lane >> 5);
-    auto crow = [&](int r) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); };
-
-    for (int st = 0; st < nst; ++st) {
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int idx = tid + 256 * i, row = idx >> 3, c16 = idx & 7, m = m0 + row;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (m < M) v = *reinterpret_cast<const uint4*>(a.q + (int64_t)m * K + st * 64 + 8 * c16);
-            *reinterpret_cast<uint4*>(&sA0[row * S_LDA + 8 * c16]) = v;
-        }
-        if (FMT == FMT_Q8_0) {
-            const uint32_t* p = reinterpret_cast<const uint32_t*>(wrow + 68 * st) + 8 * bpart;
-            uint32_t rb[9];
-#pragma unroll
-            for (int i = 0; i < 9; ++i) rb[i] = brow_ok ? p[i] : 0u;
-            uint32_t q[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) q[i] = bpart == 0 ? __builtin_amdgcn_alignbyte(rb[i + 1], rb[i], 2) : rb[i + 1];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                uint32_t t0, t1, t2, t3;
-                i8x4_to_f16(q[2 * i], t0, t1);
-                i8x4_to_f16(q[2 * i + 1], t2, t3);
-                *reinterpret_cast<uint4*>(&sB[br * S_LDA + 32 * bpart + 8 * i]) = make_uint4(t0, t1, t2, t3);
-            }
-        } else {
-            const int sb = st >> 2, c = st & 3;
-            const uint4 hdr = brow_ok ? *reinterpret_cast<const uint4*>(wrow + 144 * sb) : make_uint4(0, 0, 0, 0);
-            const uint4 qv = brow_ok ? *reinterpret_cast<const uint4*>(wrow + 144 * sb + 16 + 32 * c + 16 * bpart)
-                                     : make_uint4(0, 0, 0, 0);
-            const uint32_t qd[4] = {qv.x, qv.y, qv.z, qv.w};
-            int sc0, mn0, sc1, mn1;
-            q4k_scale_min(hdr.y, hdr.z, hdr.w, 2 * c, sc0, mn0);
-            q4k_scale_min(hdr.y, hdr.z, hdr.w, 2 * c + 1, sc1, mn1);
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                half8_t lo, hi;
-#pragma unroll
-                for (int bb = 0; bb < 8; ++bb) {
-                    const uint32_t byte = (qd[2 * hh + (bb >> 2)] >> (8 * (bb & 3))) & 0xffu;
-                    lo[bb] = (_Float16)(float)((int)(byte & 15u) * sc0);
-                    hi[bb] = (_Float16)(float)((int)(byte >> 4) * sc1);
-                }
-                *reinterpret_cast<half8_t*>(&sB[br * S_LDA + 16 * bpart + 8 * hh]) = lo;
-                *reinterpret_cast<half8_t*>(&sB[br * S_LDA + 32 + 16 * bpart + 8 * hh]) = hi;
-            }
-            if (c == 0 && bpart == 0) {
-#pragma unroll
-                for (int jq = 0; jq < 8; ++jq) {
-                    int s_, m_;
-                    q4k_scale_min(hdr.y, hdr.z, hdr.w, jq, s_, m_);
-                    sQm[jq][br] = brow_ok ? m_ : 0;
-                }
-            }
-            if (c == 0)
-                for (int idx = tid; idx < S_BM * 8; idx += 256) {
-                    const int row = idx >> 3, jq = idx & 7, m = m0 + row;
-                    sBs[jq][row] = m < M ? a.bsp[(int64_t)m * (K / 32) + 8 * sb + jq] : 0;
-                }
-        }
-        __syncthreads();
-
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            half8_t A0[2], B[2];
-#pragma unroll
-            for (int t2 = 0; t2 < 2; ++t2) {
-                A0[t2] = *reinterpret_cast<const half8_t*>(&sA0[(wm + 32 * t2 + li) * S_LDA + 16 * kk + lk]);
-                B[t2] = *reinterpret_cast<const half8_t*>(&sB[(wn + 32 * t2 + li) * S_LDA + 16 * kk + lk]);
-            }
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
-                    cb[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A0[mt], B[nt], cb[mt][nt], 0, 0, 0);
-            if (FMT == FMT_Q8_0 && (kk & 1)) {  // end of a 32-value block
-                const int blk = kk >> 1;
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int m = m0 + wm + 32 * mt + crow(r), n = n0 + wn + 32 * nt + li;
-                            if (m < M && n < N) a.sums[((int64_t)m * N + n) * nb + 2 * st + blk] = (int32_t)cb[mt][nt][r];
-                            cb[mt][nt][r] = 0.0f;
-                        }
-            }
-        }
-        if (FMT == FMT_Q4_K) {
-            const int c = st & 3;
-            if (c & 1) {  // end of a 128-value half super-block
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            if (c == 1) half0[mt][nt][r] = (int32_t)cb[mt][nt][r];
-                            else half0[mt][nt][r] += (int32_t)cb[mt][nt][r];
-                            cb[mt][nt][r] = 0.0f;
-                        }
-            }
-            if (c == 3) {
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) {
-                        const int nl = wn + 32 * nt + li;
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int ml = wm + 32 * mt + crow(r);
-                            int summ = 0;
-#pragma unroll
-                            for (int jq = 0; jq < 8; ++jq) summ += sQm[jq][nl] * sBs[jq][ml];
-                            const int m = m0 + ml, n = n0 + nl;
-                            if (m < M && n < N) {
-                                int32_t* o = a.sums + (((int64_t)m * N + n) * (K / 256) + (st >> 2)) * 10;
-#pragma unroll
-                                for (int jq = 0; jq < 8; ++jq) o[jq] = INT32_MIN;
-                                o[8] = half0[mt][nt][r];
-                                o[9] = summ;
-                            }
-                        }
-                    }
-            }
-        }
-    }
-}
-
 // ------------------------------------------------------------ launchers ----
 
 typedef void (*GemmKernel)(GemmArgs);
@@ -692,27 +510,11 @@ static hipError_t launch_fmt(const GemmArgs& a, GemmTile t, hipStream_t s)
 }
 
 hipError_t launch_gemm(int fmt, int mode, const void* w, int64_t N, int64_t K, int64_t M, const GemmBufs& b,
-                       float* y, int32_t* sums, hipStream_t s)
+                       float* y, hipStream_t s, int32_t* sums)
 {
     const int64_t row_bytes = fmt == FMT_Q8_0 ? (K / 32) * 34 : (K / 256) * 144;
-    if (sums) {
-        if (mode != MODE_B) return hipErrorInvalidValue;
-        SumsArgs a{};
-        a.w = (const uint8_t*)w;
-        a.row_bytes = row_bytes;
-        a.N = (int)N;
-        a.K = (int)K;
-        a.M = (int)M;
-        a.q = b.a0;
-        a.sd = b.sd;
-        a.bsp = b.sbs;
-        a.sums = sums;
-        const dim3 grid((unsigned)((N + S_BN - 1) / S_BN), (unsigned)((M + S_BM - 1) / S_BM));
-        if (fmt == FMT_Q8_0) hipLaunchKernelGGL(gemm_sums_kernel<FMT_Q8_0>, grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL(gemm_sums_kernel<FMT_Q4_K>, grid, dim3(256), 0, s, a);
-        return hipGetLastError();
-    }
-    if (mode == MODE_B) return launch_gemm_q(fmt, w, N, K, M, b, y, s);
+    if (mode == MODE_B) return launch_gemm_q(fmt, w, N, K, M, b, y, s, sums);
+    if (sums) return hipErrorInvalidValue;
     GemmArgs a{};
     a.w = (const uint8_t*)w;
     a.row_bytes = row_bytes;

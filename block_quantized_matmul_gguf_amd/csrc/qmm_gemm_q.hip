@@ -45,7 +45,8 @@ struct QGemmArgs {
     const int8_t* q;      // quantized activations [M][K]
     const float* dx;      // activation block scales, block-major: Q8_0 [K/32][M], Q8K [K/256][M]
     const _Float16* bsx;  // Q8K: [K/256][M][16] sub-block sums, multiples of 64 then remainders
-    float* y;
+    float* y;             // EMIT instances: may be null
+    int32_t* sums;        // EMIT: Q8_0 S per block; Q4_K S_0..S_7 and summins per super-block (slot 8 left)
 };
 
 
@@ -89,7 +90,10 @@ struct QCfg {
     static_assert(Q8 || 256 % SV == 0, "a Q4_K stage must not cross a super-block");
 };
 
-template <int FMT, int MW, int TN, int KB>
+// EMIT: the same kernel, which also writes the exact int32 block sums its
+// matrix-core steps produce (Q8_0: S per 32-value block; Q4_K: S_j per
+// sub-block and the super-block's mins sum).
+template <int FMT, int MW, int TN, int KB, bool EMIT>
 __global__ __launch_bounds__(128 * MW, 2) void gemm_q_kernel(QGemmArgs a)
 {
     using C = QCfg<FMT, MW, TN, KB>;
@@ -302,6 +306,17 @@ __global__ __launch_bounds__(128 * MW, 2) void gemm_q_kernel(QGemmArgs a)
         for (int j = 0; j < TN; ++j) {
             const i32x4_t bf = bn;
             const i32x16_t cv = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bf, izero, 0, 0, 0);
+            if constexpr (EMIT) {
+                // block blk of stage st: Q8_0 block SB*st + blk; Q4_K sub-block `sub` of super-block SV*st/256
+                const int n = n0 + 32 * j + l32;
+                const int spr = Q8 ? K / 32 : (K / 256) * 10;
+                const int idx = Q8 ? SB * st + blk : (SV * st / 256) * 10 + sub;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = m0 + wm + 8 * (r >> 2) + 4 * hl + (r & 3);
+                    if (m < M && n < N) a.sums[((int64_t)m * N + n) * spr + idx] = cv[r];
+                }
+            }
             // issue the MFMA before the previous tile's scaling, which then
             // runs while the matrix cores work (never waits on this result)
             __builtin_amdgcn_sched_barrier(0);
@@ -354,6 +369,14 @@ __global__ __launch_bounds__(128 * MW, 2) void gemm_q_kernel(QGemmArgs a)
                     const half8_t bm = *reinterpret_cast<const half8_t*>(lds + C::OFF_MJ + (par * BN + 32 * j + l32) * 16);
                     const float dm = sdm[32 * j];
                     const f32x16_t cm = __builtin_amdgcn_mfma_f32_32x32x16_f16(ax, bm, fzero, 0, 0, 0);
+                    if constexpr (EMIT) {  // summins: an exact integer in f32
+                        const int n = n0 + 32 * j + l32;
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int m = m0 + wm + 8 * (r >> 2) + 4 * hl + (r & 3);
+                            if (m < M && n < N) a.sums[((int64_t)m * N + n) * (K / 256) * 10 + (SV * st / 256) * 10 + 9] = (int32_t)cm[r];
+                        }
+                    }
 #pragma unroll
                     for (int r = 0; r < 16; ++r) acc[j][r] = __builtin_fmaf(-dxv[r] * dm, cm[r], acc[j][r]);
                 }
@@ -408,7 +431,7 @@ __global__ __launch_bounds__(128 * MW, 2) void gemm_q_kernel(QGemmArgs a)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int m = m0 + crow(r);
-                if (m < M) a.y[(int64_t)m * N + n] = acc[j][r] + red[crow(r) * BN + 32 * j + l32];
+                if (m < M && (!EMIT || a.y)) a.y[(int64_t)m * N + n] = acc[j][r] + red[crow(r) * BN + 32 * j + l32];
             }
         }
     }
@@ -477,7 +500,7 @@ static QTile pick_qtile(int64_t M, int64_t N)
     return best;
 }
 
-template <int FMT, int MW, int TN>
+template <int FMT, int MW, int TN, bool EMIT>
 static hipError_t launch_q(QGemmArgs a, hipStream_t s)
 {
     using C = QCfg<FMT, MW, TN, Q_KB>;
@@ -486,22 +509,45 @@ static hipError_t launch_q(QGemmArgs a, hipStream_t s)
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     a.nm = nm;
     a.remap = grid % 8 == 0 ? 1 : 0;
-    const void* k = (const void*)gemm_q_kernel<FMT, MW, TN, Q_KB>;
+    const void* k = (const void*)gemm_q_kernel<FMT, MW, TN, Q_KB, EMIT>;
     allow_lds_q(k, C::BYTES);
     void* args[] = {&a};
     return hipLaunchKernel(k, dim3((unsigned)grid), dim3(C::Q_NT), args, C::BYTES, s);
 }
 
-template <int FMT>
+template <int FMT, bool EMIT>
 static hipError_t launch_q_fmt(const QGemmArgs& a, QTile t, hipStream_t s)
 {
-    if (t.mw == 4) return launch_q<FMT, 4, 7>(a, s);
-    if (t.tn == 4) return launch_q<FMT, 2, 4>(a, s);
-    return launch_q<FMT, 2, 2>(a, s);
+    if (t.mw == 4) return launch_q<FMT, 4, 7, EMIT>(a, s);
+    if (t.tn == 4) return launch_q<FMT, 2, 4, EMIT>(a, s);
+    return launch_q<FMT, 2, 2, EMIT>(a, s);
+}
+
+// Q4_K traced runs: sumi = sum_j sc_j S_j of every super-block, from the S_j
+// the prefill kernel wrote and the weights' 6-bit scales (the kernel itself
+// scales each S_j in f32 and never forms sumi).
+__global__ __launch_bounds__(256) void q4k_sumi_kernel(const uint8_t* __restrict__ w, int64_t N, int K, int M,
+                                                       int32_t* __restrict__ sums)
+{
+    const int nsb = K / 256;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (m, n, super-block)
+    if (i >= (int64_t)M * N * nsb) return;
+    const int64_t mn = i / nsb;
+    const int sb = (int)(i - mn * nsb);
+    const int64_t n = mn % N;
+    const uint32_t* h = reinterpret_cast<const uint32_t*>(w + (n * nsb + sb) * 144);
+    int32_t* o = sums + i * 10;
+    int si = 0;
+    for (int j = 0; j < 8; ++j) {
+        int sc, mn_;
+        q4k_scale_min(h[1], h[2], h[3], j, sc, mn_);
+        si += sc * o[j];
+    }
+    o[8] = si;
 }
 
 hipError_t launch_gemm_q(int fmt, const void* w, int64_t N, int64_t K, int64_t M, const GemmBufs& b, float* y,
-                         hipStream_t s)
+                         hipStream_t s, int32_t* sums)
 {
     QGemmArgs a{};
     a.w = (const uint8_t*)w;
@@ -513,9 +559,18 @@ hipError_t launch_gemm_q(int fmt, const void* w, int64_t N, int64_t K, int64_t M
     a.dx = b.sd;
     a.bsx = b.xs;
     a.y = y;
+    a.sums = sums;
     const QTile t = pick_qtile(M, N);
-    const hipError_t e = fmt == FMT_Q8_0 ? launch_q_fmt<FMT_Q8_0>(a, t, s) : launch_q_fmt<FMT_Q4_K>(a, t, s);
+    const bool emit = sums != nullptr;
+    hipError_t e;
+    if (fmt == FMT_Q8_0) e = emit ? launch_q_fmt<FMT_Q8_0, true>(a, t, s) : launch_q_fmt<FMT_Q8_0, false>(a, t, s);
+    else e = emit ? launch_q_fmt<FMT_Q4_K, true>(a, t, s) : launch_q_fmt<FMT_Q4_K, false>(a, t, s);
     if (e != hipSuccess) return e;
+    if (emit && fmt == FMT_Q4_K) {
+        const int64_t items = M * N * (K / 256);
+        hipLaunchKernelGGL(q4k_sumi_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, (const uint8_t*)w, N,
+                           (int)K, (int)M, sums);
+    }
     return hipGetLastError();
 }
 

@@ -104,6 +104,9 @@ struct GemvRowArgs {
     int nunit;      // units per row (Q8_0 block pairs, Q4_K super-blocks)
     int nxi;        // 1 KB load instructions that bring x into LDS
     int xq_off, xd_off, xb_off, ring_off;  // LDS byte offsets (f32 x staged at 0)
+    // EMIT instances (mode (b), one problem): the integer parts of the run
+    int32_t* sums;  // per row: Q8_0/Q4_0/Q5_0 S per block; Q4_K per super-block S_0..S_7, sumi, summins
+    uint8_t* act;   // the quantized activation row as canonical Q8_0 / Q8K blocks (workgroup 0 writes it)
 };
 
 typedef __attribute__((address_space(1))) void* gptr_t;
@@ -143,11 +146,14 @@ QMM_DEV float wave_sum(float v)
 // a segment buffer holds LPU KB.  NSEG: segments per row.  RING: segment
 // buffers per wave (2 or 3); two segments are in flight either way.  Every
 // global load of the kernel writes LDS directly, so all waits on them are the
-// explicit ones.
-template <int FMT, int MODE, int LPU, int NSEG, int RING>
+// explicit ones.  EMIT (mode (b), one problem): the same run, which also
+// writes the integer block sums it forms and its quantized activations.
+template <int FMT, int MODE, int LPU, int NSEG, int RING, bool EMIT>
 __global__ __launch_bounds__(GR_THREADS) void gemv_row_kernel(GemvRowArgs a)
 {
     static_assert(MODE == MODE_B || NSEG == 1, "mode (a) holds one segment's activations");
+    static_assert(MODE == MODE_B || !EMIT, "integer sums exist in mode (b) only");
+    const bool emit_act = EMIT && blockIdx.x == 0 && a.act != nullptr;
     using F = GrFmt<FMT>;
     constexpr int SLOT = 1024 * LPU;
     extern __shared__ __align__(16) uint8_t lds[];
@@ -228,6 +234,12 @@ __global__ __launch_bounds__(GR_THREADS) void gemv_row_kernel(GemvRowArgs a)
             for (int i = 0; i < 8; ++i) q[i] = q8_0_q(v[i], id);
             *reinterpret_cast<u32x2_t*>(s_xq + 8 * t) = u32x2_t{pack4(q[0], q[1], q[2], q[3]), pack4(q[4], q[5], q[6], q[7])};
             if ((t & 3) == 0) s_xd[t >> 2] = dval;
+            if (emit_act) {  // canonical block t/4: f16 d, then 32 int8 (2-byte aligned)
+                uint16_t* o = reinterpret_cast<uint16_t*>(a.act + 34 * (t >> 2));
+                if ((t & 3) == 0) o[0] = dbits;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[1 + 4 * (t & 3) + i] = (uint16_t)((uint8_t)q[2 * i] | ((uint8_t)q[2 * i + 1] << 8));
+            }
         }
     } else {
         // Q8K, a 16-lane row per 256 values (16 per lane): the signed value of
@@ -267,6 +279,14 @@ __global__ __launch_bounds__(GR_THREADS) void gemv_row_kernel(GemvRowArgs a)
             const int pair = s16 + dpp_i<DPP_X1>(s16);  // the 32 values of sub-block part / 2
             if ((part & 1) == 0) s_xb[8 * sb + (part >> 1)] = pair;
             if (part == 0) s_xd[sb] = d;
+            if (emit_act) {  // canonical Q8K block sb: f32 d, 256 int8, int16 bsums[16]
+                uint8_t* o = a.act + 292 * sb;
+                if (part == 0) *reinterpret_cast<float*>(o) = d;
+                uint32_t* oq = reinterpret_cast<uint32_t*>(o + 4 + 16 * part);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) oq[i] = pack4(q[4 * i], q[4 * i + 1], q[4 * i + 2], q[4 * i + 3]);
+                reinterpret_cast<int16_t*>(o + 260)[part] = (int16_t)s16;
+            }
         }
     }
     if constexpr (MODE == MODE_B) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -363,6 +383,8 @@ __global__ __launch_bounds__(GR_THREADS) void gemv_row_kernel(GemvRowArgs a)
 #pragma unroll
                         for (int k = 0; k < 8; ++k) sq = __builtin_amdgcn_sdot4((int)v[h][k], X[sg][8 * h + k], sq, false);
                         acc = fmaf((float)(sq - F::OFF * XB[sg][h]), d[h] * DX[sg][h], acc);
+                        if constexpr (EMIT)
+                            a.sums[(int64_t)(gw + nw * j) * (2 * a.nunit) + 2 * (sg * F::SEG_UNITS + lane) + h] = sq - F::OFF * XB[sg][h];
                     }
                 }
             } else if constexpr (MODE == MODE_A && FMT == FMT_Q8_0) {
@@ -441,6 +463,11 @@ __global__ __launch_bounds__(GR_THREADS) void gemv_row_kernel(GemvRowArgs a)
                     }
                     acc = fmaf((float)s0, f16lo(W[0]) * DX[sg][0], acc);
                     acc = fmaf((float)s1, f16hi(W[8]) * DX[sg][1], acc);
+                    if constexpr (EMIT) {
+                        int32_t* o = a.sums + (int64_t)(gw + nw * j) * (2 * a.nunit) + 2 * (sg * F::SEG_UNITS + lane);
+                        o[0] = s0;
+                        o[1] = s1;
+                    }
                 }
             } else {
                 // a super-block's four lanes are all live or all not; lanes past the
@@ -468,6 +495,17 @@ __global__ __launch_bounds__(GR_THREADS) void gemv_row_kernel(GemvRowArgs a)
                 sm += dpp_i<DPP_X1>(sm);
                 sm += dpp_i<DPP_X2>(sm);
                 if (live && c == 0) acc = fmaf(DX[sg][0], f16lo(H[0]) * (float)si - f16hi(H[0]) * (float)sm, acc);
+                if constexpr (EMIT) {
+                    if (live) {  // per super-block: S_0..S_7, sumi, summins
+                        int32_t* o = a.sums + ((int64_t)(gw + nw * j) * a.nunit + sg * F::SEG_UNITS + (lane >> 2)) * 10;
+                        o[2 * c] = s0;
+                        o[2 * c + 1] = s1;
+                        if (c == 0) {
+                            o[8] = si;
+                            o[9] = sm;
+                        }
+                    }
+                }
             }
             if (RING == AHEAD && refill) {
                 lgkm_wait0();  // this buffer's reads are done before it is refilled
@@ -481,7 +519,7 @@ __global__ __launch_bounds__(GR_THREADS) void gemv_row_kernel(GemvRowArgs a)
         if (lane == (j & 63)) yv = t;
         if ((j & 63) == 63 || j == nrows - 1) {
             const int j0 = j & ~63;
-            if (lane <= (j & 63)) {
+            if (lane <= (j & 63) && (!EMIT || a.y[0])) {
                 const int r = gw + nw * (j0 + lane);  // this lane's row (differs per lane)
                 float* yp = a.y[0];
                 int r0 = 0;
@@ -496,37 +534,43 @@ __global__ __launch_bounds__(GR_THREADS) void gemv_row_kernel(GemvRowArgs a)
 
 typedef void (*GrKernel)(GemvRowArgs);
 
-template <int FMT, int MODE, int RING>
+template <int FMT, int MODE, int RING, bool EMIT>
 static GrKernel gr_kernel_ring(int lpu, int nseg)
 {
     constexpr int L = GrFmt<FMT>::LPU_MAX;
     if constexpr (MODE == MODE_B) {
-        if (nseg == 4) return gemv_row_kernel<FMT, MODE, L, 4, RING>;
-        if (nseg == 3) return gemv_row_kernel<FMT, MODE, L, 3, RING>;
-        if (nseg == 2) return gemv_row_kernel<FMT, MODE, L, 2, RING>;
+        if (nseg == 4) return gemv_row_kernel<FMT, MODE, L, 4, RING, EMIT>;
+        if (nseg == 3) return gemv_row_kernel<FMT, MODE, L, 3, RING, EMIT>;
+        if (nseg == 2) return gemv_row_kernel<FMT, MODE, L, 2, RING, EMIT>;
     }
     switch (lpu) {
-    case 1: return gemv_row_kernel<FMT, MODE, 1, 1, RING>;
-    case 2: return gemv_row_kernel<FMT, MODE, (2 < L ? 2 : L), 1, RING>;
-    case 3: return gemv_row_kernel<FMT, MODE, (3 < L ? 3 : L), 1, RING>;
-    case 4: return gemv_row_kernel<FMT, MODE, (4 < L ? 4 : L), 1, RING>;
-    default: return gemv_row_kernel<FMT, MODE, L, 1, RING>;
+    case 1: return gemv_row_kernel<FMT, MODE, 1, 1, RING, EMIT>;
+    case 2: return gemv_row_kernel<FMT, MODE, (2 < L ? 2 : L), 1, RING, EMIT>;
+    case 3: return gemv_row_kernel<FMT, MODE, (3 < L ? 3 : L), 1, RING, EMIT>;
+    case 4: return gemv_row_kernel<FMT, MODE, (4 < L ? 4 : L), 1, RING, EMIT>;
+    default: return gemv_row_kernel<FMT, MODE, L, 1, RING, EMIT>;
     }
 }
 
-template <int FMT, int MODE>
+template <int FMT, int MODE, bool EMIT>
 static GrKernel gr_kernel_mode(int lpu, int nseg, int ring)
 {
-    return ring == 3 ? gr_kernel_ring<FMT, MODE, 3>(lpu, nseg) : gr_kernel_ring<FMT, MODE, 2>(lpu, nseg);
+    return ring == 3 ? gr_kernel_ring<FMT, MODE, 3, EMIT>(lpu, nseg) : gr_kernel_ring<FMT, MODE, 2, EMIT>(lpu, nseg);
 }
 
-static GrKernel gr_kernel(int fmt, int mode, int lpu, int nseg, int ring)
+template <int FMT>
+static GrKernel gr_kernel_b(int lpu, int nseg, int ring, bool emit)
+{
+    return emit ? gr_kernel_mode<FMT, MODE_B, true>(lpu, nseg, ring) : gr_kernel_mode<FMT, MODE_B, false>(lpu, nseg, ring);
+}
+
+static GrKernel gr_kernel(int fmt, int mode, int lpu, int nseg, int ring, bool emit)
 {
     if (fmt == FMT_Q8_0)
-        return mode == MODE_A ? gr_kernel_mode<FMT_Q8_0, MODE_A>(lpu, nseg, ring) : gr_kernel_mode<FMT_Q8_0, MODE_B>(lpu, nseg, ring);
-    if (fmt == FMT_Q4_0) return gr_kernel_mode<FMT_Q4_0, MODE_B>(lpu, nseg, ring);  // mode (b) only
-    if (fmt == FMT_Q5_0) return gr_kernel_mode<FMT_Q5_0, MODE_B>(lpu, nseg, ring);
-    return mode == MODE_A ? gr_kernel_mode<FMT_Q4_K, MODE_A>(lpu, nseg, ring) : gr_kernel_mode<FMT_Q4_K, MODE_B>(lpu, nseg, ring);
+        return mode == MODE_A ? gr_kernel_mode<FMT_Q8_0, MODE_A, false>(lpu, nseg, ring) : gr_kernel_b<FMT_Q8_0>(lpu, nseg, ring, emit);
+    if (fmt == FMT_Q4_0) return gr_kernel_b<FMT_Q4_0>(lpu, nseg, ring, emit);  // mode (b) only
+    if (fmt == FMT_Q5_0) return gr_kernel_b<FMT_Q5_0>(lpu, nseg, ring, emit);
+    return mode == MODE_A ? gr_kernel_mode<FMT_Q4_K, MODE_A, false>(lpu, nseg, ring) : gr_kernel_b<FMT_Q4_K>(lpu, nseg, ring, emit);
 }
 
 // LDS layout: x as f32 (padded to whole 1 KB loads), x quantized (int8), its
@@ -560,7 +604,7 @@ static int gr_ring(int fmt, int64_t K)
 // faster here).
 bool gemv_row_supported(int fmt, int mode, int M, int64_t N, int64_t K, bool emit)
 {
-    if ((mode != MODE_A && mode != MODE_B) || M != 1 || emit) return false;
+    if ((mode != MODE_A && mode != MODE_B) || M != 1 || (emit && mode != MODE_B)) return false;
     if (fmt != FMT_Q8_0 && fmt != FMT_Q4_K && fmt != FMT_Q4_0 && fmt != FMT_Q5_0) return false;
     // Q4_0 / Q5_0 mode (a): the staged-activation kernel is faster (on the 8-layer
     // 14336 x 4096 stack 10.3 against 14.0 us for Q4_0), so only mode (b) comes here
@@ -579,8 +623,10 @@ bool gemv_row_supported(int fmt, int mode, int M, int64_t N, int64_t K, bool emi
 int gemv_row_group_max() { return GR_GROUP_MAX; }
 
 hipError_t launch_gemv_row_group(int fmt, int mode, int count, const void* const* w, const int64_t* Ns, float* const* y,
-                                 const float* x, int64_t K, hipStream_t s)
+                                 const float* x, int64_t K, hipStream_t s, const Trace* tr)
 {
+    const bool emit = tr != nullptr;
+    if (emit && (count != 1 || mode != MODE_B)) return hipErrorInvalidValue;
     if (count < 1 || count > GR_GROUP_MAX) return hipErrorInvalidValue;
     int64_t N = 0;
     for (int i = 0; i < count; ++i) {
@@ -614,7 +660,11 @@ hipError_t launch_gemv_row_group(int fmt, int mode, int count, const void* const
     const int64_t cus = device_cus();
     const int64_t rpw = (N + GR_WAVES * cus - 1) / (GR_WAVES * cus);
     const int64_t grid = (N + GR_WAVES * rpw - 1) / (GR_WAVES * rpw);
-    const GrKernel k = gr_kernel(fmt, mode, lpu, nseg, ring);
+    const GrKernel k = gr_kernel(fmt, mode, lpu, nseg, ring, emit);
+    if (emit) {
+        a.sums = tr->sums;
+        a.act = tr->act;
+    }
     static std::set<std::pair<int, const void*>> done;  // dynamic LDS above 64 KB, once per device
     static std::mutex mu;
     {
@@ -631,9 +681,10 @@ hipError_t launch_gemv_row_group(int fmt, int mode, int count, const void* const
     return e != hipSuccess ? e : hipGetLastError();
 }
 
-hipError_t launch_gemv_row(int fmt, int mode, const void* w, const float* x, int64_t N, int64_t K, float* y, hipStream_t s)
+hipError_t launch_gemv_row(int fmt, int mode, const void* w, const float* x, int64_t N, int64_t K, float* y, hipStream_t s,
+                           const Trace* tr)
 {
-    return launch_gemv_row_group(fmt, mode, 1, &w, &N, &y, x, K, s);
+    return launch_gemv_row_group(fmt, mode, 1, &w, &N, &y, x, K, s, tr);
 }
 
 }  // namespace qmm

@@ -40,13 +40,19 @@ struct GemvBufs {
 // Device buffers of the prefill path.
 struct GemmBufs {
     _Float16* a0;   // mode (a): hi part of the scaled activation rows [M][K]; mode (b): the quantized
-                    // activations as int8 [M][K] (block-sums hook: as f16)
+                    // activations as int8 [M][K]
     _Float16* a1;   // lo part [M][K]
     float* rs;      // 1/s per row [M]
     _Float16* xs;   // Q4_K mode (a): hi and lo of s * (sub-block sums) / 32; mode (b): the Q8K
                     // sub-block sums as multiples of 64 and remainders; [M][K/256][16]
-    float* sd;      // mode (b): activation block scales [M][K/32 or K/256]
-    int32_t* sbs;   // block-sums hook, Q4_K: sums of 32 quantized values [M][K/32]
+    float* sd;      // mode (b): activation block scales, block-major [K/32 or K/256][M]
+};
+
+// Outputs of a traced run (mode (b)): the kernels that compute y also write
+// the integer block sums they form and the quantized activations they use.
+struct Trace {
+    int32_t* sums;  // [M][N][block sums per row], see qmatmul_run_traced
+    uint8_t* act;   // canonical Q8_0 / Q8K blocks of x [M][row bytes], or null
 };
 
 GemvGeom gemv_geom(int fmt, int mode, int64_t N, int64_t K, int M, bool emit);
@@ -54,12 +60,13 @@ int device_cus();  // compute units of the current device (cached per device)
 
 // Decode with one activation row, weights streamed row by row.
 bool gemv_row_supported(int fmt, int mode, int M, int64_t N, int64_t K, bool emit);
-hipError_t launch_gemv_row(int fmt, int mode, const void* w, const float* x, int64_t N, int64_t K, float* y, hipStream_t s);
+hipError_t launch_gemv_row(int fmt, int mode, const void* w, const float* x, int64_t N, int64_t K, float* y, hipStream_t s,
+                           const Trace* tr = nullptr);
 // Several problems sharing x and K (their rows end to end) in one launch; at
 // most gemv_row_group_max() of them.
 int gemv_row_group_max();
 hipError_t launch_gemv_row_group(int fmt, int mode, int count, const void* const* w, const int64_t* Ns, float* const* y,
-                                 const float* x, int64_t K, hipStream_t s);
+                                 const float* x, int64_t K, hipStream_t s, const Trace* tr = nullptr);
 bool gemv_supported(int fmt, int64_t K);
 int gemv_max_splits(int fmt, int64_t K);
 
@@ -67,14 +74,19 @@ hipError_t launch_quantize_act(int act_fmt, const float* x, int64_t M, int64_t K
 hipError_t launch_quantize_weights(int fmt, const float* w, int64_t N, int64_t K, void* out, hipStream_t s);
 
 hipError_t launch_gemv(int fmt, int mode, const void* w, const float* x, int64_t N, int64_t K, int M,
-                       const GemvBufs& b, float* y, int32_t* sums, hipStream_t s);
+                       const GemvBufs& b, float* y, hipStream_t s, const Trace* tr = nullptr);
 
-hipError_t launch_gemm_prep(int fmt, int mode, const float* x, int64_t M, int64_t K, const GemmBufs& b, bool sums,
-                            hipStream_t s);
+// act != null (mode (b), traced runs): the canonical activation blocks as well
+hipError_t launch_gemm_prep(int fmt, int mode, const float* x, int64_t M, int64_t K, const GemmBufs& b, hipStream_t s,
+                            uint8_t* act = nullptr);
+// sums (mode (b) only): the traced run, see launch_gemm_q
 hipError_t launch_gemm(int fmt, int mode, const void* w, int64_t N, int64_t K, int64_t M, const GemmBufs& b,
-                       float* y, int32_t* sums, hipStream_t s);
+                       float* y, hipStream_t s, int32_t* sums = nullptr);
+// sums != null: the same kernel also writes its int32 block sums (Q8_0: S per
+// block; Q4_K: S_0..S_7, sumi (from the S_j and the weight scales) and summins
+// per super-block); y may then be null.
 hipError_t launch_gemm_q(int fmt, const void* w, int64_t N, int64_t K, int64_t M, const GemmBufs& b, float* y,
-                         hipStream_t s);
+                         hipStream_t s, int32_t* sums = nullptr);
 
 // Q4_0, Q5_0 and Q6_K weights.  Decode runs (and every Q6_K run) take the
 // ext kernels; Q4_0/Q5_0 prefill transcodes the weights to Q8_0 blocks (same
@@ -87,9 +99,11 @@ struct ExtBufs {
 };
 bool is_ext_format(int fmt);
 int64_t ext_block_bytes(int fmt);
-hipError_t launch_ext_prep(int fmt, const float* x, int64_t M, int64_t K, const ExtBufs& b, hipStream_t s);
+hipError_t launch_ext_prep(int fmt, const float* x, int64_t M, int64_t K, const ExtBufs& b, hipStream_t s,
+                           uint8_t* act = nullptr);
+// tr != null (mode (b)): the traced run, y may then be null
 hipError_t launch_ext_run(int fmt, int mode, const void* w, const float* x, int64_t N, int64_t K, int64_t M,
-                          const ExtBufs& b, float* y, int32_t* sums, hipStream_t s);
+                          const ExtBufs& b, float* y, hipStream_t s, const Trace* tr = nullptr);
 // Grouped decode (M <= 8): up to ext_group_max() problems sharing K, mode and
 // x in one launch; b is the first problem's workspace.
 int ext_group_max();

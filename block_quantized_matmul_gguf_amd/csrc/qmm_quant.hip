@@ -7,14 +7,15 @@
 
 namespace qmm {
 
-enum { LAY_AOS = 0, LAY_GEMM = 2, LAY_I8 = 3 };
+enum { LAY_AOS = 0, LAY_I8 = 3 };
 
 // One thread per 32-value block.  LAY_AOS: canonical 34-byte blocks.
-// LAY_GEMM: the values as f16 [M][K] plus f32 scales [M][K/32].  LAY_I8: the
-// values as int8 [M][K] plus f32 scales block-major [K/32][M].
+// LAY_I8: the values as int8 [M][K] plus f32 scales block-major [K/32][M]
+// (and, for a traced run, the canonical blocks in `act` as well).
 template <int LAY>
 __global__ __launch_bounds__(256) void quantize_q8_0_kernel(const float* __restrict__ x, int M, int K,
-                                                            uint8_t* __restrict__ out, float* __restrict__ sc)
+                                                            uint8_t* __restrict__ out, float* __restrict__ sc,
+                                                            uint8_t* __restrict__ act)
 {
     const int nb = K / 32;
     const int64_t blk = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -27,11 +28,9 @@ __global__ __launch_bounds__(256) void quantize_q8_0_kernel(const float* __restr
     int8_t q[32];
     q8_0_block(a, dbits, dval, q);
     if (LAY == LAY_AOS) {
-        uint16_t* o = reinterpret_cast<uint16_t*>(out + blk * 34);
-        o[0] = dbits;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) o[1 + j] = (uint16_t)((uint8_t)q[2 * j] | ((uint16_t)(uint8_t)q[2 * j + 1] << 8));
+        store_q8_0_block(out + blk * 34, dbits, q);
     } else if (LAY == LAY_I8) {
+        if (act) store_q8_0_block(act + blk * 34, dbits, q);
         uint4* o = reinterpret_cast<uint4*>(out + (int64_t)m * K + 32 * b);
 #pragma unroll
         for (int i = 0; i < 2; ++i)
@@ -40,29 +39,18 @@ __global__ __launch_bounds__(256) void quantize_q8_0_kernel(const float* __restr
                               pack4(q[16 * i + 8], q[16 * i + 9], q[16 * i + 10], q[16 * i + 11]),
                               pack4(q[16 * i + 12], q[16 * i + 13], q[16 * i + 14], q[16 * i + 15]));
         sc[(int64_t)b * M + m] = dval;
-    } else {
-        _Float16* o = reinterpret_cast<_Float16*>(out) + (int64_t)m * K + 32 * b;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            half8_t h;
-#pragma unroll
-            for (int t = 0; t < 8; ++t) h[t] = (_Float16)(float)q[8 * i + t];
-            reinterpret_cast<half8_t*>(o)[i] = h;
-        }
-        sc[(int64_t)m * nb + b] = dval;
     }
 }
 
 // One wave per 256-value block, four blocks per workgroup.  LAY_AOS: canonical
-// 292-byte blocks.  LAY_GEMM: values as f16 [M][K], f32 scales [M][K/256],
-// int32 sums of 32 consecutive values [M][K/32].  LAY_I8: values as int8
+// 292-byte blocks.  LAY_I8: values as int8
 // [M][K], f32 scales block-major [K/256][M], and per block the eight sums of
 // 32 consecutive values as f16 [K/256][M][16]: first each sum rounded down to
 // a multiple of 64, then the remainders (0..63), all exact.
 template <int LAY>
 __global__ __launch_bounds__(256) void quantize_q8k_kernel(const float* __restrict__ x, int M, int K,
                                                            uint8_t* __restrict__ out, float* __restrict__ sc,
-                                                           void* __restrict__ bs)
+                                                           void* __restrict__ bs, uint8_t* __restrict__ act)
 {
     const int nsb = K / 256;
     const int lane = threadIdx.x & 63;
@@ -75,11 +63,9 @@ __global__ __launch_bounds__(256) void quantize_q8k_kernel(const float* __restri
     int q[4], s16;
     q8k_wave(xs, lane, d, q, s16);
     if (LAY == LAY_AOS) {
-        uint8_t* o = out + blk * 292;
-        if (lane == 0) *reinterpret_cast<float*>(o) = d;
-        *reinterpret_cast<uint32_t*>(o + 4 + 4 * lane) = pack4(q[0], q[1], q[2], q[3]);
-        if ((lane & 3) == 0) *reinterpret_cast<int16_t*>(o + 260 + 2 * (lane >> 2)) = (int16_t)s16;
+        store_q8k_lane(out + blk * 292, lane, d, q, s16);
     } else if (LAY == LAY_I8) {
+        if (act) store_q8k_lane(act + blk * 292, lane, d, q, s16);
         const int pair = s16 + __shfl_down(s16, 4);  // lane 8j: bsums[2j] + bsums[2j+1]
         *reinterpret_cast<uint32_t*>(out + (int64_t)m * K + 256 * sb + 4 * lane) = pack4(q[0], q[1], q[2], q[3]);
         if (lane == 0) sc[(int64_t)sb * M + m] = d;
@@ -89,13 +75,6 @@ __global__ __launch_bounds__(256) void quantize_q8k_kernel(const float* __restri
             o[0] = (_Float16)(float)hi;
             o[8] = (_Float16)(float)(pair - hi);
         }
-    } else {
-        const int pair = s16 + __shfl_down(s16, 4);  // lane 8j: bsums[2j] + bsums[2j+1]
-        _Float16* o = reinterpret_cast<_Float16*>(out) + (int64_t)m * K + 256 * sb + 4 * lane;
-        o[0] = (_Float16)(float)q[0]; o[1] = (_Float16)(float)q[1];
-        o[2] = (_Float16)(float)q[2]; o[3] = (_Float16)(float)q[3];
-        if (lane == 0) sc[(int64_t)m * nsb + sb] = d;
-        if ((lane & 7) == 0) reinterpret_cast<int32_t*>(bs)[(int64_t)m * (K / 32) + 8 * sb + (lane >> 3)] = pair;
     }
 }
 
@@ -229,10 +208,10 @@ hipError_t launch_quantize_act(int act_fmt, const float* x, int64_t M, int64_t K
 {
     if (act_fmt == FMT_Q8_0) {
         hipLaunchKernelGGL(quantize_q8_0_kernel<LAY_AOS>, dim3(nblocks(M * (K / 32), 256)), dim3(256), 0, s,
-                           x, (int)M, (int)K, (uint8_t*)out, (float*)nullptr);
+                           x, (int)M, (int)K, (uint8_t*)out, (float*)nullptr, (uint8_t*)nullptr);
     } else {
         hipLaunchKernelGGL(quantize_q8k_kernel<LAY_AOS>, dim3(nblocks(M * (K / 256), 4)), dim3(256), 0, s,
-                           x, (int)M, (int)K, (uint8_t*)out, (float*)nullptr, (void*)nullptr);
+                           x, (int)M, (int)K, (uint8_t*)out, (float*)nullptr, (void*)nullptr, (uint8_t*)nullptr);
     }
     return hipGetLastError();
 }
@@ -245,25 +224,16 @@ hipError_t launch_quantize_weights(int fmt, const float* w, int64_t N, int64_t K
     return hipGetLastError();
 }
 
-hipError_t launch_gemm_prep(int fmt, int mode, const float* x, int64_t M, int64_t K, const GemmBufs& b, bool sums,
-                            hipStream_t s)
+hipError_t launch_gemm_prep(int fmt, int mode, const float* x, int64_t M, int64_t K, const GemmBufs& b, hipStream_t s,
+                            uint8_t* act)
 {
-    if (sums) {  // block-sums hook: quantized values as f16 and their scales
-        if (fmt == FMT_Q8_0)
-            hipLaunchKernelGGL(quantize_q8_0_kernel<LAY_GEMM>, dim3(nblocks(M * (K / 32), 256)), dim3(256), 0, s,
-                               x, (int)M, (int)K, (uint8_t*)b.a0, b.sd);
-        else
-            hipLaunchKernelGGL(quantize_q8k_kernel<LAY_GEMM>, dim3(nblocks(M * (K / 256), 4)), dim3(256), 0, s,
-                               x, (int)M, (int)K, (uint8_t*)b.a0, b.sd, b.sbs);
-        return hipGetLastError();
-    }
     if (mode == MODE_B) {  // int8 values, block scales (and Q8K sub-block sums) for the int8 kernel
         if (fmt == FMT_Q8_0)
             hipLaunchKernelGGL(quantize_q8_0_kernel<LAY_I8>, dim3(nblocks(M * (K / 32), 256)), dim3(256), 0, s,
-                               x, (int)M, (int)K, (uint8_t*)b.a0, b.sd);
+                               x, (int)M, (int)K, (uint8_t*)b.a0, b.sd, act);
         else
             hipLaunchKernelGGL(quantize_q8k_kernel<LAY_I8>, dim3(nblocks(M * (K / 256), 4)), dim3(256), 0, s,
-                               x, (int)M, (int)K, (uint8_t*)b.a0, b.sd, (void*)b.xs);
+                               x, (int)M, (int)K, (uint8_t*)b.a0, b.sd, (void*)b.xs, act);
         return hipGetLastError();
     }
     const dim3 grid((unsigned)M), block(256);

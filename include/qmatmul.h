@@ -217,15 +217,30 @@ int qmatmul_quantize_weights(int format, const float* w, int64_t N, int64_t K,
                              void* out_blocks, void* stream);
 
 /*
- * Test hook (mode (b) plans only): the integer parts of the run, from the
- * same kernels.  sums: device int32 [M x N x qmatmul_block_sums_per_row(format, K)].
- * Q8_0, Q4_0, Q5_0: S[m][n][b] = sum over block b of qw*qx with qw the signed
- * weight value (q - 8, q - 16 for Q4_0, Q5_0).  Q4_K: per super-block i ten
- * values S_0..S_7 (per 32), sumi = sum_j sc_j*S_j, summins = sum_j m_j*(bsums[2j]+bsums[2j+1]).
- * Q6_K: per super-block 17 values S_0..S_15 (per 16, qw = q - 32) and
- * sumi = sum_j sc_j*S_j.
- * Same preconditions as qmatmul_run; y is not written.
+ * Traced run (mode (b) plans only): qmatmul_run's own kernels, with the same
+ * launch configuration, compiled with a flag that also writes out the integer
+ * parts the method fixes exactly (page "同一个 GGUF，CPU 和 Metal 生成的文字不一样",
+ * section 出处: integer block dot products, then the scales).
+ *   y: as qmatmul_run writes it, bit for bit (NULL: not written).
+ *   sums: device int32 [M x N x qmatmul_block_sums_per_row(format, K)]:
+ *     Q8_0, Q4_0, Q5_0: S[m][n][b] = sum over block b of qw*qx, qw the signed
+ *       weight value (q, q - 8, q - 16);
+ *     Q4_K: per super-block ten values S_0..S_7 (per 32 values), sumi =
+ *       sum_j sc_j*S_j and summins = sum_j m_j*(bsums[2j]+bsums[2j+1]);
+ *     Q6_K: per super-block 17 values S_0..S_15 (per 16, qw = q - 32) and
+ *       sumi = sum_j sc_j*S_j.
+ *     At M > 8 the Q4_K prefill kernel scales each S_j on its own and never
+ *     forms sumi; there sumi is summed from the S_j it wrote.
+ *   act_blocks: device, M * qmatmul_row_bytes(Q8_0 or Q8_K, K) bytes, 4-byte
+ *     aligned, or NULL: the canonical quantized activation blocks, written by
+ *     the kernel that quantizes them in this run (a decode kernel's own
+ *     prologue, or the activation preparation of the prefill).
+ * Same preconditions and errors as qmatmul_run; sums must not be NULL.
  */
+int qmatmul_run_traced(const qmm_plan* plan, const void* w_blocks, const float* x, float* y, int32_t* sums,
+                       void* act_blocks, int64_t M, void* stream);
+
+/* qmatmul_run_traced(plan, w_blocks, x, NULL, sums, NULL, M, stream). */
 int qmatmul_run_block_sums(const qmm_plan* plan, const void* w_blocks, const float* x,
                            int32_t* sums, int64_t M, void* stream);
 

@@ -122,5 +122,22 @@ def integer_acts(seed: int, m: int, k: int, block: int) -> np.ndarray:
     return x
 
 
+def tie_rows(seed: int, k: int) -> np.ndarray:
+    """Two activation rows built around the quantizers' tie rules (values only).
+
+    Row 0: every 32-value block holds 127 (so an absmax/127 scale is exactly
+    1) and the half-way values 2.5, -2.5, 0.5 beside N(0,1) draws.  Row 1:
+    every 256-value block holds +8 and -8 at offsets 5 and 9 (the order of the
+    signs alternating from block to block) above N(0, 0.25) draws, so its two
+    largest magnitudes tie with opposite signs."""
+    x = np.stack([normal_f32(seed, (k,)), normal_f32(seed + 1, (k,), 0.5)])
+    for b in range(k // 32):
+        x[0, 32 * b: 32 * b + 4] = [127.0, 2.5, -2.5, 0.5]
+    for sb in range(k // 256):
+        s = 1.0 if sb % 2 == 0 else -1.0
+        x[1, 256 * sb + 5], x[1, 256 * sb + 9] = 8.0 * s, -8.0 * s
+    return x
+
+
 def random_bytes(seed: int, n: int) -> np.ndarray:
     return np.random.default_rng(seed).integers(0, 256, size=n, dtype=np.uint8)

@@ -147,14 +147,28 @@ def test_integer_special_case_is_exact(fmt, n, k, mode, m):
     assert g is not None
 
 
-@pytest.mark.parametrize("fmt,n,k", [(qmm.Q4_0, 70, 576), (qmm.Q5_0, 33, 1536), (qmm.Q6_K, 45, 768)])
-@pytest.mark.parametrize("m", [1, 3, 8, 11])
-def test_block_sums_bit_exact(fmt, n, k, m):
+@pytest.mark.parametrize("fmt,n,k", [(qmm.Q4_0, 70, 576), (qmm.Q5_0, 33, 1536), (qmm.Q6_K, 45, 768),
+                                     (qmm.Q4_0, 41, 16384), (qmm.Q6_K, 30, 4096)])
+@pytest.mark.parametrize("m", [1, 2, 3, 8, 11])
+def test_traced_run_integer_parts_bit_exact(fmt, n, k, m):
+    # the run's own kernels (one-row decode, staged decode with the activations
+    # quantized in its prologue or by the preparation launch, the Q8_0 prefill
+    # on the rewritten weights) with their integer parts written out
     wq = oracle.quantize(fmt, synth.weights_f32(7700 + n, n, k))
     x = synth.acts_f32(7701 + m, m, k)
+    ties = synth.tie_rows(7702 + m, k)
+    if m == 1:
+        x[0] = ties[1 if fmt == qmm.Q6_K else 0]
+    else:
+        x[:2] = ties
     want = oracle.block_sums(fmt, wq, n, k, x)
     with qmm.Plan(fmt, n, k, m, qmm.MODE_QACT) as p:
-        got = host(p.block_sums(dev(wq), dev(x))).astype(np.int64)
+        wd, xd = dev(wq), dev(x)
+        y, sums, act = p.run_traced(wd, xd)
+        y_run = host(p.run(wd, xd))
+    y, got, act = host(y), host(sums).astype(np.int64), host(act)
+    assert np.array_equal(y.view(np.uint32), y_run.view(np.uint32)), (NAME[fmt], m, "traced y")
+    assert np.array_equal(act, oracle.quantize(qmm.ACT_FORMAT[fmt], x)), (NAME[fmt], m, "activations")
     assert np.array_equal(got.reshape(want.shape), want), (NAME[fmt], m)
 
 

@@ -209,20 +209,47 @@ def test_integer_special_case_is_exact(fmt, mode, m):
     assert np.array_equal(y.astype(np.float64), exact)
 
 
-@pytest.mark.parametrize("fmt,n,k", [(qmm.Q8_0, 200, 576), (qmm.Q8_0, 130, 4096), (qmm.Q4_K, 100, 1536)])
-@pytest.mark.parametrize("m", [1, 3, 8, 20])
-def test_block_sums_bit_exact(fmt, n, k, m):
-    wq = oracle.quantize(fmt, synth.weights_f32(3000 + n, n, k))
-    x = synth.acts_f32(3100 + m, m, k)
+# The traced run: the kernels that compute y (the one-row decode at M = 1,
+# the tile decode at M <= 8 and past the one-row kernel's K, the int8 prefill
+# at M > 8), with their integer parts written out.  Its y equals the plain
+# run's bit for bit; its block sums and the quantized activations its own
+# prologue or preparation formed equal the oracle's.  Rows built around the
+# tie rules (half-way values; two maxima of opposite sign) are part of x.
+TRACED = [
+    (qmm.Q8_0, 200, 576, 1), (qmm.Q8_0, 130, 4096, 1), (qmm.Q8_0, 41, 16384, 1), (qmm.Q8_0, 30, 20480, 1),
+    (qmm.Q4_K, 100, 1536, 1), (qmm.Q4_K, 41, 16384, 1), (qmm.Q4_K, 30, 20480, 1),
+    (qmm.Q8_0, 200, 576, 3), (qmm.Q8_0, 130, 4096, 8), (qmm.Q4_K, 100, 1536, 2), (qmm.Q4_K, 300, 4096, 8),
+    (qmm.Q8_0, 200, 576, 20), (qmm.Q8_0, 130, 4096, 37), (qmm.Q8_0, 300, 4096, 130),
+    (qmm.Q4_K, 100, 1536, 37), (qmm.Q4_K, 300, 4096, 130), (qmm.Q4_K, 70, 256, 9),
+]
+
+
+def traced_inputs(fmt, n, k, m, seed):
+    wq = oracle.quantize(fmt, synth.weights_f32(seed, n, k))
+    x = synth.acts_f32(seed + 1, m, k)
+    ties = synth.tie_rows(seed + 2, k)
+    if m == 1:
+        x[0] = ties[1 if k % 256 == 0 and fmt != qmm.Q8_0 else 0]
+    else:
+        x[:2] = ties
+    return wq, x
+
+
+@pytest.mark.parametrize("fmt,n,k,m", TRACED, ids=[f"{FMT_NAME[f]}-{n}x{k}-M{m}" for f, n, k, m in TRACED])
+def test_traced_run_integer_parts_bit_exact(fmt, n, k, m):
+    wq, x = traced_inputs(fmt, n, k, m, 3000 + n + m)
     with qmm.Plan(fmt, n, k, m, qmm.MODE_QACT) as p:
-        got = host(p.block_sums(dev(wq), dev(x))).astype(np.int64)
-    want = oracle.block_sums(fmt, wq, n, k, x)
-    if fmt == qmm.Q4_K and m > qmm.GEMV_MAX_M:
-        # the prefill kernel folds the sub-block scales into its operands, so it
-        # yields sumi and summins per super-block but not the per-32 sums
-        got = got.reshape(m, n, -1, 10)[..., 8:]
-        want = want.reshape(m, n, -1, 10)[..., 8:]
-    assert np.array_equal(got, want)
+        wd, xd = dev(wq), dev(x)
+        y, sums, act = p.run_traced(wd, xd)
+        y_run = host(p.run(wd, xd))
+        sums_only = host(p.block_sums(wd, xd))
+    y, sums, act = host(y), host(sums).astype(np.int64), host(act)
+    assert np.array_equal(y.view(np.uint32), y_run.view(np.uint32)), "traced y differs from the plain run"
+    assert np.array_equal(act, oracle.quantize(qmm.ACT_FORMAT[fmt], x)), "quantized activations"
+    assert np.array_equal(sums, oracle.block_sums(fmt, wq, n, k, x)), "block sums"
+    assert np.array_equal(sums_only.astype(np.int64), sums)
+    yr, a = ref(fmt, qmm.MODE_QACT, wq, n, k, x)
+    assert_within(y, yr, a, f"traced {FMT_NAME[fmt]} {n}x{k} M={m}")
 
 
 @pytest.mark.parametrize("fmt,mode,m", [(qmm.Q8_0, 0, 1), (qmm.Q8_0, 1, 8), (qmm.Q4_K, 0, 8),
