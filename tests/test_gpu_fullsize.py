@@ -52,11 +52,25 @@ def check(fmt, mode, w_f32, w_gpu_blocks, x, y_gpu, cols, what):
                            f"{float((err / np.maximum(a, 1e-300)).max()):.3e}")
 
 
-def sample_cols(n, count, seed):
+def sample_cols(n, count, seed, stripe=None):
+    """`count` random columns, the first and last (ragged tile tails) and, with
+    `stripe`, one random column in every `stripe`-wide run of columns, so that
+    every output tile of that width (and its place in the XCD remapping of the
+    workgroups) is compared."""
     g = np.random.default_rng(seed)
     cols = set(g.choice(n, size=min(count, n), replace=False).tolist())
-    cols.update({0, n - 1})  # first and last rows (ragged tile tails)
+    cols.update({0, n - 1})
+    if stripe:
+        for c0 in range(0, n, stripe):
+            cols.add(int(c0 + g.integers(0, min(stripe, n - c0))))
     return np.array(sorted(cols))
+
+
+# The prefill kernels' output tiles are 64 to 224 columns wide (every width a
+# multiple of 32, the narrowest 64); the decode kernels' tiles are 16 rows of
+# the weights.  Sampling one column per 32 covers every prefill tile, one per
+# 16 every decode tile.
+PREFILL_STRIPE, DECODE_STRIPE = 32, 16
 
 
 def run_problem(fmt, mode, prob, m_max=None, cols=48, seed=0):
@@ -102,7 +116,8 @@ def test_smollm2_prefill_all_layers(mode, mname):
                     plans[key] = qmm.Plan(fmt, prob.n, prob.k, synth.PREFILL_TOKENS, mode)
                 wg = qmm.quantize_weights(fmt, torch.from_numpy(w).cuda())
                 y = host(plans[key].run(wg, xg))
-                check(fmt, mode, w, wg, x, y, sample_cols(prob.n, 8, 40 + i), f"{prob.name} fmt={fmt}")
+                check(fmt, mode, w, wg, x, y, sample_cols(prob.n, 8, 40 + i, PREFILL_STRIPE),
+                      f"{prob.name} fmt={fmt}")
     finally:
         for p in plans.values():
             p.close()
@@ -132,5 +147,6 @@ def test_scaleup_all_batch_sizes(scaleup, fmt, mode, mname):
             for m in (1, 8, 512):
                 xm = np.ascontiguousarray(x[:m])
                 y = host(p.run(wg[fmt], torch.from_numpy(xm).cuda()))
-                check(fmt, mode, w, wg[fmt], xm, y, sample_cols(n, 24 if m == 512 else 96, layer * 10 + m),
+                stripe = PREFILL_STRIPE if m == 512 else DECODE_STRIPE
+                check(fmt, mode, w, wg[fmt], xm, y, sample_cols(n, 24, layer * 10 + m, stripe),
                       f"scale-up L{layer} fmt={fmt} M={m}")

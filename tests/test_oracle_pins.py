@@ -272,6 +272,72 @@ def test_q8_k_round_trip_bound_and_range():
     assert np.all(np.abs(q).max(-1) == 127)
 
 
+# ------------------------------------------------ the flagged variants --
+# The oracle carries the readings the pages leave open behind variant flags
+# (Q8_0: x / d in place of x * (1/d), ties to even; Q8K: -128/max in place of
+# -127/max, ties to even).  Only the default reading runs anywhere else; the
+# variants are pinned here so that a flag means what it says.
+
+def test_q8_0_variants_on_a_hand_worked_block():
+    # amax 127 makes d = 1 and 1/d = 1 exactly: x * id = x / d = x
+    x = np.zeros((1, 32), np.float32)
+    x[0, :6] = [127.0, 2.5, -2.5, 0.5, 1.5, -0.5]
+    away = [127, 3, -3, 1, 2, -1]   # half away from zero (the default)
+    even = [127, 2, -2, 0, 2, 0]    # ties to even (variant bit 1)
+    for variant, want in ((0, away), (1, away), (2, even), (3, even)):
+        q = oracle.quantize(Q8_0, x, variant)[0, 2:].view(np.int8)
+        assert list(q[:6]) == want, variant
+        assert not q[6:].any()
+
+
+def test_q8_0_division_variant_differs_rarely_and_where_predicted():
+    # The survey measured that x / d and x * (1/d) disagree on a few values
+    # per million.  Predict every disagreement with NumPy's IEEE f32 division
+    # and multiplication (one correctly rounded operation each), then require
+    # the oracle's two variants to land on the predicted sides of it.
+    w = synth.weights_f32(5000, 2048, 4096)            # 8.4M values of the scale-up's layer 0
+    blocks = w.reshape(-1, 32)
+    d = (np.abs(blocks).max(1) / np.float32(127.0)).astype(np.float32)[:, None]
+    id_ = np.where(d != 0, np.float32(1.0) / np.where(d != 0, d, 1), 0).astype(np.float32)
+    t_mul = (blocks * id_).astype(np.float64)
+    t_div = (blocks / np.where(d != 0, d, 1)).astype(np.float64)
+
+    def half_away(t):
+        return np.sign(t) * np.floor(np.abs(t) + 0.5)
+
+    q_mul, q_div = half_away(t_mul), half_away(t_div)
+    differ = q_mul != q_div
+    count = int(differ.sum())
+    print(f"x/d and x*(1/d) differ on {count} of {differ.size} values")
+    assert 0 < count < 1e-5 * differ.size
+    rows = np.unique(np.argwhere(differ)[:, 0])
+    sel = blocks[rows]
+    got0 = oracle.quantize(Q8_0, sel, 0).reshape(len(rows), 34)[:, 2:].view(np.int8)
+    got1 = oracle.quantize(Q8_0, sel, 1).reshape(len(rows), 34)[:, 2:].view(np.int8)
+    assert np.array_equal(got0, q_mul[rows].astype(np.int8))
+    assert np.array_equal(got1, q_div[rows].astype(np.int8))
+    assert not np.array_equal(got0, got1)
+
+
+def test_q8_k_variants_on_a_hand_worked_block():
+    # max 2.0: iscale = -127/2 = -63.5 (default) or -128/2 = -64 (bit 0), both exact
+    x = np.zeros((1, 256), np.float32)
+    x[0, :5] = [2.0, 1.0, -0.5, 0.25, 0.0078125]
+    cases = {
+        0: ([-127, -64, 32, -16, 0], np.float32(1.0) / np.float32(-63.5)),  # -63.5, 31.75, -15.875, -0.496
+        1: ([-128, -64, 32, -16, -1], np.float32(-0.015625)),               # ..., -0.5 -> -1 (away)
+        2: ([-127, -64, 32, -16, 0], np.float32(1.0) / np.float32(-63.5)),  # -63.5 -> -64 either way
+        3: ([-128, -64, 32, -16, 0], np.float32(-0.015625)),                # -0.5 -> 0 (even)
+    }
+    for variant, (want, dwant) in cases.items():
+        blk = oracle.quantize(Q8_K, x, variant)[0]
+        q = blk[4:260].view(np.int8)
+        assert list(q[:5]) == want, variant
+        assert not q[5:].any()
+        assert blk[:4].copy().view(np.float32)[0] == dwant, variant
+        assert blk[260:262].copy().view(np.int16)[0] == sum(want), variant
+
+
 # ------------------------------------------------- integer special cases --
 
 def test_integer_case_q8_0_both_modes_exact():
