@@ -88,14 +88,15 @@ def traffic_from_profile(key):
     return None if entry is None else entry.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(layers, min_seconds=10.0):
+def cpu_baseline(layers, min_seconds=10.0, threads=None):
     """The oracle on the decode phase of the step (M = 1 and 8, both formats,
-    both modes) over the first `layers` layers, all host threads; the phase is
-    repeated until at least `min_seconds` of oracle time have been measured."""
+    both modes) over the first `layers` layers, on `threads` host threads (all
+    by default); the phase is repeated until at least `min_seconds` of oracle
+    time have been measured."""
     import oracle
     import synth
 
-    want = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    want = threads or int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     threads = oracle.set_threads(min(want, os.cpu_count() or 1))
     x = synth.acts_f32(5100, M_PREFILL, K)
     wqs = []
@@ -123,6 +124,88 @@ def cpu_baseline(layers, min_seconds=10.0):
                   f"modes a and b, N=14336 K=4096), repeated {reps} times: {total_bytes / 1e9:.2f} GB of weight "
                   f"blocks in {total_s:.1f} s",
     }
+
+
+def timed_rows(qmm, torch, runs, stream, args):
+    """[(label, fn)] -> per-call microseconds from HIP events on the launch
+    stream, each fn one launch-group of `n` calls: fn() returns n."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    out = []
+    for label, fn in runs:
+        for _ in range(max(1, args.warmup)):
+            fn()
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        calls = 0
+        for _ in range(args.steps):
+            calls += fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        out.append((label, ev[0].elapsed_time(ev[1]) * 1000.0 / calls))
+    return out
+
+
+def q4k_sixteen_layers(qmm, torch, synth, wq8, modes, xs, ys, stream, args):
+    """Decode (M = 1 and 8, both modes) over 16 stacked 14336x4096 Q4_K layers
+    (528 MB of blocks, twice the Infinity Cache): the step's 8 layers plus 8
+    more seeded the same way, rotated per launch so the weights stream from
+    HBM.  Outside the step and its value."""
+    dev = xs[1].device
+    layers = list(wq8)
+    for layer in range(LAYERS, 2 * LAYERS):
+        wf = torch.from_numpy(synth.weights_f32(5000 + layer, N, K)).to(dev)
+        layers.append(qmm.quantize_weights(qmm.Q4_K, wf))
+        del wf
+    b = layers[0].numel()
+    rows = []
+    for md, mcode in modes.items():
+        with qmm.Plan(qmm.Q4_K, N, K, max(DECODE_M), mcode) as plan:
+            def fn(m):
+                def run():
+                    for w in layers:
+                        plan.run(w, xs[m], ys[m], stream)
+                    return len(layers)
+                return run
+            for (label, us) in timed_rows(qmm, torch, [(m, fn(m)) for m in DECODE_M], stream, args):
+                rows.append({"mode": md, "M": label, "us_per_launch": round(us, 3),
+                             "weight_GBps": round(b / (us * 1e-6) / 1e9, 1),
+                             "frac_hbm": round(b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)})
+    del layers
+    torch.cuda.synchronize()
+    return {"layers": 2 * LAYERS, "bytes": b * 2 * LAYERS, "rows": rows}
+
+
+def one_gpu_share(qmm, torch, wq, fmts, modes, xs, ys, stream, args, shards=8):
+    """The kernel on one GPU's share of the scale-up when its output rows are
+    split over 8 GPUs: N = 14336/8 = 1792, K = 4096.  The 8 row shards of each
+    of the step's 8 layers (64 shards, the whole 499 / 264 MB) are rotated per
+    launch, so the weights stream from HBM.  Decode M = 1 and 8, prefill
+    M = 512, both formats and modes.  Outside the step and its value."""
+    ns = N // shards
+    rows = []
+    for f, code in fmts.items():
+        rb = wq[f][0].numel() // N
+        views = [w[i * ns:(i + 1) * ns] for w in wq[f] for i in range(shards)]  # [ns, row bytes] row shards
+        b = ns * rb
+        ysh = {m: ys[m][:, :ns].contiguous() for m in ys}
+        for md, mcode in modes.items():
+            with qmm.Plan(code, ns, K, M_PREFILL, mcode) as plan:
+                def fn(m):
+                    def run():
+                        sel = views if m <= 8 else views[::shards]  # prefill: one shard per layer
+                        for w in sel:
+                            plan.run(w, xs[m], ysh[m], stream)
+                        return len(sel)
+                    return run
+                for (m, us) in timed_rows(qmm, torch, [(m, fn(m)) for m in DECODE_M + (M_PREFILL,)], stream, args):
+                    r = {"fmt": f, "mode": md, "M": m, "us_per_launch": round(us, 3)}
+                    if m <= 8:
+                        r["weight_GBps"] = round(b / (us * 1e-6) / 1e9, 1)
+                        r["frac_hbm"] = round(b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+                    else:
+                        r["TOPS"] = round(2.0 * m * ns * K / (us * 1e-6) / 1e12, 1)
+                    rows.append(r)
+    return {"N": ns, "K": K, "shards_rotated": len(wq["q8_0"]) * shards, "rows": rows}
 
 
 def other_formats_decode(qmm, torch, wq, others, modes, xs, ys, stream, args):
@@ -567,35 +650,46 @@ def main():
         out["prefill"] = {"TOPS": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 1),
                           "frac_f16_peak": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4),
                           "frac_int8_peak": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / PEAK_I8_TOPS, 4)}
-    # roofline of the decode kernel: Q8_0 weights, quantized activations, one token
-    r = pick("gemv", "q8_0", "b", 1) or (detail[0] if detail and detail[0]["kernel"] == "gemv" else None)
-    if r is not None:
+    def gemv_roof(r):
         b = layer_bytes[r["fmt"]]
-        out["roofline"] = {
+        return {
             "kernel": f"{'gemv_row_kernel' if r['M'] == 1 else 'gemv_kernel'} {r['fmt']} mode {r['mode']} M={r['M']}",
             "bound": "hbm", "achieved": r["weight_GBps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": r["frac_hbm"], "algorithmic_bytes_per_launch": b,
             "traffic": traffic_from_profile(f"gemv:{r['fmt']}:{r['mode']}:{r['M']}"),
         }
-    rg = pick("gemm", "q8_0", "a", M_PREFILL) or next((d for d in detail if d["kernel"] == "gemm"), None)
-    if rg is not None:
-        out["roofline_gemm"] = {
-            "kernel": f"gemm_kernel {rg['fmt']} mode {rg['mode']} M={rg['M']}",
-            "bound": "mfma", "achieved": rg["TOPS"], "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
-            "frac": rg["frac_f16_peak"], "algorithmic_flops_per_launch": 2 * rg["M"] * N * K,
-            "traffic": traffic_from_profile(f"gemm:{rg['fmt']}:{rg['mode']}:{rg['M']}"),
+
+    def gemm_roof(r):
+        # mode (a) runs on the f16 matrix cores (hi/lo split), mode (b) on the int8 ones
+        int8 = r["mode"] == "b"
+        return {
+            "kernel": f"{'gemm_q_kernel' if int8 else 'gemm_kernel'} {r['fmt']} mode {r['mode']} M={r['M']}",
+            "bound": "mfma", "achieved": r["TOPS"], "peak": PEAK_I8_TOPS if int8 else PEAK_F16_TFLOPS,
+            "unit": "TOP/s" if int8 else "TFLOP/s",
+            "frac": r["frac_int8_peak"] if int8 else r["frac_f16_peak"],
+            "algorithmic_ops_per_launch": 2 * r["M"] * N * K,
+            "traffic": traffic_from_profile(f"gemm:{r['fmt']}:{r['mode']}:{r['M']}"),
         }
-    rb = pick("gemm", "q8_0", "b", M_PREFILL)
-    if rb is not None:  # mode (b) prefill runs on the int8 matrix cores
-        out["roofline_gemm_int8"] = {
-            "kernel": f"gemm_q_kernel {rb['fmt']} mode {rb['mode']} M={rb['M']}",
-            "bound": "mfma", "achieved": rb["TOPS"], "peak": PEAK_I8_TOPS, "unit": "TOP/s",
-            "frac": rb["frac_int8_peak"], "algorithmic_ops_per_launch": 2 * rb["M"] * N * K,
-            "traffic": traffic_from_profile(f"gemm:{rb['fmt']}:{rb['mode']}:{rb['M']}"),
-        }
+
+    # the step's dominant kernel: the launch group with the most time per step
+    if detail:
+        i_dom = max(range(len(detail)), key=lambda i: group_ms[i])
+        d = detail[i_dom]
+        out["roofline"] = gemv_roof(d) if d["kernel"] == "gemv" else gemm_roof(d)
+        out["roofline"]["share_of_step"] = round(group_ms[i_dom] / sum(group_ms), 4)
+    r = pick("gemv", "q8_0", "b", 1)
+    if r is not None:  # the headline decode kernel: Q8_0 weights, quantized activations, one token
+        out["roofline_gemv"] = gemv_roof(r)
+    for md in modes:
+        rg = pick("gemm", "q8_0", md, M_PREFILL)
+        if rg is not None:
+            out[f"roofline_gemm_{md}"] = gemm_roof(rg)
     out["detail"] = detail
     if others:
         out["other_formats"] = other_formats_decode(qmm, torch, wq, others, modes, xs, ys, stream, args)
+    if not args.only:
+        out["one_gpu_share"] = one_gpu_share(qmm, torch, wq, fmts, modes, xs, ys, stream, args)
+        out["q4_k_16_layers"] = q4k_sixteen_layers(qmm, torch, synth, wq["q4_k"], modes, xs, ys, stream, args)
     if not args.only and not args.no_dequant:
         out["dequantize_all"] = dequant_context(qmm, torch, wq, xs, ys, fmts, stream, args)
     out["wall_s_timed"] = round(wall_s, 3)
@@ -603,6 +697,7 @@ def main():
     out["weights_fit_infinity_cache_256MB"] = {f: layer_bytes[f] * LAYERS <= 256 * 2 ** 20 for f in fmts}
     if not args.no_cpu_baseline and not args.only:
         out["cpu_baseline"] = cpu_baseline(args.cpu_layers)
+        out["cpu_baseline_1thread"] = cpu_baseline(1, min_seconds=3.0, threads=1)
     for p in plans.values():
         p.close()
     print(json.dumps(out))

@@ -15,17 +15,18 @@
 // of 64 and a remainder in [0, 63] (exact f16 integers), so the f32 result is
 // the exact integer sum.
 //
-// A 256-thread workgroup owns a 64 x (32*TN) output tile; two run on each
-// compute unit.  Its four waves are two row halves times two K groups: K
-// advances 64 values (two blocks) per stage, group g takes block g of every
-// stage over all 32*TN columns, and the two groups' partial sums are added
-// through LDS at the end.  A stage's activation bytes, raw weight bytes and
-// scales are loaded to registers two stages ahead and written to the idle LDS
-// buffer at the start of the next stage; one barrier per stage.  Consecutive
-// lanes load consecutive 16-byte pieces of one weight row, so that a load
-// instruction touches few rows; the Q8_0 blocks (two bytes of scale before
-// their values) are realigned in registers with one lane exchange and a byte
-// permute per dword.
+// A workgroup of 128*MW threads owns a (32*MW) x (32*TN) output tile: MW
+// slices of 32 rows times two K groups (the launched 128 x 224 tile: 512
+// threads, one workgroup per compute unit on 512 x 14336).  K advances 64
+// values (two blocks) per stage, group g takes block g of every stage over
+// all 32*TN columns, and the two groups' partial sums are added through LDS at
+// the end.  Registers hold the stage after the one in LDS: they are written
+// to the idle LDS buffer one item per MFMA of the current stage, then the
+// following stage is loaded; one barrier per stage.  Consecutive lanes load
+// consecutive 16-byte pieces of one weight row, so that a load instruction
+// touches few rows; the Q8_0 blocks (two bytes of scale before their values)
+// are realigned in registers with one lane exchange and a byte permute per
+// dword.
 #include <map>
 #include <mutex>
 #include <set>
