@@ -139,10 +139,10 @@ static size_t layout(qmm_plan* p, char* base)
         return off;
     }
     if (is_ext_format(p->fmt)) {
-        // Q6_K: every run takes the ext kernels; Q4_0/Q5_0: decode runs do, and
-        // prefill runs take the Q8_0 kernels on transcoded weights.
+        // Decode runs take the ext kernels; prefill runs: Q6_K its f16 prefill
+        // kernel, Q4_0/Q5_0 the Q8_0 kernels on transcoded weights.
         const bool q6 = p->fmt == QMM_Q6_K, pre = !q6 && p->M_max > GEMV_MAX_M;
-        const int64_t Mx = q6 ? p->M_max : std::min<int64_t>(p->M_max, GEMV_MAX_M);
+        const int64_t Mx = std::min<int64_t>(p->M_max, GEMV_MAX_M);
         p->gv = GemvBufs{};
         p->gm = GemmBufs{};
         if (!a) {
@@ -150,9 +150,14 @@ static size_t layout(qmm_plan* p, char* base)
             p->ex.xd = (float*)take(4 * (size_t)Mx * (q6 ? K / 256 : K / 32));
             p->ex.xs = (int32_t*)take(4 * (size_t)Mx * (q6 ? K / 16 : K / 32));
         }
-        if (q6 && a && p->M_max > GEMV_MAX_M) {
-            // Q6_K mode (a) prefill: the weights decoded to f32, then the f32 GEMM
-            p->wdeq = (float*)take(4 * (size_t)N * K);
+        if (q6 && p->M_max > GEMV_MAX_M) {
+            // mode (a): hi, lo of x*s and 1/s; mode (b): the Q8K values as f16 and the block scales
+            const int64_t M = p->M_max;
+            p->gm.a0 = (_Float16*)take(2 * M * K);
+            p->gm.a1 = (_Float16*)take(a ? 2 * M * K : 0);
+            p->gm.rs = (float*)take(a ? 4 * M : 0);
+            p->gm.xs = nullptr;
+            p->gm.sd = (float*)take(a ? 0 : 4 * M * (K / 256));
         }
         if (pre) {
             p->ex.tw = (uint8_t*)take((size_t)N * (K / 32) * 34);
@@ -221,7 +226,7 @@ extern "C" int qmatmul_create(qmm_plan** out, int format, int64_t N, int64_t K, 
                     hipGetErrorString(e));
     }
     layout(p, (char*)p->ws);
-    const bool dense = mode == QMM_MODE_DEQUANT || (format == QMM_Q6_K && mode == QMM_MODE_F32ACT && M_max > GEMV_MAX_M);
+    const bool dense = mode == QMM_MODE_DEQUANT;
     if (dense && dense_create(&p->dense) != 0) {
         (void)hipFree(p->ws);
         delete p;
@@ -274,21 +279,16 @@ static int run_impl(const qmm_plan* p, const void* w, const float* x, float* y, 
         if (st != 0) return fail(QMM_EHIP, "rocblas_sgemm: status %d", st);
         return QMM_OK;
     }
-    if (p->fmt == QMM_Q6_K && p->mode == QMM_MODE_F32ACT && M > GEMV_MAX_M) {
-        // mode (a) prefill: the f32 product of the exactly decoded weights
-        e = launch_ext_dequantize(p->fmt, w, p->N, p->K, p->wdeq, s);
-        if (e != hipSuccess) return fail(QMM_EHIP, "kernel launch: %s", hipGetErrorString(e));
-        const int st = dense_gemm(p->dense, p->wdeq, x, y, M, p->N, p->K, s);
-        if (st != 0) return fail(QMM_EHIP, "rocblas_sgemm: status %d", st);
-        return QMM_OK;
-    }
     uint8_t* act = tr ? tr->act : nullptr;
     int32_t* sums = tr ? tr->sums : nullptr;
     if (is_ext_format(p->fmt)) {
         if (M == 1 && gemv_row_supported(p->fmt, p->mode, 1, p->N, p->K, tr != nullptr)) {
             e = launch_gemv_row(p->fmt, p->mode, w, x, p->N, p->K, y, s, tr);  // Q4_0, Q5_0: the one-row kernel
-        } else if (M <= GEMV_MAX_M || p->fmt == QMM_Q6_K) {
+        } else if (M <= GEMV_MAX_M) {
             e = launch_ext_run(p->fmt, p->mode, w, x, p->N, p->K, M, p->ex, y, s, tr);
+        } else if (p->fmt == QMM_Q6_K) {
+            e = launch_gemm_prep(FMT_Q6_K, p->mode, x, M, p->K, p->gm, s, act);
+            if (e == hipSuccess) e = launch_gemm(FMT_Q6_K, p->mode, w, p->N, p->K, M, p->gm, y, s, sums);
         } else {
             e = launch_ext_to_q8_0(p->fmt, w, p->N, p->K, p->ex.tw, s);
             if (e == hipSuccess) e = launch_gemm_prep(FMT_Q8_0, p->mode, x, M, p->K, p->gm, s, act);
@@ -327,9 +327,6 @@ int qmm::run_on_scratch(int format, int64_t N, int64_t K, int64_t M, int mode, c
     if (mode == QMM_MODE_DEQUANT)
         return fail(QMM_EUNSUPPORTED, "the dequantize-all form (mode 2) takes a library GEMM that allocates; "
                     "use qmatmul_create and qmatmul_run");
-    if (format == QMM_Q6_K && mode == QMM_MODE_F32ACT && M > GEMV_MAX_M)
-        return fail(QMM_EUNSUPPORTED, "Q6_K mode (a) at M > %d takes a library GEMM that allocates; use "
-                    "qmatmul_create and qmatmul_run", GEMV_MAX_M);
     qmm_plan p{};
     p.fmt = format;
     p.mode = mode;

@@ -1,6 +1,7 @@
-// qmm_gemm.hip -- prefill kernel (M > 8) for y = x . W^T on GGUF blocks in
-// mode (a), f32 activations; mode (b) runs on the int8 matrix cores
-// (qmm_gemm_q.hip).
+// qmm_gemm.hip -- prefill kernel (M > 8) for y = x . W^T on GGUF blocks on
+// the f16 matrix cores: Q8_0 and Q4_K in mode (a), f32 activations (their
+// mode (b) runs on the int8 matrix cores, qmm_gemm_q.hip), and Q6_K in both
+// modes.
 //
 // The activation row, scaled by the power of two s that puts its largest
 // value in [2^14, 2^15), enters as an exact f16 pair hi + lo of x*s (page
@@ -15,6 +16,21 @@
 //         whose 32-deep operands hold the eight sub-block sums' hi parts and
 //         lo parts against m_j twice.
 // y = acc / s.
+//
+// Q6_K (210 bytes per 256 values: w = d * sc * (q - 32), sc an int8 per 16
+// values).  sc * (q - 32) reaches 4096 and is not exact in f16, so each
+// 16-value scale is split as sc = 16 * sc_hi + sc_lo (sc_hi = sc >> 4, sc_lo =
+// sc & 15) and the weights enter as two exact f16 operands, 16 * sc_hi *
+// (q - 32) (multiples of 16, at most 4096) and sc_lo * (q - 32) (at most 480
+// in magnitude): their products with x sum to x * sc * (q - 32) exactly.  Both
+// go into the same accumulator over a super-block; then acc += d * C.
+// Mode (b) (page "同一个 GGUF，CPU 和 Metal 生成的文字不一样", section 出处:
+// the activations quantized to Q8K, integer dots, then the scales): the
+// activation operand is the int8 values themselves (exact in f16), one pass;
+// the two weight operands keep separate accumulators, each an exact integer in
+// f32 over a whole super-block (the first a multiple of 16 below 2^27, the
+// second below 2^24), so their sum is sumi = sum_j sc_j * S_j of the page's
+// integer form; then acc += (d_x * d) * sumi.
 //
 // A 256-thread workgroup owns a (32*TM) x (32*TN) output tile, four waves in
 // 2 x 2, each (16*TM) x (16*TN) as TM x TN MFMA tiles.  K advances 64 values
@@ -38,11 +54,13 @@ struct GemmArgs {
     int N, K, M;
     int nm;              // row blocks of the output (tiles along M)
     int remap;           // 1: give each XCD a contiguous run of tiles
-    const _Float16* hi;
-    const _Float16* lo;
-    const float* rs;     // 1/s per row
+    const _Float16* hi;  // mode (a): hi part of x*s [M][K]; mode (b): the quantized values as f16 [M][K]
+    const _Float16* lo;  // mode (a): lo part
+    const float* rs;     // mode (a): 1/s per row
     const _Float16* xs;  // Q4_K: [M][K/256][16] sub-block sums * s / 32, hi then lo
-    float* y;
+    const float* dx;     // mode (b): activation block scales, block-major [K/256][M]
+    float* y;            // EMIT instances: may be null
+    int32_t* sums;       // EMIT (Q6_K mode (b)): per super-block 17 values, sumi last (the per-16 sums not formed)
 };
 
 // LDS rows hold 64 values (128 bytes) as 8 chunks of 16 bytes; chunk c of row
@@ -52,34 +70,43 @@ constexpr int G_ROW = 128;
 QMM_DEV uint32_t swz(int row, int chunk) { return (uint32_t)(row * G_ROW + ((chunk ^ (row & 7)) << 4)); }
 
 // WM x WN waves, each owning TM x TN tiles of 16 x 16 outputs.
-template <int FMT, int WM, int WN, int TM, int TN>
+template <int FMT, int MODE, int WM, int WN, int TM, int TN>
 struct GemmCfg {
     static constexpr int NT = 64 * WM * WN;
     static constexpr int BM = 16 * TM * WM, BN = 16 * TN * WN;
-    static constexpr int A_HALF = BM * G_ROW;  // hi (or lo) of one stage, bytes
-    static constexpr int A_BYTES = 2 * A_HALF;
-    static constexpr int B_BYTES = BN * G_ROW;
+    static constexpr int NA = MODE == MODE_A ? 2 : 1;          // activation operands: hi, lo / the values
+    static constexpr int NB = FMT == FMT_Q6_K ? 2 : 1;         // weight operands (Q6_K: the split scale)
+    static constexpr int A_HALF = BM * G_ROW;  // one activation operand of one stage, bytes
+    static constexpr int A_BYTES = NA * A_HALF;
+    static constexpr int B_PART = BN * G_ROW;  // one weight operand of one stage
+    static constexpr int B_BYTES = NB * B_PART;
     static constexpr int OFF_B = 2 * A_BYTES;
     static constexpr int OFF_S = OFF_B + 2 * B_BYTES;
     // Q8_0: block scales [2 stages][2 blocks][BN] f32.
     // Q4_K, by super-block parity: {d, dmin, -, -} [2][BN] (16 B each), 32*m_j
     // [2][BN][8] f16, activation sub-block sums [2][BM][16] f16.
+    // Q6_K, by super-block parity: {d, -, -, -} [2][BN]; mode (b) also d_x [2][BM] f32.
     static constexpr int OFF_DD = OFF_S;
     static constexpr int OFF_MJ = OFF_DD + 2 * BN * 16;
     static constexpr int OFF_X = OFF_MJ + 2 * BN * 16;
-    static constexpr int BYTES = FMT == FMT_Q8_0 ? OFF_S + 2 * 2 * BN * 4 : OFF_X + 2 * BM * 32;
-    static constexpr int AU = 16 * BM / NT;            // 16-byte activation chunks per thread per stage
+    static constexpr int OFF_DXB = OFF_DD + 2 * BN * 16;  // Q6_K
+    static constexpr int BYTES = FMT == FMT_Q8_0 ? OFF_S + 2 * 2 * BN * 4
+                               : FMT == FMT_Q4_K ? OFF_X + 2 * BM * 32
+                                                 : OFF_DXB + (MODE == MODE_B ? 2 * BM * 4 : 0);
+    static constexpr int AU = 8 * NA * BM / NT;        // 16-byte activation chunks per thread per stage
     static constexpr int BU = (2 * BN + NT - 1) / NT;  // weight units (row, half) per thread per stage
     static constexpr int XU = (2 * BM + NT - 1) / NT;  // Q4_K sub-block-sum chunks per thread
-    static_assert((8 * BM) % NT == 0, "activation chunks must split evenly between hi and lo");
+    static_assert((8 * BM) % NT == 0, "activation chunks must split evenly between the operands");
+    static_assert(MODE == MODE_A || FMT == FMT_Q6_K, "mode (b) of Q8_0 and Q4_K runs on the int8 kernel");
 };
 
-template <int FMT, int WM, int WN, int TM, int TN>
+template <int FMT, int MODE, int WM, int WN, int TM, int TN, bool EMIT>
 __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_kernel(GemmArgs a)
 {
-    using C = GemmCfg<FMT, WM, WN, TM, TN>;
+    using C = GemmCfg<FMT, MODE, WM, WN, TM, TN>;
     constexpr int NT = C::NT, BM = C::BM, BN = C::BN, AU = C::AU, BU = C::BU, XU = C::XU;
-    constexpr bool Q8 = FMT == FMT_Q8_0;
+    constexpr bool Q8 = FMT == FMT_Q8_0, Q6 = FMT == FMT_Q6_K, MB = MODE == MODE_B;
+    static_assert(!EMIT || (Q6 && MB), "the traced f16 prefill is Q6_K mode (b)");
     extern __shared__ __align__(16) uint8_t lds[];
 
     const int M = a.M, N = a.N, K = a.K;
@@ -97,19 +124,29 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_kernel(GemmArg
     // Resources over this workgroup's rows: loads past the last row return zeros.
     const int64_t rb = a.row_bytes;
     const rsrc_t rhi = make_rsrc(a.hi + (int64_t)m0 * K, clamp_u32((int64_t)(M - m0) * K * 2));
-    const rsrc_t rlo = make_rsrc(a.lo + (int64_t)m0 * K, clamp_u32((int64_t)(M - m0) * K * 2));
-    const rsrc_t rw = make_rsrc(a.w + (int64_t)n0 * rb, clamp_u32((int64_t)(N - n0) * rb));
-    const rsrc_t rx = make_rsrc(Q8 ? a.hi : a.xs + (int64_t)m0 * (K / 256) * 16,
+    // (mode (b) has one activation operand: no lo part, an empty resource)
+    const rsrc_t rlo = make_rsrc(MB ? a.hi : a.lo + (int64_t)m0 * K, MB ? 0u : clamp_u32((int64_t)(M - m0) * K * 2));
+    // Q6_K rows (210 bytes per super-block) may start 2 bytes into a dword: the
+    // resource starts at the dword at or below the tile's first row (w0 bytes
+    // before it) and ends at the dword holding its last byte (a dword holding a
+    // byte of the buffer lies in the buffer's pages)
+    const uint32_t w0 = Q6 ? (uint32_t)(((uintptr_t)a.w + (uint64_t)n0 * rb) & 3u) : 0u;
+    const rsrc_t rw = make_rsrc(a.w + (int64_t)n0 * rb - w0,
+                                clamp_u32(Q6 ? ((int64_t)(N - n0) * rb + w0 + 3) & ~3ll : (int64_t)(N - n0) * rb));
+    const rsrc_t rx = make_rsrc(FMT != FMT_Q4_K ? a.hi : a.xs + (int64_t)m0 * (K / 256) * 16,
                                 clamp_u32((int64_t)(M - m0) * (K / 256) * 32));
+    // mode (b): the rows' activation scale of a super-block (block-major, this tile's rows)
+    const int drow = tid & (BM - 1);
+    auto rdx_of = [&](int sb) { return make_rsrc(a.dx + (int64_t)sb * M + m0, clamp_u32((int64_t)(M - m0) * 4)); };
 
     // ---- per-thread staging roles, fixed for the whole K loop ----
-    // activation chunk idx over [hi, lo][BM rows][8 chunks]
+    // activation chunk idx over [hi, lo][BM rows][8 chunks] (mode b: the values only)
     uint32_t ag[AU], as_[AU];
 #pragma unroll
     for (int i = 0; i < AU; ++i) {
         const int idx = (tid + NT * i) % (8 * BM), row = idx >> 3, ch = idx & 7;
         ag[i] = (uint32_t)(row * K * 2 + ch * 16);
-        as_[i] = (uint32_t)((i < AU / 2 ? 0 : C::A_HALF) + swz(row, ch));
+        as_[i] = (uint32_t)((i < AU / C::NA ? 0 : C::A_HALF) + swz(row, ch));
     }
     // weight unit (row, half): Q8_0 half = block of the stage, Q4_K half = low
     // or high nibbles (values 0-31 or 32-63 of the stage).  Each unit writes
@@ -119,7 +156,7 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_kernel(GemmArg
 #pragma unroll
     for (int i = 0; i < BU; ++i) {
         const int u = (tid + NT * i) % (2 * BN), row = u >> 1, sub = u & 1;
-        bg[i] = (uint32_t)(Q8 ? row * rb + 32 * sub : row * rb);
+        bg[i] = (uint32_t)(Q8 ? row * rb + 32 * sub : w0 + row * rb);
         bsel[i] = sub ? 0x07060504u : 0x05040302u;  // Q8_0: byte selector of the block's values
         bsh[i] = (uint32_t)sub;
         brow[i] = (uint32_t)row;
@@ -142,17 +179,25 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_kernel(GemmArg
     }
 
     // ---- staging registers, two sets (stage parity) ----
+    constexpr bool Q4 = FMT == FMT_Q4_K;
     uint4 ra[2][AU];
     uint32_t rq8[2][Q8 ? BU : 1][9];
-    uint4 rhd[2][Q8 ? 1 : BU], rqa[2][Q8 ? 1 : BU], rqb[2][Q8 ? 1 : BU];
+    uint4 rhd[2][Q4 ? BU : 1], rqa[2][Q4 ? BU : 1], rqb[2][Q4 ? BU : 1];
     uint4 rxv[XU];
+    // Q6_K: per unit the 32 bytes of low bits and of high bits and the stage's
+    // four scales, each read as whole dwords from the 4-byte-aligned address at
+    // or below the field (super-blocks are only 2-byte aligned), and the dword
+    // holding d; rsh: the unit's byte offset within those dwords (0 or 2)
+    uint32_t rql[2][Q6 ? BU : 1][9], rqh[2][Q6 ? BU : 1][9], rsc[2][Q6 ? BU : 1][2], rdd[2][Q6 ? BU : 1],
+        rsh[2][Q6 ? BU : 1];
+    float rdxv[2];
 
     auto load = [&](int st, auto setc, auto csc) {
         constexpr int SET = decltype(setc)::value;
         constexpr int CS = decltype(csc)::value;  // stage within the super-block (Q4_K)
 #pragma unroll
         for (int i = 0; i < AU; ++i)
-            ra[SET][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(i < AU / 2 ? rhi : rlo, ag[i], 128 * st, 0));
+            ra[SET][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(i < AU / C::NA ? rhi : rlo, ag[i], 128 * st, 0));
         if constexpr (Q8) {
 #pragma unroll
             for (int i = 0; i < BU; ++i) {
@@ -162,6 +207,30 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_kernel(GemmArg
 #pragma unroll
                 for (int k = 0; k < 4; ++k) { rq8[SET][i][k] = v0[k]; rq8[SET][i][4 + k] = v1[k]; }
                 rq8[SET][i][8] = v2;
+            }
+        } else if constexpr (Q6) {
+            const int sb = st >> 2;
+            auto ld9 = [&](uint32_t off, uint32_t (&r)[9]) {
+                const u32x4_t v0 = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0);
+                const u32x4_t v1 = __builtin_amdgcn_raw_buffer_load_b128(rw, off + 16, 0, 0);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) { r[k] = v0[k]; r[4 + k] = v1[k]; }
+                r[8] = __builtin_amdgcn_raw_buffer_load_b32(rw, off + 32, 0, 0);
+            };
+#pragma unroll
+            for (int i = 0; i < BU; ++i) {
+                const uint32_t base = bg[i] + 210u * (uint32_t)sb;  // this row's super-block
+                const uint32_t sh = base & 3u, al = base - sh;
+                rsh[SET][i] = sh;
+                ld9(al + 64 * (CS >> 1) + 32 * bsh[i], rql[SET][i]);  // low bits of values 64*CS + 32*half ..
+                ld9(al + 128 + 32 * (CS >> 1), rqh[SET][i]);          // their high bits
+                rsc[SET][i][0] = __builtin_amdgcn_raw_buffer_load_b32(rw, al + 192 + 4 * CS, 0, 0);
+                rsc[SET][i][1] = __builtin_amdgcn_raw_buffer_load_b32(rw, al + 196 + 4 * CS, 0, 0);
+                rdd[SET][i] = __builtin_amdgcn_raw_buffer_load_b32(rw, al + 208, 0, 0);
+            }
+            if constexpr (MB) {
+                if (CS == 0 && tid < BM)
+                    rdxv[SET] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdx_of(sb), (uint32_t)(4 * drow), 0, 0));
             }
         } else {
             const int sb = st >> 2;
@@ -183,7 +252,7 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_kernel(GemmArg
     // Items: activation chunks, then per weight unit four 8-value chunks and
     // its scales.  `item` runs one of them; the compute loop spreads them over
     // its MFMA groups.
-    constexpr int NI = AU + BU * 5 + (Q8 ? 0 : XU);
+    constexpr int NI = AU + BU * 5 + (Q4 ? XU : 0) + (Q6 && MB ? 1 : 0);
     half2_t qs_s[BU], qs_b[BU];  // Q4_K: sc and -1024*sc of the unit's sub-block
     auto item = [&](int w, int st, auto setc, auto pc, auto csc) {
         constexpr int SET = decltype(setc)::value;
@@ -206,6 +275,47 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_kernel(GemmArg
                 } else {
                     const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)(rq8[SET][i][0] >> (16 * bsh[i])));
                     reinterpret_cast<float*>(lds + C::OFF_S)[(P * 2 + bsh[i]) * BN + brow[i]] = d;
+                }
+            } else if constexpr (Q6) {
+                const uint32_t sh = rsh[SET][i];
+                if (e < 4) {
+                    // values 8e .. 8e+7 of the unit's 32: their low bits are nibble CS & 1 of
+                    // bytes 8e .. 8e+7 of the low-bit run, their high bits bit pair
+                    // 2 (CS & 1) + half of the same bytes of the high-bit run
+                    const uint32_t* ql = rql[SET][i];
+                    const uint32_t* qh = rqh[SET][i];
+                    const uint32_t l0 = __builtin_amdgcn_alignbyte(ql[2 * e + 1], ql[2 * e], sh);
+                    const uint32_t l1 = __builtin_amdgcn_alignbyte(ql[2 * e + 2], ql[2 * e + 1], sh);
+                    const uint32_t h0 = __builtin_amdgcn_alignbyte(qh[2 * e + 1], qh[2 * e], sh);
+                    const uint32_t h1 = __builtin_amdgcn_alignbyte(qh[2 * e + 2], qh[2 * e + 1], sh);
+                    constexpr int LSH = 4 * (CS & 1);
+                    const uint32_t hsh = 2 * (2 * (CS & 1) + bsh[i]);
+                    const uint32_t c0 = ((l0 >> LSH) & 0x0f0f0f0fu) | (((h0 >> hsh) & 0x03030303u) << 4);
+                    const uint32_t c1 = ((l1 >> LSH) & 0x0f0f0f0fu) | (((h1 >> hsh) & 0x03030303u) << 4);
+                    // the codes as exact f16 q - 32 (bit pattern 0x64XX is 1024 + XX)
+                    const half2_t bias = {(_Float16)-1056.0f, (_Float16)-1056.0f};
+                    half2_t v[4];
+                    v[0] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, c0, 0x05010400u)) + bias;
+                    v[1] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, c0, 0x07030602u)) + bias;
+                    v[2] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, c1, 0x05010400u)) + bias;
+                    v[3] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, c1, 0x07030602u)) + bias;
+                    // their scale, byte 2 half + e/2 of the stage's four, split as 16 sc_hi + sc_lo
+                    const uint32_t scw = __builtin_amdgcn_alignbyte(rsc[SET][i][1], rsc[SET][i][0], sh);
+                    const int sc = (int)(int8_t)(scw >> (8 * (2 * bsh[i] + (e >> 1))));
+                    const _Float16 fh = (_Float16)(float)(16 * (sc >> 4)), fl = (_Float16)(float)(sc & 15);
+                    const half2_t sh2 = {fh, fh}, sl2 = {fl, fl};
+                    uint32_t p0[4], p1[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        p0[k] = __builtin_bit_cast(uint32_t, v[k] * sh2);
+                        p1[k] = __builtin_bit_cast(uint32_t, v[k] * sl2);
+                    }
+                    *reinterpret_cast<uint4*>(bbase + bst[i][e]) = make_uint4(p0[0], p0[1], p0[2], p0[3]);
+                    *reinterpret_cast<uint4*>(bbase + C::B_PART + bst[i][e]) = make_uint4(p1[0], p1[1], p1[2], p1[3]);
+                } else if (CS == 0 && bsh[i] == 0) {  // d of the row's super-block (bytes 208, 209)
+                    const int sp = (st >> 2) & 1;
+                    const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)(rdd[SET][i] >> (8 * sh)));
+                    reinterpret_cast<float*>(lds + C::OFF_DD)[(sp * BN + brow[i]) * 4] = d;
                 }
             } else {
                 const uint4 hd = rhd[SET][i];
@@ -248,15 +358,20 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_kernel(GemmArg
             return;
         }
         w -= 5 * BU;
-        if constexpr (!Q8) {
+        if constexpr (Q4) {
             if (CS == 0 && w < XU) {
                 const int sp = (st >> 2) & 1;
                 *reinterpret_cast<uint4*>(lds + C::OFF_X + sp * BM * 32 + xs_[w]) = rxv[w];
             }
         }
+        if constexpr (Q6 && MB) {  // the rows' activation scale of the super-block
+            if (CS == 0 && tid < BM) reinterpret_cast<float*>(lds + C::OFF_DXB)[((st >> 2) & 1) * BM + drow] = rdxv[SET];
+        }
     };
 
-    f32x4_t acc[TM][TN], csb[Q8 ? 1 : TM][Q8 ? 1 : TN];
+    // csb: the super-block's sums before its scales (Q4_K, Q6_K); Q6_K mode
+    // (b) keeps the second weight operand's sums apart in csb2 (both exact)
+    f32x4_t acc[TM][TN], csb[Q8 ? 1 : TM][Q8 ? 1 : TN], csb2[Q6 && MB ? TM : 1][Q6 && MB ? TN : 1];
     const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -284,12 +399,32 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_kernel(GemmArg
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
                 ah[i] = *reinterpret_cast<const half8_t*>(sa + afr[s] + 16 * G_ROW * i);
-                al[i] = *reinterpret_cast<const half8_t*>(sa + C::A_HALF + afr[s] + 16 * G_ROW * i);
+                if constexpr (!MB) al[i] = *reinterpret_cast<const half8_t*>(sa + C::A_HALF + afr[s] + 16 * G_ROW * i);
             }
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 const half8_t bw = *reinterpret_cast<const half8_t*>(sbb + bfr[s] + 16 * G_ROW * j);
-                if constexpr (Q8) {
+                if constexpr (Q6) {
+                    const half8_t bw1 = *reinterpret_cast<const half8_t*>(sbb + C::B_PART + bfr[s] + 16 * G_ROW * j);
+                    const bool first = CS == 0 && s == 0;
+                    if constexpr (MB) {
+#pragma unroll
+                        for (int i = 0; i < TM; ++i) {
+                            csb[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[i], bw, first ? zero : csb[i][j], 0, 0, 0);
+                            csb2[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[i], bw1, first ? zero : csb2[i][j], 0, 0, 0);
+                        }
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < TM; ++i)
+                            csb[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[i], bw, first ? zero : csb[i][j], 0, 0, 0);
+#pragma unroll
+                        for (int i = 0; i < TM; ++i) csb[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[i], bw1, csb[i][j], 0, 0, 0);
+#pragma unroll
+                        for (int i = 0; i < TM; ++i) csb[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[i], bw, csb[i][j], 0, 0, 0);
+#pragma unroll
+                        for (int i = 0; i < TM; ++i) csb[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[i], bw1, csb[i][j], 0, 0, 0);
+                    }
+                } else if constexpr (Q8) {
                     const float dw = reinterpret_cast<const float*>(lds + C::OFF_S)[(P * 2 + s) * BN + wn + 16 * j + li];
                     f32x4_t cv[TM];
 #pragma unroll
@@ -331,6 +466,43 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_kernel(GemmArg
             for (int i = 0; i < TM; ++i)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[i][TN - 1][r] = __builtin_fmaf(dwp, cvp[i][r], acc[i][TN - 1][r]);
+        } else if constexpr (Q6) {
+            if (CS == 3) {  // the super-block's scales: d (and d_x) times its sums
+                const int sp = (st >> 2) & 1;
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int nl = wn + 16 * j + li;
+                    const float d = reinterpret_cast<const float*>(lds + C::OFF_DD)[(sp * BN + nl) * 4];
+#pragma unroll
+                    for (int i = 0; i < TM; ++i) {
+                        if constexpr (MB) {
+                            const f32x4_t dxv = *reinterpret_cast<const f32x4_t*>(
+                                reinterpret_cast<const float*>(lds + C::OFF_DXB) + sp * BM + wm + 16 * i + 4 * kg);
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                acc[i][j][r] = __builtin_fmaf(dxv[r] * d, csb[i][j][r] + csb2[i][j][r], acc[i][j][r]);
+                            if constexpr (EMIT) {
+                                // sumi of the super-block: both parts are exact integers; the
+                                // per-16 sums are not formed here (the scales are in the operand)
+                                const int n = n0 + nl, spr = (K / 256) * 17;
+#pragma unroll
+                                for (int r = 0; r < 4; ++r) {
+                                    const int m = m0 + wm + 16 * i + 4 * kg + r;
+                                    if (m < M && n < N) {
+                                        int32_t* o = a.sums + ((int64_t)m * N + n) * spr + 17 * (st >> 2);
+#pragma unroll
+                                        for (int q = 0; q < 16; ++q) o[q] = INT32_MIN;
+                                        o[16] = (int32_t)csb[i][j][r] + (int32_t)csb2[i][j][r];
+                                    }
+                                }
+                            }
+                        } else {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(d, csb[i][j][r], acc[i][j][r]);
+                        }
+                    }
+                }
+            }
         } else if (CS == 3) {
             const int sp = (st >> 2) & 1;
             const half8_t hz = {};
@@ -410,8 +582,9 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_kernel(GemmArg
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             mrow[r] = m0 + wm + 16 * i + 4 * kg + r;
-            rsv[r] = mrow[r] < M ? a.rs[mrow[r]] : 0.0f;
+            rsv[r] = MB ? 1.0f : mrow[r] < M ? a.rs[mrow[r]] : 0.0f;
         }
+        if (EMIT && !a.y) continue;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const int n = n0 + wn + 16 * j + li;
@@ -466,13 +639,16 @@ static const GemmTile kTiles[] = {{4, 2, 2, 7}, {4, 2, 2, 4}, {2, 2, 2, 4}, {2, 
 
 // The tile whose busiest compute unit does the least work: rounds of tiles
 // over the compute units times the tile's area, weighted by its operand
-// traffic per output (activation pairs over BN, weight bytes over BM).
-static GemmTile pick_tile(int64_t M, int64_t N)
+// traffic per output (activation pairs over BN, weight bytes over BM).  Q6_K
+// leaves out the widest tile (its three accumulators per output would not fit
+// the registers).
+static GemmTile pick_tile(int64_t M, int64_t N, int fmt)
 {
     const int64_t cus = cu_count();
-    GemmTile best = kTiles[0];
+    GemmTile best = kTiles[fmt == FMT_Q6_K ? 1 : 0];
     double bc = -1.0;
     for (const GemmTile& t : kTiles) {
+        if (fmt == FMT_Q6_K && t.tn == 7) continue;
         const int64_t bm = 16 * t.tm * t.wm, bn = 16 * t.tn * t.wn;
         const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
         const double cost = (double)((tiles + cus - 1) / cus) * (double)(bm * bn) * (1.0 + 16.0 / bm + 64.0 / bn);
@@ -484,37 +660,39 @@ static GemmTile pick_tile(int64_t M, int64_t N)
     return best;
 }
 
-template <int FMT, int WM, int WN, int TM, int TN>
+template <int FMT, int MODE, bool EMIT, int WM, int WN, int TM, int TN>
 static hipError_t launch_tile(GemmArgs a, hipStream_t s)
 {
-    using C = GemmCfg<FMT, WM, WN, TM, TN>;
+    using C = GemmCfg<FMT, MODE, WM, WN, TM, TN>;
+    static_assert(C::BYTES <= 160 * 1024, "LDS of a compute unit");
     const int nm = (a.M + C::BM - 1) / C::BM, nn = (a.N + C::BN - 1) / C::BN;
     const int64_t grid = (int64_t)nm * nn;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     a.nm = nm;
     a.remap = grid % 8 == 0 ? 1 : 0;
-    GemmKernel k = gemm_kernel<FMT, WM, WN, TM, TN>;
+    GemmKernel k = gemm_kernel<FMT, MODE, WM, WN, TM, TN, EMIT>;
     allow_lds((const void*)k, C::BYTES);
     void* args[] = {&a};
     return hipLaunchKernel((const void*)k, dim3((unsigned)grid), dim3(C::NT), args, C::BYTES, s);
 }
 
-template <int FMT>
+template <int FMT, int MODE, bool EMIT>
 static hipError_t launch_fmt(const GemmArgs& a, GemmTile t, hipStream_t s)
 {
-    if (t.wm == 4 && t.tn == 7) return launch_tile<FMT, 4, 2, 2, 7>(a, s);
-    if (t.wm == 4 && t.tn == 4) return launch_tile<FMT, 4, 2, 2, 4>(a, s);
-    if (t.tm == 2 && t.tn == 4) return launch_tile<FMT, 2, 2, 2, 4>(a, s);
-    if (t.tm == 2) return launch_tile<FMT, 2, 2, 2, 2>(a, s);
-    return launch_tile<FMT, 2, 2, 1, 2>(a, s);
+    if constexpr (FMT != FMT_Q6_K)
+        if (t.wm == 4 && t.tn == 7) return launch_tile<FMT, MODE, EMIT, 4, 2, 2, 7>(a, s);
+    if (t.wm == 4 && t.tn == 4) return launch_tile<FMT, MODE, EMIT, 4, 2, 2, 4>(a, s);
+    if (t.tm == 2 && t.tn == 4) return launch_tile<FMT, MODE, EMIT, 2, 2, 2, 4>(a, s);
+    if (t.tm == 2) return launch_tile<FMT, MODE, EMIT, 2, 2, 2, 2>(a, s);
+    return launch_tile<FMT, MODE, EMIT, 2, 2, 1, 2>(a, s);
 }
 
 hipError_t launch_gemm(int fmt, int mode, const void* w, int64_t N, int64_t K, int64_t M, const GemmBufs& b,
                        float* y, hipStream_t s, int32_t* sums)
 {
-    const int64_t row_bytes = fmt == FMT_Q8_0 ? (K / 32) * 34 : (K / 256) * 144;
-    if (mode == MODE_B) return launch_gemm_q(fmt, w, N, K, M, b, y, s, sums);
-    if (sums) return hipErrorInvalidValue;
+    const int64_t row_bytes = fmt == FMT_Q8_0 ? (K / 32) * 34 : fmt == FMT_Q4_K ? (K / 256) * 144 : (K / 256) * 210;
+    if (mode == MODE_B && fmt != FMT_Q6_K) return launch_gemm_q(fmt, w, N, K, M, b, y, s, sums);
+    if (sums && !(fmt == FMT_Q6_K && mode == MODE_B)) return hipErrorInvalidValue;
     GemmArgs a{};
     a.w = (const uint8_t*)w;
     a.row_bytes = row_bytes;
@@ -525,9 +703,15 @@ hipError_t launch_gemm(int fmt, int mode, const void* w, int64_t N, int64_t K, i
     a.lo = b.a1;
     a.rs = b.rs;
     a.xs = b.xs;
+    a.dx = b.sd;
     a.y = y;
-    const GemmTile t = pick_tile(M, N);
-    hipError_t e = fmt == FMT_Q8_0 ? launch_fmt<FMT_Q8_0>(a, t, s) : launch_fmt<FMT_Q4_K>(a, t, s);
+    a.sums = sums;
+    const GemmTile t = pick_tile(M, N, fmt);
+    hipError_t e;
+    if (fmt == FMT_Q8_0) e = launch_fmt<FMT_Q8_0, MODE_A, false>(a, t, s);
+    else if (fmt == FMT_Q4_K) e = launch_fmt<FMT_Q4_K, MODE_A, false>(a, t, s);
+    else if (mode == MODE_A) e = launch_fmt<FMT_Q6_K, MODE_A, false>(a, t, s);
+    else e = sums ? launch_fmt<FMT_Q6_K, MODE_B, true>(a, t, s) : launch_fmt<FMT_Q6_K, MODE_B, false>(a, t, s);
     if (e != hipSuccess) return e;
     return hipGetLastError();
 }

@@ -7,7 +7,7 @@
 
 namespace qmm {
 
-enum { LAY_AOS = 0, LAY_I8 = 3 };
+enum { LAY_AOS = 0, LAY_I8 = 3, LAY_F16 = 4 };
 
 // One thread per 32-value block.  LAY_AOS: canonical 34-byte blocks.
 // LAY_I8: the values as int8 [M][K] plus f32 scales block-major [K/32][M]
@@ -43,7 +43,8 @@ __global__ __launch_bounds__(256) void quantize_q8_0_kernel(const float* __restr
 }
 
 // One wave per 256-value block, four blocks per workgroup.  LAY_AOS: canonical
-// 292-byte blocks.  LAY_I8: values as int8
+// 292-byte blocks.  LAY_F16 (the f16 prefill kernel's operand): values as
+// exact f16 [M][K], f32 scales block-major [K/256][M].  LAY_I8: values as int8
 // [M][K], f32 scales block-major [K/256][M], and per block the eight sums of
 // 32 consecutive values as f16 [K/256][M][16]: first each sum rounded down to
 // a multiple of 64, then the remainders (0..63), all exact.
@@ -64,6 +65,12 @@ __global__ __launch_bounds__(256) void quantize_q8k_kernel(const float* __restri
     q8k_wave(xs, lane, d, q, s16);
     if (LAY == LAY_AOS) {
         store_q8k_lane(out + blk * 292, lane, d, q, s16);
+    } else if (LAY == LAY_F16) {
+        if (act) store_q8k_lane(act + blk * 292, lane, d, q, s16);
+        _Float16* o = reinterpret_cast<_Float16*>(out) + (int64_t)m * K + 256 * sb + 4 * lane;
+        half2_t h0 = {(_Float16)(float)q[0], (_Float16)(float)q[1]}, h1 = {(_Float16)(float)q[2], (_Float16)(float)q[3]};
+        *reinterpret_cast<u32x2_t*>(o) = u32x2_t{__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1)};
+        if (lane == 0) sc[(int64_t)sb * M + m] = d;
     } else if (LAY == LAY_I8) {
         if (act) store_q8k_lane(act + blk * 292, lane, d, q, s16);
         const int pair = s16 + __shfl_down(s16, 4);  // lane 8j: bsums[2j] + bsums[2j+1]
@@ -227,6 +234,11 @@ hipError_t launch_quantize_weights(int fmt, const float* w, int64_t N, int64_t K
 hipError_t launch_gemm_prep(int fmt, int mode, const float* x, int64_t M, int64_t K, const GemmBufs& b, hipStream_t s,
                             uint8_t* act)
 {
+    if (mode == MODE_B && fmt == FMT_Q6_K) {  // exact f16 values and block-major scales for the f16 kernel
+        hipLaunchKernelGGL(quantize_q8k_kernel<LAY_F16>, dim3(nblocks(M * (K / 256), 4)), dim3(256), 0, s,
+                           x, (int)M, (int)K, (uint8_t*)b.a0, b.sd, (void*)nullptr, act);
+        return hipGetLastError();
+    }
     if (mode == MODE_B) {  // int8 values, block scales (and Q8K sub-block sums) for the int8 kernel
         if (fmt == FMT_Q8_0)
             hipLaunchKernelGGL(quantize_q8_0_kernel<LAY_I8>, dim3(nblocks(M * (K / 32), 256)), dim3(256), 0, s,
@@ -237,7 +249,7 @@ hipError_t launch_gemm_prep(int fmt, int mode, const float* x, int64_t M, int64_
         return hipGetLastError();
     }
     const dim3 grid((unsigned)M), block(256);
-    if (fmt == FMT_Q8_0)
+    if (fmt != FMT_Q4_K)  // Q8_0, Q6_K: the hi/lo split only
         hipLaunchKernelGGL(gemm_prep_kernel<FMT_Q8_0>, grid, block, 0, s, x, (int)M, (int)K, b.a0, b.a1, b.rs, b.xs);
     else
         hipLaunchKernelGGL(gemm_prep_kernel<FMT_Q4_K>, grid, block, 0, s, x, (int)M, (int)K, b.a0, b.a1, b.rs, b.xs);

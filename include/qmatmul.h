@@ -106,15 +106,12 @@ int qmatmul_create(qmm_plan** out, int format, int64_t N, int64_t K, int64_t M_m
  * is shared by its runs: do not run one plan concurrently on two streams.
  * Q4_0 and Q5_0 runs with M > 8 first rewrite the weights as Q8_0 blocks
  * (the same dequantized values) in the plan's workspace and take the Q8_0
- * prefill kernels; Q6_K runs with M > 8 decode the weights to f32 in the
- * workspace (N*K*4 bytes) and take the library f32 GEMM in mode (a), and take
- * the decode kernels eight activation rows at a time in mode (b) (correct,
- * not tuned for throughput).
+ * prefill kernels; Q6_K runs with M > 8 take their own prefill kernel (both
+ * modes) on the f16 matrix cores.
  * A run only enqueues kernels (no allocation, memset or synchronization), so
  * runs may be captured in a HIP graph once each kernel has run eagerly (its
- * launch attributes are set on first use); the exceptions are a
- * QMM_MODE_DEQUANT plan and a Q6_K mode (a) plan at M > 8, whose product is a
- * rocBLAS call.
+ * launch attributes are set on first use); the exception is a
+ * QMM_MODE_DEQUANT plan, whose product is a rocBLAS call.
  */
 int qmatmul_run(const qmm_plan* plan, const void* w_blocks, const float* x, float* y,
                 int64_t M, void* stream);
@@ -151,8 +148,7 @@ int qmatmul_run_group(const qmm_plan* const* plans, int count, const void* const
  * mode) says what a shape needs).  w_blocks, x, y: device, as in qmatmul_run.
  * Errors: those of qmatmul_create and qmatmul_run; QMM_EINVAL when the shape
  * needs more scratch than the array holds; QMM_EUNSUPPORTED for
- * QMM_MODE_DEQUANT and for Q6_K mode (a) with M > 8 (their product is a
- * library GEMM that allocates).  Every call on a GPU uses that GPU's one
+ * QMM_MODE_DEQUANT (its product is a library GEMM that allocates).  Every call on a GPU uses that GPU's one
  * array: calls that overlap on one GPU (on two streams, or from two host
  * threads) race and must be serialized by the caller.  The first call on
  * each device looks up the array's address (no allocation); its kernels set
@@ -230,7 +226,9 @@ int qmatmul_quantize_weights(int format, const float* w, int64_t N, int64_t K,
  *     Q6_K: per super-block 17 values S_0..S_15 (per 16, qw = q - 32) and
  *       sumi = sum_j sc_j*S_j.
  *     At M > 8 the Q4_K prefill kernel scales each S_j on its own and never
- *     forms sumi; there sumi is summed from the S_j it wrote.
+ *     forms sumi; there sumi is summed from the S_j it wrote.  The Q6_K
+ *     prefill kernel (M > 8) carries the scales in its weight operand and
+ *     forms sumi exactly but no per-16 sums: there S_0..S_15 read INT32_MIN.
  *   act_blocks: device, M * qmatmul_row_bytes(Q8_0 or Q8_K, K) bytes, 4-byte
  *     aligned, or NULL: the canonical quantized activation blocks, written by
  *     the kernel that quantizes them in this run (a decode kernel's own

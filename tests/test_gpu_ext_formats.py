@@ -169,7 +169,27 @@ def test_traced_run_integer_parts_bit_exact(fmt, n, k, m):
     y, got, act = host(y), host(sums).astype(np.int64), host(act)
     assert np.array_equal(y.view(np.uint32), y_run.view(np.uint32)), (NAME[fmt], m, "traced y")
     assert np.array_equal(act, oracle.quantize(qmm.ACT_FORMAT[fmt], x)), (NAME[fmt], m, "activations")
-    assert np.array_equal(got.reshape(want.shape), want), (NAME[fmt], m)
+    got = got.reshape(want.shape)
+    if fmt == qmm.Q6_K and m > qmm.GEMV_MAX_M:
+        # the prefill kernel carries the scales in its weight operand: it forms
+        # each super-block's sumi exactly, and no per-16 sums
+        got, want = got.reshape(m, n, -1, 17), want.reshape(m, n, -1, 17)
+        assert np.all(got[..., :16] == np.iinfo(np.int32).min)
+        got, want = got[..., 16], want[..., 16]
+    assert np.array_equal(got, want), (NAME[fmt], m)
+
+
+@pytest.mark.parametrize("mode", MODES, ids=["a", "b"])
+@pytest.mark.parametrize("n,k", [(576, 1536), (45, 768), (300, 4352), (1000, 256)])
+@pytest.mark.parametrize("m", [9, 64, 130, 307])
+def test_q6_k_prefill_parity(n, k, mode, m):
+    # the Q6_K prefill kernel: several row and column tiles, ragged edges,
+    # rows that start two bytes into a dword (odd super-block counts)
+    wq = oracle.quantize(qmm.Q6_K, synth.weights_f32(7800 + n + k, n, k))
+    x = synth.acts_f32(7801 + m, m, k)
+    y = run(qmm.Q6_K, mode, wq, n, k, x)
+    yr, a = ref(qmm.Q6_K, mode, wq, n, k, x)
+    assert_within(y, yr, a, f"Q6_K {n}x{k} M={m} mode={mode}")
 
 
 @pytest.mark.parametrize("fmt,n,k", [(qmm.Q4_0, 200, 576), (qmm.Q6_K, 45, 768)])
@@ -201,7 +221,7 @@ def test_runs_are_deterministic_and_m_below_plan_maximum(fmt, mode):
 
 @pytest.mark.parametrize("fmt", [qmm.Q4_0, qmm.Q5_0, qmm.Q6_K], ids=["Q4_0", "Q5_0", "Q6_K"])
 @pytest.mark.parametrize("mode", MODES, ids=["a", "b"])
-@pytest.mark.parametrize("m", [1, 8])
+@pytest.mark.parametrize("m", [1, 8, 512])
 def test_scaleup_shape_sampled_rows(fmt, mode, m):
     # 14336 x 4096 (the scale-up projection), every output computed on the
     # GPU, 64 sampled weight rows checked against the oracle
@@ -210,10 +230,13 @@ def test_scaleup_shape_sampled_rows(fmt, mode, m):
     x = synth.acts_f32(5100, 512, k)[:m]
     wg = qmm.quantize_weights(fmt, dev(w))
     y = run(fmt, mode, host(wg), n, k, x)
-    rows = np.random.default_rng(7950 + m).choice(n, 64, replace=False)
+    g = np.random.default_rng(7950 + m)
+    rows = g.choice(n, 64, replace=False)
+    if m > qmm.GEMV_MAX_M:  # the prefill: a row in every 32 (every output tile)
+        rows = np.unique(np.concatenate([rows, np.arange(0, n, 32) + g.integers(0, 32, n // 32), [n - 1]]))
     wq = oracle.quantize(fmt, w[rows])
     assert np.array_equal(host(wg)[rows], wq)
-    yr, a = ref(fmt, mode, wq, 64, k, x)
+    yr, a = ref(fmt, mode, wq, len(rows), k, x)
     assert_within(y[:, rows], yr, a, f"{NAME[fmt]} 14336x4096 M={m} mode={mode}")
 
 
