@@ -26,6 +26,11 @@ struct qmm_plan {
     ExtBufs ex;    // Q4_0, Q5_0, Q6_K
     float* wdeq;   // dequantize-all plans: the decoded weights [N][K]
     void* dense;   // dequantize-all plans: the f32 GEMM handle
+    // Q8_0, Q4_0, Q5_0 rows with an odd number of blocks run one all-zero
+    // block longer: Kr = K + 32 (else K), the padded weights and activations
+    int64_t Kr;
+    uint8_t* wpad;
+    float* xpad;
 };
 
 static thread_local char g_err[512];
@@ -105,9 +110,6 @@ static int check_shape(int format, int64_t N, int64_t K, int64_t M_max, int mode
     if (N > (1ll << 30) || K > (1ll << 20) || M_max > (1ll << 24) || N * (K / qk) * block_bytes(format) > (1ll << 40))
         return fail(QMM_EINVAL, "shape too large: N=%lld K=%lld M_max=%lld", (long long)N, (long long)K,
                     (long long)M_max);
-    if (!gemv_supported(format, K))
-        return fail(QMM_EUNSUPPORTED, "K=%lld has no kernel for this format (Q8_0, Q4_0 and Q5_0 need K divisible "
-                    "by 64: the kernels read blocks in pairs)", (long long)K);
     return QMM_OK;
 }
 
@@ -119,10 +121,19 @@ extern "C" int qmatmul_check(int format, int64_t N, int64_t K, int64_t M_max, in
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Rows of a 32-value format with an odd number of blocks: the kernels read
+// blocks in pairs, so such rows run on a copy one all-zero block longer.
+static bool odd_blocks(int fmt, int64_t K)
+{
+    return (fmt == QMM_Q8_0 || fmt == QMM_Q4_0 || fmt == QMM_Q5_0) && (K / 32) % 2 == 1;
+}
+
 // Byte layout of the workspace; fills the buffer pointers when base != null.
 static size_t layout(qmm_plan* p, char* base)
 {
-    const int64_t K = p->K, N = p->N;
+    const bool pad = p->mode != QMM_MODE_DEQUANT && odd_blocks(p->fmt, p->K);
+    p->Kr = pad ? p->K + 32 : p->K;
+    const int64_t K = p->Kr, N = p->N;
     const int64_t units = p->fmt == QMM_Q4_K ? K / 256 : K / 32;
     const bool a = p->mode == QMM_MODE_F32ACT, q4 = p->fmt == QMM_Q4_K;
     size_t off = 0;
@@ -132,6 +143,8 @@ static size_t layout(qmm_plan* p, char* base)
         return r;
     };
     p->ex = ExtBufs{};
+    p->wpad = pad ? (uint8_t*)take((size_t)N * (K / 32) * block_bytes(p->fmt)) : nullptr;
+    p->xpad = pad ? (float*)take(4 * (size_t)p->M_max * K) : nullptr;
     if (p->mode == QMM_MODE_DEQUANT) {  // the decoded weights only
         p->wdeq = (float*)take(4 * (size_t)N * K);
         p->gv = GemvBufs{};
@@ -281,24 +294,32 @@ static int run_impl(const qmm_plan* p, const void* w, const float* x, float* y, 
     }
     uint8_t* act = tr ? tr->act : nullptr;
     int32_t* sums = tr ? tr->sums : nullptr;
+    const int64_t K = p->Kr;  // the row length the kernels run on
+    if (K != p->K) {          // an odd block count: the padded copies
+        const int bb = (int)block_bytes(p->fmt);
+        e = launch_pad(w, p->N, (int)(p->K / 32) * bb, (int)(K / 32) * bb, p->wpad, x, M, p->K, K, p->xpad, s);
+        if (e != hipSuccess) return fail(QMM_EHIP, "kernel launch: %s", hipGetErrorString(e));
+        w = p->wpad;
+        x = p->xpad;
+    }
     if (is_ext_format(p->fmt)) {
-        if (M == 1 && gemv_row_supported(p->fmt, p->mode, 1, p->N, p->K, tr != nullptr)) {
-            e = launch_gemv_row(p->fmt, p->mode, w, x, p->N, p->K, y, s, tr);  // Q4_0, Q5_0: the one-row kernel
+        if (M == 1 && gemv_row_supported(p->fmt, p->mode, 1, p->N, K, tr != nullptr)) {
+            e = launch_gemv_row(p->fmt, p->mode, w, x, p->N, K, y, s, tr);  // Q4_0, Q5_0: the one-row kernel
         } else if (M <= GEMV_MAX_M) {
-            e = launch_ext_run(p->fmt, p->mode, w, x, p->N, p->K, M, p->ex, y, s, tr);
+            e = launch_ext_run(p->fmt, p->mode, w, x, p->N, K, M, p->ex, y, s, tr);
         } else if (p->fmt == QMM_Q6_K) {
-            e = launch_gemm_prep(FMT_Q6_K, p->mode, x, M, p->K, p->gm, s, act);
-            if (e == hipSuccess) e = launch_gemm(FMT_Q6_K, p->mode, w, p->N, p->K, M, p->gm, y, s, sums);
+            e = launch_gemm_prep(FMT_Q6_K, p->mode, x, M, K, p->gm, s, act);
+            if (e == hipSuccess) e = launch_gemm(FMT_Q6_K, p->mode, w, p->N, K, M, p->gm, y, s, sums);
         } else {
-            e = launch_ext_to_q8_0(p->fmt, w, p->N, p->K, p->ex.tw, s);
-            if (e == hipSuccess) e = launch_gemm_prep(FMT_Q8_0, p->mode, x, M, p->K, p->gm, s, act);
-            if (e == hipSuccess) e = launch_gemm(FMT_Q8_0, p->mode, p->ex.tw, p->N, p->K, M, p->gm, y, s, sums);
+            e = launch_ext_to_q8_0(p->fmt, w, p->N, K, p->ex.tw, s);
+            if (e == hipSuccess) e = launch_gemm_prep(FMT_Q8_0, p->mode, x, M, K, p->gm, s, act);
+            if (e == hipSuccess) e = launch_gemm(FMT_Q8_0, p->mode, p->ex.tw, p->N, K, M, p->gm, y, s, sums);
         }
     } else if (M <= GEMV_MAX_M) {
-        e = launch_gemv(p->fmt, p->mode, w, x, p->N, p->K, (int)M, p->gv, y, s, tr);
+        e = launch_gemv(p->fmt, p->mode, w, x, p->N, K, (int)M, p->gv, y, s, tr);
     } else {
-        e = launch_gemm_prep(p->fmt, p->mode, x, M, p->K, p->gm, s, act);
-        if (e == hipSuccess) e = launch_gemm(p->fmt, p->mode, w, p->N, p->K, M, p->gm, y, s, sums);
+        e = launch_gemm_prep(p->fmt, p->mode, x, M, K, p->gm, s, act);
+        if (e == hipSuccess) e = launch_gemm(p->fmt, p->mode, w, p->N, K, M, p->gm, y, s, sums);
     }
     if (e != hipSuccess) return fail(QMM_EHIP, "kernel launch: %s", hipGetErrorString(e));
     return QMM_OK;
@@ -370,7 +391,7 @@ extern "C" int qmatmul_run_group(const qmm_plan* const* plans, int count, const 
     if (M == 0) return QMM_OK;
     const qmm_plan* p0 = plans[0];
     const hipStream_t s = (hipStream_t)stream;
-    if (M == 1 && p0->mode != QMM_MODE_DEQUANT) {
+    if (M == 1 && p0->mode != QMM_MODE_DEQUANT && p0->Kr == p0->K) {
         // one launch per gemv_row_group_max() plans, when the one-row kernel takes their rows
         int64_t total = 0;
         for (int i = 0; i < count; ++i) total += plans[i]->N;
@@ -386,7 +407,7 @@ extern "C" int qmatmul_run_group(const qmm_plan* const* plans, int count, const 
             return QMM_OK;
         }
     }
-    if (is_ext_format(p0->fmt) && ext_group_supported(p0->fmt, p0->mode, p0->K, M)) {
+    if (is_ext_format(p0->fmt) && p0->Kr == p0->K && ext_group_supported(p0->fmt, p0->mode, p0->K, M)) {
         // Q4_0, Q5_0, Q6_K decode: one launch per ext_group_max() plans, unless
         // a plan's separate run would take the one-row kernel (the grouped
         // values must be those of the separate runs)
@@ -425,8 +446,32 @@ extern "C" int qmatmul_run_traced(const qmm_plan* p, const void* w, const float*
     if (p->mode != QMM_MODE_QACT) return fail(QMM_EUNSUPPORTED, "block sums exist only for quantized activations (mode 1)");
     if (y && !aligned(y, 4)) return fail(QMM_EINVAL, "y must be 4-byte aligned");
     if (act_blocks && !aligned(act_blocks, 4)) return fail(QMM_EINVAL, "act_blocks must be 4-byte aligned");
-    const Trace tr{sums, (uint8_t*)act_blocks};
-    return run_impl(p, w, x, y, &tr, M, stream);
+    if (p->Kr == p->K) {
+        const Trace tr{sums, (uint8_t*)act_blocks};
+        return run_impl(p, w, x, y, &tr, M, stream);
+    }
+    // padded rows: the kernels' outputs (one block more per row) go to
+    // stream-ordered temporaries, then the real blocks are copied out
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t from = p->Kr / 32, keep = p->K / 32;
+    void* ts = nullptr;
+    void* ta = nullptr;
+    hipError_t e = hipMallocAsync(&ts, (size_t)M * p->N * from * 4, s);
+    if (e == hipSuccess) e = hipMallocAsync(&ta, (size_t)M * from * 34, s);
+    if (e != hipSuccess) {
+        if (ts) (void)hipFreeAsync(ts, s);
+        return fail(e == hipErrorOutOfMemory ? QMM_ENOMEM : QMM_EHIP, "hipMallocAsync: %s", hipGetErrorString(e));
+    }
+    const Trace tr{(int32_t*)ts, (uint8_t*)ta};
+    st = run_impl(p, w, x, y, &tr, M, stream);
+    if (st == QMM_OK) {
+        e = launch_unpad(ts, M * p->N, (int)from, (int)keep, 4, sums, s);
+        if (e == hipSuccess && act_blocks) e = launch_unpad(ta, M, (int)from, (int)keep, 34, act_blocks, s);
+        if (e != hipSuccess) st = fail(QMM_EHIP, "kernel launch: %s", hipGetErrorString(e));
+    }
+    (void)hipFreeAsync(ts, s);
+    (void)hipFreeAsync(ta, s);
+    return st;
 }
 
 extern "C" int qmatmul_run_block_sums(const qmm_plan* p, const void* w, const float* x, int32_t* sums, int64_t M,
@@ -456,9 +501,6 @@ extern "C" int qmatmul_dequantize_weights(int format, const void* w, int64_t N, 
     if (K % block_values(format))
         return fail(QMM_EBLOCK, "quantized tensor must have their last dim divisible by block size [%lld, %lld] %lld",
                     (long long)N, (long long)K, (long long)block_values(format));
-    if ((format == QMM_Q4_0 || format == QMM_Q5_0) && K % 64)
-        return fail(QMM_EUNSUPPORTED, "K=%lld: Q4_0 and Q5_0 rows are decoded in block pairs (K divisible by 64)",
-                    (long long)K);
     if (N == 0) return QMM_OK;
     if (!w || !out) return fail(QMM_EINVAL, "null pointer");
     if (!aligned(w, 16)) return fail(QMM_EINVAL, "w_blocks must be 16-byte aligned");

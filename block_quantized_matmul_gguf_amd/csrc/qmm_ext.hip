@@ -922,10 +922,49 @@ hipError_t launch_ext_to_q8_0(int fmt, const void* w, int64_t N, int64_t K, void
     return hipGetLastError();
 }
 
+// Q4_0 / Q5_0 rows with an odd number of blocks (2-byte aligned blocks): one
+// thread per block, bytes read one at a time; w = d * (q - offset) exactly.
+template <int FMT>
+__global__ __launch_bounds__(256) void ext_dequant_block_kernel(const uint8_t* __restrict__ w, int64_t blocks,
+                                                                float* __restrict__ out)
+{
+    constexpr int BB = FMT == FMT_Q4_0 ? 18 : 22, OFF = FMT == FMT_Q4_0 ? 8 : 16;
+    const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (b >= blocks) return;
+    const uint8_t* p = w + b * BB;
+    const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)(p[0] | (p[1] << 8)));
+    uint32_t qh = 0;
+    if constexpr (FMT == FMT_Q5_0) qh = p[2] | (p[3] << 8) | (p[4] << 16) | ((uint32_t)p[5] << 24);
+    const uint8_t* qs = p + BB - 16;
+    float v[32];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        int lo = qs[j] & 15, hi = qs[j] >> 4;
+        if constexpr (FMT == FMT_Q5_0) {
+            lo |= ((qh >> j) & 1) << 4;
+            hi |= ((qh >> (j + 16)) & 1) << 4;
+        }
+        v[j] = d * (float)(lo - OFF);
+        v[j + 16] = d * (float)(hi - OFF);
+    }
+    float* o = out + 32 * b;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) o[j] = v[j];
+}
+
 hipError_t launch_ext_dequantize(int fmt, const void* w, int64_t N, int64_t K, float* out, hipStream_t s)
 {
     const unsigned grid = ext_blocks(N * (K / 32), 256);
     const int64_t rb = fmt == FMT_Q6_K ? (K / 256) * 210 : (K / 32) * ext_block_bytes(fmt);
+    if (fmt != FMT_Q6_K && K % 64) {  // odd block count: block by block
+        if (fmt == FMT_Q4_0)
+            hipLaunchKernelGGL(ext_dequant_block_kernel<FMT_Q4_0>, dim3(grid), dim3(256), 0, s, (const uint8_t*)w,
+                               N * (K / 32), out);
+        else
+            hipLaunchKernelGGL(ext_dequant_block_kernel<FMT_Q5_0>, dim3(grid), dim3(256), 0, s, (const uint8_t*)w,
+                               N * (K / 32), out);
+        return hipGetLastError();
+    }
     if (fmt == FMT_Q4_0)
         hipLaunchKernelGGL(ext_dequant_kernel<FMT_Q4_0>, dim3(grid), dim3(256), 0, s, (const uint8_t*)w, N, (int)K, rb, out);
     else if (fmt == FMT_Q5_0)

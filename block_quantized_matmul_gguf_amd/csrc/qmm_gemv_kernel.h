@@ -559,7 +559,8 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const int m = 4 * (g & 1) + q;
-                        if (m < M && ng < N) a.sums[((int64_t)m * N + ng) * (2 * a.nlu) + blk] = C[q];
+                        // (a stage may run past the split's last unit: those units are not the row's)
+                        if (m < M && ng < N && lu < lu_cnt) a.sums[((int64_t)m * N + ng) * (2 * a.nlu) + blk] = C[q];
                     }
                 }
             } else if constexpr (FMT == FMT_Q8_0) {
@@ -600,7 +601,7 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
 #pragma unroll
                             for (int q = 0; q < 4; ++q) {
                                 const int m = 4 * (g & 1) + q;
-                                if (m < M && ng < N)
+                                if (m < M && ng < N && lu < lu_cnt)
                                     a.sums[(((int64_t)m * N + ng) * a.nlu + lu_beg + lu) * 10 + jj] = C[q];
                             }
                         }
@@ -633,7 +634,7 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
                         const int ti = sumi[q] + __shfl_xor(sumi[q], 32);
                         const int tm = summ[q] + __shfl_xor(summ[q], 32);
                         const int m = 4 * (g & 1) + q;
-                        if (g < 2 && m < M && ng < N) {
+                        if (g < 2 && m < M && ng < N && lu < lu_cnt) {
                             int32_t* o = a.sums + (((int64_t)m * N + ng) * a.nlu + lu_beg + lu) * 10;
                             o[8] = ti;
                             o[9] = tm;

@@ -122,6 +122,14 @@ void dense_destroy(void* handle);
 int dense_gemm(void* handle, const float* w, const float* x, float* y, int64_t M, int64_t N, int64_t K,
                hipStream_t s);
 
+// Odd block counts of the 32-value formats: rows copied one all-zero block
+// longer (src/dst row bytes), x copied with K..Kp-1 zero; and the traced
+// outputs of such a run cut back (of every `from` items of `unit` bytes keep
+// the first `keep`).
+hipError_t launch_pad(const void* w, int64_t N, int src_row_bytes, int dst_row_bytes, void* wpad, const float* x,
+                      int64_t M, int64_t K, int64_t Kp, float* xpad, hipStream_t s);
+hipError_t launch_unpad(const void* src, int64_t groups, int from, int keep, int unit, void* dst, hipStream_t s);
+
 // Plan-free run on caller-provided device memory (the no-allocation entry
 // point; dry_run: the argument checks only, no HIP call), and setting the
 // calling thread's error message.

@@ -231,6 +231,68 @@ hipError_t launch_quantize_weights(int fmt, const float* w, int64_t N, int64_t K
     return hipGetLastError();
 }
 
+// ---------------------------------------------------- odd block counts ----
+// Rows of a 32-value format (Q8_0, Q4_0, Q5_0) with an odd number of blocks
+// are run as rows one block longer: the weights copied with one all-zero block
+// (d = 0) appended to every row, the activations with 32 zeros appended.  The
+// extra block adds exact zeros in both modes (mode (b): an all-zero block
+// quantizes to d = 0, q = 0).  One thread per 4 bytes of a padded row.
+
+__global__ __launch_bounds__(256) void pad_rows_kernel(const uint8_t* __restrict__ src, int64_t rows, int src_bytes,
+                                                       int dst_bytes, uint8_t* __restrict__ dst)
+{
+    const int per = dst_bytes / 4;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= rows * per) return;
+    const int64_t r = i / per;
+    const int c = 4 * (int)(i - r * per);
+    const uint8_t* sp = src + r * src_bytes;
+    uint32_t v = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+        if (c + b < src_bytes) v |= (uint32_t)sp[c + b] << (8 * b);
+    *reinterpret_cast<uint32_t*>(dst + r * dst_bytes + c) = v;
+}
+
+__global__ __launch_bounds__(256) void pad_x_kernel(const float* __restrict__ x, int64_t M, int K, int Kp,
+                                                    float* __restrict__ xp)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= M * Kp) return;
+    const int64_t m = i / Kp;
+    const int k = (int)(i - m * Kp);
+    xp[i] = k < K ? x[m * K + k] : 0.0f;
+}
+
+// Keeps the first `keep` of every `from` items of `unit` bytes: the traced
+// run's block sums and activation blocks of padded rows.  One thread per byte.
+__global__ __launch_bounds__(256) void unpad_kernel(const uint8_t* __restrict__ src, int64_t groups, int from, int keep,
+                                                    int unit, uint8_t* __restrict__ dst)
+{
+    const int per = keep * unit;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= groups * per) return;
+    const int64_t g = i / per;
+    dst[i] = src[g * from * unit + (i - g * per)];
+}
+
+hipError_t launch_pad(const void* w, int64_t N, int src_row_bytes, int dst_row_bytes, void* wpad, const float* x,
+                      int64_t M, int64_t K, int64_t Kp, float* xpad, hipStream_t s)
+{
+    const int64_t wt = N * (dst_row_bytes / 4);
+    hipLaunchKernelGGL(pad_rows_kernel, dim3(nblocks(wt, 256)), dim3(256), 0, s, (const uint8_t*)w, N, src_row_bytes,
+                       dst_row_bytes, (uint8_t*)wpad);
+    hipLaunchKernelGGL(pad_x_kernel, dim3(nblocks(M * Kp, 256)), dim3(256), 0, s, x, M, (int)K, (int)Kp, xpad);
+    return hipGetLastError();
+}
+
+hipError_t launch_unpad(const void* src, int64_t groups, int from, int keep, int unit, void* dst, hipStream_t s)
+{
+    hipLaunchKernelGGL(unpad_kernel, dim3(nblocks(groups * keep * unit, 256)), dim3(256), 0, s,
+                       (const uint8_t*)src, groups, from, keep, unit, (uint8_t*)dst);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm_prep(int fmt, int mode, const float* x, int64_t M, int64_t K, const GemmBufs& b, hipStream_t s,
                             uint8_t* act)
 {

@@ -40,9 +40,12 @@
  *   QMM_Q6_K  210 B per 256 values: 128 B low 4 bits, 64 B high 2 bits, int8
  *             scales[16] (one per 16 values), f16 d; w = d*sc*(q - 32).
  * Mode (b) pairs Q4_0 and Q5_0 with Q8_0 activations and Q6_K with Q8K (page
- * "同一个 GGUF，CPU 和 Metal 生成的文字不一样", section 出处).  Q8_0, Q4_0 and
- * Q5_0 need K divisible by 64 (their kernels read blocks in pairs), the
- * K-quants K divisible by 256.
+ * "同一个 GGUF，CPU 和 Metal 生成的文字不一样", section 出处).  K must be a
+ * multiple of the block size: 32 for Q8_0, Q4_0 and Q5_0, 256 for the
+ * K-quants.  The kernels read 32-value blocks in pairs: rows with an odd
+ * number of blocks run on copies one all-zero block longer, made in the plan's
+ * workspace at every run (correct at any such K; the throughput is that of
+ * the even case plus the copies).
  *
  * Pointers named "device" must be device memory of the current HIP device
  * (e.g. torch tensor data pointers); `stream` is a hipStream_t (NULL = the
@@ -90,8 +93,7 @@ typedef struct qmm_plan qmm_plan;
  * pages' QMatMul fixes its form when it is built (page "同一个 GGUF，CPU 和
  * Metal 生成的文字不一样", section 修法).  K must be a multiple of the block
  * size, 32 (Q8_0, Q4_0, Q5_0) or 256 (Q4_K, Q6_K), the shape check of page
- * "自己量化", section "3. 量化" (QMM_EBLOCK), and of 64 for the 32-value
- * formats (QMM_EUNSUPPORTED).
+ * "自己量化", section "3. 量化" (QMM_EBLOCK).
  * Allocates the plan's device workspace on the current device (hipMalloc).
  * On success *out receives the plan; on failure *out is set to NULL.
  */
@@ -172,7 +174,7 @@ int qmatmul_destroy(qmm_plan* plan);
  * K) bytes, 16-byte aligned) -> f32 [N x K] (device, 16-byte aligned, caller
  * owned).  Every value is the exact dequantized weight (Q8_0 d*q; Q4_K
  * d*sc_j*q - dmin*m_j; Q4_0 d*(q-8); Q5_0 d*(q-16); Q6_K d*sc*(q-32)) rounded
- * once to f32.  Q4_0 and Q5_0 need K divisible by 64 (QMM_EUNSUPPORTED).
+ * once to f32.
  *
  * qmatmul_run_dequantized (QMM_MODE_DEQUANT plans only): y = x . W^T with W
  * given as that f32 [N x K] matrix; x, y as in qmatmul_run.  The product is the

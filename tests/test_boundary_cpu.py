@@ -81,7 +81,9 @@ def test_row_bytes_and_block_sums_sizes():
     ((qmm.Q8_0, 576, 576, 307, 1), qmm.OK),
     ((qmm.Q4_K, 14336, 4096, 512, 0), qmm.OK),
     ((qmm.Q5_0, 192, 576, 307, 1), qmm.OK),
-    ((qmm.Q4_0, 576, 96, 1, 0), qmm.EUNSUPPORTED),  # 32-value formats need K % 64 == 0
+    ((qmm.Q4_0, 576, 96, 1, 0), qmm.OK),       # an odd number of 32-value blocks
+    ((qmm.Q8_0, 576, 96, 1, 1), qmm.OK),
+    ((qmm.Q5_0, 100, 4128, 40, 0), qmm.OK),
     ((qmm.Q4_0, 576, 40, 1, 0), qmm.EBLOCK),
     ((qmm.Q6_K, 576, 576, 1, 1), qmm.EBLOCK),
     ((qmm.Q6_K, 576, 768, 512, 0), qmm.OK),
@@ -128,7 +130,7 @@ def test_quantize_entry_points_validate_on_host():
     assert lib.qmatmul_quantize_weights(qmm.Q4_K, None, 1, 576, None, None) == qmm.EBLOCK
     assert lib.qmatmul_quantize_weights(qmm.Q6_K, None, 1, 576, None, None) == qmm.EBLOCK
     assert lib.qmatmul_quantize_weights(qmm.Q5_0, None, 2, 64, None, None) == qmm.EINVAL
-    assert lib.qmatmul_dequantize_weights(qmm.Q4_0, None, 2, 96, None, None) == qmm.EUNSUPPORTED  # pairs
+    assert lib.qmatmul_dequantize_weights(qmm.Q4_0, None, 2, 96, None, None) == qmm.EINVAL  # odd block count: ok, null
     assert lib.qmatmul_dequantize_weights(qmm.Q8_K, None, 1, 256, None, None) == qmm.EUNSUPPORTED
     assert lib.qmatmul_dequantize_weights(qmm.Q4_K, None, 1, 576, None, None) == qmm.EBLOCK
     assert lib.qmatmul_dequantize_weights(qmm.Q8_0, None, 0, 64, None, None) == qmm.OK   # N = 0

@@ -240,6 +240,55 @@ def test_scaleup_shape_sampled_rows(fmt, mode, m):
     assert_within(y[:, rows], yr, a, f"{NAME[fmt]} 14336x4096 M={m} mode={mode}")
 
 
+# Rows with an odd number of 32-value blocks (K % 64 == 32): the plan runs
+# them on copies one all-zero block longer.  Every path (the one-row decode,
+# the staged and tile decodes, the prefill) in both modes, single and traced
+# runs, grouped runs and the dequantize-all decode.
+ODD = [(qmm.Q8_0, 96), (qmm.Q8_0, 608), (qmm.Q8_0, 4128), (qmm.Q4_0, 96), (qmm.Q4_0, 608), (qmm.Q5_0, 608),
+       (qmm.Q5_0, 4128)]
+ODD_NAME = {qmm.Q8_0: "Q8_0", **NAME}
+
+
+@pytest.mark.parametrize("mode", MODES, ids=["a", "b"])
+@pytest.mark.parametrize("fmt,k", ODD, ids=[f"{ODD_NAME[f]}-{k}" for f, k in ODD])
+@pytest.mark.parametrize("m", [1, 3, 8, 37])
+def test_odd_block_count_parity(fmt, k, mode, m):
+    n = 77
+    wq = oracle.quantize(fmt, synth.weights_f32(7850 + k, n, k))
+    x = synth.acts_f32(7851 + m, m, k)
+    assert qmm.check(fmt, n, k, m, mode) == qmm.OK
+    y = run(fmt, mode, wq, n, k, x)
+    yr, a = ref(fmt, mode, wq, n, k, x)
+    assert_within(y, yr, a, f"{ODD_NAME[fmt]} {n}x{k} M={m} mode={mode}")
+    if mode == qmm.MODE_QACT:
+        with qmm.Plan(fmt, n, k, m, mode) as p:
+            yt, sums, act = p.run_traced(dev(wq), dev(x))
+            yt, sums, act = host(yt), host(sums).astype(np.int64), host(act)
+        assert np.array_equal(yt.view(np.uint32), y.view(np.uint32))
+        assert np.array_equal(sums, oracle.block_sums(fmt, wq, n, k, x))
+        assert np.array_equal(act, oracle.quantize(qmm.Q8_0, x))
+
+
+@pytest.mark.parametrize("fmt,k", [(qmm.Q8_0, 608), (qmm.Q4_0, 96), (qmm.Q5_0, 4128)])
+def test_odd_block_count_dequantize_and_group(fmt, k):
+    ns = [64, 33]
+    wqs = [oracle.quantize(fmt, synth.weights_f32(7860 + n, n, k)) for n in ns]
+    want = oracle.dequantize(fmt, wqs[0], k).astype(np.float32)
+    assert np.array_equal(host(qmm.dequantize_weights(fmt, dev(wqs[0]), ns[0], k)), want)
+    x = synth.acts_f32(7870, 1, k)
+    for mode in (qmm.MODE_F32ACT, qmm.MODE_QACT):
+        plans = [qmm.Plan(fmt, n, k, 1, mode) for n in ns]
+        try:
+            wg = [dev(w) for w in wqs]
+            sep = [host(p.run(w, dev(x))) for p, w in zip(plans, wg)]
+            grp = [host(y) for y in qmm.run_group(plans, wg, dev(x))]
+        finally:
+            for p in plans:
+                p.close()
+        for a_, b_ in zip(sep, grp):
+            assert np.array_equal(a_, b_)
+
+
 # Long rows: more units than two per lane (each lane walks its units), and
 # activations too large to stage in LDS (read from global memory).
 LONG = [(qmm.Q4_0, 40, 16384), (qmm.Q5_0, 24, 9216), (qmm.Q6_K, 40, 14336)]
