@@ -391,9 +391,9 @@ def small_workload(args, qmm, torch, synth, stream):
                     "TOPS_graph": round(flop / (gus * 1e-6) / 1e12, 3),
                     "launches": len(probs)}
                 del g
-                if phase == "decode":
-                    # the same step with each layer's q/k/v and gate/up as one grouped run on
-                    # one activation row (that of q, or gate), the others as before
+                if True:
+                    # the same pass with each layer's q/k/v and gate/up as one grouped run on
+                    # one activation matrix (that of q, or gate), the others as before
                     groups = []
                     for base in range(0, len(probs) - 1, 7):  # q k v o gate up down
                         groups += [[base, base + 1, base + 2], [base + 3], [base + 4, base + 5], [base + 6]]
@@ -421,7 +421,7 @@ def small_workload(args, qmm, torch, synth, stream):
                         torch.cuda.synchronize()
                         assert all(torch.equal(a, b) for a, b in zip(y, ref)), f"grouped graph replay {rep} differs"
                     gus = timed(g.replay, 10)
-                    out["passes"][f"decode_grouped:{pname}:{md}"] = {
+                    out["passes"][f"{phase}_grouped:{pname}:{md}"] = {
                         "ms_per_pass_stream": round(us / 1000.0, 3), "ms_per_pass_graph": round(gus / 1000.0, 3),
                         "TOPS_stream": round(flop / (us * 1e-6) / 1e12, 3),
                         "TOPS_graph": round(flop / (gus * 1e-6) / 1e12, 3),

@@ -430,6 +430,31 @@ extern "C" int qmatmul_run_group(const qmm_plan* const* plans, int count, const 
             return QMM_OK;
         }
     }
+    if (M > GEMV_MAX_M && p0->mode != QMM_MODE_DEQUANT && p0->Kr == p0->K) {
+        // prefill: the activations prepared once (in plan 0's workspace), then one
+        // launch per gemm_group_max() plans; Q4_0/Q5_0 weights first rewritten as
+        // Q8_0 blocks in each plan's workspace, as in their separate runs
+        const int kf = p0->fmt == QMM_Q4_0 || p0->fmt == QMM_Q5_0 ? FMT_Q8_0 : p0->fmt;
+        hipError_t e = launch_gemm_prep(kf, p0->mode, x, M, p0->K, p0->gm, s);
+        const int gmax = gemm_group_max();
+        for (int i = 0; i < count && e == hipSuccess; i += gmax) {
+            const int c = count - i < gmax ? count - i : gmax;
+            const void* wk[QMM_GROUP_MAX];
+            int64_t Ns[QMM_GROUP_MAX];
+            for (int j = 0; j < c && e == hipSuccess; ++j) {
+                const qmm_plan* pj = plans[i + j];
+                Ns[j] = pj->N;
+                wk[j] = w[i + j];
+                if (kf != p0->fmt) {
+                    e = launch_ext_to_q8_0(pj->fmt, w[i + j], pj->N, pj->K, pj->ex.tw, s);
+                    wk[j] = pj->ex.tw;
+                }
+            }
+            if (e == hipSuccess) e = launch_gemm_group(kf, p0->mode, c, wk, Ns, y + i, p0->K, M, p0->gm, s);
+        }
+        if (e != hipSuccess) return fail(QMM_EHIP, "kernel launch: %s", hipGetErrorString(e));
+        return QMM_OK;
+    }
     for (int i = 0; i < count; ++i) {
         const int st = run_impl(plans[i], w[i], x, y[i], nullptr, M, stream);
         if (st != QMM_OK) return st;

@@ -185,6 +185,37 @@ QMM_DEV void pair_codes(const uint32_t* r, uint32_t v[2][8], float d[2])
     }
 }
 
+// Grouped prefill launches: up to PG_MAX problems sharing K, the mode and the
+// activations (a layer's q/k/v or gate/up projections), each with its own
+// weights, outputs and rows; problem p owns column tiles t0[p] .. t0[p+1]-1
+// of the launch, so every output tile belongs to one problem and computes
+// what that problem's own launch computes.
+constexpr int PG_MAX = 4;
+struct PrefillGroup {
+    const uint8_t* w[PG_MAX];
+    float* y[PG_MAX];
+    int n[PG_MAX];       // rows (outputs) of each problem
+    int t0[PG_MAX + 1];  // first column tile of each problem; t0[groups] = all column tiles
+    int groups;
+};
+// The problem of column tile nt (a chain of selects: no indexed access to the
+// kernel arguments): its weights, outputs, rows and first column tile.
+QMM_DEV void pg_locate(const PrefillGroup& g, int nt, const uint8_t*& w, float*& y, int& n, int& tile0)
+{
+    w = g.w[0];
+    y = g.y[0];
+    n = g.n[0];
+    tile0 = 0;
+#pragma unroll
+    for (int q = 1; q < PG_MAX; ++q) {
+        const bool in = q < g.groups && nt >= g.t0[q];
+        w = in ? g.w[q] : w;
+        y = in ? g.y[q] : y;
+        n = in ? g.n[q] : n;
+        tile0 = in ? g.t0[q] : tile0;
+    }
+}
+
 // Q8_0 GEMV block-pair k permutation.  Inside a 4-byte-aligned pair of
 // blocks (68 bytes), lane group g (0..3) of the MFMA operand takes the 8
 // weight bytes at dwords (1+2g, 2+2g) of the even block; group 3 takes dword

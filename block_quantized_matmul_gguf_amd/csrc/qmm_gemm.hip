@@ -49,9 +49,9 @@
 namespace qmm {
 
 struct GemmArgs {
-    const uint8_t* w;
+    PrefillGroup g;      // the problems: weights, outputs (EMIT instances: may be null), rows
     int64_t row_bytes;
-    int N, K, M;
+    int K, M;
     int nm;              // row blocks of the output (tiles along M)
     int remap;           // 1: give each XCD a contiguous run of tiles
     const _Float16* hi;  // mode (a): hi part of x*s [M][K]; mode (b): the quantized values as f16 [M][K]
@@ -59,7 +59,6 @@ struct GemmArgs {
     const float* rs;     // mode (a): 1/s per row
     const _Float16* xs;  // Q4_K: [M][K/256][16] sub-block sums * s / 32, hi then lo
     const float* dx;     // mode (b): activation block scales, block-major [K/256][M]
-    float* y;            // EMIT instances: may be null
     int32_t* sums;       // EMIT (Q6_K mode (b)): per super-block 17 values, sumi last (the per-16 sums not formed)
 };
 
@@ -109,14 +108,19 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_kernel(GemmArg
     static_assert(!EMIT || (Q6 && MB), "the traced f16 prefill is Q6_K mode (b)");
     extern __shared__ __align__(16) uint8_t lds[];
 
-    const int M = a.M, N = a.N, K = a.K;
+    const int M = a.M, K = a.K;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     int t = blockIdx.x;
     if (a.remap) {
         const int per = (int)gridDim.x >> 3;
         t = (t & 7) * per + (t >> 3);
     }
-    const int m0 = (t % a.nm) * BM, n0 = (t / a.nm) * BN;
+    // this tile's problem (grouped launches) and its place in it
+    const uint8_t* W;
+    float* Y;
+    int N, tile0;
+    pg_locate(a.g, t / a.nm, W, Y, N, tile0);
+    const int m0 = (t % a.nm) * BM, n0 = (t / a.nm - tile0) * BN;
     const int wm = (wave % WM) * 16 * TM, wn = (wave / WM) * 16 * TN;
     const int nst = K / 64;
     const int li = lane & 15, kg = lane >> 4;
@@ -130,8 +134,8 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_kernel(GemmArg
     // resource starts at the dword at or below the tile's first row (w0 bytes
     // before it) and ends at the dword holding its last byte (a dword holding a
     // byte of the buffer lies in the buffer's pages)
-    const uint32_t w0 = Q6 ? (uint32_t)(((uintptr_t)a.w + (uint64_t)n0 * rb) & 3u) : 0u;
-    const rsrc_t rw = make_rsrc(a.w + (int64_t)n0 * rb - w0,
+    const uint32_t w0 = Q6 ? (uint32_t)(((uintptr_t)W + (uint64_t)n0 * rb) & 3u) : 0u;
+    const rsrc_t rw = make_rsrc(W + (int64_t)n0 * rb - w0,
                                 clamp_u32(Q6 ? ((int64_t)(N - n0) * rb + w0 + 3) & ~3ll : (int64_t)(N - n0) * rb));
     const rsrc_t rx = make_rsrc(FMT != FMT_Q4_K ? a.hi : a.xs + (int64_t)m0 * (K / 256) * 16,
                                 clamp_u32((int64_t)(M - m0) * (K / 256) * 32));
@@ -584,14 +588,14 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_kernel(GemmArg
             mrow[r] = m0 + wm + 16 * i + 4 * kg + r;
             rsv[r] = MB ? 1.0f : mrow[r] < M ? a.rs[mrow[r]] : 0.0f;
         }
-        if (EMIT && !a.y) continue;
+        if (EMIT && !Y) continue;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const int n = n0 + wn + 16 * j + li;
             if (n >= N) continue;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                if (mrow[r] < M) a.y[(int64_t)mrow[r] * N + n] = acc[i][j][r] * rsv[r];
+                if (mrow[r] < M) Y[(int64_t)mrow[r] * N + n] = acc[i][j][r] * rsv[r];
         }
     }
 }
@@ -665,8 +669,11 @@ static hipError_t launch_tile(GemmArgs a, hipStream_t s)
 {
     using C = GemmCfg<FMT, MODE, WM, WN, TM, TN>;
     static_assert(C::BYTES <= 160 * 1024, "LDS of a compute unit");
-    const int nm = (a.M + C::BM - 1) / C::BM, nn = (a.N + C::BN - 1) / C::BN;
-    const int64_t grid = (int64_t)nm * nn;
+    const int nm = (a.M + C::BM - 1) / C::BM;
+    a.g.t0[0] = 0;
+    for (int p = 0; p < PG_MAX; ++p)
+        a.g.t0[p + 1] = a.g.t0[p] + (p < a.g.groups ? (a.g.n[p] + C::BN - 1) / C::BN : 0);
+    const int64_t grid = (int64_t)nm * a.g.t0[a.g.groups];
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     a.nm = nm;
     a.remap = grid % 8 == 0 ? 1 : 0;
@@ -687,16 +694,24 @@ static hipError_t launch_fmt(const GemmArgs& a, GemmTile t, hipStream_t s)
     return launch_tile<FMT, MODE, EMIT, 2, 2, 1, 2>(a, s);
 }
 
-hipError_t launch_gemm(int fmt, int mode, const void* w, int64_t N, int64_t K, int64_t M, const GemmBufs& b,
-                       float* y, hipStream_t s, int32_t* sums)
+// count problems sharing K, the mode and the prepared activations b (one
+// launch; the same per-output arithmetic as separate launches).
+hipError_t launch_gemm_group(int fmt, int mode, int count, const void* const* w, const int64_t* Ns, float* const* y,
+                             int64_t K, int64_t M, const GemmBufs& b, hipStream_t s, int32_t* sums)
 {
-    const int64_t row_bytes = fmt == FMT_Q8_0 ? (K / 32) * 34 : fmt == FMT_Q4_K ? (K / 256) * 144 : (K / 256) * 210;
-    if (mode == MODE_B && fmt != FMT_Q6_K) return launch_gemm_q(fmt, w, N, K, M, b, y, s, sums);
+    if (count < 1 || count > PG_MAX || (sums && count != 1)) return hipErrorInvalidValue;
+    if (mode == MODE_B && fmt != FMT_Q6_K) return launch_gemm_q_group(fmt, count, w, Ns, y, K, M, b, s, sums);
     if (sums && !(fmt == FMT_Q6_K && mode == MODE_B)) return hipErrorInvalidValue;
     GemmArgs a{};
-    a.w = (const uint8_t*)w;
-    a.row_bytes = row_bytes;
-    a.N = (int)N;
+    int64_t ntot = 0;
+    for (int p = 0; p < count; ++p) {
+        a.g.w[p] = (const uint8_t*)w[p];
+        a.g.y[p] = y[p];
+        a.g.n[p] = (int)Ns[p];
+        ntot += Ns[p];
+    }
+    a.g.groups = count;
+    a.row_bytes = fmt == FMT_Q8_0 ? (K / 32) * 34 : fmt == FMT_Q4_K ? (K / 256) * 144 : (K / 256) * 210;
     a.K = (int)K;
     a.M = (int)M;
     a.hi = b.a0;
@@ -704,9 +719,8 @@ hipError_t launch_gemm(int fmt, int mode, const void* w, int64_t N, int64_t K, i
     a.rs = b.rs;
     a.xs = b.xs;
     a.dx = b.sd;
-    a.y = y;
     a.sums = sums;
-    const GemmTile t = pick_tile(M, N, fmt);
+    const GemmTile t = pick_tile(M, ntot, fmt);
     hipError_t e;
     if (fmt == FMT_Q8_0) e = launch_fmt<FMT_Q8_0, MODE_A, false>(a, t, s);
     else if (fmt == FMT_Q4_K) e = launch_fmt<FMT_Q4_K, MODE_A, false>(a, t, s);
@@ -714,6 +728,14 @@ hipError_t launch_gemm(int fmt, int mode, const void* w, int64_t N, int64_t K, i
     else e = sums ? launch_fmt<FMT_Q6_K, MODE_B, true>(a, t, s) : launch_fmt<FMT_Q6_K, MODE_B, false>(a, t, s);
     if (e != hipSuccess) return e;
     return hipGetLastError();
+}
+
+int gemm_group_max() { return PG_MAX; }
+
+hipError_t launch_gemm(int fmt, int mode, const void* w, int64_t N, int64_t K, int64_t M, const GemmBufs& b,
+                       float* y, hipStream_t s, int32_t* sums)
+{
+    return launch_gemm_group(fmt, mode, 1, &w, &N, &y, K, M, b, s, sums);
 }
 
 }  // namespace qmm

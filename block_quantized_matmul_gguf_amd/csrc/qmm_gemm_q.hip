@@ -38,15 +38,14 @@
 namespace qmm {
 
 struct QGemmArgs {
-    const uint8_t* w;
+    PrefillGroup g;       // the problems: weights, outputs (EMIT instances: may be null), rows
     int64_t row_bytes;
-    int N, K, M;
+    int K, M;
     int nm;               // row tiles of the output
     int remap;            // 1: give each XCD a contiguous run of tiles
     const int8_t* q;      // quantized activations [M][K]
     const float* dx;      // activation block scales, block-major: Q8_0 [K/32][M], Q8K [K/256][M]
     const _Float16* bsx;  // Q8K: [K/256][M][16] sub-block sums, multiples of 64 then remainders
-    float* y;             // EMIT instances: may be null
     int32_t* sums;        // EMIT: Q8_0 S per block; Q4_K S_0..S_7 and summins per super-block (slot 8 left)
 };
 
@@ -102,14 +101,19 @@ __global__ __launch_bounds__(128 * MW, 2) void gemm_q_kernel(QGemmArgs a)
     constexpr bool Q8 = C::Q8;
     extern __shared__ __align__(16) uint8_t lds[];
 
-    const int M = a.M, N = a.N, K = a.K;
+    const int M = a.M, K = a.K;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     int t = blockIdx.x;
     if (a.remap) {
         const int per = (int)gridDim.x >> 3;
         t = (t & 7) * per + (t >> 3);
     }
-    const int m0 = (t % a.nm) * Q_BM, n0 = (t / a.nm) * BN;
+    // this tile's problem (grouped launches) and its place in it
+    const uint8_t* W;
+    float* Y;
+    int N, tile0;
+    pg_locate(a.g, t / a.nm, W, Y, N, tile0);
+    const int m0 = (t % a.nm) * Q_BM, n0 = (t / a.nm - tile0) * BN;
     const int wm = (wave % MW) * 32, g = wave / MW;
     const int l32 = lane & 31, hl = lane >> 5;
     const int nst = (K + SV - 1) / SV;
@@ -122,7 +126,7 @@ __global__ __launch_bounds__(128 * MW, 2) void gemm_q_kernel(QGemmArgs a)
     // M and K.  Past the end of a ragged last stage, the staging reads the
     // next row's bytes into blocks that are never multiplied.
     const rsrc_t rq = make_rsrc(a.q + (int64_t)m0 * K, clamp_u32((int64_t)(M - m0) * K));
-    const rsrc_t rw = make_rsrc(a.w + (int64_t)n0 * rb, clamp_u32((int64_t)(N - n0) * rb));
+    const rsrc_t rw = make_rsrc(W + (int64_t)n0 * rb, clamp_u32((int64_t)(N - n0) * rb));
     const uint32_t dx_bytes = clamp_u32((int64_t)(M - m0) * 4), bsx_bytes = clamp_u32((int64_t)(M - m0) * 32);
     auto rdx_of = [&](int blk) { return make_rsrc(a.dx + (int64_t)blk * M + m0, dx_bytes); };
 
@@ -432,7 +436,7 @@ __global__ __launch_bounds__(128 * MW, 2) void gemm_q_kernel(QGemmArgs a)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int m = m0 + crow(r);
-                if (m < M && (!EMIT || a.y)) a.y[(int64_t)m * N + n] = acc[j][r] + red[crow(r) * BN + 32 * j + l32];
+                if (m < M && (!EMIT || Y)) Y[(int64_t)m * N + n] = acc[j][r] + red[crow(r) * BN + 32 * j + l32];
             }
         }
     }
@@ -505,8 +509,11 @@ template <int FMT, int MW, int TN, bool EMIT>
 static hipError_t launch_q(QGemmArgs a, hipStream_t s)
 {
     using C = QCfg<FMT, MW, TN, Q_KB>;
-    const int nm = (a.M + C::Q_BM - 1) / C::Q_BM, nn = (a.N + C::BN - 1) / C::BN;
-    const int64_t grid = (int64_t)nm * nn;
+    const int nm = (a.M + C::Q_BM - 1) / C::Q_BM;
+    a.g.t0[0] = 0;
+    for (int p = 0; p < PG_MAX; ++p)
+        a.g.t0[p + 1] = a.g.t0[p] + (p < a.g.groups ? (a.g.n[p] + C::BN - 1) / C::BN : 0);
+    const int64_t grid = (int64_t)nm * a.g.t0[a.g.groups];
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     a.nm = nm;
     a.remap = grid % 8 == 0 ? 1 : 0;
@@ -547,32 +554,44 @@ __global__ __launch_bounds__(256) void q4k_sumi_kernel(const uint8_t* __restrict
     o[8] = si;
 }
 
-hipError_t launch_gemm_q(int fmt, const void* w, int64_t N, int64_t K, int64_t M, const GemmBufs& b, float* y,
-                         hipStream_t s, int32_t* sums)
+hipError_t launch_gemm_q_group(int fmt, int count, const void* const* w, const int64_t* Ns, float* const* y,
+                               int64_t K, int64_t M, const GemmBufs& b, hipStream_t s, int32_t* sums)
 {
+    if (count < 1 || count > PG_MAX || (sums && count != 1)) return hipErrorInvalidValue;
     QGemmArgs a{};
-    a.w = (const uint8_t*)w;
+    int64_t ntot = 0;
+    for (int p = 0; p < count; ++p) {
+        a.g.w[p] = (const uint8_t*)w[p];
+        a.g.y[p] = y[p];
+        a.g.n[p] = (int)Ns[p];
+        ntot += Ns[p];
+    }
+    a.g.groups = count;
     a.row_bytes = fmt == FMT_Q8_0 ? (K / 32) * 34 : (K / 256) * 144;
-    a.N = (int)N;
     a.K = (int)K;
     a.M = (int)M;
     a.q = (const int8_t*)b.a0;
     a.dx = b.sd;
     a.bsx = b.xs;
-    a.y = y;
     a.sums = sums;
-    const QTile t = pick_qtile(M, N);
+    const QTile t = pick_qtile(M, ntot);
     const bool emit = sums != nullptr;
     hipError_t e;
     if (fmt == FMT_Q8_0) e = emit ? launch_q_fmt<FMT_Q8_0, true>(a, t, s) : launch_q_fmt<FMT_Q8_0, false>(a, t, s);
     else e = emit ? launch_q_fmt<FMT_Q4_K, true>(a, t, s) : launch_q_fmt<FMT_Q4_K, false>(a, t, s);
     if (e != hipSuccess) return e;
     if (emit && fmt == FMT_Q4_K) {
-        const int64_t items = M * N * (K / 256);
-        hipLaunchKernelGGL(q4k_sumi_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, (const uint8_t*)w, N,
-                           (int)K, (int)M, sums);
+        const int64_t items = M * Ns[0] * (K / 256);
+        hipLaunchKernelGGL(q4k_sumi_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, (const uint8_t*)w[0],
+                           Ns[0], (int)K, (int)M, sums);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_gemm_q(int fmt, const void* w, int64_t N, int64_t K, int64_t M, const GemmBufs& b, float* y,
+                         hipStream_t s, int32_t* sums)
+{
+    return launch_gemm_q_group(fmt, 1, &w, &N, &y, K, M, b, s, sums);
 }
 
 }  // namespace qmm

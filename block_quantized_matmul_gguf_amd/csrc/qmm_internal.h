@@ -87,6 +87,13 @@ hipError_t launch_gemm(int fmt, int mode, const void* w, int64_t N, int64_t K, i
 // per super-block); y may then be null.
 hipError_t launch_gemm_q(int fmt, const void* w, int64_t N, int64_t K, int64_t M, const GemmBufs& b, float* y,
                          hipStream_t s, int32_t* sums = nullptr);
+// Grouped prefill: count (<= 4) problems sharing K, the mode and the prepared
+// activations b in one launch, each output computed as its own launch would.
+hipError_t launch_gemm_group(int fmt, int mode, int count, const void* const* w, const int64_t* Ns, float* const* y,
+                             int64_t K, int64_t M, const GemmBufs& b, hipStream_t s, int32_t* sums = nullptr);
+hipError_t launch_gemm_q_group(int fmt, int count, const void* const* w, const int64_t* Ns, float* const* y,
+                               int64_t K, int64_t M, const GemmBufs& b, hipStream_t s, int32_t* sums = nullptr);
+int gemm_group_max();
 
 // Q4_0, Q5_0 and Q6_K weights.  Decode runs (and every Q6_K run) take the
 // ext kernels; Q4_0/Q5_0 prefill transcodes the weights to Q8_0 blocks (same

@@ -130,8 +130,10 @@ int qmatmul_run(const qmm_plan* plan, const void* w_blocks, const float* x, floa
  * Q4_0, Q5_0 and Q6_K (where their activations fit in LDS), the plans' rows
  * go to one launch per four plans (the activations are loaded and quantized
  * once per workgroup for all of them), giving bit-for-bit the values
- * separate runs give; otherwise the plans run one after another as with
- * qmatmul_run.  Errors: as
+ * separate runs give; at M > 8 the activations are prepared once and the
+ * plans' output tiles go to one prefill launch per four plans (again the
+ * separate runs' values bit for bit); otherwise the plans run one after
+ * another as with qmatmul_run.  Errors: as
  * qmatmul_run for each plan, and QMM_EINVAL for null arrays, count out of
  * range or plans that differ in format, K or mode.
  */

@@ -26,12 +26,53 @@ CASES = [(qmm.Q8_0, qmm.MODE_F32ACT, 1), (qmm.Q8_0, qmm.MODE_QACT, 8), (qmm.Q4_K
          # the other formats: one-row kernel, staged decode (in-kernel and separate activation
          # quantization), the Q8_0 rewrite for the prefill, Q6_K's eight-row launches
          (qmm.Q5_0, qmm.MODE_QACT, 1), (qmm.Q5_0, qmm.MODE_F32ACT, 1), (qmm.Q4_0, qmm.MODE_QACT, 8),
-         (qmm.Q4_0, qmm.MODE_F32ACT, 96), (qmm.Q6_K, qmm.MODE_QACT, 1), (qmm.Q6_K, qmm.MODE_QACT, 12)]
+         (qmm.Q4_0, qmm.MODE_F32ACT, 96), (qmm.Q6_K, qmm.MODE_QACT, 1), (qmm.Q6_K, qmm.MODE_QACT, 12),
+         (qmm.Q6_K, qmm.MODE_F32ACT, 96),
+         # an odd block count (the padded copies)
+         (qmm.Q8_0, qmm.MODE_QACT, 1), ]
+
+
+@pytest.mark.parametrize("fmt,mode", [(qmm.Q8_0, qmm.MODE_F32ACT), (qmm.Q8_0, qmm.MODE_QACT), (qmm.Q4_K, qmm.MODE_QACT),
+                                      (qmm.Q5_0, qmm.MODE_QACT), (qmm.Q6_K, qmm.MODE_F32ACT)])
+def test_graph_replays_of_grouped_prefill(fmt, mode):
+    # a layer's q/k/v (576, 192, 192 rows) as one grouped run at M = 307, captured
+    k, m, ns = (1536 if fmt in (qmm.Q4_K, qmm.Q6_K) else 576), 307, [576, 192, 192]
+    dev = torch.device("cuda")
+    w = [torch.from_numpy(oracle.quantize(fmt, synth.weights_f32(7200 + n + i, n, k))).to(dev) for i, n in enumerate(ns)]
+    x = torch.from_numpy(synth.acts_f32(7300, m, k)).to(dev)
+    ys = [torch.empty((m, n), dtype=torch.float32, device=dev) for n in ns]
+    plans = [qmm.Plan(fmt, n, k, m, mode) for n in ns]
+    try:
+        stream = torch.cuda.current_stream()
+        qmm.run_group(plans, w, x, ys, stream)
+        torch.cuda.synchronize()
+        ref = [t.clone() for t in ys]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            qmm.run_group(plans, w, x, ys, torch.cuda.current_stream())
+        for rep in range(4):
+            for t in ys:
+                t.fill_(float("nan"))
+            qmm.run_group(plans, w, x, ys, stream)  # eager work between replays
+            torch.cuda.synchronize()
+            assert all(torch.equal(a, b) for a, b in zip(ys, ref))
+            for t in ys:
+                t.fill_(float("nan"))
+            g.replay()
+            torch.cuda.synchronize()
+            for i, (a, b) in enumerate(zip(ys, ref)):
+                assert torch.equal(a, b), f"replay {rep}, plan {i} differs from the eager grouped run"
+        del g
+    finally:
+        for p in plans:
+            p.close()
 
 
 @pytest.mark.parametrize("fmt,mode,m", CASES, ids=[f"fmt{f}-mode{md}-M{m}" for f, md, m in CASES])
 def test_graph_replays_match_eager_runs(fmt, mode, m):
     n, k = 640, 1536 if fmt in (qmm.Q4_K, qmm.Q6_K) else 576
+    if (fmt, mode, m) == CASES[-1]:
+        k = 608  # 19 blocks
     dev = torch.device("cuda")
     w = [torch.from_numpy(oracle.quantize(fmt, synth.weights_f32(7000 + i, n, k))).to(dev) for i in range(3)]
     x = torch.from_numpy(synth.acts_f32(7100 + m, m, k)).to(dev)

@@ -297,6 +297,38 @@ def test_grouped_run_equals_separate_runs(fmt, k, ns, mode, m):
         assert_within(grp[i], yr, a, f"group plan {i} {FMT_NAME[fmt]} {n}x{k} M={m} mode={mode}")
 
 
+# Grouped prefill (M > 8): the activations prepared once, the plans' output
+# tiles in one launch per four plans; bit for bit the separate runs.
+PGROUPS = [
+    (qmm.Q8_0, 576, [576, 192, 192]),             # q, k, v
+    (qmm.Q8_0, 576, [1536, 1536]),                # gate, up
+    (qmm.Q4_K, 1536, [576, 100, 300, 64, 33]),    # five plans: two launches
+    (qmm.Q6_K, 512, [200, 77]),
+    (qmm.Q4_0, 576, [576, 192]),                  # rewritten as Q8_0 blocks per plan
+    (qmm.Q5_0, 1536, [96, 130]),
+]
+
+
+@pytest.mark.parametrize("m", [9, 37, 307])
+@pytest.mark.parametrize("mode", [qmm.MODE_F32ACT, qmm.MODE_QACT], ids=["a", "b"])
+@pytest.mark.parametrize("fmt,k,ns", PGROUPS, ids=[f"fmt{f}-{k}-{len(ns)}" for f, k, ns in PGROUPS])
+def test_grouped_prefill_equals_separate_runs(fmt, k, ns, mode, m):
+    x = synth.acts_f32(8300 + k + m, m, k)
+    wqs = [oracle.quantize(fmt, synth.weights_f32(8400 + i + n, n, k)) for i, n in enumerate(ns)]
+    plans = [qmm.Plan(fmt, n, k, m, mode) for n in ns]
+    try:
+        xg, wg = dev(x), [dev(w) for w in wqs]
+        sep = [host(p.run(w, xg)) for p, w in zip(plans, wg)]
+        grp = [host(y) for y in qmm.run_group(plans, wg, xg)]
+    finally:
+        for p in plans:
+            p.close()
+    for i, (n, wq) in enumerate(zip(ns, wqs)):
+        assert np.array_equal(grp[i].view(np.uint32), sep[i].view(np.uint32)), f"plan {i} ({n} rows)"
+        yr, a = ref(fmt, mode, wq, n, k, x)
+        assert_within(grp[i], yr, a, f"grouped prefill plan {i} fmt={fmt} {n}x{k} M={m} mode={mode}")
+
+
 def test_grouped_run_rejects_mixed_plans():
     x = dev(synth.acts_f32(8200, 1, 576))
     w = dev(oracle.quantize(oracle.Q8_0, synth.weights_f32(8201, 64, 576)))
