@@ -48,6 +48,7 @@ SIGNATURES = {
     "qmatmul_run_dequantized": (_int, [_p, _p, _p, _p, _i64, _p]),
     "qmatmul_run_group": (_int, [ctypes.POINTER(_p), _int, ctypes.POINTER(_p), _p, ctypes.POINTER(_p), _i64, _p]),
     "qmatmul_run_noalloc": (_int, [_int, _i64, _i64, _i64, _int, _p, _p, _p, _p]),
+    "qmatmul_quantize_q4_k_search": (_int, [_p, _i64, _i64, _p, _p]),
     "qmatmul_check": (_int, [_int, _i64, _i64, _i64, _int]),
     "qmatmul_row_bytes": (_i64, [_int, _i64]),
     "qmatmul_block_sums_per_row": (_i64, [_int, _i64]),
@@ -320,6 +321,22 @@ def quantize_weights(fmt: int, w, out=None, stream=None):
         out = torch.empty((n, rb), dtype=torch.uint8, device=w.device)
     _need(out, torch.uint8, (n, rb), "out")
     _check(lib().qmatmul_quantize_weights(fmt, _ptr(w), n, k, _ptr(out), _stream(stream)), "qmatmul_quantize_weights")
+    return out
+
+
+def quantize_q4_k_search(w, out=None, stream=None):
+    """Q4_K blocks of the rows of w (float32 [N, K] on the GPU) with the
+    least-squares search for each sub-block's scale and min."""
+    torch = _torch()
+    _need(w, torch.float32, None, "w")
+    n, k = w.shape
+    rb = row_bytes(Q4_K, k)
+    if rb < 0:
+        raise ValueError(f"K={k} is not a multiple of 256")
+    if out is None:
+        out = torch.empty((n, rb), dtype=torch.uint8, device=w.device)
+    _need(out, torch.uint8, (n, rb), "out")
+    _check(lib().qmatmul_quantize_q4_k_search(_ptr(w), n, k, _ptr(out), _stream(stream)), "qmatmul_quantize_q4_k_search")
     return out
 
 

@@ -573,6 +573,22 @@ extern "C" int qmatmul_quantize_weights(int format, const float* w, int64_t N, i
     return QMM_OK;
 }
 
+extern "C" int qmatmul_quantize_q4_k_search(const float* w, int64_t N, int64_t K, void* out, void* stream)
+{
+    g_err[0] = 0;
+    if (N < 0 || K <= 0) return fail(QMM_EINVAL, "bad sizes N=%lld K=%lld", (long long)N, (long long)K);
+    if (K % 256)
+        return fail(QMM_EBLOCK, "quantized tensor must have their last dim divisible by block size [%lld, %lld] 256",
+                    (long long)N, (long long)K);
+    if (N == 0) return QMM_OK;
+    if (!w || !out) return fail(QMM_EINVAL, "null pointer");
+    if (!aligned(w, 16)) return fail(QMM_EINVAL, "w must be 16-byte aligned");
+    if (!aligned(out, 16)) return fail(QMM_EINVAL, "out_blocks must be 16-byte aligned");
+    hipError_t e = launch_quantize_q4_k_search(w, N, K, out, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(QMM_EHIP, "kernel launch: %s", hipGetErrorString(e));
+    return QMM_OK;
+}
+
 extern "C" const char* qmatmul_status_string(int status)
 {
     switch (status) {

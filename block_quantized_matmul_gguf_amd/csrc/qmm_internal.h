@@ -72,6 +72,7 @@ int gemv_max_splits(int fmt, int64_t K);
 
 hipError_t launch_quantize_act(int act_fmt, const float* x, int64_t M, int64_t K, void* out, hipStream_t s);
 hipError_t launch_quantize_weights(int fmt, const float* w, int64_t N, int64_t K, void* out, hipStream_t s);
+hipError_t launch_quantize_q4_k_search(const float* w, int64_t N, int64_t K, void* out, hipStream_t s);
 
 hipError_t launch_gemv(int fmt, int mode, const void* w, const float* x, int64_t N, int64_t K, int M,
                        const GemvBufs& b, float* y, hipStream_t s, const Trace* tr = nullptr);

@@ -150,6 +150,89 @@ __global__ __launch_bounds__(256) void gemm_prep_kernel(const float* __restrict_
 // re-quantized against the stored scales: q = clamp(round((x + dmin*m_j) /
 // (d*sc_j)), 0, 15).  The pages name QTensor::quantize(&w, Q4K) but not its
 // search (page "自己量化", section "3. 量化"); this is the plain min/max rule.
+//
+// SEARCH: each sub-block's scale and min come from a least-squares search
+// instead.  For the sub-block's lo = min(0, min x), hi = max x, r = hi - lo,
+// the codes q = clamp(round((x - lo) * c), 0, 15) are tried for the plain
+// rule's c = 15 / r and for c = (140 + k) / (10 r), k = 0..20; each gets the
+// least-squares line x ~ a q + b (b forced to 0, a refitted alone, when the
+// fit gives b > 0: the format's offset -dmin*m is never positive; a <= 0 or
+// all-equal codes skip the candidate), and the first of smallest squared error
+// wins, the plain rule's (a = r/15, b = lo) competing first.  scale = a,
+// min = -b; the super-block stage is the plain rule's.  Sums run in index
+// order, one IEEE operation at a time, so the bytes are those of the oracle.
+QMM_DEV void q4k_sub_range(const float* x, float& lo, float& hi)
+{
+    lo = 0.0f;
+    hi = x[0];
+    for (int l = 0; l < 32; ++l) {
+        const float t = x[l];
+        lo = t < lo ? t : lo;
+        hi = t > hi ? t : hi;
+    }
+}
+
+QMM_DEV void q4k_search_fit(const float* x, float& scale, float& minv)
+{
+#pragma clang fp contract(off)
+    float lo, hi;
+    q4k_sub_range(x, lo, hi);
+    const float r = hi - lo;
+    float best_a = r / 15.0f, best_b = lo;
+    if (r == 0.0f) {
+        scale = best_a;
+        minv = -best_b;
+        return;
+    }
+    float best_e = 0.0f;
+    {
+        const float c = 15.0f / r;
+        for (int l = 0; l < 32; ++l) {
+            int q = (int)roundf((x[l] - lo) * c);
+            q = q < 0 ? 0 : (q > 15 ? 15 : q);
+            const float t = best_a * (float)q + best_b - x[l];
+            best_e = best_e + t * t;
+        }
+    }
+    for (int k = 0; k <= 20; ++k) {
+        const float c = (float)(140 + k) / (10.0f * r);
+        int sq = 0, sqq = 0;
+        float sx = 0.0f, sqx = 0.0f;
+        for (int l = 0; l < 32; ++l) {
+            int v = (int)roundf((x[l] - lo) * c);
+            v = v < 0 ? 0 : (v > 15 ? 15 : v);
+            sq += v;
+            sqq += v * v;
+            sx = sx + x[l];
+            sqx = sqx + (float)v * x[l];
+        }
+        const int dd = 32 * sqq - sq * sq;
+        if (dd == 0) continue;
+        float a = (32.0f * sqx - (float)sq * sx) / (float)dd;
+        float b = (sx - a * (float)sq) / 32.0f;
+        if (b > 0.0f) {
+            b = 0.0f;
+            a = sqx / (float)sqq;
+        }
+        if (!(a > 0.0f)) continue;
+        float e = 0.0f;
+        for (int l = 0; l < 32; ++l) {
+            int v = (int)roundf((x[l] - lo) * c);
+            v = v < 0 ? 0 : (v > 15 ? 15 : v);
+            const float t = a * (float)v + b - x[l];
+            e = e + t * t;
+        }
+        if (e < best_e) {
+            best_e = e;
+            best_a = a;
+            best_b = b;
+        }
+    }
+    scale = best_a;
+    minv = -best_b;
+}
+
+template <bool SEARCH>
 __global__ __launch_bounds__(256) void quantize_q4_k_kernel(const float* __restrict__ w, int N, int K,
                                                             uint8_t* __restrict__ out)
 {
@@ -161,14 +244,14 @@ __global__ __launch_bounds__(256) void quantize_q4_k_kernel(const float* __restr
     float scale[8], minv[8];
     float max_scale = 0.0f, max_min = 0.0f;
     for (int j = 0; j < 8; ++j) {
-        float lo = 0.0f, hi = v[32 * j];
-        for (int l = 0; l < 32; ++l) {
-            const float t = v[32 * j + l];
-            lo = t < lo ? t : lo;
-            hi = t > hi ? t : hi;
+        if constexpr (SEARCH) {
+            q4k_search_fit(v + 32 * j, scale[j], minv[j]);
+        } else {
+            float lo, hi;
+            q4k_sub_range(v + 32 * j, lo, hi);
+            scale[j] = (hi - lo) / 15.0f;
+            minv[j] = -lo;
         }
-        scale[j] = (hi - lo) / 15.0f;
-        minv[j] = -lo;
         max_scale = scale[j] > max_scale ? scale[j] : max_scale;
         max_min = minv[j] > max_min ? minv[j] : max_min;
     }
@@ -226,7 +309,14 @@ hipError_t launch_quantize_act(int act_fmt, const float* x, int64_t M, int64_t K
 hipError_t launch_quantize_weights(int fmt, const float* w, int64_t N, int64_t K, void* out, hipStream_t s)
 {
     if (fmt == FMT_Q8_0) return launch_quantize_act(FMT_Q8_0, w, N, K, out, s);
-    hipLaunchKernelGGL(quantize_q4_k_kernel, dim3(nblocks(N * (K / 256), 256)), dim3(256), 0, s,
+    hipLaunchKernelGGL(quantize_q4_k_kernel<false>, dim3(nblocks(N * (K / 256), 256)), dim3(256), 0, s,
+                       w, (int)N, (int)K, (uint8_t*)out);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_q4_k_search(const float* w, int64_t N, int64_t K, void* out, hipStream_t s)
+{
+    hipLaunchKernelGGL(quantize_q4_k_kernel<true>, dim3(nblocks(N * (K / 256), 256)), dim3(256), 0, s,
                        w, (int)N, (int)K, (uint8_t*)out);
     return hipGetLastError();
 }

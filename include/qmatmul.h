@@ -217,6 +217,19 @@ int qmatmul_quantize_weights(int format, const float* w, int64_t N, int64_t K,
                              void* out_blocks, void* stream);
 
 /*
+ * Q4_K weight quantizer with a search (the page "自己量化", section "3. 量化",
+ * names QTensor::quantize(&w, Q4K) without describing its search): per
+ * 32-value sub-block, candidate codes for 22 scales around the min/max
+ * rule's (that rule's own among them), each refitted by least squares to a
+ * scale and a non-negative min, the smallest squared error kept; then the
+ * super-block's 6-bit scales and mins and the 4-bit values as
+ * qmatmul_quantize_weights(QMM_Q4_K, ...) forms them.  w: device f32 [N x K],
+ * K % 256 == 0; out_blocks: device, N * qmatmul_row_bytes(QMM_Q4_K, K) bytes;
+ * both 16-byte aligned.  One thread per super-block (an offline step).
+ */
+int qmatmul_quantize_q4_k_search(const float* w, int64_t N, int64_t K, void* out_blocks, void* stream);
+
+/*
  * Traced run (mode (b) plans only): qmatmul_run's own kernels, with the same
  * launch configuration, compiled with a flag that also writes out the integer
  * parts the method fixes exactly (page "同一个 GGUF，CPU 和 Metal 生成的文字不一样",

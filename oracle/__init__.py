@@ -42,7 +42,7 @@ def _load():
     lib.orc_f16_to_f64.argtypes = [ctypes.c_uint16]
     lib.orc_f16_to_f64.restype = ctypes.c_double
     for name in ("orc_quantize_q8_0", "orc_quantize_q8k", "orc_quantize_q4_k", "orc_quantize_q4_0",
-                 "orc_quantize_q5_0", "orc_quantize_q6_k"):
+                 "orc_quantize_q5_0", "orc_quantize_q6_k", "orc_quantize_q4_k_search"):
         getattr(lib, name).argtypes = [_p, _i64, _i64, _p]
         getattr(lib, name).restype = None
     for name in ("orc_quantize_q8_0_v", "orc_quantize_q8k_v"):
@@ -116,6 +116,17 @@ def quantize(fmt: int, x, variant: int = 0) -> np.ndarray:
         getattr(lib, name)(_ptr(x), r, k, _ptr(out))
     else:
         raise ValueError(fmt)
+    return out
+
+
+def quantize_q4_k_search(x) -> np.ndarray:
+    """Q4_K blocks of the rows of x with the least-squares search for each
+    sub-block's scale and min (qmm_oracle.c, orc_quantize_q4_k_search)."""
+    x = _f32(x)
+    r, k = x.shape
+    _check_k(Q4_K, k)
+    out = np.zeros((r, row_bytes(Q4_K, k)), dtype=np.uint8)
+    _load().orc_quantize_q4_k_search(_ptr(x), r, k, _ptr(out))
     return out
 
 

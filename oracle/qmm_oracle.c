@@ -224,64 +224,169 @@ static int q4k_nibble(const uint8_t* qs, int e)
  * to 6 bits against the super-block maximum / 63, then the 4-bit values
  * re-quantized against the stored f16 scales.
  */
+/* The super-block stage shared by both Q4_K rules: given each sub-block's
+ * scale and min (>= 0), d = max scale / 63 and dmin = max min / 63 (stored as
+ * f16), 6-bit sc_j and m_j against those maxima, then every value requantized
+ * against the stored effective scale and min. */
+static void q4k_pack(const float* v, const float scale[8], const float minv[8], uint8_t* blk)
+{
+    float max_scale = 0.0f, max_min = 0.0f;
+    for (int j = 0; j < 8; ++j) {
+        if (scale[j] > max_scale) max_scale = scale[j];
+        if (minv[j] > max_min) max_min = minv[j];
+    }
+    int sc[8], mn[8];
+    float isc = max_scale > 0.0f ? 63.0f / max_scale : 0.0f;
+    float imn = max_min > 0.0f ? 63.0f / max_min : 0.0f;
+    for (int j = 0; j < 8; ++j) {
+        int a = (int)roundf(isc * scale[j]);
+        int c = (int)roundf(imn * minv[j]);
+        sc[j] = a > 63 ? 63 : a;
+        mn[j] = c > 63 ? 63 : c;
+    }
+    uint16_t dh = orc_f32_to_f16(max_scale / 63.0f);
+    uint16_t mh = orc_f32_to_f16(max_min / 63.0f);
+    wr16(blk, dh);
+    wr16(blk + 2, mh);
+    uint8_t* s = blk + 4;
+    for (int j = 0; j < 4; ++j) {
+        s[j] = (uint8_t)((sc[j] & 63) | ((sc[j + 4] >> 4) << 6));
+        s[j + 4] = (uint8_t)((mn[j] & 63) | ((mn[j + 4] >> 4) << 6));
+        s[j + 8] = (uint8_t)((sc[j + 4] & 15) | ((mn[j + 4] & 15) << 4));
+    }
+    float dq = (float)orc_f16_to_f64(dh);
+    float mq = (float)orc_f16_to_f64(mh);
+    uint8_t* qs = blk + 16;
+    memset(qs, 0, 128);
+    for (int e = 0; e < QK_K; ++e) {
+        int j = e / 32;
+        float d_eff = dq * (float)sc[j];
+        float m_eff = mq * (float)mn[j];
+        int q = 0;
+        if (d_eff != 0.0f) {
+            q = (int)roundf((v[e] + m_eff) / d_eff);
+            if (q < 0) q = 0;
+            if (q > 15) q = 15;
+        }
+        int c = e / 64, l = e % 64;
+        if (l < 32) qs[32 * c + l] |= (uint8_t)q;
+        else qs[32 * c + (l - 32)] |= (uint8_t)(q << 4);
+    }
+}
+
+/* lo = min(0, min x), hi = max x over a 32-value sub-block */
+static void sub_range(const float* x, float* lo, float* hi)
+{
+    *lo = 0.0f;
+    *hi = x[0];
+    for (int l = 0; l < 32; ++l) {
+        if (x[l] < *lo) *lo = x[l];
+        if (x[l] > *hi) *hi = x[l];
+    }
+}
+
 void orc_quantize_q4_k(const float* w, int64_t rows, int64_t K, uint8_t* out)
 {
     const int64_t nb = K / QK_K;
     for (int64_t r = 0; r < rows; ++r) {
         for (int64_t b = 0; b < nb; ++b) {
             const float* v = w + r * K + b * QK_K;
-            uint8_t* blk = out + (r * nb + b) * Q4_K_BYTES;
             float scale[8], minv[8];
-            float max_scale = 0.0f, max_min = 0.0f;
             for (int j = 0; j < 8; ++j) {
-                float lo = 0.0f, hi = v[32 * j];
-                for (int l = 0; l < 32; ++l) {
-                    float t = v[32 * j + l];
-                    if (t < lo) lo = t;
-                    if (t > hi) hi = t;
-                }
+                float lo, hi;
+                sub_range(v + 32 * j, &lo, &hi);
                 scale[j] = (hi - lo) / 15.0f;
                 minv[j] = -lo;
-                if (scale[j] > max_scale) max_scale = scale[j];
-                if (minv[j] > max_min) max_min = minv[j];
             }
-            int sc[8], mn[8];
-            float isc = max_scale > 0.0f ? 63.0f / max_scale : 0.0f;
-            float imn = max_min > 0.0f ? 63.0f / max_min : 0.0f;
-            for (int j = 0; j < 8; ++j) {
-                int a = (int)roundf(isc * scale[j]);
-                int c = (int)roundf(imn * minv[j]);
-                sc[j] = a > 63 ? 63 : a;
-                mn[j] = c > 63 ? 63 : c;
-            }
-            uint16_t dh = orc_f32_to_f16(max_scale / 63.0f);
-            uint16_t mh = orc_f32_to_f16(max_min / 63.0f);
-            wr16(blk, dh);
-            wr16(blk + 2, mh);
-            uint8_t* s = blk + 4;
-            for (int j = 0; j < 4; ++j) {
-                s[j] = (uint8_t)((sc[j] & 63) | ((sc[j + 4] >> 4) << 6));
-                s[j + 4] = (uint8_t)((mn[j] & 63) | ((mn[j + 4] >> 4) << 6));
-                s[j + 8] = (uint8_t)((sc[j + 4] & 15) | ((mn[j + 4] & 15) << 4));
-            }
-            float dq = (float)orc_f16_to_f64(dh);
-            float mq = (float)orc_f16_to_f64(mh);
-            uint8_t* qs = blk + 16;
-            memset(qs, 0, 128);
-            for (int e = 0; e < QK_K; ++e) {
-                int j = e / 32;
-                float d_eff = dq * (float)sc[j];
-                float m_eff = mq * (float)mn[j];
-                int q = 0;
-                if (d_eff != 0.0f) {
-                    q = (int)roundf((v[e] + m_eff) / d_eff);
-                    if (q < 0) q = 0;
-                    if (q > 15) q = 15;
-                }
-                int c = e / 64, l = e % 64;
-                if (l < 32) qs[32 * c + l] |= (uint8_t)q;
-                else qs[32 * c + (l - 32)] |= (uint8_t)(q << 4);
-            }
+            q4k_pack(v, scale, minv, out + (r * nb + b) * Q4_K_BYTES);
+        }
+    }
+}
+
+/*
+ * Q4_K weights with a search for each sub-block's scale and min (the page
+ * "自己量化", section "3. 量化", names QTensor::quantize(&w, Q4K) but not its
+ * search; this is a plain least-squares search written from the definition
+ * of the format).  For a sub-block x[0..31] with lo = min(0, min x), hi =
+ * max x, r = hi - lo:
+ *   candidate codes q_l = clamp(round((x_l - lo) * c), 0, 15) for the plain
+ *   rule's c = 15 / r and for c = (140 + k) / (10 r), k = 0..20 (steps of
+ *   0.1 around 15 codes per range);
+ *   for each, the least-squares line x ~ a q + b over the 32 values (b forced
+ *   to 0 by refitting a alone when the fit gives b > 0: the format's offset
+ *   is -dmin*m <= 0), a candidate with a <= 0 or all codes equal skipped;
+ *   kept: the first candidate of smallest squared error sum (a q + b - x)^2,
+ *   the plain rule's (a = r/15, b = lo) competing first.
+ * Then scale = a, min = -b, and the super-block stage of the plain rule.
+ * All sums run in index order in f32, one IEEE operation at a time.
+ */
+static void q4k_search_fit(const float* x, float* scale, float* minv)
+{
+    float lo, hi;
+    sub_range(x, &lo, &hi);
+    const float r = hi - lo;
+    float best_a = r / 15.0f, best_b = lo;
+    if (r == 0.0f) {
+        *scale = best_a;
+        *minv = -best_b;
+        return;
+    }
+    float best_e = 0.0f;
+    {
+        const float c = 15.0f / r;
+        for (int l = 0; l < 32; ++l) {
+            int q = (int)roundf((x[l] - lo) * c);
+            q = q < 0 ? 0 : q > 15 ? 15 : q;
+            const float t = best_a * (float)q + best_b - x[l];
+            best_e = best_e + t * t;
+        }
+    }
+    for (int k = 0; k <= 20; ++k) {
+        const float c = (float)(140 + k) / (10.0f * r);
+        int q[32], sq = 0, sqq = 0;
+        float sx = 0.0f, sqx = 0.0f;
+        for (int l = 0; l < 32; ++l) {
+            int v = (int)roundf((x[l] - lo) * c);
+            v = v < 0 ? 0 : v > 15 ? 15 : v;
+            q[l] = v;
+            sq += v;
+            sqq += v * v;
+            sx = sx + x[l];
+            sqx = sqx + (float)v * x[l];
+        }
+        const int dd = 32 * sqq - sq * sq;
+        if (dd == 0) continue;
+        float a = (32.0f * sqx - (float)sq * sx) / (float)dd;
+        float b = (sx - a * (float)sq) / 32.0f;
+        if (b > 0.0f) {
+            b = 0.0f;
+            a = sqx / (float)sqq;
+        }
+        if (!(a > 0.0f)) continue;
+        float e = 0.0f;
+        for (int l = 0; l < 32; ++l) {
+            const float t = a * (float)q[l] + b - x[l];
+            e = e + t * t;
+        }
+        if (e < best_e) {
+            best_e = e;
+            best_a = a;
+            best_b = b;
+        }
+    }
+    *scale = best_a;
+    *minv = -best_b;
+}
+
+void orc_quantize_q4_k_search(const float* w, int64_t rows, int64_t K, uint8_t* out)
+{
+    const int64_t nb = K / QK_K;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const float* v = w + r * K + b * QK_K;
+            float scale[8], minv[8];
+            for (int j = 0; j < 8; ++j) q4k_search_fit(v + 32 * j, &scale[j], &minv[j]);
+            q4k_pack(v, scale, minv, out + (r * nb + b) * Q4_K_BYTES);
         }
     }
 }

@@ -99,6 +99,16 @@ def test_quantize_weights_bit_exact(fmt, n, k):
     assert np.array_equal(got, oracle.quantize(fmt, w))
 
 
+@pytest.mark.parametrize("n,k", [(96, 1536), (33, 4096), (7, 256)])
+def test_quantize_q4_k_search_bit_exact(n, k):
+    w = synth.weights_f32(935 + n, n, k)
+    w[0, :256] = 0.0
+    w[0, 7:256:32], w[0, 20:256:32] = 0.5, 1.0  # the hand-worked block (the search moves it)
+    w[1, :32] = np.linspace(-0.75, 3.0, 32, dtype=np.float32)
+    got = host(qmm.quantize_q4_k_search(dev(w)))
+    assert np.array_equal(got, oracle.quantize_q4_k_search(w))
+
+
 def test_activation_quantization_is_row_local_on_gpu():
     x = synth.acts_f32(940, 37, 1536)
     full = host(qmm.quantize_act(qmm.Q8_K, dev(x)))

@@ -235,6 +235,55 @@ def test_q4_k_quantizer_round_trip_bound():
     assert worst < 0.25 * synth.W_SIGMA
 
 
+# ------------------------------------------------ Q4_K with the search --
+# The search tries code assignments for 22 scales around the min/max rule's
+# and keeps the least-squares line of smallest squared error (the min/max
+# rule's own fit competing first), then packs like the min/max rule.
+
+def test_q4_k_search_hand_worked_block():
+    # Every sub-block: 30 zeros, 0.5 and 1.0.  The min/max rule spans [0, 1]
+    # with 15 steps (scale 1/15): 0.5 falls at 7.5 steps, so one of the two
+    # nonzero values is off by half a step.  The codes 7 and 14 lie on the
+    # line x = q/14 exactly (the candidate c = 14/r, k = 0): the search takes
+    # it (scale 1/14, min about 0).  Packing: d = f16((1/14)/63), whose bits
+    # are 0x14A5 (1/882 = 2^-10 * 1.1610..., mantissa 165); dmin = 0 (the min
+    # is far below the f16 range); sc_j = m_j = 63; requantized against
+    # d_eff = f16(d) * 63 = 0.0714369: 0.5 -> 7, 1.0 -> 14.  The min/max rule
+    # instead stores d = f16((1/15)/63) = 0x1456 and codes 7 and 15.
+    x = np.zeros((1, 256), np.float32)
+    for j in range(8):
+        x[0, 32 * j + 7], x[0, 32 * j + 20] = 0.5, 1.0
+    for fn, dbits, codes in ((oracle.quantize_q4_k_search, 0x14A5, (7, 14)),
+                             (lambda v: oracle.quantize(Q4_K, v), 0x1456, (7, 15))):
+        blk = fn(x)[0]
+        assert (int(blk[0]) | int(blk[1]) << 8) == dbits and blk[2] == 0 and blk[3] == 0
+        deq, qv, sc_m, d, dmin = py_q4k_decode(blk)
+        assert [sm[0] for sm in sc_m] == [63] * 8
+        for j in range(8):
+            assert (qv[32 * j + 7], qv[32 * j + 20]) == codes
+            assert not any(qv[32 * j + l] for l in range(32) if l not in (7, 20))
+
+
+def test_q4_k_search_round_trip_bound_and_gain():
+    # the packing stage is the min/max rule's, so its bound holds; the search
+    # lowers the error on N(0, 0.02) weights
+    w = synth.weights_f32(33, 64, 1536)
+    blk = oracle.quantize_q4_k_search(w).reshape(64, 6, 144)
+    sq_search = 0.0
+    for r in range(64):
+        for b in range(6):
+            deq, qv, sc_m, d, dmin = py_q4k_decode(blk[r, b])
+            x = w[r, 256 * b:256 * (b + 1)].astype(np.float64)
+            qv = np.array(qv)
+            d_eff = np.array([d * sc_m[e // 32][0] for e in range(256)])
+            inside = (qv > 0) & (qv < 15)
+            assert np.all(np.abs(x - deq)[inside] <= 0.5 * d_eff[inside] * (1 + 1e-5))
+            sq_search += float(((x - deq) ** 2).sum())
+    plain = oracle.dequantize(Q4_K, oracle.quantize(Q4_K, w), 1536).astype(np.float64)
+    sq_plain = float(((plain - w) ** 2).sum())
+    assert sq_search < 0.9 * sq_plain
+
+
 # ------------------------------------------------------------------- Q8K --
 
 def test_q8_k_handbuilt_quantization():
