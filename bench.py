@@ -64,28 +64,48 @@ def parse():
     return p.parse_args()
 
 
-def kernel_source_hash():
+CSRC = os.path.join(ROOT, "block_quantized_matmul_gguf_amd", "csrc")
+
+
+def kernel_sources(main):
+    """The source file `main` (under csrc/) and every csrc header it includes, directly or not."""
+    seen, todo = set(), [main]
+    while todo:
+        name = todo.pop()
+        if name in seen or not os.path.isfile(os.path.join(CSRC, name)):
+            continue
+        seen.add(name)
+        with open(os.path.join(CSRC, name)) as f:
+            for line in f:
+                line = line.strip()
+                if line.startswith("#include \""):
+                    todo.append(line.split("\"")[1])
+    return sorted(seen)
+
+
+def kernel_source_hash(main):
+    """Hash of the sources that build the kernels of `main` (its text and its headers')."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "block_quantized_matmul_gguf_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
+    for name in kernel_sources(main):
+        with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
 
 def traffic_from_profile(key):
     """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel sources; else None."""
+    on the current sources of that kernel (each entry names its source file and
+    the hash of it and its headers); else None."""
     path = os.path.join(ROOT, "profiles", "counters.json")
     try:
         with open(path) as f:
             data = json.load(f)
     except (OSError, ValueError):
         return None
-    if data.get("source_hash") != kernel_source_hash():
-        return None
     entry = data.get("kernels", {}).get(key)
-    return None if entry is None else entry.get("hbm_bytes_per_launch")
+    if not entry or not entry.get("source") or entry.get("source_hash") != kernel_source_hash(entry["source"]):
+        return None
+    return entry.get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(layers, min_seconds=10.0, threads=None):
@@ -663,7 +683,9 @@ def main():
         # mode (a) runs on the f16 matrix cores (hi/lo split), mode (b) on the int8 ones
         int8 = r["mode"] == "b"
         return {
-            "kernel": f"{'gemm_q_kernel' if int8 else 'gemm_kernel'} {r['fmt']} mode {r['mode']} M={r['M']}",
+            # one run = the activation preparation launch + the prefill kernel, timed together
+            "kernel": (f"{'quantize_' + ('q8_0' if r['fmt'] == 'q8_0' else 'q8k') + '_kernel + gemm_q_kernel' if int8 else 'gemm_prep_kernel + gemm_kernel'}"
+                       f" {r['fmt']} mode {r['mode']} M={r['M']} (one run)"),
             "bound": "mfma", "achieved": r["TOPS"], "peak": PEAK_I8_TOPS if int8 else PEAK_F16_TFLOPS,
             "unit": "TOP/s" if int8 else "TFLOP/s",
             "frac": r["frac_int8_peak"] if int8 else r["frac_f16_peak"],
