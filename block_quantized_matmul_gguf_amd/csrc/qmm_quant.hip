@@ -9,36 +9,49 @@ namespace qmm {
 
 enum { LAY_AOS = 0, LAY_I8 = 3, LAY_F16 = 4 };
 
-// One thread per 32-value block.  LAY_AOS: canonical 34-byte blocks.
-// LAY_I8: the values as int8 [M][K] plus f32 scales block-major [K/32][M]
-// (and, for a traced run, the canonical blocks in `act` as well).
+// Lanes sub = 0..7 of a group of eight hold values 4*sub .. 4*sub+3 of a
+// 34-byte block; lane 0 also holds d.
+QMM_DEV void store_q8_0_part(uint8_t* o, int sub, uint16_t dbits, const int q[4])
+{
+    uint16_t* h = reinterpret_cast<uint16_t*>(o);  // blocks are 2-byte aligned
+    if (sub == 0) h[0] = dbits;
+    h[1 + 2 * sub] = (uint16_t)((uint8_t)q[0] | ((uint16_t)(uint8_t)q[1] << 8));
+    h[2 + 2 * sub] = (uint16_t)((uint8_t)q[2] | ((uint16_t)(uint8_t)q[3] << 8));
+}
+
+// Eight lanes per 32-value block, four values per lane, so that a wave reads
+// (and writes) eight consecutive blocks of a row contiguously.  The block's
+// max|x| is reduced over its eight lanes (a maximum: the same in any order)
+// and the scale and values come from q8_0_scale / q8_0_q, as in every Q8_0
+// quantizer.  LAY_AOS: canonical 34-byte blocks.  LAY_I8: the values as int8
+// [M][K] plus f32 scales block-major [K/32][M] (and, for a traced run, the
+// canonical blocks in `act` as well).
 template <int LAY>
 __global__ __launch_bounds__(256) void quantize_q8_0_kernel(const float* __restrict__ x, int M, int K,
                                                             uint8_t* __restrict__ out, float* __restrict__ sc,
                                                             uint8_t* __restrict__ act)
 {
     const int nb = K / 32;
-    const int64_t blk = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (blk >= (int64_t)M * nb) return;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t blk = t >> 3;
+    const int sub = (int)(t & 7);
+    if (blk >= (int64_t)M * nb) return;  // a block's eight lanes leave together
     const int m = (int)(blk / nb), b = (int)(blk % nb);
-    float a[32];
-    load32(x + (int64_t)m * K + 32 * b, a);
+    const float4 v = *reinterpret_cast<const float4*>(x + (int64_t)m * K + 32 * b + 4 * sub);
+    float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    amax = fmaxf(amax, __shfl_xor(amax, 4));
+    float id, dval;
     uint16_t dbits;
-    float dval;
-    int8_t q[32];
-    q8_0_block(a, dbits, dval, q);
+    q8_0_scale(amax, id, dbits, dval);
+    const int q[4] = {q8_0_q(v.x, id), q8_0_q(v.y, id), q8_0_q(v.z, id), q8_0_q(v.w, id)};
     if (LAY == LAY_AOS) {
-        store_q8_0_block(out + blk * 34, dbits, q);
+        store_q8_0_part(out + blk * 34, sub, dbits, q);
     } else if (LAY == LAY_I8) {
-        if (act) store_q8_0_block(act + blk * 34, dbits, q);
-        uint4* o = reinterpret_cast<uint4*>(out + (int64_t)m * K + 32 * b);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-            o[i] = make_uint4(pack4(q[16 * i], q[16 * i + 1], q[16 * i + 2], q[16 * i + 3]),
-                              pack4(q[16 * i + 4], q[16 * i + 5], q[16 * i + 6], q[16 * i + 7]),
-                              pack4(q[16 * i + 8], q[16 * i + 9], q[16 * i + 10], q[16 * i + 11]),
-                              pack4(q[16 * i + 12], q[16 * i + 13], q[16 * i + 14], q[16 * i + 15]));
-        sc[(int64_t)b * M + m] = dval;
+        if (act) store_q8_0_part(act + blk * 34, sub, dbits, q);
+        *reinterpret_cast<uint32_t*>(out + (int64_t)m * K + 32 * b + 4 * sub) = pack4(q[0], q[1], q[2], q[3]);
+        if (sub == 0) sc[(int64_t)b * M + m] = dval;
     }
 }
 
@@ -89,24 +102,26 @@ __global__ __launch_bounds__(256) void quantize_q8k_kernel(const float* __restri
 // by the power of two s that puts its largest magnitude in [2^14, 2^15) and
 // split into f16 hi + lo; rs = 1/s.  Q4_K also gets the sums of x*s over every
 // 32 values, divided by 32 so that they stay below 2^15, split the same way
-// and laid out [M][K/256][8 hi, 8 lo].
+// and laid out [M][K/256][8 hi, 8 lo].  Thread t takes the row's float4 chunks
+// t, t + 256, ..., so every wave load reads (and every store writes) one
+// contiguous run; a 32-value sum is formed by the eight threads holding it.
 template <int FMT>
 __global__ __launch_bounds__(256) void gemm_prep_kernel(const float* __restrict__ x, int M, int K,
                                                         _Float16* __restrict__ hi, _Float16* __restrict__ lo,
                                                         float* __restrict__ rs, _Float16* __restrict__ xs)
 {
+#pragma clang fp contract(off)
     __shared__ float red[4];
     const int m = blockIdx.x;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const float* v = x + (int64_t)m * K;
-    const int n32 = K / 32, nsb = K / 256;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const float4* v = reinterpret_cast<const float4*>(x + (int64_t)m * K);
+    const int nc = K / 4;  // a multiple of 8: whole 32-value groups
 
     float am = 0.0f;
-    for (int u = threadIdx.x; u < n32; u += 256) {
-        float e[32];
-        load32(v + 32 * u, e);
-#pragma unroll
-        for (int j = 0; j < 32; ++j) am = fmaxf(am, fabsf(e[j]));
+#pragma unroll 4
+    for (int c = tid; c < nc; c += 256) {
+        const float4 e = v[c];
+        am = fmaxf(am, fmaxf(fmaxf(fabsf(e.x), fabsf(e.y)), fmaxf(fabsf(e.z), fabsf(e.w))));
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
@@ -115,30 +130,41 @@ __global__ __launch_bounds__(256) void gemm_prep_kernel(const float* __restrict_
     am = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     const int sexp = split_exp(am);
     const float s = ldexpf(1.0f, sexp);
-    if (threadIdx.x == 0) rs[m] = ldexpf(1.0f, -sexp);
+    if (tid == 0) rs[m] = ldexpf(1.0f, -sexp);
 
     _Float16* oh = hi + (int64_t)m * K;
     _Float16* ol = lo + (int64_t)m * K;
-    _Float16* ox = FMT == FMT_Q4_K ? xs + (int64_t)m * nsb * 16 : nullptr;
-    for (int u = threadIdx.x; u < n32; u += 256) {
-        float e[32];
-        _Float16 h[32], l[32];
-        load32(v + 32 * u, e);
-        const float sum = split_chunk(e, s, h, l);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            half8_t vh, vl;
-#pragma unroll
-            for (int t = 0; t < 8; ++t) { vh[t] = h[8 * i + t]; vl[t] = l[8 * i + t]; }
-            reinterpret_cast<half8_t*>(oh + 32 * u)[i] = vh;
-            reinterpret_cast<half8_t*>(ol + 32 * u)[i] = vl;
+    _Float16* ox = FMT == FMT_Q4_K ? xs + (int64_t)m * (K / 256) * 16 : nullptr;
+    const int steps = (nc + 255) / 256;
+    for (int i = 0; i < steps; ++i) {  // every thread takes each step (the sums below)
+        const int c = tid + 256 * i;
+        const bool ok = c < nc;  // the same for the eight threads of a 32-value group
+        const float4 e = ok ? v[c] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        float t[4];
+        _Float16 h[4], l[4];
+        split_one(e.x, s, h[0], l[0], t[0]);
+        split_one(e.y, s, h[1], l[1], t[1]);
+        split_one(e.z, s, h[2], l[2], t[2]);
+        split_one(e.w, s, h[3], l[3], t[3]);
+        if (ok) {
+            reinterpret_cast<u32x2_t*>(oh)[c] = u32x2_t{__builtin_bit_cast(uint32_t, half2_t{h[0], h[1]}),
+                                                        __builtin_bit_cast(uint32_t, half2_t{h[2], h[3]})};
+            reinterpret_cast<u32x2_t*>(ol)[c] = u32x2_t{__builtin_bit_cast(uint32_t, half2_t{l[0], l[1]}),
+                                                        __builtin_bit_cast(uint32_t, half2_t{l[2], l[3]})};
         }
-        if (FMT == FMT_Q4_K) {
-            _Float16 sh, sl;
-            float t;
-            split_one(sum, 0.03125f, sh, sl, t);
-            ox[16 * (u >> 3) + (u & 7)] = sh;
-            ox[16 * (u >> 3) + 8 + (u & 7)] = sl;
+        if constexpr (FMT == FMT_Q4_K) {
+            float sum = ((t[0] + t[1]) + t[2]) + t[3];
+            sum += __shfl_xor(sum, 1);
+            sum += __shfl_xor(sum, 2);
+            sum += __shfl_xor(sum, 4);
+            if (ok && (lane & 7) == 0) {
+                const int u = c >> 3;  // 32-value group of the row
+                _Float16 sh, sl;
+                float tt;
+                split_one(sum, 0.03125f, sh, sl, tt);
+                ox[16 * (u >> 3) + (u & 7)] = sh;
+                ox[16 * (u >> 3) + 8 + (u & 7)] = sl;
+            }
         }
     }
 }
@@ -297,7 +323,7 @@ static unsigned nblocks(int64_t items, int per) { return (unsigned)((items + per
 hipError_t launch_quantize_act(int act_fmt, const float* x, int64_t M, int64_t K, void* out, hipStream_t s)
 {
     if (act_fmt == FMT_Q8_0) {
-        hipLaunchKernelGGL(quantize_q8_0_kernel<LAY_AOS>, dim3(nblocks(M * (K / 32), 256)), dim3(256), 0, s,
+        hipLaunchKernelGGL(quantize_q8_0_kernel<LAY_AOS>, dim3(nblocks(M * (K / 32) * 8, 256)), dim3(256), 0, s,
                            x, (int)M, (int)K, (uint8_t*)out, (float*)nullptr, (uint8_t*)nullptr);
     } else {
         hipLaunchKernelGGL(quantize_q8k_kernel<LAY_AOS>, dim3(nblocks(M * (K / 256), 4)), dim3(256), 0, s,
@@ -393,7 +419,7 @@ hipError_t launch_gemm_prep(int fmt, int mode, const float* x, int64_t M, int64_
     }
     if (mode == MODE_B) {  // int8 values, block scales (and Q8K sub-block sums) for the int8 kernel
         if (fmt == FMT_Q8_0)
-            hipLaunchKernelGGL(quantize_q8_0_kernel<LAY_I8>, dim3(nblocks(M * (K / 32), 256)), dim3(256), 0, s,
+            hipLaunchKernelGGL(quantize_q8_0_kernel<LAY_I8>, dim3(nblocks(M * (K / 32) * 8, 256)), dim3(256), 0, s,
                                x, (int)M, (int)K, (uint8_t*)b.a0, b.sd, act);
         else
             hipLaunchKernelGGL(quantize_q8k_kernel<LAY_I8>, dim3(nblocks(M * (K / 256), 4)), dim3(256), 0, s,
