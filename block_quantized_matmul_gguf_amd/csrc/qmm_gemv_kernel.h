@@ -264,8 +264,28 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
     constexpr int NTPT = MODE == MODE_A ? 8 : 4;  // tasks per thread at most (64 values)
     const int nb32 = lu_cnt * (VPL / 32);         // 32-value blocks in this split
     const int ntasks = MODE == MODE_A ? M * nb32 * 4 : (FMT == FMT_Q8_0 ? M * nb32 * 2 : M * lu_cnt * 16);
-    const int npw = min(GV_WAVES, (ntasks + 63) / 64);  // waves with tasks (the first npw)
+    // mode (a) with eight rows: wave w takes row w whole (tasks lane, lane + 64, ...),
+    // so each row's maximum is a reduction inside one wave; otherwise task t =
+    // tid + 512 c, the waves sharing rows and the maxima meeting in LDS
+    const int per_row = ntasks / M;
+    const bool wrow = MODE == MODE_A && M == GV_WAVES && per_row <= 64 * NTPT;
+    const int npw = wrow ? GV_WAVES : min(GV_WAVES, (ntasks + 63) / 64);  // waves with tasks (the first npw)
     const bool xw = wave < npw;
+    // task c of this thread: its row m, its index r in the row, and whether it exists
+    auto task = [&](int c, int& m, int& r, bool& live) {
+        if (wrow) {
+            m = wave;
+            r = lane + 64 * c;
+            live = r < per_row;
+        } else {
+            const int t = tid + GV_THREADS * c;
+            live = t < ntasks;
+            m = t / per_row;
+            r = t - m * per_row;
+        }
+    };
+    // whether this wave has a task c at all (uniform per wave)
+    auto has_task = [&](int c) { return wrow ? 64 * c < per_row : 64 * wave + GV_THREADS * c < ntasks; };
     int* s_sync = reinterpret_cast<int*>(s_misc) + 24;  // row maxima in, operand ready
     const rsrc_t xr = make_rsrc(a.x, (uint32_t)(M * K * 4));
     const int k0 = lu_beg * VPL;
@@ -273,11 +293,10 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
     if (xw) {
 #pragma unroll
         for (int c = 0; c < NTPT; ++c) {
-            if (64 * wave + GV_THREADS * c >= ntasks) break;  // uniform per wave
-            const int t = tid + GV_THREADS * c;
-            const bool live = t < ntasks;
-            const int per_row = ntasks / M;
-            const int m = t / per_row, r = t - m * per_row;
+            if (!has_task(c)) break;
+            int m, r;
+            bool live;
+            task(c, m, r, live);
             uint32_t o[4];  // float offsets of the slot's values: 4 + 4 + 4 + 4, or 4 + 2 + 2 (mode a)
             if constexpr (MODE == MODE_A) {
                 const int b = r >> 2, kg = r & 3;
@@ -322,7 +341,7 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
                     const bool wrap = r2 == 1;
                     const u32x2_t lo = __builtin_amdgcn_raw_buffer_load_b64(xr, wrap ? o[3] + 8 : o[3], 0, 0);
                     const u32x2_t hi2 = __builtin_amdgcn_raw_buffer_load_b64(
-                        xr, wrap ? (live ? (uint32_t)((t / per_row) * K + k0 + 32 * (r >> 1)) * 4 : 0x80000000u)
+                        xr, wrap ? (live ? (uint32_t)(m * K + k0 + 32 * (r >> 1)) * 4 : 0x80000000u)
                                  : o[3] + 8, 0, 0);
                     xv[c][12] = __uint_as_float(lo[0]); xv[c][13] = __uint_as_float(lo[1]);
                     xv[c][14] = __uint_as_float(hi2[0]); xv[c][15] = __uint_as_float(hi2[1]);
@@ -357,11 +376,21 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
     } else {
         prime();
     }
+    float wmax = 0.0f;  // wave-per-row form: this wave's row maximum
     if constexpr (MODE == MODE_A) {
         // power-of-two scale per row over this split, then the hi/lo f16 split; a wave
         // whose tasks share a row reduces its maximum first (one LDS atomic per wave)
-        if (xw) {
-            const int per_row = ntasks / M;
+        if (xw && wrow) {
+            // (tasks past the row are zeros: they leave the maximum unchanged)
+#pragma unroll
+            for (int c = 0; c < NTPT; ++c) {
+                if (!has_task(c)) break;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) wmax = fmaxf(wmax, fabsf(xv[c][i]));
+            }
+            wmax = wave_max(wmax);
+            if (lane == 0) s_misc[16 + wave] = wmax;  // for the outputs' 2^-e
+        } else if (xw) {
 #pragma unroll
             for (int c = 0; c < NTPT; ++c) {
                 if (64 * wave + GV_THREADS * c >= ntasks) break;
@@ -384,14 +413,14 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
     if (xw) {
 #pragma unroll
         for (int c = 0; c < NTPT; ++c) {
-            if (64 * wave + GV_THREADS * c >= ntasks) break;
-            const int t = tid + GV_THREADS * c;
-            const bool live = t < ntasks;
-            const int per_row = ntasks / M;
-            const int m = t / per_row, r = t - m * per_row;
+            if (!has_task(c)) break;
+            int m, r;
+            bool live;
+            task(c, m, r, live);
             if constexpr (MODE == MODE_A) {
                 const int b = r >> 2, kg = r & 3;
-                const float sc = ldexpf(1.0f, split_exp(__uint_as_float(reinterpret_cast<const unsigned*>(s_misc)[16 + (live ? m : 0)])));
+                const float rmax = wrow ? wmax : __uint_as_float(reinterpret_cast<const unsigned*>(s_misc)[16 + (live ? m : 0)]);
+                const float sc = ldexpf(1.0f, split_exp(rmax));
                 half8_t vh, vl;
                 float sum = 0.0f;
 #pragma unroll
