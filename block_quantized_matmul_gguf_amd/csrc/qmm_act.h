@@ -38,8 +38,7 @@ QMM_DEV void q8_0_block(const float a[32], uint16_t& dbits, float& dval, int8_t 
 }
 
 // Q8K: the signed element of largest |x| picks the scale, the first index
-// winning ties; q8k_better says whether candidate (ob, oi) beats (best, bi).
-QMM_DEV bool q8k_better(float ob, int oi, float best, int bi) { return ob > best || (ob == best && oi < bi); }
+// winning ties (the sign of the scale depends on which of +-max comes first).
 // From that element mx (and its |mx| = best): iscale = -127/mx, d = 1/iscale;
 // an all-zero block gives iscale = d = 0.
 QMM_DEV void q8k_scale(float mx, float best, float& iscale, float& d)
@@ -52,6 +51,27 @@ QMM_DEV void q8k_scale(float mx, float best, float& iscale, float& d)
         d = 1.0f / iscale;
     }
 }
+// The signed element of largest |x| of a 256-value block held by 16
+// consecutive lanes in index order (each lane's elements precede the next
+// lane's), each lane passing `best`, the largest |x| of its elements, and
+// `bv`, the first of them with that magnitude.  The block's max |x| is
+// reduced over the 16 lanes; the lowest lane whose `best` reaches it holds the
+// first element with it (first index on ties).  Every lane of the 16 gets
+// that element, and the max |x| in `amax`.
+QMM_DEV float q8k_row16_max(float best, float bv, float& amax)
+{
+    float am = best;
+    am = fmaxf(am, dpp_f<DPP_X1>(am));
+    am = fmaxf(am, dpp_f<DPP_X2>(am));
+    am = fmaxf(am, dpp_f<DPP_HMIRROR>(am));
+    am = fmaxf(am, dpp_f<DPP_MIRROR>(am));
+    const int lane = (int)__lane_id();
+    const uint64_t hit = __ballot(best == am);
+    const uint32_t row = (uint32_t)(hit >> (lane & 48)) & 0xffffu;  // never 0: some lane holds the max
+    amax = am;
+    return __shfl(bv, (lane & 48) + __builtin_ctz(row));
+}
+
 // q = min(127, round-half-away(iscale * x)).
 QMM_DEV int q8k_q(float x, float iscale)
 {
@@ -76,22 +96,20 @@ QMM_DEV void load32(const float* __restrict__ v, float a[32])
 // 4i..4i+3 hold bsums[i] in s16.
 QMM_DEV void q8k_wave(const float xs[4], int lane, float& d, int q[4], int& s16)
 {
-    float best = -1.0f;
-    int bi = 0;
+    // the lane's largest |x| and the first of its elements with it
+    float best = -1.0f, bv = 0.0f;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const float a = fabsf(xs[u]);
-        if (a > best) { best = a; bi = 4 * lane + u; }
+        if (a > best) { best = a; bv = xs[u]; }
     }
+    // the block's max |x|; the lowest lane reaching it holds the first index
+    float am = best;
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float ob = __shfl_xor(best, off);
-        const int oi = __shfl_xor(bi, off);
-        if (q8k_better(ob, oi, best, bi)) { best = ob; bi = oi; }
-    }
-    const int sel = bi & 3;
-    const float mine = sel == 0 ? xs[0] : sel == 1 ? xs[1] : sel == 2 ? xs[2] : xs[3];
-    const float mx = __shfl(mine, bi >> 2);
+    for (int off = 1; off < 64; off <<= 1) am = fmaxf(am, __shfl_xor(am, off));
+    const int owner = __builtin_ctzll(__ballot(best == am));  // the same in every lane
+    const float mx = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bv), owner));
+    best = am;
     float iscale;
     q8k_scale(mx, best, iscale, d);
 #pragma unroll

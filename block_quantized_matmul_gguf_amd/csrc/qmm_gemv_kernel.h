@@ -477,22 +477,15 @@ __global__ __launch_bounds__(GV_THREADS, 4) void gemv_kernel(GemvArgs a)
                 }
             } else {
                 const int sb = r >> 4, sl16 = r & 15;
-                // the super-block's signed element of largest |x|, first index on ties
+                // the super-block's signed element of largest |x|, first index on ties:
+                // this lane's first element of largest |x|, then over the 16 lanes
                 float best = -1.0f, bv = 0.0f;
-                int bi = 0;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const float av = fabsf(xv[c][i]);
-                    if (av > best) { best = av; bv = xv[c][i]; bi = 16 * sl16 + i; }
+                    if (av > best) { best = av; bv = xv[c][i]; }
                 }
-                // over the 16 lanes of the super-block (the order of the combine does not matter)
-                auto pick = [&](float ob, float ov, int oi) {
-                    if (q8k_better(ob, oi, best, bi)) { best = ob; bv = ov; bi = oi; }
-                };
-                pick(dpp_f<DPP_X1>(best), dpp_f<DPP_X1>(bv), dpp_i<DPP_X1>(bi));
-                pick(dpp_f<DPP_X2>(best), dpp_f<DPP_X2>(bv), dpp_i<DPP_X2>(bi));
-                pick(dpp_f<DPP_HMIRROR>(best), dpp_f<DPP_HMIRROR>(bv), dpp_i<DPP_HMIRROR>(bi));
-                pick(dpp_f<DPP_MIRROR>(best), dpp_f<DPP_MIRROR>(bv), dpp_i<DPP_MIRROR>(bi));
+                bv = q8k_row16_max(best, bv, best);
                 float iscale, d;
                 q8k_scale(bv, best, iscale, d);
                 int q[16], s16 = 0;

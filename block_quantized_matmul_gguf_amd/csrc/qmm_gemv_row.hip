@@ -253,19 +253,12 @@ __global__ __launch_bounds__(GR_THREADS) void gemv_row_kernel(GemvRowArgs a)
                 v[4 * c] = q4[0]; v[4 * c + 1] = q4[1]; v[4 * c + 2] = q4[2]; v[4 * c + 3] = q4[3];
             }
             float best = -1.0f, bv = 0.0f;
-            int bi = 0;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const float av = fabsf(v[i]);
-                if (av > best) { best = av; bv = v[i]; bi = 16 * part + i; }
+                if (av > best) { best = av; bv = v[i]; }
             }
-            auto pick = [&](float ob, float ov, int oi) {
-                if (q8k_better(ob, oi, best, bi)) { best = ob; bv = ov; bi = oi; }
-            };
-            pick(dpp_f<DPP_X1>(best), dpp_f<DPP_X1>(bv), dpp_i<DPP_X1>(bi));
-            pick(dpp_f<DPP_X2>(best), dpp_f<DPP_X2>(bv), dpp_i<DPP_X2>(bi));
-            pick(dpp_f<DPP_HMIRROR>(best), dpp_f<DPP_HMIRROR>(bv), dpp_i<DPP_HMIRROR>(bi));
-            pick(dpp_f<DPP_MIRROR>(best), dpp_f<DPP_MIRROR>(bv), dpp_i<DPP_MIRROR>(bi));
+            bv = q8k_row16_max(best, bv, best);
             float iscale, d;
             q8k_scale(bv, best, iscale, d);
             int q[16], s16 = 0;
