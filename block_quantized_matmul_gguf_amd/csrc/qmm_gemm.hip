@@ -18,12 +18,16 @@
 // y = acc / s.
 //
 // Q6_K (210 bytes per 256 values: w = d * sc * (q - 32), sc an int8 per 16
-// values).  sc * (q - 32) reaches 4096 and is not exact in f16, so each
-// 16-value scale is split as sc = 16 * sc_hi + sc_lo (sc_hi = sc >> 4, sc_lo =
-// sc & 15) and the weights enter as two exact f16 operands, 16 * sc_hi *
-// (q - 32) (multiples of 16, at most 4096) and sc_lo * (q - 32) (at most 480
-// in magnitude): their products with x sum to x * sc * (q - 32) exactly.  Both
-// go into the same accumulator over a super-block; then acc += d * C.
+// values).  Mode (a): the weights enter as the exact f16 values q - 32 and the
+// scale is applied per 16 values: v_mfma_f32_32x32x16_f16 takes one 16-value
+// sub-block (K = 16) of a 32 x 32 tile, two of them (hi, lo) give its sum C,
+// and acc += (d * sc) * C in f32 (d * sc is exact in f32).  Mode (b) keeps the
+// scales in the operand, where sc * (q - 32) reaches 4096 and is not exact in
+// f16: each 16-value scale is split as sc = 16 * sc_hi + sc_lo (sc_hi = sc >>
+// 4, sc_lo = sc & 15) and the weights enter as two exact f16 operands, 16 *
+// sc_hi * (q - 32) (multiples of 16, at most 4096) and sc_lo * (q - 32) (at
+// most 480 in magnitude): their products with x sum to x * sc * (q - 32)
+// exactly.
 // Mode (b) (page "同一个 GGUF，CPU 和 Metal 生成的文字不一样", section 出处:
 // the activations quantized to Q8K, integer dots, then the scales): the
 // activation operand is the int8 values themselves (exact in f16), one pass;
@@ -74,7 +78,10 @@ struct GemmCfg {
     static constexpr int NT = 64 * WM * WN;
     static constexpr int BM = 16 * TM * WM, BN = 16 * TN * WN;
     static constexpr int NA = MODE == MODE_A ? 2 : 1;          // activation operands: hi, lo / the values
-    static constexpr int NB = FMT == FMT_Q6_K ? 2 : 1;         // weight operands (Q6_K: the split scale)
+    // Q6_K mode (a) runs on 32 x 32 x 16 MFMAs (K = one 16-value sub-block):
+    // one weight operand (q - 32) and the sub-block scale d * sc in f32
+    static constexpr bool Q6A = FMT == FMT_Q6_K && MODE == MODE_A;
+    static constexpr int NB = FMT == FMT_Q6_K && MODE == MODE_B ? 2 : 1;  // weight operands (Q6_K (b): the split scale)
     static constexpr int A_HALF = BM * G_ROW;  // one activation operand of one stage, bytes
     static constexpr int A_BYTES = NA * A_HALF;
     static constexpr int B_PART = BN * G_ROW;  // one weight operand of one stage
@@ -84,19 +91,23 @@ struct GemmCfg {
     // Q8_0: block scales [2 stages][2 blocks][BN] f32.
     // Q4_K, by super-block parity: {d, dmin, -, -} [2][BN] (16 B each), 32*m_j
     // [2][BN][8] f16, activation sub-block sums [2][BM][16] f16.
-    // Q6_K, by super-block parity: {d, -, -, -} [2][BN]; mode (b) also d_x [2][BM] f32.
+    // Q6_K mode (b), by super-block parity: {d, -, -, -} [2][BN], d_x [2][BM] f32.
+    // Q6_K mode (a): d * sc of the stage's four sub-blocks [2 stages][BN][4] f32.
     static constexpr int OFF_DD = OFF_S;
     static constexpr int OFF_MJ = OFF_DD + 2 * BN * 16;
     static constexpr int OFF_X = OFF_MJ + 2 * BN * 16;
-    static constexpr int OFF_DXB = OFF_DD + 2 * BN * 16;  // Q6_K
+    static constexpr int OFF_DXB = OFF_DD + 2 * BN * 16;  // Q6_K mode (b)
+    static constexpr int OFF_SC = OFF_S;                  // Q6_K mode (a)
     static constexpr int BYTES = FMT == FMT_Q8_0 ? OFF_S + 2 * 2 * BN * 4
                                : FMT == FMT_Q4_K ? OFF_X + 2 * BM * 32
-                                                 : OFF_DXB + (MODE == MODE_B ? 2 * BM * 4 : 0);
+                               : MODE == MODE_A  ? OFF_SC + 2 * BN * 16
+                                                 : OFF_DXB + 2 * BM * 4;
     static constexpr int AU = 8 * NA * BM / NT;        // 16-byte activation chunks per thread per stage
     static constexpr int BU = (2 * BN + NT - 1) / NT;  // weight units (row, half) per thread per stage
     static constexpr int XU = (2 * BM + NT - 1) / NT;  // Q4_K sub-block-sum chunks per thread
     static_assert((8 * BM) % NT == 0, "activation chunks must split evenly between the operands");
     static_assert(MODE == MODE_A || FMT == FMT_Q6_K, "mode (b) of Q8_0 and Q4_K runs on the int8 kernel");
+    static_assert(!Q6A || (TM % 2 == 0 && TN % 2 == 0), "32 x 32 tiles");
 };
 
 template <int FMT, int MODE, int WM, int WN, int TM, int TN, bool EMIT>
@@ -303,9 +314,21 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_kernel(GemmArg
                     v[1] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, c0, 0x07030602u)) + bias;
                     v[2] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, c1, 0x05010400u)) + bias;
                     v[3] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, c1, 0x07030602u)) + bias;
-                    // their scale, byte 2 half + e/2 of the stage's four, split as 16 sc_hi + sc_lo
+                    // their scale, byte 2 half + e/2 of the stage's four
                     const uint32_t scw = __builtin_amdgcn_alignbyte(rsc[SET][i][1], rsc[SET][i][0], sh);
                     const int sc = (int)(int8_t)(scw >> (8 * (2 * bsh[i] + (e >> 1))));
+                    if constexpr (!MB) {
+                        // mode (a): the values q - 32 as they are, and d * sc (exact in f32) once per sub-block
+                        *reinterpret_cast<uint4*>(bbase + bst[i][e]) =
+                            make_uint4(__builtin_bit_cast(uint32_t, v[0]), __builtin_bit_cast(uint32_t, v[1]),
+                                       __builtin_bit_cast(uint32_t, v[2]), __builtin_bit_cast(uint32_t, v[3]));
+                        if ((e & 1) == 0) {
+                            const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)(rdd[SET][i] >> (8 * sh)));
+                            reinterpret_cast<float*>(lds + C::OFF_SC)[(P * BN + brow[i]) * 4 + 2 * bsh[i] + (e >> 1)] = d * (float)sc;
+                        }
+                        return;
+                    }
+                    // mode (b): split as 16 sc_hi + sc_lo
                     const _Float16 fh = (_Float16)(float)(16 * (sc >> 4)), fl = (_Float16)(float)(sc & 15);
                     const half2_t sh2 = {fh, fh}, sl2 = {fl, fl};
                     uint32_t p0[4], p1[4];
@@ -316,7 +339,7 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_kernel(GemmArg
                     }
                     *reinterpret_cast<uint4*>(bbase + bst[i][e]) = make_uint4(p0[0], p0[1], p0[2], p0[3]);
                     *reinterpret_cast<uint4*>(bbase + C::B_PART + bst[i][e]) = make_uint4(p1[0], p1[1], p1[2], p1[3]);
-                } else if (CS == 0 && bsh[i] == 0) {  // d of the row's super-block (bytes 208, 209)
+                } else if (MB && CS == 0 && bsh[i] == 0) {  // mode (b): d of the row's super-block (bytes 208, 209)
                     const int sp = (st >> 2) & 1;
                     const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)(rdd[SET][i] >> (8 * sh)));
                     reinterpret_cast<float*>(lds + C::OFF_DD)[(sp * BN + brow[i]) * 4] = d;
@@ -375,12 +398,23 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_kernel(GemmArg
 
     // csb: the super-block's sums before its scales (Q4_K, Q6_K); Q6_K mode
     // (b) keeps the second weight operand's sums apart in csb2 (both exact)
-    f32x4_t acc[TM][TN], csb[Q8 ? 1 : TM][Q8 ? 1 : TN], csb2[Q6 && MB ? TM : 1][Q6 && MB ? TN : 1];
+    // acc32: Q6_K mode (a), TM/2 x TN/2 tiles of 32 x 32 outputs
+    constexpr bool Q6A = C::Q6A;
+    constexpr int TM2 = Q6A ? TM / 2 : 1, TN2 = Q6A ? TN / 2 : 1;
+    f32x4_t acc[Q6A ? 1 : TM][Q6A ? 1 : TN], csb[Q8 || Q6A ? 1 : TM][Q8 || Q6A ? 1 : TN],
+        csb2[Q6 && MB ? TM : 1][Q6 && MB ? TN : 1];
+    f32x16_t acc32[TM2][TN2];
     const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    const f32x16_t zero16 = {};
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < (Q6A ? 1 : TM); ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = zero;
+        for (int j = 0; j < (Q6A ? 1 : TN); ++j) acc[i][j] = zero;
+#pragma unroll
+    for (int i = 0; i < TM2; ++i)
+#pragma unroll
+        for (int j = 0; j < TN2; ++j) acc32[i][j] = zero16;
+    const int l32 = lane & 31, hl = lane >> 5;  // 32 x 32 operands: row l32, k-half hl
 
     // ---- one stage: MFMAs out of buffer P, interleaved with staging stage st+1
     // (register set SET ^ 1) into buffer P ^ 1 when STORE ----
@@ -395,6 +429,43 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_kernel(GemmArg
         if (LOAD) load(st + 2, IP{}, ICS2{});
         const uint8_t* sa = lds + P * C::A_BYTES;
         const uint8_t* sbb = lds + C::OFF_B + P * C::B_BYTES;
+        if constexpr (Q6A) {
+            // four 16-value sub-blocks per stage: per 32 x 32 tile two MFMAs (hi, lo)
+            // on the exact f16 values q - 32, then acc += (d * sc) * C in f32
+            const float* scs = reinterpret_cast<const float*>(lds + C::OFF_SC) + P * BN * 4;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                half8_t ah[TM2], al[TM2];
+#pragma unroll
+                for (int i = 0; i < TM2; ++i) {
+                    const uint32_t o = swz(wm + 32 * i + l32, 2 * u + hl);
+                    ah[i] = *reinterpret_cast<const half8_t*>(sa + o);
+                    al[i] = *reinterpret_cast<const half8_t*>(sa + C::A_HALF + o);
+                }
+#pragma unroll
+                for (int j = 0; j < TN2; ++j) {
+                    const int nl = wn + 32 * j + l32;
+                    const half8_t bw = *reinterpret_cast<const half8_t*>(sbb + swz(nl, 2 * u + hl));
+                    const float sc = scs[nl * 4 + u];
+#pragma unroll
+                    for (int i = 0; i < TM2; ++i) {
+                        f32x16_t c = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[i], bw, zero16, 0, 0, 0);
+                        c = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[i], bw, c, 0, 0, 0);
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) acc32[i][j][r] = __builtin_fmaf(sc, c[r], acc32[i][j][r]);
+                    }
+                    if (STORE) {
+                        constexpr int R = 4 * TN2;
+                        const int rg = u * TN2 + j;
+#pragma unroll
+                        for (int w = 0; w < NI; ++w)
+                            if ((w * R) / NI == rg) item(w, st + 1, IQ{}, IQ{}, ICS1{});
+                    }
+                }
+            }
+            __syncthreads();
+            return;
+        }
         f32x4_t cvp[TM];
         float dwp = 0.0f;
 #pragma unroll
@@ -579,6 +650,22 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_kernel(GemmArg
         iter(st + 3, I1{}, I3{}, F_{}, F_{});
     }
 
+    if constexpr (Q6A) {  // 32 x 32 tiles: lane l holds rows 8 (r / 4) + 4 (l / 32) + r % 4 of column l % 32
+#pragma unroll
+        for (int i = 0; i < TM2; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * hl + (r & 3);
+                if (m >= M) continue;
+                const float rsv = a.rs[m];
+#pragma unroll
+                for (int j = 0; j < TN2; ++j) {
+                    const int n = n0 + wn + 32 * j + l32;
+                    if (n < N) Y[(int64_t)m * N + n] = acc32[i][j][r] * rsv;
+                }
+            }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         float rsv[4];
@@ -646,13 +733,14 @@ static const GemmTile kTiles[] = {{4, 2, 2, 7}, {4, 2, 2, 4}, {2, 2, 2, 4}, {2, 
 // traffic per output (activation pairs over BN, weight bytes over BM).  Q6_K
 // leaves out the widest tile (its three accumulators per output would not fit
 // the registers).
-static GemmTile pick_tile(int64_t M, int64_t N, int fmt)
+static GemmTile pick_tile(int64_t M, int64_t N, int fmt, int mode)
 {
     const int64_t cus = cu_count();
     GemmTile best = kTiles[fmt == FMT_Q6_K ? 1 : 0];
     double bc = -1.0;
     for (const GemmTile& t : kTiles) {
         if (fmt == FMT_Q6_K && t.tn == 7) continue;
+        if (fmt == FMT_Q6_K && mode == MODE_A && t.tm == 1) continue;  // 32 x 32 tiles
         const int64_t bm = 16 * t.tm * t.wm, bn = 16 * t.tn * t.wn;
         const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
         const double cost = (double)((tiles + cus - 1) / cus) * (double)(bm * bn) * (1.0 + 16.0 / bm + 64.0 / bn);
@@ -691,7 +779,8 @@ static hipError_t launch_fmt(const GemmArgs& a, GemmTile t, hipStream_t s)
     if (t.wm == 4 && t.tn == 4) return launch_tile<FMT, MODE, EMIT, 4, 2, 2, 4>(a, s);
     if (t.tm == 2 && t.tn == 4) return launch_tile<FMT, MODE, EMIT, 2, 2, 2, 4>(a, s);
     if (t.tm == 2) return launch_tile<FMT, MODE, EMIT, 2, 2, 2, 2>(a, s);
-    return launch_tile<FMT, MODE, EMIT, 2, 2, 1, 2>(a, s);
+    if constexpr (FMT == FMT_Q6_K && MODE == MODE_A) return hipErrorInvalidValue;  // 32 x 32 tiles only
+    else return launch_tile<FMT, MODE, EMIT, 2, 2, 1, 2>(a, s);
 }
 
 // count problems sharing K, the mode and the prepared activations b (one
@@ -720,7 +809,7 @@ hipError_t launch_gemm_group(int fmt, int mode, int count, const void* const* w,
     a.xs = b.xs;
     a.dx = b.sd;
     a.sums = sums;
-    const GemmTile t = pick_tile(M, ntot, fmt);
+    const GemmTile t = pick_tile(M, ntot, fmt, mode);
     hipError_t e;
     if (fmt == FMT_Q8_0) e = launch_fmt<FMT_Q8_0, MODE_A, false>(a, t, s);
     else if (fmt == FMT_Q4_K) e = launch_fmt<FMT_Q4_K, MODE_A, false>(a, t, s);
