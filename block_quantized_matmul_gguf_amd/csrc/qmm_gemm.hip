@@ -725,8 +725,11 @@ struct GemmTile {
 // Tile shapes, largest first: 128 x 224 fills 256 compute units exactly on
 // 512 x 14336; the smaller ones keep short or narrow problems spread out
 // (32 x 64 runs the 576-wide projections at M = 307 in 11 us against 18 us
-// with 64 x 128).
-static const GemmTile kTiles[] = {{4, 2, 2, 7}, {4, 2, 2, 4}, {2, 2, 2, 4}, {2, 2, 2, 2}, {2, 2, 1, 2}};
+// with 64 x 128).  128 x 256 (waves 2 x 4, 64 x 64 each) serves the Q6_K mode
+// (a) path, whose 32 x 32 tiles need even tile counts: one tile per compute
+// unit on 512 x 14336 and one weight unit per thread (208 us against 288 us
+// with 128 x 128).
+static const GemmTile kTiles[] = {{4, 2, 2, 7}, {4, 2, 2, 4}, {2, 4, 4, 4}, {2, 2, 2, 4}, {2, 2, 2, 2}, {2, 2, 1, 2}};
 
 // The tile whose busiest compute unit does the least work: rounds of tiles
 // over the compute units times the tile's area, weighted by its operand
@@ -741,6 +744,7 @@ static GemmTile pick_tile(int64_t M, int64_t N, int fmt, int mode)
     for (const GemmTile& t : kTiles) {
         if (fmt == FMT_Q6_K && t.tn == 7) continue;
         if (fmt == FMT_Q6_K && mode == MODE_A && t.tm == 1) continue;  // 32 x 32 tiles
+        if (t.wn == 4 && !(fmt == FMT_Q6_K && mode == MODE_A)) continue;  // the 32 x 32 path's wide tile
         const int64_t bm = 16 * t.tm * t.wm, bn = 16 * t.tn * t.wn;
         const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
         const double cost = (double)((tiles + cus - 1) / cus) * (double)(bm * bn) * (1.0 + 16.0 / bm + 64.0 / bn);
@@ -776,6 +780,8 @@ static hipError_t launch_fmt(const GemmArgs& a, GemmTile t, hipStream_t s)
 {
     if constexpr (FMT != FMT_Q6_K)
         if (t.wm == 4 && t.tn == 7) return launch_tile<FMT, MODE, EMIT, 4, 2, 2, 7>(a, s);
+    if constexpr (FMT == FMT_Q6_K && MODE == MODE_A)
+        if (t.wn == 4) return launch_tile<FMT, MODE, EMIT, 2, 4, 4, 4>(a, s);
     if (t.wm == 4 && t.tn == 4) return launch_tile<FMT, MODE, EMIT, 4, 2, 2, 4>(a, s);
     if (t.tm == 2 && t.tn == 4) return launch_tile<FMT, MODE, EMIT, 2, 2, 2, 4>(a, s);
     if (t.tm == 2) return launch_tile<FMT, MODE, EMIT, 2, 2, 2, 2>(a, s);
