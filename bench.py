@@ -458,8 +458,8 @@ def formats_workload(args, qmm, torch, synth, stream):
     Q5_0 and Q6_K, quantized by the library, rotated per launch (264, 323 and
     385 MB: HBM-resident), both modes, M = 1 and 8 (decode) and 512 (prefill:
     Q4_0/Q5_0 rewrite the weights as Q8_0 blocks and take the Q8_0 kernels,
-    Q6_K takes the decode kernels eight rows at a time).  Per-launch times
-    from HIP events on the launch stream."""
+    Q6_K runs on the f16 prefill kernel).  Per-launch times from HIP events on
+    the launch stream.  --only fmt:mode:M (e.g. q6_k:a:512) keeps one row."""
     dev = torch.device("cuda:0")
     fmts = {"q4_0": qmm.Q4_0, "q5_0": qmm.Q5_0, "q6_k": qmm.Q6_K}
     modes = {"a": qmm.MODE_F32ACT, "b": qmm.MODE_QACT}
@@ -468,7 +468,14 @@ def formats_workload(args, qmm, torch, synth, stream):
     xs = {m: x[:m].contiguous() for m in DECODE_M + (M_PREFILL,)}
     ys = {m: torch.empty((m, N), dtype=torch.float32, device=dev) for m in DECODE_M + (M_PREFILL,)}
     rows = []
+    only = args.only.split(":") if args.only else []
+
+    def wanted(*key):
+        return all(str(v) == p for v, p in zip(key, only))
+
     for f, code in fmts.items():
+        if not wanted(f):
+            continue
         wq = []
         for layer in range(LAYERS):
             wf = torch.from_numpy(synth.weights_f32(5000 + layer, N, K)).to(dev)
@@ -476,8 +483,12 @@ def formats_workload(args, qmm, torch, synth, stream):
             del wf
         b = wq[0].numel()
         for md, mcode in modes.items():
+            if not wanted(f, md):
+                continue
             with qmm.Plan(code, N, K, M_PREFILL, mcode) as plan:
                 for m in DECODE_M + (M_PREFILL,):
+                    if not wanted(f, md, m):
+                        continue
                     reps = args.steps if m <= 8 else max(2, args.steps // 4)
                     for _ in range(max(1, args.warmup)):
                         for l in range(LAYERS):
