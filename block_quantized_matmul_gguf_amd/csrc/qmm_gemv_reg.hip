@@ -1,0 +1,379 @@
+// qmm_gemv_reg.hip -- decode with two to eight f32 activation rows (mode (a))
+// for Q8_0 and Q4_K weights, the activation operand held in registers.
+//
+// The pages' decode step streams every weight once per token (page "同一个
+// GGUF，CPU 和 Metal 生成的文字不一样", section 修法: the CPU decode is bound by
+// the weight bytes), so the weights must keep HBM busy from the start.  The
+// tile kernel (qmm_gemv_kernel.h) builds the activation operand of the whole
+// K range in LDS (f16 hi and lo of eight rows: 128 KB at K = 4096), which
+// leaves room for only two shallow weight stages per wave.  Here K is split
+// eight ways instead, one slice per wave of a 512-thread workgroup, and each
+// wave keeps its slice's operand in registers (64 VGPRs at K = 4096):
+//   * a workgroup owns a run of 16-row tiles; for each tile every wave
+//     streams its K slice of the 16 rows through a ring of D stage buffers in
+//     LDS filled by 16-byte buffer-to-LDS loads (D stages in flight, the whole
+//     LDS but the tile partials available to the ring);
+//   * the activation values of the slice are loaded first, their row maxima
+//     taken (the power-of-two scale 2^e of a row is per wave and slice: each
+//     wave scales its partial sums back by 2^-e, exactly), then the ring is
+//     primed and the values are split into f16 hi and lo while it fills;
+//   * v_mfma_f32_16x16x32_f16 with A rows 0..7 = hi and 8..15 = lo of the
+//     eight activation rows and the weights as exact f16 integers, the same
+//     weight decode and block-scale epilogue as the tile kernel;
+//   * at the end of a tile the eight slices' partial sums meet in LDS behind
+//     one barrier and are added in slice order (deterministic).
+// Operand lanes n and n + 8 of a 16-lane row need the same eight x values
+// (hi for rows 0..7, lo for rows 8..15): each loads four, splits them, and the
+// pair trades the half the other needs with one DPP row rotation.
+#include <mutex>
+#include <set>
+#include <type_traits>
+#include <utility>
+
+#include "qmm_gemv_kernel.h"
+#include "qmm_internal.h"
+
+namespace qmm {
+
+struct GemvRegArgs {
+    const uint8_t* w;
+    int64_t w_bytes;  // N * row_bytes
+    int row_bytes;
+    int N, K, M;
+    int nlu;    // load units per row (Q8_0 block pairs, Q4_K super-blocks)
+    int tiles;  // 16-row tiles
+    int T;      // tiles per workgroup
+    const float* x;
+    float* y;
+};
+
+constexpr int GR_PART_BYTES = 2 * GV_WAVES * 128 * 4;  // tile partials, two slots: [slot][wave][8 rows][16]
+
+// U: load units per wave slice (K <= 8 U units), P: units per stage, D: ring depth.
+template <int FMT, int U, int P, int D>
+struct GrCfg {
+    static constexpr int LUB = FMT == FMT_Q8_0 ? 68 : 144;
+    static constexpr int STEPS = FMT == FMT_Q8_0 ? 2 : 8;  // matrix-core steps (32 values) per unit
+    static constexpr int CPR = gv_cpr(FMT, P);              // 16-byte chunks per row and stage
+    static constexpr int SBY = 16 * 16 * CPR;               // one stage buffer (16 rows, unpadded)
+    static constexpr int TL = (16 * CPR + 63) / 64;         // load instructions per stage
+    static constexpr int SUMS = FMT == FMT_Q4_K ? U * 8 * 8 * 4 : 0;  // per wave: x*2^e sums [U*8 sub-blocks][8 rows]
+    static constexpr int OFF_PART = GV_WAVES * D * SBY;
+    static constexpr int OFF_SUMS = OFF_PART + GR_PART_BYTES;
+    static constexpr int LDS = OFF_SUMS + GV_WAVES * SUMS;
+    static_assert(U % P == 0 && gv_ring_ok(FMT, P) && D >= 2 && (D - 1) * TL <= 63, "ring of LDS-direct stages");
+    static_assert(LDS <= GV_LDS_MAX, "LDS of a compute unit");
+};
+
+// DPP row_ror:8 -- lane n of a 16-lane row receives lane (n + 8) % 16.
+QMM_DEV uint32_t ror8(uint32_t v) { return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x128, 0xF, 0xF, false); }
+QMM_DEV uint32_t pack_h2(_Float16 a, _Float16 b) { return __builtin_bit_cast(uint32_t, half2_t{a, b}); }
+
+template <int FMT, int U, int P, int D>
+__global__ __launch_bounds__(GV_THREADS, 2) void gemv_reg_kernel(GemvRegArgs a)
+{
+    using C = GrCfg<FMT, U, P, D>;
+    constexpr int LUB = C::LUB, STEPS = C::STEPS, CPR = C::CPR, SBY = C::SBY, TL = C::TL;
+    constexpr int S = U / P;  // stages per tile
+    static_assert(S == 1 || S == 2, "one or two stages per tile");
+    constexpr int VPL = FMT == FMT_Q8_0 ? 64 : 256;
+    extern __shared__ __align__(16) uint8_t lds[];
+
+    const int M = a.M, N = a.N, K = a.K;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 15, g = lane >> 4;
+    const int r8 = n & 7;         // the activation row of this lane's operand values
+    const bool upper = n >= 8;    // operand rows 8..15 (lo); loads values 4..7 of its k-group
+    const int t0 = blockIdx.x * a.T;
+    const int nt = min(a.T, a.tiles - t0);  // tiles of this workgroup, >= 1
+    const int u0 = wave * U;                // first unit of this wave's slice
+    const int ureal = max(0, min(U, a.nlu - u0));
+    const int sreal = (ureal + P - 1) / P;  // stages of a tile holding real units
+    const int Q = nt * S;                   // stages per wave
+    uint8_t* ring = lds + wave * (D * SBY);
+    float* part = reinterpret_cast<float*>(lds + C::OFF_PART);
+    float* sums = reinterpret_cast<float*>(lds + C::OFF_SUMS + wave * C::SUMS);
+
+    // ---- the weight stream: chunk f = 64t + lane of a stage is row f/CPR, chunk f%CPR ----
+    uint32_t go[TL];
+#pragma unroll
+    for (int t = 0; t < TL; ++t) {
+        const int f = 64 * t + lane, r = f / CPR, c = f - r * CPR;
+        go[t] = f < 16 * CPR ? (uint32_t)(r * a.row_bytes + 16 * c) : 0x80000000u;
+    }
+    constexpr int TAIL = 16 * CPR - 64 * (TL - 1);  // live lanes of the last load
+    int iq = 0;  // next stage to issue
+    // stage iq into ring buffer `slot`: the tile's rows as a buffer (rows past N, and
+    // stages without real units, read as zero); lanes past the last chunk stay off
+    auto issue = [&](int slot) {
+        const int tile = t0 + iq / S, s = iq % S;
+        const bool real = s < sreal;
+        const int64_t tb = (int64_t)tile * 16 * a.row_bytes;
+        const int64_t left = a.w_bytes - tb;
+        const uint32_t nrec = real && left > 0 ? (uint32_t)min(left, (int64_t)16 * a.row_bytes) : 0u;
+        const rsrc_t wr = make_rsrc(a.w + (real ? tb : 0), nrec);
+        const uint32_t so = (uint32_t)((u0 + s * P) * LUB);
+        uint8_t* buf = ring + slot * SBY;
+#pragma unroll
+        for (int t = 0; t < TL; ++t)
+            if (t < TL - 1 || lane < TAIL) ld128_lds(wr, buf + 1024 * t, go[t] + so);
+        ++iq;
+    };
+
+    // ---- the activation values of this wave's slice, four per lane and step ----
+    // Q8_0 even block: k-group g holds the block's values 2+8g .. 9+8g (group 3:
+    // 26..31, 0, 1), the order in which the weights' bytes follow their scale;
+    // odd block and Q4_K: 8g .. 8g+7.  Lanes n < 8 take the first four, n >= 8 the
+    // last four.  Units past the slice's real ones and rows past M read as zero.
+    issue(0);  // the first stage flies while the activations load
+    const rsrc_t xr = make_rsrc(a.x, clamp_u32((int64_t)M * K * 4));
+    float xv[U * STEPS][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const bool live = u < ureal;
+#pragma unroll
+        for (int p = 0; p < STEPS; ++p) {
+            const int base = r8 * K + (u0 + u) * VPL + 32 * p;
+            float* v = xv[u * STEPS + p];
+            if (FMT == FMT_Q8_0 && p == 0) {
+                const int oa = upper ? (g < 3 ? 6 + 8 * g : 30) : (g < 3 ? 2 + 8 * g : 26);
+                const int ob = upper ? (g < 3 ? 8 + 8 * g : 0) : oa + 2;
+                const u32x2_t va = __builtin_amdgcn_raw_buffer_load_b64(xr, live ? (uint32_t)(base + oa) * 4 : 0x80000000u, 0, 0);
+                const u32x2_t vb = __builtin_amdgcn_raw_buffer_load_b64(xr, live ? (uint32_t)(base + ob) * 4 : 0x80000000u, 0, 0);
+                v[0] = __uint_as_float(va[0]); v[1] = __uint_as_float(va[1]);
+                v[2] = __uint_as_float(vb[0]); v[3] = __uint_as_float(vb[1]);
+            } else {
+                const float4 t = ldx16(xr, live ? (uint32_t)(base + 8 * g + (upper ? 4 : 0)) * 4 : 0x80000000u);
+                v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+            }
+        }
+    }
+    // the row maximum over the slice: lanes n, n + 8 of every 16-lane row hold row n % 8
+    float mx = 0.0f;
+#pragma unroll
+    for (int i = 0; i < U * STEPS; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fabsf(xv[i][e]));
+    mx = fmaxf(mx, __uint_as_float(ror8(__float_as_uint(mx))));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const int ex = split_exp(mx);
+    const float sc = ldexpf(1.0f, ex);
+    // (every activation load has been waited for above; the ring loads below are
+    // not tracked by the compiler and must not be moved ahead of that wait)
+    __builtin_amdgcn_sched_barrier(0);
+
+    // the rest of the ring, then the split while it fills
+#pragma unroll
+    for (int i = 1; i < D; ++i)
+        if (iq < Q) issue(i);
+
+    half8_t areg[U][STEPS];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int p = 0; p < STEPS; ++p) {
+            const float* v = xv[u * STEPS + p];
+            _Float16 h[4], l[4];
+            float xs[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) split_one(v[e], sc, h[e], l[e], xs[e]);
+            // operand slots of the four values: Q8_0 in order; Q4_K slot e holds element
+            // nib_perm(e) of the k-group (the order the nibble decoder yields)
+            uint32_t h0, h1, l0, l1;
+            if constexpr (FMT == FMT_Q8_0) {
+                h0 = pack_h2(h[0], h[1]); h1 = pack_h2(h[2], h[3]);
+                l0 = pack_h2(l[0], l[1]); l1 = pack_h2(l[2], l[3]);
+            } else {
+                h0 = pack_h2(h[0], h[2]); h1 = pack_h2(h[1], h[3]);
+                l0 = pack_h2(l[0], l[2]); l1 = pack_h2(l[1], l[3]);
+            }
+            // lanes n < 8 keep hi and receive the partner's hi; lanes n >= 8 keep lo
+            const uint32_t s0 = ror8(upper ? h0 : l0), s1 = ror8(upper ? h1 : l1);
+            const u32x4_t op = upper ? u32x4_t{s0, s1, l0, l1} : u32x4_t{h0, h1, s0, s1};
+            areg[u][p] = __builtin_bit_cast(half8_t, op);
+            if constexpr (FMT == FMT_Q4_K) {
+                // the sub-block's sum of x*2^e (for the mins term): 32 values over the
+                // lanes n, n + 8 of the four k-groups
+                float t = ((xs[0] + xs[1]) + xs[2]) + xs[3];
+                t += __uint_as_float(ror8(__float_as_uint(t)));
+                t += __shfl_xor(t, 16);
+                t += __shfl_xor(t, 32);
+                if (lane < 8) sums[(u * 8 + p) * 8 + lane] = t;
+            }
+        }
+    }
+    // 2^-e of this lane's four output rows 4 (g & 1) + q (row r's exponent sits in lane r)
+    float rsc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int e0 = __builtin_amdgcn_readlane(ex, q), e1 = __builtin_amdgcn_readlane(ex, 4 + q);
+        rsc[q] = ldexpf(1.0f, -((g & 1) ? e1 : e0));
+    }
+
+    // ---- main loop ----
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    const f32x4_t zf = {0.0f, 0.0f, 0.0f, 0.0f};
+    const uint32_t sel3 = g == 3 ? 0x07060100u : 0x03020100u;  // Q8_0 even block, k-group 3: q0, q1
+    uint32_t nibm = 0x000f000fu, nibc = 0x64006400u;           // Q4_K nibble decode constants
+    asm volatile("" : "+v"(nibm), "+v"(nibc));
+    const bool lo_lane = g >= 2;  // output rows 8..15: the lo parts (no mins term there)
+
+    auto compute = [&](const uint8_t* sbuf, auto sc_) {
+        constexpr int s = decltype(sc_)::value;
+        const uint8_t* rrow = sbuf + n * (16 * CPR);
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            const int u = s * P + j;
+            if (u >= ureal) break;  // wave-uniform: units past the slice are not the row's
+            const uint8_t* rp = rrow + j * LUB;
+            if constexpr (FMT == FMT_Q8_0) {
+                const uint32_t E0 = lds32(rp), E8 = lds32(rp + 32);
+                const uint8_t* xe = rp + 4 + 8 * g;
+                const uint8_t* xo = rp + 36 + 8 * g;
+                const half8_t Be = i8x8_to_f16(lds32(xe), __builtin_amdgcn_perm(E0, lds32(xe + 4), sel3));
+                const half8_t Bo = i8x8_to_f16(lds32(xo), lds32(xo + 4));
+                const f32x4_t Ce = __builtin_amdgcn_mfma_f32_16x16x32_f16(areg[s * P + j][0], Be, zf, 0, 0, 0);
+                const f32x4_t Co = __builtin_amdgcn_mfma_f32_16x16x32_f16(areg[s * P + j][1], Bo, zf, 0, 0, 0);
+                const float de = f16lo(E0), dd = f16hi(E8);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[q] = fmaf(Co[q], dd, fmaf(Ce[q], de, acc[q]));
+            } else {
+                const u32x4_t H = lds128(rp);
+                const float d = f16lo(H[0]), dmin = f16hi(H[0]);
+                const uint32_t s0 = H[1], s1 = H[2], s2 = H[3];
+                const uint32_t sc4[2] = {s0 & 0x3f3f3f3fu, (s2 & 0x0f0f0f0fu) | ((s0 >> 2) & 0x30303030u)};
+                const uint32_t mn4[2] = {s1 & 0x3f3f3f3fu, ((s2 >> 4) & 0x0f0f0f0fu) | ((s1 >> 2) & 0x30303030u)};
+                const float* xsp = sums + (s * P + j) * 64 + 4 * (g & 1);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const u32x2_t Qv = lds64(rp + 16 + 32 * c + 8 * g);
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int jj = 2 * c + h;
+                        const half8_t B = nib8_to_f16(Qv[0], Qv[1], 4 * h, nibm, nibc);
+                        const f32x4_t Cv = __builtin_amdgcn_mfma_f32_16x16x32_f16(areg[s * P + j][jj], B, zf, 0, 0, 0);
+                        const float dsc = d * (float)((sc4[jj >> 2] >> (8 * (jj & 3))) & 0xffu);
+                        const float dmm = lo_lane ? 0.0f : dmin * (float)((mn4[jj >> 2] >> (8 * (jj & 3))) & 0xffu);
+                        const f32x4_t xs = *reinterpret_cast<const f32x4_t*>(xsp + jj * 8);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) acc[q] = fmaf(-dmm, xs[q], fmaf(Cv[q], dsc, acc[q]));
+                    }
+                }
+            }
+        }
+    };
+
+    int slot = 0;
+    for (int tt = 0; tt < nt; ++tt) {
+        auto stage = [&](auto sc_) {
+            constexpr int s = decltype(sc_)::value;
+            const int q = tt * S + s;
+            vm_wait_ahead<TL, D - 1>(min(D - 1, Q - 1 - q));  // stage q has landed
+            if (s < sreal) compute(ring + slot * SBY, sc_);
+            if (iq < Q) {
+                lgkm_wait0();  // this buffer's reads are done before it is refilled
+                issue(slot);
+            }
+            slot = slot == D - 1 ? 0 : slot + 1;
+        };
+        stage(std::integral_constant<int, 0>{});
+        if constexpr (S > 1) stage(std::integral_constant<int, 1>{});
+
+        // the tile's partial of this slice: hi + lo (lanes g and g + 2), scaled back by
+        // 2^-e, parked in LDS; after one barrier the slices are added in order
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q] += __shfl_xor(acc[q], 32);
+        float* ps = part + ((tt & 1) * GV_WAVES + wave) * 128;
+        if (lane < 32) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) ps[(4 * (g & 1) + q) * 16 + n] = acc[q] * rsc[q];
+        }
+        acc = zf;
+        lgkm_wait0();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (tid < 128) {
+            const int m = tid >> 4, ng = (t0 + tt) * 16 + (tid & 15);
+            const float* pp = part + (tt & 1) * GV_WAVES * 128 + tid;
+            float v = 0.0f;
+#pragma unroll
+            for (int w = 0; w < GV_WAVES; ++w) v += pp[w * 128];
+            if (m < M && ng < N) a.y[(int64_t)m * N + ng] = v;
+        }
+    }
+}
+
+typedef void (*GrKernel)(GemvRegArgs);
+
+template <int FMT, int U, int P, int D>
+static hipError_t gr_launch(const GemvRegArgs& a, int grid, hipStream_t s)
+{
+    using C = GrCfg<FMT, U, P, D>;
+    GrKernel k = gemv_reg_kernel<FMT, U, P, D>;
+    static std::set<std::pair<int, const void*>> done;
+    static std::mutex mu;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        if (done.insert(std::make_pair(dev, (const void*)k)).second) {
+            (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+            (void)hipGetLastError();
+        }
+    }
+    GemvRegArgs args = a;
+    void* argv[] = {&args};
+    return hipLaunchKernel((const void*)k, dim3(grid), dim3(GV_THREADS), argv, C::LDS, s);
+}
+
+// Units per wave slice for this K, or 0 when the slice's operand would not fit
+// the registers (64 VGPRs at most: Q8_0 8 block pairs, Q4_K 2 super-blocks,
+// so K <= 4096).
+static int gr_units(int fmt, int64_t K)
+{
+    const int64_t nlu = fmt == FMT_Q8_0 ? K / 64 : K / 256;
+    const int64_t per = (nlu + GV_WAVES - 1) / GV_WAVES;
+    if (fmt == FMT_Q8_0) return per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : per <= 8 ? 8 : 0;
+    return per <= 1 ? 1 : per <= 2 ? 2 : 0;
+}
+
+bool gemv_reg_supported(int fmt, int mode, int M, int64_t N, int64_t K)
+{
+    if (mode != MODE_A || M < 2 || M > GEMV_MAX_M || N < 1) return false;
+    if (fmt == FMT_Q8_0) { if (K % 64 != 0) return false; }
+    else if (fmt == FMT_Q4_K) { if (K % 256 != 0) return false; }
+    else return false;
+    return gr_units(fmt, K) > 0 && (int64_t)M * K * 4 <= 0xffffffffll;
+}
+
+hipError_t launch_gemv_reg(int fmt, const void* w, const float* x, int64_t N, int64_t K, int M, float* y, hipStream_t s)
+{
+    if (!gemv_reg_supported(fmt, MODE_A, M, N, K)) return hipErrorInvalidValue;
+    GemvRegArgs a{};
+    a.w = (const uint8_t*)w;
+    a.nlu = (int)(fmt == FMT_Q8_0 ? K / 64 : K / 256);
+    a.row_bytes = a.nlu * (fmt == FMT_Q8_0 ? 68 : 144);
+    a.w_bytes = N * (int64_t)a.row_bytes;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.M = M;
+    a.tiles = (int)((N + 15) / 16);
+    const int cus = device_cus();
+    a.T = (a.tiles + cus - 1) / cus;
+    const int grid = (a.tiles + a.T - 1) / a.T;
+    a.x = x;
+    a.y = y;
+    const int U = gr_units(fmt, K);
+    if (fmt == FMT_Q8_0) {
+        if (U == 8) return gr_launch<FMT_Q8_0, 8, 4, 4>(a, grid, s);
+        if (U == 4) return gr_launch<FMT_Q8_0, 4, 4, 4>(a, grid, s);
+        if (U == 2) return gr_launch<FMT_Q8_0, 2, 2, 4>(a, grid, s);
+        return gr_launch<FMT_Q8_0, 1, 1, 4>(a, grid, s);
+    }
+    if (U == 2) return gr_launch<FMT_Q4_K, 2, 1, 4>(a, grid, s);
+    return gr_launch<FMT_Q4_K, 1, 1, 4>(a, grid, s);
+}
+
+}  // namespace qmm

@@ -276,6 +276,37 @@ def test_runs_are_deterministic_and_reuse_the_plan(fmt, mode, m):
     assert np.array_equal(y1, y2)
 
 
+# Mode (a) decode with 2..8 rows (K <= 4096) runs with each wave's slice of
+# the activation operand in registers, K split over the eight waves.  Shapes:
+# one tile, ragged N, the largest slices (Q8_0 K = 4096: eight block pairs per
+# wave), slices past the row's end (K = 1536: six of eight slices real; K =
+# 576: the fifth slice one pair, the rest empty).  Three runs of one plan must
+# agree bit for bit.
+REG_SHAPES = [
+    (qmm.Q8_0, 16, 2048, 3),
+    (qmm.Q8_0, 200, 4096, 8),
+    (qmm.Q8_0, 4100, 1024, 2),
+    (qmm.Q8_0, 130, 1536, 5),
+    (qmm.Q8_0, 77, 576, 7),
+    (qmm.Q4_K, 130, 4096, 5),
+    (qmm.Q4_K, 64, 2048, 8),
+    (qmm.Q4_K, 33, 1536, 8),
+]
+
+
+@pytest.mark.parametrize("fmt,n,k,m", REG_SHAPES, ids=[f"{FMT_NAME[f]}-{n}x{k}-M{m}" for f, n, k, m in REG_SHAPES])
+def test_decode_register_operand_and_k_halves(fmt, n, k, m):
+    wq = oracle.quantize(fmt, synth.weights_f32(4100 + n, n, k))
+    x = synth.acts_f32(4200 + m, m, k)
+    with qmm.Plan(fmt, n, k, m, qmm.MODE_F32ACT) as p:
+        wd, xd = dev(wq), dev(x)
+        ys = [host(p.run(wd, xd)) for _ in range(3)]
+    for y in ys[1:]:
+        assert np.array_equal(y, ys[0])
+    yr, a = ref(fmt, qmm.MODE_F32ACT, wq, n, k, x)
+    assert_within(ys[0], yr, a, f"{FMT_NAME[fmt]} {n}x{k} M={m}")
+
+
 # Grouped runs: plans sharing format, K and mode and one x.  At M = 1 the
 # one-row kernel takes all of their rows in one launch (per four plans) and
 # must give what separate runs give, bit for bit; other M run the plans in turn.

@@ -57,6 +57,8 @@ PAIRS = [
     (qmm.Q8_0, B, (576, 1536, 37), (192, 576, 9)),
     (qmm.Q8_0, A, (1000, 1536, 37), (576, 576, 1)),
     (qmm.Q8_0, B, (14336, 4096, 8), (576, 1536, 1)),
+    (qmm.Q8_0, A, (14336, 4096, 8), (576, 1536, 5)),
+    (qmm.Q4_K, A, (600, 4096, 8), (130, 4096, 2)),
     (qmm.Q4_K, B, (576, 1536, 37), (300, 512, 8)),
     (qmm.Q4_K, A, (576, 4096, 130), (192, 1536, 1)),
     (qmm.Q4_0, B, (576, 1536, 20), (192, 576, 1)),
