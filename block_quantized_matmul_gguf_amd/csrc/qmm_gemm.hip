@@ -193,11 +193,15 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_kernel(GemmArg
         bfr[s] = swz(wn + li, 4 * s + kg);
     }
 
-    // ---- staging registers, two sets (stage parity) ----
+    // ---- staging registers, two sets (stage parity); Q4_K mode (a) keeps one set
+    // (the next stage is loaded once the current registers are in LDS), which
+    // keeps its accumulators and operands in registers ----
     constexpr bool Q4 = FMT == FMT_Q4_K;
-    uint4 ra[2][AU];
+    constexpr bool ONESET = Q4 && !MB;
+    constexpr int NSET = ONESET ? 1 : 2;
+    uint4 ra[NSET][AU];
     uint32_t rq8[2][Q8 ? BU : 1][9];
-    uint4 rhd[2][Q4 ? BU : 1], rqa[2][Q4 ? BU : 1], rqb[2][Q4 ? BU : 1];
+    uint4 rhd[NSET][Q4 ? BU : 1], rqa[NSET][Q4 ? BU : 1], rqb[NSET][Q4 ? BU : 1];
     uint4 rxv[XU];
     // Q6_K: per unit the 32 bytes of low bits and of high bits and the stage's
     // four scales, each read as whole dwords from the 4-byte-aligned address at
@@ -208,7 +212,7 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_kernel(GemmArg
     float rdxv[2];
 
     auto load = [&](int st, auto setc, auto csc) {
-        constexpr int SET = decltype(setc)::value;
+        constexpr int SET = ONESET ? 0 : decltype(setc)::value;
         constexpr int CS = decltype(csc)::value;  // stage within the super-block (Q4_K)
 #pragma unroll
         for (int i = 0; i < AU; ++i)
@@ -270,7 +274,7 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_kernel(GemmArg
     constexpr int NI = AU + BU * 5 + (Q4 ? XU : 0) + (Q6 && MB ? 1 : 0);
     half2_t qs_s[BU], qs_b[BU];  // Q4_K: sc and -1024*sc of the unit's sub-block
     auto item = [&](int w, int st, auto setc, auto pc, auto csc) {
-        constexpr int SET = decltype(setc)::value;
+        constexpr int SET = ONESET ? 0 : decltype(setc)::value;
         constexpr int P = decltype(pc)::value;
         constexpr int CS = decltype(csc)::value;
         if (w < AU) {
@@ -426,7 +430,7 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_kernel(GemmArg
         using IQ = std::integral_constant<int, P ^ 1>;
         using ICS1 = std::integral_constant<int, (CS + 1) & 3>;
         using ICS2 = std::integral_constant<int, (CS + 2) & 3>;
-        if (LOAD) load(st + 2, IP{}, ICS2{});
+        if (LOAD && !ONESET) load(st + 2, IP{}, ICS2{});
         const uint8_t* sa = lds + P * C::A_BYTES;
         const uint8_t* sbb = lds + C::OFF_B + P * C::B_BYTES;
         if constexpr (Q6A) {
@@ -536,6 +540,7 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_kernel(GemmArg
                 }
             }
         }
+        if (LOAD && ONESET) load(st + 2, IP{}, ICS2{});  // the registers of stage st + 1 are in LDS
         if constexpr (Q8) {
 #pragma unroll
             for (int i = 0; i < TM; ++i)
@@ -610,11 +615,13 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_kernel(GemmArg
     using T_ = std::true_type;
     using F_ = std::false_type;
 
-    // prologue: stages 0 and 1 in flight, stage 0 staged into buffer 0
+    // prologue: stages 0 and 1 in flight, stage 0 staged into buffer 0 (one register
+    // set: stage 1 is loaded once stage 0 is staged)
     load(0, I0{}, I0{});
-    if (nst > 1) load(1, I1{}, I1{});
+    if (nst > 1 && !ONESET) load(1, I1{}, I1{});
 #pragma unroll
     for (int w = 0; w < NI; ++w) item(w, 0, I0{}, I0{}, I0{});
+    if (nst > 1 && ONESET) load(1, I1{}, I1{});
     __syncthreads();
 
     if constexpr (Q8) {
