@@ -193,14 +193,14 @@ __global__ __launch_bounds__(64 * WM * WN, WM * WN / 4) void gemm_kernel(GemmArg
         bfr[s] = swz(wn + li, 4 * s + kg);
     }
 
-    // ---- staging registers, two sets (stage parity); Q4_K mode (a) keeps one set
-    // (the next stage is loaded once the current registers are in LDS), which
-    // keeps its accumulators and operands in registers ----
+    // ---- staging registers, two sets (stage parity); mode (a) of Q8_0 and Q4_K
+    // keeps one set (the next stage is loaded once the current registers are in
+    // LDS): fewer registers (Q4_K spilled with two) and measured faster ----
     constexpr bool Q4 = FMT == FMT_Q4_K;
-    constexpr bool ONESET = Q4 && !MB;
+    constexpr bool ONESET = (Q4 || Q8) && !MB;
     constexpr int NSET = ONESET ? 1 : 2;
     uint4 ra[NSET][AU];
-    uint32_t rq8[2][Q8 ? BU : 1][9];
+    uint32_t rq8[NSET][Q8 ? BU : 1][9];
     uint4 rhd[NSET][Q4 ? BU : 1], rqa[NSET][Q4 ? BU : 1], rqb[NSET][Q4 ? BU : 1];
     uint4 rxv[XU];
     // Q6_K: per unit the 32 bytes of low bits and of high bits and the stage's
