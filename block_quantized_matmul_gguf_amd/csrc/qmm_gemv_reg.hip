@@ -122,10 +122,10 @@ __global__ __launch_bounds__(GV_THREADS, 2) void gemv_reg_kernel(GemvRegArgs a)
     };
 
     // ---- the activation values of this wave's slice, four per lane and step ----
-    // Q8_0 even block: k-group g holds the block's values 2+8g .. 9+8g (group 3:
-    // 26..31, 0, 1), the order in which the weights' bytes follow their scale;
-    // odd block and Q4_K: 8g .. 8g+7.  Lanes n < 8 take the first four, n >= 8 the
-    // last four.  Units past the slice's real ones and rows past M read as zero.
+    // k-group g holds the block's values 8g .. 8g+7 (the Q8_0 even block's weight
+    // bytes, which start two bytes into a dword, are realigned when gathered).
+    // Lanes n < 8 take the first four, n >= 8 the last four, with one 16-byte
+    // load.  Units past the slice's real ones and rows past M read as zero.
     issue(0);  // the first stage flies while the activations load
     const rsrc_t xr = make_rsrc(a.x, clamp_u32((int64_t)M * K * 4));
     float xv[U * STEPS][4];
@@ -136,17 +136,8 @@ __global__ __launch_bounds__(GV_THREADS, 2) void gemv_reg_kernel(GemvRegArgs a)
         for (int p = 0; p < STEPS; ++p) {
             const int base = r8 * K + (u0 + u) * VPL + 32 * p;
             float* v = xv[u * STEPS + p];
-            if (FMT == FMT_Q8_0 && p == 0) {
-                const int oa = upper ? (g < 3 ? 6 + 8 * g : 30) : (g < 3 ? 2 + 8 * g : 26);
-                const int ob = upper ? (g < 3 ? 8 + 8 * g : 0) : oa + 2;
-                const u32x2_t va = __builtin_amdgcn_raw_buffer_load_b64(xr, live ? (uint32_t)(base + oa) * 4 : 0x80000000u, 0, 0);
-                const u32x2_t vb = __builtin_amdgcn_raw_buffer_load_b64(xr, live ? (uint32_t)(base + ob) * 4 : 0x80000000u, 0, 0);
-                v[0] = __uint_as_float(va[0]); v[1] = __uint_as_float(va[1]);
-                v[2] = __uint_as_float(vb[0]); v[3] = __uint_as_float(vb[1]);
-            } else {
-                const float4 t = ldx16(xr, live ? (uint32_t)(base + 8 * g + (upper ? 4 : 0)) * 4 : 0x80000000u);
-                v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
-            }
+            const float4 t = ldx16(xr, live ? (uint32_t)(base + 8 * g + (upper ? 4 : 0)) * 4 : 0x80000000u);
+            v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
         }
     }
     // the row maximum over the slice: lanes n, n + 8 of every 16-lane row hold row n % 8
@@ -215,7 +206,6 @@ __global__ __launch_bounds__(GV_THREADS, 2) void gemv_reg_kernel(GemvRegArgs a)
     // ---- main loop ----
     f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
     const f32x4_t zf = {0.0f, 0.0f, 0.0f, 0.0f};
-    const uint32_t sel3 = g == 3 ? 0x07060100u : 0x03020100u;  // Q8_0 even block, k-group 3: q0, q1
     uint32_t nibm = 0x000f000fu, nibc = 0x64006400u;           // Q4_K nibble decode constants
     asm volatile("" : "+v"(nibm), "+v"(nibc));
     const bool lo_lane = g >= 2;  // output rows 8..15: the lo parts (no mins term there)
@@ -229,10 +219,12 @@ __global__ __launch_bounds__(GV_THREADS, 2) void gemv_reg_kernel(GemvRegArgs a)
             if (u >= ureal) break;  // wave-uniform: units past the slice are not the row's
             const uint8_t* rp = rrow + j * LUB;
             if constexpr (FMT == FMT_Q8_0) {
+                // even block: values 8g .. 8g+7 are bytes 2+8g .. 9+8g of the pair
                 const uint32_t E0 = lds32(rp), E8 = lds32(rp + 32);
-                const uint8_t* xe = rp + 4 + 8 * g;
+                const uint8_t* xe = rp + 8 * g;
                 const uint8_t* xo = rp + 36 + 8 * g;
-                const half8_t Be = i8x8_to_f16(lds32(xe), __builtin_amdgcn_perm(E0, lds32(xe + 4), sel3));
+                const uint32_t e0 = lds32(xe), e1 = lds32(xe + 4), e2 = lds32(xe + 8);
+                const half8_t Be = i8x8_to_f16(__builtin_amdgcn_alignbyte(e1, e0, 2), __builtin_amdgcn_alignbyte(e2, e1, 2));
                 const half8_t Bo = i8x8_to_f16(lds32(xo), lds32(xo + 4));
                 const f32x4_t Ce = __builtin_amdgcn_mfma_f32_16x16x32_f16(areg[s * P + j][0], Be, zf, 0, 0, 0);
                 const f32x4_t Co = __builtin_amdgcn_mfma_f32_16x16x32_f16(areg[s * P + j][1], Bo, zf, 0, 0, 0);
