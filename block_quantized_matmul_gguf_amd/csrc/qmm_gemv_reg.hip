@@ -13,7 +13,8 @@
 //     streams its K slice of the 16 rows through a ring of D stage buffers in
 //     LDS filled by 16-byte buffer-to-LDS loads (D stages in flight, the whole
 //     LDS but the tile partials available to the ring);
-//   * the activation values of the slice are loaded first, their row maxima
+//   * the activation values of the slice are loaded first (lane quads kept
+//     inside one row, then moved to the operand lanes), their row maxima
 //     taken (the power-of-two scale 2^e of a row is per wave and slice: each
 //     wave scales its partial sums back by 2^-e, exactly), then the ring is
 //     primed and the values are split into f16 hi and lo while it fills;
@@ -124,22 +125,31 @@ __global__ __launch_bounds__(GV_THREADS, 2) void gemv_reg_kernel(GemvRegArgs a)
     // ---- the activation values of this wave's slice, four per lane and step ----
     // k-group g holds the block's values 8g .. 8g+7 (the Q8_0 even block's weight
     // bytes, which start two bytes into a dword, are realigned when gathered).
-    // Lanes n < 8 take the first four, n >= 8 the last four, with one 16-byte
-    // load.  Units past the slice's real ones and rows past M read as zero.
-    issue(0);  // the first stage flies while the activations load
+    // Operand lanes n < 8 take the first four, n >= 8 the last four.  They are
+    // loaded with each lane quad inside one row (lane l: row l / 8, values
+    // 4 (l % 8) .. +3 of the step; quads that span rows took the 128 KB of a
+    // workgroup about 2 us longer to arrive) and moved to the operand lanes with
+    // one ds_bpermute per dword.  Units past the slice's real ones and rows past
+    // M read as zero.  Every wave's activation loads are issued before any
+    // weight load of the workgroup, then the first stage follows.
     const rsrc_t xr = make_rsrc(a.x, clamp_u32((int64_t)M * K * 4));
-    float xv[U * STEPS][4];
+    u32x4_t xt[U * STEPS];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const bool live = u < ureal;
 #pragma unroll
-        for (int p = 0; p < STEPS; ++p) {
-            const int base = r8 * K + (u0 + u) * VPL + 32 * p;
-            float* v = xv[u * STEPS + p];
-            const float4 t = ldx16(xr, live ? (uint32_t)(base + 8 * g + (upper ? 4 : 0)) * 4 : 0x80000000u);
-            v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
-        }
+        for (int p = 0; p < STEPS; ++p)
+            xt[u * STEPS + p] = ld128(xr, live ? (uint32_t)((lane >> 3) * K + (u0 + u) * VPL + 32 * p + 4 * (lane & 7)) * 4
+                                               : 0x80000000u);
     }
+    __builtin_amdgcn_s_barrier();
+    issue(0);  // the first stage flies while the activations arrive
+    const int src4 = 4 * (r8 * 8 + 2 * g + (upper ? 1 : 0));  // the load lane holding this lane's four values
+    float xv[U * STEPS][4];
+#pragma unroll
+    for (int i = 0; i < U * STEPS; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xv[i][e] = __int_as_float(__builtin_amdgcn_ds_bpermute(src4, (int)xt[i][e]));
     // the row maximum over the slice: lanes n, n + 8 of every 16-lane row hold row n % 8
     float mx = 0.0f;
 #pragma unroll
