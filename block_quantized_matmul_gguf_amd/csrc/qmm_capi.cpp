@@ -305,6 +305,8 @@ static int run_impl(const qmm_plan* p, const void* w, const float* x, float* y, 
     if (is_ext_format(p->fmt)) {
         if (M == 1 && gemv_row_supported(p->fmt, p->mode, 1, p->N, K, tr != nullptr)) {
             e = launch_gemv_row(p->fmt, p->mode, w, x, p->N, K, y, s, tr);  // Q4_0, Q5_0: the one-row kernel
+        } else if (M <= GEMV_MAX_M && !tr && gemv_reg_supported(p->fmt, p->mode, (int)M, p->N, K)) {
+            e = launch_gemv_reg(p->fmt, w, x, p->N, K, (int)M, y, s);  // Q4_0, Q5_0 mode (a), 2..8 rows
         } else if (M <= GEMV_MAX_M) {
             e = launch_ext_run(p->fmt, p->mode, w, x, p->N, K, M, p->ex, y, s, tr);
         } else if (p->fmt == QMM_Q6_K) {
@@ -407,10 +409,11 @@ extern "C" int qmatmul_run_group(const qmm_plan* const* plans, int count, const 
             return QMM_OK;
         }
     }
-    if (is_ext_format(p0->fmt) && p0->Kr == p0->K && ext_group_supported(p0->fmt, p0->mode, p0->K, M)) {
+    if (is_ext_format(p0->fmt) && p0->Kr == p0->K && ext_group_supported(p0->fmt, p0->mode, p0->K, M) &&
+        !gemv_reg_supported(p0->fmt, p0->mode, (int)M, 1, p0->K)) {
         // Q4_0, Q5_0, Q6_K decode: one launch per ext_group_max() plans, unless
-        // a plan's separate run would take the one-row kernel (the grouped
-        // values must be those of the separate runs)
+        // a plan's separate run would take the one-row or the register-operand
+        // kernel (the grouped values must be those of the separate runs)
         int64_t total = 0;
         bool row_alone = false;
         for (int i = 0; i < count; ++i) {

@@ -1,5 +1,6 @@
 // qmm_gemv_reg.hip -- decode with two to eight f32 activation rows (mode (a))
-// for Q8_0 and Q4_K weights, the activation operand held in registers.
+// for Q8_0, Q4_K, Q4_0 and Q5_0 weights, the activation operand held in
+// registers.
 //
 // The pages' decode step streams every weight once per token (page "同一个
 // GGUF，CPU 和 Metal 生成的文字不一样", section 修法: the CPU decode is bound by
@@ -19,8 +20,9 @@
 //     wave scales its partial sums back by 2^-e, exactly), then the ring is
 //     primed and the values are split into f16 hi and lo while it fills;
 //   * v_mfma_f32_16x16x32_f16 with A rows 0..7 = hi and 8..15 = lo of the
-//     eight activation rows and the weights as exact f16 integers, the same
-//     weight decode and block-scale epilogue as the tile kernel;
+//     eight activation rows and the weights as exact f16 integers (Q8_0 q;
+//     Q4_K q; Q4_0 q - 8; Q5_0 q - 16), the block scales applied in f32 after
+//     each block (Q4_K's mins term from the sub-block sums of x*2^e);
 //   * at the end of a tile the eight slices' partial sums meet in LDS behind
 //     one barrier and are added in slice order (deterministic).
 // Operand lanes n and n + 8 of a 16-lane row need the same eight x values
@@ -41,7 +43,7 @@ struct GemvRegArgs {
     int64_t w_bytes;  // N * row_bytes
     int row_bytes;
     int N, K, M;
-    int nlu;    // load units per row (Q8_0 block pairs, Q4_K super-blocks)
+    int nlu;    // load units per row (block pairs of the 32-value formats, Q4_K super-blocks)
     int tiles;  // 16-row tiles
     int T;      // tiles per workgroup
     const float* x;
@@ -50,25 +52,47 @@ struct GemvRegArgs {
 
 constexpr int GR_PART_BYTES = 2 * GV_WAVES * 128 * 4;  // tile partials, two slots: [slot][wave][8 rows][16]
 
+// Bytes of a load unit: a block pair of the 32-value formats (the pair keeps
+// every unit 4-byte aligned), a Q4_K super-block.
+constexpr int gr_lub(int fmt) { return fmt == FMT_Q8_0 ? 68 : fmt == FMT_Q4_0 ? 36 : fmt == FMT_Q5_0 ? 44 : 144; }
+
 // U: load units per wave slice (K <= 8 U units), P: units per stage, D: ring depth.
 template <int FMT, int U, int P, int D>
 struct GrCfg {
-    static constexpr int LUB = FMT == FMT_Q8_0 ? 68 : 144;
-    static constexpr int STEPS = FMT == FMT_Q8_0 ? 2 : 8;  // matrix-core steps (32 values) per unit
-    static constexpr int CPR = gv_cpr(FMT, P);              // 16-byte chunks per row and stage
+    static constexpr int LUB = gr_lub(FMT);
+    static constexpr int STEPS = FMT == FMT_Q4_K ? 8 : 2;   // matrix-core steps (32 values) per unit
+    static constexpr int CPR = (LUB * P + 15) / 16;         // 16-byte chunks per row and stage
     static constexpr int SBY = 16 * 16 * CPR;               // one stage buffer (16 rows, unpadded)
     static constexpr int TL = (16 * CPR + 63) / 64;         // load instructions per stage
     static constexpr int SUMS = FMT == FMT_Q4_K ? U * 8 * 8 * 4 : 0;  // per wave: x*2^e sums [U*8 sub-blocks][8 rows]
     static constexpr int OFF_PART = GV_WAVES * D * SBY;
     static constexpr int OFF_SUMS = OFF_PART + GR_PART_BYTES;
     static constexpr int LDS = OFF_SUMS + GV_WAVES * SUMS;
-    static_assert(U % P == 0 && gv_ring_ok(FMT, P) && D >= 2 && (D - 1) * TL <= 63, "ring of LDS-direct stages");
+    // an odd chunk count puts the 16 rows of a stage in different LDS banks
+    static_assert(U % P == 0 && (CPR & 1) == 1 && D >= 2 && (D - 1) * TL <= 63, "ring of LDS-direct stages");
     static_assert(LDS <= GV_LDS_MAX, "LDS of a compute unit");
 };
 
 // DPP row_ror:8 -- lane n of a 16-lane row receives lane (n + 8) % 16.
 QMM_DEV uint32_t ror8(uint32_t v) { return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x128, 0xF, 0xF, false); }
 QMM_DEV uint32_t pack_h2(_Float16 a, _Float16 b) { return __builtin_bit_cast(uint32_t, half2_t{a, b}); }
+
+// Eight unsigned codes (bytes of d0, d1, each below 64) -> eight exact f16
+// (code - OFF) in order: byte b under 0x64 is the f16 1024 + b, then one packed
+// subtraction of 1024 + OFF.
+template <int OFF>
+QMM_DEV half8_t u8x8_to_f16(uint32_t d0, uint32_t d1)
+{
+    const half2_t bias = {(_Float16)(-1024.0f - OFF), (_Float16)(-1024.0f - OFF)};
+    const half2_t h0 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, d0, 0x04010400u)) + bias;
+    const half2_t h1 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, d0, 0x04030402u)) + bias;
+    const half2_t h2 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, d1, 0x04010400u)) + bias;
+    const half2_t h3 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, d1, 0x04030402u)) + bias;
+    half8_t r;
+    r[0] = h0[0]; r[1] = h0[1]; r[2] = h1[0]; r[3] = h1[1];
+    r[4] = h2[0]; r[5] = h2[1]; r[6] = h3[0]; r[7] = h3[1];
+    return r;
+}
 
 template <int FMT, int U, int P, int D>
 __global__ __launch_bounds__(GV_THREADS, 2) void gemv_reg_kernel(GemvRegArgs a)
@@ -77,7 +101,7 @@ __global__ __launch_bounds__(GV_THREADS, 2) void gemv_reg_kernel(GemvRegArgs a)
     constexpr int LUB = C::LUB, STEPS = C::STEPS, CPR = C::CPR, SBY = C::SBY, TL = C::TL;
     constexpr int S = U / P;  // stages per tile
     static_assert(S == 1 || S == 2, "one or two stages per tile");
-    constexpr int VPL = FMT == FMT_Q8_0 ? 64 : 256;
+    constexpr int VPL = FMT == FMT_Q4_K ? 256 : 64;
     extern __shared__ __align__(16) uint8_t lds[];
 
     const int M = a.M, N = a.N, K = a.K;
@@ -123,8 +147,8 @@ __global__ __launch_bounds__(GV_THREADS, 2) void gemv_reg_kernel(GemvRegArgs a)
     };
 
     // ---- the activation values of this wave's slice, four per lane and step ----
-    // k-group g holds the block's values 8g .. 8g+7 (the Q8_0 even block's weight
-    // bytes, which start two bytes into a dword, are realigned when gathered).
+    // k-group g holds the block's values 8g .. 8g+7 (the even block of a pair, whose
+    // weight bytes start two bytes into a dword, is realigned when gathered).
     // Operand lanes n < 8 take the first four, n >= 8 the last four.  They are
     // loaded with each lane quad inside one row (lane l: row l / 8, values
     // 4 (l % 8) .. +3 of the step; quads that span rows took the 128 KB of a
@@ -180,10 +204,10 @@ __global__ __launch_bounds__(GV_THREADS, 2) void gemv_reg_kernel(GemvRegArgs a)
             float xs[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) split_one(v[e], sc, h[e], l[e], xs[e]);
-            // operand slots of the four values: Q8_0 in order; Q4_K slot e holds element
-            // nib_perm(e) of the k-group (the order the nibble decoder yields)
+            // operand slots of the four values: in order, but Q4_K slot e holds element
+            // nib_perm(e) of the k-group (the order its nibble decoder yields)
             uint32_t h0, h1, l0, l1;
-            if constexpr (FMT == FMT_Q8_0) {
+            if constexpr (FMT != FMT_Q4_K) {
                 h0 = pack_h2(h[0], h[1]); h1 = pack_h2(h[2], h[3]);
                 l0 = pack_h2(l[0], l[1]); l1 = pack_h2(l[2], l[3]);
             } else {
@@ -239,6 +263,31 @@ __global__ __launch_bounds__(GV_THREADS, 2) void gemv_reg_kernel(GemvRegArgs a)
                 const f32x4_t Ce = __builtin_amdgcn_mfma_f32_16x16x32_f16(areg[s * P + j][0], Be, zf, 0, 0, 0);
                 const f32x4_t Co = __builtin_amdgcn_mfma_f32_16x16x32_f16(areg[s * P + j][1], Bo, zf, 0, 0, 0);
                 const float de = f16lo(E0), dd = f16hi(E8);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[q] = fmaf(Co[q], dd, fmaf(Ce[q], de, acc[q]));
+            } else if constexpr (FMT == FMT_Q4_0 || FMT == FMT_Q5_0) {
+                // pair of blocks: Q4_0 d | qs[16], Q5_0 d | qh[4] | qs[16], twice.  k-group g
+                // takes the low (g < 2) or high nibbles of qs bytes 8 (g & 1) .. +7, Q5_0
+                // with bits 8g .. 8g+7 of qh as their fifth bits
+                constexpr int QS0 = FMT == FMT_Q4_0 ? 2 : 6, HALF = LUB / 2, QS1 = HALF + QS0;
+                constexpr int OFF = FMT == FMT_Q4_0 ? 8 : 16;
+                const int sh = 4 * (g >> 1), qo = 8 * (g & 1);
+                const uint32_t a0 = lds32(rp + QS0 - 2 + qo), a1 = lds32(rp + QS0 + 2 + qo), a2 = lds32(rp + QS0 + 6 + qo);
+                uint32_t ce0 = (__builtin_amdgcn_alignbyte(a1, a0, 2) >> sh) & 0x0f0f0f0fu;
+                uint32_t ce1 = (__builtin_amdgcn_alignbyte(a2, a1, 2) >> sh) & 0x0f0f0f0fu;
+                uint32_t co0 = (lds32(rp + QS1 + qo) >> sh) & 0x0f0f0f0fu;
+                uint32_t co1 = (lds32(rp + QS1 + qo + 4) >> sh) & 0x0f0f0f0fu;
+                if constexpr (FMT == FMT_Q5_0) {
+                    const uint32_t he = __builtin_amdgcn_alignbyte(lds32(rp + 4), lds32(rp), 2), ho = lds32(rp + HALF + 2);
+                    ce0 |= spread4((he >> (8 * g)) & 15u);
+                    ce1 |= spread4((he >> (8 * g + 4)) & 15u);
+                    co0 |= spread4((ho >> (8 * g)) & 15u);
+                    co1 |= spread4((ho >> (8 * g + 4)) & 15u);
+                }
+                const half8_t Be = u8x8_to_f16<OFF>(ce0, ce1), Bo = u8x8_to_f16<OFF>(co0, co1);
+                const f32x4_t Ce = __builtin_amdgcn_mfma_f32_16x16x32_f16(areg[s * P + j][0], Be, zf, 0, 0, 0);
+                const f32x4_t Co = __builtin_amdgcn_mfma_f32_16x16x32_f16(areg[s * P + j][1], Bo, zf, 0, 0, 0);
+                const float de = f16lo(lds32(rp)), dd = f16hi(lds32(rp + HALF - 2));
 #pragma unroll
                 for (int q = 0; q < 4; ++q) acc[q] = fmaf(Co[q], dd, fmaf(Ce[q], de, acc[q]));
             } else {
@@ -331,20 +380,20 @@ static hipError_t gr_launch(const GemvRegArgs& a, int grid, hipStream_t s)
 }
 
 // Units per wave slice for this K, or 0 when the slice's operand would not fit
-// the registers (64 VGPRs at most: Q8_0 8 block pairs, Q4_K 2 super-blocks,
-// so K <= 4096).
+// the registers (64 VGPRs at most: 8 block pairs, Q4_K 2 super-blocks, so
+// K <= 4096).
 static int gr_units(int fmt, int64_t K)
 {
-    const int64_t nlu = fmt == FMT_Q8_0 ? K / 64 : K / 256;
+    const int64_t nlu = fmt == FMT_Q4_K ? K / 256 : K / 64;
     const int64_t per = (nlu + GV_WAVES - 1) / GV_WAVES;
-    if (fmt == FMT_Q8_0) return per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : per <= 8 ? 8 : 0;
+    if (fmt != FMT_Q4_K) return per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : per <= 8 ? 8 : 0;
     return per <= 1 ? 1 : per <= 2 ? 2 : 0;
 }
 
 bool gemv_reg_supported(int fmt, int mode, int M, int64_t N, int64_t K)
 {
     if (mode != MODE_A || M < 2 || M > GEMV_MAX_M || N < 1) return false;
-    if (fmt == FMT_Q8_0) { if (K % 64 != 0) return false; }
+    if (fmt == FMT_Q8_0 || fmt == FMT_Q4_0 || fmt == FMT_Q5_0) { if (K % 64 != 0) return false; }
     else if (fmt == FMT_Q4_K) { if (K % 256 != 0) return false; }
     else return false;
     return gr_units(fmt, K) > 0 && (int64_t)M * K * 4 <= 0xffffffffll;
@@ -355,8 +404,8 @@ hipError_t launch_gemv_reg(int fmt, const void* w, const float* x, int64_t N, in
     if (!gemv_reg_supported(fmt, MODE_A, M, N, K)) return hipErrorInvalidValue;
     GemvRegArgs a{};
     a.w = (const uint8_t*)w;
-    a.nlu = (int)(fmt == FMT_Q8_0 ? K / 64 : K / 256);
-    a.row_bytes = a.nlu * (fmt == FMT_Q8_0 ? 68 : 144);
+    a.nlu = (int)(fmt == FMT_Q4_K ? K / 256 : K / 64);
+    a.row_bytes = a.nlu * gr_lub(fmt);
     a.w_bytes = N * (int64_t)a.row_bytes;
     a.N = (int)N;
     a.K = (int)K;
@@ -373,6 +422,18 @@ hipError_t launch_gemv_reg(int fmt, const void* w, const float* x, int64_t N, in
         if (U == 4) return gr_launch<FMT_Q8_0, 4, 4, 4>(a, grid, s);
         if (U == 2) return gr_launch<FMT_Q8_0, 2, 2, 4>(a, grid, s);
         return gr_launch<FMT_Q8_0, 1, 1, 4>(a, grid, s);
+    }
+    if (fmt == FMT_Q4_0) {
+        if (U == 8) return gr_launch<FMT_Q4_0, 8, 4, 4>(a, grid, s);
+        if (U == 4) return gr_launch<FMT_Q4_0, 4, 4, 4>(a, grid, s);
+        if (U == 2) return gr_launch<FMT_Q4_0, 2, 2, 4>(a, grid, s);
+        return gr_launch<FMT_Q4_0, 1, 1, 4>(a, grid, s);
+    }
+    if (fmt == FMT_Q5_0) {  // two pairs are 88 bytes: an even chunk count, so stages of one pair there
+        if (U == 8) return gr_launch<FMT_Q5_0, 8, 4, 4>(a, grid, s);
+        if (U == 4) return gr_launch<FMT_Q5_0, 4, 4, 4>(a, grid, s);
+        if (U == 2) return gr_launch<FMT_Q5_0, 2, 1, 4>(a, grid, s);
+        return gr_launch<FMT_Q5_0, 1, 1, 4>(a, grid, s);
     }
     if (U == 2) return gr_launch<FMT_Q4_K, 2, 1, 4>(a, grid, s);
     return gr_launch<FMT_Q4_K, 1, 1, 4>(a, grid, s);

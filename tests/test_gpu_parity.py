@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 import block_quantized_matmul_gguf_amd as qmm  # noqa: E402
 
 TOL = 1e-5
-FMT_NAME = {qmm.Q8_0: "Q8_0", qmm.Q4_K: "Q4_K"}
+FMT_NAME = {qmm.Q8_0: "Q8_0", qmm.Q4_K: "Q4_K", qmm.Q4_0: "Q4_0", qmm.Q5_0: "Q5_0"}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -280,8 +280,9 @@ def test_runs_are_deterministic_and_reuse_the_plan(fmt, mode, m):
 # the activation operand in registers, K split over the eight waves.  Shapes:
 # one tile, ragged N, the largest slices (Q8_0 K = 4096: eight block pairs per
 # wave), slices past the row's end (K = 1536: six of eight slices real; K =
-# 576: the fifth slice one pair, the rest empty).  Three runs of one plan must
-# agree bit for bit.
+# 576: the fifth slice one pair, the rest empty).  Q4_0 and Q5_0 (the page's
+# own Q4K file) take the same kernel with their block pairs, every stage width
+# (four pairs, two, one).  Three runs of one plan must agree bit for bit.
 REG_SHAPES = [
     (qmm.Q8_0, 16, 2048, 3),
     (qmm.Q8_0, 200, 4096, 8),
@@ -291,6 +292,14 @@ REG_SHAPES = [
     (qmm.Q4_K, 130, 4096, 5),
     (qmm.Q4_K, 64, 2048, 8),
     (qmm.Q4_K, 33, 1536, 8),
+    (qmm.Q4_0, 130, 4096, 8),
+    (qmm.Q4_0, 300, 1024, 6),
+    (qmm.Q4_0, 77, 576, 3),
+    (qmm.Q4_0, 40, 128, 2),
+    (qmm.Q5_0, 130, 4096, 8),
+    (qmm.Q5_0, 4100, 1024, 2),
+    (qmm.Q5_0, 33, 1536, 7),
+    (qmm.Q5_0, 64, 128, 4),
 ]
 
 

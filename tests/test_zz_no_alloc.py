@@ -62,6 +62,7 @@ PAIRS = [
     (qmm.Q4_K, B, (576, 1536, 37), (300, 512, 8)),
     (qmm.Q4_K, A, (576, 4096, 130), (192, 1536, 1)),
     (qmm.Q4_0, B, (576, 1536, 20), (192, 576, 1)),
+    (qmm.Q5_0, A, (1536, 4096, 8), (576, 576, 3)),
     (qmm.Q5_0, A, (576, 1536, 8), (192, 576, 3)),
     (qmm.Q6_K, B, (576, 1536, 37), (192, 512, 8)),
     (qmm.Q6_K, A, (576, 1536, 37), (192, 512, 1)),
