@@ -1,5 +1,5 @@
 // qmm_gemv_reg.hip -- decode with two to eight f32 activation rows (mode (a))
-// for Q8_0, Q4_K, Q4_0 and Q5_0 weights, the activation operand held in
+// for Q8_0, Q4_K, Q4_0, Q5_0 and Q6_K weights, the activation operand held in
 // registers.
 //
 // The pages' decode step streams every weight once per token (page "同一个
@@ -21,8 +21,10 @@
 //     primed and the values are split into f16 hi and lo while it fills;
 //   * v_mfma_f32_16x16x32_f16 with A rows 0..7 = hi and 8..15 = lo of the
 //     eight activation rows and the weights as exact f16 integers (Q8_0 q;
-//     Q4_K q; Q4_0 q - 8; Q5_0 q - 16), the block scales applied in f32 after
-//     each block (Q4_K's mins term from the sub-block sums of x*2^e);
+//     Q4_K q; Q4_0 q - 8; Q5_0 q - 16; Q6_K sh (q - 32) and sl (q - 32) for
+//     its per-16 scale sc = 16 sh + sl), the block scales applied in f32 after
+//     each block (Q4_K's mins term from the sub-block sums of x*2^e; Q6_K's d
+//     once per super-block);
 //   * at the end of a tile the eight slices' partial sums meet in LDS behind
 //     one barrier and are added in slice order (deterministic).
 // Operand lanes n and n + 8 of a 16-lane row need the same eight x values
@@ -43,7 +45,7 @@ struct GemvRegArgs {
     int64_t w_bytes;  // N * row_bytes
     int row_bytes;
     int N, K, M;
-    int nlu;    // load units per row (block pairs of the 32-value formats, Q4_K super-blocks)
+    int nlu;    // load units per row (block pairs of the 32-value formats, Q4_K super-blocks, Q6_K super-block pairs)
     int tiles;  // 16-row tiles
     int T;      // tiles per workgroup
     const float* x;
@@ -52,15 +54,20 @@ struct GemvRegArgs {
 
 constexpr int GR_PART_BYTES = 2 * GV_WAVES * 128 * 4;  // tile partials, two slots: [slot][wave][8 rows][16]
 
-// Bytes of a load unit: a block pair of the 32-value formats (the pair keeps
-// every unit 4-byte aligned), a Q4_K super-block.
-constexpr int gr_lub(int fmt) { return fmt == FMT_Q8_0 ? 68 : fmt == FMT_Q4_0 ? 36 : fmt == FMT_Q5_0 ? 44 : 144; }
+// Bytes of a load unit: a block pair of the 32-value formats and a super-block
+// pair of Q6_K (pairs keep every unit 4-byte aligned), a Q4_K super-block.
+constexpr int gr_lub(int fmt)
+{
+    return fmt == FMT_Q8_0 ? 68 : fmt == FMT_Q4_0 ? 36 : fmt == FMT_Q5_0 ? 44 : fmt == FMT_Q6_K ? 420 : 144;
+}
+// Values of a load unit.
+constexpr int gr_vpl(int fmt) { return fmt == FMT_Q4_K ? 256 : fmt == FMT_Q6_K ? 512 : 64; }
 
 // U: load units per wave slice (K <= 8 U units), P: units per stage, D: ring depth.
 template <int FMT, int U, int P, int D>
 struct GrCfg {
     static constexpr int LUB = gr_lub(FMT);
-    static constexpr int STEPS = FMT == FMT_Q4_K ? 8 : 2;   // matrix-core steps (32 values) per unit
+    static constexpr int STEPS = gr_vpl(FMT) / 32;           // matrix-core steps (32 values) per unit
     static constexpr int CPR = (LUB * P + 15) / 16;         // 16-byte chunks per row and stage
     static constexpr int SBY = 16 * 16 * CPR;               // one stage buffer (16 rows, unpadded)
     static constexpr int TL = (16 * CPR + 63) / 64;         // load instructions per stage
@@ -101,7 +108,7 @@ __global__ __launch_bounds__(GV_THREADS, 2) void gemv_reg_kernel(GemvRegArgs a)
     constexpr int LUB = C::LUB, STEPS = C::STEPS, CPR = C::CPR, SBY = C::SBY, TL = C::TL;
     constexpr int S = U / P;  // stages per tile
     static_assert(S == 1 || S == 2, "one or two stages per tile");
-    constexpr int VPL = FMT == FMT_Q4_K ? 256 : 64;
+    constexpr int VPL = gr_vpl(FMT);
     extern __shared__ __align__(16) uint8_t lds[];
 
     const int M = a.M, N = a.N, K = a.K;
@@ -290,6 +297,49 @@ __global__ __launch_bounds__(GV_THREADS, 2) void gemv_reg_kernel(GemvRegArgs a)
                 const float de = f16lo(lds32(rp)), dd = f16hi(lds32(rp + HALF - 2));
 #pragma unroll
                 for (int q = 0; q < 4; ++q) acc[q] = fmaf(Co[q], dd, fmaf(Ce[q], de, acc[q]));
+            } else if constexpr (FMT == FMT_Q6_K) {
+                // two super-blocks of ql[128] | qh[64] | sc[16] (int8) | d (f16), the second
+                // two bytes into a dword.  Step p (32 values) of one: half h = p / 4, quarter
+                // q = p % 4; k-group g takes l = 8g .. 8g+7 of the quarter, low bits in nibble
+                // q / 2 of ql[64h + 32 (q & 1) + l], high bits in bit pair q of qh[32h + l],
+                // scale sc[2p + g / 2].  The scale enters the weights as 16 sh + sl (sl in
+                // 0..15): both products with q - 32 are exact f16 integers, and the two
+                // sums of a super-block meet in f32 after its last step.
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    const uint8_t* sp = rp + 210 * b;
+                    auto ld8 = [&](int off, uint32_t& v0, uint32_t& v1) {
+                        if (b == 0) {
+                            v0 = lds32(sp + off);
+                            v1 = lds32(sp + off + 4);
+                        } else {
+                            const uint32_t a0 = lds32(sp + off - 2), a1 = lds32(sp + off + 2), a2 = lds32(sp + off + 6);
+                            v0 = __builtin_amdgcn_alignbyte(a1, a0, 2);
+                            v1 = __builtin_amdgcn_alignbyte(a2, a1, 2);
+                        }
+                    };
+                    f32x4_t Ch = zf, Cl = zf;
+#pragma unroll
+                    for (int p = 0; p < 8; ++p) {
+                        const int h = p >> 2, q = p & 3;
+                        uint32_t l0, l1, h0, h1;
+                        ld8(64 * h + 32 * (q & 1) + 8 * g, l0, l1);
+                        ld8(128 + 32 * h + 8 * g, h0, h1);
+                        const int ns = 4 * (q >> 1), hs = 2 * q;
+                        const uint32_t c0 = ((l0 >> ns) & 0x0f0f0f0fu) | (((h0 >> hs) & 0x03030303u) << 4);
+                        const uint32_t c1 = ((l1 >> ns) & 0x0f0f0f0fu) | (((h1 >> hs) & 0x03030303u) << 4);
+                        const half8_t B = u8x8_to_f16<32>(c0, c1);
+                        const int sa = 210 * b + 192 + 2 * p + (g >> 1);  // the scale's byte in the unit
+                        const int sc = (int)(int8_t)(lds32(rp + (sa & ~3)) >> (8 * (sa & 3)));
+                        const _Float16 fh = (_Float16)(sc >> 4), fl = (_Float16)(sc & 15);
+                        const half8_t shv = {fh, fh, fh, fh, fh, fh, fh, fh}, slv = {fl, fl, fl, fl, fl, fl, fl, fl};
+                        Ch = __builtin_amdgcn_mfma_f32_16x16x32_f16(areg[s * P + j][8 * b + p], B * shv, Ch, 0, 0, 0);
+                        Cl = __builtin_amdgcn_mfma_f32_16x16x32_f16(areg[s * P + j][8 * b + p], B * slv, Cl, 0, 0, 0);
+                    }
+                    const float d = b == 0 ? f16lo(lds32(rp + 208)) : f16hi(lds32(rp + 416));
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc[q] = fmaf(fmaf(16.0f, Ch[q], Cl[q]), d, acc[q]);
+                }
             } else {
                 const u32x4_t H = lds128(rp);
                 const float d = f16lo(H[0]), dmin = f16hi(H[0]);
@@ -384,10 +434,11 @@ static hipError_t gr_launch(const GemvRegArgs& a, int grid, hipStream_t s)
 // K <= 4096).
 static int gr_units(int fmt, int64_t K)
 {
-    const int64_t nlu = fmt == FMT_Q4_K ? K / 256 : K / 64;
+    const int64_t nlu = K / gr_vpl(fmt);
     const int64_t per = (nlu + GV_WAVES - 1) / GV_WAVES;
-    if (fmt != FMT_Q4_K) return per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : per <= 8 ? 8 : 0;
-    return per <= 1 ? 1 : per <= 2 ? 2 : 0;
+    if (fmt == FMT_Q6_K) return per <= 1 ? 1 : 0;
+    if (fmt == FMT_Q4_K) return per <= 1 ? 1 : per <= 2 ? 2 : 0;
+    return per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : per <= 8 ? 8 : 0;
 }
 
 bool gemv_reg_supported(int fmt, int mode, int M, int64_t N, int64_t K)
@@ -395,6 +446,7 @@ bool gemv_reg_supported(int fmt, int mode, int M, int64_t N, int64_t K)
     if (mode != MODE_A || M < 2 || M > GEMV_MAX_M || N < 1) return false;
     if (fmt == FMT_Q8_0 || fmt == FMT_Q4_0 || fmt == FMT_Q5_0) { if (K % 64 != 0) return false; }
     else if (fmt == FMT_Q4_K) { if (K % 256 != 0) return false; }
+    else if (fmt == FMT_Q6_K) { if (K % 512 != 0) return false; }  // super-block pairs: 4-byte-aligned rows
     else return false;
     return gr_units(fmt, K) > 0 && (int64_t)M * K * 4 <= 0xffffffffll;
 }
@@ -404,7 +456,7 @@ hipError_t launch_gemv_reg(int fmt, const void* w, const float* x, int64_t N, in
     if (!gemv_reg_supported(fmt, MODE_A, M, N, K)) return hipErrorInvalidValue;
     GemvRegArgs a{};
     a.w = (const uint8_t*)w;
-    a.nlu = (int)(fmt == FMT_Q4_K ? K / 256 : K / 64);
+    a.nlu = (int)(K / gr_vpl(fmt));
     a.row_bytes = a.nlu * gr_lub(fmt);
     a.w_bytes = N * (int64_t)a.row_bytes;
     a.N = (int)N;
@@ -435,6 +487,7 @@ hipError_t launch_gemv_reg(int fmt, const void* w, const float* x, int64_t N, in
         if (U == 2) return gr_launch<FMT_Q5_0, 2, 1, 4>(a, grid, s);
         return gr_launch<FMT_Q5_0, 1, 1, 4>(a, grid, s);
     }
+    if (fmt == FMT_Q6_K) return gr_launch<FMT_Q6_K, 1, 1, 2>(a, grid, s);  // 432-byte stage rows: two fit
     if (U == 2) return gr_launch<FMT_Q4_K, 2, 1, 4>(a, grid, s);
     return gr_launch<FMT_Q4_K, 1, 1, 4>(a, grid, s);
 }

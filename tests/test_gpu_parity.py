@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 import block_quantized_matmul_gguf_amd as qmm  # noqa: E402
 
 TOL = 1e-5
-FMT_NAME = {qmm.Q8_0: "Q8_0", qmm.Q4_K: "Q4_K", qmm.Q4_0: "Q4_0", qmm.Q5_0: "Q5_0"}
+FMT_NAME = {qmm.Q8_0: "Q8_0", qmm.Q4_K: "Q4_K", qmm.Q4_0: "Q4_0", qmm.Q5_0: "Q5_0", qmm.Q6_K: "Q6_K"}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -282,7 +282,9 @@ def test_runs_are_deterministic_and_reuse_the_plan(fmt, mode, m):
 # wave), slices past the row's end (K = 1536: six of eight slices real; K =
 # 576: the fifth slice one pair, the rest empty).  Q4_0 and Q5_0 (the page's
 # own Q4K file) take the same kernel with their block pairs, every stage width
-# (four pairs, two, one).  Three runs of one plan must agree bit for bit.
+# (four pairs, two, one); Q6_K (the downloaded file's ffn_down) with super-block
+# pairs (K % 512 == 0; K = 1536: three of eight slices real).  Three runs of
+# one plan must agree bit for bit.
 REG_SHAPES = [
     (qmm.Q8_0, 16, 2048, 3),
     (qmm.Q8_0, 200, 4096, 8),
@@ -300,6 +302,10 @@ REG_SHAPES = [
     (qmm.Q5_0, 4100, 1024, 2),
     (qmm.Q5_0, 33, 1536, 7),
     (qmm.Q5_0, 64, 128, 4),
+    (qmm.Q6_K, 130, 4096, 8),
+    (qmm.Q6_K, 4100, 1024, 2),
+    (qmm.Q6_K, 77, 1536, 3),
+    (qmm.Q6_K, 40, 512, 5),
 ]
 
 
