@@ -305,8 +305,8 @@ static int run_impl(const qmm_plan* p, const void* w, const float* x, float* y, 
     if (is_ext_format(p->fmt)) {
         if (M == 1 && gemv_row_supported(p->fmt, p->mode, 1, p->N, K, tr != nullptr)) {
             e = launch_gemv_row(p->fmt, p->mode, w, x, p->N, K, y, s, tr);  // Q4_0, Q5_0: the one-row kernel
-        } else if (M <= GEMV_MAX_M && !tr && gemv_reg_supported(p->fmt, p->mode, (int)M, p->N, K)) {
-            e = launch_gemv_reg(p->fmt, w, x, p->N, K, (int)M, y, s);  // Q4_0, Q5_0 mode (a), 2..8 rows
+        } else if (M <= GEMV_MAX_M && gemv_reg_supported(p->fmt, p->mode, (int)M, p->N, K)) {
+            e = launch_gemv_reg(p->fmt, p->mode, w, x, p->N, K, (int)M, y, s, tr);  // 2..8 rows, K <= 4096
         } else if (M <= GEMV_MAX_M) {
             e = launch_ext_run(p->fmt, p->mode, w, x, p->N, K, M, p->ex, y, s, tr);
         } else if (p->fmt == QMM_Q6_K) {

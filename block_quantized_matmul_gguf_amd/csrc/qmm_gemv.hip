@@ -181,7 +181,7 @@ hipError_t launch_gemv(int fmt, int mode, const void* w, const float* x, int64_t
     const bool emit = tr != nullptr;
     if (emit && mode != MODE_B) return hipErrorInvalidValue;
     if (gemv_row_supported(fmt, mode, M, N, K, emit)) return launch_gemv_row(fmt, mode, w, x, N, K, y, s, tr);
-    if (!emit && gemv_reg_supported(fmt, mode, M, N, K)) return launch_gemv_reg(fmt, w, x, N, K, M, y, s);
+    if (!emit && gemv_reg_supported(fmt, mode, M, N, K)) return launch_gemv_reg(fmt, mode, w, x, N, K, M, y, s, nullptr);
     const GemvGeom g = gemv_geom(fmt, mode, N, K, M, emit);
     if (g.grid <= 0) return hipErrorInvalidConfiguration;
     GemvArgs a{};

@@ -1,5 +1,6 @@
-// qmm_gemv_reg.hip -- decode with two to eight f32 activation rows (mode (a))
-// for Q8_0, Q4_K, Q4_0, Q5_0 and Q6_K weights, the activation operand held in
+// qmm_gemv_reg.hip -- decode with two to eight activation rows for Q8_0, Q4_K,
+// Q4_0, Q5_0 and Q6_K weights (mode (a); mode (b) for the formats whose
+// activations are quantized per 32 values), the activation operand held in
 // registers.
 //
 // The pages' decode step streams every weight once per token (page "同一个
@@ -30,6 +31,15 @@
 // Operand lanes n and n + 8 of a 16-lane row need the same eight x values
 // (hi for rows 0..7, lo for rows 8..15): each loads four, splits them, and the
 // pair trades the half the other needs with one DPP row rotation.
+//
+// Mode (b) (Q8_0, Q4_0, Q5_0 weights: the activation rows quantized to Q8_0,
+// page "同一个 GGUF，CPU 和 Metal 生成的文字不一样", section 出处): each wave quantizes
+// the blocks of its slice in registers with the standalone quantizer's device
+// functions (a block's 32 values sit in eight lanes, whose maximum meets in
+// three lane exchanges), A rows 0..7 take the int8 values as exact f16 (rows
+// 8..15 zero), so the matrix core's f32 sum of a block is the exact integer
+// block sum S, and acc += S (d_w d_x).  The traced instances also write S and
+// the quantized activation blocks.
 #include <mutex>
 #include <set>
 #include <type_traits>
@@ -49,7 +59,9 @@ struct GemvRegArgs {
     int tiles;  // 16-row tiles
     int T;      // tiles per workgroup
     const float* x;
-    float* y;
+    float* y;        // may be null in a traced run
+    int32_t* sums;   // traced mode (b): [M][N][K/32] integer block sums
+    uint8_t* act;    // traced mode (b): the quantized activations as canonical Q8_0 blocks [M][K/32], or null
 };
 
 constexpr int GR_PART_BYTES = 2 * GV_WAVES * 128 * 4;  // tile partials, two slots: [slot][wave][8 rows][16]
@@ -64,7 +76,7 @@ constexpr int gr_lub(int fmt)
 constexpr int gr_vpl(int fmt) { return fmt == FMT_Q4_K ? 256 : fmt == FMT_Q6_K ? 512 : 64; }
 
 // U: load units per wave slice (K <= 8 U units), P: units per stage, D: ring depth.
-template <int FMT, int U, int P, int D>
+template <int FMT, int MODE, int U, int P, int D>
 struct GrCfg {
     static constexpr int LUB = gr_lub(FMT);
     static constexpr int STEPS = gr_vpl(FMT) / 32;           // matrix-core steps (32 values) per unit
@@ -72,9 +84,13 @@ struct GrCfg {
     static constexpr int SBY = 16 * 16 * CPR;               // one stage buffer (16 rows, unpadded)
     static constexpr int TL = (16 * CPR + 63) / 64;         // load instructions per stage
     static constexpr int SUMS = FMT == FMT_Q4_K ? U * 8 * 8 * 4 : 0;  // per wave: x*2^e sums [U*8 sub-blocks][8 rows]
+    static constexpr int DXB = MODE == MODE_B ? U * STEPS * 8 * 4 : 0;  // per wave, mode (b): d_x [block][8 rows]
     static constexpr int OFF_PART = GV_WAVES * D * SBY;
     static constexpr int OFF_SUMS = OFF_PART + GR_PART_BYTES;
-    static constexpr int LDS = OFF_SUMS + GV_WAVES * SUMS;
+    static constexpr int OFF_DX = OFF_SUMS + GV_WAVES * SUMS;
+    static constexpr int LDS = OFF_DX + GV_WAVES * DXB;
+    static_assert(MODE == MODE_A || FMT == FMT_Q8_0 || FMT == FMT_Q4_0 || FMT == FMT_Q5_0,
+                  "mode (b) here: the formats with Q8_0 activations");
     // an odd chunk count puts the 16 rows of a stage in different LDS banks
     static_assert(U % P == 0 && (CPR & 1) == 1 && D >= 2 && (D - 1) * TL <= 63, "ring of LDS-direct stages");
     static_assert(LDS <= GV_LDS_MAX, "LDS of a compute unit");
@@ -101,10 +117,11 @@ QMM_DEV half8_t u8x8_to_f16(uint32_t d0, uint32_t d1)
     return r;
 }
 
-template <int FMT, int U, int P, int D>
+template <int FMT, int MODE, int U, int P, int D, bool EMIT>
 __global__ __launch_bounds__(GV_THREADS, 2) void gemv_reg_kernel(GemvRegArgs a)
 {
-    using C = GrCfg<FMT, U, P, D>;
+    static_assert(!EMIT || MODE == MODE_B, "integer block sums exist in mode (b) only");
+    using C = GrCfg<FMT, MODE, U, P, D>;
     constexpr int LUB = C::LUB, STEPS = C::STEPS, CPR = C::CPR, SBY = C::SBY, TL = C::TL;
     constexpr int S = U / P;  // stages per tile
     static_assert(S == 1 || S == 2, "one or two stages per tile");
@@ -126,6 +143,7 @@ __global__ __launch_bounds__(GV_THREADS, 2) void gemv_reg_kernel(GemvRegArgs a)
     uint8_t* ring = lds + wave * (D * SBY);
     float* part = reinterpret_cast<float*>(lds + C::OFF_PART);
     float* sums = reinterpret_cast<float*>(lds + C::OFF_SUMS + wave * C::SUMS);
+    float* dxs = reinterpret_cast<float*>(lds + C::OFF_DX + wave * C::DXB);
 
     // ---- the weight stream: chunk f = 64t + lane of a stage is row f/CPR, chunk f%CPR ----
     uint32_t go[TL];
@@ -181,16 +199,28 @@ __global__ __launch_bounds__(GV_THREADS, 2) void gemv_reg_kernel(GemvRegArgs a)
     for (int i = 0; i < U * STEPS; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) xv[i][e] = __int_as_float(__builtin_amdgcn_ds_bpermute(src4, (int)xt[i][e]));
-    // the row maximum over the slice: lanes n, n + 8 of every 16-lane row hold row n % 8
+    // mode (a): the row maximum over the slice; mode (b): each block's maximum |x|
+    // (lanes n, n + 8 of every 16-lane row hold row n % 8)
     float mx = 0.0f;
+    float bam[MODE == MODE_B ? U * STEPS : 1];
+    if constexpr (MODE == MODE_A) {
 #pragma unroll
-    for (int i = 0; i < U * STEPS; ++i)
+        for (int i = 0; i < U * STEPS; ++i)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fabsf(xv[i][e]));
-    mx = fmaxf(mx, __uint_as_float(ror8(__float_as_uint(mx))));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const int ex = split_exp(mx);
+            for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fabsf(xv[i][e]));
+        mx = fmaxf(mx, __uint_as_float(ror8(__float_as_uint(mx))));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+    } else {
+#pragma unroll
+        for (int i = 0; i < U * STEPS; ++i) {
+            float t = fmaxf(fmaxf(fabsf(xv[i][0]), fabsf(xv[i][1])), fmaxf(fabsf(xv[i][2]), fabsf(xv[i][3])));
+            t = fmaxf(t, __uint_as_float(ror8(__float_as_uint(t))));
+            t = fmaxf(t, __shfl_xor(t, 16));
+            bam[i] = fmaxf(t, __shfl_xor(t, 32));
+        }
+    }
+    const int ex = MODE == MODE_A ? split_exp(mx) : 0;
     const float sc = ldexpf(1.0f, ex);
     // (every activation load has been waited for above; the ring loads below are
     // not tracked by the compiler and must not be moved ahead of that wait)
@@ -202,11 +232,34 @@ __global__ __launch_bounds__(GV_THREADS, 2) void gemv_reg_kernel(GemvRegArgs a)
         if (iq < Q) issue(i);
 
     half8_t areg[U][STEPS];
+    const bool emit_act = EMIT && blockIdx.x == 0 && a.act != nullptr && r8 < M;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
 #pragma unroll
         for (int p = 0; p < STEPS; ++p) {
             const float* v = xv[u * STEPS + p];
+            if constexpr (MODE == MODE_B) {
+                // the block's Q8_0 scale and values (bytes of the standalone quantizer);
+                // lanes n < 8 keep theirs and receive the partner's, lanes n >= 8 are zero rows
+                float id, dval;
+                uint16_t dbits;
+                q8_0_scale(bam[u * STEPS + p], id, dbits, dval);
+                int qv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) qv[e] = q8_0_q(v[e], id);
+                const uint32_t h0 = pack_h2((_Float16)qv[0], (_Float16)qv[1]), h1 = pack_h2((_Float16)qv[2], (_Float16)qv[3]);
+                const uint32_t s0 = ror8(h0), s1 = ror8(h1);
+                areg[u][p] = __builtin_bit_cast(half8_t, upper ? u32x4_t{0u, 0u, 0u, 0u} : u32x4_t{h0, h1, s0, s1});
+                if (!upper && g == 0) dxs[(u * STEPS + p) * 8 + n] = dval;
+                if (emit_act && u < ureal) {
+                    // canonical block 2 (u0 + u) + p of row r8: f16 d, then the 32 int8
+                    uint8_t* o = a.act + ((int64_t)r8 * (2 * a.nlu) + 2 * (u0 + u) + p) * 34;
+                    if (!upper && g == 0) *reinterpret_cast<uint16_t*>(o) = dbits;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[2 + 8 * g + (upper ? 4 : 0) + e] = (uint8_t)qv[e];
+                }
+                continue;
+            }
             _Float16 h[4], l[4];
             float xs[4];
 #pragma unroll
@@ -241,7 +294,7 @@ __global__ __launch_bounds__(GV_THREADS, 2) void gemv_reg_kernel(GemvRegArgs a)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int e0 = __builtin_amdgcn_readlane(ex, q), e1 = __builtin_amdgcn_readlane(ex, 4 + q);
-        rsc[q] = ldexpf(1.0f, -((g & 1) ? e1 : e0));
+        rsc[q] = MODE == MODE_A ? ldexpf(1.0f, -((g & 1) ? e1 : e0)) : 1.0f;
     }
 
     // ---- main loop ----
@@ -251,7 +304,34 @@ __global__ __launch_bounds__(GV_THREADS, 2) void gemv_reg_kernel(GemvRegArgs a)
     asm volatile("" : "+v"(nibm), "+v"(nibc));
     const bool lo_lane = g >= 2;  // output rows 8..15: the lo parts (no mins term there)
 
-    auto compute = [&](const uint8_t* sbuf, auto sc_) {
+    // a block pair's two matrix-core sums (block 2 (u0 + u) and the next) into acc:
+    // mode (a) times the weight scales; mode (b) the exact integer sums times d_w d_x
+    auto pair_epi = [&](const f32x4_t& Ce, const f32x4_t& Co, float de, float dd, int u, int tile) {
+        if constexpr (MODE == MODE_A) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[q] = fmaf(Co[q], dd, fmaf(Ce[q], de, acc[q]));
+        } else {
+            const f32x4_t xe = *reinterpret_cast<const f32x4_t*>(dxs + (u * 2) * 8 + 4 * (g & 1));
+            const f32x4_t xo = *reinterpret_cast<const f32x4_t*>(dxs + (u * 2 + 1) * 8 + 4 * (g & 1));
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[q] = fmaf(Co[q], dd * xo[q], fmaf(Ce[q], de * xe[q], acc[q]));
+            if constexpr (EMIT) {
+                const int ng = tile * 16 + n;
+                if (g < 2 && ng < N) {
+                    int32_t* o = a.sums + ((int64_t)(4 * g) * N + ng) * (2 * a.nlu) + 2 * (u0 + u);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        if (4 * g + q < M) {
+                            o[(int64_t)q * N * (2 * a.nlu)] = (int32_t)Ce[q];
+                            o[(int64_t)q * N * (2 * a.nlu) + 1] = (int32_t)Co[q];
+                        }
+                    }
+                }
+            }
+        }
+    };
+
+    auto compute = [&](const uint8_t* sbuf, auto sc_, int tile) {
         constexpr int s = decltype(sc_)::value;
         const uint8_t* rrow = sbuf + n * (16 * CPR);
 #pragma unroll
@@ -269,9 +349,7 @@ __global__ __launch_bounds__(GV_THREADS, 2) void gemv_reg_kernel(GemvRegArgs a)
                 const half8_t Bo = i8x8_to_f16(lds32(xo), lds32(xo + 4));
                 const f32x4_t Ce = __builtin_amdgcn_mfma_f32_16x16x32_f16(areg[s * P + j][0], Be, zf, 0, 0, 0);
                 const f32x4_t Co = __builtin_amdgcn_mfma_f32_16x16x32_f16(areg[s * P + j][1], Bo, zf, 0, 0, 0);
-                const float de = f16lo(E0), dd = f16hi(E8);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) acc[q] = fmaf(Co[q], dd, fmaf(Ce[q], de, acc[q]));
+                pair_epi(Ce, Co, f16lo(E0), f16hi(E8), s * P + j, tile);
             } else if constexpr (FMT == FMT_Q4_0 || FMT == FMT_Q5_0) {
                 // pair of blocks: Q4_0 d | qs[16], Q5_0 d | qh[4] | qs[16], twice.  k-group g
                 // takes the low (g < 2) or high nibbles of qs bytes 8 (g & 1) .. +7, Q5_0
@@ -294,9 +372,7 @@ __global__ __launch_bounds__(GV_THREADS, 2) void gemv_reg_kernel(GemvRegArgs a)
                 const half8_t Be = u8x8_to_f16<OFF>(ce0, ce1), Bo = u8x8_to_f16<OFF>(co0, co1);
                 const f32x4_t Ce = __builtin_amdgcn_mfma_f32_16x16x32_f16(areg[s * P + j][0], Be, zf, 0, 0, 0);
                 const f32x4_t Co = __builtin_amdgcn_mfma_f32_16x16x32_f16(areg[s * P + j][1], Bo, zf, 0, 0, 0);
-                const float de = f16lo(lds32(rp)), dd = f16hi(lds32(rp + HALF - 2));
-#pragma unroll
-                for (int q = 0; q < 4; ++q) acc[q] = fmaf(Co[q], dd, fmaf(Ce[q], de, acc[q]));
+                pair_epi(Ce, Co, f16lo(lds32(rp)), f16hi(lds32(rp + HALF - 2)), s * P + j, tile);
             } else if constexpr (FMT == FMT_Q6_K) {
                 // two super-blocks of ql[128] | qh[64] | sc[16] (int8) | d (f16), the second
                 // two bytes into a dword.  Step p (32 values) of one: half h = p / 4, quarter
@@ -372,7 +448,7 @@ __global__ __launch_bounds__(GV_THREADS, 2) void gemv_reg_kernel(GemvRegArgs a)
             constexpr int s = decltype(sc_)::value;
             const int q = tt * S + s;
             vm_wait_ahead<TL, D - 1>(min(D - 1, Q - 1 - q));  // stage q has landed
-            if (s < sreal) compute(ring + slot * SBY, sc_);
+            if (s < sreal) compute(ring + slot * SBY, sc_, t0 + tt);
             if (iq < Q) {
                 lgkm_wait0();  // this buffer's reads are done before it is refilled
                 issue(slot);
@@ -401,18 +477,18 @@ __global__ __launch_bounds__(GV_THREADS, 2) void gemv_reg_kernel(GemvRegArgs a)
             float v = 0.0f;
 #pragma unroll
             for (int w = 0; w < GV_WAVES; ++w) v += pp[w * 128];
-            if (m < M && ng < N) a.y[(int64_t)m * N + ng] = v;
+            if (m < M && ng < N && a.y) a.y[(int64_t)m * N + ng] = v;
         }
     }
 }
 
 typedef void (*GrKernel)(GemvRegArgs);
 
-template <int FMT, int U, int P, int D>
+template <int FMT, int MODE, int U, int P, int D, bool EMIT>
 static hipError_t gr_launch(const GemvRegArgs& a, int grid, hipStream_t s)
 {
-    using C = GrCfg<FMT, U, P, D>;
-    GrKernel k = gemv_reg_kernel<FMT, U, P, D>;
+    using C = GrCfg<FMT, MODE, U, P, D>;
+    GrKernel k = gemv_reg_kernel<FMT, MODE, U, P, D, EMIT>;
     static std::set<std::pair<int, const void*>> done;
     static std::mutex mu;
     int dev = 0;
@@ -443,7 +519,10 @@ static int gr_units(int fmt, int64_t K)
 
 bool gemv_reg_supported(int fmt, int mode, int M, int64_t N, int64_t K)
 {
-    if (mode != MODE_A || M < 2 || M > GEMV_MAX_M || N < 1) return false;
+    if (M < 2 || M > GEMV_MAX_M || N < 1) return false;
+    // mode (b): Q4_0 and Q5_0 (Q8_0 runs its integer tile kernel)
+    if (mode == MODE_B) { if (fmt != FMT_Q4_0 && fmt != FMT_Q5_0) return false; }
+    else if (mode != MODE_A) return false;
     if (fmt == FMT_Q8_0 || fmt == FMT_Q4_0 || fmt == FMT_Q5_0) { if (K % 64 != 0) return false; }
     else if (fmt == FMT_Q4_K) { if (K % 256 != 0) return false; }
     else if (fmt == FMT_Q6_K) { if (K % 512 != 0) return false; }  // super-block pairs: 4-byte-aligned rows
@@ -451,9 +530,28 @@ bool gemv_reg_supported(int fmt, int mode, int M, int64_t N, int64_t K)
     return gr_units(fmt, K) > 0 && (int64_t)M * K * 4 <= 0xffffffffll;
 }
 
-hipError_t launch_gemv_reg(int fmt, const void* w, const float* x, int64_t N, int64_t K, int M, float* y, hipStream_t s)
+// The instances of the 32-value formats: stages of four block pairs where the
+// slice has them (two or one below), and for Q5_0 one pair where two would be an
+// even chunk count.
+template <int FMT, int MODE, bool EMIT>
+static hipError_t gr_launch_pairs(int U, const GemvRegArgs& a, int grid, hipStream_t s)
 {
-    if (!gemv_reg_supported(fmt, MODE_A, M, N, K)) return hipErrorInvalidValue;
+    if (U == 8) return gr_launch<FMT, MODE, 8, 4, 4, EMIT>(a, grid, s);
+    if (U == 4) return gr_launch<FMT, MODE, 4, 4, 4, EMIT>(a, grid, s);
+    if (U == 2) return gr_launch<FMT, MODE, 2, (FMT == FMT_Q5_0 ? 1 : 2), 4, EMIT>(a, grid, s);
+    return gr_launch<FMT, MODE, 1, 1, 4, EMIT>(a, grid, s);
+}
+
+template <int FMT>
+static hipError_t gr_launch_b(int U, bool emit, const GemvRegArgs& a, int grid, hipStream_t s)
+{
+    return emit ? gr_launch_pairs<FMT, MODE_B, true>(U, a, grid, s) : gr_launch_pairs<FMT, MODE_B, false>(U, a, grid, s);
+}
+
+hipError_t launch_gemv_reg(int fmt, int mode, const void* w, const float* x, int64_t N, int64_t K, int M, float* y,
+                           hipStream_t s, const Trace* tr)
+{
+    if (!gemv_reg_supported(fmt, mode, M, N, K) || (tr && mode != MODE_B)) return hipErrorInvalidValue;
     GemvRegArgs a{};
     a.w = (const uint8_t*)w;
     a.nlu = (int)(K / gr_vpl(fmt));
@@ -468,28 +566,19 @@ hipError_t launch_gemv_reg(int fmt, const void* w, const float* x, int64_t N, in
     const int grid = (a.tiles + a.T - 1) / a.T;
     a.x = x;
     a.y = y;
+    a.sums = tr ? tr->sums : nullptr;
+    a.act = tr ? tr->act : nullptr;
     const int U = gr_units(fmt, K);
-    if (fmt == FMT_Q8_0) {
-        if (U == 8) return gr_launch<FMT_Q8_0, 8, 4, 4>(a, grid, s);
-        if (U == 4) return gr_launch<FMT_Q8_0, 4, 4, 4>(a, grid, s);
-        if (U == 2) return gr_launch<FMT_Q8_0, 2, 2, 4>(a, grid, s);
-        return gr_launch<FMT_Q8_0, 1, 1, 4>(a, grid, s);
+    if (mode == MODE_B) {
+        if (fmt == FMT_Q4_0) return gr_launch_b<FMT_Q4_0>(U, tr != nullptr, a, grid, s);
+        return gr_launch_b<FMT_Q5_0>(U, tr != nullptr, a, grid, s);
     }
-    if (fmt == FMT_Q4_0) {
-        if (U == 8) return gr_launch<FMT_Q4_0, 8, 4, 4>(a, grid, s);
-        if (U == 4) return gr_launch<FMT_Q4_0, 4, 4, 4>(a, grid, s);
-        if (U == 2) return gr_launch<FMT_Q4_0, 2, 2, 4>(a, grid, s);
-        return gr_launch<FMT_Q4_0, 1, 1, 4>(a, grid, s);
-    }
-    if (fmt == FMT_Q5_0) {  // two pairs are 88 bytes: an even chunk count, so stages of one pair there
-        if (U == 8) return gr_launch<FMT_Q5_0, 8, 4, 4>(a, grid, s);
-        if (U == 4) return gr_launch<FMT_Q5_0, 4, 4, 4>(a, grid, s);
-        if (U == 2) return gr_launch<FMT_Q5_0, 2, 1, 4>(a, grid, s);
-        return gr_launch<FMT_Q5_0, 1, 1, 4>(a, grid, s);
-    }
-    if (fmt == FMT_Q6_K) return gr_launch<FMT_Q6_K, 1, 1, 2>(a, grid, s);  // 432-byte stage rows: two fit
-    if (U == 2) return gr_launch<FMT_Q4_K, 2, 1, 4>(a, grid, s);
-    return gr_launch<FMT_Q4_K, 1, 1, 4>(a, grid, s);
+    if (fmt == FMT_Q8_0) return gr_launch_pairs<FMT_Q8_0, MODE_A, false>(U, a, grid, s);
+    if (fmt == FMT_Q4_0) return gr_launch_pairs<FMT_Q4_0, MODE_A, false>(U, a, grid, s);
+    if (fmt == FMT_Q5_0) return gr_launch_pairs<FMT_Q5_0, MODE_A, false>(U, a, grid, s);
+    if (fmt == FMT_Q6_K) return gr_launch<FMT_Q6_K, MODE_A, 1, 1, 2, false>(a, grid, s);  // 432-byte stage rows: two fit
+    if (U == 2) return gr_launch<FMT_Q4_K, MODE_A, 2, 1, 4, false>(a, grid, s);
+    return gr_launch<FMT_Q4_K, MODE_A, 1, 1, 4, false>(a, grid, s);
 }
 
 }  // namespace qmm

@@ -77,7 +77,8 @@ hipError_t launch_quantize_q4_k_search(const float* w, int64_t N, int64_t K, voi
 // Decode with 2..8 f32 activation rows (mode (a), Q8_0 and Q4_K, K <= 4096):
 // the activation operand in registers, K split over the eight waves.
 bool gemv_reg_supported(int fmt, int mode, int M, int64_t N, int64_t K);
-hipError_t launch_gemv_reg(int fmt, const void* w, const float* x, int64_t N, int64_t K, int M, float* y, hipStream_t s);
+hipError_t launch_gemv_reg(int fmt, int mode, const void* w, const float* x, int64_t N, int64_t K, int M, float* y,
+                           hipStream_t s, const Trace* tr);
 
 hipError_t launch_gemv(int fmt, int mode, const void* w, const float* x, int64_t N, int64_t K, int M,
                        const GemvBufs& b, float* y, hipStream_t s, const Trace* tr = nullptr);
