@@ -1,7 +1,6 @@
 // qmm_gemv_reg.hip -- decode with two to eight activation rows for Q8_0, Q4_K,
-// Q4_0, Q5_0 and Q6_K weights (mode (a); mode (b) for the formats whose
-// activations are quantized per 32 values), the activation operand held in
-// registers.
+// Q4_0, Q5_0 and Q6_K weights (mode (a); mode (b) for Q4_0, Q5_0 and Q6_K),
+// the activation operand held in registers.
 //
 // The pages' decode step streams every weight once per token (page "同一个
 // GGUF，CPU 和 Metal 生成的文字不一样", section 修法: the CPU decode is bound by
@@ -32,14 +31,17 @@
 // (hi for rows 0..7, lo for rows 8..15): each loads four, splits them, and the
 // pair trades the half the other needs with one DPP row rotation.
 //
-// Mode (b) (Q8_0, Q4_0, Q5_0 weights: the activation rows quantized to Q8_0,
-// page "同一个 GGUF，CPU 和 Metal 生成的文字不一样", section 出处): each wave quantizes
-// the blocks of its slice in registers with the standalone quantizer's device
-// functions (a block's 32 values sit in eight lanes, whose maximum meets in
-// three lane exchanges), A rows 0..7 take the int8 values as exact f16 (rows
-// 8..15 zero), so the matrix core's f32 sum of a block is the exact integer
-// block sum S, and acc += S (d_w d_x).  The traced instances also write S and
-// the quantized activation blocks.
+// Mode (b) (page "同一个 GGUF，CPU 和 Metal 生成的文字不一样", section 出处: the
+// activation rows quantized to Q8_0 for the 32-value formats, to Q8K for Q6_K):
+// each wave quantizes the blocks of its slice in registers with the standalone
+// quantizer's device functions (a 32-value block sits in eight lanes, whose
+// maximum meets in three lane exchanges; a Q8K block in the same eight lanes
+// over eight steps, the first element of largest magnitude found with its
+// index), A rows 0..7 take the int8 values as exact f16 (rows 8..15 zero), so
+// the matrix core's f32 sums are exact integers: S per block, Q6_K's two
+// scale-split sums per super-block (sumi = 16 Ch + Cl); acc += S (d_w d_x).
+// The traced instances also write the integer parts and the quantized
+// activation blocks (Q6_K's per-16 sums from two more matrix-core steps).
 #include <mutex>
 #include <set>
 #include <type_traits>
@@ -89,8 +91,8 @@ struct GrCfg {
     static constexpr int OFF_SUMS = OFF_PART + GR_PART_BYTES;
     static constexpr int OFF_DX = OFF_SUMS + GV_WAVES * SUMS;
     static constexpr int LDS = OFF_DX + GV_WAVES * DXB;
-    static_assert(MODE == MODE_A || FMT == FMT_Q8_0 || FMT == FMT_Q4_0 || FMT == FMT_Q5_0,
-                  "mode (b) here: the formats with Q8_0 activations");
+    static_assert(MODE == MODE_A || FMT == FMT_Q8_0 || FMT == FMT_Q4_0 || FMT == FMT_Q5_0 || FMT == FMT_Q6_K,
+                  "mode (b) here: the formats with Q8_0 activations, and Q6_K");
     // an odd chunk count puts the 16 rows of a stage in different LDS banks
     static_assert(U % P == 0 && (CPR & 1) == 1 && D >= 2 && (D - 1) * TL <= 63, "ring of LDS-direct stages");
     static_assert(LDS <= GV_LDS_MAX, "LDS of a compute unit");
@@ -211,13 +213,43 @@ __global__ __launch_bounds__(GV_THREADS, 2) void gemv_reg_kernel(GemvRegArgs a)
         mx = fmaxf(mx, __uint_as_float(ror8(__float_as_uint(mx))));
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-    } else {
+    } else if constexpr (FMT != FMT_Q6_K) {
 #pragma unroll
         for (int i = 0; i < U * STEPS; ++i) {
             float t = fmaxf(fmaxf(fabsf(xv[i][0]), fabsf(xv[i][1])), fmaxf(fabsf(xv[i][2]), fabsf(xv[i][3])));
             t = fmaxf(t, __uint_as_float(ror8(__float_as_uint(t))));
             t = fmaxf(t, __shfl_xor(t, 16));
             bam[i] = fmaxf(t, __shfl_xor(t, 32));
+        }
+    }
+    // mode (b), Q6_K: the Q8K scale of each super-block of x (eight steps): the
+    // signed element of largest |x|, the first index on ties; lane (n, g) holds
+    // elements 32 p + 8 g + 4 (n >= 8) + e of the block, in index order within the lane
+    constexpr int NQK = MODE == MODE_B && FMT == FMT_Q6_K ? U * STEPS / 8 : 1;
+    float kis[NQK];
+    if constexpr (MODE == MODE_B && FMT == FMT_Q6_K) {
+#pragma unroll
+        for (int b = 0; b < NQK; ++b) {
+            float best = -1.0f, bv = 0.0f;
+            int bidx = 0;
+#pragma unroll
+            for (int p = 0; p < 8; ++p)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float v = xv[8 * b + p][e];
+                    if (fabsf(v) > best) { best = fabsf(v); bv = v; bidx = 32 * p + 8 * g + (upper ? 4 : 0) + e; }
+                }
+            auto meet = [&](float ob, float obv, int oidx) {
+                if (ob > best || (ob == best && oidx < bidx)) { best = ob; bv = obv; bidx = oidx; }
+            };
+            meet(__uint_as_float(ror8(__float_as_uint(best))), __uint_as_float(ror8(__float_as_uint(bv))), (int)ror8((uint32_t)bidx));
+            meet(__shfl_xor(best, 16), __shfl_xor(bv, 16), __shfl_xor(bidx, 16));
+            meet(__shfl_xor(best, 32), __shfl_xor(bv, 32), __shfl_xor(bidx, 32));
+            float d;
+            q8k_scale(bv, best, kis[b], d);
+            if (!upper && g == 0) dxs[b * 8 + n] = d;
+            if (EMIT && blockIdx.x == 0 && a.act != nullptr && r8 < M && (b >> 1) < ureal && !upper && g == 0)
+                *reinterpret_cast<float*>(a.act + ((int64_t)r8 * (K / 256) + 2 * u0 + b) * 292) = d;
         }
     }
     const int ex = MODE == MODE_A ? split_exp(mx) : 0;
@@ -241,10 +273,30 @@ __global__ __launch_bounds__(GV_THREADS, 2) void gemv_reg_kernel(GemvRegArgs a)
             if constexpr (MODE == MODE_B) {
                 // the block's Q8_0 scale and values (bytes of the standalone quantizer);
                 // lanes n < 8 keep theirs and receive the partner's, lanes n >= 8 are zero rows
+                int qv[4];
+                if constexpr (FMT == FMT_Q6_K) {
+                    const int b = (u * STEPS + p) >> 3, pp = p & 7;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) qv[e] = q8k_q(v[e], kis[b]);
+                    const uint32_t h0 = pack_h2((_Float16)qv[0], (_Float16)qv[1]), h1 = pack_h2((_Float16)qv[2], (_Float16)qv[3]);
+                    const uint32_t s0 = ror8(h0), s1 = ror8(h1);
+                    areg[u][p] = __builtin_bit_cast(half8_t, upper ? u32x4_t{0u, 0u, 0u, 0u} : u32x4_t{h0, h1, s0, s1});
+                    if (emit_act && u < ureal) {
+                        // canonical Q8K block 2 (u0 + u) + (p / 8) of row r8: f32 d, 256 int8,
+                        // int16 sums of each 16 values (the pair of k-groups g, g ^ 1)
+                        uint8_t* o = a.act + ((int64_t)r8 * (K / 256) + 2 * u0 + b) * 292;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) o[4 + 32 * pp + 8 * g + (upper ? 4 : 0) + e] = (uint8_t)qv[e];
+                        int s16 = (qv[0] + qv[1]) + (qv[2] + qv[3]);
+                        s16 += (int)ror8((uint32_t)s16);
+                        s16 += __shfl_xor(s16, 16);
+                        if (!upper && (g & 1) == 0) reinterpret_cast<int16_t*>(o + 260)[2 * pp + (g >> 1)] = (int16_t)s16;
+                    }
+                    continue;
+                }
                 float id, dval;
                 uint16_t dbits;
                 q8_0_scale(bam[u * STEPS + p], id, dbits, dval);
-                int qv[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) qv[e] = q8_0_q(v[e], id);
                 const uint32_t h0 = pack_h2((_Float16)qv[0], (_Float16)qv[1]), h1 = pack_h2((_Float16)qv[2], (_Float16)qv[3]);
@@ -411,10 +463,44 @@ __global__ __launch_bounds__(GV_THREADS, 2) void gemv_reg_kernel(GemvRegArgs a)
                         const half8_t shv = {fh, fh, fh, fh, fh, fh, fh, fh}, slv = {fl, fl, fl, fl, fl, fl, fl, fl};
                         Ch = __builtin_amdgcn_mfma_f32_16x16x32_f16(areg[s * P + j][8 * b + p], B * shv, Ch, 0, 0, 0);
                         Cl = __builtin_amdgcn_mfma_f32_16x16x32_f16(areg[s * P + j][8 * b + p], B * slv, Cl, 0, 0, 0);
+                        if constexpr (EMIT) {
+                            // the per-16 sums S_2p, S_2p+1 (weights q - 32): k-groups 0, 1 and 2, 3
+                            const half8_t zh = {};
+                            const f32x4_t S0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(areg[s * P + j][8 * b + p], g < 2 ? B : zh, zf, 0, 0, 0);
+                            const f32x4_t S1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(areg[s * P + j][8 * b + p], g < 2 ? zh : B, zf, 0, 0, 0);
+                            const int ng = tile * 16 + n, sbk = 2 * (u0 + s * P + j) + b;
+                            if (g < 2 && ng < N) {
+#pragma unroll
+                                for (int q = 0; q < 4; ++q) {
+                                    if (4 * g + q < M) {
+                                        int32_t* o = a.sums + ((int64_t)(4 * g + q) * N + ng) * (17 * (K / 256)) + 17 * sbk + 2 * p;
+                                        o[0] = (int32_t)S0[q];
+                                        o[1] = (int32_t)S1[q];
+                                    }
+                                }
+                            }
+                        }
                     }
                     const float d = b == 0 ? f16lo(lds32(rp + 208)) : f16hi(lds32(rp + 416));
+                    if constexpr (MODE == MODE_A) {
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) acc[q] = fmaf(fmaf(16.0f, Ch[q], Cl[q]), d, acc[q]);
+                        for (int q = 0; q < 4; ++q) acc[q] = fmaf(fmaf(16.0f, Ch[q], Cl[q]), d, acc[q]);
+                    } else {
+                        // sumi = 16 Ch + Cl, both exact integers; d_x of the super-block's rows
+                        const f32x4_t dx = *reinterpret_cast<const f32x4_t*>(dxs + (2 * (s * P + j) + b) * 8 + 4 * (g & 1));
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) acc[q] = fmaf(fmaf(16.0f, Ch[q], Cl[q]), d * dx[q], acc[q]);
+                        if constexpr (EMIT) {
+                            const int ng = tile * 16 + n, sbk = 2 * (u0 + s * P + j) + b;
+                            if (g < 2 && ng < N) {
+#pragma unroll
+                                for (int q = 0; q < 4; ++q)
+                                    if (4 * g + q < M)
+                                        a.sums[((int64_t)(4 * g + q) * N + ng) * (17 * (K / 256)) + 17 * sbk + 16] =
+                                            16 * (int32_t)Ch[q] + (int32_t)Cl[q];
+                            }
+                        }
+                    }
                 }
             } else {
                 const u32x4_t H = lds128(rp);
@@ -520,8 +606,8 @@ static int gr_units(int fmt, int64_t K)
 bool gemv_reg_supported(int fmt, int mode, int M, int64_t N, int64_t K)
 {
     if (M < 2 || M > GEMV_MAX_M || N < 1) return false;
-    // mode (b): Q4_0 and Q5_0 (Q8_0 runs its integer tile kernel)
-    if (mode == MODE_B) { if (fmt != FMT_Q4_0 && fmt != FMT_Q5_0) return false; }
+    // mode (b): Q4_0, Q5_0, Q6_K (Q8_0 and Q4_K run their integer tile kernel)
+    if (mode == MODE_B) { if (fmt != FMT_Q4_0 && fmt != FMT_Q5_0 && fmt != FMT_Q6_K) return false; }
     else if (mode != MODE_A) return false;
     if (fmt == FMT_Q8_0 || fmt == FMT_Q4_0 || fmt == FMT_Q5_0) { if (K % 64 != 0) return false; }
     else if (fmt == FMT_Q4_K) { if (K % 256 != 0) return false; }
@@ -571,7 +657,8 @@ hipError_t launch_gemv_reg(int fmt, int mode, const void* w, const float* x, int
     const int U = gr_units(fmt, K);
     if (mode == MODE_B) {
         if (fmt == FMT_Q4_0) return gr_launch_b<FMT_Q4_0>(U, tr != nullptr, a, grid, s);
-        return gr_launch_b<FMT_Q5_0>(U, tr != nullptr, a, grid, s);
+        if (fmt == FMT_Q5_0) return gr_launch_b<FMT_Q5_0>(U, tr != nullptr, a, grid, s);
+        return tr ? gr_launch<FMT_Q6_K, MODE_B, 1, 1, 2, true>(a, grid, s) : gr_launch<FMT_Q6_K, MODE_B, 1, 1, 2, false>(a, grid, s);
     }
     if (fmt == FMT_Q8_0) return gr_launch_pairs<FMT_Q8_0, MODE_A, false>(U, a, grid, s);
     if (fmt == FMT_Q4_0) return gr_launch_pairs<FMT_Q4_0, MODE_A, false>(U, a, grid, s);
