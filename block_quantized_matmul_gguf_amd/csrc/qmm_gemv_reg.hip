@@ -341,6 +341,23 @@ __global__ __launch_bounds__(GV_THREADS, 2) void gemv_reg_kernel(GemvRegArgs a)
             }
         }
     }
+    // Q4_K: the A operand of the mins term per super-block: rows 0..7 carry the
+    // eight sub-block sums of x*2^e of their activation row, divided by 32 (below
+    // 2^15: f16-safe) and split into f16 hi (k 0..7) and lo (k 8..15); rows 8..15 zero
+    half8_t amin[FMT == FMT_Q4_K ? U : 1];
+    if constexpr (FMT == FMT_Q4_K) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            half8_t v;
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                const float t = (!upper && g < 2) ? sums[(u * 8 + jj) * 8 + r8] * 0.03125f : 0.0f;
+                const _Float16 hi = (_Float16)t;
+                v[jj] = g == 0 ? hi : (_Float16)(t - (float)hi);
+            }
+            amin[u] = v;
+        }
+    }
     // 2^-e of this lane's four output rows 4 (g & 1) + q (row r's exponent sits in lane r)
     float rsc[4];
 #pragma unroll
@@ -354,7 +371,6 @@ __global__ __launch_bounds__(GV_THREADS, 2) void gemv_reg_kernel(GemvRegArgs a)
     const f32x4_t zf = {0.0f, 0.0f, 0.0f, 0.0f};
     uint32_t nibm = 0x000f000fu, nibc = 0x64006400u;           // Q4_K nibble decode constants
     asm volatile("" : "+v"(nibm), "+v"(nibc));
-    const bool lo_lane = g >= 2;  // output rows 8..15: the lo parts (no mins term there)
 
     // a block pair's two matrix-core sums (block 2 (u0 + u) and the next) into acc:
     // mode (a) times the weight scales; mode (b) the exact integer sums times d_w d_x
@@ -508,22 +524,34 @@ __global__ __launch_bounds__(GV_THREADS, 2) void gemv_reg_kernel(GemvRegArgs a)
                 const uint32_t s0 = H[1], s1 = H[2], s2 = H[3];
                 const uint32_t sc4[2] = {s0 & 0x3f3f3f3fu, (s2 & 0x0f0f0f0fu) | ((s0 >> 2) & 0x30303030u)};
                 const uint32_t mn4[2] = {s1 & 0x3f3f3f3fu, ((s2 >> 4) & 0x0f0f0f0fu) | ((s1 >> 2) & 0x30303030u)};
-                const float* xsp = sums + (s * P + j) * 64 + 4 * (g & 1);
+                // the weights enter as exact f16 sc_j q (at most 945: one fused multiply-add
+                // on the 1024 + q bit pattern); the super-block's sum stays in the
+                // accumulator.  Mins: one more matrix-core step against the sub-block sums
+                f32x4_t Cs = zf;
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     const u32x2_t Qv = lds64(rp + 16 + 32 * c + 8 * g);
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
                         const int jj = 2 * c + h;
-                        const half8_t B = nib8_to_f16(Qv[0], Qv[1], 4 * h, nibm, nibc);
-                        const f32x4_t Cv = __builtin_amdgcn_mfma_f32_16x16x32_f16(areg[s * P + j][jj], B, zf, 0, 0, 0);
-                        const float dsc = d * (float)((sc4[jj >> 2] >> (8 * (jj & 3))) & 0xffu);
-                        const float dmm = lo_lane ? 0.0f : dmin * (float)((mn4[jj >> 2] >> (8 * (jj & 3))) & 0xffu);
-                        const f32x4_t xs = *reinterpret_cast<const f32x4_t*>(xsp + jj * 8);
+                        const _Float16 sc = (_Float16)(float)((sc4[jj >> 2] >> (8 * (jj & 3))) & 0xffu);
+                        const half2_t s2 = {sc, sc}, o2 = {(_Float16)(-1024.0f) * sc, (_Float16)(-1024.0f) * sc};
+                        const uint32_t w0 = Qv[0] >> (4 * h), w1 = Qv[1] >> (4 * h);
+                        half8_t B;
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) acc[q] = fmaf(-dmm, xs[q], fmaf(Cv[q], dsc, acc[q]));
+                        for (int t = 0; t < 4; ++t) {
+                            const uint32_t src = (t < 2 ? w0 : w1) >> (8 * (t & 1));
+                            const half2_t v = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, (src & nibm) | (nibc & ~nibm)), s2, o2);
+                            B[2 * t] = v[0];
+                            B[2 * t + 1] = v[1];
+                        }
+                        Cs = __builtin_amdgcn_mfma_f32_16x16x32_f16(areg[s * P + j][jj], B, Cs, 0, 0, 0);
                     }
                 }
+                const half8_t Bm0 = u8x8_to_f16<0>(mn4[0], mn4[1]), zh = {};
+                const f32x4_t Cm = __builtin_amdgcn_mfma_f32_16x16x32_f16(amin[s * P + j], g < 2 ? Bm0 : zh, zf, 0, 0, 0);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[q] = fmaf(d, Cs[q], fmaf(-32.0f * dmin, Cm[q], acc[q]));
             }
         }
     };
