@@ -86,7 +86,8 @@ struct GrCfg {
     static constexpr int SBY = 16 * 16 * CPR;               // one stage buffer (16 rows, unpadded)
     static constexpr int TL = (16 * CPR + 63) / 64;         // load instructions per stage
     static constexpr int SUMS = FMT == FMT_Q4_K ? U * 8 * 8 * 4 : 0;  // per wave: x*2^e sums [U*8 sub-blocks][8 rows]
-    static constexpr int DXB = MODE == MODE_B ? U * STEPS * 8 * 4 : 0;  // per wave, mode (b): d_x [block][8 rows]
+    // per wave, mode (b): d_x [block][8 rows]; Q8_0 blocks also 1/d [row][block] and the f16 bits of d
+    static constexpr int DXB = MODE == MODE_B ? U * STEPS * 8 * (FMT == FMT_Q6_K ? 4 : 10) : 0;
     static constexpr int OFF_PART = GV_WAVES * D * SBY;
     static constexpr int OFF_SUMS = OFF_PART + GR_PART_BYTES;
     static constexpr int OFF_DX = OFF_SUMS + GV_WAVES * SUMS;
@@ -221,6 +222,26 @@ __global__ __launch_bounds__(GV_THREADS, 2) void gemv_reg_kernel(GemvRegArgs a)
             t = fmaxf(t, __shfl_xor(t, 16));
             bam[i] = fmaxf(t, __shfl_xor(t, 32));
         }
+        // the block scales, two per lane instead of every lane all of its row's: lane l
+        // takes row l % 8, blocks l / 8 and l / 8 + 8 (its own maxima, picked by index);
+        // 1/d, d and its f16 bits go to LDS for the row's lanes
+        float* ids = dxs + U * STEPS * 8;
+        uint16_t* dbs = reinterpret_cast<uint16_t*>(ids + U * STEPS * 8);
+#pragma unroll
+        for (int k = 0; k < (U * STEPS + 7) / 8; ++k) {
+            const int bi = (lane >> 3) + 8 * k, row = lane & 7;
+            float am = bam[0];
+#pragma unroll
+            for (int i = 1; i < U * STEPS; ++i) am = bi == i ? bam[i] : am;
+            if (bi < U * STEPS) {
+                float id, dval;
+                uint16_t dbits;
+                q8_0_scale(am, id, dbits, dval);
+                ids[row * (U * STEPS) + bi] = id;
+                dxs[bi * 8 + row] = dval;
+                dbs[row * (U * STEPS) + bi] = dbits;
+            }
+        }
     }
     // mode (b), Q6_K: the Q8K scale of each super-block of x (eight steps): the
     // signed element of largest |x|, the first index on ties; lane (n, g) holds
@@ -294,19 +315,18 @@ __global__ __launch_bounds__(GV_THREADS, 2) void gemv_reg_kernel(GemvRegArgs a)
                     }
                     continue;
                 }
-                float id, dval;
-                uint16_t dbits;
-                q8_0_scale(bam[u * STEPS + p], id, dbits, dval);
+                const float* ids = dxs + U * STEPS * 8;
+                const float id = ids[r8 * (U * STEPS) + u * STEPS + p];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) qv[e] = q8_0_q(v[e], id);
                 const uint32_t h0 = pack_h2((_Float16)qv[0], (_Float16)qv[1]), h1 = pack_h2((_Float16)qv[2], (_Float16)qv[3]);
                 const uint32_t s0 = ror8(h0), s1 = ror8(h1);
                 areg[u][p] = __builtin_bit_cast(half8_t, upper ? u32x4_t{0u, 0u, 0u, 0u} : u32x4_t{h0, h1, s0, s1});
-                if (!upper && g == 0) dxs[(u * STEPS + p) * 8 + n] = dval;
                 if (emit_act && u < ureal) {
                     // canonical block 2 (u0 + u) + p of row r8: f16 d, then the 32 int8
+                    const uint16_t* dbs = reinterpret_cast<const uint16_t*>(ids + U * STEPS * 8);
                     uint8_t* o = a.act + ((int64_t)r8 * (2 * a.nlu) + 2 * (u0 + u) + p) * 34;
-                    if (!upper && g == 0) *reinterpret_cast<uint16_t*>(o) = dbits;
+                    if (!upper && g == 0) *reinterpret_cast<uint16_t*>(o) = dbs[r8 * (U * STEPS) + u * STEPS + p];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) o[2 + 8 * g + (upper ? 4 : 0) + e] = (uint8_t)qv[e];
                 }
