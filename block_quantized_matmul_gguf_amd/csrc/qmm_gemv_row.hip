@@ -1,5 +1,5 @@
 // qmm_gemv_row.hip -- decode kernel for one activation row (M == 1), Q8_0,
-// Q4_K, Q4_0 and Q5_0 weights, modes (a) and (b).
+// Q4_K, Q4_0, Q5_0 and Q6_K weights, modes (a) and (b).
 //
 // Mode (a) is the Metal form of the same page and section: f32 activations
 // against the dequantized weights, y[n] = sum_k w[n][k] x[k], w = d q (Q8_0)
@@ -72,9 +72,13 @@ constexpr int GR_LDS_MAX = 160 * 1024;
 // Q4_0 and Q5_0 weights (mode (b)) take the Q8_0 path with their own block
 // pairs (36 and 44 bytes, 4-byte aligned since K % 64 == 0) and Q8_0
 // activations; S = sum q x - offset * sum x per block, exact in int32.
-constexpr int gr_unit_bytes(int fmt) { return fmt == FMT_Q8_0 ? 68 : fmt == FMT_Q4_0 ? 36 : fmt == FMT_Q5_0 ? 44 : 144; }
-constexpr int gr_unit_values(int fmt) { return fmt == FMT_Q4_K ? 256 : 64; }
-constexpr int gr_seg_units(int fmt) { return fmt == FMT_Q4_K ? 16 : 64; }
+constexpr int gr_unit_bytes(int fmt)
+{
+    return fmt == FMT_Q8_0 ? 68 : fmt == FMT_Q4_0 ? 36 : fmt == FMT_Q5_0 ? 44 : fmt == FMT_Q6_K ? 210 : 144;
+}
+constexpr bool gr_kq(int fmt) { return fmt == FMT_Q4_K || fmt == FMT_Q6_K; }  // super-blocks, Q8K activations
+constexpr int gr_unit_values(int fmt) { return gr_kq(fmt) ? 256 : 64; }
+constexpr int gr_seg_units(int fmt) { return gr_kq(fmt) ? 16 : 64; }
 constexpr int gr_seg_bytes(int fmt) { return gr_seg_units(fmt) * gr_unit_bytes(fmt); }
 constexpr bool gr_pairs(int fmt) { return fmt == FMT_Q4_0 || fmt == FMT_Q5_0; }  // 4-bit pairs with an offset
 
@@ -82,7 +86,7 @@ template <int FMT>
 struct GrFmt {
     static constexpr int UNIT_BYTES = gr_unit_bytes(FMT);  // a block pair / a super-block
     static constexpr int UNIT_VALUES = gr_unit_values(FMT);
-    static constexpr int LANES_PER_UNIT = FMT == FMT_Q4_K ? 4 : 1;
+    static constexpr int LANES_PER_UNIT = gr_kq(FMT) ? 4 : 1;
     static constexpr int SEG_UNITS = 64 / LANES_PER_UNIT;
     static constexpr int SEG_BYTES = SEG_UNITS * UNIT_BYTES;  // 4352 / 2304 / 2304 / 2816
     static constexpr int LPU_MAX = (SEG_BYTES + 1023) / 1024;  // 5 / 3 / 3 / 3
@@ -108,6 +112,8 @@ struct GemvRowArgs {
     int32_t* sums;  // per row: Q8_0/Q4_0/Q5_0 S per block; Q4_K per super-block S_0..S_7, sumi, summins
     uint8_t* act;   // the quantized activation row as canonical Q8_0 / Q8K blocks (workgroup 0 writes it)
 };
+
+QMM_DEV uint32_t gr_lds32(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
 
 typedef __attribute__((address_space(1))) void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
@@ -215,7 +221,7 @@ __global__ __launch_bounds__(GR_THREADS) void gemv_row_kernel(GemvRowArgs a)
 
     // ---- quantize x into LDS (mode b) ----
     if constexpr (MODE == MODE_A) {
-    } else if constexpr (FMT != FMT_Q4_K) {
+    } else if constexpr (!gr_kq(FMT)) {
         // 8 values per task, the four tasks of a 32-value block a lane quad
         for (int t = tid; t < K / 8; t += GR_THREADS) {
             const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(s_xf + 8 * t);
@@ -285,9 +291,28 @@ __global__ __launch_bounds__(GR_THREADS) void gemv_row_kernel(GemvRowArgs a)
     if constexpr (MODE == MODE_B) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
     // ---- mode (a): this lane's 64 f32 activation values (and Q4_K's sub-block sums) ----
+    // Q6_K: lane quarter c of a super-block takes values 128 h + l + 32 k, h = c / 2,
+    // l in 16 (c % 2) .. +15, k = 0..3 (the values whose low and high bits share its
+    // bytes), as four runs of 16; XS their sums
     float XF[MODE == MODE_A ? 64 : 1];
-    float XS[2] = {0.0f, 0.0f};
-    if constexpr (MODE == MODE_A) {
+    float XS[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (MODE == MODE_A && FMT == FMT_Q6_K) {
+        const int unit = min(lane / 4, a.nunit - 1), c = lane & 3;
+        const float* base = s_xf + 256 * unit + 128 * (c >> 1) + 16 * (c & 1);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {
+                const f32x4_t v = *reinterpret_cast<const f32x4_t*>(base + 32 * k + 4 * cc);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) XF[16 * k + 4 * cc + e] = v[e];
+            }
+            float t = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) t += XF[16 * k + i];
+            XS[k] = t;
+        }
+    } else if constexpr (MODE == MODE_A) {
         const int unit = min(lane / F::LANES_PER_UNIT, a.nunit - 1);
         const f32x4_t* q = reinterpret_cast<const f32x4_t*>(s_xf + F::UNIT_VALUES * unit + 64 * (lane % F::LANES_PER_UNIT));
 #pragma unroll
@@ -314,11 +339,28 @@ __global__ __launch_bounds__(GR_THREADS) void gemv_row_kernel(GemvRowArgs a)
     constexpr int NB = MODE == MODE_B ? NSEG : 1;
     int X[NB][16];
     float DX[NB][2];
-    int XB[NB][2];
+    int XB[NB][4];
 #pragma unroll
     for (int sg = 0; sg < NB && MODE == MODE_B; ++sg) {
         const int unit = min(sg * F::SEG_UNITS + lane / F::LANES_PER_UNIT, a.nunit - 1);
         const int c = lane % F::LANES_PER_UNIT;
+        if constexpr (FMT == FMT_Q6_K) {
+            // the four runs of 16 (see mode (a)) and the sum of each
+            const int8_t* base = s_xq + 256 * unit + 128 * (c >> 1) + 16 * (c & 1);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const u32x4_t v = *reinterpret_cast<const u32x4_t*>(base + 32 * k);
+                int t = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    X[sg][4 * k + e] = (int)v[e];
+                    t = __builtin_amdgcn_sdot4((int)v[e], 0x01010101, t, false);
+                }
+                XB[sg][k] = t;
+            }
+            DX[sg][0] = DX[sg][1] = s_xd[unit];
+            continue;
+        }
         const u32x4_t* q = reinterpret_cast<const u32x4_t*>(s_xq + F::UNIT_VALUES * unit + 64 * c);
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
@@ -405,6 +447,89 @@ __global__ __launch_bounds__(GR_THREADS) void gemv_row_kernel(GemvRowArgs a)
                     }
                     acc = fmaf(s0a + s0b, f16lo(W[0]), acc);
                     acc = fmaf(s1a + s1b, f16hi(W[8]), acc);
+                }
+            } else if constexpr (FMT == FMT_Q6_K) {
+                // super-block ui (210 bytes: ql[128] | qh[64] | sc[16] int8 | d f16; the odd
+                // ones start two bytes into a dword), lane quarter c: values 128 hh + 32 k +
+                // l, l in l0 .. l0+15: low bits in nibble k / 2 of ql[64 hh + 32 (k & 1) + l],
+                // high bits in bit pair k of qh[32 hh + l], scale sc[8 hh + 2 k + c % 2].
+                // Lanes past the segment read its last super-block and add nothing.
+                const bool live = lane < 4 * units;
+                const int c = lane & 3, hh = c >> 1, l0 = 16 * (c & 1);
+                const int ui = min(lane >> 2, units - 1);
+                const uint8_t* sp = sbuf + 210 * ui;
+                const uint32_t sh = (uint32_t)(ui & 1) * 2u;  // byte shift of this super-block
+                auto ld = [&](int off, uint32_t* r, int nd) {  // nd dwords from sp + off
+                    const uint8_t* pa = sp + off - sh;
+                    uint32_t w[5];
+#pragma unroll
+                    for (int i = 0; i < 5; ++i) w[i] = i <= nd ? gr_lds32(pa + 4 * i) : 0u;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (i < nd) r[i] = __builtin_amdgcn_alignbyte(w[i + 1], w[i], sh);
+                };
+                uint32_t qa[4], qb[4], qh[4], scw[2];
+                ld(64 * hh + l0, qa, 4);
+                ld(64 * hh + 32 + l0, qb, 4);
+                ld(128 + 32 * hh + l0, qh, 4);
+                ld(192 + 8 * hh, scw, 2);
+                const uint32_t dw = gr_lds32(sp + 208 - sh);
+                const float d = sh ? f16hi(dw) : f16lo(dw);
+                uint32_t code[4][4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    code[0][t] = (qa[t] & 0x0f0f0f0fu) | ((qh[t] & 0x03030303u) << 4);
+                    code[1][t] = (qb[t] & 0x0f0f0f0fu) | (((qh[t] >> 2) & 0x03030303u) << 4);
+                    code[2][t] = ((qa[t] >> 4) & 0x0f0f0f0fu) | (((qh[t] >> 4) & 0x03030303u) << 4);
+                    code[3][t] = ((qb[t] >> 4) & 0x0f0f0f0fu) | (((qh[t] >> 6) & 0x03030303u) << 4);
+                }
+                int sc[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int bi = 2 * k + (c & 1);
+                    sc[k] = (int)(int8_t)(scw[bi >> 2] >> (8 * (bi & 3)));
+                }
+                if constexpr (MODE == MODE_A) {
+                    // exact f32 codes against the f32 values; q - 32 through the run sums
+                    float t = 0.0f;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        float sa = 0.0f, sb = 0.0f;
+#pragma unroll
+                        for (int tt = 0; tt < 4; ++tt) {
+                            uint32_t cw = code[k][tt];
+                            asm volatile("" : "+v"(cw));  // one v_cvt_f32_ubyteN per value
+#pragma unroll
+                            for (int b = 0; b < 4; ++b) {
+                                const float qf = (float)((cw >> (8 * b)) & 0xffu);
+                                if (b < 2) sa = fmaf(qf, XF[16 * k + 4 * tt + b], sa);
+                                else sb = fmaf(qf, XF[16 * k + 4 * tt + b], sb);
+                            }
+                        }
+                        t = fmaf((float)sc[k], (sa + sb) - 32.0f * XS[k], t);
+                    }
+                    if (live) acc = fmaf(d, t, acc);
+                } else {
+                    int si = 0, S[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        int sk = 0;
+#pragma unroll
+                        for (int tt = 0; tt < 4; ++tt) sk = __builtin_amdgcn_sdot4((int)code[k][tt], X[sg][4 * k + tt], sk, false);
+                        S[k] = sk - 32 * XB[sg][k];
+                        si += sc[k] * S[k];
+                    }
+                    si += dpp_i<DPP_X1>(si);  // the super-block's four lanes (exact)
+                    si += dpp_i<DPP_X2>(si);
+                    if (live && c == 0) acc = fmaf(DX[sg][0], d * (float)si, acc);
+                    if constexpr (EMIT) {
+                        if (live) {  // per super-block: S_0..S_15, sumi
+                            int32_t* o = a.sums + ((int64_t)(gw + nw * j) * a.nunit + sg * F::SEG_UNITS + (lane >> 2)) * 17;
+#pragma unroll
+                            for (int k = 0; k < 4; ++k) o[8 * hh + 2 * k + (c & 1)] = S[k];
+                            if (c == 0) o[16] = si;
+                        }
+                    }
                 }
             } else if constexpr (MODE == MODE_A) {
                 if (lane < 4 * units) {
@@ -563,6 +688,8 @@ static GrKernel gr_kernel(int fmt, int mode, int lpu, int nseg, int ring, bool e
         return mode == MODE_A ? gr_kernel_mode<FMT_Q8_0, MODE_A, false>(lpu, nseg, ring) : gr_kernel_b<FMT_Q8_0>(lpu, nseg, ring, emit);
     if (fmt == FMT_Q4_0) return gr_kernel_b<FMT_Q4_0>(lpu, nseg, ring, emit);  // mode (b) only
     if (fmt == FMT_Q5_0) return gr_kernel_b<FMT_Q5_0>(lpu, nseg, ring, emit);
+    if (fmt == FMT_Q6_K)
+        return mode == MODE_A ? gr_kernel_mode<FMT_Q6_K, MODE_A, false>(lpu, nseg, ring) : gr_kernel_b<FMT_Q6_K>(lpu, nseg, ring, emit);
     return mode == MODE_A ? gr_kernel_mode<FMT_Q4_K, MODE_A, false>(lpu, nseg, ring) : gr_kernel_b<FMT_Q4_K>(lpu, nseg, ring, emit);
 }
 
@@ -577,8 +704,8 @@ static GrLayout gr_layout(int fmt, int64_t K, int ring)
     l.nxi = (int)((4 * K + 1023) / 1024);
     l.xq_off = 1024 * l.nxi;
     l.xd_off = l.xq_off + (int)K;
-    l.xb_off = l.xd_off + (int)(fmt != FMT_Q4_K ? K / 8 : K / 64);
-    l.ring_off = (l.xb_off + (int)(fmt != FMT_Q4_K ? 0 : K / 8) + 15) / 16 * 16;
+    l.xb_off = l.xd_off + (int)(!gr_kq(fmt) ? K / 8 : K / 64);
+    l.ring_off = (l.xb_off + (int)(!gr_kq(fmt) ? 0 : K / 8) + 15) / 16 * 16;
     const int slot_max = 1024 * ((gr_seg_bytes(fmt) + 1023) / 1024);
     l.bytes = l.ring_off + GR_WAVES * ring * slot_max;
     return l;
@@ -598,7 +725,8 @@ static int gr_ring(int fmt, int64_t K)
 bool gemv_row_supported(int fmt, int mode, int M, int64_t N, int64_t K, bool emit)
 {
     if ((mode != MODE_A && mode != MODE_B) || M != 1 || (emit && mode != MODE_B)) return false;
-    if (fmt != FMT_Q8_0 && fmt != FMT_Q4_K && fmt != FMT_Q4_0 && fmt != FMT_Q5_0) return false;
+    if (fmt != FMT_Q8_0 && fmt != FMT_Q4_K && fmt != FMT_Q4_0 && fmt != FMT_Q5_0 && fmt != FMT_Q6_K) return false;
+    if (fmt == FMT_Q6_K && K % 512 != 0) return false;  // an even super-block count: 4-byte-aligned rows
     // Q4_0 / Q5_0 mode (a): the staged-activation kernel is faster (on the 8-layer
     // 14336 x 4096 stack 10.3 against 14.0 us for Q4_0), so only mode (b) comes here
     if (gr_pairs(fmt) && mode == MODE_A) return false;
@@ -606,7 +734,7 @@ bool gemv_row_supported(int fmt, int mode, int M, int64_t N, int64_t K, bool emi
     const int nseg_max = mode == MODE_A ? 1 : GR_NSEG_MAX;  // mode (a) holds one segment's f32 activations
     if (K % vpu != 0 || K / vpu > (int64_t)nseg_max * gr_seg_units(fmt)) return false;
     if (mode == MODE_A) {
-        const int64_t lanes = (K / vpu) * (fmt == FMT_Q4_K ? 4 : 1);
+        const int64_t lanes = (K / vpu) * (gr_kq(fmt) ? 4 : 1);
         const int64_t rows_per_wave = (N + GR_WAVES * (int64_t)device_cus() - 1) / (GR_WAVES * (int64_t)device_cus());
         if (lanes < 32 && rows_per_wave > 4) return false;
     }

@@ -111,7 +111,7 @@ def test_matmul_parity(fmt, n, k, mode, m):
 
 
 @pytest.mark.parametrize("mode", MODES, ids=["a", "b"])
-@pytest.mark.parametrize("fmt,k", [(qmm.Q4_0, 1536), (qmm.Q5_0, 576), (qmm.Q6_K, 768)])
+@pytest.mark.parametrize("fmt,k", [(qmm.Q4_0, 1536), (qmm.Q5_0, 576), (qmm.Q6_K, 768), (qmm.Q6_K, 1024)])
 @pytest.mark.parametrize("m", [1, 4, 12])
 def test_matmul_parity_on_random_bytes(fmt, k, mode, m):
     n = 50
@@ -120,6 +120,27 @@ def test_matmul_parity_on_random_bytes(fmt, k, mode, m):
     y = run(fmt, mode, wq, n, k, x)
     yr, a = ref(fmt, mode, wq, n, k, x)
     assert_within(y, yr, a, f"{NAME[fmt]} random bytes M={m} mode={mode}")
+
+
+# Q6_K at M = 1 with an even super-block count runs on the one-row kernel (four
+# lanes per super-block, odd super-blocks two bytes into a dword): partial
+# segments (2 and 6 super-blocks), a whole one, mode (b)'s two and four segments,
+# ragged N; three runs bit-equal.
+Q6_ROW = [(77, 512), (1000, 1536), (130, 4096), (40, 8192), (33, 16384)]
+
+
+@pytest.mark.parametrize("mode", MODES, ids=["a", "b"])
+@pytest.mark.parametrize("n,k", Q6_ROW, ids=[f"{n}x{k}" for n, k in Q6_ROW])
+def test_q6_k_one_row_parity(n, k, mode):
+    wq = oracle.quantize(qmm.Q6_K, synth.weights_f32(7600 + n + k, n, k))
+    x = synth.acts_f32(7601 + k, 1, k)
+    with qmm.Plan(qmm.Q6_K, n, k, 1, mode) as p:
+        wd, xd = dev(wq), dev(x)
+        ys = [host(p.run(wd, xd)) for _ in range(3)]
+    for y in ys[1:]:
+        assert np.array_equal(y.view(np.uint32), ys[0].view(np.uint32))
+    yr, a = ref(qmm.Q6_K, mode, wq, n, k, x)
+    assert_within(ys[0], yr, a, f"Q6_K {n}x{k} M=1 mode={mode}")
 
 
 @pytest.mark.parametrize("fmt,n,k", [(qmm.Q4_0, 40, 256), (qmm.Q5_0, 40, 256), (qmm.Q6_K, 24, 512)])
