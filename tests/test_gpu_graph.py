@@ -28,6 +28,9 @@ CASES = [(qmm.Q8_0, qmm.MODE_F32ACT, 1), (qmm.Q8_0, qmm.MODE_QACT, 8), (qmm.Q4_K
          (qmm.Q5_0, qmm.MODE_QACT, 1), (qmm.Q5_0, qmm.MODE_F32ACT, 1), (qmm.Q4_0, qmm.MODE_QACT, 8),
          (qmm.Q4_0, qmm.MODE_F32ACT, 96), (qmm.Q6_K, qmm.MODE_QACT, 1), (qmm.Q6_K, qmm.MODE_QACT, 12),
          (qmm.Q6_K, qmm.MODE_F32ACT, 96),
+         # the register-operand decode (2..8 rows) in both modes, and the one-row Q6_K kernel
+         (qmm.Q8_0, qmm.MODE_F32ACT, 8), (qmm.Q4_K, qmm.MODE_F32ACT, 5), (qmm.Q5_0, qmm.MODE_F32ACT, 3),
+         (qmm.Q6_K, qmm.MODE_QACT, 8), (qmm.Q6_K, qmm.MODE_F32ACT, 1),
          # an odd block count (the padded copies)
          (qmm.Q8_0, qmm.MODE_QACT, 1), ]
 
