@@ -13,7 +13,8 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqmatmul.so")
 SOURCES = ["qmm_capi.cpp", "qmm_quant.hip", "qmm_gemv.hip", "qmm_gemv_row.hip", "qmm_gemm.hip", "qmm_gemm_q.hip",
-           "qmm_dequant.hip", "qmm_ext.hip", "qmm_noalloc.hip", "qmm_gemv_b.hip", "qmm_gemv_emit.hip", "qmm_gemv_reg.hip"]
+           "qmm_dequant.hip", "qmm_ext.hip", "qmm_noalloc.hip", "qmm_gemv_b.hip", "qmm_gemv_emit.hip", "qmm_gemv_reg.hip",
+           "qmm_gemm_s.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

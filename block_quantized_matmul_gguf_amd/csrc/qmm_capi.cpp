@@ -264,6 +264,8 @@ extern "C" int qmatmul_destroy(qmm_plan* p)
 
 static bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+constexpr int PG_GROUP_S = 4;  // problems per short-row launch
+
 static int check_run(const qmm_plan* p, const void* w, const float* x, const void* y, int64_t M)
 {
     if (!p) return fail(QMM_EINVAL, "plan is NULL");
@@ -314,11 +316,18 @@ static int run_impl(const qmm_plan* p, const void* w, const float* x, float* y, 
             if (e == hipSuccess) e = launch_gemm(FMT_Q6_K, p->mode, w, p->N, K, M, p->gm, y, s, sums);
         } else {
             e = launch_ext_to_q8_0(p->fmt, w, p->N, K, p->ex.tw, s);
-            if (e == hipSuccess) e = launch_gemm_prep(FMT_Q8_0, p->mode, x, M, K, p->gm, s, act);
-            if (e == hipSuccess) e = launch_gemm(FMT_Q8_0, p->mode, p->ex.tw, p->N, K, M, p->gm, y, s, sums);
+            const void* tw = p->ex.tw;
+            if (e == hipSuccess && gemm_s_supported(FMT_Q8_0, p->mode, K, p->N, M)) {
+                e = launch_gemm_s(p->mode, 1, &tw, &p->N, &y, x, K, M, s, tr);
+            } else {
+                if (e == hipSuccess) e = launch_gemm_prep(FMT_Q8_0, p->mode, x, M, K, p->gm, s, act);
+                if (e == hipSuccess) e = launch_gemm(FMT_Q8_0, p->mode, p->ex.tw, p->N, K, M, p->gm, y, s, sums);
+            }
         }
     } else if (M <= GEMV_MAX_M) {
         e = launch_gemv(p->fmt, p->mode, w, x, p->N, K, (int)M, p->gv, y, s, tr);
+    } else if (gemm_s_supported(p->fmt, p->mode, K, p->N, M)) {
+        e = launch_gemm_s(p->mode, 1, &w, &p->N, &y, x, K, M, s, tr);  // short rows: one launch
     } else {
         e = launch_gemm_prep(p->fmt, p->mode, x, M, K, p->gm, s, act);
         if (e == hipSuccess) e = launch_gemm(p->fmt, p->mode, w, p->N, K, M, p->gm, y, s, sums);
@@ -438,22 +447,40 @@ extern "C" int qmatmul_run_group(const qmm_plan* const* plans, int count, const 
         // launch per gemm_group_max() plans; Q4_0/Q5_0 weights first rewritten as
         // Q8_0 blocks in each plan's workspace, as in their separate runs
         const int kf = p0->fmt == QMM_Q4_0 || p0->fmt == QMM_Q5_0 ? FMT_Q8_0 : p0->fmt;
-        hipError_t e = launch_gemm_prep(kf, p0->mode, x, M, p0->K, p0->gm, s);
-        const int gmax = gemm_group_max();
-        for (int i = 0; i < count && e == hipSuccess; i += gmax) {
-            const int c = count - i < gmax ? count - i : gmax;
-            const void* wk[QMM_GROUP_MAX];
-            int64_t Ns[QMM_GROUP_MAX];
-            for (int j = 0; j < c && e == hipSuccess; ++j) {
-                const qmm_plan* pj = plans[i + j];
-                Ns[j] = pj->N;
-                wk[j] = w[i + j];
-                if (kf != p0->fmt) {
-                    e = launch_ext_to_q8_0(pj->fmt, w[i + j], pj->N, pj->K, pj->ex.tw, s);
-                    wk[j] = pj->ex.tw;
+        // Each plan takes the kernel its own run takes (so grouped outputs equal
+        // separate runs bit for bit): plans with short rows and a one-round grid
+        // go to the short-row kernel, which prepares its own activations; the
+        // rest share one preparation and the K-staged kernels.
+        int sp[QMM_GROUP_MAX], op[QMM_GROUP_MAX], ns = 0, no = 0;
+        for (int i = 0; i < count; ++i) {
+            if (gemm_s_supported(kf, p0->mode, p0->K, plans[i]->N, M)) sp[ns++] = i;
+            else op[no++] = i;
+        }
+        hipError_t e = no > 0 ? launch_gemm_prep(kf, p0->mode, x, M, p0->K, p0->gm, s) : hipSuccess;
+        for (int part = 0; part < 2; ++part) {
+            const int* idx = part == 0 ? sp : op;
+            const int cnt = part == 0 ? ns : no;
+            const int gmax = part == 0 ? PG_GROUP_S : gemm_group_max();
+            for (int i = 0; i < cnt && e == hipSuccess; i += gmax) {
+                const int c = cnt - i < gmax ? cnt - i : gmax;
+                const void* wk[QMM_GROUP_MAX];
+                int64_t Ns[QMM_GROUP_MAX];
+                float* ys[QMM_GROUP_MAX];
+                for (int j = 0; j < c && e == hipSuccess; ++j) {
+                    const int q = idx[i + j];
+                    const qmm_plan* pj = plans[q];
+                    Ns[j] = pj->N;
+                    wk[j] = w[q];
+                    ys[j] = y[q];
+                    if (kf != p0->fmt) {  // Q4_0/Q5_0: rewritten as Q8_0 blocks, as in their separate runs
+                        e = launch_ext_to_q8_0(pj->fmt, w[q], pj->N, pj->K, pj->ex.tw, s);
+                        wk[j] = pj->ex.tw;
+                    }
                 }
+                if (e == hipSuccess)
+                    e = part == 0 ? launch_gemm_s(p0->mode, c, wk, Ns, ys, x, p0->K, M, s)
+                                  : launch_gemm_group(kf, p0->mode, c, wk, Ns, ys, p0->K, M, p0->gm, s);
             }
-            if (e == hipSuccess) e = launch_gemm_group(kf, p0->mode, c, wk, Ns, y + i, p0->K, M, p0->gm, s);
         }
         if (e != hipSuccess) return fail(QMM_EHIP, "kernel launch: %s", hipGetErrorString(e));
         return QMM_OK;

@@ -1,0 +1,409 @@
+// qmm_gemm_s.hip -- prefill (M > 8) of Q8_0 weights with short rows (K <= 1536),
+// the activation preparation done inside the launch.
+//
+// The pages' SmolLM2-135M prefill (page "GGUF", section 在 candle 里跑一个 GGUF:
+// a 37-token prompt, then 270 teacher-forced tokens) is 211 products with K =
+// 576 or 1536 at M = 307.  There the K-staged tile kernels (qmm_gemm.hip,
+// qmm_gemm_q.hip) wait on one global round trip per 64-value stage, after a
+// separate launch that prepares the activations.  Here a 256-thread workgroup
+// owns 16 activation rows x 64 weight rows and takes its K range in one go:
+//   * each wave copies its 16 weight rows (raw blocks, at most 576 values of
+//     each row at a time) into its own LDS buffer with 16-byte buffer-to-LDS
+//     loads, issued first; rows past N read as zero;
+//   * the workgroup loads its 16 activation rows (f32) into registers, a row
+//     per 16 lanes, and prepares them itself: mode (a) the row's power-of-two
+//     scale and the f16 hi/lo split, mode (b) the Q8_0 blocks through the
+//     standalone quantizer's device functions (the same bytes), written to LDS
+//     in matrix-core operand order;
+//   * v_mfma_f32_16x16x32_f16 per 32-value block: A = the 16 rows' hi and
+//     then lo parts (mode (a)) or their int8 values as exact f16 (mode (b):
+//     the f32 sum is the exact integer block sum), B = the block's int8
+//     weights as exact f16; acc += d_w C (mode (a)), acc += (d_w d_x) C (b).
+// Grouped launches number the problems' column tiles end to end; traced runs
+// (mode (b)) write the block sums and the quantized activation blocks.
+#include <algorithm>
+#include <mutex>
+#include <set>
+#include <utility>
+
+#include "qmm_act.h"
+#include "qmm_gemv_kernel.h"
+#include "qmm_internal.h"
+
+namespace qmm {
+
+namespace {
+
+constexpr int GS_NT = 256;                 // threads: four waves
+constexpr int GS_BM = 16;                  // activation rows per tile
+constexpr int GS_BN = 64;                  // weight rows per tile, 16 per wave
+constexpr int GS_KMAX = 1536;              // longest row
+constexpr int GS_JMAX = GS_KMAX / 64;      // 16-byte activation loads per thread
+constexpr int GS_PIECE = 576;              // most values of a row staged at once
+constexpr int64_t GS_NMAX = 8192;          // widest launch (all problems' rows)
+constexpr int GS_TLP = 12;                 // most loads of one wave's piece (pieces of at most 576 values)
+
+struct GemmSArgs {
+    PrefillGroup g;
+    const float* x;
+    int32_t* sums;  // traced runs: [M][N][K/32]
+    uint8_t* act;   // traced runs: canonical Q8_0 blocks [M][K/32], or null
+    int K, M, nm, remap;
+    int row_bytes;  // K / 32 * 34
+    int kp;         // values per staged piece of a row (divides K, a multiple of 64)
+    int cpr;        // pieces: 16-byte chunks per LDS weight row (odd: the 16 rows in different banks)
+    int nbuf;       // weight buffers per wave (2: piece p + 1 lands while p is summed)
+    int bsz;        // bytes of one weight buffer
+    int off_dx;     // mode (a): row exponents [16]; mode (b): d_x [K/32][16]
+    int off_b;      // the weight buffers, [wave][nbuf]
+};
+
+// One block pair's operands: w = the weight dwords (even block's three, odd
+// block's two, the two holding d0 and d1); a = the activation operand chunks
+// (mode (a): even hi, even lo, odd hi, odd lo; mode (b): even, odd, then d_x of
+// the lane's four rows for each block).
+struct GsPair {
+    uint32_t w[7];
+    u32x4_t a[4];
+};
+
+QMM_DEV uint32_t gs_h2(_Float16 a, _Float16 b) { return __builtin_bit_cast(uint32_t, half2_t{a, b}); }
+
+template <int MODE, bool EMIT>
+__global__ __launch_bounds__(GS_NT, 2) void gemm_s_kernel(GemmSArgs a)
+{
+    static_assert(!EMIT || MODE == MODE_B, "integer block sums exist in mode (b) only");
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int K = a.K, M = a.M, nb = K / 32;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // the tile: row tiles of one column tile are consecutive, and with the
+    // remap each XCD (workgroups id % 8) takes a contiguous run of them
+    const int G = (int)gridDim.x, id = (int)blockIdx.x;
+    const int L = a.remap ? (id & 7) * (G >> 3) + (id >> 3) : id;
+    const int mt = L % a.nm, nt = L / a.nm;
+    const uint8_t* W;
+    float* Y;
+    int N, tile0;
+    pg_locate(a.g, nt, W, Y, N, tile0);
+    const int m0 = mt * GS_BM;
+    const int n0 = (nt - tile0) * GS_BN + 16 * wave;  // this wave's first weight row
+
+    // ---- activations: row rho of the tile in lanes 16 rho .. +15 (one DPP row),
+    // lane c16 holding values 64 j + 4 c16 .. +3; rows past M read as zero ----
+    const int rho = tid >> 4, c16 = tid & 15, nj = K / 64;
+    const rsrc_t xr = make_rsrc(a.x + (int64_t)m0 * K, clamp_u32((int64_t)(M - m0) * K * 4));
+    f32x4_t xv[GS_JMAX];
+#pragma unroll
+    for (int j = 0; j < GS_JMAX; ++j)
+        xv[j] = j < nj ? __builtin_bit_cast(f32x4_t, ld128(xr, (uint32_t)(rho * K + 64 * j + 4 * c16) * 4u))
+                       : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // ---- weights: piece p (values p*kp .. +kp of each row) of the wave's 16 rows.
+    // Whole rows (kp == K): the 16 rows are one contiguous, 16-byte aligned run of
+    // bytes, copied as is (LDS row stride = row_bytes).  Pieces: row r's chunk c
+    // (16 bytes from the piece's start) lands at row r * 16 cpr; a row's last chunk
+    // may run past its piece (into bytes never read back). ----
+    const bool whole = a.kp == K;
+    const int rs = whole ? a.row_bytes : 16 * a.cpr, pb = a.kp / 32 * 34;
+    const int64_t wb = (int64_t)n0 * a.row_bytes, wleft = (int64_t)N * a.row_bytes - wb;
+    const rsrc_t wr = make_rsrc(W + (wleft > 0 ? wb : 0), wleft > 0 ? (uint32_t)min(wleft, (int64_t)16 * a.row_bytes) : 0u);
+    const int nchunk = whole ? a.row_bytes : 16 * a.cpr, tl = (nchunk + 63) / 64;
+    auto issue = [&](int p) {
+        uint8_t* buf = lds + a.off_b + (wave * a.nbuf + p % a.nbuf) * a.bsz;
+        for (int t = 0; t < tl; ++t) {
+            const int f = 64 * t + lane;
+            if (f < nchunk) {
+                uint32_t off = 16u * (uint32_t)f;
+                if (!whole) {
+                    const int r = f / a.cpr;
+                    off = (uint32_t)(r * a.row_bytes + p * pb + 16 * (f - r * a.cpr));
+                }
+                ld128_lds(wr, buf + 1024 * t, off);
+            }
+        }
+    };
+    const int np = K / a.kp;
+    issue(0);
+    if (a.nbuf > 1 && np > 1) issue(1);
+
+    // operand chunks: mode (a) [block][hi, lo][64 lanes][16 B], mode (b) [block][64 lanes][16 B];
+    // lane r + 16 g of a chunk holds row r's values 8 g .. 8 g + 7 of the block
+    uint8_t* A = lds;
+    const int blk_hi = c16 >> 3, kg = (c16 & 7) >> 1, half_off = 8 * (c16 & 1);
+    if constexpr (MODE == MODE_A) {
+        float mx = 0.0f;
+#pragma unroll
+        for (int j = 0; j < GS_JMAX; ++j)
+            if (j < nj)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fabsf(xv[j][e]));
+        mx = fmaxf(mx, dpp_f<DPP_X1>(mx));
+        mx = fmaxf(mx, dpp_f<DPP_X2>(mx));
+        mx = fmaxf(mx, dpp_f<DPP_HMIRROR>(mx));
+        mx = fmaxf(mx, dpp_f<DPP_MIRROR>(mx));
+        const int ex = split_exp(mx);
+        const float sc = ldexpf(1.0f, ex);
+        if (c16 == 0) reinterpret_cast<int*>(lds + a.off_dx)[rho] = ex;
+#pragma unroll
+        for (int j = 0; j < GS_JMAX; ++j) {
+            if (j < nj) {
+                _Float16 h[4], l[4];
+                float xs;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) split_one(xv[j][e], sc, h[e], l[e], xs);
+                const int s = 2 * j + blk_hi;
+                uint8_t* dst = A + ((2 * s) * 64 + rho + 16 * kg) * 16 + half_off;
+                *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{gs_h2(h[0], h[1]), gs_h2(h[2], h[3])};
+                *reinterpret_cast<u32x2_t*>(dst + 1024) = u32x2_t{gs_h2(l[0], l[1]), gs_h2(l[2], l[3])};
+            }
+        }
+    } else {
+        float* dxs = reinterpret_cast<float*>(lds + a.off_dx);
+#pragma unroll
+        for (int j = 0; j < GS_JMAX; ++j) {
+            if (j < nj) {
+                // the block's max |x| over its eight lanes
+                float am = fmaxf(fmaxf(fabsf(xv[j][0]), fabsf(xv[j][1])), fmaxf(fabsf(xv[j][2]), fabsf(xv[j][3])));
+                am = fmaxf(am, dpp_f<DPP_X1>(am));
+                am = fmaxf(am, dpp_f<DPP_X2>(am));
+                am = fmaxf(am, dpp_f<DPP_HMIRROR>(am));
+                float qid, dval;
+                uint16_t dbits;
+                q8_0_scale(am, qid, dbits, dval);
+                int q[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) q[e] = q8_0_q(xv[j][e], qid);
+                const int s = 2 * j + blk_hi;
+                uint8_t* dst = A + (s * 64 + rho + 16 * kg) * 16 + half_off;
+                *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{gs_h2((_Float16)q[0], (_Float16)q[1]), gs_h2((_Float16)q[2], (_Float16)q[3])};
+                if ((c16 & 7) == 0) dxs[s * 16 + rho] = dval;
+                if constexpr (EMIT) {
+                    // canonical block s of row m0 + rho: f16 d, then the 32 int8 (column tile 0 writes them)
+                    if (nt == 0 && a.act != nullptr && m0 + rho < M) {
+                        uint8_t* o = a.act + ((int64_t)(m0 + rho) * nb + s) * 34;
+                        if ((c16 & 7) == 0) {
+                            o[0] = (uint8_t)(dbits & 0xffu);
+                            o[1] = (uint8_t)(dbits >> 8);
+                        }
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) o[2 + 4 * (c16 & 7) + e] = (uint8_t)q[e];
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- blocks: lane (n, g) holds outputs rows 4 g + i, column n0 + n ----
+    const int n = lane & 15, g = lane >> 4, col = n0 + n;
+    const float* dxs = reinterpret_cast<const float*>(lds + a.off_dx);
+    const f32x4_t zf = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4_t acc = zf;
+    const int ppp = a.kp / 64;  // block pairs per piece
+    for (int p = 0; p < np; ++p) {
+        // this wave's piece p has landed (piece p + 1 may still be in flight; traced
+        // runs' stores are counted too, so they wait for everything)
+        if (EMIT || a.nbuf == 1 || p + 1 >= np) vm_wait<0>();
+        else vm_wait_ahead<1, GS_TLP>(tl);
+        const uint8_t* rrow = lds + a.off_b + (wave * a.nbuf + p % a.nbuf) * a.bsz + n * rs;
+        // software-pipelined over the piece's block pairs: the operands of pair q + 1
+        // are read while pair q is on the matrix cores, and pair q's scales are
+        // applied after pair q + 1's matrix-core steps are issued
+        auto load = [&](int q, GsPair& o) {
+            // pair q: d0 | 32 int8 | d1 | 32 int8 (68 B, dword-aligned); the even
+            // block's values 8g .. 8g+7 start two bytes into a dword
+            const uint8_t* rp = rrow + 68 * q;
+            const int s0 = 2 * (p * ppp + q);
+            o.w[0] = lds32(rp + 8 * g);
+            o.w[1] = lds32(rp + 8 * g + 4);
+            o.w[2] = lds32(rp + 8 * g + 8);
+            o.w[3] = lds32(rp + 36 + 8 * g);
+            o.w[4] = lds32(rp + 40 + 8 * g);
+            o.w[5] = lds32(rp);
+            o.w[6] = lds32(rp + 32);
+            if constexpr (MODE == MODE_A) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) o.a[c] = lds128(A + ((2 * s0 + c) * 64 + lane) * 16);
+            } else {
+                o.a[0] = lds128(A + (s0 * 64 + lane) * 16);
+                o.a[1] = lds128(A + ((s0 + 1) * 64 + lane) * 16);
+                o.a[2] = __builtin_bit_cast(u32x4_t, *reinterpret_cast<const f32x4_t*>(dxs + s0 * 16 + 4 * g));
+                o.a[3] = __builtin_bit_cast(u32x4_t, *reinterpret_cast<const f32x4_t*>(dxs + (s0 + 1) * 16 + 4 * g));
+            }
+        };
+        // pair sums Ce, Co (blocks s0, s0 + 1) into acc with the pair's scales
+        auto apply = [&](const f32x4_t& Ce, const f32x4_t& Co, const GsPair& o, int s0) {
+            const float de = f16lo(o.w[5]), dd = f16hi(o.w[6]);
+            if constexpr (MODE == MODE_A) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = fmaf(Co[i], dd, fmaf(Ce[i], de, acc[i]));
+            } else {
+                const f32x4_t xe = __builtin_bit_cast(f32x4_t, o.a[2]), xo = __builtin_bit_cast(f32x4_t, o.a[3]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = fmaf(Co[i], dd * xo[i], fmaf(Ce[i], de * xe[i], acc[i]));
+                if constexpr (EMIT) {
+                    if (col < N) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int m = m0 + 4 * g + i;
+                            if (m < M) {
+                                int32_t* out = a.sums + ((int64_t)m * N + col) * nb + s0;
+                                out[0] = (int32_t)Ce[i];
+                                out[1] = (int32_t)Co[i];
+                            }
+                        }
+                    }
+                }
+            }
+        };
+        GsPair cur, prv;
+        f32x4_t pCe = zf, pCo = zf;
+        load(0, cur);
+        for (int q = 0; q < ppp; ++q) {
+            GsPair nxt;
+            if (q + 1 < ppp) load(q + 1, nxt);
+            const half8_t Be = i8x8_to_f16(__builtin_amdgcn_alignbyte(cur.w[1], cur.w[0], 2), __builtin_amdgcn_alignbyte(cur.w[2], cur.w[1], 2));
+            const half8_t Bo = i8x8_to_f16(cur.w[3], cur.w[4]);
+            f32x4_t Ce, Co;
+            if constexpr (MODE == MODE_A) {
+                Ce = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, cur.a[0]), Be, zf, 0, 0, 0);
+                Co = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, cur.a[2]), Bo, zf, 0, 0, 0);
+                Ce = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, cur.a[1]), Be, Ce, 0, 0, 0);
+                Co = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, cur.a[3]), Bo, Co, 0, 0, 0);
+            } else {
+                Ce = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, cur.a[0]), Be, zf, 0, 0, 0);
+                Co = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, cur.a[1]), Bo, zf, 0, 0, 0);
+            }
+            if (q > 0) apply(pCe, pCo, prv, 2 * (p * ppp + q - 1));
+            pCe = Ce;
+            pCo = Co;
+            prv = cur;
+            cur = nxt;
+        }
+        apply(pCe, pCo, prv, 2 * (p * ppp + ppp - 1));
+        if (p + a.nbuf < np) {
+            // every read of this buffer has returned before the next piece overwrites it
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            issue(p + a.nbuf);
+        }
+    }
+
+    if (Y != nullptr && col < N) {
+        const int* se = reinterpret_cast<const int*>(lds + a.off_dx);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = m0 + 4 * g + i;
+            if (m < M) {
+                float v = acc[i];
+                if constexpr (MODE == MODE_A) v *= ldexpf(1.0f, -se[4 * g + i]);
+                Y[(int64_t)m * N + col] = v;
+            }
+        }
+    }
+}
+
+void gs_allow_lds(const void* k, int bytes)
+{
+    static std::set<std::pair<int, const void*>> done;
+    static std::mutex mu;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!done.insert(std::make_pair(dev, k)).second) return;
+    (void)hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    (void)hipGetLastError();
+}
+
+// The largest multiple of 64 that divides K and is at most GS_PIECE.
+int gs_piece(int64_t K)
+{
+    int kp = (int)(std::min<int64_t>(K, GS_PIECE) / 64) * 64;
+    while (kp > 64 && K % kp != 0) kp -= 64;
+    return kp;
+}
+
+}  // namespace
+
+// LDS bytes of a launch and its buffer plan: whole rows when they fit; else
+// pieces of at most 576 values, two buffers per wave where they fit (the
+// largest such piece), one otherwise.
+static int gs_plan(int mode, int64_t K, GemmSArgs& a)
+{
+    const int nb = (int)(K / 32);
+    const int abytes = mode == MODE_A ? nb * 2048 : nb * 1024;
+    const int dxbytes = mode == MODE_A ? 64 : nb * 64;
+    a.row_bytes = nb * 34;
+    a.off_dx = abytes;
+    a.off_b = (abytes + dxbytes + 15) & ~15;
+    const int room = 160 * 1024 - a.off_b;
+    if (4 * 16 * a.row_bytes <= room) {
+        a.kp = (int)K;
+        a.cpr = 0;
+        a.nbuf = 1;
+        a.bsz = 16 * a.row_bytes;
+    } else {
+        auto bsz = [](int kp) { return 16 * 16 * (((kp / 32 * 34 + 15) / 16) | 1); };
+        a.nbuf = 1;
+        a.kp = gs_piece(K);
+        for (int kp = a.kp; kp >= 64; kp -= 64)
+            if (K % kp == 0 && 4 * 2 * bsz(kp) <= room) {
+                a.kp = kp;
+                a.nbuf = 2;
+                break;
+            }
+        a.cpr = ((a.kp / 32 * 34 + 15) / 16) | 1;
+        a.bsz = bsz(a.kp);
+    }
+    return a.off_b + 4 * a.nbuf * a.bsz;
+}
+
+// Short rows, and a grid of at most one workgroup per compute unit: with more
+// tiles the K-staged kernels, whose larger tiles reread fewer bytes, are faster
+// (the 1536 x 576 gate and up pair at M = 307: 960 tiles, 17.5 us against
+// 14.4 us).  The test is per problem, so a grouped run gives each problem the
+// kernel of its own run.
+bool gemm_s_supported(int fmt, int mode, int64_t K, int64_t Ntot, int64_t M)
+{
+    if (!(fmt == FMT_Q8_0 && M > GEMV_MAX_M && K > 0 && K % 64 == 0 && K <= GS_KMAX && Ntot > 0 && Ntot <= GS_NMAX))
+        return false;
+    GemmSArgs a{};
+    const int bytes = gs_plan(mode, K, a);
+    const int64_t grid = ((M + GS_BM - 1) / GS_BM) * ((Ntot + GS_BN - 1) / GS_BN);
+    return bytes <= 160 * 1024 && grid <= (int64_t)device_cus();
+}
+
+hipError_t launch_gemm_s(int mode, int count, const void* const* w, const int64_t* Ns, float* const* y,
+                         const float* x, int64_t K, int64_t M, hipStream_t s, const Trace* tr)
+{
+    if (count < 1 || count > PG_MAX || (tr && (count != 1 || mode != MODE_B))) return hipErrorInvalidValue;
+    if (!(K > 0 && K % 64 == 0 && K <= GS_KMAX && M > 0)) return hipErrorInvalidValue;
+    GemmSArgs a{};
+    a.g.groups = count;
+    a.g.t0[0] = 0;
+    for (int p = 0; p < PG_MAX; ++p) {
+        const bool on = p < count;
+        a.g.w[p] = on ? (const uint8_t*)w[p] : nullptr;
+        a.g.y[p] = on ? y[p] : nullptr;
+        a.g.n[p] = on ? (int)Ns[p] : 0;
+        a.g.t0[p + 1] = a.g.t0[p] + (on ? (int)((Ns[p] + GS_BN - 1) / GS_BN) : 0);
+    }
+    a.x = x;
+    a.sums = tr ? tr->sums : nullptr;
+    a.act = tr ? tr->act : nullptr;
+    a.K = (int)K;
+    a.M = (int)M;
+    a.nm = (int)((M + GS_BM - 1) / GS_BM);
+    const int bytes = gs_plan(mode, K, a);
+    const int64_t grid = (int64_t)a.nm * a.g.t0[count];
+    if (grid < 1 || grid > 0x7fffffff || bytes > 160 * 1024) return hipErrorInvalidConfiguration;
+    a.remap = grid % 8 == 0 ? 1 : 0;
+    const void* k = mode == MODE_A ? (const void*)gemm_s_kernel<MODE_A, false>
+                    : tr           ? (const void*)gemm_s_kernel<MODE_B, true>
+                                   : (const void*)gemm_s_kernel<MODE_B, false>;
+    gs_allow_lds(k, bytes);
+    void* args[] = {&a};
+    return hipLaunchKernel(k, dim3((unsigned)grid), dim3(GS_NT), args, (size_t)bytes, s);
+}
+
+}  // namespace qmm
