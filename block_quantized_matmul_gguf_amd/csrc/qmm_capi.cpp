@@ -315,11 +315,10 @@ static int run_impl(const qmm_plan* p, const void* w, const float* x, float* y, 
             e = launch_gemm_prep(FMT_Q6_K, p->mode, x, M, K, p->gm, s, act);
             if (e == hipSuccess) e = launch_gemm(FMT_Q6_K, p->mode, w, p->N, K, M, p->gm, y, s, sums);
         } else {
-            e = launch_ext_to_q8_0(p->fmt, w, p->N, K, p->ex.tw, s);
-            const void* tw = p->ex.tw;
-            if (e == hipSuccess && gemm_s_supported(FMT_Q8_0, p->mode, K, p->N, M)) {
-                e = launch_gemm_s(p->mode, 1, &tw, &p->N, &y, x, K, M, s, tr);
+            if (gemm_s_supported(p->fmt, p->mode, K, p->N, M)) {  // short rows: the blocks as they are
+                e = launch_gemm_s(p->fmt, p->mode, 1, &w, &p->N, &y, x, K, M, s, tr);
             } else {
+                e = launch_ext_to_q8_0(p->fmt, w, p->N, K, p->ex.tw, s);
                 if (e == hipSuccess) e = launch_gemm_prep(FMT_Q8_0, p->mode, x, M, K, p->gm, s, act);
                 if (e == hipSuccess) e = launch_gemm(FMT_Q8_0, p->mode, p->ex.tw, p->N, K, M, p->gm, y, s, sums);
             }
@@ -327,7 +326,7 @@ static int run_impl(const qmm_plan* p, const void* w, const float* x, float* y, 
     } else if (M <= GEMV_MAX_M) {
         e = launch_gemv(p->fmt, p->mode, w, x, p->N, K, (int)M, p->gv, y, s, tr);
     } else if (gemm_s_supported(p->fmt, p->mode, K, p->N, M)) {
-        e = launch_gemm_s(p->mode, 1, &w, &p->N, &y, x, K, M, s, tr);  // short rows: one launch
+        e = launch_gemm_s(p->fmt, p->mode, 1, &w, &p->N, &y, x, K, M, s, tr);  // short rows: one launch
     } else {
         e = launch_gemm_prep(p->fmt, p->mode, x, M, K, p->gm, s, act);
         if (e == hipSuccess) e = launch_gemm(p->fmt, p->mode, w, p->N, K, M, p->gm, y, s, sums);
@@ -453,7 +452,7 @@ extern "C" int qmatmul_run_group(const qmm_plan* const* plans, int count, const 
         // rest share one preparation and the K-staged kernels.
         int sp[QMM_GROUP_MAX], op[QMM_GROUP_MAX], ns = 0, no = 0;
         for (int i = 0; i < count; ++i) {
-            if (gemm_s_supported(kf, p0->mode, p0->K, plans[i]->N, M)) sp[ns++] = i;
+            if (gemm_s_supported(p0->fmt, p0->mode, p0->K, plans[i]->N, M)) sp[ns++] = i;
             else op[no++] = i;
         }
         hipError_t e = no > 0 ? launch_gemm_prep(kf, p0->mode, x, M, p0->K, p0->gm, s) : hipSuccess;
@@ -472,13 +471,13 @@ extern "C" int qmatmul_run_group(const qmm_plan* const* plans, int count, const 
                     Ns[j] = pj->N;
                     wk[j] = w[q];
                     ys[j] = y[q];
-                    if (kf != p0->fmt) {  // Q4_0/Q5_0: rewritten as Q8_0 blocks, as in their separate runs
+                    if (part == 1 && kf != p0->fmt) {  // Q4_0/Q5_0: rewritten as Q8_0 blocks, as in their separate runs
                         e = launch_ext_to_q8_0(pj->fmt, w[q], pj->N, pj->K, pj->ex.tw, s);
                         wk[j] = pj->ex.tw;
                     }
                 }
                 if (e == hipSuccess)
-                    e = part == 0 ? launch_gemm_s(p0->mode, c, wk, Ns, ys, x, p0->K, M, s)
+                    e = part == 0 ? launch_gemm_s(p0->fmt, p0->mode, c, wk, Ns, ys, x, p0->K, M, s)
                                   : launch_gemm_group(kf, p0->mode, c, wk, Ns, ys, p0->K, M, p0->gm, s);
             }
         }

@@ -1,5 +1,5 @@
-// qmm_gemm_s.hip -- prefill (M > 8) of Q8_0 weights with short rows (K <= 1536),
-// the activation preparation done inside the launch.
+// qmm_gemm_s.hip -- prefill (M > 8) of Q8_0, Q4_0 and Q5_0 weights with short
+// rows (K <= 1536), the activation preparation done inside the launch.
 //
 // The pages' SmolLM2-135M prefill (page "GGUF", section 在 candle 里跑一个 GGUF:
 // a 37-token prompt, then 270 teacher-forced tokens) is 211 products with K =
@@ -17,8 +17,9 @@
 //     in matrix-core operand order;
 //   * v_mfma_f32_16x16x32_f16 per 32-value block: A = the 16 rows' hi and
 //     then lo parts (mode (a)) or their int8 values as exact f16 (mode (b):
-//     the f32 sum is the exact integer block sum), B = the block's int8
-//     weights as exact f16; acc += d_w C (mode (a)), acc += (d_w d_x) C (b).
+//     the f32 sum is the exact integer block sum), B = the block's weights as
+//     exact f16 (Q8_0 q, Q4_0 q - 8, Q5_0 q - 16, decoded from block pairs,
+//     the 4-byte-aligned load units); acc += d_w C (mode (a)), (d_w d_x) C (b).
 // Grouped launches number the problems' column tiles end to end; traced runs
 // (mode (b)) write the block sums and the quantized activation blocks.
 #include <algorithm>
@@ -49,7 +50,7 @@ struct GemmSArgs {
     int32_t* sums;  // traced runs: [M][N][K/32]
     uint8_t* act;   // traced runs: canonical Q8_0 blocks [M][K/32], or null
     int K, M, nm, remap;
-    int row_bytes;  // K / 32 * 34
+    int row_bytes;  // K / 64 block pairs of gs_lub(fmt) bytes
     int kp;         // values per staged piece of a row (divides K, a multiple of 64)
     int cpr;        // pieces: 16-byte chunks per LDS weight row (odd: the 16 rows in different banks)
     int nbuf;       // weight buffers per wave (2: piece p + 1 lands while p is summed)
@@ -58,20 +59,40 @@ struct GemmSArgs {
     int off_b;      // the weight buffers, [wave][nbuf]
 };
 
-// One block pair's operands: w = the weight dwords (even block's three, odd
-// block's two, the two holding d0 and d1); a = the activation operand chunks
+// Bytes of a block pair (64 values): Q8_0 d | 32 int8, Q4_0 d | qs[16],
+// Q5_0 d | qh[4] | qs[16], twice.
+constexpr int gs_lub(int fmt) { return fmt == FMT_Q8_0 ? 68 : fmt == FMT_Q4_0 ? 36 : 44; }
+
+// Eight 5-bit codes (bytes of c0, c1) -> eight exact f16 (code - OFF) in order:
+// byte b under 0x64 is the f16 1024 + b, then one packed subtraction.
+template <int OFF>
+QMM_DEV half8_t gs_codes_f16(uint32_t c0, uint32_t c1)
+{
+    const half2_t bias = {(_Float16)(-1024.0f - OFF), (_Float16)(-1024.0f - OFF)};
+    u32x4_t r;
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, c0, 0x04010400u)) + bias);
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, c0, 0x04030402u)) + bias);
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, c1, 0x04010400u)) + bias);
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, c1, 0x04030402u)) + bias);
+    return __builtin_bit_cast(half8_t, r);
+}
+
+// One block pair's operands: w = the weight dwords (the even block's three,
+// the odd block's two, the two holding d0 and d1, Q5_0's two of fifth bits);
+// a = the activation operand chunks
 // (mode (a): even hi, even lo, odd hi, odd lo; mode (b): even, odd, then d_x of
 // the lane's four rows for each block).
 struct GsPair {
-    uint32_t w[7];
+    uint32_t w[9];
     u32x4_t a[4];
 };
 
 QMM_DEV uint32_t gs_h2(_Float16 a, _Float16 b) { return __builtin_bit_cast(uint32_t, half2_t{a, b}); }
 
-template <int MODE, bool EMIT>
+template <int FMT, int MODE, bool EMIT>
 __global__ __launch_bounds__(GS_NT, 2) void gemm_s_kernel(GemmSArgs a)
 {
+    constexpr int LUB = gs_lub(FMT), HALF = LUB / 2;
     static_assert(!EMIT || MODE == MODE_B, "integer block sums exist in mode (b) only");
     extern __shared__ __align__(16) uint8_t lds[];
     const int K = a.K, M = a.M, nb = K / 32;
@@ -105,7 +126,7 @@ __global__ __launch_bounds__(GS_NT, 2) void gemm_s_kernel(GemmSArgs a)
     // (16 bytes from the piece's start) lands at row r * 16 cpr; a row's last chunk
     // may run past its piece (into bytes never read back). ----
     const bool whole = a.kp == K;
-    const int rs = whole ? a.row_bytes : 16 * a.cpr, pb = a.kp / 32 * 34;
+    const int rs = whole ? a.row_bytes : 16 * a.cpr, pb = a.kp / 64 * LUB;
     const int64_t wb = (int64_t)n0 * a.row_bytes, wleft = (int64_t)N * a.row_bytes - wb;
     const rsrc_t wr = make_rsrc(W + (wleft > 0 ? wb : 0), wleft > 0 ? (uint32_t)min(wleft, (int64_t)16 * a.row_bytes) : 0u);
     const int nchunk = whole ? a.row_bytes : 16 * a.cpr, tl = (nchunk + 63) / 64;
@@ -211,17 +232,33 @@ __global__ __launch_bounds__(GS_NT, 2) void gemm_s_kernel(GemmSArgs a)
         // are read while pair q is on the matrix cores, and pair q's scales are
         // applied after pair q + 1's matrix-core steps are issued
         auto load = [&](int q, GsPair& o) {
-            // pair q: d0 | 32 int8 | d1 | 32 int8 (68 B, dword-aligned); the even
-            // block's values 8g .. 8g+7 start two bytes into a dword
-            const uint8_t* rp = rrow + 68 * q;
+            // pair q (dword-aligned); the even block's values start two bytes into a dword
+            const uint8_t* rp = rrow + LUB * q;
             const int s0 = 2 * (p * ppp + q);
-            o.w[0] = lds32(rp + 8 * g);
-            o.w[1] = lds32(rp + 8 * g + 4);
-            o.w[2] = lds32(rp + 8 * g + 8);
-            o.w[3] = lds32(rp + 36 + 8 * g);
-            o.w[4] = lds32(rp + 40 + 8 * g);
+            if constexpr (FMT == FMT_Q8_0) {
+                // values 8g .. 8g+7 of a block are its bytes 2 + 8g .. 9 + 8g
+                o.w[0] = lds32(rp + 8 * g);
+                o.w[1] = lds32(rp + 8 * g + 4);
+                o.w[2] = lds32(rp + 8 * g + 8);
+                o.w[3] = lds32(rp + 36 + 8 * g);
+                o.w[4] = lds32(rp + 40 + 8 * g);
+            } else {
+                // values 8g .. 8g+7: the low (g < 2) or high nibbles of qs bytes
+                // 8 (g & 1) .. +7, Q5_0 with bits 8g .. 8g+7 of qh as fifth bits
+                constexpr int QS0 = FMT == FMT_Q4_0 ? 2 : 6, QS1 = HALF + QS0;
+                const int qo = 8 * (g & 1);
+                o.w[0] = lds32(rp + QS0 - 2 + qo);
+                o.w[1] = lds32(rp + QS0 + 2 + qo);
+                o.w[2] = lds32(rp + QS0 + 6 + qo);
+                o.w[3] = lds32(rp + QS1 + qo);
+                o.w[4] = lds32(rp + QS1 + qo + 4);
+                if constexpr (FMT == FMT_Q5_0) {
+                    o.w[7] = lds32(rp + 4);
+                    o.w[8] = lds32(rp + HALF + 2);
+                }
+            }
             o.w[5] = lds32(rp);
-            o.w[6] = lds32(rp + 32);
+            o.w[6] = lds32(rp + HALF - 2);
             if constexpr (MODE == MODE_A) {
 #pragma unroll
                 for (int c = 0; c < 4; ++c) o.a[c] = lds128(A + ((2 * s0 + c) * 64 + lane) * 16);
@@ -263,8 +300,27 @@ __global__ __launch_bounds__(GS_NT, 2) void gemm_s_kernel(GemmSArgs a)
         for (int q = 0; q < ppp; ++q) {
             GsPair nxt;
             if (q + 1 < ppp) load(q + 1, nxt);
-            const half8_t Be = i8x8_to_f16(__builtin_amdgcn_alignbyte(cur.w[1], cur.w[0], 2), __builtin_amdgcn_alignbyte(cur.w[2], cur.w[1], 2));
-            const half8_t Bo = i8x8_to_f16(cur.w[3], cur.w[4]);
+            half8_t Be, Bo;
+            if constexpr (FMT == FMT_Q8_0) {
+                Be = i8x8_to_f16(__builtin_amdgcn_alignbyte(cur.w[1], cur.w[0], 2), __builtin_amdgcn_alignbyte(cur.w[2], cur.w[1], 2));
+                Bo = i8x8_to_f16(cur.w[3], cur.w[4]);
+            } else {
+                const int sh = 4 * (g >> 1);
+                uint32_t ce0 = (__builtin_amdgcn_alignbyte(cur.w[1], cur.w[0], 2) >> sh) & 0x0f0f0f0fu;
+                uint32_t ce1 = (__builtin_amdgcn_alignbyte(cur.w[2], cur.w[1], 2) >> sh) & 0x0f0f0f0fu;
+                uint32_t co0 = (cur.w[3] >> sh) & 0x0f0f0f0fu;
+                uint32_t co1 = (cur.w[4] >> sh) & 0x0f0f0f0fu;
+                if constexpr (FMT == FMT_Q5_0) {
+                    const uint32_t he = __builtin_amdgcn_alignbyte(cur.w[7], cur.w[5], 2), ho = cur.w[8];
+                    ce0 |= spread4((he >> (8 * g)) & 15u);
+                    ce1 |= spread4((he >> (8 * g + 4)) & 15u);
+                    co0 |= spread4((ho >> (8 * g)) & 15u);
+                    co1 |= spread4((ho >> (8 * g + 4)) & 15u);
+                }
+                constexpr int OFF = FMT == FMT_Q4_0 ? 8 : 16;
+                Be = gs_codes_f16<OFF>(ce0, ce1);
+                Bo = gs_codes_f16<OFF>(co0, co1);
+            }
             f32x4_t Ce, Co;
             if constexpr (MODE == MODE_A) {
                 Ce = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, cur.a[0]), Be, zf, 0, 0, 0);
@@ -325,15 +381,23 @@ int gs_piece(int64_t K)
 
 }  // namespace
 
+template <int FMT>
+static const void* gs_kernel(int mode, bool traced)
+{
+    return mode == MODE_A ? (const void*)gemm_s_kernel<FMT, MODE_A, false>
+           : traced       ? (const void*)gemm_s_kernel<FMT, MODE_B, true>
+                          : (const void*)gemm_s_kernel<FMT, MODE_B, false>;
+}
+
 // LDS bytes of a launch and its buffer plan: whole rows when they fit; else
 // pieces of at most 576 values, two buffers per wave where they fit (the
 // largest such piece), one otherwise.
-static int gs_plan(int mode, int64_t K, GemmSArgs& a)
+static int gs_plan(int fmt, int mode, int64_t K, GemmSArgs& a)
 {
-    const int nb = (int)(K / 32);
+    const int nb = (int)(K / 32), lub = gs_lub(fmt);
     const int abytes = mode == MODE_A ? nb * 2048 : nb * 1024;
     const int dxbytes = mode == MODE_A ? 64 : nb * 64;
-    a.row_bytes = nb * 34;
+    a.row_bytes = (int)(K / 64) * lub;
     a.off_dx = abytes;
     a.off_b = (abytes + dxbytes + 15) & ~15;
     const int room = 160 * 1024 - a.off_b;
@@ -343,7 +407,7 @@ static int gs_plan(int mode, int64_t K, GemmSArgs& a)
         a.nbuf = 1;
         a.bsz = 16 * a.row_bytes;
     } else {
-        auto bsz = [](int kp) { return 16 * 16 * (((kp / 32 * 34 + 15) / 16) | 1); };
+        auto bsz = [lub](int kp) { return 16 * 16 * (((kp / 64 * lub + 15) / 16) | 1); };
         a.nbuf = 1;
         a.kp = gs_piece(K);
         for (int kp = a.kp; kp >= 64; kp -= 64)
@@ -352,7 +416,7 @@ static int gs_plan(int mode, int64_t K, GemmSArgs& a)
                 a.nbuf = 2;
                 break;
             }
-        a.cpr = ((a.kp / 32 * 34 + 15) / 16) | 1;
+        a.cpr = ((a.kp / 64 * lub + 15) / 16) | 1;
         a.bsz = bsz(a.kp);
     }
     return a.off_b + 4 * a.nbuf * a.bsz;
@@ -365,19 +429,20 @@ static int gs_plan(int mode, int64_t K, GemmSArgs& a)
 // kernel of its own run.
 bool gemm_s_supported(int fmt, int mode, int64_t K, int64_t Ntot, int64_t M)
 {
-    if (!(fmt == FMT_Q8_0 && M > GEMV_MAX_M && K > 0 && K % 64 == 0 && K <= GS_KMAX && Ntot > 0 && Ntot <= GS_NMAX))
+    if (!((fmt == FMT_Q8_0 || fmt == FMT_Q4_0 || fmt == FMT_Q5_0) && M > GEMV_MAX_M && K > 0 && K % 64 == 0 && K <= GS_KMAX && Ntot > 0 && Ntot <= GS_NMAX))
         return false;
     GemmSArgs a{};
-    const int bytes = gs_plan(mode, K, a);
+    const int bytes = gs_plan(fmt, mode, K, a);
     const int64_t grid = ((M + GS_BM - 1) / GS_BM) * ((Ntot + GS_BN - 1) / GS_BN);
     return bytes <= 160 * 1024 && grid <= (int64_t)device_cus();
 }
 
-hipError_t launch_gemm_s(int mode, int count, const void* const* w, const int64_t* Ns, float* const* y,
+hipError_t launch_gemm_s(int fmt, int mode, int count, const void* const* w, const int64_t* Ns, float* const* y,
                          const float* x, int64_t K, int64_t M, hipStream_t s, const Trace* tr)
 {
     if (count < 1 || count > PG_MAX || (tr && (count != 1 || mode != MODE_B))) return hipErrorInvalidValue;
-    if (!(K > 0 && K % 64 == 0 && K <= GS_KMAX && M > 0)) return hipErrorInvalidValue;
+    if (!(K > 0 && K % 64 == 0 && K <= GS_KMAX && M > 0) || !(fmt == FMT_Q8_0 || fmt == FMT_Q4_0 || fmt == FMT_Q5_0))
+        return hipErrorInvalidValue;
     GemmSArgs a{};
     a.g.groups = count;
     a.g.t0[0] = 0;
@@ -394,13 +459,13 @@ hipError_t launch_gemm_s(int mode, int count, const void* const* w, const int64_
     a.K = (int)K;
     a.M = (int)M;
     a.nm = (int)((M + GS_BM - 1) / GS_BM);
-    const int bytes = gs_plan(mode, K, a);
+    const int bytes = gs_plan(fmt, mode, K, a);
     const int64_t grid = (int64_t)a.nm * a.g.t0[count];
     if (grid < 1 || grid > 0x7fffffff || bytes > 160 * 1024) return hipErrorInvalidConfiguration;
     a.remap = grid % 8 == 0 ? 1 : 0;
-    const void* k = mode == MODE_A ? (const void*)gemm_s_kernel<MODE_A, false>
-                    : tr           ? (const void*)gemm_s_kernel<MODE_B, true>
-                                   : (const void*)gemm_s_kernel<MODE_B, false>;
+    const void* k = fmt == FMT_Q8_0 ? gs_kernel<FMT_Q8_0>(mode, tr != nullptr)
+                    : fmt == FMT_Q4_0 ? gs_kernel<FMT_Q4_0>(mode, tr != nullptr)
+                                      : gs_kernel<FMT_Q5_0>(mode, tr != nullptr);
     gs_allow_lds(k, bytes);
     void* args[] = {&a};
     return hipLaunchKernel(k, dim3((unsigned)grid), dim3(GS_NT), args, (size_t)bytes, s);

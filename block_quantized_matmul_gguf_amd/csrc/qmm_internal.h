@@ -101,13 +101,13 @@ hipError_t launch_gemm_group(int fmt, int mode, int count, const void* const* w,
 hipError_t launch_gemm_q_group(int fmt, int count, const void* const* w, const int64_t* Ns, float* const* y,
                                int64_t K, int64_t M, const GemmBufs& b, hipStream_t s, int32_t* sums = nullptr);
 int gemm_group_max();
-// Q8_0 prefill with short rows (M > 8, K % 64 == 0, K <= 1536, at most 8192
-// output columns over the problems, a grid of one round): one launch that prepares its own
+// Q8_0, Q4_0 and Q5_0 prefill with short rows (M > 8, K % 64 == 0, K <= 1536,
+// at most 8192 output columns, a grid of one round per problem): one launch that prepares its own
 // activations (no preparation launch, no workspace); count (<= 4) problems
 // share K, the mode and x; a traced run (tr, mode (b), count == 1) also writes
 // the block sums [M][N][K/32] and the canonical activation blocks.
 bool gemm_s_supported(int fmt, int mode, int64_t K, int64_t Ntot, int64_t M);
-hipError_t launch_gemm_s(int mode, int count, const void* const* w, const int64_t* Ns, float* const* y,
+hipError_t launch_gemm_s(int fmt, int mode, int count, const void* const* w, const int64_t* Ns, float* const* y,
                          const float* x, int64_t K, int64_t M, hipStream_t s, const Trace* tr = nullptr);
 
 // Q4_0, Q5_0 and Q6_K weights.  Decode runs (and every Q6_K run) take the

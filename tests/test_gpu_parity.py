@@ -232,6 +232,7 @@ TRACED = [
     (qmm.Q8_0, 200, 576, 20), (qmm.Q8_0, 130, 4096, 37), (qmm.Q8_0, 300, 4096, 130),
     (qmm.Q4_K, 100, 1536, 37), (qmm.Q4_K, 300, 4096, 130), (qmm.Q4_K, 70, 256, 9),
     (qmm.Q8_0, 100, 1088, 20), (qmm.Q8_0, 70, 1536, 37), (qmm.Q8_0, 40, 64, 9),
+    (qmm.Q4_0, 70, 576, 37), (qmm.Q5_0, 100, 1088, 20), (qmm.Q5_0, 130, 1536, 9),
 ]
 
 
@@ -354,26 +355,30 @@ def test_grouped_run_equals_separate_runs(fmt, k, ns, mode, m):
         assert_within(grp[i], yr, a, f"group plan {i} {FMT_NAME[fmt]} {n}x{k} M={m} mode={mode}")
 
 
-# Q8_0 prefill with short rows (K <= 1536, at most 8192 columns): one launch
-# that prepares its own activations.  Whole rows staged at once (K <= 576) and
-# in pieces (1024: two of 512; 1088: seventeen of 64; 1536: three of 512),
-# ragged M and N, the widest launch; rows 0 and 1 built around the tie rules.
-SHORT = [(40, 64, 9), (200, 576, 17), (576, 576, 307), (130, 1024, 37), (100, 1088, 20), (576, 1536, 37),
-         (8192, 576, 10), (70, 1536, 307), (8100, 1536, 9)]
+# Prefill with short rows (Q8_0, Q4_0, Q5_0; K <= 1536, at most 8192 columns, a
+# one-round grid): one launch that prepares its own activations.  Whole rows
+# staged at once and in pieces (mode (a) at K = 1536: four of 384, two buffers
+# per wave), block pairs from K = 64 up, ragged M and N, the widest launch; rows
+# 0 and 1 built around the tie rules.
+SHORT = [(qmm.Q8_0, 40, 64, 9), (qmm.Q8_0, 200, 576, 17), (qmm.Q8_0, 576, 576, 307), (qmm.Q8_0, 130, 1024, 37),
+         (qmm.Q8_0, 100, 1088, 20), (qmm.Q8_0, 576, 1536, 37), (qmm.Q8_0, 8192, 576, 10),
+         (qmm.Q8_0, 70, 1536, 307), (qmm.Q8_0, 8100, 1536, 9),
+         (qmm.Q4_0, 40, 64, 9), (qmm.Q4_0, 576, 576, 307), (qmm.Q4_0, 100, 1088, 20), (qmm.Q4_0, 576, 1536, 37),
+         (qmm.Q5_0, 40, 128, 9), (qmm.Q5_0, 576, 576, 307), (qmm.Q5_0, 130, 1024, 37), (qmm.Q5_0, 70, 1536, 307)]
 
 
 @pytest.mark.parametrize("mode", [qmm.MODE_F32ACT, qmm.MODE_QACT], ids=["a", "b"])
-@pytest.mark.parametrize("n,k,m", SHORT, ids=[f"{n}x{k}-M{m}" for n, k, m in SHORT])
-def test_short_row_prefill(n, k, m, mode):
-    wq = oracle.quantize(qmm.Q8_0, synth.weights_f32(7000 + n + k, n, k))
+@pytest.mark.parametrize("fmt,n,k,m", SHORT, ids=[f"{FMT_NAME[f]}-{n}x{k}-M{m}" for f, n, k, m in SHORT])
+def test_short_row_prefill(fmt, n, k, m, mode):
+    wq = oracle.quantize(fmt, synth.weights_f32(7000 + n + k, n, k))
     x = synth.acts_f32(7001 + m + k, m, k)
     x[:2] = synth.tie_rows(7002 + k, k)
-    with qmm.Plan(qmm.Q8_0, n, k, m, mode) as p:
+    with qmm.Plan(fmt, n, k, m, mode) as p:
         wd, xd = dev(wq), dev(x)
         ys = [host(p.run(wd, xd)) for _ in range(2)]
     assert np.array_equal(ys[0].view(np.uint32), ys[1].view(np.uint32)), "two runs differ"
-    yr, a = ref(qmm.Q8_0, mode, wq, n, k, x)
-    assert_within(ys[0], yr, a, f"short-row prefill {n}x{k} M={m} mode={mode}")
+    yr, a = ref(fmt, mode, wq, n, k, x)
+    assert_within(ys[0], yr, a, f"short-row prefill {FMT_NAME[fmt]} {n}x{k} M={m} mode={mode}")
 
 
 # Grouped prefill (M > 8): the activations prepared once, the plans' output
