@@ -31,6 +31,8 @@ CASES = [(qmm.Q8_0, qmm.MODE_F32ACT, 1), (qmm.Q8_0, qmm.MODE_QACT, 8), (qmm.Q4_K
          # the register-operand decode (2..8 rows) in both modes, and the one-row Q6_K kernel
          (qmm.Q8_0, qmm.MODE_F32ACT, 8), (qmm.Q4_K, qmm.MODE_F32ACT, 5), (qmm.Q5_0, qmm.MODE_F32ACT, 3),
          (qmm.Q6_K, qmm.MODE_QACT, 8), (qmm.Q6_K, qmm.MODE_F32ACT, 1),
+         # the short-row prefill (activations prepared in the launch)
+         (qmm.Q8_0, qmm.MODE_F32ACT, 96), (qmm.Q5_0, qmm.MODE_QACT, 40),
          # an odd block count (the padded copies)
          (qmm.Q8_0, qmm.MODE_QACT, 1), ]
 

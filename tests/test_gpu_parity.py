@@ -390,6 +390,9 @@ PGROUPS = [
     (qmm.Q6_K, 512, [200, 77]),
     (qmm.Q4_0, 576, [576, 192]),                  # rewritten as Q8_0 blocks per plan
     (qmm.Q5_0, 1536, [96, 130]),
+    # at M = 307 the wide plan takes the K-staged kernel and the others the short-row kernel
+    (qmm.Q8_0, 576, [2048, 192, 64]),
+    (qmm.Q5_0, 576, [4096, 100]),
 ]
 
 
