@@ -35,7 +35,6 @@ namespace qmm {
 
 namespace {
 
-constexpr int GS_NT = 256;                 // threads: four waves
 constexpr int GS_BM = 16;                  // activation rows per tile
 constexpr int GS_BN = 64;                  // weight rows per tile, 16 per wave
 constexpr int GS_KMAX = 1536;              // longest row
@@ -89,15 +88,23 @@ struct GsPair {
 
 QMM_DEV uint32_t gs_h2(_Float16 a, _Float16 b) { return __builtin_bit_cast(uint32_t, half2_t{a, b}); }
 
-template <int FMT, int MODE, bool EMIT>
-__global__ __launch_bounds__(GS_NT, 2) void gemm_s_kernel(GemmSArgs a)
+// NW: waves per workgroup.  4: wave w copies and computes the 16 weight rows of
+// column block w.  8 (whole rows only): waves w and w + 4 share column block w,
+// each issuing half of its loads and of the activation loads and taking half of
+// the block pairs (their partial sums added at the end, lower half first); the
+// loads leave eight waves per workgroup about twice as fast as four.
+template <int FMT, int MODE, bool EMIT, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void gemm_s_kernel(GemmSArgs a)
 {
+    static_assert(NW == 4 || NW == 8, "four or eight waves");
+    constexpr int S = NW / 4;  // halves of the workgroup
     constexpr int LUB = gs_lub(FMT), HALF = LUB / 2;
     static_assert(!EMIT || MODE == MODE_B, "integer block sums exist in mode (b) only");
     extern __shared__ __align__(16) uint8_t lds[];
     const int K = a.K, M = a.M, nb = K / 32;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int blk = wave & 3, hf = S == 2 ? wave >> 2 : 0;  // column block, half
     // the tile: row tiles of one column tile are consecutive, and with the
     // remap each XCD (workgroups id % 8) takes a contiguous run of them
     const int G = (int)gridDim.x, id = (int)blockIdx.x;
@@ -108,17 +115,21 @@ __global__ __launch_bounds__(GS_NT, 2) void gemm_s_kernel(GemmSArgs a)
     int N, tile0;
     pg_locate(a.g, nt, W, Y, N, tile0);
     const int m0 = mt * GS_BM;
-    const int n0 = (nt - tile0) * GS_BN + 16 * wave;  // this wave's first weight row
+    const int n0 = (nt - tile0) * GS_BN + 16 * blk;  // the first weight row of the wave's column block
 
     // ---- activations: row rho of the tile in lanes 16 rho .. +15 (one DPP row),
     // lane c16 holding values 64 j + 4 c16 .. +3; rows past M read as zero ----
-    const int rho = tid >> 4, c16 = tid & 15, nj = K / 64;
+    // (with eight waves, half hf takes the chunks j = 2 i + hf)
+    const int rho = (tid & 255) >> 4, c16 = tid & 15, nj = K / 64;
     const rsrc_t xr = make_rsrc(a.x + (int64_t)m0 * K, clamp_u32((int64_t)(M - m0) * K * 4));
-    f32x4_t xv[GS_JMAX];
+    constexpr int JI = GS_JMAX / S;
+    f32x4_t xv[JI];
 #pragma unroll
-    for (int j = 0; j < GS_JMAX; ++j)
-        xv[j] = j < nj ? __builtin_bit_cast(f32x4_t, ld128(xr, (uint32_t)(rho * K + 64 * j + 4 * c16) * 4u))
+    for (int i = 0; i < JI; ++i) {
+        const int j = S * i + hf;
+        xv[i] = j < nj ? __builtin_bit_cast(f32x4_t, ld128(xr, (uint32_t)(rho * K + 64 * j + 4 * c16) * 4u))
                        : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
 
     // ---- weights: piece p (values p*kp .. +kp of each row) of the wave's 16 rows.
     // Whole rows (kp == K): the 16 rows are one contiguous, 16-byte aligned run of
@@ -130,9 +141,10 @@ __global__ __launch_bounds__(GS_NT, 2) void gemm_s_kernel(GemmSArgs a)
     const int64_t wb = (int64_t)n0 * a.row_bytes, wleft = (int64_t)N * a.row_bytes - wb;
     const rsrc_t wr = make_rsrc(W + (wleft > 0 ? wb : 0), wleft > 0 ? (uint32_t)min(wleft, (int64_t)16 * a.row_bytes) : 0u);
     const int nchunk = whole ? a.row_bytes : 16 * a.cpr, tl = (nchunk + 63) / 64;
+    const int th = (tl + S - 1) / S, t0 = hf * th, t1 = min(tl, t0 + th);  // this wave's loads of a piece
     auto issue = [&](int p) {
-        uint8_t* buf = lds + a.off_b + (wave * a.nbuf + p % a.nbuf) * a.bsz;
-        for (int t = 0; t < tl; ++t) {
+        uint8_t* buf = lds + a.off_b + (blk * a.nbuf + p % a.nbuf) * a.bsz;
+        for (int t = t0; t < t1; ++t) {
             const int f = 64 * t + lane;
             if (f < nchunk) {
                 uint32_t off = 16u * (uint32_t)f;
@@ -155,24 +167,31 @@ __global__ __launch_bounds__(GS_NT, 2) void gemm_s_kernel(GemmSArgs a)
     if constexpr (MODE == MODE_A) {
         float mx = 0.0f;
 #pragma unroll
-        for (int j = 0; j < GS_JMAX; ++j)
-            if (j < nj)
+        for (int i = 0; i < JI; ++i)
+            if (S * i + hf < nj)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fabsf(xv[j][e]));
+                for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fabsf(xv[i][e]));
         mx = fmaxf(mx, dpp_f<DPP_X1>(mx));
         mx = fmaxf(mx, dpp_f<DPP_X2>(mx));
         mx = fmaxf(mx, dpp_f<DPP_HMIRROR>(mx));
         mx = fmaxf(mx, dpp_f<DPP_MIRROR>(mx));
+        if constexpr (S == 2) {  // the two halves' maxima of the row meet in LDS
+            float* hm = reinterpret_cast<float*>(lds + a.off_dx + 64);
+            if (c16 == 0) hm[16 * hf + rho] = mx;
+            __syncthreads();
+            mx = fmaxf(hm[rho], hm[16 + rho]);
+        }
         const int ex = split_exp(mx);
         const float sc = ldexpf(1.0f, ex);
-        if (c16 == 0) reinterpret_cast<int*>(lds + a.off_dx)[rho] = ex;
+        if (c16 == 0 && hf == 0) reinterpret_cast<int*>(lds + a.off_dx)[rho] = ex;
 #pragma unroll
-        for (int j = 0; j < GS_JMAX; ++j) {
+        for (int i = 0; i < JI; ++i) {
+            const int j = S * i + hf;
             if (j < nj) {
                 _Float16 h[4], l[4];
                 float xs;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) split_one(xv[j][e], sc, h[e], l[e], xs);
+                for (int e = 0; e < 4; ++e) split_one(xv[i][e], sc, h[e], l[e], xs);
                 const int s = 2 * j + blk_hi;
                 uint8_t* dst = A + ((2 * s) * 64 + rho + 16 * kg) * 16 + half_off;
                 *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{gs_h2(h[0], h[1]), gs_h2(h[2], h[3])};
@@ -182,10 +201,11 @@ __global__ __launch_bounds__(GS_NT, 2) void gemm_s_kernel(GemmSArgs a)
     } else {
         float* dxs = reinterpret_cast<float*>(lds + a.off_dx);
 #pragma unroll
-        for (int j = 0; j < GS_JMAX; ++j) {
+        for (int i = 0; i < JI; ++i) {
+            const int j = S * i + hf;
             if (j < nj) {
                 // the block's max |x| over its eight lanes
-                float am = fmaxf(fmaxf(fabsf(xv[j][0]), fabsf(xv[j][1])), fmaxf(fabsf(xv[j][2]), fabsf(xv[j][3])));
+                float am = fmaxf(fmaxf(fabsf(xv[i][0]), fabsf(xv[i][1])), fmaxf(fabsf(xv[i][2]), fabsf(xv[i][3])));
                 am = fmaxf(am, dpp_f<DPP_X1>(am));
                 am = fmaxf(am, dpp_f<DPP_X2>(am));
                 am = fmaxf(am, dpp_f<DPP_HMIRROR>(am));
@@ -194,7 +214,7 @@ __global__ __launch_bounds__(GS_NT, 2) void gemm_s_kernel(GemmSArgs a)
                 q8_0_scale(am, qid, dbits, dval);
                 int q[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) q[e] = q8_0_q(xv[j][e], qid);
+                for (int e = 0; e < 4; ++e) q[e] = q8_0_q(xv[i][e], qid);
                 const int s = 2 * j + blk_hi;
                 uint8_t* dst = A + (s * 64 + rho + 16 * kg) * 16 + half_off;
                 *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{gs_h2((_Float16)q[0], (_Float16)q[1]), gs_h2((_Float16)q[2], (_Float16)q[3])};
@@ -214,6 +234,7 @@ __global__ __launch_bounds__(GS_NT, 2) void gemm_s_kernel(GemmSArgs a)
             }
         }
     }
+    if constexpr (S == 2) vm_wait<0>();  // the halves share their rows: every load lands before the barrier
     __syncthreads();
 
     // ---- blocks: lane (n, g) holds outputs rows 4 g + i, column n0 + n ----
@@ -227,7 +248,8 @@ __global__ __launch_bounds__(GS_NT, 2) void gemm_s_kernel(GemmSArgs a)
         // runs' stores are counted too, so they wait for everything)
         if (EMIT || a.nbuf == 1 || p + 1 >= np) vm_wait<0>();
         else vm_wait_ahead<1, GS_TLP>(tl);
-        const uint8_t* rrow = lds + a.off_b + (wave * a.nbuf + p % a.nbuf) * a.bsz + n * rs;
+        const uint8_t* rrow = lds + a.off_b + (blk * a.nbuf + p % a.nbuf) * a.bsz + n * rs;
+        const int hp = (ppp + S - 1) / S, qa = hf * hp, qb = min(ppp, qa + hp);  // this wave's pairs
         // software-pipelined over the piece's block pairs: the operands of pair q + 1
         // are read while pair q is on the matrix cores, and pair q's scales are
         // applied after pair q + 1's matrix-core steps are issued
@@ -296,10 +318,10 @@ __global__ __launch_bounds__(GS_NT, 2) void gemm_s_kernel(GemmSArgs a)
         };
         GsPair cur, prv;
         f32x4_t pCe = zf, pCo = zf;
-        load(0, cur);
-        for (int q = 0; q < ppp; ++q) {
+        if (qa < qb) load(qa, cur);
+        for (int q = qa; q < qb; ++q) {
             GsPair nxt;
-            if (q + 1 < ppp) load(q + 1, nxt);
+            if (q + 1 < qb) load(q + 1, nxt);
             half8_t Be, Bo;
             if constexpr (FMT == FMT_Q8_0) {
                 Be = i8x8_to_f16(__builtin_amdgcn_alignbyte(cur.w[1], cur.w[0], 2), __builtin_amdgcn_alignbyte(cur.w[2], cur.w[1], 2));
@@ -331,13 +353,13 @@ __global__ __launch_bounds__(GS_NT, 2) void gemm_s_kernel(GemmSArgs a)
                 Ce = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, cur.a[0]), Be, zf, 0, 0, 0);
                 Co = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, cur.a[1]), Bo, zf, 0, 0, 0);
             }
-            if (q > 0) apply(pCe, pCo, prv, 2 * (p * ppp + q - 1));
+            if (q > qa) apply(pCe, pCo, prv, 2 * (p * ppp + q - 1));
             pCe = Ce;
             pCo = Co;
             prv = cur;
             cur = nxt;
         }
-        apply(pCe, pCo, prv, 2 * (p * ppp + ppp - 1));
+        if (qa < qb) apply(pCe, pCo, prv, 2 * (p * ppp + qb - 1));
         if (p + a.nbuf < np) {
             // every read of this buffer has returned before the next piece overwrites it
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -345,6 +367,15 @@ __global__ __launch_bounds__(GS_NT, 2) void gemm_s_kernel(GemmSArgs a)
         }
     }
 
+    if constexpr (S == 2) {
+        // the upper half's partial sums join the lower half's (in that order)
+        __syncthreads();  // the activation operand's bytes take them
+        f32x4_t* part = reinterpret_cast<f32x4_t*>(lds);
+        if (hf == 1) part[blk * 64 + lane] = acc;
+        __syncthreads();
+        if (hf == 1) return;
+        acc += part[blk * 64 + lane];
+    }
     if (Y != nullptr && col < N) {
         const int* se = reinterpret_cast<const int*>(lds + a.off_dx);
 #pragma unroll
@@ -381,12 +412,17 @@ int gs_piece(int64_t K)
 
 }  // namespace
 
-template <int FMT>
-static const void* gs_kernel(int mode, bool traced)
+template <int FMT, int NW>
+static const void* gs_kernel_nw(int mode, bool traced)
 {
-    return mode == MODE_A ? (const void*)gemm_s_kernel<FMT, MODE_A, false>
-           : traced       ? (const void*)gemm_s_kernel<FMT, MODE_B, true>
-                          : (const void*)gemm_s_kernel<FMT, MODE_B, false>;
+    return mode == MODE_A ? (const void*)gemm_s_kernel<FMT, MODE_A, false, NW>
+           : traced       ? (const void*)gemm_s_kernel<FMT, MODE_B, true, NW>
+                          : (const void*)gemm_s_kernel<FMT, MODE_B, false, NW>;
+}
+template <int FMT>
+static const void* gs_kernel(int mode, bool traced, int nw)
+{
+    return nw == 8 ? gs_kernel_nw<FMT, 8>(mode, traced) : gs_kernel_nw<FMT, 4>(mode, traced);
 }
 
 // LDS bytes of a launch and its buffer plan: whole rows when they fit; else
@@ -395,8 +431,9 @@ static const void* gs_kernel(int mode, bool traced)
 static int gs_plan(int fmt, int mode, int64_t K, GemmSArgs& a)
 {
     const int nb = (int)(K / 32), lub = gs_lub(fmt);
-    const int abytes = mode == MODE_A ? nb * 2048 : nb * 1024;
-    const int dxbytes = mode == MODE_A ? 64 : nb * 64;
+    // the activation operand's bytes also take the upper half's partial sums (4 KB)
+    const int abytes = std::max(mode == MODE_A ? nb * 2048 : nb * 1024, 4096);
+    const int dxbytes = mode == MODE_A ? 256 : nb * 64;
     a.row_bytes = (int)(K / 64) * lub;
     a.off_dx = abytes;
     a.off_b = (abytes + dxbytes + 15) & ~15;
@@ -463,12 +500,13 @@ hipError_t launch_gemm_s(int fmt, int mode, int count, const void* const* w, con
     const int64_t grid = (int64_t)a.nm * a.g.t0[count];
     if (grid < 1 || grid > 0x7fffffff || bytes > 160 * 1024) return hipErrorInvalidConfiguration;
     a.remap = grid % 8 == 0 ? 1 : 0;
-    const void* k = fmt == FMT_Q8_0 ? gs_kernel<FMT_Q8_0>(mode, tr != nullptr)
-                    : fmt == FMT_Q4_0 ? gs_kernel<FMT_Q4_0>(mode, tr != nullptr)
-                                      : gs_kernel<FMT_Q5_0>(mode, tr != nullptr);
+    const int nw = a.kp == (int)K ? 8 : 4;  // eight waves with whole rows
+    const void* k = fmt == FMT_Q8_0 ? gs_kernel<FMT_Q8_0>(mode, tr != nullptr, nw)
+                    : fmt == FMT_Q4_0 ? gs_kernel<FMT_Q4_0>(mode, tr != nullptr, nw)
+                                      : gs_kernel<FMT_Q5_0>(mode, tr != nullptr, nw);
     gs_allow_lds(k, bytes);
     void* args[] = {&a};
-    return hipLaunchKernel(k, dim3((unsigned)grid), dim3(GS_NT), args, (size_t)bytes, s);
+    return hipLaunchKernel(k, dim3((unsigned)grid), dim3(64 * nw), args, (size_t)bytes, s);
 }
 
 }  // namespace qmm
