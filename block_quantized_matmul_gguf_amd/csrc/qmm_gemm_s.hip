@@ -5,11 +5,11 @@
 // a 37-token prompt, then 270 teacher-forced tokens) is 211 products with K =
 // 576 or 1536 at M = 307.  There the K-staged tile kernels (qmm_gemm.hip,
 // qmm_gemm_q.hip) wait on one global round trip per 64-value stage, after a
-// separate launch that prepares the activations.  Here a 256-thread workgroup
+// separate launch that prepares the activations.  Here a 512-thread workgroup
 // owns 16 activation rows x 64 weight rows and takes its K range in one go:
-//   * each wave copies its 16 weight rows (raw blocks, at most 576 values of
-//     each row at a time) into its own LDS buffer with 16-byte buffer-to-LDS
-//     loads, issued first; rows past N read as zero;
+//   * each pair of waves copies its column block's 16 weight rows (raw blocks,
+//     whole rows, or pieces of at most 576 values where LDS is short) into an
+//     LDS buffer with 16-byte buffer-to-LDS loads; rows past N read as zero;
 //   * the workgroup loads its 16 activation rows (f32) into registers, a row
 //     per 16 lanes, and prepares them itself: mode (a) the row's power-of-two
 //     scale and the f16 hi/lo split, mode (b) the Q8_0 blocks through the
@@ -35,6 +35,7 @@ namespace qmm {
 
 namespace {
 
+constexpr int GS_NT = 512;                 // threads: eight waves
 constexpr int GS_BM = 16;                  // activation rows per tile
 constexpr int GS_BN = 64;                  // weight rows per tile, 16 per wave
 constexpr int GS_KMAX = 1536;              // longest row
@@ -88,23 +89,23 @@ struct GsPair {
 
 QMM_DEV uint32_t gs_h2(_Float16 a, _Float16 b) { return __builtin_bit_cast(uint32_t, half2_t{a, b}); }
 
-// NW: waves per workgroup.  4: wave w copies and computes the 16 weight rows of
-// column block w.  8 (whole rows only): waves w and w + 4 share column block w,
-// each issuing half of its loads and of the activation loads and taking half of
-// the block pairs (their partial sums added at the end, lower half first); the
-// loads leave eight waves per workgroup about twice as fast as four.
-template <int FMT, int MODE, bool EMIT, int NW>
-__global__ __launch_bounds__(64 * NW, 2) void gemm_s_kernel(GemmSArgs a)
+// Eight waves: waves w and w + 4 share column block w (its 16 weight rows), each
+// issuing half of the block's loads and of the activation loads and taking half
+// of the block pairs; their partial sums are added at the end, lower half first.
+// The loads leave eight waves per workgroup faster than four (four waves, one
+// per column block: a 576 x 576 product at M = 307 took 7.6 against 7.1 us,
+// 576 x 1536 in mode (b) 14.8 against 12.1 us, in mode (a) 16.1 against 13.6).
+template <int FMT, int MODE, bool EMIT>
+__global__ __launch_bounds__(GS_NT, 2) void gemm_s_kernel(GemmSArgs a)
 {
-    static_assert(NW == 4 || NW == 8, "four or eight waves");
-    constexpr int S = NW / 4;  // halves of the workgroup
+    constexpr int S = 2;  // halves of the workgroup
     constexpr int LUB = gs_lub(FMT), HALF = LUB / 2;
     static_assert(!EMIT || MODE == MODE_B, "integer block sums exist in mode (b) only");
     extern __shared__ __align__(16) uint8_t lds[];
     const int K = a.K, M = a.M, nb = K / 32;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int blk = wave & 3, hf = S == 2 ? wave >> 2 : 0;  // column block, half
+    const int blk = wave & 3, hf = wave >> 2;  // column block, half
     // the tile: row tiles of one column tile are consecutive, and with the
     // remap each XCD (workgroups id % 8) takes a contiguous run of them
     const int G = (int)gridDim.x, id = (int)blockIdx.x;
@@ -119,7 +120,7 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_s_kernel(GemmSArgs a)
 
     // ---- activations: row rho of the tile in lanes 16 rho .. +15 (one DPP row),
     // lane c16 holding values 64 j + 4 c16 .. +3; rows past M read as zero ----
-    // (with eight waves, half hf takes the chunks j = 2 i + hf)
+    // (half hf takes the chunks j = 2 i + hf)
     const int rho = (tid & 255) >> 4, c16 = tid & 15, nj = K / 64;
     const rsrc_t xr = make_rsrc(a.x + (int64_t)m0 * K, clamp_u32((int64_t)(M - m0) * K * 4));
     constexpr int JI = GS_JMAX / S;
@@ -131,7 +132,8 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_s_kernel(GemmSArgs a)
                        : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
 
-    // ---- weights: piece p (values p*kp .. +kp of each row) of the wave's 16 rows.
+    // ---- weights: piece p (values p*kp .. +kp of each row) of column block blk's 16
+    // rows, half of the loads from each of the block's two waves.
     // Whole rows (kp == K): the 16 rows are one contiguous, 16-byte aligned run of
     // bytes, copied as is (LDS row stride = row_bytes).  Pieces: row r's chunk c
     // (16 bytes from the piece's start) lands at row r * 16 cpr; a row's last chunk
@@ -175,7 +177,7 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_s_kernel(GemmSArgs a)
         mx = fmaxf(mx, dpp_f<DPP_X2>(mx));
         mx = fmaxf(mx, dpp_f<DPP_HMIRROR>(mx));
         mx = fmaxf(mx, dpp_f<DPP_MIRROR>(mx));
-        if constexpr (S == 2) {  // the two halves' maxima of the row meet in LDS
+        {  // the two halves' maxima of the row meet in LDS
             float* hm = reinterpret_cast<float*>(lds + a.off_dx + 64);
             if (c16 == 0) hm[16 * hf + rho] = mx;
             __syncthreads();
@@ -234,7 +236,6 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_s_kernel(GemmSArgs a)
             }
         }
     }
-    if constexpr (S == 2) vm_wait<0>();  // the halves share their rows: every load lands before the barrier
     __syncthreads();
 
     // ---- blocks: lane (n, g) holds outputs rows 4 g + i, column n0 + n ----
@@ -246,8 +247,14 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_s_kernel(GemmSArgs a)
     for (int p = 0; p < np; ++p) {
         // this wave's piece p has landed (piece p + 1 may still be in flight; traced
         // runs' stores are counted too, so they wait for everything)
-        if (EMIT || a.nbuf == 1 || p + 1 >= np) vm_wait<0>();
-        else vm_wait_ahead<1, GS_TLP>(tl);
+        // both halves read the block's rows: each waits for its loads of piece p (traced
+        // runs' stores count too, so they wait for everything), then a barrier; piece
+        // p + 1 then goes into the buffer of piece p - 1, which every wave is done with
+        // (pieces 0 and 1 were issued at the start)
+        if (EMIT || a.nbuf == 1 || p + 1 >= np || p > 0) vm_wait<0>();
+        else vm_wait_ahead<1, GS_TLP>(t1 - t0);
+        __syncthreads();
+        if (a.nbuf > 1 && p >= 1 && p + 1 < np) issue(p + 1);
         const uint8_t* rrow = lds + a.off_b + (blk * a.nbuf + p % a.nbuf) * a.bsz + n * rs;
         const int hp = (ppp + S - 1) / S, qa = hf * hp, qb = min(ppp, qa + hp);  // this wave's pairs
         // software-pipelined over the piece's block pairs: the operands of pair q + 1
@@ -360,14 +367,13 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_s_kernel(GemmSArgs a)
             cur = nxt;
         }
         if (qa < qb) apply(pCe, pCo, prv, 2 * (p * ppp + qb - 1));
-        if (p + a.nbuf < np) {
-            // every read of this buffer has returned before the next piece overwrites it
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            issue(p + a.nbuf);
+        if (a.nbuf == 1 && p + 1 < np) {
+            __syncthreads();  // both halves are done with the buffer
+            issue(p + 1);
         }
     }
 
-    if constexpr (S == 2) {
+    {
         // the upper half's partial sums join the lower half's (in that order)
         __syncthreads();  // the activation operand's bytes take them
         f32x4_t* part = reinterpret_cast<f32x4_t*>(lds);
@@ -412,17 +418,12 @@ int gs_piece(int64_t K)
 
 }  // namespace
 
-template <int FMT, int NW>
-static const void* gs_kernel_nw(int mode, bool traced)
-{
-    return mode == MODE_A ? (const void*)gemm_s_kernel<FMT, MODE_A, false, NW>
-           : traced       ? (const void*)gemm_s_kernel<FMT, MODE_B, true, NW>
-                          : (const void*)gemm_s_kernel<FMT, MODE_B, false, NW>;
-}
 template <int FMT>
-static const void* gs_kernel(int mode, bool traced, int nw)
+static const void* gs_kernel(int mode, bool traced)
 {
-    return nw == 8 ? gs_kernel_nw<FMT, 8>(mode, traced) : gs_kernel_nw<FMT, 4>(mode, traced);
+    return mode == MODE_A ? (const void*)gemm_s_kernel<FMT, MODE_A, false>
+           : traced       ? (const void*)gemm_s_kernel<FMT, MODE_B, true>
+                          : (const void*)gemm_s_kernel<FMT, MODE_B, false>;
 }
 
 // LDS bytes of a launch and its buffer plan: whole rows when they fit; else
@@ -500,13 +501,12 @@ hipError_t launch_gemm_s(int fmt, int mode, int count, const void* const* w, con
     const int64_t grid = (int64_t)a.nm * a.g.t0[count];
     if (grid < 1 || grid > 0x7fffffff || bytes > 160 * 1024) return hipErrorInvalidConfiguration;
     a.remap = grid % 8 == 0 ? 1 : 0;
-    const int nw = a.kp == (int)K ? 8 : 4;  // eight waves with whole rows
-    const void* k = fmt == FMT_Q8_0 ? gs_kernel<FMT_Q8_0>(mode, tr != nullptr, nw)
-                    : fmt == FMT_Q4_0 ? gs_kernel<FMT_Q4_0>(mode, tr != nullptr, nw)
-                                      : gs_kernel<FMT_Q5_0>(mode, tr != nullptr, nw);
+    const void* k = fmt == FMT_Q8_0 ? gs_kernel<FMT_Q8_0>(mode, tr != nullptr)
+                    : fmt == FMT_Q4_0 ? gs_kernel<FMT_Q4_0>(mode, tr != nullptr)
+                                      : gs_kernel<FMT_Q5_0>(mode, tr != nullptr);
     gs_allow_lds(k, bytes);
     void* args[] = {&a};
-    return hipLaunchKernel(k, dim3((unsigned)grid), dim3(64 * nw), args, (size_t)bytes, s);
+    return hipLaunchKernel(k, dim3((unsigned)grid), dim3(GS_NT), args, (size_t)bytes, s);
 }
 
 }  // namespace qmm
