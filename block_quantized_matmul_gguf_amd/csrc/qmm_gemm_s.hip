@@ -62,6 +62,8 @@ struct GemmSArgs {
 // Bytes of a block pair (64 values): Q8_0 d | 32 int8, Q4_0 d | qs[16],
 // Q5_0 d | qh[4] | qs[16], twice.
 constexpr int gs_lub(int fmt) { return fmt == FMT_Q8_0 ? 68 : fmt == FMT_Q4_0 ? 36 : 44; }
+// Bytes of a row: block pairs, or Q4_K super-blocks (144 B per 256 values).
+constexpr int64_t gs_row_bytes(int fmt, int64_t K) { return fmt == FMT_Q4_K ? K / 256 * 144 : K / 64 * gs_lub(fmt); }
 
 // Eight 5-bit codes (bytes of c0, c1) -> eight exact f16 (code - OFF) in order:
 // byte b under 0x64 is the f16 1024 + b, then one packed subtraction.
@@ -100,6 +102,7 @@ __global__ __launch_bounds__(GS_NT, 2) void gemm_s_kernel(GemmSArgs a)
 {
     constexpr int S = 2;  // halves of the workgroup
     constexpr int LUB = gs_lub(FMT), HALF = LUB / 2;
+    constexpr bool QK = FMT == FMT_Q4_K;  // Q4_K (mode (a), whole rows): super-blocks, not block pairs
     static_assert(!EMIT || MODE == MODE_B, "integer block sums exist in mode (b) only");
     extern __shared__ __align__(16) uint8_t lds[];
     const int K = a.K, M = a.M, nb = K / 32;
@@ -139,7 +142,7 @@ __global__ __launch_bounds__(GS_NT, 2) void gemm_s_kernel(GemmSArgs a)
     // (16 bytes from the piece's start) lands at row r * 16 cpr; a row's last chunk
     // may run past its piece (into bytes never read back). ----
     const bool whole = a.kp == K;
-    const int rs = whole ? a.row_bytes : 16 * a.cpr, pb = a.kp / 64 * LUB;
+    const int rs = whole ? a.row_bytes : 16 * a.cpr, pb = QK ? 0 : a.kp / 64 * LUB;
     const int64_t wb = (int64_t)n0 * a.row_bytes, wleft = (int64_t)N * a.row_bytes - wb;
     const rsrc_t wr = make_rsrc(W + (wleft > 0 ? wb : 0), wleft > 0 ? (uint32_t)min(wleft, (int64_t)16 * a.row_bytes) : 0u);
     const int nchunk = whole ? a.row_bytes : 16 * a.cpr, tl = (nchunk + 63) / 64;
@@ -191,10 +194,18 @@ __global__ __launch_bounds__(GS_NT, 2) void gemm_s_kernel(GemmSArgs a)
             const int j = S * i + hf;
             if (j < nj) {
                 _Float16 h[4], l[4];
-                float xs;
+                float xs[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) split_one(xv[i][e], sc, h[e], l[e], xs);
+                for (int e = 0; e < 4; ++e) split_one(xv[i][e], sc, h[e], l[e], xs[e]);
                 const int s = 2 * j + blk_hi;
+                if constexpr (QK) {
+                    // the 32-value sub-block's sum of x*2^e (the mins term), over its eight lanes
+                    float t = (xs[0] + xs[1]) + (xs[2] + xs[3]);
+                    t += dpp_f<DPP_X1>(t);
+                    t += dpp_f<DPP_X2>(t);
+                    t += dpp_f<DPP_HMIRROR>(t);
+                    if ((c16 & 7) == 0) reinterpret_cast<float*>(lds + a.off_dx + 256)[s * 16 + rho] = t;
+                }
                 uint8_t* dst = A + ((2 * s) * 64 + rho + 16 * kg) * 16 + half_off;
                 *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{gs_h2(h[0], h[1]), gs_h2(h[2], h[3])};
                 *reinterpret_cast<u32x2_t*>(dst + 1024) = u32x2_t{gs_h2(l[0], l[1]), gs_h2(l[2], l[3])};
@@ -245,8 +256,6 @@ __global__ __launch_bounds__(GS_NT, 2) void gemm_s_kernel(GemmSArgs a)
     f32x4_t acc = zf;
     const int ppp = a.kp / 64;  // block pairs per piece
     for (int p = 0; p < np; ++p) {
-        // this wave's piece p has landed (piece p + 1 may still be in flight; traced
-        // runs' stores are counted too, so they wait for everything)
         // both halves read the block's rows: each waits for its loads of piece p (traced
         // runs' stores count too, so they wait for everything), then a barrier; piece
         // p + 1 then goes into the buffer of piece p - 1, which every wave is done with
@@ -256,6 +265,37 @@ __global__ __launch_bounds__(GS_NT, 2) void gemm_s_kernel(GemmSArgs a)
         __syncthreads();
         if (a.nbuf > 1 && p >= 1 && p + 1 < np) issue(p + 1);
         const uint8_t* rrow = lds + a.off_b + (blk * a.nbuf + p % a.nbuf) * a.bsz + n * rs;
+        if constexpr (QK) {
+            // super-blocks u of this wave's half: f16 d, dmin | 12 bytes of 6-bit scales
+            // and mins | 128 bytes of nibbles (sub-block 2c: low nibbles of bytes 32c ..
+            // 32c+31, 2c+1: high nibbles); the weights enter as exact f16 q (0 .. 15),
+            // acc += (d sc_j) C_j - (dmin m_j) X_j with X_j the sub-block's sum of x*2^e
+            const int nsb = K / 256, hq = (nsb + 1) / 2, ua = hf * hq, ub = min(nsb, ua + hq);
+            const float* xsum = reinterpret_cast<const float*>(lds + a.off_dx + 256);
+            for (int u = ua; u < ub; ++u) {
+                const uint8_t* rp = rrow + 144 * u;
+                const u32x4_t H = lds128(rp);
+                const float d = f16lo(H[0]), dmin = f16hi(H[0]);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const u32x2_t Qv = lds64(rp + 16 + 32 * c + 8 * g);
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const int jj = 2 * c + hh, s = 8 * u + jj;
+                        int scj, mnj;
+                        q4k_scale_min(H[1], H[2], H[3], jj, scj, mnj);
+                        const half8_t B = gs_codes_f16<0>((Qv[0] >> (4 * hh)) & 0x0f0f0f0fu, (Qv[1] >> (4 * hh)) & 0x0f0f0f0fu);
+                        f32x4_t C = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, lds128(A + ((2 * s) * 64 + lane) * 16)), B, zf, 0, 0, 0);
+                        C = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, lds128(A + ((2 * s + 1) * 64 + lane) * 16)), B, C, 0, 0, 0);
+                        const f32x4_t X = *reinterpret_cast<const f32x4_t*>(xsum + s * 16 + 4 * g);
+                        const float ds = d * (float)scj, dm = dmin * (float)mnj;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc[i] = fmaf(-dm, X[i], fmaf(ds, C[i], acc[i]));
+                    }
+                }
+            }
+            continue;
+        }
         const int hp = (ppp + S - 1) / S, qa = hf * hp, qb = min(ppp, qa + hp);  // this wave's pairs
         // software-pipelined over the piece's block pairs: the operands of pair q + 1
         // are read while pair q is on the matrix cores, and pair q's scales are
@@ -434,12 +474,13 @@ static int gs_plan(int fmt, int mode, int64_t K, GemmSArgs& a)
     const int nb = (int)(K / 32), lub = gs_lub(fmt);
     // the activation operand's bytes also take the upper half's partial sums (4 KB)
     const int abytes = std::max(mode == MODE_A ? nb * 2048 : nb * 1024, 4096);
-    const int dxbytes = mode == MODE_A ? 256 : nb * 64;
-    a.row_bytes = (int)(K / 64) * lub;
+    // mode (a): row exponents, the halves' row maxima; Q4_K also the sub-block sums [K/32][16]
+    const int dxbytes = mode == MODE_A ? 256 + (fmt == FMT_Q4_K ? nb * 64 : 0) : nb * 64;
+    a.row_bytes = (int)gs_row_bytes(fmt, K);
     a.off_dx = abytes;
     a.off_b = (abytes + dxbytes + 15) & ~15;
     const int room = 160 * 1024 - a.off_b;
-    if (4 * 16 * a.row_bytes <= room) {
+    if (4 * 16 * a.row_bytes <= room || fmt == FMT_Q4_K) {  // Q4_K: whole rows only
         a.kp = (int)K;
         a.cpr = 0;
         a.nbuf = 1;
@@ -467,7 +508,8 @@ static int gs_plan(int fmt, int mode, int64_t K, GemmSArgs& a)
 // kernel of its own run.
 bool gemm_s_supported(int fmt, int mode, int64_t K, int64_t Ntot, int64_t M)
 {
-    if (!((fmt == FMT_Q8_0 || fmt == FMT_Q4_0 || fmt == FMT_Q5_0) && M > GEMV_MAX_M && K > 0 && K % 64 == 0 && K <= GS_KMAX && Ntot > 0 && Ntot <= GS_NMAX))
+    if (fmt == FMT_Q4_K && !(mode == MODE_A && K % 256 == 0)) return false;
+    if (!((fmt == FMT_Q8_0 || fmt == FMT_Q4_0 || fmt == FMT_Q5_0 || fmt == FMT_Q4_K) && M > GEMV_MAX_M && K > 0 && K % 64 == 0 && K <= GS_KMAX && Ntot > 0 && Ntot <= GS_NMAX))
         return false;
     GemmSArgs a{};
     const int bytes = gs_plan(fmt, mode, K, a);
@@ -479,7 +521,8 @@ hipError_t launch_gemm_s(int fmt, int mode, int count, const void* const* w, con
                          const float* x, int64_t K, int64_t M, hipStream_t s, const Trace* tr)
 {
     if (count < 1 || count > PG_MAX || (tr && (count != 1 || mode != MODE_B))) return hipErrorInvalidValue;
-    if (!(K > 0 && K % 64 == 0 && K <= GS_KMAX && M > 0) || !(fmt == FMT_Q8_0 || fmt == FMT_Q4_0 || fmt == FMT_Q5_0))
+    if (!(K > 0 && K % 64 == 0 && K <= GS_KMAX && M > 0) ||
+        !(fmt == FMT_Q8_0 || fmt == FMT_Q4_0 || fmt == FMT_Q5_0 || (fmt == FMT_Q4_K && mode == MODE_A && !tr && K % 256 == 0)))
         return hipErrorInvalidValue;
     GemmSArgs a{};
     a.g.groups = count;
@@ -503,7 +546,8 @@ hipError_t launch_gemm_s(int fmt, int mode, int count, const void* const* w, con
     a.remap = grid % 8 == 0 ? 1 : 0;
     const void* k = fmt == FMT_Q8_0 ? gs_kernel<FMT_Q8_0>(mode, tr != nullptr)
                     : fmt == FMT_Q4_0 ? gs_kernel<FMT_Q4_0>(mode, tr != nullptr)
-                                      : gs_kernel<FMT_Q5_0>(mode, tr != nullptr);
+                    : fmt == FMT_Q5_0 ? gs_kernel<FMT_Q5_0>(mode, tr != nullptr)
+                                      : (const void*)gemm_s_kernel<FMT_Q4_K, MODE_A, false>;
     gs_allow_lds(k, bytes);
     void* args[] = {&a};
     return hipLaunchKernel(k, dim3((unsigned)grid), dim3(GS_NT), args, (size_t)bytes, s);
