@@ -102,7 +102,7 @@ __global__ __launch_bounds__(GS_NT, 2) void gemm_s_kernel(GemmSArgs a)
 {
     constexpr int S = 2;  // halves of the workgroup
     constexpr int LUB = gs_lub(FMT), HALF = LUB / 2;
-    constexpr bool QK = FMT == FMT_Q4_K;  // Q4_K (mode (a), whole rows): super-blocks, not block pairs
+    constexpr bool QK = FMT == FMT_Q4_K;  // Q4_K (whole rows): super-blocks, not block pairs
     static_assert(!EMIT || MODE == MODE_B, "integer block sums exist in mode (b) only");
     extern __shared__ __align__(16) uint8_t lds[];
     const int K = a.K, M = a.M, nb = K / 32;
@@ -211,6 +211,98 @@ __global__ __launch_bounds__(GS_NT, 2) void gemm_s_kernel(GemmSArgs a)
                 *reinterpret_cast<u32x2_t*>(dst + 1024) = u32x2_t{gs_h2(l[0], l[1]), gs_h2(l[2], l[3])};
             }
         }
+    } else if constexpr (QK) {
+        // Q8K per 256 values (super-block u: chunks 4u .. 4u+3, the halves holding
+        // alternate ones): the signed element of largest |x|, the first index on ties,
+        // met over the row's 16 lanes (DPP) and then over the two halves (LDS); the
+        // values, the sums of each 16 and of each 32 (the mins term) in LDS
+        const int nsb = K / 256;
+        float* dxk = reinterpret_cast<float*>(lds + a.off_dx);                  // [u][16] d_x
+        int* bsub = reinterpret_cast<int*>(lds + a.off_dx + nsb * 64);          // [K/32][16] sums of 32
+        float* meet = reinterpret_cast<float*>(lds + a.off_dx + nsb * 64 + nb * 64);  // [u][half][16][3]
+        float kbest[GS_JMAX / 4], kbv[GS_JMAX / 4];
+        int kidx[GS_JMAX / 4];
+#pragma unroll
+        for (int u = 0; u < GS_JMAX / 4; ++u) {
+            float best = -1.0f, bv = 0.0f;
+            int bidx = 0;
+#pragma unroll
+            for (int i = 0; i < JI; ++i) {
+                const int j = S * i + hf;
+                if (j < nj && (j >> 2) == u) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float v = xv[i][e];
+                        if (fabsf(v) > best) { best = fabsf(v); bv = v; bidx = 64 * (j & 3) + 4 * c16 + e; }
+                    }
+                }
+            }
+            auto meet1 = [&](float ob, float obv, int oidx) {
+                if (ob > best || (ob == best && oidx < bidx)) { best = ob; bv = obv; bidx = oidx; }
+            };
+            meet1(dpp_f<DPP_X1>(best), dpp_f<DPP_X1>(bv), dpp_i<DPP_X1>(bidx));
+            meet1(dpp_f<DPP_X2>(best), dpp_f<DPP_X2>(bv), dpp_i<DPP_X2>(bidx));
+            meet1(dpp_f<DPP_HMIRROR>(best), dpp_f<DPP_HMIRROR>(bv), dpp_i<DPP_HMIRROR>(bidx));
+            meet1(dpp_f<DPP_MIRROR>(best), dpp_f<DPP_MIRROR>(bv), dpp_i<DPP_MIRROR>(bidx));
+            if (u < nsb && c16 == 0) {
+                float* m3 = meet + ((u * 2 + hf) * 16 + rho) * 3;
+                m3[0] = best;
+                m3[1] = bv;
+                m3[2] = __int_as_float(bidx);
+            }
+            kbest[u] = best;
+            kbv[u] = bv;
+            kidx[u] = bidx;
+        }
+        __syncthreads();
+        float kis[GS_JMAX / 4];
+#pragma unroll
+        for (int u = 0; u < GS_JMAX / 4; ++u) {
+            float best = kbest[u], bv = kbv[u];
+            int bidx = kidx[u];
+            if (u < nsb) {
+                const float* m3 = meet + ((u * 2 + (hf ^ 1)) * 16 + rho) * 3;
+                const float ob = m3[0], obv = m3[1];
+                const int oidx = __float_as_int(m3[2]);
+                if (ob > best || (ob == best && oidx < bidx)) { best = ob; bv = obv; bidx = oidx; }
+            }
+            float dk;
+            q8k_scale(bv, best, kis[u], dk);
+            if (u < nsb && c16 == 0 && hf == 0) dxk[u * 16 + rho] = dk;
+            if constexpr (EMIT)
+                if (u < nsb && c16 == 0 && hf == 0 && nt == 0 && a.act != nullptr && m0 + rho < M)
+                    *reinterpret_cast<float*>(a.act + ((int64_t)(m0 + rho) * nsb + u) * 292) = dk;
+        }
+#pragma unroll
+        for (int i = 0; i < JI; ++i) {
+            const int j = S * i + hf;
+            if (j < nj) {
+                float isc = kis[0];
+#pragma unroll
+                for (int u = 1; u < GS_JMAX / 4; ++u) isc = (j >> 2) == u ? kis[u] : isc;
+                int q[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) q[e] = q8k_q(xv[i][e], isc);
+                const int s = 2 * j + blk_hi;
+                uint8_t* dst = A + (s * 64 + rho + 16 * kg) * 16 + half_off;
+                *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{gs_h2((_Float16)q[0], (_Float16)q[1]), gs_h2((_Float16)q[2], (_Float16)q[3])};
+                // sums of 16 (a lane quad) and of 32 (eight lanes)
+                int s16 = (q[0] + q[1]) + (q[2] + q[3]);
+                s16 += dpp_i<DPP_X1>(s16);
+                s16 += dpp_i<DPP_X2>(s16);
+                const int s32 = s16 + dpp_i<DPP_HMIRROR>(s16);
+                if ((c16 & 7) == 0) bsub[s * 16 + rho] = s32;
+                if constexpr (EMIT) {
+                    if (nt == 0 && a.act != nullptr && m0 + rho < M) {
+                        // canonical Q8K block j / 4 of row m0 + rho: f32 d, 256 int8, int16 sums of 16
+                        uint8_t* o = a.act + ((int64_t)(m0 + rho) * nsb + (j >> 2)) * 292;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) o[4 + 64 * (j & 3) + 4 * c16 + e] = (uint8_t)q[e];
+                        if ((c16 & 3) == 0) reinterpret_cast<int16_t*>(o + 260)[4 * (j & 3) + (c16 >> 2)] = (int16_t)s16;
+                    }
+                }
+            }
+        }
     } else {
         float* dxs = reinterpret_cast<float*>(lds + a.off_dx);
 #pragma unroll
@@ -270,12 +362,17 @@ __global__ __launch_bounds__(GS_NT, 2) void gemm_s_kernel(GemmSArgs a)
             // and mins | 128 bytes of nibbles (sub-block 2c: low nibbles of bytes 32c ..
             // 32c+31, 2c+1: high nibbles); the weights enter as exact f16 q (0 .. 15),
             // acc += (d sc_j) C_j - (dmin m_j) X_j with X_j the sub-block's sum of x*2^e
+            // mode (b): S_j exact (q up to 15 against int8 values: below 2^24), sumi and
+            // summins in int32, acc += d_x (d sumi - dmin summins)
             const int nsb = K / 256, hq = (nsb + 1) / 2, ua = hf * hq, ub = min(nsb, ua + hq);
             const float* xsum = reinterpret_cast<const float*>(lds + a.off_dx + 256);
+            const float* dxk = reinterpret_cast<const float*>(lds + a.off_dx);
+            const int* bsub = reinterpret_cast<const int*>(lds + a.off_dx + nsb * 64);
             for (int u = ua; u < ub; ++u) {
                 const uint8_t* rp = rrow + 144 * u;
                 const u32x4_t H = lds128(rp);
                 const float d = f16lo(H[0]), dmin = f16hi(H[0]);
+                int sumi[4] = {0, 0, 0, 0}, summ[4] = {0, 0, 0, 0};
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     const u32x2_t Qv = lds64(rp + 16 + 32 * c + 8 * g);
@@ -285,12 +382,44 @@ __global__ __launch_bounds__(GS_NT, 2) void gemm_s_kernel(GemmSArgs a)
                         int scj, mnj;
                         q4k_scale_min(H[1], H[2], H[3], jj, scj, mnj);
                         const half8_t B = gs_codes_f16<0>((Qv[0] >> (4 * hh)) & 0x0f0f0f0fu, (Qv[1] >> (4 * hh)) & 0x0f0f0f0fu);
-                        f32x4_t C = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, lds128(A + ((2 * s) * 64 + lane) * 16)), B, zf, 0, 0, 0);
-                        C = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, lds128(A + ((2 * s + 1) * 64 + lane) * 16)), B, C, 0, 0, 0);
-                        const f32x4_t X = *reinterpret_cast<const f32x4_t*>(xsum + s * 16 + 4 * g);
-                        const float ds = d * (float)scj, dm = dmin * (float)mnj;
+                        if constexpr (MODE == MODE_A) {
+                            f32x4_t C = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, lds128(A + ((2 * s) * 64 + lane) * 16)), B, zf, 0, 0, 0);
+                            C = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, lds128(A + ((2 * s + 1) * 64 + lane) * 16)), B, C, 0, 0, 0);
+                            const f32x4_t X = *reinterpret_cast<const f32x4_t*>(xsum + s * 16 + 4 * g);
+                            const float ds = d * (float)scj, dm = dmin * (float)mnj;
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) acc[i] = fmaf(-dm, X[i], fmaf(ds, C[i], acc[i]));
+                            for (int i = 0; i < 4; ++i) acc[i] = fmaf(-dm, X[i], fmaf(ds, C[i], acc[i]));
+                        } else {
+                            const f32x4_t C = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, lds128(A + (s * 64 + lane) * 16)), B, zf, 0, 0, 0);
+                            const i32x4_t Bs = *reinterpret_cast<const i32x4_t*>(bsub + s * 16 + 4 * g);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                sumi[i] += scj * (int)C[i];
+                                summ[i] += mnj * Bs[i];
+                            }
+                            if constexpr (EMIT) {
+                                if (col < N)
+#pragma unroll
+                                    for (int i = 0; i < 4; ++i)
+                                        if (m0 + 4 * g + i < M)
+                                            a.sums[(((int64_t)(m0 + 4 * g + i) * N + col) * nsb + u) * 10 + jj] = (int32_t)C[i];
+                            }
+                        }
+                    }
+                }
+                if constexpr (MODE == MODE_B) {
+                    const f32x4_t dx = *reinterpret_cast<const f32x4_t*>(dxk + u * 16 + 4 * g);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[i] = fmaf(dx[i] * d, (float)sumi[i], fmaf(-dx[i] * dmin, (float)summ[i], acc[i]));
+                    if constexpr (EMIT) {
+                        if (col < N)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                if (m0 + 4 * g + i < M) {
+                                    int32_t* o = a.sums + (((int64_t)(m0 + 4 * g + i) * N + col) * nsb + u) * 10;
+                                    o[8] = sumi[i];
+                                    o[9] = summ[i];
+                                }
                     }
                 }
             }
@@ -475,7 +604,10 @@ static int gs_plan(int fmt, int mode, int64_t K, GemmSArgs& a)
     // the activation operand's bytes also take the upper half's partial sums (4 KB)
     const int abytes = std::max(mode == MODE_A ? nb * 2048 : nb * 1024, 4096);
     // mode (a): row exponents, the halves' row maxima; Q4_K also the sub-block sums [K/32][16]
-    const int dxbytes = mode == MODE_A ? 256 + (fmt == FMT_Q4_K ? nb * 64 : 0) : nb * 64;
+    const int nsb = (int)(K / 256);
+    const int dxbytes = mode == MODE_A ? 256 + (fmt == FMT_Q4_K ? nb * 64 : 0)
+                        : fmt == FMT_Q4_K ? nsb * 64 + nb * 64 + nsb * 2 * 16 * 12  // d_x, sums of 32, the halves' maxima
+                                          : nb * 64;
     a.row_bytes = (int)gs_row_bytes(fmt, K);
     a.off_dx = abytes;
     a.off_b = (abytes + dxbytes + 15) & ~15;
@@ -508,7 +640,7 @@ static int gs_plan(int fmt, int mode, int64_t K, GemmSArgs& a)
 // kernel of its own run.
 bool gemm_s_supported(int fmt, int mode, int64_t K, int64_t Ntot, int64_t M)
 {
-    if (fmt == FMT_Q4_K && !(mode == MODE_A && K % 256 == 0)) return false;
+    if (fmt == FMT_Q4_K && K % 256 != 0) return false;
     if (!((fmt == FMT_Q8_0 || fmt == FMT_Q4_0 || fmt == FMT_Q5_0 || fmt == FMT_Q4_K) && M > GEMV_MAX_M && K > 0 && K % 64 == 0 && K <= GS_KMAX && Ntot > 0 && Ntot <= GS_NMAX))
         return false;
     GemmSArgs a{};
@@ -522,7 +654,7 @@ hipError_t launch_gemm_s(int fmt, int mode, int count, const void* const* w, con
 {
     if (count < 1 || count > PG_MAX || (tr && (count != 1 || mode != MODE_B))) return hipErrorInvalidValue;
     if (!(K > 0 && K % 64 == 0 && K <= GS_KMAX && M > 0) ||
-        !(fmt == FMT_Q8_0 || fmt == FMT_Q4_0 || fmt == FMT_Q5_0 || (fmt == FMT_Q4_K && mode == MODE_A && !tr && K % 256 == 0)))
+        !(fmt == FMT_Q8_0 || fmt == FMT_Q4_0 || fmt == FMT_Q5_0 || (fmt == FMT_Q4_K && K % 256 == 0)))
         return hipErrorInvalidValue;
     GemmSArgs a{};
     a.g.groups = count;
@@ -547,7 +679,7 @@ hipError_t launch_gemm_s(int fmt, int mode, int count, const void* const* w, con
     const void* k = fmt == FMT_Q8_0 ? gs_kernel<FMT_Q8_0>(mode, tr != nullptr)
                     : fmt == FMT_Q4_0 ? gs_kernel<FMT_Q4_0>(mode, tr != nullptr)
                     : fmt == FMT_Q5_0 ? gs_kernel<FMT_Q5_0>(mode, tr != nullptr)
-                                      : (const void*)gemm_s_kernel<FMT_Q4_K, MODE_A, false>;
+                                      : gs_kernel<FMT_Q4_K>(mode, tr != nullptr);
     gs_allow_lds(k, bytes);
     void* args[] = {&a};
     return hipLaunchKernel(k, dim3((unsigned)grid), dim3(GS_NT), args, (size_t)bytes, s);

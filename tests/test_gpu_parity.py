@@ -233,6 +233,7 @@ TRACED = [
     (qmm.Q4_K, 100, 1536, 37), (qmm.Q4_K, 300, 4096, 130), (qmm.Q4_K, 70, 256, 9),
     (qmm.Q8_0, 100, 1088, 20), (qmm.Q8_0, 70, 1536, 37), (qmm.Q8_0, 40, 64, 9),
     (qmm.Q4_0, 70, 576, 37), (qmm.Q5_0, 100, 1088, 20), (qmm.Q5_0, 130, 1536, 9),
+    (qmm.Q4_K, 70, 1536, 307), (qmm.Q4_K, 200, 512, 20),
 ]
 
 
@@ -355,7 +356,7 @@ def test_grouped_run_equals_separate_runs(fmt, k, ns, mode, m):
         assert_within(grp[i], yr, a, f"group plan {i} {FMT_NAME[fmt]} {n}x{k} M={m} mode={mode}")
 
 
-# Prefill with short rows (Q8_0, Q4_0, Q5_0, and Q4_K in mode (a); K <= 1536, at most 8192 columns, a
+# Prefill with short rows (Q8_0, Q4_0, Q5_0, Q4_K; K <= 1536, at most 8192 columns, a
 # one-round grid): one launch that prepares its own activations.  Whole rows
 # staged at once and in pieces (mode (a) at K = 1536: four of 384, two buffers
 # per wave), block pairs from K = 64 up, ragged M and N, the widest launch; rows
@@ -365,7 +366,7 @@ SHORT = [(qmm.Q8_0, 40, 64, 9), (qmm.Q8_0, 200, 576, 17), (qmm.Q8_0, 576, 576, 3
          (qmm.Q8_0, 70, 1536, 307), (qmm.Q8_0, 8100, 1536, 9),
          (qmm.Q4_0, 40, 64, 9), (qmm.Q4_0, 576, 576, 307), (qmm.Q4_0, 100, 1088, 20), (qmm.Q4_0, 576, 1536, 37),
          (qmm.Q5_0, 40, 128, 9), (qmm.Q5_0, 576, 576, 307), (qmm.Q5_0, 130, 1024, 37), (qmm.Q5_0, 70, 1536, 307),
-         # Q4_K in mode (a) (mode (b) keeps the K-staged kernels): super-blocks, whole rows
+         # Q4_K: super-blocks, whole rows (mode (b): Q8K values and sums formed in the launch)
          (qmm.Q4_K, 100, 256, 9), (qmm.Q4_K, 300, 512, 20), (qmm.Q4_K, 576, 1536, 37), (qmm.Q4_K, 70, 1536, 307)]
 
 
