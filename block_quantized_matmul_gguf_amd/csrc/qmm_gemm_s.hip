@@ -1,5 +1,5 @@
-// qmm_gemm_s.hip -- prefill (M > 8) of Q8_0, Q4_0 and Q5_0 weights with short
-// rows (K <= 1536), the activation preparation done inside the launch.
+// qmm_gemm_s.hip -- prefill (M > 8) of Q8_0, Q4_0, Q5_0 and Q4_K weights with
+// short rows (K <= 1536), the activation preparation done inside the launch.
 //
 // The pages' SmolLM2-135M prefill (page "GGUF", section 在 candle 里跑一个 GGUF:
 // a 37-token prompt, then 270 teacher-forced tokens) is 211 products with K =
@@ -12,14 +12,16 @@
 //     LDS buffer with 16-byte buffer-to-LDS loads; rows past N read as zero;
 //   * the workgroup loads its 16 activation rows (f32) into registers, a row
 //     per 16 lanes, and prepares them itself: mode (a) the row's power-of-two
-//     scale and the f16 hi/lo split, mode (b) the Q8_0 blocks through the
-//     standalone quantizer's device functions (the same bytes), written to LDS
-//     in matrix-core operand order;
+//     scale and the f16 hi/lo split, mode (b) the Q8_0 (Q8K for Q4_K) blocks
+//     through the standalone quantizer's device functions (the same bytes),
+//     written to LDS in matrix-core operand order;
 //   * v_mfma_f32_16x16x32_f16 per 32-value block: A = the 16 rows' hi and
 //     then lo parts (mode (a)) or their int8 values as exact f16 (mode (b):
 //     the f32 sum is the exact integer block sum), B = the block's weights as
 //     exact f16 (Q8_0 q, Q4_0 q - 8, Q5_0 q - 16, decoded from block pairs,
 //     the 4-byte-aligned load units); acc += d_w C (mode (a)), (d_w d_x) C (b).
+//     Q4_K: the nibbles q per 32-value sub-block, with the scales, mins and
+//     (mode (b)) the integer sumi and summins applied per super-block.
 // Grouped launches number the problems' column tiles end to end; traced runs
 // (mode (b)) write the block sums and the quantized activation blocks.
 #include <algorithm>
