@@ -106,10 +106,12 @@ int qmatmul_create(qmm_plan** out, int format, int64_t N, int64_t K, int64_t M_m
  * decode (GEMV) kernels, larger M the prefill (GEMM) kernels.  The caller owns
  * w, x and y; the plan keeps no pointer after the call.  The plan's workspace
  * is shared by its runs: do not run one plan concurrently on two streams.
- * Q4_0 and Q5_0 runs with M > 8 first rewrite the weights as Q8_0 blocks
- * (the same dequantized values) in the plan's workspace and take the Q8_0
- * prefill kernels; Q6_K runs with M > 8 take their own prefill kernel (both
- * modes) on the f16 matrix cores.
+ * At M > 8, Q8_0, Q4_0, Q5_0 and Q4_K runs with short rows (K <= 1536, at
+ * most 8192 rows of W, a grid of at most one workgroup per compute unit) take
+ * one launch that prepares its own activations; other Q4_0 and Q5_0 runs
+ * first rewrite the weights as Q8_0 blocks (the same dequantized values) in
+ * the plan's workspace and take the Q8_0 prefill kernels; Q6_K runs with
+ * M > 8 take their own prefill kernel (both modes) on the f16 matrix cores.
  * A run only enqueues kernels (no allocation, memset or synchronization), so
  * runs may be captured in a HIP graph once each kernel has run eagerly (its
  * launch attributes are set on first use); the exception is a
@@ -130,8 +132,9 @@ int qmatmul_run(const qmm_plan* plan, const void* w_blocks, const float* x, floa
  * Q4_0, Q5_0 and Q6_K (where their activations fit in LDS), the plans' rows
  * go to one launch per four plans (the activations are loaded and quantized
  * once per workgroup for all of them), giving bit-for-bit the values
- * separate runs give; at M > 8 the activations are prepared once and the
- * plans' output tiles go to one prefill launch per four plans (again the
+ * separate runs give; at M > 8 each plan takes the prefill kernel its own run
+ * takes, the plans' output tiles going to one launch per four plans of that
+ * kernel (the activations prepared once for the K-staged kernels; again the
  * separate runs' values bit for bit); otherwise the plans run one after
  * another as with qmatmul_run.  Errors: as
  * qmatmul_run for each plan, and QMM_EINVAL for null arrays, count out of
@@ -242,14 +245,16 @@ int qmatmul_quantize_q4_k_search(const float* w, int64_t N, int64_t K, void* out
  *       sum_j sc_j*S_j and summins = sum_j m_j*(bsums[2j]+bsums[2j+1]);
  *     Q6_K: per super-block 17 values S_0..S_15 (per 16, qw = q - 32) and
  *       sumi = sum_j sc_j*S_j.
- *     At M > 8 the Q4_K prefill kernel scales each S_j on its own and never
- *     forms sumi; there sumi is summed from the S_j it wrote.  The Q6_K
+ *     At M > 8 the K-staged Q4_K prefill kernel scales each S_j on its own
+ *     and never forms sumi; there sumi is summed from the S_j it wrote (the
+ *     short-row kernel forms it in int32 itself).  The Q6_K
  *     prefill kernel (M > 8) carries the scales in its weight operand and
  *     forms sumi exactly but no per-16 sums: there S_0..S_15 read INT32_MIN.
  *   act_blocks: device, M * qmatmul_row_bytes(Q8_0 or Q8_K, K) bytes, 4-byte
  *     aligned, or NULL: the canonical quantized activation blocks, written by
  *     the kernel that quantizes them in this run (a decode kernel's own
- *     prologue, or the activation preparation of the prefill).
+ *     prologue, the short-row prefill's, or the prefill's activation
+ *     preparation).
  * Same preconditions and errors as qmatmul_run; sums must not be NULL.
  */
 int qmatmul_run_traced(const qmm_plan* plan, const void* w_blocks, const float* x, float* y, int32_t* sums,
