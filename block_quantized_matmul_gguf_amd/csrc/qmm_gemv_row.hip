@@ -717,11 +717,11 @@ static int gr_ring(int fmt, int64_t K)
     return gr_layout(fmt, K, 3).bytes <= GR_LDS_MAX ? 3 : 2;
 }
 
-// Rows shorter than a segment leave lanes idle while mode (a)'s per-row
-// arithmetic still costs the whole wave: with fewer than half the lanes busy
-// and more than four rows per wave, mode (a) stays on the tile kernel (the
-// 49152 x 576 lm_head: 21.6 us here against 8.5 us there; 576-row shapes run
-// faster here).
+// Rows shorter than a segment leave lanes idle while the per-row arithmetic
+// still costs the whole wave: with fewer than half the lanes busy and more
+// than four rows per wave, both modes stay on the tile kernel (the 49152 x 576
+// lm_head with its blocks in the caches: mode (a) 21.6 us here against 8.5 us
+// there, mode (b) 13.0 against 7.8 us; 576-row shapes run faster here).
 bool gemv_row_supported(int fmt, int mode, int M, int64_t N, int64_t K, bool emit)
 {
     if ((mode != MODE_A && mode != MODE_B) || M != 1 || (emit && mode != MODE_B)) return false;
@@ -733,7 +733,7 @@ bool gemv_row_supported(int fmt, int mode, int M, int64_t N, int64_t K, bool emi
     const int vpu = gr_unit_values(fmt);
     const int nseg_max = mode == MODE_A ? 1 : GR_NSEG_MAX;  // mode (a) holds one segment's f32 activations
     if (K % vpu != 0 || K / vpu > (int64_t)nseg_max * gr_seg_units(fmt)) return false;
-    if (mode == MODE_A) {
+    {
         const int64_t lanes = (K / vpu) * (gr_kq(fmt) ? 4 : 1);
         const int64_t rows_per_wave = (N + GR_WAVES * (int64_t)device_cus() - 1) / (GR_WAVES * (int64_t)device_cus());
         if (lanes < 32 && rows_per_wave > 4) return false;
