@@ -125,14 +125,16 @@ __global__ __launch_bounds__(GS_NT, 2) void gemm_s_kernel(GemmSArgs a)
 
     // ---- activations: row rho of the tile in lanes 16 rho .. +15 (one DPP row),
     // lane c16 holding values 64 j + 4 c16 .. +3; rows past M read as zero ----
-    // (half hf takes the chunks j = 2 i + hf)
+    // (half hf takes the chunks j = 2 i + hf; for Q4_K whole super-blocks, the
+    // chunks of super-blocks hf, hf + 2, ..., so a Q8K block stays in one half)
+    auto jof = [&](int i) { return QK ? 4 * (2 * (i >> 2) + hf) + (i & 3) : S * i + hf; };
     const int rho = (tid & 255) >> 4, c16 = tid & 15, nj = K / 64;
     const rsrc_t xr = make_rsrc(a.x + (int64_t)m0 * K, clamp_u32((int64_t)(M - m0) * K * 4));
     constexpr int JI = GS_JMAX / S;
     f32x4_t xv[JI];
 #pragma unroll
     for (int i = 0; i < JI; ++i) {
-        const int j = S * i + hf;
+        const int j = jof(i);
         xv[i] = j < nj ? __builtin_bit_cast(f32x4_t, ld128(xr, (uint32_t)(rho * K + 64 * j + 4 * c16) * 4u))
                        : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
@@ -175,7 +177,7 @@ __global__ __launch_bounds__(GS_NT, 2) void gemm_s_kernel(GemmSArgs a)
         float mx = 0.0f;
 #pragma unroll
         for (int i = 0; i < JI; ++i)
-            if (S * i + hf < nj)
+            if (jof(i) < nj)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fabsf(xv[i][e]));
         mx = fmaxf(mx, dpp_f<DPP_X1>(mx));
@@ -193,7 +195,7 @@ __global__ __launch_bounds__(GS_NT, 2) void gemm_s_kernel(GemmSArgs a)
         if (c16 == 0 && hf == 0) reinterpret_cast<int*>(lds + a.off_dx)[rho] = ex;
 #pragma unroll
         for (int i = 0; i < JI; ++i) {
-            const int j = S * i + hf;
+            const int j = jof(i);
             if (j < nj) {
                 _Float16 h[4], l[4];
                 float xs[4];
@@ -214,23 +216,21 @@ __global__ __launch_bounds__(GS_NT, 2) void gemm_s_kernel(GemmSArgs a)
             }
         }
     } else if constexpr (QK) {
-        // Q8K per 256 values (super-block u: chunks 4u .. 4u+3, the halves holding
-        // alternate ones): the signed element of largest |x|, the first index on ties,
-        // met over the row's 16 lanes (DPP) and then over the two halves (LDS); the
-        // values, the sums of each 16 and of each 32 (the mins term) in LDS
+        // Q8K per 256 values (super-block u: chunks 4u .. 4u+3, all in half u % 2):
+        // the signed element of largest |x|, the first index on ties, met over the
+        // row's 16 lanes (DPP); the values, the sums of each 16 and of each 32 (the
+        // mins term) in LDS
         const int nsb = K / 256;
         float* dxk = reinterpret_cast<float*>(lds + a.off_dx);                  // [u][16] d_x
         int* bsub = reinterpret_cast<int*>(lds + a.off_dx + nsb * 64);          // [K/32][16] sums of 32
-        float* meet = reinterpret_cast<float*>(lds + a.off_dx + nsb * 64 + nb * 64);  // [u][half][16][3]
-        float kbest[GS_JMAX / 4], kbv[GS_JMAX / 4];
-        int kidx[GS_JMAX / 4];
+        float kis[GS_JMAX / 4];
 #pragma unroll
         for (int u = 0; u < GS_JMAX / 4; ++u) {
             float best = -1.0f, bv = 0.0f;
             int bidx = 0;
 #pragma unroll
             for (int i = 0; i < JI; ++i) {
-                const int j = S * i + hf;
+                const int j = jof(i);
                 if (j < nj && (j >> 2) == u) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -246,38 +246,16 @@ __global__ __launch_bounds__(GS_NT, 2) void gemm_s_kernel(GemmSArgs a)
             meet1(dpp_f<DPP_X2>(best), dpp_f<DPP_X2>(bv), dpp_i<DPP_X2>(bidx));
             meet1(dpp_f<DPP_HMIRROR>(best), dpp_f<DPP_HMIRROR>(bv), dpp_i<DPP_HMIRROR>(bidx));
             meet1(dpp_f<DPP_MIRROR>(best), dpp_f<DPP_MIRROR>(bv), dpp_i<DPP_MIRROR>(bidx));
-            if (u < nsb && c16 == 0) {
-                float* m3 = meet + ((u * 2 + hf) * 16 + rho) * 3;
-                m3[0] = best;
-                m3[1] = bv;
-                m3[2] = __int_as_float(bidx);
-            }
-            kbest[u] = best;
-            kbv[u] = bv;
-            kidx[u] = bidx;
-        }
-        __syncthreads();
-        float kis[GS_JMAX / 4];
-#pragma unroll
-        for (int u = 0; u < GS_JMAX / 4; ++u) {
-            float best = kbest[u], bv = kbv[u];
-            int bidx = kidx[u];
-            if (u < nsb) {
-                const float* m3 = meet + ((u * 2 + (hf ^ 1)) * 16 + rho) * 3;
-                const float ob = m3[0], obv = m3[1];
-                const int oidx = __float_as_int(m3[2]);
-                if (ob > best || (ob == best && oidx < bidx)) { best = ob; bv = obv; bidx = oidx; }
-            }
             float dk;
             q8k_scale(bv, best, kis[u], dk);
-            if (u < nsb && c16 == 0 && hf == 0) dxk[u * 16 + rho] = dk;
+            if (u < nsb && c16 == 0 && (u & 1) == hf) dxk[u * 16 + rho] = dk;
             if constexpr (EMIT)
-                if (u < nsb && c16 == 0 && hf == 0 && nt == 0 && a.act != nullptr && m0 + rho < M)
+                if (u < nsb && c16 == 0 && (u & 1) == hf && nt == 0 && a.act != nullptr && m0 + rho < M)
                     *reinterpret_cast<float*>(a.act + ((int64_t)(m0 + rho) * nsb + u) * 292) = dk;
         }
 #pragma unroll
         for (int i = 0; i < JI; ++i) {
-            const int j = S * i + hf;
+            const int j = jof(i);
             if (j < nj) {
                 float isc = kis[0];
 #pragma unroll
@@ -309,7 +287,7 @@ __global__ __launch_bounds__(GS_NT, 2) void gemm_s_kernel(GemmSArgs a)
         float* dxs = reinterpret_cast<float*>(lds + a.off_dx);
 #pragma unroll
         for (int i = 0; i < JI; ++i) {
-            const int j = S * i + hf;
+            const int j = jof(i);
             if (j < nj) {
                 // the block's max |x| over its eight lanes
                 float am = fmaxf(fmaxf(fabsf(xv[i][0]), fabsf(xv[i][1])), fmaxf(fabsf(xv[i][2]), fabsf(xv[i][3])));
@@ -608,7 +586,7 @@ static int gs_plan(int fmt, int mode, int64_t K, GemmSArgs& a)
     // mode (a): row exponents, the halves' row maxima; Q4_K also the sub-block sums [K/32][16]
     const int nsb = (int)(K / 256);
     const int dxbytes = mode == MODE_A ? 256 + (fmt == FMT_Q4_K ? nb * 64 : 0)
-                        : fmt == FMT_Q4_K ? nsb * 64 + nb * 64 + nsb * 2 * 16 * 12  // d_x, sums of 32, the halves' maxima
+                        : fmt == FMT_Q4_K ? nsb * 64 + nb * 64  // d_x, sums of 32
                                           : nb * 64;
     a.row_bytes = (int)gs_row_bytes(fmt, K);
     a.off_dx = abytes;
